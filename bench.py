@@ -1,0 +1,209 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X dense GEMM C = A @ B (one GPU).
+
+One step is one C = A @ B over the 4096^3 fp16-input / fp32-accumulate problem
+(row-major A and B, fp32 C; entries uniform[-1, 1) rounded to fp16, seed 0),
+launched through the library's C ABI in the configuration its heuristic picks.
+The fp32 4096^3 problem (the other half of the headline metric) and the other
+benchmark shapes are timed the same way and reported alongside.
+
+Timing: W untimed warm-up steps, then exactly K steps back to back, bracketed by
+torch.cuda.synchronize(); the duration is taken from HIP events recorded on the
+launch stream around the K launches (one kernel per step, so this is also the
+average kernel duration). Inputs are resident in HBM before timing starts.
+
+CPU baseline: the oracle (plain fp64 triple loop, OpenMP) timed on the host
+cores on a bounded sample of the same problem (its first r rows; about 10-20 s
+of CPU work), reported as TFLOP/s of the sample.
+
+Prints one JSON line. --gpus above 1 is refused: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3}   # MI355X dense matrix peaks
+HBM_GBPS = 8000.0
+KERNEL_SOURCES = ["kernels.h", "device_common.h", "menu.h", "inst_family.inc"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "dense_gemm_06_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extra", action="store_true", help="time only the headline problem")
+    p.add_argument("--only", default=None, help="time only this benchmark problem (for profiling)")
+    return p.parse_args()
+
+
+def device_problem(name, seed=0):
+    import torch
+    import gemm_inputs as gi
+    ops = gi.make_config(name, seed=seed)
+    def dev(a):
+        import numpy as np
+        t = torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a)
+        return t.to("cuda")
+    A, B = dev(ops.A), dev(ops.B)
+    C = torch.empty((ops.M, ops.N), dtype=torch.float32, device="cuda")
+    return ops, A, B, C
+
+
+def time_problem(name, steps, warmup):
+    """Warm up, then time exactly `steps` launches with HIP events on the launch stream."""
+    import torch
+    import dense_gemm_06_amd as dg
+    ops, A, B, C = device_problem(name)
+    stream = torch.cuda.current_stream()
+    s = stream.cuda_stream
+    args = (dg.GEMM_OP_N, dg.OP_CODE[ops.op_b], ops.M, ops.N, ops.K, A.data_ptr(), ops.lda, B.data_ptr(), ops.ldb,
+            C.data_ptr(), ops.N, dg.DTYPE_CODE[ops.dtype])
+    cus, arch = dg.gemm_device_info(0)
+    _, cfg = dg.gemm_plan(args[0], args[1], ops.M, ops.N, ops.K, ops.lda, ops.ldb, ops.N, args[-1],
+                          A.data_ptr(), B.data_ptr(), C.data_ptr(), cus, arch)
+    for _ in range(warmup):
+        dg.gemm_ex(*args, None, s)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        dg.gemm_ex(*args, None, s)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / steps
+    flops = 2.0 * ops.M * ops.N * ops.K
+    del A, B, C
+    return dict(problem=name, ms_per_step=ms, tflops=flops / (ms * 1e-3) / 1e12, wall_s=wall, dtype=ops.dtype,
+                M=ops.M, N=ops.N, K=ops.K, op_b=ops.op_b, flops=flops, cfg=cfg, cus=cus, arch=arch,
+                peak=PEAK_TFLOPS[ops.dtype])
+
+
+def cpu_baseline(name, target_s):
+    """The oracle on the first r rows of `name`, r chosen for about target_s seconds."""
+    import gemm_inputs as gi
+    import oracle
+    ops = gi.make_config(name)
+    oracle.build(force=False)
+    r = 4
+    _, t = oracle.timed_gemm_ref(ops, rows=list(range(r)))
+    per_row = max(t / r, 1e-4)
+    r = int(max(4, min(ops.M, target_s / per_row)))
+    _, t = oracle.timed_gemm_ref(ops, rows=list(range(r)))
+    flops = 2.0 * r * ops.N * ops.K
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"rows 0..{r - 1} of the {ops.M}x{ops.N}x{ops.K} {ops.dtype} problem "
+                      f"({r / ops.M:.4f} of its work), Cref only, fp64 accumulation; {t:.2f} s",
+            "seconds": t, "cpu_model": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def load_traffic(problem, cfg):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they match this kernel build."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    rec = data.get(problem)
+    if not rec or rec.get("kernel_source_hash") != kernel_source_hash() or rec.get("kernel_id") != cfg.kernel_id:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {a.gpus}); this build has no multi-GPU path",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import dense_gemm_06_amd as dg
+    dg.library()   # fail loudly if the HIP library is missing
+
+    headline = a.only or "c4_f16_4096"
+    main_res = time_problem(headline, a.steps, a.warmup)
+    extras = {}
+    if not a.no_extra and not a.only:
+        for name in ("c3_f32_4096", "c1_f32_256", "c2_f32_1024", "c5_bf16_ragged"):
+            extras[name] = time_problem(name, max(5, a.steps // 2), max(2, a.warmup // 2))
+
+    cfg = main_res["cfg"]
+    traffic = load_traffic(headline, cfg)
+    roof = {"bound": "mfma", "achieved": main_res["tflops"], "peak": main_res["peak"], "unit": "TFLOP/s",
+            "frac": main_res["tflops"] / main_res["peak"], "traffic": traffic,
+            "kernel": f"mfma16_gemm {cfg.bm}x{cfg.bn}x{cfg.bk} waves {cfg.waves_m}x{cfg.waves_n}"
+            if cfg.variant == 2 else f"lds_gemm {cfg.bm}x{cfg.bn}",
+            "flops_per_launch": main_res["flops"], "launch_ms": main_res["ms_per_step"]}
+    out = {
+        "metric": "GEMM TFLOP/s (2MNK/t) at 4096^3 fp16-in/fp32-acc (value) and fp32 (fp32 field); % of MFMA peak",
+        "value": round(main_res["tflops"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(main_res["ms_per_step"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": main_res["dtype"],
+        "data": "synthetic (seeded uniform[-1,1) rounded to the input dtype)",
+        "config": {"workload": f"C=A@B {main_res['M']}x{main_res['N']}x{main_res['K']} {main_res['dtype']} in, "
+                               f"fp32 acc/out, row-major A,B", "M": main_res["M"], "N": main_res["N"],
+                   "K": main_res["K"], "kernel_cfg": {k: v for k, v in cfg.as_dict().items() if k != "est_cycles"},
+                   "cus": main_res["cus"], "arch": main_res["arch"]},
+        "pct_of_peak": round(100 * main_res["tflops"] / main_res["peak"], 2),
+        "roofline": roof,
+    }
+    if "c3_f32_4096" in extras:
+        r = extras["c3_f32_4096"]
+        out["fp32"] = {"value": round(r["tflops"], 3), "unit": "TFLOP/s", "ms_per_step": round(r["ms_per_step"], 6),
+                       "peak": r["peak"], "frac": r["tflops"] / r["peak"],
+                       "kernel_cfg": {k: v for k, v in r["cfg"].as_dict().items() if k != "est_cycles"}}
+    if extras:
+        out["other_problems"] = {k: {"tflops": round(v["tflops"], 3), "ms_per_step": round(v["ms_per_step"], 6),
+                                     "frac_of_peak": round(v["tflops"] / v["peak"], 4),
+                                     "tile": f"{v['cfg'].bm}x{v['cfg'].bn}",
+                                     "variant": "mfma" if v["cfg"].variant == 2 else "lds"}
+                                 for k, v in extras.items()}
+    if not a.no_cpu_baseline and not a.only:
+        out["cpu_baseline"] = cpu_baseline(headline, a.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

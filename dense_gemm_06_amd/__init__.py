@@ -1,0 +1,200 @@
+"""Python binding of the MI355X dense GEMM library (libdensegemm.so).
+
+The functions mirror the C ABI in include/gemm.h one to one (gemm, gemm_ex,
+gemm_plan, gemm_menu_size / gemm_menu_entry, gemm_device_info,
+gemm_status_string, gemm_last_error) and only marshal arguments: every step of
+the product runs in the library's HIP kernels. A nonzero status raises
+GemmError carrying the library's own description.
+
+``gemm_tensors`` is a convenience for torch tensors: it reads pointers, leading
+dimensions and the current stream off the tensors and calls gemm_ex. Torch
+provides device memory and streams only.
+
+The library is loaded on first use. If it has not been built (``python -m
+dense_gemm_06_amd.build``) every call raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, fields
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdensegemm.so")
+
+GEMM_F32, GEMM_F16, GEMM_BF16 = 0, 1, 2
+GEMM_OP_N, GEMM_OP_T = 0, 1
+GEMM_OK = 0
+GEMM_ERR_INVALID_VALUE = 1
+GEMM_ERR_NULL_POINTER = 2
+GEMM_ERR_UNSUPPORTED = 3
+GEMM_ERR_DEVICE = 4
+GEMM_ERR_LAUNCH = 5
+GEMM_VARIANT_AUTO, GEMM_VARIANT_LDS, GEMM_VARIANT_MFMA = 0, 1, 2
+
+DTYPE_CODE = {"f32": GEMM_F32, "f16": GEMM_F16, "bf16": GEMM_BF16}
+OP_CODE = {"N": GEMM_OP_N, "T": GEMM_OP_T}
+
+
+class gemm_config(ctypes.Structure):
+    _fields_ = [
+        ("variant", ctypes.c_int32), ("bm", ctypes.c_int32), ("bn", ctypes.c_int32), ("bk", ctypes.c_int32),
+        ("vec", ctypes.c_int32), ("xcd_remap", ctypes.c_int32), ("group_m", ctypes.c_int32),
+        ("waves_m", ctypes.c_int32), ("waves_n", ctypes.c_int32),
+        ("thread_m", ctypes.c_int32), ("thread_n", ctypes.c_int32),
+        ("threads", ctypes.c_int32), ("lds_bytes", ctypes.c_int32), ("grid", ctypes.c_int32),
+        ("kernel_id", ctypes.c_int32), ("tiles_m", ctypes.c_int64), ("tiles_n", ctypes.c_int64),
+        ("est_cycles", ctypes.c_double),
+    ]
+
+    def as_dict(self) -> dict:
+        return {f[0]: getattr(self, f[0]) for f in self._fields_}
+
+
+def request(variant: int = GEMM_VARIANT_AUTO, bm: int = 0, bn: int = 0, vec: int = -1,
+            xcd_remap: int = -1, group_m: int = 0) -> gemm_config:
+    """A gemm_config with only the "in" fields set (0 / -1: heuristic decides)."""
+    c = gemm_config()
+    c.variant, c.bm, c.bn, c.vec, c.xcd_remap, c.group_m = variant, bm, bn, vec, xcd_remap, group_m
+    return c
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: {gemm_status_string(status)} -- {detail}")
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m dense_gemm_06_amd.build` "
+                           "(there is no fallback implementation)")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+    cfgp = ctypes.POINTER(gemm_config)
+    lib.gemm.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, i32, vp]
+    lib.gemm.restype = i32
+    lib.gemm_ex.argtypes = [i32, i32, i64, i64, i64, vp, i64, vp, i64, vp, i64, i32, cfgp, vp]
+    lib.gemm_ex.restype = i32
+    lib.gemm_plan.argtypes = [i32, i32, i64, i64, i64, i64, i64, i64, i32, ctypes.c_size_t, ctypes.c_size_t,
+                              ctypes.c_size_t, i32, ctypes.c_char_p, cfgp, cfgp]
+    lib.gemm_plan.restype = i32
+    lib.gemm_menu_size.argtypes = []
+    lib.gemm_menu_size.restype = i32
+    lib.gemm_menu_entry.argtypes = [i32, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32), cfgp]
+    lib.gemm_menu_entry.restype = i32
+    lib.gemm_device_info.argtypes = [i32, ctypes.POINTER(i32), ctypes.c_char_p, i32]
+    lib.gemm_device_info.restype = i32
+    lib.gemm_status_string.argtypes = [i32]
+    lib.gemm_status_string.restype = ctypes.c_char_p
+    lib.gemm_last_error.argtypes = []
+    lib.gemm_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def library():
+    """The loaded ctypes library (loads it on first call)."""
+    return _load()
+
+
+def gemm_status_string(status: int) -> str:
+    return _load().gemm_status_string(status).decode()
+
+
+def gemm_last_error() -> str:
+    return _load().gemm_last_error().decode()
+
+
+def _check(st: int, where: str):
+    if st != GEMM_OK:
+        raise GemmError(st, where, gemm_last_error())
+
+
+def gemm(M, N, K, A, lda, B, ldb, C, ldc, dtype, stream=None, check=True) -> int:
+    """C ABI gemm: pointers are device addresses (ints), dtype a GEMM_* code."""
+    st = _load().gemm(M, N, K, A, lda, B, ldb, C, ldc, dtype, stream)
+    if check:
+        _check(st, "gemm")
+    return st
+
+
+def gemm_ex(opA, opB, M, N, K, A, lda, B, ldb, C, ldc, dtype, cfg: gemm_config | None = None,
+            stream=None, check=True) -> int:
+    st = _load().gemm_ex(opA, opB, M, N, K, A, lda, B, ldb, C, ldc, dtype,
+                         ctypes.byref(cfg) if cfg is not None else None, stream)
+    if check:
+        _check(st, "gemm_ex")
+    return st
+
+
+def gemm_plan(opA, opB, M, N, K, lda, ldb, ldc, dtype, a_addr=0, b_addr=0, c_addr=0, num_cus=256,
+              arch="gfx950", req: gemm_config | None = None, check=True):
+    """Host-only: the configuration gemm_ex would launch. Returns (status, gemm_config)."""
+    out = gemm_config()
+    st = _load().gemm_plan(opA, opB, M, N, K, lda, ldb, ldc, dtype, a_addr, b_addr, c_addr, num_cus,
+                           arch.encode() if arch is not None else None,
+                           ctypes.byref(req) if req is not None else None, ctypes.byref(out))
+    if check:
+        _check(st, "gemm_plan")
+    return st, out
+
+
+def gemm_menu():
+    """Every compiled kernel configuration as dicts (variant, dtype, opb, tile fields)."""
+    lib = _load()
+    out = []
+    for i in range(lib.gemm_menu_size()):
+        v, d, o = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+        c = gemm_config()
+        _check(lib.gemm_menu_entry(i, ctypes.byref(v), ctypes.byref(d), ctypes.byref(o), ctypes.byref(c)),
+               "gemm_menu_entry")
+        e = c.as_dict()
+        e.update(variant=v.value, dtype=d.value, opb=o.value)
+        out.append(e)
+    return out
+
+
+def gemm_device_info(device: int = 0):
+    """(compute-unit count, architecture name) of a HIP device."""
+    n = ctypes.c_int()
+    buf = ctypes.create_string_buffer(64)
+    _check(_load().gemm_device_info(device, ctypes.byref(n), buf, 64), "gemm_device_info")
+    return n.value, buf.value.decode()
+
+
+# ----------------------------------------------------------------------------- torch convenience
+def _torch_dtype_code(t):
+    import torch
+    m = {torch.float32: GEMM_F32, torch.float16: GEMM_F16, torch.bfloat16: GEMM_BF16}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def gemm_tensors(A, B, C, op_b: str = "N", cfg: gemm_config | None = None, stream=None):
+    """C[:M,:N] = A @ B for torch CUDA tensors (row-major views with unit inner stride).
+
+    A: (M, K). B: (K, N) for op_b 'N', or its column-major storage (N, K) for op_b 'T'.
+    C: (M, N) float32. Leading dimensions are taken from the row strides.
+    """
+    import torch
+    if A.dim() != 2 or B.dim() != 2 or C.dim() != 2:
+        raise ValueError("A, B, C must be 2-D")
+    if A.stride(1) != 1 or B.stride(1) != 1 or C.stride(1) != 1:
+        raise ValueError("A, B, C need unit stride along their last dimension")
+    if C.dtype != torch.float32 or A.dtype != B.dtype:
+        raise TypeError("C must be float32 and A, B share one dtype")
+    M, K = A.shape
+    N = B.shape[1] if op_b == "N" else B.shape[0]
+    if (B.shape[0] if op_b == "N" else B.shape[1]) != K or tuple(C.shape) != (M, N):
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)} (op {op_b}), C {tuple(C.shape)}")
+    s = stream if stream is not None else torch.cuda.current_stream(A.device).cuda_stream
+    return gemm_ex(GEMM_OP_N, OP_CODE[op_b], M, N, K, A.data_ptr(), max(A.stride(0), 1), B.data_ptr(),
+                   max(B.stride(0), 1), C.data_ptr(), max(C.stride(0), 1), _torch_dtype_code(A), cfg, s)

@@ -1,0 +1,193 @@
+// gemm_api.cpp -- the C ABI declared in include/gemm.h.
+//
+// Validation and planning are host-only (plan.cpp); this file adds the device
+// query, the pointer checks and the launch. Every status from the HIP runtime
+// is checked and turned into a gemm_status with a description, in the spirit of
+// the chapter's runtime that raises on any nonzero driver status and says what
+// failed ("GPU architecture and mapping kernels", section 12.10).
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/gemm.h"
+#include "launch.h"
+#include "plan.h"
+
+namespace {
+
+struct DeviceInfo {
+    bool valid = false;
+    int status = GEMM_ERR_DEVICE;
+    int num_cus = 0;
+    char arch[64] = {0};
+};
+
+std::mutex g_dev_mutex;
+std::vector<DeviceInfo> g_devs;
+
+// Per-device (CU count, architecture), queried once per device.
+int device_info(int dev, DeviceInfo* out) {
+    std::lock_guard<std::mutex> lock(g_dev_mutex);
+    if (dev < 0) {
+        dg::set_error("invalid device index %d", dev);
+        return GEMM_ERR_DEVICE;
+    }
+    if ((size_t)dev >= g_devs.size()) g_devs.resize(dev + 1);
+    DeviceInfo& d = g_devs[dev];
+    if (!d.valid) {
+        hipDeviceProp_t prop;
+        hipError_t e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) {
+            dg::set_error("hipGetDeviceProperties(%d) failed: %s", dev, hipGetErrorString(e));
+            return GEMM_ERR_DEVICE;
+        }
+        d.num_cus = prop.multiProcessorCount;
+        strncpy(d.arch, prop.gcnArchName, sizeof d.arch - 1);
+        d.valid = true;
+    }
+    *out = d;
+    return GEMM_OK;
+}
+
+bool ranges_overlap(uintptr_t a, uint64_t alen, uintptr_t b, uint64_t blen) {
+    if (alen == 0 || blen == 0) return false;
+    return a < b + blen && b < a + alen;
+}
+
+int launch(int id, const dg::GemmArgs& args, unsigned grid, hipStream_t s) {
+    const dg::MenuEntry& e = dg::kMenu[id];
+    int rc = -1;
+    if (e.variant == dg::V_LDS) {
+        rc = e.dtype == dg::DT_F32 ? dg::launch_lds_f32(id, args, grid, s)
+             : e.dtype == dg::DT_F16 ? dg::launch_lds_f16(id, args, grid, s)
+                                     : dg::launch_lds_bf16(id, args, grid, s);
+    } else {
+        rc = e.dtype == dg::DT_F32 ? dg::launch_mfma_f32(id, args, grid, s)
+             : e.dtype == dg::DT_F16 ? dg::launch_mfma_f16(id, args, grid, s)
+                                     : dg::launch_mfma_bf16(id, args, grid, s);
+    }
+    return rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_ex(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+            int64_t ldb, float* C, int64_t ldc, int dtype, const gemm_config* cfg, void* stream) {
+    dg::clear_error();
+    int st = dg::validate(opA, opB, M, N, K, lda, ldb, ldc, dtype);
+    if (st != GEMM_OK) return st;
+    if (M == 0 || N == 0) return GEMM_OK;
+    if (C == nullptr || (K > 0 && (A == nullptr || B == nullptr))) {
+        dg::set_error("NULL operand: A = %p, B = %p, C = %p (M = %lld, N = %lld, K = %lld)", A, B, (void*)C,
+                      (long long)M, (long long)N, (long long)K);
+        return GEMM_ERR_NULL_POINTER;
+    }
+    const uint64_t es = dtype == GEMM_F32 ? 4 : 2;
+    const uint64_t clen = ((uint64_t)(M - 1) * ldc + N) * 4;
+    if (K > 0) {
+        const uint64_t alen = ((uint64_t)(M - 1) * lda + K) * es;
+        const uint64_t blen = (opB == GEMM_OP_N ? (uint64_t)(K - 1) * ldb + N : (uint64_t)(N - 1) * ldb + K) * es;
+        if (ranges_overlap((uintptr_t)C, clen, (uintptr_t)A, alen) ||
+            ranges_overlap((uintptr_t)C, clen, (uintptr_t)B, blen)) {
+            dg::set_error("C overlaps A or B; the output must not alias an input");
+            return GEMM_ERR_INVALID_VALUE;
+        }
+    }
+    int dev = 0;
+    hipError_t he = hipGetDevice(&dev);
+    if (he != hipSuccess) {
+        dg::set_error("hipGetDevice failed: %s", hipGetErrorString(he));
+        return GEMM_ERR_DEVICE;
+    }
+    DeviceInfo info;
+    st = device_info(dev, &info);
+    if (st != GEMM_OK) return st;
+    gemm_config plan;
+    st = dg::plan(opA, opB, M, N, K, lda, ldb, ldc, dtype, (uintptr_t)A, (uintptr_t)B, (uintptr_t)C, info.num_cus,
+                  info.arch, cfg, &plan);
+    if (st != GEMM_OK) return st;
+
+    dg::GemmArgs args;
+    args.A = A;
+    args.B = B;
+    args.C = C;
+    args.lda = lda;
+    args.ldb = ldb;
+    args.ldc = ldc;
+    args.M = (int)M;
+    args.N = (int)N;
+    args.K = (int)K;
+    args.tiles_m = (int)plan.tiles_m;
+    args.tiles_n = (int)plan.tiles_n;
+    args.group_m = plan.group_m;
+    args.xcd_remap = plan.xcd_remap;
+    (void)hipGetLastError();  // clear a stale error left by earlier unrelated work
+    if (launch(plan.kernel_id, args, (unsigned)plan.grid, (hipStream_t)stream) != 0) {
+        dg::set_error("internal: kernel %d has no launcher", plan.kernel_id);
+        return GEMM_ERR_LAUNCH;
+    }
+    he = hipGetLastError();
+    if (he != hipSuccess) {
+        dg::set_error("kernel launch failed: %s", hipGetErrorString(he));
+        return GEMM_ERR_LAUNCH;
+    }
+    return GEMM_OK;
+}
+
+int gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb, float* C,
+         int64_t ldc, int dtype, void* stream) {
+    return gemm_ex(GEMM_OP_N, GEMM_OP_N, M, N, K, A, lda, B, ldb, C, ldc, dtype, nullptr, stream);
+}
+
+int gemm_plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int dtype,
+              uintptr_t a_addr, uintptr_t b_addr, uintptr_t c_addr, int num_cus, const char* arch,
+              const gemm_config* request, gemm_config* out) {
+    dg::clear_error();
+    if (out == nullptr) {
+        dg::set_error("gemm_plan: out is NULL");
+        return GEMM_ERR_NULL_POINTER;
+    }
+    return dg::plan(opA, opB, M, N, K, lda, ldb, ldc, dtype, a_addr, b_addr, c_addr, num_cus, arch, request, out);
+}
+
+int gemm_menu_size(void) { return dg::kMenuSize; }
+
+int gemm_menu_entry(int index, int* variant, int* dtype, int* opb, gemm_config* out) {
+    dg::clear_error();
+    return dg::menu_entry(index, variant, dtype, opb, out);
+}
+
+int gemm_device_info(int device, int* num_cus, char* arch, int len) {
+    dg::clear_error();
+    DeviceInfo info;
+    int st = device_info(device, &info);
+    if (st != GEMM_OK) return st;
+    if (num_cus) *num_cus = info.num_cus;
+    if (arch && len > 0) {
+        strncpy(arch, info.arch, (size_t)len - 1);
+        arch[len - 1] = '\0';
+    }
+    return GEMM_OK;
+}
+
+const char* gemm_status_string(int status) {
+    switch (status) {
+        case GEMM_OK: return "GEMM_OK";
+        case GEMM_ERR_INVALID_VALUE: return "GEMM_ERR_INVALID_VALUE: an argument is out of range";
+        case GEMM_ERR_NULL_POINTER: return "GEMM_ERR_NULL_POINTER: a required operand pointer is NULL";
+        case GEMM_ERR_UNSUPPORTED: return "GEMM_ERR_UNSUPPORTED: valid request not implemented by this build";
+        case GEMM_ERR_DEVICE: return "GEMM_ERR_DEVICE: no usable gfx950 device";
+        case GEMM_ERR_LAUNCH: return "GEMM_ERR_LAUNCH: the kernel launch failed";
+        default: return "unknown gemm_status";
+    }
+}
+
+const char* gemm_last_error(void) { return dg::last_error(); }
+
+}  // extern "C"

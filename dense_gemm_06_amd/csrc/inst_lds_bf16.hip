@@ -1,0 +1,5 @@
+// Kernels of the lds family with bf16 inputs.
+#define DG_FAMILY_VARIANT dg::V_LDS
+#define DG_FAMILY_DTYPE dg::DT_BF16
+#define DG_FAMILY_LAUNCH launch_lds_bf16
+#include "inst_family.inc"

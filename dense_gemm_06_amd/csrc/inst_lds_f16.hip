@@ -1,0 +1,5 @@
+// Kernels of the lds family with f16 inputs.
+#define DG_FAMILY_VARIANT dg::V_LDS
+#define DG_FAMILY_DTYPE dg::DT_F16
+#define DG_FAMILY_LAUNCH launch_lds_f16
+#include "inst_family.inc"

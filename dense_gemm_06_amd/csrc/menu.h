@@ -1,0 +1,77 @@
+// menu.h -- the compiled kernel configurations and the launch-argument block.
+//
+// Internal to the library. Host-only code (the planner) reads the menu as plain
+// data; the HIP translation units instantiate one kernel per entry. Keeping the
+// list in one X-macro is what keeps the two sides consistent.
+#pragma once
+#include <stdint.h>
+
+namespace dg {
+
+enum Variant { V_LDS = 1, V_MFMA = 2 };
+enum Dtype { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+
+// One kernel configuration.
+//   variant : V_LDS (LDS-staged SIMT FMA) or V_MFMA (matrix cores)
+//   dtype   : input element type (accumulation and C are fp32)
+//   opb     : 0 = B row-major K x N, 1 = B column-major (row-major N x K)
+//   vec     : 1 = 16-byte global loads (needs aligned bases and leading dims),
+//             0 = element-wise loads (any alignment)
+//   bm, bn, bk : block tile; wm x wn : wave grid (MFMA); tm x tn : thread tile (LDS)
+struct MenuEntry {
+    int id, variant, dtype, opb, vec, bm, bn, bk, wm, wn, tm, tn, threads, lds_bytes;
+};
+
+// X(id, variant, dtype, opb, vec, bm, bn, bk, wm, wn, tm, tn, threads, lds_bytes)
+// The largest MFMA tile is 256 x 256 (2 x 4 waves) for 16-bit inputs and 256 x 128
+// (4 x 2 waves) for fp32; the fp32 kernel's 64 x 64 tile uses a 4 x 1 wave grid
+// (its row-major-B path needs 64-wide wave tiles).
+// LDS bytes: LDS variant holds two fp32 stages of A^T (bk x bm) and B (bk x bn);
+// MFMA variant holds two stages of the input-typed A (bm x bk) and B (bk x bn).
+#define DG_LDS_ENTRIES(X, base, dt, bk)                                                  \
+    X(base + 0, V_LDS, dt, 0, 1, 128, 128, bk, 1, 1, 8, 8, 256, 2 * 4 * bk * 256)          \
+    X(base + 1, V_LDS, dt, 1, 1, 128, 128, bk, 1, 1, 8, 8, 256, 2 * 4 * bk * 256)          \
+    X(base + 2, V_LDS, dt, 0, 0, 128, 128, bk, 1, 1, 8, 8, 256, 2 * 4 * bk * 256)          \
+    X(base + 3, V_LDS, dt, 1, 0, 128, 128, bk, 1, 1, 8, 8, 256, 2 * 4 * bk * 256)          \
+    X(base + 4, V_LDS, dt, 0, 1, 64, 64, bk, 1, 1, 4, 4, 256, 2 * 4 * bk * 128)            \
+    X(base + 5, V_LDS, dt, 1, 1, 64, 64, bk, 1, 1, 4, 4, 256, 2 * 4 * bk * 128)            \
+    X(base + 6, V_LDS, dt, 0, 0, 64, 64, bk, 1, 1, 4, 4, 256, 2 * 4 * bk * 128)            \
+    X(base + 7, V_LDS, dt, 1, 0, 64, 64, bk, 1, 1, 4, 4, 256, 2 * 4 * bk * 128)
+
+#define DG_MFMA_ENTRIES(X, base, dt, es, bk, BBM, BBN, BWM, BWN, w64m, w64n)                            \
+    X(base + 0, V_MFMA, dt, 0, 1, BBM, BBN, bk, BWM, BWN, 0, 0, 512, 2 * es * bk * (BBM + BBN)) \
+    X(base + 1, V_MFMA, dt, 1, 1, BBM, BBN, bk, BWM, BWN, 0, 0, 512, 2 * es * bk * (BBM + BBN)) \
+    X(base + 2, V_MFMA, dt, 0, 0, BBM, BBN, bk, BWM, BWN, 0, 0, 512, 2 * es * bk * (BBM + BBN)) \
+    X(base + 3, V_MFMA, dt, 1, 0, BBM, BBN, bk, BWM, BWN, 0, 0, 512, 2 * es * bk * (BBM + BBN)) \
+    X(base + 4, V_MFMA, dt, 0, 1, 128, 128, bk, 2, 2, 0, 0, 256, 2 * es * bk * 256)        \
+    X(base + 5, V_MFMA, dt, 1, 1, 128, 128, bk, 2, 2, 0, 0, 256, 2 * es * bk * 256)        \
+    X(base + 6, V_MFMA, dt, 0, 0, 128, 128, bk, 2, 2, 0, 0, 256, 2 * es * bk * 256)        \
+    X(base + 7, V_MFMA, dt, 1, 0, 128, 128, bk, 2, 2, 0, 0, 256, 2 * es * bk * 256)        \
+    X(base + 8, V_MFMA, dt, 0, 1, 64, 64, bk, w64m, w64n, 0, 0, 256, 2 * es * bk * 128)    \
+    X(base + 9, V_MFMA, dt, 1, 1, 64, 64, bk, w64m, w64n, 0, 0, 256, 2 * es * bk * 128)    \
+    X(base + 10, V_MFMA, dt, 0, 0, 64, 64, bk, w64m, w64n, 0, 0, 256, 2 * es * bk * 128)   \
+    X(base + 11, V_MFMA, dt, 1, 0, 64, 64, bk, w64m, w64n, 0, 0, 256, 2 * es * bk * 128)
+
+#define DG_MENU(X)                                              \
+    DG_LDS_ENTRIES(X, 0, DT_F32, 16)            \
+    DG_LDS_ENTRIES(X, 8, DT_F16, 32)            \
+    DG_LDS_ENTRIES(X, 16, DT_BF16, 32)          \
+    DG_MFMA_ENTRIES(X, 24, DT_F32, 4, 32, 256, 128, 4, 2, 4, 1) \
+    DG_MFMA_ENTRIES(X, 36, DT_F16, 2, 64, 256, 256, 2, 4, 2, 2) \
+    DG_MFMA_ENTRIES(X, 48, DT_BF16, 2, 64, 256, 256, 2, 4, 2, 2)
+
+constexpr int kMenuSize = 60;
+
+// Arguments every kernel receives (by value).
+struct GemmArgs {
+    const void* A;
+    const void* B;
+    float* C;
+    int64_t lda, ldb, ldc;  // in elements
+    int M, N, K;
+    int tiles_m, tiles_n;   // ceil(M / bm), ceil(N / bn)
+    int group_m;            // tile rows per raster group (L2 locality)
+    int xcd_remap;          // 1: give each XCD a contiguous range of tiles
+};
+
+}  // namespace dg

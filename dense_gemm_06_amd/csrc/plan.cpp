@@ -1,0 +1,255 @@
+// plan.cpp -- argument validation and the launch heuristic (host only, no HIP).
+//
+// The heuristic plays the role of gpu_opt_choice in "GPU architecture and
+// mapping kernels" (section 12.9) for one operation, C = A @ B: threads are laid
+// out along the contiguous axis (fixed inside each kernel), tiles are powers of
+// two with masked edges instead of a divisibility requirement, a register
+// micro-tile (or MFMA wave tile) is always used because the kernel reduces, and
+// the grid must fill the machine (the chapter's exercise on a minimum block
+// count): among the compiled configurations it picks the one with the lowest
+// estimated time, where the estimate counts how many rounds of workgroups the
+// 256 compute units need. 16-byte global loads are used only when the operand
+// bases and leading dimensions are 16-byte aligned (the learn-cutedsl README's
+// point that vector copies need a known 16-byte alignment).
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <cmath>
+#include <string>
+
+#include "../../include/gemm.h"
+#include "menu.h"
+#include "plan.h"
+
+namespace dg {
+
+static thread_local std::string g_last_error;
+
+void set_error(const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+}
+void clear_error() { g_last_error.clear(); }
+const char* last_error() { return g_last_error.c_str(); }
+
+const MenuEntry kMenu[kMenuSize] = {
+#define DG_ENTRY(id, variant, dtype, opb, vec, bm, bn, bk, wm, wn, tm, tn, threads, lds) \
+    {id, variant, dtype, opb, vec, bm, bn, bk, wm, wn, tm, tn, threads, lds},
+    DG_MENU(DG_ENTRY)
+#undef DG_ENTRY
+};
+
+static const char* dtype_name(int dt) { return dt == 0 ? "fp32" : dt == 1 ? "fp16" : "bf16"; }
+static int elem_size(int dt) { return dt == DT_F32 ? 4 : 2; }
+
+int validate(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+             int dtype) {
+    if (dtype < 0 || dtype > 2) {
+        set_error("dtype %d is not GEMM_F32 (0), GEMM_F16 (1) or GEMM_BF16 (2)", dtype);
+        return GEMM_ERR_INVALID_VALUE;
+    }
+    if ((opA != GEMM_OP_N && opA != GEMM_OP_T) || (opB != GEMM_OP_N && opB != GEMM_OP_T)) {
+        set_error("opA = %d / opB = %d: operand flags must be GEMM_OP_N (0) or GEMM_OP_T (1)", opA, opB);
+        return GEMM_ERR_INVALID_VALUE;
+    }
+    if (M < 0 || N < 0 || K < 0) {
+        set_error("negative size: M = %lld, N = %lld, K = %lld", (long long)M, (long long)N, (long long)K);
+        return GEMM_ERR_INVALID_VALUE;
+    }
+    const int64_t minlda = std::max<int64_t>(1, K);
+    const int64_t minldb = opB == GEMM_OP_N ? std::max<int64_t>(1, N) : std::max<int64_t>(1, K);
+    const int64_t minldc = std::max<int64_t>(1, N);
+    if (lda < minlda) {
+        set_error("lda = %lld is smaller than max(1, K) = %lld", (long long)lda, (long long)minlda);
+        return GEMM_ERR_INVALID_VALUE;
+    }
+    if (ldb < minldb) {
+        set_error("ldb = %lld is smaller than %s = %lld", (long long)ldb,
+                  opB == GEMM_OP_N ? "max(1, N) for row-major B" : "max(1, K) for column-major B",
+                  (long long)minldb);
+        return GEMM_ERR_INVALID_VALUE;
+    }
+    if (ldc < minldc) {
+        set_error("ldc = %lld is smaller than max(1, N) = %lld", (long long)ldc, (long long)minldc);
+        return GEMM_ERR_INVALID_VALUE;
+    }
+    if (opA == GEMM_OP_T) {
+        set_error("opA = GEMM_OP_T (column-major A) is not implemented by this library");
+        return GEMM_ERR_UNSUPPORTED;
+    }
+    // The kernels index rows, columns and k with 32-bit integers (tile origins
+    // plus one tile of slack must stay representable).
+    const int64_t lim = (int64_t)1 << 30;
+    if (M >= lim || N >= lim || K >= lim) {
+        set_error("sizes must be below 2^30 (M = %lld, N = %lld, K = %lld)", (long long)M, (long long)N,
+                  (long long)K);
+        return GEMM_ERR_UNSUPPORTED;
+    }
+    // Per-thread global offsets are 32-bit: up to 256 rows of a leading dimension.
+    const int64_t ldlim = (int64_t)1 << 23;
+    if (lda >= ldlim || ldb >= ldlim) {
+        set_error("leading dimensions must be below 2^23 elements (lda = %lld, ldb = %lld)", (long long)lda,
+                  (long long)ldb);
+        return GEMM_ERR_UNSUPPORTED;
+    }
+    if ((M + 255) / 256 * ((N + 255) / 256) >= lim || ((M + 63) / 64) * ((N + 63) / 64) >= ((int64_t)1 << 31)) {
+        set_error("too many output tiles for one launch (M = %lld, N = %lld)", (long long)M, (long long)N);
+        return GEMM_ERR_UNSUPPORTED;
+    }
+    return GEMM_OK;
+}
+
+// Matrix throughput per compute unit per clock and a per-tile efficiency
+// factor (smaller tiles reuse each loaded byte fewer times and leave the
+// matrix units waiting on LDS and global memory more often).
+static double rate_per_cu(const MenuEntry& e) {
+    if (e.variant == V_LDS) return 128.0;  // 64 lanes x 2 FLOP per FMA, one wave64 FMA per SIMD per 4 clocks x 4 SIMDs
+    return e.dtype == DT_F32 ? 256.0 : 4096.0;
+}
+static double tile_efficiency(const MenuEntry& e) {
+    const int t = std::min(e.bm, e.bn);
+    if (e.variant == V_LDS) return t >= 128 ? 0.6 : 0.35;
+    return t >= 256 ? 0.85 : t >= 128 ? 0.7 : 0.45;
+}
+static int blocks_per_cu(const MenuEntry& e) {
+    const int by_lds = (160 * 1024) / e.lds_bytes;
+    const int by_waves = 32 / (e.threads / 64);  // 8 waves per SIMD x 4 SIMDs
+    return std::max(1, std::min(by_lds, by_waves));
+}
+
+static bool aligned16(uintptr_t a) { return (a & 15) == 0; }
+
+int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int dtype,
+         uintptr_t a, uintptr_t b, uintptr_t c, int num_cus, const char* arch, const gemm_config* req,
+         gemm_config* out) {
+    (void)c;
+    int st = validate(opA, opB, M, N, K, lda, ldb, ldc, dtype);
+    if (st != GEMM_OK) return st;
+    if (arch == nullptr || strncmp(arch, "gfx950", 6) != 0) {
+        set_error("device architecture '%s' is not gfx950; the kernels are built for gfx950 only",
+                  arch ? arch : "(null)");
+        return GEMM_ERR_DEVICE;
+    }
+    if (num_cus <= 0) {
+        set_error("compute-unit count %d must be positive", num_cus);
+        return GEMM_ERR_INVALID_VALUE;
+    }
+    const int es = elem_size(dtype);
+    const bool vec_ok = aligned16(a) && aligned16(b) && (lda * es) % 16 == 0 && (ldb * es) % 16 == 0;
+
+    int want_variant = GEMM_VARIANT_AUTO, want_bm = 0, want_bn = 0, want_vec = -1, want_remap = -1, want_group = 0;
+    if (req) {
+        want_variant = req->variant;
+        want_bm = req->bm;
+        want_bn = req->bn;
+        want_vec = req->vec;
+        want_remap = req->xcd_remap;
+        want_group = req->group_m;
+        if (want_variant < 0 || want_variant > 2 || want_vec < -1 || want_vec > 1 || want_remap < -1 ||
+            want_remap > 1 || want_group < 0 || want_bm < 0 || want_bn < 0) {
+            set_error("invalid requested configuration (variant %d, bm %d, bn %d, vec %d, xcd_remap %d, group_m %d)",
+                      want_variant, want_bm, want_bn, want_vec, want_remap, want_group);
+            return GEMM_ERR_INVALID_VALUE;
+        }
+        if (want_vec == 1 && !vec_ok) {
+            set_error("16-byte loads requested but A/B bases or leading dimensions are not 16-byte aligned");
+            return GEMM_ERR_UNSUPPORTED;
+        }
+    }
+
+    const MenuEntry* best = nullptr;
+    double best_cost = 0;
+    for (const MenuEntry& e : kMenu) {
+        if (e.dtype != dtype || e.opb != opB) continue;
+        if (want_variant != GEMM_VARIANT_AUTO && e.variant != want_variant) continue;
+        if (want_bm && e.bm != want_bm) continue;
+        if (want_bn && e.bn != want_bn) continue;
+        const int vec = want_vec >= 0 ? want_vec : (vec_ok ? 1 : 0);
+        if (e.vec != vec) continue;
+        const int64_t tiles = ((M + e.bm - 1) / e.bm) * ((N + e.bn - 1) / e.bn);
+        const int64_t kpad = ((K + e.bk - 1) / e.bk) * e.bk;
+        const int occ = blocks_per_cu(e);
+        const int64_t concurrent = (int64_t)num_cus * occ;
+        const int64_t rounds = (tiles + concurrent - 1) / concurrent;
+        const int64_t resident = std::min<int64_t>(occ, (tiles + num_cus - 1) / num_cus);
+        const double tile_cycles = 2.0 * e.bm * e.bn * std::max<int64_t>(kpad, e.bk) / (rate_per_cu(e) * tile_efficiency(e));
+        const double cost = (double)rounds * (double)std::max<int64_t>(resident, 1) * tile_cycles;
+        if (!best || cost < best_cost * (1 - 1e-9) ||
+            (cost <= best_cost * (1 + 1e-9) && e.bm * e.bn > best->bm * best->bn)) {
+            best = &e;
+            best_cost = cost;
+        }
+    }
+    if (!best) {
+        set_error("no compiled kernel matches: dtype %s, opB %s, variant %d, bm %d, bn %d, vec %d",
+                  dtype_name(dtype), opB == GEMM_OP_N ? "N" : "T", want_variant, want_bm, want_bn, want_vec);
+        return GEMM_ERR_UNSUPPORTED;
+    }
+    const MenuEntry& e = *best;
+    gemm_config cfg;
+    memset(&cfg, 0, sizeof cfg);
+    cfg.variant = e.variant;
+    cfg.bm = e.bm;
+    cfg.bn = e.bn;
+    cfg.bk = e.bk;
+    cfg.vec = e.vec;
+    cfg.waves_m = e.variant == V_MFMA ? e.wm : 1;
+    cfg.waves_n = e.variant == V_MFMA ? e.wn : 1;
+    cfg.thread_m = e.tm;
+    cfg.thread_n = e.tn;
+    cfg.threads = e.threads;
+    cfg.lds_bytes = e.lds_bytes;
+    cfg.kernel_id = e.id;
+    cfg.tiles_m = (M + e.bm - 1) / e.bm;
+    cfg.tiles_n = (N + e.bn - 1) / e.bn;
+    cfg.grid = (int32_t)(cfg.tiles_m * cfg.tiles_n);
+    // Group enough tile rows that one XCD's share of the grid forms a compact
+    // rectangle; the remap needs the grid to split evenly over the 8 XCDs.
+    int gm = want_group;
+    if (gm == 0) {
+        const int64_t per_xcd = std::max<int64_t>(1, cfg.grid / 8);
+        gm = 1;
+        while ((int64_t)gm * gm * 2 < per_xcd && gm < cfg.tiles_m) gm *= 2;
+    }
+    cfg.group_m = (int32_t)std::max<int64_t>(1, std::min<int64_t>(gm, cfg.tiles_m));
+    cfg.xcd_remap = want_remap >= 0 ? want_remap : ((cfg.grid % 8 == 0 && cfg.grid >= 16) ? 1 : 0);
+    cfg.est_cycles = best_cost;
+    *out = cfg;
+    return GEMM_OK;
+}
+
+int menu_entry(int index, int* variant, int* dtype, int* opb, gemm_config* out) {
+    if (index < 0 || index >= kMenuSize) {
+        set_error("menu index %d out of range [0, %d)", index, kMenuSize);
+        return GEMM_ERR_INVALID_VALUE;
+    }
+    const MenuEntry& e = kMenu[index];
+    if (variant) *variant = e.variant;
+    if (dtype) *dtype = e.dtype;
+    if (opb) *opb = e.opb;
+    if (out) {
+        memset(out, 0, sizeof *out);
+        out->variant = e.variant;
+        out->bm = e.bm;
+        out->bn = e.bn;
+        out->bk = e.bk;
+        out->vec = e.vec;
+        out->waves_m = e.variant == V_MFMA ? e.wm : 1;
+        out->waves_n = e.variant == V_MFMA ? e.wn : 1;
+        out->thread_m = e.tm;
+        out->thread_n = e.tn;
+        out->threads = e.threads;
+        out->lds_bytes = e.lds_bytes;
+        out->kernel_id = e.id;
+        out->xcd_remap = -1;
+    }
+    return GEMM_OK;
+}
+
+}  // namespace dg

@@ -1,0 +1,23 @@
+// plan.h -- internal interface between the C ABI and the host-only planner.
+#pragma once
+#include <stdint.h>
+
+#include "../../include/gemm.h"
+#include "menu.h"
+
+namespace dg {
+
+extern const MenuEntry kMenu[kMenuSize];
+
+void set_error(const char* fmt, ...);
+void clear_error();
+const char* last_error();
+
+int validate(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+             int dtype);
+int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int dtype,
+         uintptr_t a, uintptr_t b, uintptr_t c, int num_cus, const char* arch, const gemm_config* req,
+         gemm_config* out);
+int menu_entry(int index, int* variant, int* dtype, int* opb, gemm_config* out);
+
+}  // namespace dg

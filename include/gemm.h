@@ -1,0 +1,140 @@
+/*
+ * gemm.h -- C ABI of the MI355X (gfx950) dense GEMM library.
+ *
+ * The library computes the dense matrix product C = A @ B, the operation of
+ * "Shared memory and tensor cores" (ML compiler from scratch, chapter 13):
+ * section 13.1 sets up C = A @ B and its memory traffic, section 13.3 the
+ * block-tiled shared-memory kernel, section 13.8 the tensor-core contract
+ * (16-bit inputs, products exact, accumulation in fp32). Two kernel families
+ * implement it on gfx950: an LDS-staged SIMT kernel and a matrix-core (MFMA)
+ * kernel; a heuristic picks one per call (the role of gpu_opt_choice in
+ * "GPU architecture and mapping kernels", section 12.9).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - C[i][j] = sum_{k<K} A(i,k) * B(k,j) for 0 <= i < M, 0 <= j < N, accumulated
+ *    in fp32, written to C in fp32. C is overwritten: there is no alpha or beta,
+ *    and prior contents (NaN included) are ignored.
+ *  - Storage is row-major with BLAS-style leading dimensions in ELEMENTS:
+ *      A(i,k) = A[i*lda + k]                      (opA = GEMM_OP_N, lda >= max(1,K))
+ *      B(k,j) = B[k*ldb + j]                      (opB = GEMM_OP_N, ldb >= max(1,N))
+ *      B(k,j) = B[j*ldb + k]  (column-major B)    (opB = GEMM_OP_T, ldb >= max(1,K))
+ *      C[i][j] = C[i*ldc + j]                     (ldc >= max(1,N))
+ *    Column-major B is the layout the learn-cutedsl README's naive kernel reads
+ *    (B indexed as [column, k]) and the one its layout section calls typical.
+ *  - dtype gives the element type of A and B: GEMM_F32 (IEEE binary32),
+ *    GEMM_F16 (IEEE binary16), GEMM_BF16 (bfloat16). C is always fp32.
+ *  - Pointers A, B, C are DEVICE pointers (memory the caller allocated on the
+ *    current HIP device); the caller owns them and the stream. A and B must not
+ *    overlap C (the kernels read them through restrict-qualified pointers);
+ *    overlap is detected and rejected. No alignment is required: 16-byte global
+ *    loads are used only when the bases and leading dimensions allow them.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued on
+ *    it and the call returns without synchronizing; faults during execution
+ *    surface at the caller's next synchronization.
+ *  - Degenerate shapes: M == 0 or N == 0 is a successful no-op (nothing is
+ *    launched, C untouched); K == 0 writes C[:M,:N] = 0, the empty sum.
+ *  - Errors: every argument is validated before anything is enqueued, so a
+ *    failing call launches nothing. Calls return a gemm_status; the thread-local
+ *    gemm_last_error() describes what was rejected and why. Nothing aborts and
+ *    no C++ exception crosses this interface.
+ *  - State: the library allocates no device memory and keeps no workspace; the
+ *    only state is a per-device cache of (compute-unit count, architecture)
+ *    filled on first use. All entry points are thread-safe.
+ */
+#ifndef DENSE_GEMM_06_AMD_GEMM_H
+#define DENSE_GEMM_06_AMD_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { GEMM_F32 = 0, GEMM_F16 = 1, GEMM_BF16 = 2 } gemm_dtype;
+
+typedef enum { GEMM_OP_N = 0, GEMM_OP_T = 1 } gemm_op;
+
+typedef enum {
+    GEMM_OK = 0,
+    GEMM_ERR_INVALID_VALUE = 1, /* negative size, bad enum, short leading dimension, C overlaps A or B */
+    GEMM_ERR_NULL_POINTER = 2,  /* NULL operand for a non-empty product */
+    GEMM_ERR_UNSUPPORTED = 3,   /* valid request this build does not implement (opA = T, sizes >= 2^31,
+                                   a forced configuration that does not exist or does not fit) */
+    GEMM_ERR_DEVICE = 4,        /* no HIP device, or the current device is not gfx950 */
+    GEMM_ERR_LAUNCH = 5         /* the kernel launch itself failed */
+} gemm_status;
+
+typedef enum { GEMM_VARIANT_AUTO = 0, GEMM_VARIANT_LDS = 1, GEMM_VARIANT_MFMA = 2 } gemm_variant;
+
+/*
+ * A launch configuration, in the role of the chapter's Opts / launch_dims:
+ * which kernel, its tiles, and the grid. As an INPUT (gemm_ex, gemm_plan) only
+ * the fields marked "in" are read; 0 / -1 there mean "let the heuristic choose".
+ * As an OUTPUT every field describes the launch gemm_ex would make.
+ */
+typedef struct gemm_config {
+    int32_t variant;   /* in/out: gemm_variant (AUTO lets the heuristic choose) */
+    int32_t bm, bn;    /* in/out: block tile (0 = any) */
+    int32_t bk;        /* out: k depth of one LDS stage */
+    int32_t vec;       /* in/out: -1 any, 0 element-wise global loads, 1 16-byte loads */
+    int32_t xcd_remap; /* in/out: -1 auto, 0 off, 1 contiguous tile ranges per XCD */
+    int32_t group_m;   /* in/out: 0 auto; tile rows per raster group */
+    int32_t waves_m, waves_n;   /* out: wave grid of an MFMA workgroup (1 x 1 for LDS) */
+    int32_t thread_m, thread_n; /* out: per-thread micro-tile of the LDS kernel (0 for MFMA) */
+    int32_t threads;   /* out: workgroup size */
+    int32_t lds_bytes; /* out: LDS per workgroup */
+    int32_t grid;      /* out: workgroups launched (tiles_m * tiles_n) */
+    int32_t kernel_id; /* out: index into the library's kernel menu */
+    int64_t tiles_m, tiles_n; /* out */
+    double est_cycles; /* out: the heuristic's cost estimate (clock cycles) */
+} gemm_config;
+
+/*
+ * gemm -- C = A @ B with row-major A (M x K), row-major B (K x N), row-major fp32 C.
+ * Exactly gemm_ex(GEMM_OP_N, GEMM_OP_N, ..., cfg = NULL, stream).
+ */
+int gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+         float* C, int64_t ldc, int dtype, void* stream);
+
+/*
+ * gemm_ex -- as gemm, with BLAS-style operand flags and an optional forced
+ * configuration. opA must be GEMM_OP_N (GEMM_OP_T returns GEMM_ERR_UNSUPPORTED).
+ * opB = GEMM_OP_T reads B column-major (B(k,j) = B[j*ldb + k]). cfg = NULL runs
+ * the heuristic; otherwise its "in" fields restrict the choice (a request no
+ * compiled kernel satisfies returns GEMM_ERR_UNSUPPORTED).
+ */
+int gemm_ex(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+            int64_t ldb, float* C, int64_t ldc, int dtype, const gemm_config* cfg, void* stream);
+
+/*
+ * gemm_plan -- host-only: the configuration gemm_ex would launch for these
+ * arguments, without touching any device. a_addr, b_addr, c_addr are the
+ * operand addresses (only their alignment is used), num_cus the compute-unit
+ * count and arch the device architecture name (e.g. "gfx950"). Applies the same
+ * validation as gemm_ex except pointer checks; fills *out on success.
+ */
+int gemm_plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+              int dtype, uintptr_t a_addr, uintptr_t b_addr, uintptr_t c_addr, int num_cus, const char* arch,
+              const gemm_config* request, gemm_config* out);
+
+/* Number of compiled kernel configurations, and entry i of that menu (GEMM_OK, or
+ * GEMM_ERR_INVALID_VALUE for an index out of range). Host-only. */
+int gemm_menu_size(void);
+int gemm_menu_entry(int index, int* variant, int* dtype, int* opb, gemm_config* out);
+
+/* Compute-unit count and architecture name (NUL-terminated, truncated to len)
+ * of HIP device `device`. Returns GEMM_ERR_DEVICE if it cannot be queried. */
+int gemm_device_info(int device, int* num_cus, char* arch, int len);
+
+/* Static description of a gemm_status value. */
+const char* gemm_status_string(int status);
+
+/* Thread-local description of the last failure on this thread ("" after success). */
+const char* gemm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DENSE_GEMM_06_AMD_GEMM_H */

@@ -1,0 +1,171 @@
+"""CPU tests of the C ABI: the library loads, exports what include/gemm.h declares,
+validates arguments before touching a device, and plans launches as documented.
+
+No kernel is launched here: only host-side entry points (gemm_plan, the menu,
+status strings) and gemm/gemm_ex calls whose arguments are rejected (or are
+empty problems) before any device access.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dense_gemm_06_amd as dg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built():
+    if not os.path.exists(dg.LIB_PATH):
+        from dense_gemm_06_amd import build
+        build.build()
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "gemm.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while")))
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert set(names) == {"gemm", "gemm_ex", "gemm_plan", "gemm_menu_size", "gemm_menu_entry",
+                          "gemm_device_info", "gemm_status_string", "gemm_last_error"}
+    lib = dg.library()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for st in range(6):
+        assert dg.gemm_status_string(st).startswith(["GEMM_OK", "GEMM_ERR_INVALID_VALUE", "GEMM_ERR_NULL_POINTER",
+                                                     "GEMM_ERR_UNSUPPORTED", "GEMM_ERR_DEVICE",
+                                                     "GEMM_ERR_LAUNCH"][st])
+    assert dg.gemm_status_string(99) == "unknown gemm_status"
+
+
+def test_menu_is_complete():
+    menu = dg.gemm_menu()
+    assert len(menu) == dg.library().gemm_menu_size() == 60
+    seen = set()
+    for e in menu:
+        assert e["lds_bytes"] <= 160 * 1024
+        assert e["threads"] in (256, 512)
+        seen.add((e["variant"], e["dtype"], e["opb"], e["vec"], e["bm"], e["bn"]))
+    for variant in (1, 2):
+        for dtype in (0, 1, 2):
+            for opb in (0, 1):
+                for vec in (0, 1):
+                    tiles = {(bm, bn) for (v, d, o, ve, bm, bn) in seen if (v, d, o, ve) == (variant, dtype, opb, vec)}
+                    assert len(tiles) >= 2, (variant, dtype, opb, vec)
+    assert dg.library().gemm_menu_entry(60, None, None, None, None) == dg.GEMM_ERR_INVALID_VALUE
+
+
+def plan(M, N, K, dtype="f32", op_b="N", lda=None, ldb=None, ldc=None, a=0, b=0, c=0, cus=256, arch="gfx950",
+         req=None):
+    lda = lda if lda is not None else max(1, K)
+    ldb = ldb if ldb is not None else (max(1, N) if op_b == "N" else max(1, K))
+    ldc = ldc if ldc is not None else max(1, N)
+    return dg.gemm_plan(0, dg.OP_CODE[op_b], M, N, K, lda, ldb, ldc, dg.DTYPE_CODE[dtype], a, b, c, cus, arch,
+                        req, check=False)
+
+
+def test_plan_benchmark_configs():
+    st, c = plan(4096, 4096, 4096, "f16")
+    assert st == 0 and c.variant == dg.GEMM_VARIANT_MFMA and (c.bm, c.bn) == (256, 256) and c.grid == 256
+    assert c.vec == 1 and c.xcd_remap == 1 and c.threads == 512
+    st, c = plan(4096, 4096, 4096, "f32")
+    assert st == 0 and c.variant == dg.GEMM_VARIANT_MFMA and c.vec == 1
+    # ragged bf16 with column-major B and odd leading dimensions: element-wise loads
+    st, c = plan(3001, 5003, 1037, "bf16", "T", lda=1037, ldb=1037, ldc=5003)
+    assert st == 0 and c.variant == dg.GEMM_VARIANT_MFMA and c.vec == 0
+    assert c.tiles_m == -(-3001 // c.bm) and c.tiles_n == -(-5003 // c.bn)
+
+
+def test_plan_fills_the_machine():
+    """A smaller problem gets smaller tiles so that the grid covers the compute units."""
+    st, c = plan(1024, 1024, 1024, "f32")
+    assert st == 0 and c.grid >= 256
+    st, c = plan(256, 256, 256, "f32")
+    assert st == 0 and (c.bm, c.bn) == (64, 64)
+    # a tall-skinny problem still picks a tile count close to the CU count or more
+    st, c = plan(8192, 64, 4096, "f16")
+    assert st == 0 and c.grid >= 64
+
+
+def test_plan_alignment_rules():
+    # misaligned base pointer or leading dimension -> element-wise loads
+    assert plan(512, 512, 512, "f16", a=2)[1].vec == 0
+    assert plan(512, 512, 512, "f16", lda=516)[1].vec == 0     # 1032 bytes per row
+    assert plan(512, 512, 512, "f16", lda=520)[1].vec == 1     # 1040 bytes = 65 x 16
+    assert plan(512, 512, 512, "f32", ldb=514)[1].vec == 0
+    # forcing 16-byte loads on misaligned data is refused
+    st, _ = plan(512, 512, 512, "f16", a=2, req=dg.request(vec=1))
+    assert st == dg.GEMM_ERR_UNSUPPORTED
+
+
+def test_plan_forced_configurations():
+    st, c = plan(1000, 1000, 1000, "f32", req=dg.request(variant=dg.GEMM_VARIANT_LDS))
+    assert st == 0 and c.variant == dg.GEMM_VARIANT_LDS and c.thread_m in (4, 8)
+    st, c = plan(1000, 1000, 1000, "f16", req=dg.request(variant=dg.GEMM_VARIANT_MFMA, bm=128, bn=128))
+    assert st == 0 and (c.bm, c.bn) == (128, 128)
+    st, c = plan(1000, 1000, 1000, "f16", req=dg.request(bm=96))
+    assert st == dg.GEMM_ERR_UNSUPPORTED and "no compiled kernel" in dg.gemm_last_error()
+    st, c = plan(1000, 1000, 1000, "f16", req=dg.request(xcd_remap=0, group_m=3))
+    assert st == 0 and c.xcd_remap == 0 and c.group_m == 3
+    st, _ = plan(1000, 1000, 1000, "f16", req=dg.request(variant=7))
+    assert st == dg.GEMM_ERR_INVALID_VALUE
+
+
+@pytest.mark.parametrize("args,status,needle", [
+    (dict(M=-1, N=4, K=4), dg.GEMM_ERR_INVALID_VALUE, "negative size"),
+    (dict(M=4, N=4, K=4, lda=3), dg.GEMM_ERR_INVALID_VALUE, "lda"),
+    (dict(M=4, N=4, K=4, ldb=3), dg.GEMM_ERR_INVALID_VALUE, "ldb"),
+    (dict(M=4, N=4, K=8, op_b="T", ldb=7), dg.GEMM_ERR_INVALID_VALUE, "column-major"),
+    (dict(M=4, N=4, K=4, ldc=3), dg.GEMM_ERR_INVALID_VALUE, "ldc"),
+    (dict(M=4, N=4, K=4, arch="gfx942"), dg.GEMM_ERR_DEVICE, "gfx942"),
+    (dict(M=4, N=4, K=4, cus=0), dg.GEMM_ERR_INVALID_VALUE, "compute-unit"),
+    (dict(M=1 << 30, N=4, K=4), dg.GEMM_ERR_UNSUPPORTED, "2^30"),
+    (dict(M=4, N=4, K=4, lda=1 << 23), dg.GEMM_ERR_UNSUPPORTED, "2^23"),
+])
+def test_plan_rejections(args, status, needle):
+    st, _ = plan(**args)
+    assert st == status
+    assert needle in dg.gemm_last_error()
+
+
+def test_plan_bad_enums():
+    lib = dg.library()
+    out = dg.gemm_config()
+    assert lib.gemm_plan(0, 0, 4, 4, 4, 4, 4, 4, 3, 0, 0, 0, 256, b"gfx950", None, ctypes.byref(out)) == 1
+    assert lib.gemm_plan(0, 2, 4, 4, 4, 4, 4, 4, 0, 0, 0, 0, 256, b"gfx950", None, ctypes.byref(out)) == 1
+    assert lib.gemm_plan(1, 0, 4, 4, 4, 4, 4, 4, 0, 0, 0, 0, 256, b"gfx950", None, ctypes.byref(out)) == 3
+    assert "opA" in dg.gemm_last_error()
+    assert lib.gemm_plan(0, 0, 4, 4, 4, 4, 4, 4, 0, 0, 0, 0, 256, None, None, ctypes.byref(out)) == 4
+    assert lib.gemm_plan(0, 0, 4, 4, 4, 4, 4, 4, 0, 0, 0, 0, 256, b"gfx950", None, None) == 2
+
+
+def test_gemm_rejects_before_device_access():
+    """Invalid arguments are refused before any HIP call (works without a GPU)."""
+    f32 = dg.GEMM_F32
+    assert dg.gemm(4, 4, 4, 0x1000, 4, 0x2000, 4, 0, 4, f32, check=False) == dg.GEMM_ERR_NULL_POINTER
+    assert dg.gemm(4, 4, 4, 0, 4, 0x2000, 4, 0x3000, 4, f32, check=False) == dg.GEMM_ERR_NULL_POINTER
+    assert dg.gemm(-4, 4, 4, 0x1000, 4, 0x2000, 4, 0x3000, 4, f32, check=False) == dg.GEMM_ERR_INVALID_VALUE
+    assert dg.gemm(4, 4, 4, 0x1000, 4, 0x2000, 4, 0x3000, 4, 9, check=False) == dg.GEMM_ERR_INVALID_VALUE
+    # C overlapping A (A spans 64 bytes from 0x1000; C starts inside it)
+    assert dg.gemm(4, 4, 4, 0x1000, 4, 0x8000, 4, 0x1020, 4, f32, check=False) == dg.GEMM_ERR_INVALID_VALUE
+    assert "overlaps" in dg.gemm_last_error()
+    # C overlapping column-major B
+    assert dg.gemm_ex(0, 1, 4, 4, 4, 0x1000, 4, 0x8000, 4, 0x8010, 4, f32, check=False) == \
+        dg.GEMM_ERR_INVALID_VALUE
+    assert dg.gemm_ex(1, 0, 4, 4, 4, 0x1000, 4, 0x8000, 4, 0x9000, 4, f32, check=False) == dg.GEMM_ERR_UNSUPPORTED
+    # empty products succeed without a launch; NULL pointers are fine when nothing is touched
+    assert dg.gemm(0, 4, 4, 0, 4, 0, 4, 0, 4, f32, check=False) == dg.GEMM_OK
+    assert dg.gemm(4, 0, 4, 0, 4, 0, 4, 0, 1, f32, check=False) == dg.GEMM_OK
+    assert dg.gemm_last_error() == ""
+    with pytest.raises(dg.GemmError) as ei:
+        dg.gemm(4, 4, 4, 0, 4, 0x2000, 4, 0x3000, 4, f32)
+    assert ei.value.status == dg.GEMM_ERR_NULL_POINTER and "NULL operand" in str(ei.value)

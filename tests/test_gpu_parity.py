@@ -1,0 +1,238 @@
+"""GPU parity: the HIP kernels against the CPU oracle, through the C ABI.
+
+Criterion (every floating-point case): max_ij |C - Cref| / sum_k |A_ik||B_kj|
+<= 1e-5 for fp32 inputs and <= 1e-4 for fp16/bf16 inputs, with Cref and the
+denominator from the oracle in fp64. Integer-valued inputs (every partial sum
+an integer below 2^24, exact in fp32 accumulation in any order) must match the
+oracle bit for bit. Writes outside C[:M, :N] are checked against a sentinel.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import dense_gemm_06_amd as dg
+import gemm_inputs as gi
+import oracle
+from oracle.check import TOL, normalized_error
+
+from gpu_util import SENTINEL, check_untouched, run_ops
+
+pytestmark = pytest.mark.gpu
+
+DT_NAME = {0: "f32", 1: "f16", 2: "bf16"}
+
+
+def _menu():
+    return dg.gemm_menu() if _lib_built() else []
+
+
+def _lib_built():
+    import os
+    return os.path.exists(dg.LIB_PATH)
+
+
+MENU = _menu()
+MENU_IDS = [f"k{e['kernel_id']}-{'lds' if e['variant'] == 1 else 'mfma'}-{DT_NAME[e['dtype']]}-"
+            f"op{'NT'[e['opb']]}-{'v16' if e['vec'] else 'v1'}-{e['bm']}x{e['bn']}" for e in MENU]
+
+
+def forced(e):
+    return dg.request(variant=e["variant"], bm=e["bm"], bn=e["bn"], vec=e["vec"])
+
+
+def ragged_shape(e):
+    """Two full tiles plus a ragged remainder in M and N, three k-tiles plus a tail."""
+    return 2 * e["bm"] + 37, 2 * e["bn"] + 19, 3 * e["bk"] + 13
+
+
+def aligned_ld(n, dtype):
+    q = 4 if dtype == "f32" else 8
+    return -(-n // q) * q
+
+
+def make_case(e, kind, seed):
+    dtype, op_b = DT_NAME[e["dtype"]], "NT"[e["opb"]]
+    M, N, K = ragged_shape(e)
+    if e["vec"]:
+        lda = aligned_ld(K + 1, dtype)
+        ldb = aligned_ld((N if op_b == "N" else K) + 1, dtype)
+    else:
+        lda = K + 3
+        ldb = (N if op_b == "N" else K) + 5
+    if kind == "int":
+        i = np.arange(M)[:, None]
+        k = np.arange(K)[None, :]
+        a = (((7 * i + 3 * k + seed) % 7) - 3).astype(np.float32)
+        kk = np.arange(K)[:, None]
+        j = np.arange(N)[None, :]
+        b = (((5 * kk + 2 * j + 1) % 7) - 3).astype(np.float32)
+        return gi.from_values(a, b, dtype, op_b, lda=lda, ldb=ldb)
+    return gi.make_operands(M, N, K, dtype, "normal", seed=seed, op_b=op_b, lda=lda, ldb=ldb)
+
+
+@pytest.mark.parametrize("e", MENU, ids=MENU_IDS)
+def test_kernel_random_ragged(e):
+    ops = make_case(e, "rand", seed=e["kernel_id"])
+    ldc = ops.N + 3
+    print(f"case kernel {e['kernel_id']} M={ops.M} N={ops.N} K={ops.K} lda={ops.lda} ldb={ops.ldb}", flush=True)
+    C = run_ops(ops, cfg=forced(e), ldc=ldc)
+    check_untouched(C, ops.M, ops.N)
+    Cref, D = oracle.gemm_ref(ops)
+    err = normalized_error(C[:ops.M, :ops.N], Cref, D)
+    assert err <= TOL[ops.dtype], err
+
+
+@pytest.mark.parametrize("e", MENU, ids=MENU_IDS)
+def test_kernel_integer_exact(e):
+    ops = make_case(e, "int", seed=e["kernel_id"] % 5)
+    print(f"case kernel {e['kernel_id']} integer M={ops.M} N={ops.N} K={ops.K}", flush=True)
+    C = run_ops(ops, cfg=forced(e), ldc=ops.N + 1)
+    check_untouched(C, ops.M, ops.N)
+    Cref, _ = oracle.gemm_ref(ops, want_d=False)
+    got = C[:ops.M, :ops.N].astype(np.float64)
+    bad = np.argwhere(got != Cref)
+    assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:5].tolist()}"
+
+
+def sample_rows(M, bm=256, n_random=16, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = set(range(min(8, M))) | set(range(max(0, M - 8), M))
+    for t in range(bm, M, bm):             # rows on both sides of tile boundaries
+        rows |= {t - 1, t}
+    rows |= set(rng.integers(0, M, n_random).tolist())
+    return np.array(sorted(r for r in rows if 0 <= r < M), dtype=np.int64)
+
+
+def checksum_property(C, ops, tol):
+    """All rows: |sum_j C_ij - sum_j Cref_ij| <= tol * sum_j D_ij, via A (B 1) and |A| (|B| 1)."""
+    from test_oracle_pins import logical
+    a, b = logical(ops)
+    ref = a @ (b @ np.ones(ops.N))
+    dsum = np.abs(a) @ (np.abs(b) @ np.ones(ops.N))
+    got = C[:ops.M, :ops.N].astype(np.float64).sum(axis=1)
+    assert np.all(np.abs(got - ref) <= tol * dsum * 1.0001 + 1e-300)
+
+
+@pytest.mark.parametrize("name", list(gi.CONFIGS))
+def test_benchmark_config_heuristic(name):
+    """The five benchmark problems at full size, in the configuration the heuristic picks."""
+    ops = gi.make_config(name)
+    ldc = ops.N
+    print(f"case config {name}", flush=True)
+    C = run_ops(ops, ldc=ldc, extra_rows=1)
+    check_untouched(C, ops.M, ops.N)
+    assert np.all(np.isfinite(C[:ops.M, :ops.N]))
+    full = ops.M * ops.N * ops.K <= 1024 ** 3
+    rows = None if full else sample_rows(ops.M)
+    Cref, D = oracle.gemm_ref(ops, rows=rows)
+    got = C[:ops.M, :ops.N] if rows is None else C[rows, :ops.N]
+    err = normalized_error(got, Cref, D)
+    print(f"{name}: normalized error {err:.3e} over {'all' if rows is None else len(rows)} rows", flush=True)
+    assert err <= TOL[ops.dtype], err
+    if not full:
+        checksum_property(C, ops, TOL[ops.dtype])
+
+
+@pytest.mark.parametrize("name,variant", [("c2_f32_1024", 1), ("c3_f32_4096", 1), ("c4_f16_4096", 1),
+                                          ("c5_bf16_ragged", 1), ("c1_f32_256", 1)])
+def test_benchmark_config_lds_kernel(name, variant):
+    """The LDS-staged SIMT kernel on the benchmark problems (forced)."""
+    ops = gi.make_config(name)
+    C = run_ops(ops, cfg=dg.request(variant=variant), extra_rows=1)
+    check_untouched(C, ops.M, ops.N)
+    rows = sample_rows(ops.M, n_random=8)
+    Cref, D = oracle.gemm_ref(ops, rows=rows)
+    err = normalized_error(C[rows, :ops.N], Cref, D)
+    assert err <= TOL[ops.dtype], err
+
+
+def test_c4_integer_exact_full_size():
+    """4096^3 fp16 with integer entries: every sampled row bit-exact, in the benchmark configuration."""
+    M = N = K = 4096
+    i = np.arange(M)[:, None]
+    k = np.arange(K)[None, :]
+    a = (((7 * i + 3 * k) % 7) - 3).astype(np.float32)
+    b = (((5 * np.arange(K)[:, None] + 2 * np.arange(N)[None, :] + 1) % 7) - 3).astype(np.float32)
+    ops = gi.from_values(a, b, "f16")
+    C = run_ops(ops, extra_rows=0)
+    rows = sample_rows(M, n_random=8)
+    Cref, _ = oracle.gemm_ref(ops, rows=rows, want_d=False)
+    assert np.array_equal(C[rows].astype(np.float64), Cref)
+
+
+# ------------------------------------------------------------------ edge cases
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_k_zero_writes_zeros(dtype):
+    ops = gi.make_operands(70, 90, 0, dtype)
+    C = run_ops(ops, fill=np.float32(np.nan), ldc=93, extra_rows=0)
+    assert np.all(C[:, :90] == 0)
+    assert np.all(np.isnan(C[:, 90:]))
+
+
+@pytest.mark.parametrize("M,N", [(0, 5), (5, 0), (0, 0)])
+def test_empty_output_untouched(M, N):
+    ops = gi.make_operands(M, N, 16, "f32")
+    C = run_ops(ops, ldc=max(N, 1) + 2, extra_rows=3)
+    assert np.all(C == SENTINEL)
+
+
+@pytest.mark.parametrize("dtype,op_b", [("f32", "N"), ("f16", "N"), ("bf16", "T"), ("f16", "T"), ("f32", "T")])
+@pytest.mark.parametrize("shape", [(1, 1, 1), (1, 333, 77), (257, 1, 65), (17, 19, 3), (33, 47, 8195)])
+def test_small_and_degenerate_shapes(dtype, op_b, shape):
+    M, N, K = shape
+    ops = gi.make_operands(M, N, K, dtype, "uniform", seed=M + N + K, op_b=op_b)
+    C = run_ops(ops, ldc=N + 2)
+    check_untouched(C, M, N)
+    Cref, D = oracle.gemm_ref(ops)
+    assert normalized_error(C[:M, :N], Cref, D) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("op_b", ["N", "T"])
+def test_misaligned_bases(dtype, op_b):
+    """Operands starting 1 element past a 16-byte boundary run the element-wise path correctly."""
+    ops = gi.make_operands(300, 200, 150, dtype, "normal", seed=9, op_b=op_b)
+    C = run_ops(ops, a_off=1, b_off=1, c_off=1, ldc=201)
+    check_untouched(C, ops.M, ops.N)
+    Cref, D = oracle.gemm_ref(ops)
+    assert normalized_error(C[:ops.M, :ops.N], Cref, D) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,op_b", [("f32", "N"), ("f16", "N"), ("bf16", "T")])
+def test_identity_and_permutation(dtype, op_b):
+    """A = I gives C = B exactly; A = P gives the rows of B permuted exactly."""
+    rng = np.random.default_rng(3)
+    n, N = 300, 270
+    base = gi.make_operands(n, N, n, dtype, "normal", seed=4, op_b=op_b)
+    from test_oracle_pins import logical
+    _, b = logical(base)
+    for P in (np.eye(n, dtype=np.float32), np.eye(n, dtype=np.float32)[rng.permutation(n)]):
+        ops = gi.Operands(n, N, n, dtype, op_b, n, base.ldb, gi.to_storage(P, dtype).reshape(-1), base.B)
+        C = run_ops(ops)
+        expect = P.astype(np.float64) @ b
+        assert np.array_equal(C[:n, :N].astype(np.float64), expect)
+
+
+def test_repeatable_and_stream():
+    """Two runs give identical bits; a non-default stream works."""
+    import torch
+    ops = gi.make_operands(1000, 1100, 900, "f16", "uniform", seed=1)
+    C1 = run_ops(ops)
+    s = torch.cuda.Stream()
+    C2 = run_ops(ops, stream=s.cuda_stream)
+    assert np.array_equal(C1, C2)
+
+
+def test_overlap_rejected_on_device():
+    import torch
+    t = torch.zeros(4096, dtype=torch.float32, device="cuda")
+    p = t.data_ptr()
+    st = dg.gemm(16, 16, 16, p, 16, p + 4096, 16, p + 512, 16, dg.GEMM_F32, check=False)
+    assert st == dg.GEMM_ERR_INVALID_VALUE
+    assert torch.all(t == 0)
+
+
+def test_device_info():
+    n, arch = dg.gemm_device_info(0)
+    assert arch.startswith("gfx950") and n > 0
