@@ -52,6 +52,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="time only the headline problem")
     p.add_argument("--only", default=None, help="time only this benchmark problem (for profiling)")
+    p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                   help="instead of GEMMs, run 5 plain device copies of MIB MiB (calibrates HBM counters)")
     return p.parse_args()
 
 
@@ -106,10 +108,11 @@ def cpu_baseline(name, target_s):
     import oracle
     ops = gi.make_config(name)
     oracle.build(force=False)
-    r = 4
-    _, t = oracle.timed_gemm_ref(ops, rows=list(range(r)))
-    per_row = max(t / r, 1e-4)
-    r = int(max(4, min(ops.M, target_s / per_row)))
+    # calibrate: the per-call fixed cost (decoding B) cancels in the difference
+    _, t1 = oracle.timed_gemm_ref(ops, rows=list(range(16)))
+    _, t2 = oracle.timed_gemm_ref(ops, rows=list(range(48)))
+    per_row = max((t2 - t1) / 32, 1e-5)
+    r = int(max(16, min(ops.M, target_s / per_row)))
     _, t = oracle.timed_gemm_ref(ops, rows=list(range(r)))
     flops = 2.0 * r * ops.N * ops.K
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(), "kind": "oracle",
@@ -152,6 +155,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if a.copy_probe:
+        n = a.copy_probe * (1 << 20) // 4
+        src = torch.rand(n, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "copies": 5}))
+        return
     import dense_gemm_06_amd as dg
     dg.library()   # fail loudly if the HIP library is missing
 

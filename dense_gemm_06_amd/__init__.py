@@ -75,6 +75,14 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is not built; run `python -m dense_gemm_06_amd.build` "
                            "(there is no fallback implementation)")
+    # Device memory and streams come from torch, so the library must run on the
+    # same HIP runtime instance: load torch's runtime first, which then also
+    # satisfies the library's libamdhip64 dependency. Loading the library first
+    # would bring in a second HIP/HSA runtime and neither would see the device.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
     cfgp = ctypes.POINTER(gemm_config)
