@@ -132,6 +132,17 @@ def _cpu_model():
     return None
 
 
+def kernel_name(cfg, dtype):
+    """The kernel template a configuration launches (as named in the rocprofv3 traces)."""
+    if cfg.variant == 1:
+        base = "lds_gemm"
+    elif dtype == "f32":
+        base = "mfma32_gemm"
+    else:
+        base = {1: "mfma16_gemm", 2: "mfma16_pp", 3: "mfma16_dma"}[cfg.schedule]
+    return f"{base} {cfg.bm}x{cfg.bn}x{cfg.bk} waves {cfg.waves_m}x{cfg.waves_n}"
+
+
 def load_traffic(problem, cfg):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they match this kernel build."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
@@ -179,8 +190,7 @@ def main():
     traffic = load_traffic(headline, cfg)
     roof = {"bound": "mfma", "achieved": main_res["tflops"], "peak": main_res["peak"], "unit": "TFLOP/s",
             "frac": main_res["tflops"] / main_res["peak"], "traffic": traffic,
-            "kernel": f"mfma16_gemm {cfg.bm}x{cfg.bn}x{cfg.bk} waves {cfg.waves_m}x{cfg.waves_n}"
-            if cfg.variant == 2 else f"lds_gemm {cfg.bm}x{cfg.bn}",
+            "kernel": kernel_name(cfg, main_res["dtype"]),
             "flops_per_launch": main_res["flops"], "launch_ms": main_res["ms_per_step"]}
     out = {
         "metric": "GEMM TFLOP/s (2MNK/t) at 4096^3 fp16-in/fp32-acc (value) and fp32 (fp32 field); % of MFMA peak",

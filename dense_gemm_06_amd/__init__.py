@@ -43,7 +43,8 @@ class gemm_config(ctypes.Structure):
         ("waves_m", ctypes.c_int32), ("waves_n", ctypes.c_int32),
         ("thread_m", ctypes.c_int32), ("thread_n", ctypes.c_int32),
         ("threads", ctypes.c_int32), ("lds_bytes", ctypes.c_int32), ("grid", ctypes.c_int32),
-        ("kernel_id", ctypes.c_int32), ("tiles_m", ctypes.c_int64), ("tiles_n", ctypes.c_int64),
+        ("kernel_id", ctypes.c_int32), ("schedule", ctypes.c_int32),
+        ("tiles_m", ctypes.c_int64), ("tiles_n", ctypes.c_int64),
         ("est_cycles", ctypes.c_double),
     ]
 
@@ -52,10 +53,12 @@ class gemm_config(ctypes.Structure):
 
 
 def request(variant: int = GEMM_VARIANT_AUTO, bm: int = 0, bn: int = 0, vec: int = -1,
-            xcd_remap: int = -1, group_m: int = 0) -> gemm_config:
+            xcd_remap: int = -1, group_m: int = 0, waves_m: int = 0, waves_n: int = 0,
+            schedule: int = 0) -> gemm_config:
     """A gemm_config with only the "in" fields set (0 / -1: heuristic decides)."""
     c = gemm_config()
     c.variant, c.bm, c.bn, c.vec, c.xcd_remap, c.group_m = variant, bm, bn, vec, xcd_remap, group_m
+    c.waves_m, c.waves_n, c.schedule = waves_m, waves_n, schedule
     return c
 
 

@@ -36,20 +36,30 @@ namespace dg {
 // ---------------------------------------------------------------------------
 // LDS layouts
 //
+// gfx950 LDS, as measured with bank-conflict counters on this hardware: 64 banks
+// of 4 bytes (a 256-byte period). 8-byte reads, including the transpose reads,
+// are served 32 consecutive lanes at a time. 16-byte reads are served in four
+// phases of 16 lanes built from lane quads: lane l is in phase
+// (l / 32, parity of bits 2..4 of l), e.g. lanes 0-3, 12-15, 20-23, 24-27.
+// A phase is conflict-free when its lanes touch distinct 16-byte positions of
+// the 256-byte bank period (section 13.6's rule, with these banks and phases).
+//
 // K-major tiles (A, and B when it is column-major): row r holds BK consecutive k
-// as 16-byte chunks; chunk c is stored at chunk position c ^ kmaj_swz(r). A
-// wave's fragment read touches 16 consecutive rows at one chunk column; the XOR
-// spreads them over all chunk positions of a 128-byte bank line (section 13.6's
-// swizzle: no padding, composes with 16-byte accesses).
-__device__ __forceinline__ int kmaj_swz(int r) { return (r ^ (r >> 3)) & 7; }
+// as 16-byte chunks (128-byte rows); chunk c is stored at position c ^ (r & 7).
+// A fragment read takes rows r0..r0+15 at chunk columns c0 (lanes 0-15) and
+// c0+1 (lanes 16-31); under the phase grouping above every phase then covers all
+// 16 positions once. No padding, and 16-byte accesses stay aligned.
+__device__ __forceinline__ int kmaj_swz(int r) { return r & 7; }
 
 // N-major tile of a 16-bit row-major B: row k holds BN consecutive n as 16-byte
-// chunks; chunk c is stored at c ^ nmaj_swz(k). The transpose reads of one wave
-// touch rows {32s + 8g + 4h + r : g, r in 0..3}; the swizzle gives each of those
-// 16 rows a distinct XOR so their 32-byte pieces land on distinct banks.
+// chunks; chunk c is stored at c ^ nmaj_swz(k). The transpose reads of one
+// 32-lane phase touch 8 rows {8g + 4h + r : g in 0..1, r in 0..3} at two
+// neighbouring chunks; the eight even XOR values 2((k & 3) | 4((k >> 3) & 1))
+// send the even chunk to the 8 even positions and the odd chunk to the 8 odd
+// ones, so the phase hits all 16 positions once.
 template <int CHUNKS>
 __device__ __forceinline__ int nmaj_swz(int k) {
-    return (((k & 3) << 1) | ((k >> 3) & 1) | (((k >> 4) & 1) << 3)) & (CHUNKS - 1);
+    return (((k & 3) | (((k >> 3) & 1) << 2)) << 1) & (CHUNKS - 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -240,7 +250,9 @@ __global__ __launch_bounds__(256) void lds_gemm(GemmArgs g) {
 // fp16 / bf16 inputs, v_mfma_f32_16x16x32: each lane supplies 8 consecutive k
 // of one row of P and one column of Q (k = 8(l/16) + slot).
 template <int DT, int OPB, bool VEC, int BM, int BN, int BK, int WM, int WN>
-__global__ __launch_bounds__(WM * WN * 64) void mfma16_gemm(GemmArgs g) {
+__global__ __launch_bounds__(WM * WN * 64)
+__attribute__((amdgpu_waves_per_eu(1, (BM / WM) * (BN / WN) >= 128 * 128 ? 1 : 8)))
+void mfma16_gemm(GemmArgs g) {
     constexpr int NT = WM * WN * 64;
     constexpr int TWM = BM / WM, TWN = BN / WN;  // wave tile
     constexpr int SM = TWM / 16, SN = TWN / 16;  // 16 x 16 subtiles per wave
@@ -350,7 +362,12 @@ __global__ __launch_bounds__(WM * WN * 64) void mfma16_gemm(GemmArgs g) {
         if (kt + 1 < nk) load_tiles(kt + 1);
 #pragma unroll
         for (int ks = 0; ks < BK / 32; ++ks) {
-            u32x4 pb[SN];
+            u32x4 qa[SM], pb[SN];
+#pragma unroll
+            for (int i = 0; i < SM; ++i) {
+                const int r = wmi * TWM + i * 16 + l16;
+                qa[i] = *reinterpret_cast<const u32x4*>(&sA[cur][r * BK + (((ks * 4 + lg) ^ kmaj_swz(r)) << 3)]);
+            }
 #pragma unroll
             for (int j = 0; j < SN; ++j) {
                 if (OPB == 0) {
@@ -380,20 +397,16 @@ __global__ __launch_bounds__(WM * WN * 64) void mfma16_gemm(GemmArgs g) {
                 }
             }
 #pragma unroll
-            for (int i = 0; i < SM; ++i) {
-                // the A fragment of subtile row i lives only across its SN instructions
-                const int r = wmi * TWM + i * 16 + l16;
-                const u32x4 qa = *reinterpret_cast<const u32x4*>(&sA[cur][r * BK + (((ks * 4 + lg) ^ kmaj_swz(r)) << 3)]);
+            for (int i = 0; i < SM; ++i)
 #pragma unroll
                 for (int j = 0; j < SN; ++j) {
                     if (DT == DT_F16)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                            __builtin_bit_cast(f16x8, pb[j]), __builtin_bit_cast(f16x8, qa), acc[i][j], 0, 0, 0);
+                            __builtin_bit_cast(f16x8, pb[j]), __builtin_bit_cast(f16x8, qa[i]), acc[i][j], 0, 0, 0);
                     else
                         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8, pb[j]), __builtin_bit_cast(bf16x8, qa), acc[i][j], 0, 0, 0);
+                            __builtin_bit_cast(bf16x8, pb[j]), __builtin_bit_cast(bf16x8, qa[i]), acc[i][j], 0, 0, 0);
                 }
-            }
         }
         if (kt + 1 < nk) store_tiles(cur ^ 1);
         __syncthreads();
@@ -615,6 +628,396 @@ __global__ __launch_bounds__(WM * WN * 64) void mfma32_gemm(GemmArgs g) {
                 }
             }
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Ping-pong MFMA kernel for 16-bit inputs on full 256 x 256 tiles (M and N
+// multiples of 256, K a multiple of 32, 16-byte aligned operands).
+//
+// The register-staged kernel above runs every wave through the same sequence
+// (load, wait, MFMA, store, barrier), so the matrix unit idles whenever all
+// waves wait on memory together. Here the 8 waves form two groups of 4, one
+// wave of each group per SIMD, and the groups run one phase apart: in every
+// phase one group issues a block of 32 MFMAs (16x16x32) from registers while the
+// other reads its fragments of the next k-tile from LDS and starts direct
+// global -> LDS copies (global_load_lds_dwordx4, no registers involved) three
+// k-tiles ahead. One barrier ends each phase.
+//
+// LDS: 4 stages of 32 KB (A: 256 rows x 32 k, B: 32 k x 256 n or 256 n x 32 k).
+// Group 0 computes C rows 0..127 of the tile and copies A; group 1 computes rows
+// 128..255 and copies B; wave w of a group owns columns 64w..64w+63.
+// Tile q lives in stage q mod 4: group 0 reads it in phase 2q, group 1 in phase
+// 2q+1, and its stage is refilled (tile q+4) from phase 2q+2 on. Before each
+// barrier a wave waits for its own LDS reads (so a stage is never overwritten
+// while read) and, before the barrier that precedes phase 2q, for its own copies
+// of tile q (vmcnt counts its copies of tiles q+1 and q+2 still in flight).
+//
+// 64-byte k-major rows: chunk c of row r is stored at c ^ ((r >> 1) & 3), which
+// keeps the 16-byte fragment reads (16 rows x 4 chunks) conflict-free under the
+// gfx950 phase rule above; the row-major B tile uses nmaj_swz like the
+// register-staged kernel.
+__device__ __forceinline__ int kmaj64_swz(int r) { return (r >> 1) & 3; }
+
+// Swizzles for the 32x32x16 fragment reads of mfma16_dma (64-byte k-major rows read
+// 32 rows at a time; 512-byte n-major rows read as 4 rows x 64 bytes per 32-lane
+// transpose phase), conflict-free under the gfx950 rules above.
+__device__ __forceinline__ int kmaj32_swz(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int nmaj32_swz(int k) { return (k & 3) << 2; }
+
+#define DG_GLB(p) ((__attribute__((address_space(1))) void*)(p))
+#define DG_LDSV(p) ((__attribute__((address_space(3))) void*)(p))
+
+template <int DT, int OPB>
+__global__ __launch_bounds__(512) void mfma16_pp(GemmArgs g) {
+    constexpr int BM = 256, BN = 256, BK = 32, S = 4;
+    constexpr int SA = BM * BK, SB = BN * BK;  // halfs per stage
+    __shared__ __attribute__((aligned(1024))) uint16_t sA[S][SA];
+    __shared__ __attribute__((aligned(1024))) uint16_t sB[S][SB];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int grp = wave >> 2, wl = wave & 3;
+    const int l16 = lane & 15, lg = lane >> 4;
+    int tm, tn;
+    tile_coords(g, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int nk = g.K / BK;
+    const uint16_t* __restrict__ A = static_cast<const uint16_t*>(g.A);
+    const uint16_t* __restrict__ B = static_cast<const uint16_t*>(g.B);
+
+    // Direct copies: each wave issues 4 copies of 1 KB (64 lanes x 16 B) per tile.
+    // Lane L of block b lands at LDS byte b*1024 + 16L, i.e. at a fixed swizzled
+    // position; it loads the logical chunk that belongs there.
+    const uint16_t* src[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int b = wl * 4 + i;
+        if (grp == 0 || OPB == 1) {
+            const int row = b * 16 + (lane >> 2);
+            const int c = (lane & 3) ^ kmaj64_swz(row);
+            src[i] = grp == 0 ? A + (size_t)(m0 + row) * g.lda + c * 8 : B + (size_t)(n0 + row) * g.ldb + c * 8;
+        } else {
+            const int row = b * 2 + (lane >> 5);
+            const int c = (lane & 31) ^ nmaj_swz<BN / 8>(row);
+            src[i] = B + (size_t)row * g.ldb + n0 + c * 8;
+        }
+    }
+    const size_t kstep = (grp == 1 && OPB == 0) ? (size_t)BK * g.ldb : (size_t)BK;  // elements per k-tile
+    auto issue = [&](int t) {
+        uint16_t* dst = grp == 0 ? sA[t & 3] : sB[t & 3];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_global_load_lds(DG_GLB(src[i] + (size_t)t * kstep), DG_LDSV(dst + (wl * 4 + i) * 512), 16,
+                                             0, 0);
+    };
+
+    // qa: Q fragments (A rows); pb: P fragments of column-major B; ph: the two
+    // 4-k halves of a row-major-B P fragment, read by transpose reads issued as
+    // inline asm. The compiler cannot tell those reads from the in-flight LDS-DMA
+    // writes and would otherwise wait for every copy (vmcnt(0)) before them; the
+    // asm form leaves the ordering to the explicit waits of sync_phase. Their
+    // results are combined into MFMA operands only after the lgkmcnt(0) wait and
+    // barrier that end the phase.
+    u32x4 qa[8], pb[4];
+    u32x2 ph[4][2];
+    auto load_frags = [&](int t) {
+        const uint16_t* a = sA[t & 3];
+        const uint16_t* bb = sB[t & 3];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = grp * 128 + i * 16 + l16;
+            qa[i] = *reinterpret_cast<const u32x4*>(a + r * BK + ((lg ^ kmaj64_swz(r)) << 3));
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (OPB == 0) {
+                // transpose reads: in each 16-lane group, lane i addresses row kb + i/4 at
+                // columns nb + 4(i%4); lane i then holds column nb + i of rows kb..kb+3.
+                const int col = wl * 64 + j * 16 + ((l16 & 3) << 2);
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int krow = lg * 8 + hh * 4 + (l16 >> 2);
+                    const uint16_t* p = bb + krow * BN + (((col >> 3) ^ nmaj_swz<BN / 8>(krow)) << 3) + (col & 7);
+                    const uint32_t addr = (uint32_t)reinterpret_cast<uintptr_t>(DG_LDSV(p));
+                    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(ph[j][hh]) : "v"(addr));
+                }
+            } else {
+                const int r = wl * 64 + j * 16 + l16;
+                pb[j] = *reinterpret_cast<const u32x4*>(bb + r * BK + ((lg ^ kmaj64_swz(r)) << 3));
+            }
+        }
+    };
+
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto mma = [&]() {
+        if (OPB == 0) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pb[j] = u32x4{ph[j][0][0], ph[j][0][1], ph[j][1][0], ph[j][1][1]};
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (DT == DT_F16)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, pb[j]),
+                                                                      __builtin_bit_cast(f16x8, qa[i]), acc[i][j], 0, 0, 0);
+                else
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pb[j]),
+                                                                       __builtin_bit_cast(bf16x8, qa[i]), acc[i][j], 0, 0, 0);
+            }
+    };
+    // End of a phase: own LDS reads done, then (optionally) own copies of the next
+    // tile done, then the workgroup barrier. The asm statements are compiler
+    // memory barriers; the waits are explicit because LDS-DMA completion is not
+    // tracked by the compiler for later LDS reads.
+    auto sync_phase = [&](int vm_allowed) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (vm_allowed >= 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        else if (vm_allowed >= 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        else if (vm_allowed >= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        asm volatile("s_barrier" ::: "memory");
+    };
+
+    // prologue: tiles 0, 1, 2 in flight; tile 0 complete before the first phase
+    for (int t = 0; t < 3 && t < nk; ++t) issue(t);
+    sync_phase(4 * min(2, nk - 1));
+
+    for (int q = 0; q < nk; ++q) {
+        // phase 2q: group 0 fetches tile q, group 1 multiplies tile q-1
+        if (grp == 0) {
+            load_frags(q);
+            if (q + 3 < nk) issue(q + 3);
+        } else if (q > 0) {
+            mma();
+        }
+        sync_phase(-1);
+        // phase 2q+1: group 0 multiplies tile q, group 1 fetches tile q
+        if (grp == 0) {
+            mma();
+        } else {
+            load_frags(q);
+            if (q + 3 < nk) issue(q + 3);
+        }
+        sync_phase(4 * max(0, min(2, nk - 2 - q)));
+    }
+    if (grp == 1) mma();
+
+    // epilogue: lane owns C[m][n..n+3]
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int m = m0 + grp * 128 + i * 16 + l16;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int n = n0 + wl * 64 + j * 16 + lg * 4;
+            float* cp = g.C + (size_t)m * g.ldc + n;
+            const f32x4 v = acc[i][j];
+            if ((reinterpret_cast<uintptr_t>(cp) & 15) == 0) {
+                *reinterpret_cast<f32x4*>(cp) = v;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) cp[e] = v[e];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Software-pipelined MFMA kernel for 16-bit inputs on full 256 x 256 tiles (M and
+// N multiples of 256, K a multiple of 32, 16-byte aligned operands).
+//
+// All 8 waves (2 x 4, 128 x 64 each, two per SIMD) multiply. The k loop runs in
+// steps of 16 (one v_mfma_f32_32x32x16 per 32 x 32 subtile); the fragments of
+// step s+1 are read from LDS while the 8 MFMAs of step s execute (two register
+// sets). Tiles of k = 32 reach LDS through direct copies issued four tiles ahead
+// into a ring of 4 stages, and one
+// barrier per tile publishes the next tile and retires the stage just read.
+//
+// Tile t sits in stage t mod 4. Its fragments are read in steps 2t-1 (k 0..15)
+// and 2t (k 16..31). The barrier between steps 2t and 2t+1 requires tile t+1 to
+// be complete (each wave waits for its own copies of it; the copies of tiles
+// t+2 and t+3 may still be in flight) and all reads of stage t mod 4 done; right
+// after it, tile t+4 is copied into that stage.
+//
+// Fragment reads are inline asm (the compiler would otherwise wait for every
+// in-flight copy before the transpose reads, see mfma16_pp), so their waits are
+// explicit: before the MFMAs of a step, lgkmcnt(8) retires the previous step's 8
+// reads while this step's 8 stay in flight, and a scheduling barrier keeps the
+// MFMAs below that wait.
+template <int DT, int OPB>
+__global__ __launch_bounds__(512) void mfma16_dma(GemmArgs g) {
+    constexpr int BM = 256, BN = 256, BK = 32, S = 4;
+    constexpr int SA = BM * BK, SB = BN * BK;  // halfs per stage
+    __shared__ __attribute__((aligned(1024))) uint16_t sA[S][SA];
+    __shared__ __attribute__((aligned(1024))) uint16_t sB[S][SB];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 2, wn = wave & 3;  // wave tile rows wm*128.., columns wn*64..
+    const int l32 = lane & 31, lh = lane >> 5;
+    int tm, tn;
+    tile_coords(g, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int nk = g.K / BK;
+    const uint16_t* __restrict__ A = static_cast<const uint16_t*>(g.A);
+    const uint16_t* __restrict__ B = static_cast<const uint16_t*>(g.B);
+
+    // copies: waves 0-3 copy the A tile, waves 4-7 the B tile, 4 blocks of 1 KB each
+    const uint16_t* src[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int b = wn * 4 + i;
+        if (wm == 0 || OPB == 1) {
+            const int row = b * 16 + (lane >> 2);
+            const int c = (lane & 3) ^ kmaj32_swz(row);
+            src[i] = wm == 0 ? A + (size_t)(m0 + row) * g.lda + c * 8 : B + (size_t)(n0 + row) * g.ldb + c * 8;
+        } else {
+            const int row = b * 2 + (lane >> 5);
+            const int c = (lane & 31) ^ nmaj32_swz(row);
+            src[i] = B + (size_t)row * g.ldb + n0 + c * 8;
+        }
+    }
+    const size_t kstep = (wm == 1 && OPB == 0) ? (size_t)BK * g.ldb : (size_t)BK;
+    auto issue = [&](int t) {
+        uint16_t* dst = wm == 0 ? sA[t & 3] : sB[t & 3];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_global_load_lds(DG_GLB(src[i] + (size_t)t * kstep), DG_LDSV(dst + (wn * 4 + i) * 512), 16,
+                                             0, 0);
+    };
+
+    // LDS byte addresses of this lane's fragment reads within a stage, for k16 step 0;
+    // step 1 and the stage offset are added at use.
+    uint32_t qaddr[2][4], paddr[2][2][2];
+    const uint32_t baseA = (uint32_t)reinterpret_cast<uintptr_t>(DG_LDSV(&sA[0][0]));
+    const uint32_t baseB = (uint32_t)reinterpret_cast<uintptr_t>(DG_LDSV(&sB[0][0]));
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = wm * 128 + i * 32 + l32;
+            qaddr[ks][i] = baseA + 2 * (r * BK + (((ks * 2 + lh) ^ kmaj32_swz(r)) << 3));
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            if (OPB == 0) {
+                const int gp = lane >> 4, i16 = lane & 15;
+                const int col = wn * 64 + j * 32 + (gp & 1) * 16 + ((i16 & 3) << 2);
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int krow = ks * 16 + (gp >> 1) * 8 + hh * 4 + (i16 >> 2);
+                    paddr[ks][j][hh] = baseB + 2 * (krow * BN + (((col >> 3) ^ nmaj32_swz(krow)) << 3) + (col & 7));
+                }
+            } else {
+                const int r = wn * 64 + j * 32 + l32;
+                paddr[ks][j][0] = baseB + 2 * (r * BK + (((ks * 2 + lh) ^ kmaj32_swz(r)) << 3));
+                paddr[ks][j][1] = 0;
+            }
+        }
+    }
+
+    // register set f: Q fragments; P fragments of column-major B (pb) or the two
+    // 4-k halves of a row-major-B P fragment (ph), combined only after the wait.
+    u32x4 qa[2][4], pb[2][2];
+    u32x2 ph[2][2][2];
+    auto load_frags = [&](int f, int t, int ks) {
+        const uint32_t so = (uint32_t)(t & 3) * (SA * 2);  // stage offset in bytes (SA == SB)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            asm volatile("ds_read_b128 %0, %1" : "=v"(qa[f][i]) : "v"(qaddr[ks][i] + so));
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            if (OPB == 0) {
+                asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(ph[f][j][0]) : "v"(paddr[ks][j][0] + so));
+                asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(ph[f][j][1]) : "v"(paddr[ks][j][1] + so));
+            } else {
+                asm volatile("ds_read_b128 %0, %1" : "=v"(pb[f][j]) : "v"(paddr[ks][j][0] + so));
+            }
+        }
+    };
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    // Wait until at most `newer` LDS reads are outstanding, then multiply set f.
+    auto mma = [&](int f, int newer) {
+        if (newer >= 8) asm volatile("s_waitcnt lgkmcnt(8)" ::: "memory");
+        else if (newer >= 6) asm volatile("s_waitcnt lgkmcnt(6)" ::: "memory");
+        else asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        if (OPB == 0) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                pb[f][j] = u32x4{ph[f][j][0][0], ph[f][j][0][1], ph[f][j][1][0], ph[f][j][1][1]};
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                if (DT == DT_F16)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, pb[f][j]),
+                                                                      __builtin_bit_cast(f16x8, qa[f][i]), acc[i][j],
+                                                                      0, 0, 0);
+                else
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, pb[f][j]),
+                                                                       __builtin_bit_cast(bf16x8, qa[f][i]), acc[i][j],
+                                                                       0, 0, 0);
+            }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    constexpr int READS = OPB == 0 ? 8 : 6;  // LDS reads per step
+    auto tile_barrier = [&](int vm_allowed) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (vm_allowed >= 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+        else if (vm_allowed >= 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        else if (vm_allowed >= 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        asm volatile("s_barrier" ::: "memory");
+    };
+
+    // prologue: tiles 0..3 in flight, tile 0 published, first fragments requested
+    for (int t = 0; t < S && t < nk; ++t) issue(t);
+    tile_barrier(4 * (min(S, nk) - 1));
+    load_frags(0, 0, 0);
+
+    for (int t = 0; t < nk - 1; ++t) {
+        // step 2t: k 16..31 of tile t requested, k 0..15 multiplied
+        load_frags(1, t, 1);
+        mma(0, READS);
+        // publish tile t+1, retire stage t mod 4
+        tile_barrier(4 * max(0, min(2, nk - 2 - t)));
+        if (t + S < nk) issue(t + S);
+        // step 2t+1: k 0..15 of tile t+1 requested, k 16..31 of tile t multiplied
+        load_frags(0, t + 1, 0);
+        mma(1, READS);
+    }
+    // last tile: no further copies or barriers
+    load_frags(1, nk - 1, 1);
+    mma(0, READS);
+    mma(1, 0);
+
+    // epilogue: lane owns C[m][n..n+3] for four n runs per subtile
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = m0 + wm * 128 + i * 32 + l32;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const int n = n0 + wn * 64 + j * 32 + rg * 8 + lh * 4;
+                float* cp = g.C + (size_t)m * g.ldc + n;
+                const f32x4 v = {acc[i][j][4 * rg], acc[i][j][4 * rg + 1], acc[i][j][4 * rg + 2], acc[i][j][4 * rg + 3]};
+                if ((reinterpret_cast<uintptr_t>(cp) & 15) == 0) {
+                    *reinterpret_cast<f32x4*>(cp) = v;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) cp[e] = v[e];
+                }
+            }
     }
 }
 

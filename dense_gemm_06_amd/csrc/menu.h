@@ -18,39 +18,61 @@ enum Dtype { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
 //   vec     : 1 = 16-byte global loads (needs aligned bases and leading dims),
 //             0 = element-wise loads (any alignment)
 //   bm, bn, bk : block tile; wm x wn : wave grid (MFMA); tm x tn : thread tile (LDS)
+//   sched   : 1 = register-staged double buffer (any shape), 2 = ping-pong with
+//             direct global->LDS copies, 3 = software-pipelined with direct
+//             copies (2 and 3: full tiles only -- M, N multiples of bm, bn, K a
+//             multiple of bk, 16-byte aligned operands)
 struct MenuEntry {
-    int id, variant, dtype, opb, vec, bm, bn, bk, wm, wn, tm, tn, threads, lds_bytes;
+    int id, variant, dtype, opb, vec, bm, bn, bk, wm, wn, tm, tn, threads, lds_bytes, sched;
 };
 
-// X(id, variant, dtype, opb, vec, bm, bn, bk, wm, wn, tm, tn, threads, lds_bytes)
+// X(id, variant, dtype, opb, vec, bm, bn, bk, wm, wn, tm, tn, threads, lds_bytes, sched)
 // The largest MFMA tile is 256 x 256 (2 x 4 waves) for 16-bit inputs and 256 x 128
 // (4 x 2 waves) for fp32; the fp32 kernel's 64 x 64 tile uses a 4 x 1 wave grid
 // (its row-major-B path needs 64-wide wave tiles).
 // LDS bytes: LDS variant holds two fp32 stages of A^T (bk x bm) and B (bk x bn);
 // MFMA variant holds two stages of the input-typed A (bm x bk) and B (bk x bn).
 #define DG_LDS_ENTRIES(X, base, dt, bk)                                                  \
-    X(base + 0, V_LDS, dt, 0, 1, 128, 128, bk, 1, 1, 8, 8, 256, 2 * 4 * bk * 256)          \
-    X(base + 1, V_LDS, dt, 1, 1, 128, 128, bk, 1, 1, 8, 8, 256, 2 * 4 * bk * 256)          \
-    X(base + 2, V_LDS, dt, 0, 0, 128, 128, bk, 1, 1, 8, 8, 256, 2 * 4 * bk * 256)          \
-    X(base + 3, V_LDS, dt, 1, 0, 128, 128, bk, 1, 1, 8, 8, 256, 2 * 4 * bk * 256)          \
-    X(base + 4, V_LDS, dt, 0, 1, 64, 64, bk, 1, 1, 4, 4, 256, 2 * 4 * bk * 128)            \
-    X(base + 5, V_LDS, dt, 1, 1, 64, 64, bk, 1, 1, 4, 4, 256, 2 * 4 * bk * 128)            \
-    X(base + 6, V_LDS, dt, 0, 0, 64, 64, bk, 1, 1, 4, 4, 256, 2 * 4 * bk * 128)            \
-    X(base + 7, V_LDS, dt, 1, 0, 64, 64, bk, 1, 1, 4, 4, 256, 2 * 4 * bk * 128)
+    X(base + 0, V_LDS, dt, 0, 1, 128, 128, bk, 1, 1, 8, 8, 256, 2 * 4 * bk * 256, 1)          \
+    X(base + 1, V_LDS, dt, 1, 1, 128, 128, bk, 1, 1, 8, 8, 256, 2 * 4 * bk * 256, 1)          \
+    X(base + 2, V_LDS, dt, 0, 0, 128, 128, bk, 1, 1, 8, 8, 256, 2 * 4 * bk * 256, 1)          \
+    X(base + 3, V_LDS, dt, 1, 0, 128, 128, bk, 1, 1, 8, 8, 256, 2 * 4 * bk * 256, 1)          \
+    X(base + 4, V_LDS, dt, 0, 1, 64, 64, bk, 1, 1, 4, 4, 256, 2 * 4 * bk * 128, 1)            \
+    X(base + 5, V_LDS, dt, 1, 1, 64, 64, bk, 1, 1, 4, 4, 256, 2 * 4 * bk * 128, 1)            \
+    X(base + 6, V_LDS, dt, 0, 0, 64, 64, bk, 1, 1, 4, 4, 256, 2 * 4 * bk * 128, 1)            \
+    X(base + 7, V_LDS, dt, 1, 0, 64, 64, bk, 1, 1, 4, 4, 256, 2 * 4 * bk * 128, 1)
 
 #define DG_MFMA_ENTRIES(X, base, dt, es, bk, BBM, BBN, BWM, BWN, w64m, w64n)                            \
-    X(base + 0, V_MFMA, dt, 0, 1, BBM, BBN, bk, BWM, BWN, 0, 0, 512, 2 * es * bk * (BBM + BBN)) \
-    X(base + 1, V_MFMA, dt, 1, 1, BBM, BBN, bk, BWM, BWN, 0, 0, 512, 2 * es * bk * (BBM + BBN)) \
-    X(base + 2, V_MFMA, dt, 0, 0, BBM, BBN, bk, BWM, BWN, 0, 0, 512, 2 * es * bk * (BBM + BBN)) \
-    X(base + 3, V_MFMA, dt, 1, 0, BBM, BBN, bk, BWM, BWN, 0, 0, 512, 2 * es * bk * (BBM + BBN)) \
-    X(base + 4, V_MFMA, dt, 0, 1, 128, 128, bk, 2, 2, 0, 0, 256, 2 * es * bk * 256)        \
-    X(base + 5, V_MFMA, dt, 1, 1, 128, 128, bk, 2, 2, 0, 0, 256, 2 * es * bk * 256)        \
-    X(base + 6, V_MFMA, dt, 0, 0, 128, 128, bk, 2, 2, 0, 0, 256, 2 * es * bk * 256)        \
-    X(base + 7, V_MFMA, dt, 1, 0, 128, 128, bk, 2, 2, 0, 0, 256, 2 * es * bk * 256)        \
-    X(base + 8, V_MFMA, dt, 0, 1, 64, 64, bk, w64m, w64n, 0, 0, 256, 2 * es * bk * 128)    \
-    X(base + 9, V_MFMA, dt, 1, 1, 64, 64, bk, w64m, w64n, 0, 0, 256, 2 * es * bk * 128)    \
-    X(base + 10, V_MFMA, dt, 0, 0, 64, 64, bk, w64m, w64n, 0, 0, 256, 2 * es * bk * 128)   \
-    X(base + 11, V_MFMA, dt, 1, 0, 64, 64, bk, w64m, w64n, 0, 0, 256, 2 * es * bk * 128)
+    X(base + 0, V_MFMA, dt, 0, 1, BBM, BBN, bk, BWM, BWN, 0, 0, 512, 2 * es * bk * (BBM + BBN), 1) \
+    X(base + 1, V_MFMA, dt, 1, 1, BBM, BBN, bk, BWM, BWN, 0, 0, 512, 2 * es * bk * (BBM + BBN), 1) \
+    X(base + 2, V_MFMA, dt, 0, 0, BBM, BBN, bk, BWM, BWN, 0, 0, 512, 2 * es * bk * (BBM + BBN), 1) \
+    X(base + 3, V_MFMA, dt, 1, 0, BBM, BBN, bk, BWM, BWN, 0, 0, 512, 2 * es * bk * (BBM + BBN), 1) \
+    X(base + 4, V_MFMA, dt, 0, 1, 128, 128, bk, 2, 2, 0, 0, 256, 2 * es * bk * 256, 1)        \
+    X(base + 5, V_MFMA, dt, 1, 1, 128, 128, bk, 2, 2, 0, 0, 256, 2 * es * bk * 256, 1)        \
+    X(base + 6, V_MFMA, dt, 0, 0, 128, 128, bk, 2, 2, 0, 0, 256, 2 * es * bk * 256, 1)        \
+    X(base + 7, V_MFMA, dt, 1, 0, 128, 128, bk, 2, 2, 0, 0, 256, 2 * es * bk * 256, 1)        \
+    X(base + 8, V_MFMA, dt, 0, 1, 64, 64, bk, w64m, w64n, 0, 0, 256, 2 * es * bk * 128, 1)    \
+    X(base + 9, V_MFMA, dt, 1, 1, 64, 64, bk, w64m, w64n, 0, 0, 256, 2 * es * bk * 128, 1)    \
+    X(base + 10, V_MFMA, dt, 0, 0, 64, 64, bk, w64m, w64n, 0, 0, 256, 2 * es * bk * 128, 1)   \
+    X(base + 11, V_MFMA, dt, 1, 0, 64, 64, bk, w64m, w64n, 0, 0, 256, 2 * es * bk * 128, 1)
+
+// 16-bit 256 x 256 tiles with 4 waves of 128 x 128 (one wave per SIMD, accumulators in
+// the accumulation registers): half the LDS reads per FLOP of the 8-wave layout.
+#define DG_MFMA_WIDE(X, base, dt)                                                        \
+    X(base + 0, V_MFMA, dt, 0, 1, 256, 256, 64, 2, 2, 0, 0, 256, 2 * 2 * 64 * 512, 1)         \
+    X(base + 1, V_MFMA, dt, 1, 1, 256, 256, 64, 2, 2, 0, 0, 256, 2 * 2 * 64 * 512, 1)         \
+    X(base + 2, V_MFMA, dt, 0, 0, 256, 256, 64, 2, 2, 0, 0, 256, 2 * 2 * 64 * 512, 1)         \
+    X(base + 3, V_MFMA, dt, 1, 0, 256, 256, 64, 2, 2, 0, 0, 256, 2 * 2 * 64 * 512, 1)
+
+// Ping-pong kernels (16-bit inputs, full 256 x 256 tiles, 4 LDS stages of k = 32).
+#define DG_MFMA_PP(X, base, dt)                                                          \
+    X(base + 0, V_MFMA, dt, 0, 1, 256, 256, 32, 2, 4, 0, 0, 512, 4 * 2 * 32 * 512, 2)      \
+    X(base + 1, V_MFMA, dt, 1, 1, 256, 256, 32, 2, 4, 0, 0, 512, 4 * 2 * 32 * 512, 2)
+
+// Software-pipelined kernels with direct LDS copies (16-bit inputs, full tiles).
+#define DG_MFMA_DMA(X, base, dt)                                                         \
+    X(base + 0, V_MFMA, dt, 0, 1, 256, 256, 32, 2, 4, 0, 0, 512, 4 * 2 * 32 * 512, 3)      \
+    X(base + 1, V_MFMA, dt, 1, 1, 256, 256, 32, 2, 4, 0, 0, 512, 4 * 2 * 32 * 512, 3)
 
 #define DG_MENU(X)                                              \
     DG_LDS_ENTRIES(X, 0, DT_F32, 16)            \
@@ -58,9 +80,15 @@ struct MenuEntry {
     DG_LDS_ENTRIES(X, 16, DT_BF16, 32)          \
     DG_MFMA_ENTRIES(X, 24, DT_F32, 4, 32, 256, 128, 4, 2, 4, 1) \
     DG_MFMA_ENTRIES(X, 36, DT_F16, 2, 64, 256, 256, 2, 4, 2, 2) \
-    DG_MFMA_ENTRIES(X, 48, DT_BF16, 2, 64, 256, 256, 2, 4, 2, 2)
+    DG_MFMA_ENTRIES(X, 48, DT_BF16, 2, 64, 256, 256, 2, 4, 2, 2) \
+    DG_MFMA_WIDE(X, 60, DT_F16)                                  \
+    DG_MFMA_WIDE(X, 64, DT_BF16)                                 \
+    DG_MFMA_PP(X, 68, DT_F16)                                    \
+    DG_MFMA_PP(X, 70, DT_BF16)                                   \
+    DG_MFMA_DMA(X, 72, DT_F16)                                   \
+    DG_MFMA_DMA(X, 74, DT_BF16)
 
-constexpr int kMenuSize = 60;
+constexpr int kMenuSize = 76;
 
 // Arguments every kernel receives (by value).
 struct GemmArgs {

@@ -80,12 +80,16 @@ typedef struct gemm_config {
     int32_t vec;       /* in/out: -1 any, 0 element-wise global loads, 1 16-byte loads */
     int32_t xcd_remap; /* in/out: -1 auto, 0 off, 1 contiguous tile ranges per XCD */
     int32_t group_m;   /* in/out: 0 auto; tile rows per raster group */
-    int32_t waves_m, waves_n;   /* out: wave grid of an MFMA workgroup (1 x 1 for LDS) */
+    int32_t waves_m, waves_n;   /* in/out: wave grid of an MFMA workgroup (1 x 1 for LDS); 0 = any */
     int32_t thread_m, thread_n; /* out: per-thread micro-tile of the LDS kernel (0 for MFMA) */
     int32_t threads;   /* out: workgroup size */
     int32_t lds_bytes; /* out: LDS per workgroup */
     int32_t grid;      /* out: workgroups launched (tiles_m * tiles_n) */
     int32_t kernel_id; /* out: index into the library's kernel menu */
+    int32_t schedule;  /* in/out: 0 any; 1 register-staged double buffer (any shape); 2 ping-pong
+                          with direct global->LDS copies; 3 software-pipelined with direct
+                          global->LDS copies (2 and 3: MFMA, 16-bit inputs, M and N multiples
+                          of 256, K a multiple of 32, 16-byte aligned operands) */
     int64_t tiles_m, tiles_n; /* out */
     double est_cycles; /* out: the heuristic's cost estimate (clock cycles) */
 } gemm_config;

@@ -49,19 +49,21 @@ def test_status_strings():
 
 def test_menu_is_complete():
     menu = dg.gemm_menu()
-    assert len(menu) == dg.library().gemm_menu_size() == 60
+    assert len(menu) == dg.library().gemm_menu_size() == 76
     seen = set()
     for e in menu:
         assert e["lds_bytes"] <= 160 * 1024
         assert e["threads"] in (256, 512)
         seen.add((e["variant"], e["dtype"], e["opb"], e["vec"], e["bm"], e["bn"]))
+        if e["variant"] == dg.GEMM_VARIANT_MFMA:
+            assert e["waves_m"] * e["waves_n"] * 64 == e["threads"]
     for variant in (1, 2):
         for dtype in (0, 1, 2):
             for opb in (0, 1):
                 for vec in (0, 1):
                     tiles = {(bm, bn) for (v, d, o, ve, bm, bn) in seen if (v, d, o, ve) == (variant, dtype, opb, vec)}
                     assert len(tiles) >= 2, (variant, dtype, opb, vec)
-    assert dg.library().gemm_menu_entry(60, None, None, None, None) == dg.GEMM_ERR_INVALID_VALUE
+    assert dg.library().gemm_menu_entry(76, None, None, None, None) == dg.GEMM_ERR_INVALID_VALUE
 
 
 def plan(M, N, K, dtype="f32", op_b="N", lda=None, ldb=None, ldc=None, a=0, b=0, c=0, cus=256, arch="gfx950",
@@ -76,13 +78,25 @@ def plan(M, N, K, dtype="f32", op_b="N", lda=None, ldb=None, ldc=None, a=0, b=0,
 def test_plan_benchmark_configs():
     st, c = plan(4096, 4096, 4096, "f16")
     assert st == 0 and c.variant == dg.GEMM_VARIANT_MFMA and (c.bm, c.bn) == (256, 256) and c.grid == 256
-    assert c.vec == 1 and c.xcd_remap == 1 and c.threads == 512
+    assert c.vec == 1 and c.threads == 512 and c.schedule >= 2
     st, c = plan(4096, 4096, 4096, "f32")
     assert st == 0 and c.variant == dg.GEMM_VARIANT_MFMA and c.vec == 1
     # ragged bf16 with column-major B and odd leading dimensions: element-wise loads
     st, c = plan(3001, 5003, 1037, "bf16", "T", lda=1037, ldb=1037, ldc=5003)
-    assert st == 0 and c.variant == dg.GEMM_VARIANT_MFMA and c.vec == 0
+    assert st == 0 and c.variant == dg.GEMM_VARIANT_MFMA and c.vec == 0 and c.schedule == 1
     assert c.tiles_m == -(-3001 // c.bm) and c.tiles_n == -(-5003 // c.bn)
+
+
+def test_plan_ping_pong_eligibility():
+    """Whole tiles, K a multiple of 32 and aligned operands, or no ping-pong."""
+    assert plan(4096, 4096, 4096, "bf16")[1].schedule >= 2
+    assert plan(4096, 4096, 4096, "f16", "T")[1].schedule >= 2
+    assert plan(4096, 4096, 4096 + 16, "f16")[1].schedule == 1
+    assert plan(4096 + 8, 4096, 4096, "f16")[1].schedule == 1
+    assert plan(4096, 4096, 4096, "f16", a=2)[1].schedule == 1
+    assert plan(4096, 4096, 4096, "f32")[1].schedule == 1
+    st, _ = plan(4000, 4096, 4096, "f16", req=dg.request(schedule=2))
+    assert st == dg.GEMM_ERR_UNSUPPORTED
 
 
 def test_plan_fills_the_machine():

@@ -34,15 +34,23 @@ def _lib_built():
 
 MENU = _menu()
 MENU_IDS = [f"k{e['kernel_id']}-{'lds' if e['variant'] == 1 else 'mfma'}-{DT_NAME[e['dtype']]}-"
-            f"op{'NT'[e['opb']]}-{'v16' if e['vec'] else 'v1'}-{e['bm']}x{e['bn']}" for e in MENU]
+            f"op{'NT'[e['opb']]}-{'v16' if e['vec'] else 'v1'}-{e['bm']}x{e['bn']}-w{e['waves_m']}x{e['waves_n']}"
+            f"{ {1: '', 2: '-pp', 3: '-dma'}[e['schedule']] }"
+            for e in MENU]
 
 
 def forced(e):
-    return dg.request(variant=e["variant"], bm=e["bm"], bn=e["bn"], vec=e["vec"])
+    return dg.request(variant=e["variant"], bm=e["bm"], bn=e["bn"], vec=e["vec"], waves_m=e["waves_m"],
+                      waves_n=e["waves_n"], schedule=e["schedule"])
 
 
 def ragged_shape(e):
-    """Two full tiles plus a ragged remainder in M and N, three k-tiles plus a tail."""
+    """Two full tiles plus a ragged remainder in M and N, three k-tiles plus a tail.
+
+    Ping-pong kernels take only whole tiles: 2 x 3 tiles and 9 k-tiles (an odd
+    count, so both LDS-stage parities and the prefetch tail are exercised)."""
+    if e["schedule"] >= 2:
+        return 2 * e["bm"], 3 * e["bn"], 9 * e["bk"]
     return 2 * e["bm"] + 37, 2 * e["bn"] + 19, 3 * e["bk"] + 13
 
 
@@ -81,6 +89,18 @@ def test_kernel_random_ragged(e):
     Cref, D = oracle.gemm_ref(ops)
     err = normalized_error(C[:ops.M, :ops.N], Cref, D)
     assert err <= TOL[ops.dtype], err
+
+
+@pytest.mark.parametrize("schedule", [2, 3])
+@pytest.mark.parametrize("k_tiles", [1, 2, 3, 4, 5, 6, 130])
+@pytest.mark.parametrize("dtype,op_b", [("f16", "N"), ("bf16", "N"), ("f16", "T"), ("bf16", "T")])
+def test_full_tile_kernels_k_tile_counts(schedule, k_tiles, dtype, op_b):
+    """Prologue and tail of the direct-copy kernels for every small k-tile count, and a long K."""
+    ops = gi.make_operands(256, 512, 32 * k_tiles, dtype, "normal", seed=k_tiles, op_b=op_b)
+    C = run_ops(ops, cfg=dg.request(schedule=schedule), ldc=ops.N + 4)
+    check_untouched(C, ops.M, ops.N)
+    Cref, D = oracle.gemm_ref(ops)
+    assert normalized_error(C[:ops.M, :ops.N], Cref, D) <= TOL[dtype]
 
 
 @pytest.mark.parametrize("e", MENU, ids=MENU_IDS)

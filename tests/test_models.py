@@ -53,3 +53,57 @@ def test_bank_model_reproduces_13_6():
     got["column walk T=32 load s[tx*32+k]"] = lds_model.passes(lambda t: tid(t)[1] * 32 + k)
     got["column walk T=32 load s[tx*33+k] (padded row)"] = lds_model.passes(lambda t: tid(t)[1] * 33 + k)
     assert got == gold
+
+
+# ---- the kernels' LDS layouts under the measured gfx950 bank rules ----------------
+def _kmaj(r):            # chunk swizzle of k-major tiles (A, column-major B)
+    return r & 7
+
+
+def _nmaj(k, chunks=32):  # chunk swizzle of a 16-bit row-major B tile
+    return (((k & 3) | (((k >> 3) & 1) << 2)) << 1) & (chunks - 1)
+
+
+def test_gfx950_model_reproduces_probe_signatures():
+    """The measured signatures: contiguous 16-byte reads are conflict-free, 8-lane
+    groups at a 256-byte stride conflict 2-way, 32-lane 8-byte groups are served together."""
+    P = lds_model.gfx950_passes
+    assert P(lambda l: l * 16, 16) == 1
+    assert P(lambda l: (l % 16) * 16 + (l // 16) * 512, 16) == 1
+    assert P(lambda l: (l % 8) * 16 + (l // 8) * 256, 16) == 2
+    assert P(lambda l: (l % 4) * 16 + (l // 4) * 128, 16) == 2
+    assert P(lambda l: l * 8, 8) == 1
+    assert P(lambda l: (l % 16) * 8 + (l // 16) * 256, 8) == 2
+    assert P(lambda l: (l % 32) * 8 + (l // 32) * 512, 8) == 1
+    # the first A-fragment swizzle, (r ^ (r >> 3)) & 7, measured 2-way
+    old = lambda l: (l & 15) * 128 + (((l >> 4) ^ (((l & 15) ^ ((l & 15) >> 3)) & 7)) << 4)
+    assert P(old, 16) == 2
+
+
+@pytest.mark.parametrize("ks", [0, 1])
+def test_a_fragment_reads_conflict_free(ks):
+    """16 rows x 2 chunk columns per 16-byte read, rows of 128 bytes (BK = 64 halfs or 32 floats)."""
+    for r0 in (0, 16, 112):
+        addr = lambda l: (r0 + (l & 15)) * 128 + ((((ks * 4 + (l >> 4)) ^ _kmaj(r0 + (l & 15)))) << 4)
+        assert lds_model.gfx950_passes(addr, 16) == 1
+
+
+@pytest.mark.parametrize("bn", [128, 256])
+def test_transpose_reads_conflict_free(bn):
+    chunks = bn // 8
+    for j in range(bn // 16 if bn < 256 else 4):
+        for hh in (0, 1):
+            for ks in (0, 1):
+                def addr(l):
+                    l16, lg = l & 15, l >> 4
+                    col = j * 16 + ((l16 & 3) << 2)
+                    k = ks * 32 + lg * 8 + hh * 4 + (l16 >> 2)
+                    return k * bn * 2 + (((col >> 3) ^ _nmaj(k, chunks)) << 4) + (col & 7) * 2
+                assert lds_model.gfx950_passes(addr, 8) == 1
+
+
+def test_fp32_row_major_b_reads_conflict_free():
+    """fp32 MFMA kernel: lane reads a float4 along n of row kk + 4*(l//16) + s."""
+    for s_ in range(4):
+        addr = lambda l: (4 * (l >> 4) + s_) * 256 * 4 + 4 * (l & 15) * 4
+        assert lds_model.gfx950_passes(addr, 16) == 1
