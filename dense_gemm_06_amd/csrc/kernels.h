@@ -29,6 +29,8 @@
 // and leading dimensions that are multiples of 16 bytes; the host checks) and
 // otherwise element-wise loads.
 #pragma once
+#include <type_traits>
+
 #include "device_common.h"
 
 namespace dg {
@@ -833,26 +835,28 @@ __global__ __launch_bounds__(512) void mfma16_pp(GemmArgs g) {
 // steps of 16 (one v_mfma_f32_32x32x16 per 32 x 32 subtile); the fragments of
 // step s+1 are read from LDS while the 8 MFMAs of step s execute (two register
 // sets). Tiles of k = 32 reach LDS through direct copies issued four tiles ahead
-// into a ring of 4 stages, and one
-// barrier per tile publishes the next tile and retires the stage just read.
+// into a ring of 4 stages, and one barrier per tile publishes the next tile and
+// retires the stage just read.
 //
 // Tile t sits in stage t mod 4. Its fragments are read in steps 2t-1 (k 0..15)
 // and 2t (k 16..31). The barrier between steps 2t and 2t+1 requires tile t+1 to
-// be complete (each wave waits for its own copies of it; the copies of tiles
-// t+2 and t+3 may still be in flight) and all reads of stage t mod 4 done; right
-// after it, tile t+4 is copied into that stage.
+// be complete (each wave waits for its own copies of it; copies of tiles t+2 and
+// t+3 may still be in flight) and all reads of stage t mod 4 done; right after
+// it, tile t+4 is copied into that stage.
 //
-// Fragment reads are inline asm (the compiler would otherwise wait for every
-// in-flight copy before the transpose reads, see mfma16_pp), so their waits are
-// explicit: before the MFMAs of a step, lgkmcnt(8) retires the previous step's 8
-// reads while this step's 8 stay in flight, and a scheduling barrier keeps the
-// MFMAs below that wait.
+// On this chip the matrix unit and the rest of a SIMD's instruction stream do
+// not overlap well, so the loop is kept short: the loop is unrolled once per
+// stage so every fragment read is a fixed per-lane base plus an immediate
+// offset, and the copies are issued from scalar base addresses. The copies are
+// inline asm, which keeps them out of the compiler's view: it would otherwise
+// wait for every in-flight copy before each LDS read. Their completion is
+// waited for explicitly (vmcnt) before the barrier that publishes a tile.
 template <int DT, int OPB>
 __global__ __launch_bounds__(512) void mfma16_dma(GemmArgs g) {
     constexpr int BM = 256, BN = 256, BK = 32, S = 4;
-    constexpr int SA = BM * BK, SB = BN * BK;  // halfs per stage
-    __shared__ __attribute__((aligned(1024))) uint16_t sA[S][SA];
-    __shared__ __attribute__((aligned(1024))) uint16_t sB[S][SB];
+    constexpr int SA = BM * BK, SB = BN * BK;  // halfs per stage (16 KB each)
+    __shared__ __attribute__((aligned(1024))) uint16_t sA[S * SA];
+    __shared__ __attribute__((aligned(1024))) uint16_t sB[S * SB];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 2, wn = wave & 3;  // wave tile rows wm*128.., columns wn*64..
@@ -861,79 +865,111 @@ __global__ __launch_bounds__(512) void mfma16_dma(GemmArgs g) {
     tile_coords(g, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int nk = g.K / BK;
-    const uint16_t* __restrict__ A = static_cast<const uint16_t*>(g.A);
-    const uint16_t* __restrict__ B = static_cast<const uint16_t*>(g.B);
 
-    // copies: waves 0-3 copy the A tile, waves 4-7 the B tile, 4 blocks of 1 KB each
-    const uint16_t* src[4];
+    // ---- copies: waves 0-3 copy the A tile, waves 4-7 the B tile; 4 blocks of 1 KB
+    // each per wave. Lane L of block b lands at LDS byte b*1024 + 16L and loads the
+    // logical 16-byte chunk that belongs at that swizzled position.
+    const bool copiesA = wm == 0;
+    const bool kmajor = copiesA || OPB == 1;
+    uint32_t voff[4];  // per-lane byte offset from the wave-uniform global base
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int b = wn * 4 + i;
-        if (wm == 0 || OPB == 1) {
+        if (kmajor) {
             const int row = b * 16 + (lane >> 2);
             const int c = (lane & 3) ^ kmaj32_swz(row);
-            src[i] = wm == 0 ? A + (size_t)(m0 + row) * g.lda + c * 8 : B + (size_t)(n0 + row) * g.ldb + c * 8;
+            voff[i] = (uint32_t)(row * (copiesA ? g.lda : g.ldb) + c * 8) * 2u;
         } else {
             const int row = b * 2 + (lane >> 5);
             const int c = (lane & 31) ^ nmaj32_swz(row);
-            src[i] = B + (size_t)row * g.ldb + n0 + c * 8;
+            voff[i] = (uint32_t)(row * g.ldb + c * 8) * 2u;
         }
     }
-    const size_t kstep = (wm == 1 && OPB == 0) ? (size_t)BK * g.ldb : (size_t)BK;
+    const uint64_t gbase = copiesA ? reinterpret_cast<uint64_t>(static_cast<const uint16_t*>(g.A) + (size_t)m0 * g.lda)
+                           : OPB == 0 ? reinterpret_cast<uint64_t>(static_cast<const uint16_t*>(g.B) + n0)
+                                      : reinterpret_cast<uint64_t>(static_cast<const uint16_t*>(g.B) + (size_t)n0 * g.ldb);
+    const uint64_t gstep = (!copiesA && OPB == 0) ? (uint64_t)BK * g.ldb * 2u : (uint64_t)BK * 2u;  // bytes per k-tile
+    const uint32_t ldsdst = (uint32_t)reinterpret_cast<uintptr_t>(DG_LDSV(copiesA ? sA : sB)) + (uint32_t)(wn * 4) * 1024u;
+    // wave-uniform values, moved to scalar registers (the compiler cannot prove a
+    // value derived from threadIdx.x / 64 is uniform). readfirstlane returns a signed
+    // int: each half goes through uint32_t before widening, or a low word with bit 31
+    // set would sign-extend into the high word of the address.
+    auto uniform64 = [](uint64_t v) {
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+        return ((uint64_t)hi << 32) | (uint64_t)lo;
+    };
+    const uint64_t gb = uniform64(gbase);
+    const uint64_t gs = uniform64(gstep);
+    const uint32_t ld0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)ldsdst);
     auto issue = [&](int t) {
-        uint16_t* dst = wm == 0 ? sA[t & 3] : sB[t & 3];
+        const uint64_t gp = gb + (uint64_t)t * gs;
+        const uint32_t d = ld0 + (uint32_t)(t & 3) * (SA * 2);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_global_load_lds(DG_GLB(src[i] + (size_t)t * kstep), DG_LDSV(dst + (wn * 4 + i) * 512), 16,
-                                             0, 0);
+            // An SALU write of M0 needs one wait state before an LDS DMA reads it; the
+            // compiler's hazard pass does not look inside asm, so the nop is explicit.
+            // M0 is not declared clobbered (the compiler reserves it); no other code in
+            // this kernel reads M0.
+            asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2" ::"v"(voff[i]),
+                         "s"(d + i * 1024u), "s"(gp)
+                         : "memory");
     };
 
-    // LDS byte addresses of this lane's fragment reads within a stage, for k16 step 0;
-    // step 1 and the stage offset are added at use.
-    uint32_t qaddr[2][4], paddr[2][2][2];
-    const uint32_t baseA = (uint32_t)reinterpret_cast<uintptr_t>(DG_LDSV(&sA[0][0]));
-    const uint32_t baseB = (uint32_t)reinterpret_cast<uintptr_t>(DG_LDSV(&sB[0][0]));
+    // ---- fragment reads: per-lane bases; subtile, k step and stage are immediates.
+    // Q (A rows): k-major 64-byte rows, chunk (ks*2 + lane/32) ^ kmaj32_swz(row); the
+    // swizzle depends on the lane only (rows differ by multiples of 32 between
+    // subtiles), so one base per k step.
+    const char* sAb = reinterpret_cast<const char*>(sA);
+    const char* sBb = reinterpret_cast<const char*>(sB);
+    const char* qb[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
+        const int r = wm * 128 + l32;
+        qb[ks] = sAb + r * 64 + (((ks * 2 + lh) ^ kmaj32_swz(r)) << 4);
+    }
+    // P (B columns): row-major B through transpose reads (4 consecutive k of one n per
+    // lane), or column-major B like Q.
+    const char* pbase[2][2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = wm * 128 + i * 32 + l32;
-            qaddr[ks][i] = baseA + 2 * (r * BK + (((ks * 2 + lh) ^ kmaj32_swz(r)) << 3));
-        }
+    for (int j = 0; j < 2; ++j) {
+        if (OPB == 0) {
+            const int gp = lane >> 4, i16 = lane & 15;
+            const int col = wn * 64 + j * 32 + (gp & 1) * 16 + ((i16 & 3) << 2);
+            const int krow = (gp >> 1) * 8 + (i16 >> 2);  // ks*16 and hh*4 rows are added as immediates
+            pbase[j][0] = sBb + krow * 512 + ((((col >> 3) ^ nmaj32_swz(krow))) << 4) + (col & 7) * 2;
+            pbase[j][1] = nullptr;
+        } else {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            if (OPB == 0) {
-                const int gp = lane >> 4, i16 = lane & 15;
-                const int col = wn * 64 + j * 32 + (gp & 1) * 16 + ((i16 & 3) << 2);
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int krow = ks * 16 + (gp >> 1) * 8 + hh * 4 + (i16 >> 2);
-                    paddr[ks][j][hh] = baseB + 2 * (krow * BN + (((col >> 3) ^ nmaj32_swz(krow)) << 3) + (col & 7));
-                }
-            } else {
+            for (int ks = 0; ks < 2; ++ks) {
                 const int r = wn * 64 + j * 32 + l32;
-                paddr[ks][j][0] = baseB + 2 * (r * BK + (((ks * 2 + lh) ^ kmaj32_swz(r)) << 3));
-                paddr[ks][j][1] = 0;
+                pbase[j][ks] = sBb + r * 64 + (((ks * 2 + lh) ^ kmaj32_swz(r)) << 4);
             }
         }
     }
 
-    // register set f: Q fragments; P fragments of column-major B (pb) or the two
-    // 4-k halves of a row-major-B P fragment (ph), combined only after the wait.
     u32x4 qa[2][4], pb[2][2];
-    u32x2 ph[2][2][2];
-    auto load_frags = [&](int f, int t, int ks) {
-        const uint32_t so = (uint32_t)(t & 3) * (SA * 2);  // stage offset in bytes (SA == SB)
+    auto load_frags = [&](int f, auto stage_c, int ks) {
+        constexpr int st = decltype(stage_c)::value;
+        constexpr int so = st * SA * 2;  // stage offset in bytes
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            asm volatile("ds_read_b128 %0, %1" : "=v"(qa[f][i]) : "v"(qaddr[ks][i] + so));
+            qa[f][i] = *DG_LDS_PTR(const u32x4, qb[ks] + so + i * 32 * 64);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             if (OPB == 0) {
-                asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(ph[f][j][0]) : "v"(paddr[ks][j][0] + so));
-                asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(ph[f][j][1]) : "v"(paddr[ks][j][1] + so));
+                const char* p = pbase[j][0] + so + ks * 16 * 512;
+                u32x2 h0, h1;
+                if (DT == DT_F16) {
+                    h0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4f16(DG_LDS_PTR(fp16x4_t, p)));
+                    h1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4f16(DG_LDS_PTR(fp16x4_t, p + 4 * 512)));
+                } else {
+                    h0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(DG_LDS_PTR(bf16x4_t, p)));
+                    h1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(DG_LDS_PTR(bf16x4_t, p + 4 * 512)));
+                }
+                pb[f][j] = u32x4{h0[0], h0[1], h1[0], h1[1]};
             } else {
-                asm volatile("ds_read_b128 %0, %1" : "=v"(pb[f][j]) : "v"(paddr[ks][j][0] + so));
+                pb[f][j] = *DG_LDS_PTR(const u32x4, pbase[j][ks] + so);
             }
         }
     };
@@ -943,17 +979,7 @@ __global__ __launch_bounds__(512) void mfma16_dma(GemmArgs g) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-    // Wait until at most `newer` LDS reads are outstanding, then multiply set f.
-    auto mma = [&](int f, int newer) {
-        if (newer >= 8) asm volatile("s_waitcnt lgkmcnt(8)" ::: "memory");
-        else if (newer >= 6) asm volatile("s_waitcnt lgkmcnt(6)" ::: "memory");
-        else asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-        if (OPB == 0) {
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                pb[f][j] = u32x4{ph[f][j][0][0], ph[f][j][0][1], ph[f][j][1][0], ph[f][j][1][1]};
-        }
+    auto mma = [&](int f) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -967,9 +993,7 @@ __global__ __launch_bounds__(512) void mfma16_dma(GemmArgs g) {
                                                                        __builtin_bit_cast(bf16x8, qa[f][i]), acc[i][j],
                                                                        0, 0, 0);
             }
-        __builtin_amdgcn_sched_barrier(0);
     };
-    constexpr int READS = OPB == 0 ? 8 : 6;  // LDS reads per step
     auto tile_barrier = [&](int vm_allowed) {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (vm_allowed >= 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
@@ -978,27 +1002,58 @@ __global__ __launch_bounds__(512) void mfma16_dma(GemmArgs g) {
         else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         asm volatile("s_barrier" ::: "memory");
     };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    // One tile t (stage ST = t mod 4): step 2t multiplies set 0 while reading k 16..31
+    // of tile t into set 1; after the barrier, step 2t+1 multiplies set 1 while reading
+    // k 0..15 of tile t+1 into set 0.
+    auto tile = [&](auto st_c, int t) {
+        constexpr int st = decltype(st_c)::value;
+        using NEXT = std::integral_constant<int, (st + 1) & 3>;
+        load_frags(1, st_c, 1);
+        mma(0);
+        tile_barrier(4 * max(0, min(2, nk - 2 - t)));
+        if (t + S < nk) issue(t + S);
+        load_frags(0, NEXT{}, 0);
+        mma(1);
+    };
 
     // prologue: tiles 0..3 in flight, tile 0 published, first fragments requested
     for (int t = 0; t < S && t < nk; ++t) issue(t);
     tile_barrier(4 * (min(S, nk) - 1));
-    load_frags(0, 0, 0);
+    load_frags(0, I0{}, 0);
 
-    for (int t = 0; t < nk - 1; ++t) {
-        // step 2t: k 16..31 of tile t requested, k 0..15 multiplied
-        load_frags(1, t, 1);
-        mma(0, READS);
-        // publish tile t+1, retire stage t mod 4
-        tile_barrier(4 * max(0, min(2, nk - 2 - t)));
-        if (t + S < nk) issue(t + S);
-        // step 2t+1: k 0..15 of tile t+1 requested, k 16..31 of tile t multiplied
-        load_frags(0, t + 1, 0);
-        mma(1, READS);
+    int t = 0;
+    for (; t + 4 <= nk - 1; t += 4) {
+        tile(I0{}, t);
+        tile(I1{}, t + 1);
+        tile(I2{}, t + 2);
+        tile(I3{}, t + 3);
     }
-    // last tile: no further copies or barriers
-    load_frags(1, nk - 1, 1);
-    mma(0, READS);
-    mma(1, 0);
+    // remaining tiles before the last one (t is a multiple of 4 here)
+    if (t < nk - 1) {
+        tile(I0{}, t);
+        ++t;
+        if (t < nk - 1) {
+            tile(I1{}, t);
+            ++t;
+            if (t < nk - 1) {
+                tile(I2{}, t);
+                ++t;
+            }
+        }
+    }
+    // last tile (stage (nk-1) mod 4): no further copies or barriers
+    switch ((nk - 1) & 3) {
+        case 0: load_frags(1, I0{}, 1); break;
+        case 1: load_frags(1, I1{}, 1); break;
+        case 2: load_frags(1, I2{}, 1); break;
+        default: load_frags(1, I3{}, 1); break;
+    }
+    mma(0);
+    mma(1);
 
     // epilogue: lane owns C[m][n..n+3] for four n runs per subtile
 #pragma unroll

@@ -26,6 +26,15 @@ struct MenuEntry {
     int id, variant, dtype, opb, vec, bm, bn, bk, wm, wn, tm, tn, threads, lds_bytes, sched;
 };
 
+// Schedules the planner may choose and the launcher will run. Schedule 3 is
+// compiled but switched off: its copy code had two defects that made it address
+// memory it does not own (an M0 write read by the next LDS DMA without the wait
+// state the GFX9 family requires, and a copy base address built from a signed
+// readfirstlane result, which sign-extends when bit 31 of the low word is set).
+// Both are corrected in the kernel; it stays off until the corrected kernel has
+// passed its parity tests on the device.
+constexpr bool schedule_enabled(int sched) { return sched != 3; }
+
 // X(id, variant, dtype, opb, vec, bm, bn, bk, wm, wn, tm, tn, threads, lds_bytes, sched)
 // The largest MFMA tile is 256 x 256 (2 x 4 waves) for 16-bit inputs and 256 x 128
 // (4 x 2 waves) for fp32; the fp32 kernel's 64 x 64 tile uses a 4 x 1 wave grid

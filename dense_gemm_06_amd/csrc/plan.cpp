@@ -165,6 +165,11 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
                       want_variant, want_bm, want_bn, want_vec, want_remap, want_group);
             return GEMM_ERR_INVALID_VALUE;
         }
+        if (want_sched && !schedule_enabled(want_sched)) {
+            set_error("schedule %d is switched off in this library (its kernel has not passed parity on the device)",
+                      want_sched);
+            return GEMM_ERR_UNSUPPORTED;
+        }
         if (want_vec == 1 && !vec_ok) {
             set_error("16-byte loads requested but A/B bases or leading dimensions are not 16-byte aligned");
             return GEMM_ERR_UNSUPPORTED;
@@ -180,6 +185,7 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
         if (want_bn && e.bn != want_bn) continue;
         if (want_wm && (e.variant == V_MFMA ? e.wm : 1) != want_wm) continue;
         if (want_sched && e.sched != want_sched) continue;
+        if (!schedule_enabled(e.sched)) continue;
         // the ping-pong kernel copies whole tiles: no masking of M, N or K edges
         if (e.sched >= 2 && (M % e.bm != 0 || N % e.bn != 0 || K % e.bk != 0 || K == 0)) continue;
         if (want_wn && (e.variant == V_MFMA ? e.wn : 1) != want_wn) continue;

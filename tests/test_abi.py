@@ -99,6 +99,18 @@ def test_plan_ping_pong_eligibility():
     assert st == dg.GEMM_ERR_UNSUPPORTED
 
 
+def test_plan_never_selects_switched_off_schedule():
+    """Schedule 3 is compiled but switched off: never chosen, and a forced request is refused."""
+    for dtype in ("f16", "bf16"):
+        for op_b in "NT":
+            for shape in ((4096, 4096, 4096), (256, 512, 32), (8192, 8192, 8192)):
+                st, c = plan(*shape, dtype, op_b)
+                assert st == 0 and c.schedule != 3
+            st, _ = plan(4096, 4096, 4096, dtype, op_b, req=dg.request(schedule=3))
+            assert st == dg.GEMM_ERR_UNSUPPORTED
+    assert "switched off" in dg.gemm_last_error()
+
+
 def test_plan_fills_the_machine():
     """A smaller problem gets smaller tiles so that the grid covers the compute units."""
     st, c = plan(1024, 1024, 1024, "f32")

@@ -39,6 +39,19 @@ MENU_IDS = [f"k{e['kernel_id']}-{'lds' if e['variant'] == 1 else 'mfma'}-{DT_NAM
             for e in MENU]
 
 
+# The software-pipelined direct-copy kernel (schedule 3) faulted on the device: its
+# copy asm read M0 without the required wait state, and its copy base address was
+# sign-extended from a signed readfirstlane result. Both are corrected in the kernel
+# source, but the library keeps the schedule switched off (the planner refuses it)
+# until the corrected kernel is run again; its cases stay here, skipped.
+SCHED3_OFF = "schedule 3 switched off after device faults (M0 wait state, sign-extended copy base); fix not yet run"
+
+
+def menu_params():
+    return [pytest.param(e, id=i, marks=pytest.mark.skip(reason=SCHED3_OFF)) if e["schedule"] == 3
+            else pytest.param(e, id=i) for e, i in zip(MENU, MENU_IDS)]
+
+
 def forced(e):
     return dg.request(variant=e["variant"], bm=e["bm"], bn=e["bn"], vec=e["vec"], waves_m=e["waves_m"],
                       waves_n=e["waves_n"], schedule=e["schedule"])
@@ -79,7 +92,7 @@ def make_case(e, kind, seed):
     return gi.make_operands(M, N, K, dtype, "normal", seed=seed, op_b=op_b, lda=lda, ldb=ldb)
 
 
-@pytest.mark.parametrize("e", MENU, ids=MENU_IDS)
+@pytest.mark.parametrize("e", menu_params())
 def test_kernel_random_ragged(e):
     ops = make_case(e, "rand", seed=e["kernel_id"])
     ldc = ops.N + 3
@@ -91,7 +104,7 @@ def test_kernel_random_ragged(e):
     assert err <= TOL[ops.dtype], err
 
 
-@pytest.mark.parametrize("schedule", [2, 3])
+@pytest.mark.parametrize("schedule", [2, pytest.param(3, marks=pytest.mark.skip(reason=SCHED3_OFF))])
 @pytest.mark.parametrize("k_tiles", [1, 2, 3, 4, 5, 6, 130])
 @pytest.mark.parametrize("dtype,op_b", [("f16", "N"), ("bf16", "N"), ("f16", "T"), ("bf16", "T")])
 def test_full_tile_kernels_k_tile_counts(schedule, k_tiles, dtype, op_b):
@@ -103,7 +116,7 @@ def test_full_tile_kernels_k_tile_counts(schedule, k_tiles, dtype, op_b):
     assert normalized_error(C[:ops.M, :ops.N], Cref, D) <= TOL[dtype]
 
 
-@pytest.mark.parametrize("e", MENU, ids=MENU_IDS)
+@pytest.mark.parametrize("e", menu_params())
 def test_kernel_integer_exact(e):
     ops = make_case(e, "int", seed=e["kernel_id"] % 5)
     print(f"case kernel {e['kernel_id']} integer M={ops.M} N={ops.N} K={ops.K}", flush=True)
