@@ -1,0 +1,402 @@
+// kernel_mfma.h -- register-staged MFMA kernels (any shape, masked edges).
+#pragma once
+#include "lds_layout.h"
+
+namespace dg {
+
+// MFMA kernels: operand roles.
+//
+// The matrix instruction computes D(16x16) += P(16 x k) * Q(k x 16) with D held
+// as 4 consecutive rows of one column per lane (lane l: rows 4(l/16)..+3, column
+// l%16). The kernels feed P = a 16 x k block of B^T (rows are n) and Q = a k x 16
+// block of A^T (columns are m), so D = (A B)^T block and each lane ends up with
+// 4 consecutive n of one row m of C: a 16-byte store per lane. P and Q use the
+// same (lane, slot) -> k assignment, so the instruction's internal k order never
+// matters: any k permutation applied identically to both operands leaves the sum
+// unchanged.
+
+// fp16 / bf16 inputs, v_mfma_f32_16x16x32: each lane supplies 8 consecutive k
+// of one row of P and one column of Q (k = 8(l/16) + slot).
+template <int DT, int OPB, bool VEC, int BM, int BN, int BK, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64)
+__attribute__((amdgpu_waves_per_eu(1, (BM / WM) * (BN / WN) >= 128 * 128 ? 1 : 8)))
+void mfma16_gemm(GemmArgs g) {
+    constexpr int NT = WM * WN * 64;
+    constexpr int TWM = BM / WM, TWN = BN / WN;  // wave tile
+    constexpr int SM = TWM / 16, SN = TWN / 16;  // 16 x 16 subtiles per wave
+    constexpr int KC = BK / 8;                   // 16-byte chunks per k-row
+    constexpr int NC = BN / 8;                   // 16-byte chunks per n-row
+    constexpr int LA = BM * KC / NT;
+    constexpr int LB = OPB == 0 ? BK * NC / NT : BN * KC / NT;
+    static_assert(BK % 32 == 0 && KC == 8, "k tile must be 64 (8 chunks per row)");
+    static_assert(LA >= 1 && LB >= 1 && (BM * KC) % NT == 0, "tile does not divide the thread count");
+    static_assert(OPB == 1 || NC >= 8, "row-major B tile needs at least 8 chunks per row");
+
+    __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * BK];
+    __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * BK];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wmi = wave / WN, wni = wave % WN;
+    const int l16 = lane & 15, lg = lane >> 4;
+    int tm, tn;
+    tile_coords(g, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int M = g.M, N = g.N, K = g.K;
+    const uint16_t* __restrict__ A = static_cast<const uint16_t*>(g.A);
+    const uint16_t* __restrict__ B = static_cast<const uint16_t*>(g.B);
+
+    // Global addresses: a wave-uniform base per k-tile plus a 32-bit per-thread
+    // offset (the host bounds the leading dimensions so offsets fit).
+    const uint16_t* __restrict__ Ablk = A + (size_t)m0 * g.lda;
+    const uint16_t* __restrict__ Bblk = OPB == 0 ? B + n0 : B + (size_t)n0 * g.ldb;
+    const uint32_t lda = (uint32_t)g.lda, ldb = (uint32_t)g.ldb;
+    const int mlim = M - m0, nlim = N - n0;
+    const bool interior = mlim >= BM && nlim >= BN;  // uniform: no row/column masking needed
+    uint16_t ra[LA][8], rb[LB][8];
+    auto load_tiles = [&](int kt) {
+        const int k0 = kt * BK;
+        const uint16_t* Ak = Ablk + k0;
+        const uint16_t* Bk = OPB == 0 ? Bblk + (size_t)k0 * g.ldb : Bblk + k0;
+        if (interior && k0 + BK <= K) {
+#pragma unroll
+            for (int p = 0; p < LA; ++p) {
+                const int idx = tid + NT * p, row = idx / KC, c = idx % KC;
+                load_chunk_full<uint16_t, 8, VEC>(ra[p], Ak + (row * lda + c * 8));
+            }
+#pragma unroll
+            for (int p = 0; p < LB; ++p) {
+                const int idx = tid + NT * p;
+                const int row = OPB == 0 ? idx / NC : idx / KC, c = OPB == 0 ? idx % NC : idx % KC;
+                load_chunk_full<uint16_t, 8, VEC>(rb[p], Bk + (row * ldb + c * 8));
+            }
+            return;
+        }
+#pragma unroll
+        for (int p = 0; p < LA; ++p) {
+            const int idx = tid + NT * p, row = idx / KC, c = idx % KC;
+            const int valid = row < mlim ? min(8, K - k0 - c * 8) : 0;
+            load_chunk<uint16_t, 8, VEC>(ra[p], Ak + (row * lda + c * 8), valid);
+        }
+#pragma unroll
+        for (int p = 0; p < LB; ++p) {
+            const int idx = tid + NT * p;
+            if (OPB == 0) {
+                const int row = idx / NC, c = idx % NC;
+                const int valid = k0 + row < K ? min(8, nlim - c * 8) : 0;
+                load_chunk<uint16_t, 8, VEC>(rb[p], Bk + (row * ldb + c * 8), valid);
+            } else {
+                const int row = idx / KC, c = idx % KC;
+                const int valid = row < nlim ? min(8, K - k0 - c * 8) : 0;
+                load_chunk<uint16_t, 8, VEC>(rb[p], Bk + (row * ldb + c * 8), valid);
+            }
+        }
+    };
+    auto store_tiles = [&](int buf) {
+#pragma unroll
+        for (int p = 0; p < LA; ++p) {
+            const int idx = tid + NT * p, row = idx / KC, c = idx % KC;
+            *reinterpret_cast<u32x4*>(&sA[buf][row * BK + ((c ^ kmaj_swz(row)) << 3)]) =
+                *reinterpret_cast<const u32x4*>(ra[p]);
+        }
+#pragma unroll
+        for (int p = 0; p < LB; ++p) {
+            const int idx = tid + NT * p;
+            if (OPB == 0) {
+                const int row = idx / NC, c = idx % NC;
+                *reinterpret_cast<u32x4*>(&sB[buf][row * BN + ((c ^ nmaj_swz<NC>(row)) << 3)]) =
+                    *reinterpret_cast<const u32x4*>(rb[p]);
+            } else {
+                const int row = idx / KC, c = idx % KC;
+                *reinterpret_cast<u32x4*>(&sB[buf][row * BK + ((c ^ kmaj_swz(row)) << 3)]) =
+                    *reinterpret_cast<const u32x4*>(rb[p]);
+            }
+        }
+    };
+
+    f32x4 acc[SM][SN];
+#pragma unroll
+    for (int i = 0; i < SM; ++i)
+#pragma unroll
+        for (int j = 0; j < SN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nk = (K + BK - 1) / BK;
+    if (nk > 0) {
+        load_tiles(0);
+        store_tiles(0);
+    }
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < nk) load_tiles(kt + 1);
+#pragma unroll
+        for (int ks = 0; ks < BK / 32; ++ks) {
+            u32x4 qa[SM], pb[SN];
+#pragma unroll
+            for (int i = 0; i < SM; ++i) {
+                const int r = wmi * TWM + i * 16 + l16;
+                qa[i] = *reinterpret_cast<const u32x4*>(&sA[cur][r * BK + (((ks * 4 + lg) ^ kmaj_swz(r)) << 3)]);
+            }
+#pragma unroll
+            for (int j = 0; j < SN; ++j) {
+                if (OPB == 0) {
+                    // transpose reads: within each 16-lane group, lane i addresses row
+                    // kb + i/4 at columns nb + 4(i%4); lane j receives column nb + j of
+                    // rows kb..kb+3 (4 consecutive k).
+                    const int nb = wni * TWN + j * 16;
+                    const int col = nb + ((l16 & 3) << 2);
+                    u32x2 h[2];
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const int krow = ks * 32 + lg * 8 + hh * 4 + (l16 >> 2);
+                        const uint16_t* p =
+                            &sB[cur][krow * BN + (((col >> 3) ^ nmaj_swz<NC>(krow)) << 3) + (col & 7)];
+                        if (DT == DT_F16) {
+                            fp16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4f16(DG_LDS_PTR(fp16x4_t, p));
+                            h[hh] = __builtin_bit_cast(u32x2, t);
+                        } else {
+                            bf16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(DG_LDS_PTR(bf16x4_t, p));
+                            h[hh] = __builtin_bit_cast(u32x2, t);
+                        }
+                    }
+                    pb[j] = u32x4{h[0][0], h[0][1], h[1][0], h[1][1]};
+                } else {
+                    const int r = wni * TWN + j * 16 + l16;
+                    pb[j] = *reinterpret_cast<const u32x4*>(&sB[cur][r * BK + (((ks * 4 + lg) ^ kmaj_swz(r)) << 3)]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < SM; ++i)
+#pragma unroll
+                for (int j = 0; j < SN; ++j) {
+                    if (DT == DT_F16)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            __builtin_bit_cast(f16x8, pb[j]), __builtin_bit_cast(f16x8, qa[i]), acc[i][j], 0, 0, 0);
+                    else
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, pb[j]), __builtin_bit_cast(bf16x8, qa[i]), acc[i][j], 0, 0, 0);
+                }
+        }
+        if (kt + 1 < nk) store_tiles(cur ^ 1);
+        __syncthreads();
+    }
+
+    // epilogue: lane owns C[m][n..n+3]
+#pragma unroll
+    for (int i = 0; i < SM; ++i) {
+        const int m = m0 + wmi * TWM + i * 16 + l16;
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < SN; ++j) {
+            const int n = n0 + wni * TWN + j * 16 + lg * 4;
+            float* cp = g.C + (size_t)m * g.ldc + n;
+            const f32x4 v = acc[i][j];
+            if (n + 3 < N && (reinterpret_cast<uintptr_t>(cp) & 15) == 0) {
+                *reinterpret_cast<f32x4*>(cp) = v;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (n + e < N) cp[e] = v[e];
+            }
+        }
+    }
+}
+
+// fp32 inputs, v_mfma_f32_16x16x4_f32: each lane supplies one k of one row of P
+// and one column of Q per instruction. Four consecutive instructions (steps
+// s = 0..3) take k = 4(l/16) + s, so a lane reads one float4 along k of A (and
+// of a column-major B) and uses one component per step.
+//
+// Row-major B: a lane reads a float4 along n instead; P subtile u of a 64-wide
+// group holds the columns n = 4(l%16) + u, so the four subtiles share one read
+// and, at the store, a lane owns 16 consecutive n of one row of C.
+template <int OPB, bool VEC, int BM, int BN, int BK, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64) void mfma32_gemm(GemmArgs g) {
+    constexpr int NT = WM * WN * 64;
+    constexpr int TWM = BM / WM, TWN = BN / WN;
+    constexpr int SM = TWM / 16, SN = TWN / 16, QN = TWN / 64;
+    constexpr int KC = BK / 4;  // 16-byte chunks per k-row
+    constexpr int NC = BN / 4;  // 16-byte chunks per n-row
+    constexpr int LA = BM * KC / NT;
+    constexpr int LB = OPB == 0 ? BK * NC / NT : BN * KC / NT;
+    static_assert(KC == 8, "k tile must be 32 (8 chunks per row)");
+    static_assert(OPB == 1 || TWN % 64 == 0, "row-major B needs 64-wide wave tiles");
+    static_assert(LA >= 1 && LB >= 1 && (BM * KC) % NT == 0, "tile does not divide the thread count");
+
+    __shared__ __attribute__((aligned(16))) float sA[2][BM * BK];
+    __shared__ __attribute__((aligned(16))) float sB[2][BN * BK];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wmi = wave / WN, wni = wave % WN;
+    const int l16 = lane & 15, lg = lane >> 4;
+    int tm, tn;
+    tile_coords(g, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int M = g.M, N = g.N, K = g.K;
+    const float* __restrict__ A = static_cast<const float*>(g.A);
+    const float* __restrict__ B = static_cast<const float*>(g.B);
+
+    const float* __restrict__ Ablk = A + (size_t)m0 * g.lda;
+    const float* __restrict__ Bblk = OPB == 0 ? B + n0 : B + (size_t)n0 * g.ldb;
+    const uint32_t lda = (uint32_t)g.lda, ldb = (uint32_t)g.ldb;
+    const int mlim = M - m0, nlim = N - n0;
+    const bool interior = mlim >= BM && nlim >= BN;  // uniform: no row/column masking needed
+    float ra[LA][4], rb[LB][4];
+    auto load_tiles = [&](int kt) {
+        const int k0 = kt * BK;
+        const float* Ak = Ablk + k0;
+        const float* Bk = OPB == 0 ? Bblk + (size_t)k0 * g.ldb : Bblk + k0;
+        if (interior && k0 + BK <= K) {
+#pragma unroll
+            for (int p = 0; p < LA; ++p) {
+                const int idx = tid + NT * p, row = idx / KC, c = idx % KC;
+                load_chunk_full<float, 4, VEC>(ra[p], Ak + (row * lda + c * 4));
+            }
+#pragma unroll
+            for (int p = 0; p < LB; ++p) {
+                const int idx = tid + NT * p;
+                const int row = OPB == 0 ? idx / NC : idx / KC, c = OPB == 0 ? idx % NC : idx % KC;
+                load_chunk_full<float, 4, VEC>(rb[p], Bk + (row * ldb + c * 4));
+            }
+            return;
+        }
+#pragma unroll
+        for (int p = 0; p < LA; ++p) {
+            const int idx = tid + NT * p, row = idx / KC, c = idx % KC;
+            const int valid = row < mlim ? min(4, K - k0 - c * 4) : 0;
+            load_chunk<float, 4, VEC>(ra[p], Ak + (row * lda + c * 4), valid);
+        }
+#pragma unroll
+        for (int p = 0; p < LB; ++p) {
+            const int idx = tid + NT * p;
+            if (OPB == 0) {
+                const int row = idx / NC, c = idx % NC;
+                const int valid = k0 + row < K ? min(4, nlim - c * 4) : 0;
+                load_chunk<float, 4, VEC>(rb[p], Bk + (row * ldb + c * 4), valid);
+            } else {
+                const int row = idx / KC, c = idx % KC;
+                const int valid = row < nlim ? min(4, K - k0 - c * 4) : 0;
+                load_chunk<float, 4, VEC>(rb[p], Bk + (row * ldb + c * 4), valid);
+            }
+        }
+    };
+    auto store_tiles = [&](int buf) {
+#pragma unroll
+        for (int p = 0; p < LA; ++p) {
+            const int idx = tid + NT * p, row = idx / KC, c = idx % KC;
+            *reinterpret_cast<f32x4*>(&sA[buf][row * BK + ((c ^ kmaj_swz(row)) << 2)]) =
+                f32x4{ra[p][0], ra[p][1], ra[p][2], ra[p][3]};
+        }
+#pragma unroll
+        for (int p = 0; p < LB; ++p) {
+            const int idx = tid + NT * p;
+            if (OPB == 0) {
+                const int row = idx / NC, c = idx % NC;
+                *reinterpret_cast<f32x4*>(&sB[buf][row * BN + (c << 2)]) =
+                    f32x4{rb[p][0], rb[p][1], rb[p][2], rb[p][3]};
+            } else {
+                const int row = idx / KC, c = idx % KC;
+                *reinterpret_cast<f32x4*>(&sB[buf][row * BK + ((c ^ kmaj_swz(row)) << 2)]) =
+                    f32x4{rb[p][0], rb[p][1], rb[p][2], rb[p][3]};
+            }
+        }
+    };
+
+    f32x4 acc[SM][SN];
+#pragma unroll
+    for (int i = 0; i < SM; ++i)
+#pragma unroll
+        for (int j = 0; j < SN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nk = (K + BK - 1) / BK;
+    if (nk > 0) {
+        load_tiles(0);
+        store_tiles(0);
+    }
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < nk) load_tiles(kt + 1);
+#pragma unroll
+        for (int kk = 0; kk < BK; kk += 16) {
+            f32x4 qa[SM];
+#pragma unroll
+            for (int i = 0; i < SM; ++i) {
+                const int r = wmi * TWM + i * 16 + l16;
+                qa[i] = *reinterpret_cast<const f32x4*>(&sA[cur][r * BK + ((((kk >> 2) + lg) ^ kmaj_swz(r)) << 2)]);
+            }
+            if (OPB == 0) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const int krow = kk + 4 * lg + s;
+                    f32x4 pq[QN];
+#pragma unroll
+                    for (int q = 0; q < QN; ++q)
+                        pq[q] = *reinterpret_cast<const f32x4*>(&sB[cur][krow * BN + wni * TWN + q * 64 + 4 * l16]);
+#pragma unroll
+                    for (int i = 0; i < SM; ++i)
+#pragma unroll
+                        for (int q = 0; q < QN; ++q)
+#pragma unroll
+                            for (int u = 0; u < 4; ++u)
+                                acc[i][4 * q + u] =
+                                    __builtin_amdgcn_mfma_f32_16x16x4f32(pq[q][u], qa[i][s], acc[i][4 * q + u], 0, 0, 0);
+                }
+            } else {
+                f32x4 pb[SN];
+#pragma unroll
+                for (int j = 0; j < SN; ++j) {
+                    const int r = wni * TWN + j * 16 + l16;
+                    pb[j] = *reinterpret_cast<const f32x4*>(&sB[cur][r * BK + ((((kk >> 2) + lg) ^ kmaj_swz(r)) << 2)]);
+                }
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+#pragma unroll
+                    for (int i = 0; i < SM; ++i)
+#pragma unroll
+                        for (int j = 0; j < SN; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(pb[j][s], qa[i][s], acc[i][j], 0, 0, 0);
+            }
+        }
+        if (kt + 1 < nk) store_tiles(cur ^ 1);
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int i = 0; i < SM; ++i) {
+        const int m = m0 + wmi * TWM + i * 16 + l16;
+        if (m >= M) continue;
+        if (OPB == 0) {
+#pragma unroll
+            for (int q = 0; q < QN; ++q)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int n = n0 + wni * TWN + q * 64 + 16 * lg + 4 * r;
+                    float* cp = g.C + (size_t)m * g.ldc + n;
+                    const f32x4 v = {acc[i][4 * q][r], acc[i][4 * q + 1][r], acc[i][4 * q + 2][r], acc[i][4 * q + 3][r]};
+                    if (n + 3 < N && (reinterpret_cast<uintptr_t>(cp) & 15) == 0) {
+                        *reinterpret_cast<f32x4*>(cp) = v;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (n + e < N) cp[e] = v[e];
+                    }
+                }
+        } else {
+#pragma unroll
+            for (int j = 0; j < SN; ++j) {
+                const int n = n0 + wni * TWN + j * 16 + lg * 4;
+                float* cp = g.C + (size_t)m * g.ldc + n;
+                const f32x4 v = acc[i][j];
+                if (n + 3 < N && (reinterpret_cast<uintptr_t>(cp) & 15) == 0) {
+                    *reinterpret_cast<f32x4*>(cp) = v;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < N) cp[e] = v[e];
+                }
+            }
+        }
+    }
+}
+
+}  // namespace dg

@@ -19,9 +19,10 @@ enum Dtype { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
 //             0 = element-wise loads (any alignment)
 //   bm, bn, bk : block tile; wm x wn : wave grid (MFMA); tm x tn : thread tile (LDS)
 //   sched   : 1 = register-staged double buffer (any shape), 2 = ping-pong with
-//             direct global->LDS copies, 3 = software-pipelined with direct
-//             copies (2 and 3: full tiles only -- M, N multiples of bm, bn, K a
-//             multiple of bk, 16-byte aligned operands)
+//             direct global->LDS copies on 16x16x32 MFMAs, 3 = software-pipelined
+//             with direct copies, 4 = ping-pong on 32x32x16 MFMAs (2-4: full tiles
+//             only -- M, N multiples of bm, bn, K a multiple of bk, 16-byte aligned
+//             operands)
 struct MenuEntry {
     int id, variant, dtype, opb, vec, bm, bn, bk, wm, wn, tm, tn, threads, lds_bytes, sched;
 };
@@ -78,6 +79,11 @@ constexpr bool schedule_enabled(int sched) { return sched != 3; }
     X(base + 0, V_MFMA, dt, 0, 1, 256, 256, 32, 2, 4, 0, 0, 512, 4 * 2 * 32 * 512, 2)      \
     X(base + 1, V_MFMA, dt, 1, 1, 256, 256, 32, 2, 4, 0, 0, 512, 4 * 2 * 32 * 512, 2)
 
+// The same ping-pong schedule on v_mfma_f32_32x32x16 (half the MFMA instructions).
+#define DG_MFMA_PP32(X, base, dt)                                                        \
+    X(base + 0, V_MFMA, dt, 0, 1, 256, 256, 32, 2, 4, 0, 0, 512, 4 * 2 * 32 * 512, 4)      \
+    X(base + 1, V_MFMA, dt, 1, 1, 256, 256, 32, 2, 4, 0, 0, 512, 4 * 2 * 32 * 512, 4)
+
 // Software-pipelined kernels with direct LDS copies (16-bit inputs, full tiles).
 #define DG_MFMA_DMA(X, base, dt)                                                         \
     X(base + 0, V_MFMA, dt, 0, 1, 256, 256, 32, 2, 4, 0, 0, 512, 4 * 2 * 32 * 512, 3)      \
@@ -95,9 +101,11 @@ constexpr bool schedule_enabled(int sched) { return sched != 3; }
     DG_MFMA_PP(X, 68, DT_F16)                                    \
     DG_MFMA_PP(X, 70, DT_BF16)                                   \
     DG_MFMA_DMA(X, 72, DT_F16)                                   \
-    DG_MFMA_DMA(X, 74, DT_BF16)
+    DG_MFMA_DMA(X, 74, DT_BF16)                                  \
+    DG_MFMA_PP32(X, 76, DT_F16)                                  \
+    DG_MFMA_PP32(X, 78, DT_BF16)
 
-constexpr int kMenuSize = 76;
+constexpr int kMenuSize = 80;
 
 // Arguments every kernel receives (by value).
 struct GemmArgs {

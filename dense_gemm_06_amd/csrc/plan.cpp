@@ -117,6 +117,7 @@ static double tile_efficiency(const MenuEntry& e) {
     // measured at 4096^3 fp16: ping-pong 144 us, software-pipelined 164 us,
     // register-staged 256 x 256 165 us
     if (e.sched == 2) return 0.97;
+    if (e.sched == 4) return 0.96;
     if (e.sched == 3) return 0.85;
     if (e.variant == V_LDS) return t >= 128 ? 0.6 : 0.35;
     return t >= 256 ? 0.85 : t >= 128 ? 0.7 : 0.45;
@@ -159,7 +160,7 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
         want_wm = req->waves_m;
         want_wn = req->waves_n;
         want_sched = req->schedule;
-        if (want_sched < 0 || want_sched > 3 || want_wm < 0 || want_wn < 0 || want_variant < 0 || want_variant > 2 || want_vec < -1 || want_vec > 1 || want_remap < -1 ||
+        if (want_sched < 0 || want_sched > 4 || want_wm < 0 || want_wn < 0 || want_variant < 0 || want_variant > 2 || want_vec < -1 || want_vec > 1 || want_remap < -1 ||
             want_remap > 1 || want_group < 0 || want_bm < 0 || want_bn < 0) {
             set_error("invalid requested configuration (variant %d, bm %d, bn %d, vec %d, xcd_remap %d, group_m %d)",
                       want_variant, want_bm, want_bn, want_vec, want_remap, want_group);
@@ -186,7 +187,7 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
         if (want_wm && (e.variant == V_MFMA ? e.wm : 1) != want_wm) continue;
         if (want_sched && e.sched != want_sched) continue;
         if (!schedule_enabled(e.sched)) continue;
-        // the ping-pong kernel copies whole tiles: no masking of M, N or K edges
+        // the direct-copy kernels copy whole tiles: no masking of M, N or K edges
         if (e.sched >= 2 && (M % e.bm != 0 || N % e.bn != 0 || K % e.bk != 0 || K == 0)) continue;
         if (want_wn && (e.variant == V_MFMA ? e.wn : 1) != want_wn) continue;
         const int vec = want_vec >= 0 ? want_vec : (vec_ok ? 1 : 0);

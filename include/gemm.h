@@ -87,9 +87,11 @@ typedef struct gemm_config {
     int32_t grid;      /* out: workgroups launched (tiles_m * tiles_n) */
     int32_t kernel_id; /* out: index into the library's kernel menu */
     int32_t schedule;  /* in/out: 0 any; 1 register-staged double buffer (any shape); 2 ping-pong
-                          with direct global->LDS copies; 3 software-pipelined with direct
-                          global->LDS copies (2 and 3: MFMA, 16-bit inputs, M and N multiples
-                          of 256, K a multiple of 32, 16-byte aligned operands) */
+                          with direct global->LDS copies on 16x16x32 MFMAs; 3 software-pipelined
+                          with direct global->LDS copies (switched off: requests for it return
+                          GEMM_ERR_UNSUPPORTED); 4 ping-pong on 32x32x16 MFMAs (2-4: MFMA,
+                          16-bit inputs, M and N multiples of 256, K a multiple of 32, 16-byte
+                          aligned operands) */
     int64_t tiles_m, tiles_n; /* out */
     double est_cycles; /* out: the heuristic's cost estimate (clock cycles) */
 } gemm_config;

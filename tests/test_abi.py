@@ -49,7 +49,7 @@ def test_status_strings():
 
 def test_menu_is_complete():
     menu = dg.gemm_menu()
-    assert len(menu) == dg.library().gemm_menu_size() == 76
+    assert len(menu) == dg.library().gemm_menu_size() == 80
     seen = set()
     for e in menu:
         assert e["lds_bytes"] <= 160 * 1024
@@ -63,7 +63,7 @@ def test_menu_is_complete():
                 for vec in (0, 1):
                     tiles = {(bm, bn) for (v, d, o, ve, bm, bn) in seen if (v, d, o, ve) == (variant, dtype, opb, vec)}
                     assert len(tiles) >= 2, (variant, dtype, opb, vec)
-    assert dg.library().gemm_menu_entry(76, None, None, None, None) == dg.GEMM_ERR_INVALID_VALUE
+    assert dg.library().gemm_menu_entry(80, None, None, None, None) == dg.GEMM_ERR_INVALID_VALUE
 
 
 def plan(M, N, K, dtype="f32", op_b="N", lda=None, ldb=None, ldc=None, a=0, b=0, c=0, cus=256, arch="gfx950",
