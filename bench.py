@@ -61,7 +61,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="time only the headline problem")
-    p.add_argument("--only", default=None, help="time only this benchmark problem (for profiling)")
+    p.add_argument("--only", default=None, help="time only this benchmark problem, or grouped workload (for profiling)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="instead of GEMMs, run 5 plain device copies of MIB MiB (calibrates HBM counters)")
     return p.parse_args()
@@ -117,6 +117,50 @@ def time_problem(name, steps, warmup):
                 kernel_tflops=flops / (launch_ms * 1e-3) / 1e12, wall_s=wall, dtype=ops.dtype,
                 M=ops.M, N=ops.N, K=ops.K, op_b=ops.op_b, flops=flops, cfg=cfg, cus=cus, arch=arch,
                 peak=PEAK_TFLOPS[ops.dtype])
+
+
+# Grouped workloads: `count` independent problems of one shape, run as one grouped
+# launch (the README's grouped example: four 256^3 fp32 GEMMs).
+GROUPED = {"g4_f32_256": dict(count=4, M=256, N=256, K=256, dtype="f32")}
+
+
+def time_grouped(name, steps, warmup):
+    """One step = every problem of the group in one gemm_grouped call; the same
+    problems as separate gemm_ex launches are timed alongside for comparison."""
+    import torch
+    import numpy as np
+    import dense_gemm_06_amd as dg
+    import gemm_inputs as gi
+    spec = GROUPED[name]
+    dev = lambda a: torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to("cuda")
+    ops = [gi.make_operands(spec["M"], spec["N"], spec["K"], spec["dtype"], "uniform", seed=s)
+           for s in range(spec["count"])]
+    bufs = [(dev(o.A), dev(o.B), torch.empty((o.M, o.N), dtype=torch.float32, device="cuda")) for o in ops]
+    probs = [dg.problem(o.M, o.N, o.K, A.data_ptr(), o.lda, B.data_ptr(), o.ldb, C.data_ptr(), o.N)
+             for o, (A, B, C) in zip(ops, bufs)]
+    code = dg.DTYPE_CODE[spec["dtype"]]
+    stream = torch.cuda.current_stream()
+    s = stream.cuda_stream
+    _, cfg = dg.gemm_grouped_plan(0, 0, code, probs)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms = timed(lambda: dg.gemm_grouped(0, 0, code, probs, None, s))
+    ms_sep = timed(lambda: [dg.gemm_ex(0, 0, o.M, o.N, o.K, A.data_ptr(), o.lda, B.data_ptr(), o.ldb,
+                                       C.data_ptr(), o.N, code, None, s) for o, (A, B, C) in zip(ops, bufs)])
+    flops = 2.0 * spec["count"] * spec["M"] * spec["N"] * spec["K"]
+    return dict(problem=name, ms_per_step=ms, tflops=flops / (ms * 1e-3) / 1e12, separate_ms=ms_sep,
+                separate_tflops=flops / (ms_sep * 1e-3) / 1e12, cfg=cfg, peak=PEAK_TFLOPS[spec["dtype"]])
 
 
 def cpu_baseline(name, target_s):
@@ -196,6 +240,10 @@ def main():
     import dense_gemm_06_amd as dg
     dg.library()   # fail loudly if the HIP library is missing
 
+    if a.only in GROUPED:
+        r = time_grouped(a.only, a.steps, a.warmup)
+        print(json.dumps({k: (v.as_dict() if k == "cfg" else v) for k, v in r.items()}), flush=True)
+        return
     headline = a.only or "c4_f16_4096"
     main_res = time_problem(headline, a.steps, a.warmup)
     extras = {}
@@ -244,6 +292,17 @@ def main():
                                      "tile": f"{v['cfg'].bm}x{v['cfg'].bn}",
                                      "variant": "mfma" if v["cfg"].variant == 2 else "lds"}
                                  for k, v in extras.items()}
+    if not a.no_extra and not a.only:
+        grouped = {}
+        for name in GROUPED:
+            r = time_grouped(name, max(5, a.steps // 2), max(2, a.warmup // 2))
+            grouped[name] = {"workload": f"{GROUPED[name]['count']} x {GROUPED[name]['M']}x{GROUPED[name]['N']}x"
+                                         f"{GROUPED[name]['K']} {GROUPED[name]['dtype']} in one grouped launch",
+                             "tflops": round(r["tflops"], 3), "ms_per_step": round(r["ms_per_step"], 6),
+                             "frac_of_peak": round(r["tflops"] / r["peak"], 4),
+                             "separate_launches_ms": round(r["separate_ms"], 6),
+                             "tile": f"{r['cfg'].bm}x{r['cfg'].bn}", "grid": r["cfg"].grid}
+        out["grouped"] = grouped
     if not a.no_cpu_baseline and not a.only:
         out["cpu_baseline"] = cpu_baseline(headline, a.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -1,9 +1,10 @@
 """Python binding of the MI355X dense GEMM library (libdensegemm.so).
 
 The functions mirror the C ABI in include/gemm.h one to one (gemm, gemm_ex,
-gemm_plan, gemm_menu_size / gemm_menu_entry, gemm_device_info,
-gemm_status_string, gemm_last_error) and only marshal arguments: every step of
-the product runs in the library's HIP kernels. A nonzero status raises
+gemm_plan, gemm_grouped, gemm_grouped_plan, gemm_strided_batched,
+gemm_menu_size / gemm_menu_entry, gemm_device_info, gemm_status_string,
+gemm_last_error) and only marshal arguments: every step of the product runs in
+the library's HIP kernels. A nonzero status raises
 GemmError carrying the library's own description.
 
 ``gemm_tensors`` is a convenience for torch tensors: it reads pointers, leading
@@ -46,6 +47,7 @@ class gemm_config(ctypes.Structure):
         ("kernel_id", ctypes.c_int32), ("schedule", ctypes.c_int32),
         ("tiles_m", ctypes.c_int64), ("tiles_n", ctypes.c_int64),
         ("est_cycles", ctypes.c_double),
+        ("tiles_total", ctypes.c_int64), ("launches", ctypes.c_int32), ("max_grid", ctypes.c_int32),
     ]
 
     def as_dict(self) -> dict:
@@ -54,12 +56,30 @@ class gemm_config(ctypes.Structure):
 
 def request(variant: int = GEMM_VARIANT_AUTO, bm: int = 0, bn: int = 0, vec: int = -1,
             xcd_remap: int = -1, group_m: int = 0, waves_m: int = 0, waves_n: int = 0,
-            schedule: int = 0) -> gemm_config:
+            schedule: int = 0, max_grid: int = 0) -> gemm_config:
     """A gemm_config with only the "in" fields set (0 / -1: heuristic decides)."""
     c = gemm_config()
     c.variant, c.bm, c.bn, c.vec, c.xcd_remap, c.group_m = variant, bm, bn, vec, xcd_remap, group_m
-    c.waves_m, c.waves_n, c.schedule = waves_m, waves_n, schedule
+    c.waves_m, c.waves_n, c.schedule, c.max_grid = waves_m, waves_n, schedule, max_grid
     return c
+
+
+class gemm_problem(ctypes.Structure):
+    """One entry of a grouped call: `batch` problems of one shape at element strides."""
+    _fields_ = [
+        ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+        ("A", ctypes.c_void_p), ("lda", ctypes.c_int64), ("stride_a", ctypes.c_int64),
+        ("B", ctypes.c_void_p), ("ldb", ctypes.c_int64), ("stride_b", ctypes.c_int64),
+        ("C", ctypes.c_void_p), ("ldc", ctypes.c_int64), ("stride_c", ctypes.c_int64),
+        ("batch", ctypes.c_int64),
+    ]
+
+
+def problem(M, N, K, A, lda, B, ldb, C, ldc, batch=1, stride_a=0, stride_b=0, stride_c=0) -> gemm_problem:
+    p = gemm_problem()
+    p.M, p.N, p.K, p.A, p.lda, p.stride_a = M, N, K, A, lda, stride_a
+    p.B, p.ldb, p.stride_b, p.C, p.ldc, p.stride_c, p.batch = B, ldb, stride_b, C, ldc, stride_c, batch
+    return p
 
 
 class GemmError(RuntimeError):
@@ -96,6 +116,14 @@ def _load():
     lib.gemm_plan.argtypes = [i32, i32, i64, i64, i64, i64, i64, i64, i32, ctypes.c_size_t, ctypes.c_size_t,
                               ctypes.c_size_t, i32, ctypes.c_char_p, cfgp, cfgp]
     lib.gemm_plan.restype = i32
+    probp = ctypes.POINTER(gemm_problem)
+    lib.gemm_grouped.argtypes = [i32, i32, i32, probp, i32, cfgp, vp]
+    lib.gemm_grouped.restype = i32
+    lib.gemm_grouped_plan.argtypes = [i32, i32, i32, probp, i32, i32, ctypes.c_char_p, cfgp, cfgp]
+    lib.gemm_grouped_plan.restype = i32
+    lib.gemm_strided_batched.argtypes = [i32, i32, i64, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64, i64, i64,
+                                         i32, cfgp, vp]
+    lib.gemm_strided_batched.restype = i32
     lib.gemm_menu_size.argtypes = []
     lib.gemm_menu_size.restype = i32
     lib.gemm_menu_entry.argtypes = [i32, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32), cfgp]
@@ -155,6 +183,46 @@ def gemm_plan(opA, opB, M, N, K, lda, ldb, ldc, dtype, a_addr=0, b_addr=0, c_add
     if check:
         _check(st, "gemm_plan")
     return st, out
+
+
+def _problem_array(problems):
+    if problems is None:
+        return None, 0
+    arr = (gemm_problem * max(len(problems), 1))(*problems)
+    return arr, len(problems)
+
+
+def gemm_grouped(opA, opB, dtype, problems, cfg: gemm_config | None = None, stream=None, check=True,
+                 count: int | None = None) -> int:
+    """All problems (a list of gemm_problem) in one persistent launch per 16 entries."""
+    arr, n = _problem_array(problems)
+    st = _load().gemm_grouped(opA, opB, dtype, arr, n if count is None else count,
+                              ctypes.byref(cfg) if cfg is not None else None, stream)
+    if check:
+        _check(st, "gemm_grouped")
+    return st
+
+
+def gemm_grouped_plan(opA, opB, dtype, problems, num_cus=256, arch="gfx950", req: gemm_config | None = None,
+                      check=True, count: int | None = None):
+    """Host-only: the configuration gemm_grouped would use. Returns (status, gemm_config)."""
+    arr, n = _problem_array(problems)
+    out = gemm_config()
+    st = _load().gemm_grouped_plan(opA, opB, dtype, arr, n if count is None else count, num_cus,
+                                   arch.encode() if arch is not None else None,
+                                   ctypes.byref(req) if req is not None else None, ctypes.byref(out))
+    if check:
+        _check(st, "gemm_grouped_plan")
+    return st, out
+
+
+def gemm_strided_batched(opA, opB, M, N, K, A, lda, stride_a, B, ldb, stride_b, C, ldc, stride_c, batch, dtype,
+                         cfg: gemm_config | None = None, stream=None, check=True) -> int:
+    st = _load().gemm_strided_batched(opA, opB, M, N, K, A, lda, stride_a, B, ldb, stride_b, C, ldc, stride_c,
+                                      batch, dtype, ctypes.byref(cfg) if cfg is not None else None, stream)
+    if check:
+        _check(st, "gemm_strided_batched")
+    return st
 
 
 def gemm_menu():

@@ -34,6 +34,19 @@ template <> __device__ __forceinline__ float decode<DT_BF16>(uint16_t x) {
     return __uint_as_float((uint32_t)x << 16);
 }
 
+// Raster of tile `bid` inside one problem of tiles_m x tiles_n tiles: groups of
+// `group_m` tile rows walked column by column (as tile_coords without the XCD
+// renumbering).
+__device__ __forceinline__ void raster(int bid, int tiles_m, int tiles_n, int group_m, int& tm, int& tn) {
+    const int per_group = group_m * tiles_n;
+    const int group = bid / per_group;
+    const int first_m = group * group_m;
+    const int rows = min(tiles_m - first_m, group_m);
+    const int in_group = bid - group * per_group;
+    tm = first_m + in_group % rows;
+    tn = in_group / rows;
+}
+
 // Map a linear workgroup id to a (tile row, tile column).
 //
 // Workgroups are handed to the 8 XCDs round-robin (id % 8), and each XCD has
@@ -48,14 +61,45 @@ __device__ __forceinline__ void tile_coords(const GemmArgs& g, int& tm, int& tn)
         const int per = nblk >> 3;
         bid = (bid & 7) * per + (bid >> 3);
     }
-    const int gm = g.group_m;
-    const int per_group = gm * g.tiles_n;
-    const int group = bid / per_group;
-    const int first_m = group * gm;
-    const int rows = min(g.tiles_m - first_m, gm);
-    const int in_group = bid - group * per_group;
-    tm = first_m + in_group % rows;
-    tn = in_group / rows;
+    raster(bid, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
+}
+
+// Persistent workgroup number of this workgroup: with xcd_remap the ids are
+// renumbered so that the workgroups of one XCD (hardware id mod 8) get a
+// contiguous block of numbers, hence tiles that are adjacent in linear order.
+__device__ __forceinline__ int persistent_id(int xcd_remap) {
+    int bid = blockIdx.x;
+    const int nblk = gridDim.x;
+    if (xcd_remap && (nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+    return bid;
+}
+
+// Linear tile t of a grouped launch -> the problem's arguments and tile
+// coordinates. The segment search is a short scalar loop over the table (the
+// role of the README's prefix-sum search in its grouped scheduler); ES is the
+// input element size in bytes.
+template <int ES>
+__device__ __forceinline__ void group_tile(const GroupArgs& ga, int t, GemmArgs& g, int& tm, int& tn) {
+    int s = 0;
+    while (s + 1 < ga.count && t >= ga.seg[s + 1].tile_begin) ++s;
+    const GroupSeg& sg = ga.seg[s];
+    const int per = sg.tiles_m * sg.tiles_n;
+    const int local = t - (int)sg.tile_begin;
+    const int b = local / per;
+    raster(local - b * per, sg.tiles_m, sg.tiles_n, sg.group_m, tm, tn);
+    g.A = static_cast<const char*>(sg.A) + (size_t)b * (size_t)sg.sa * ES;
+    g.B = static_cast<const char*>(sg.B) + (size_t)b * (size_t)sg.sb * ES;
+    g.C = sg.C + (size_t)b * (size_t)sg.sc;
+    g.lda = sg.lda;
+    g.ldb = sg.ldb;
+    g.ldc = sg.ldc;
+    g.M = sg.M;
+    g.N = sg.N;
+    g.K = sg.K;
+    g.tiles_m = sg.tiles_m;
+    g.tiles_n = sg.tiles_n;
+    g.group_m = sg.group_m;
+    g.xcd_remap = 0;
 }
 
 // Load V consecutive elements starting at p into a register chunk, zero-filling

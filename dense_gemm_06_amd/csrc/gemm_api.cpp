@@ -73,9 +73,183 @@ int launch(int id, const dg::GemmArgs& args, unsigned grid, hipStream_t s) {
     return rc;
 }
 
+int launch_grouped(int id, const dg::GroupArgs& args, unsigned grid, hipStream_t s) {
+    const dg::MenuEntry& e = dg::kMenu[id];
+    if (e.variant == dg::V_LDS) {
+        return e.dtype == dg::DT_F32 ? dg::launch_lds_f32_grouped(id, args, grid, s)
+               : e.dtype == dg::DT_F16 ? dg::launch_lds_f16_grouped(id, args, grid, s)
+                                       : dg::launch_lds_bf16_grouped(id, args, grid, s);
+    }
+    return e.dtype == dg::DT_F32 ? dg::launch_mfma_f32_grouped(id, args, grid, s)
+           : e.dtype == dg::DT_F16 ? dg::launch_mfma_f16_grouped(id, args, grid, s)
+                                   : dg::launch_mfma_bf16_grouped(id, args, grid, s);
+}
+
+// Byte extent of `batch` matrices of rows x cols (leading dimension ld) placed
+// `stride` elements apart, or 0 when it does not fit in the address space.
+uint64_t extent(int64_t batch, int64_t stride, int64_t rows, int64_t cols, int64_t ld, int64_t es) {
+    const unsigned __int128 n = (unsigned __int128)(batch - 1) * (uint64_t)stride + (unsigned __int128)(rows - 1) * (uint64_t)ld +
+                                (uint64_t)cols;
+    const unsigned __int128 bytes = n * (uint64_t)es;
+    return bytes >> 62 ? 0 : (uint64_t)bytes;
+}
+
 }  // namespace
 
 extern "C" {
+
+int gemm_grouped(int opA, int opB, int dtype, const gemm_problem* problems, int count, const gemm_config* cfg,
+                 void* stream) {
+    dg::clear_error();
+    if (count < 0) {
+        dg::set_error("count = %d must be non-negative", count);
+        return GEMM_ERR_INVALID_VALUE;
+    }
+    if (count == 0) return GEMM_OK;
+    if (problems == nullptr) {
+        dg::set_error("problems is NULL with count = %d", count);
+        return GEMM_ERR_NULL_POINTER;
+    }
+    struct Range { uintptr_t lo; uint64_t len; int index; };
+    std::vector<Range> outs, ins;
+    const int64_t es = dtype == GEMM_F32 ? 4 : 2;
+    int with_work = 0;
+    for (int i = 0; i < count; ++i) {
+        const gemm_problem& p = problems[i];
+        int st = dg::validate_problem(opA, opB, dtype, p, i);
+        if (st != GEMM_OK) return st;
+        if (p.M == 0 || p.N == 0 || p.batch == 0) continue;
+        if (p.batch >= ((int64_t)1 << 31)) {
+            dg::set_error("problem %d: batch = %lld must be below 2^31", i, (long long)p.batch);
+            return GEMM_ERR_UNSUPPORTED;
+        }
+        if (p.C == nullptr || (p.K > 0 && (p.A == nullptr || p.B == nullptr))) {
+            dg::set_error("problem %d: NULL operand: A = %p, B = %p, C = %p (M = %lld, N = %lld, K = %lld)", i, p.A,
+                          p.B, (void*)p.C, (long long)p.M, (long long)p.N, (long long)p.K);
+            return GEMM_ERR_NULL_POINTER;
+        }
+        const uint64_t clen = extent(p.batch, p.stride_c, p.M, p.N, p.ldc, 4);
+        uint64_t alen = 1, blen = 1;
+        if (p.K > 0) {
+            alen = extent(p.batch, p.stride_a, p.M, p.K, p.lda, es);
+            blen = opB == GEMM_OP_N ? extent(p.batch, p.stride_b, p.K, p.N, p.ldb, es)
+                                    : extent(p.batch, p.stride_b, p.N, p.K, p.ldb, es);
+        }
+        if (clen == 0 || alen == 0 || blen == 0) {
+            dg::set_error("problem %d: the operands' address ranges do not fit in 64 bits", i);
+            return GEMM_ERR_INVALID_VALUE;
+        }
+        outs.push_back({(uintptr_t)p.C, clen, i});
+        if (p.K > 0) {
+            ins.push_back({(uintptr_t)p.A, alen, i});
+            ins.push_back({(uintptr_t)p.B, blen, i});
+        }
+        ++with_work;
+    }
+    if (with_work == 0) return GEMM_OK;
+    for (size_t o = 0; o < outs.size(); ++o) {
+        for (const Range& r : ins)
+            if (ranges_overlap(outs[o].lo, outs[o].len, r.lo, r.len)) {
+                dg::set_error("the output of problem %d overlaps an input of problem %d", outs[o].index, r.index);
+                return GEMM_ERR_INVALID_VALUE;
+            }
+        for (size_t q = o + 1; q < outs.size(); ++q)
+            if (ranges_overlap(outs[o].lo, outs[o].len, outs[q].lo, outs[q].len)) {
+                dg::set_error("the outputs of problems %d and %d overlap", outs[o].index, outs[q].index);
+                return GEMM_ERR_INVALID_VALUE;
+            }
+    }
+    int dev = 0;
+    hipError_t he = hipGetDevice(&dev);
+    if (he != hipSuccess) {
+        dg::set_error("hipGetDevice failed: %s", hipGetErrorString(he));
+        return GEMM_ERR_DEVICE;
+    }
+    DeviceInfo info;
+    int st = device_info(dev, &info);
+    if (st != GEMM_OK) return st;
+    gemm_config plan;
+    st = dg::plan_grouped(opA, opB, dtype, problems, count, info.num_cus, info.arch, cfg, &plan);
+    if (st != GEMM_OK) return st;
+
+    // segment tables, at most kMaxGroupSegments per launch
+    std::vector<dg::GroupArgs> launches;
+    for (int i = 0; i < count; ++i) {
+        const gemm_problem& p = problems[i];
+        if (p.M == 0 || p.N == 0 || p.batch == 0) continue;
+        if (launches.empty() || launches.back().count == dg::kMaxGroupSegments) {
+            launches.emplace_back();
+            dg::GroupArgs& a = launches.back();
+            memset(&a, 0, sizeof a);
+        }
+        dg::GroupArgs& a = launches.back();
+        dg::GroupSeg& sg = a.seg[a.count++];
+        sg.A = p.A;
+        sg.B = p.B;
+        sg.C = p.C;
+        sg.sa = p.stride_a;
+        sg.sb = p.stride_b;
+        sg.sc = p.stride_c;
+        sg.lda = (int)p.lda;
+        sg.ldb = (int)p.ldb;
+        sg.ldc = (int)p.ldc;
+        sg.M = (int)p.M;
+        sg.N = (int)p.N;
+        sg.K = (int)p.K;
+        sg.batch = (int)p.batch;
+        sg.tiles_m = (int)((p.M + plan.bm - 1) / plan.bm);
+        sg.tiles_n = (int)((p.N + plan.bn - 1) / plan.bn);
+        const int gm = plan.group_m ? plan.group_m : dg::default_group_m(sg.tiles_m, sg.tiles_n);
+        sg.group_m = std::max(1, std::min(gm, sg.tiles_m));
+        sg.tile_begin = a.total_tiles;
+        a.total_tiles += sg.batch * sg.tiles_m * sg.tiles_n;  // < 2^31 in total (checked by the planner)
+    }
+    (void)hipGetLastError();  // clear a stale error left by earlier unrelated work
+    for (dg::GroupArgs& a : launches) {
+        const unsigned grid = (unsigned)std::min<int64_t>(a.total_tiles, plan.grid);
+        a.xcd_remap = plan.xcd_remap;
+        if (launch_grouped(plan.kernel_id, a, grid, (hipStream_t)stream) != 0) {
+            dg::set_error("internal: kernel %d has no grouped launcher", plan.kernel_id);
+            return GEMM_ERR_LAUNCH;
+        }
+        he = hipGetLastError();
+        if (he != hipSuccess) {
+            dg::set_error("grouped kernel launch failed: %s", hipGetErrorString(he));
+            return GEMM_ERR_LAUNCH;
+        }
+    }
+    return GEMM_OK;
+}
+
+int gemm_grouped_plan(int opA, int opB, int dtype, const gemm_problem* problems, int count, int num_cus,
+                      const char* arch, const gemm_config* request, gemm_config* out) {
+    dg::clear_error();
+    if (out == nullptr) {
+        dg::set_error("gemm_grouped_plan: out is NULL");
+        return GEMM_ERR_NULL_POINTER;
+    }
+    return dg::plan_grouped(opA, opB, dtype, problems, count, num_cus, arch, request, out);
+}
+
+int gemm_strided_batched(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                         int64_t stride_a, const void* B, int64_t ldb, int64_t stride_b, float* C, int64_t ldc,
+                         int64_t stride_c, int64_t batch, int dtype, const gemm_config* cfg, void* stream) {
+    gemm_problem p;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.A = A;
+    p.lda = lda;
+    p.stride_a = stride_a;
+    p.B = B;
+    p.ldb = ldb;
+    p.stride_b = stride_b;
+    p.C = C;
+    p.ldc = ldc;
+    p.stride_c = stride_c;
+    p.batch = batch;
+    return gemm_grouped(opA, opB, dtype, &p, 1, cfg, stream);
+}
 
 int gemm_ex(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
             int64_t ldb, float* C, int64_t ldc, int dtype, const gemm_config* cfg, void* stream) {

@@ -2,4 +2,5 @@
 #define DG_FAMILY_VARIANT dg::V_LDS
 #define DG_FAMILY_DTYPE dg::DT_F16
 #define DG_FAMILY_LAUNCH launch_lds_f16
+#define DG_FAMILY_LAUNCH_GROUPED launch_lds_f16_grouped
 #include "inst_family.inc"

@@ -14,7 +14,7 @@ namespace dg {
 // converted to fp32, with an XOR swizzle at float4 granularity on the transposed
 // stores.
 template <int DT, int OPB, bool VEC, int BM, int BN, int BK>
-__global__ __launch_bounds__(256) void lds_gemm(GemmArgs g) {
+__device__ __forceinline__ void lds_tile(const GemmArgs& g, int tm, int tn) {
     typedef typename Elem<DT>::type T;
     constexpr int V = Elem<DT>::vec;   // elements per 16-byte chunk
     constexpr int RA = BM / 64, RB = BN / 64;
@@ -30,8 +30,6 @@ __global__ __launch_bounds__(256) void lds_gemm(GemmArgs g) {
     __shared__ __attribute__((aligned(16))) float sB[2][BK * BN];
 
     const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-    int tm, tn;
-    tile_coords(g, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int M = g.M, N = g.N, K = g.K;
     const T* __restrict__ A = static_cast<const T*>(g.A);
@@ -174,6 +172,25 @@ __global__ __launch_bounds__(256) void lds_gemm(GemmArgs g) {
                 }
             }
         }
+}
+
+template <int DT, int OPB, bool VEC, int BM, int BN, int BK>
+__global__ __launch_bounds__(256) void lds_gemm(GemmArgs g) {
+    int tm, tn;
+    tile_coords(g, tm, tn);
+    lds_tile<DT, OPB, VEC, BM, BN, BK>(g, tm, tn);
+}
+
+// Persistent grouped form (see mfma16_gemm_grouped).
+template <int DT, int OPB, bool VEC, int BM, int BN, int BK>
+__global__ __launch_bounds__(256) void lds_gemm_grouped(GroupArgs ga) {
+    for (int t = persistent_id(ga.xcd_remap); t < ga.total_tiles; t += gridDim.x) {
+        GemmArgs g;
+        int tm, tn;
+        group_tile<(int)sizeof(typename Elem<DT>::type)>(ga, t, g, tm, tn);
+        __syncthreads();
+        lds_tile<DT, OPB, VEC, BM, BN, BK>(g, tm, tn);
+    }
 }
 
 }  // namespace dg

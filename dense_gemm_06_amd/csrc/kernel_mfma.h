@@ -18,9 +18,7 @@ namespace dg {
 // fp16 / bf16 inputs, v_mfma_f32_16x16x32: each lane supplies 8 consecutive k
 // of one row of P and one column of Q (k = 8(l/16) + slot).
 template <int DT, int OPB, bool VEC, int BM, int BN, int BK, int WM, int WN>
-__global__ __launch_bounds__(WM * WN * 64)
-__attribute__((amdgpu_waves_per_eu(1, (BM / WM) * (BN / WN) >= 128 * 128 ? 1 : 8)))
-void mfma16_gemm(GemmArgs g) {
+__device__ __forceinline__ void mfma16_tile(const GemmArgs& g, int tm, int tn) {
     constexpr int NT = WM * WN * 64;
     constexpr int TWM = BM / WM, TWN = BN / WN;  // wave tile
     constexpr int SM = TWM / 16, SN = TWN / 16;  // 16 x 16 subtiles per wave
@@ -38,8 +36,6 @@ void mfma16_gemm(GemmArgs g) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wmi = wave / WN, wni = wave % WN;
     const int l16 = lane & 15, lg = lane >> 4;
-    int tm, tn;
-    tile_coords(g, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int M = g.M, N = g.N, K = g.K;
     const uint16_t* __restrict__ A = static_cast<const uint16_t*>(g.A);
@@ -201,6 +197,31 @@ void mfma16_gemm(GemmArgs g) {
     }
 }
 
+template <int DT, int OPB, bool VEC, int BM, int BN, int BK, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64)
+__attribute__((amdgpu_waves_per_eu(1, (BM / WM) * (BN / WN) >= 128 * 128 ? 1 : 8)))
+void mfma16_gemm(GemmArgs g) {
+    int tm, tn;
+    tile_coords(g, tm, tn);
+    mfma16_tile<DT, OPB, VEC, BM, BN, BK, WM, WN>(g, tm, tn);
+}
+
+// Persistent grouped form: each workgroup takes linear tiles id, id + grid, ...
+// of all problems; the barrier before each tile keeps the previous tile's LDS
+// reads ahead of the next tile's LDS writes.
+template <int DT, int OPB, bool VEC, int BM, int BN, int BK, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64)
+__attribute__((amdgpu_waves_per_eu(1, (BM / WM) * (BN / WN) >= 128 * 128 ? 1 : 8)))
+void mfma16_gemm_grouped(GroupArgs ga) {
+    for (int t = persistent_id(ga.xcd_remap); t < ga.total_tiles; t += gridDim.x) {
+        GemmArgs g;
+        int tm, tn;
+        group_tile<2>(ga, t, g, tm, tn);
+        __syncthreads();
+        mfma16_tile<DT, OPB, VEC, BM, BN, BK, WM, WN>(g, tm, tn);
+    }
+}
+
 // fp32 inputs, v_mfma_f32_16x16x4_f32: each lane supplies one k of one row of P
 // and one column of Q per instruction. Four consecutive instructions (steps
 // s = 0..3) take k = 4(l/16) + s, so a lane reads one float4 along k of A (and
@@ -210,7 +231,7 @@ void mfma16_gemm(GemmArgs g) {
 // group holds the columns n = 4(l%16) + u, so the four subtiles share one read
 // and, at the store, a lane owns 16 consecutive n of one row of C.
 template <int OPB, bool VEC, int BM, int BN, int BK, int WM, int WN>
-__global__ __launch_bounds__(WM * WN * 64) void mfma32_gemm(GemmArgs g) {
+__device__ __forceinline__ void mfma32_tile(const GemmArgs& g, int tm, int tn) {
     constexpr int NT = WM * WN * 64;
     constexpr int TWM = BM / WM, TWN = BN / WN;
     constexpr int SM = TWM / 16, SN = TWN / 16, QN = TWN / 64;
@@ -228,8 +249,6 @@ __global__ __launch_bounds__(WM * WN * 64) void mfma32_gemm(GemmArgs g) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wmi = wave / WN, wni = wave % WN;
     const int l16 = lane & 15, lg = lane >> 4;
-    int tm, tn;
-    tile_coords(g, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int M = g.M, N = g.N, K = g.K;
     const float* __restrict__ A = static_cast<const float*>(g.A);
@@ -396,6 +415,24 @@ __global__ __launch_bounds__(WM * WN * 64) void mfma32_gemm(GemmArgs g) {
                 }
             }
         }
+    }
+}
+
+template <int OPB, bool VEC, int BM, int BN, int BK, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64) void mfma32_gemm(GemmArgs g) {
+    int tm, tn;
+    tile_coords(g, tm, tn);
+    mfma32_tile<OPB, VEC, BM, BN, BK, WM, WN>(g, tm, tn);
+}
+
+template <int OPB, bool VEC, int BM, int BN, int BK, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64) void mfma32_gemm_grouped(GroupArgs ga) {
+    for (int t = persistent_id(ga.xcd_remap); t < ga.total_tiles; t += gridDim.x) {
+        GemmArgs g;
+        int tm, tn;
+        group_tile<4>(ga, t, g, tm, tn);
+        __syncthreads();
+        mfma32_tile<OPB, VEC, BM, BN, BK, WM, WN>(g, tm, tn);
     }
 }
 

@@ -36,6 +36,13 @@ struct MenuEntry {
 // passed its parity tests on the device.
 constexpr bool schedule_enabled(int sched) { return sched != 3; }
 
+// Configurations that also have a grouped (persistent) form: the register-staged
+// schedule, which masks every edge, except the 4-wave 256 x 256 tiles (their
+// grouped form runs out of registers).
+constexpr bool grouped_capable(int sched, int bm, int bn, int wm, int wn) {
+    return sched == 1 && !(bm == 256 && bn == 256 && wm * wn == 4);
+}
+
 // X(id, variant, dtype, opb, vec, bm, bn, bk, wm, wn, tm, tn, threads, lds_bytes, sched)
 // The largest MFMA tile is 256 x 256 (2 x 4 waves) for 16-bit inputs and 256 x 128
 // (4 x 2 waves) for fp32; the fp32 kernel's 64 x 64 tile uses a 4 x 1 wave grid
@@ -117,6 +124,35 @@ struct GemmArgs {
     int tiles_m, tiles_n;   // ceil(M / bm), ceil(N / bn)
     int group_m;            // tile rows per raster group (L2 locality)
     int xcd_remap;          // 1: give each XCD a contiguous range of tiles
+};
+
+// Grouped launches ("Grouped Tile Scheduler" of the learn-cutedsl README, section
+// 8.4): one persistent grid walks the tiles of several problems. A segment is
+// `batch` problems of one shape whose operands sit at fixed element strides
+// (batch = 1 for a single problem); its tiles occupy linear tile indices
+// [tile_begin, tile_begin + batch * tiles_m * tiles_n). Segments with no tiles are
+// left out of the table, so tile_begin is strictly increasing.
+struct GroupSeg {
+    const void* A;
+    const void* B;
+    float* C;
+    int64_t sa, sb, sc;      // batch strides, in elements
+    int64_t tile_begin;
+    int lda, ldb, ldc;       // in elements (< 2^23, checked on the host)
+    int M, N, K, batch;
+    int tiles_m, tiles_n, group_m;
+};
+
+// The segment table travels in the kernel arguments (16 x 96 bytes); larger
+// groups are split over several launches by the host.
+constexpr int kMaxGroupSegments = 16;
+
+struct GroupArgs {
+    int count;          // segments in seg[]
+    int total_tiles;    // tiles of all segments
+    int xcd_remap;      // 1: give each XCD a contiguous block of persistent workgroups
+    int pad;
+    GroupSeg seg[kMaxGroupSegments];
 };
 
 }  // namespace dg

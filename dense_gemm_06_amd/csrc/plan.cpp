@@ -232,14 +232,191 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
     cfg.grid = (int32_t)(cfg.tiles_m * cfg.tiles_n);
     // Group enough tile rows that one XCD's share of the grid forms a compact
     // rectangle; the remap needs the grid to split evenly over the 8 XCDs.
-    int gm = want_group;
-    if (gm == 0) {
-        const int64_t per_xcd = std::max<int64_t>(1, cfg.grid / 8);
-        gm = 1;
-        while ((int64_t)gm * gm * 2 < per_xcd && gm < cfg.tiles_m) gm *= 2;
-    }
+    const int gm = want_group ? want_group : default_group_m(cfg.tiles_m, cfg.tiles_n);
     cfg.group_m = (int32_t)std::max<int64_t>(1, std::min<int64_t>(gm, cfg.tiles_m));
+    cfg.tiles_total = cfg.tiles_m * cfg.tiles_n;
+    cfg.launches = 1;
     cfg.xcd_remap = want_remap >= 0 ? want_remap : ((cfg.grid % 8 == 0 && cfg.grid >= 16) ? 1 : 0);
+    cfg.est_cycles = best_cost;
+    *out = cfg;
+    return GEMM_OK;
+}
+
+int default_group_m(int64_t tiles_m, int64_t tiles_n) {
+    const int64_t per_xcd = std::max<int64_t>(1, tiles_m * tiles_n / 8);
+    int gm = 1;
+    while ((int64_t)gm * gm * 2 < per_xcd && gm < tiles_m) gm *= 2;
+    return gm;
+}
+
+int validate_problem(int opA, int opB, int dtype, const gemm_problem& p, int index) {
+    int st = validate(opA, opB, p.M, p.N, p.K, p.lda, p.ldb, p.ldc, dtype);
+    if (st != GEMM_OK) {
+        const std::string why = g_last_error;
+        set_error("problem %d: %s", index, why.c_str());
+        return st;
+    }
+    if (p.batch < 0 || p.stride_a < 0 || p.stride_b < 0 || p.stride_c < 0) {
+        set_error("problem %d: batch (%lld) and strides (%lld, %lld, %lld) must be non-negative", index,
+                  (long long)p.batch, (long long)p.stride_a, (long long)p.stride_b, (long long)p.stride_c);
+        return GEMM_ERR_INVALID_VALUE;
+    }
+    if (p.ldc >= ((int64_t)1 << 31)) {
+        set_error("problem %d: ldc = %lld must be below 2^31 in a grouped call", index, (long long)p.ldc);
+        return GEMM_ERR_UNSUPPORTED;
+    }
+    if (p.batch > 1 && p.M > 0 && p.N > 0 && p.stride_c < (p.M - 1) * p.ldc + p.N) {
+        set_error("problem %d: stride_c = %lld is smaller than one output, (M-1)*ldc + N = %lld, so the batch's "
+                  "outputs would overlap", index, (long long)p.stride_c, (long long)((p.M - 1) * p.ldc + p.N));
+        return GEMM_ERR_INVALID_VALUE;
+    }
+    return GEMM_OK;
+}
+
+// Grouped heuristic: the same cost model as plan(), with the work of every
+// problem spread over the compute units the persistent grid occupies; a tile is
+// never split, so the longest tile bounds the estimate from below.
+int plan_grouped(int opA, int opB, int dtype, const gemm_problem* probs, int count, int num_cus, const char* arch,
+                 const gemm_config* req, gemm_config* out) {
+    if (count < 0) {
+        set_error("count = %d must be non-negative", count);
+        return GEMM_ERR_INVALID_VALUE;
+    }
+    if (count > 0 && probs == nullptr) {
+        set_error("problems is NULL with count = %d", count);
+        return GEMM_ERR_NULL_POINTER;
+    }
+    for (int i = 0; i < count; ++i) {
+        const int st = validate_problem(opA, opB, dtype, probs[i], i);
+        if (st != GEMM_OK) return st;
+    }
+    if (arch == nullptr || strncmp(arch, "gfx950", 6) != 0) {
+        set_error("device architecture '%s' is not gfx950; the kernels are built for gfx950 only",
+                  arch ? arch : "(null)");
+        return GEMM_ERR_DEVICE;
+    }
+    if (num_cus <= 0) {
+        set_error("compute-unit count %d must be positive", num_cus);
+        return GEMM_ERR_INVALID_VALUE;
+    }
+    const int es = elem_size(dtype);
+    bool vec_ok = true;
+    for (int i = 0; i < count; ++i) {
+        const gemm_problem& p = probs[i];
+        if (p.M == 0 || p.N == 0 || p.batch == 0) continue;
+        const bool strided = p.batch > 1;
+        vec_ok = vec_ok && aligned16((uintptr_t)p.A) && aligned16((uintptr_t)p.B) && (p.lda * es) % 16 == 0 &&
+                 (p.ldb * es) % 16 == 0 && (!strided || ((p.stride_a * es) % 16 == 0 && (p.stride_b * es) % 16 == 0));
+    }
+    int want_variant = GEMM_VARIANT_AUTO, want_bm = 0, want_bn = 0, want_vec = -1, want_remap = -1, want_group = 0;
+    int want_wm = 0, want_wn = 0, want_sched = 0, want_grid = 0;
+    if (req) {
+        want_variant = req->variant;
+        want_bm = req->bm;
+        want_bn = req->bn;
+        want_vec = req->vec;
+        want_remap = req->xcd_remap;
+        want_group = req->group_m;
+        want_wm = req->waves_m;
+        want_wn = req->waves_n;
+        want_sched = req->schedule;
+        want_grid = req->max_grid;
+        if (want_variant < 0 || want_variant > 2 || want_vec < -1 || want_vec > 1 || want_remap < -1 || want_remap > 1 ||
+            want_group < 0 || want_bm < 0 || want_bn < 0 || want_wm < 0 || want_wn < 0 || want_sched < 0 ||
+            want_grid < 0) {
+            set_error("invalid requested configuration (variant %d, bm %d, bn %d, vec %d, xcd_remap %d, group_m %d, "
+                      "max_grid %d)", want_variant, want_bm, want_bn, want_vec, want_remap, want_group, want_grid);
+            return GEMM_ERR_INVALID_VALUE;
+        }
+        if (want_sched > 1) {
+            set_error("schedule %d has no grouped form; grouped calls run the register-staged schedule (1)",
+                      want_sched);
+            return GEMM_ERR_UNSUPPORTED;
+        }
+        if (want_vec == 1 && !vec_ok) {
+            set_error("16-byte loads requested but some base, leading dimension or batch stride is not 16-byte "
+                      "aligned");
+            return GEMM_ERR_UNSUPPORTED;
+        }
+    }
+    const MenuEntry* best = nullptr;
+    double best_cost = 0;
+    int64_t best_tiles = 0, best_grid = 0;
+    for (const MenuEntry& e : kMenu) {
+        if (e.dtype != dtype || e.opb != opB) continue;
+        if (!grouped_capable(e.sched, e.bm, e.bn, e.wm, e.wn)) continue;
+        if (want_variant != GEMM_VARIANT_AUTO && e.variant != want_variant) continue;
+        if (want_bm && e.bm != want_bm) continue;
+        if (want_bn && e.bn != want_bn) continue;
+        if (want_wm && (e.variant == V_MFMA ? e.wm : 1) != want_wm) continue;
+        if (want_wn && (e.variant == V_MFMA ? e.wn : 1) != want_wn) continue;
+        const int vec = want_vec >= 0 ? want_vec : (vec_ok ? 1 : 0);
+        if (e.vec != vec) continue;
+        int64_t tiles = 0;
+        double work = 0, longest = 0;
+        for (int i = 0; i < count; ++i) {
+            const gemm_problem& p = probs[i];
+            if (p.M == 0 || p.N == 0 || p.batch == 0) continue;
+            const int64_t t = p.batch * ((p.M + e.bm - 1) / e.bm) * ((p.N + e.bn - 1) / e.bn);
+            const int64_t kpad = std::max<int64_t>(((p.K + e.bk - 1) / e.bk) * e.bk, e.bk);
+            const double tc = 2.0 * e.bm * e.bn * (double)kpad / (rate_per_cu(e) * tile_efficiency(e));
+            tiles += t;
+            work += (double)t * tc;
+            longest = std::max(longest, tc);
+        }
+        int64_t grid = std::min<int64_t>(tiles, (int64_t)num_cus * blocks_per_cu(e));
+        if (want_grid) grid = std::min<int64_t>(grid, want_grid);
+        const double cost = tiles == 0 ? 0 : std::max(work / (double)std::min<int64_t>(grid, num_cus), longest);
+        if (!best || cost < best_cost * (1 - 1e-9) ||
+            (cost <= best_cost * (1 + 1e-9) && e.bm * e.bn > best->bm * best->bn)) {
+            best = &e;
+            best_cost = cost;
+            best_tiles = tiles;
+            best_grid = grid;
+        }
+    }
+    if (!best) {
+        set_error("no compiled grouped kernel matches: dtype %s, opB %s, variant %d, bm %d, bn %d, vec %d",
+                  dtype_name(dtype), opB == GEMM_OP_N ? "N" : "T", want_variant, want_bm, want_bn, want_vec);
+        return GEMM_ERR_UNSUPPORTED;
+    }
+    // linear tile indices and the persistent loop's t + grid stay below 2^31
+    if (best_tiles >= ((int64_t)1 << 31) - ((int64_t)1 << 16)) {
+        set_error("%lld output tiles in one grouped call; at most 2^31 - 2^16 are supported", (long long)best_tiles);
+        return GEMM_ERR_UNSUPPORTED;
+    }
+    const MenuEntry& e = *best;
+    gemm_config cfg;
+    memset(&cfg, 0, sizeof cfg);
+    cfg.variant = e.variant;
+    cfg.bm = e.bm;
+    cfg.bn = e.bn;
+    cfg.bk = e.bk;
+    cfg.vec = e.vec;
+    cfg.waves_m = e.variant == V_MFMA ? e.wm : 1;
+    cfg.waves_n = e.variant == V_MFMA ? e.wn : 1;
+    cfg.thread_m = e.tm;
+    cfg.thread_n = e.tn;
+    cfg.threads = e.threads;
+    cfg.lds_bytes = e.lds_bytes;
+    cfg.kernel_id = e.id;
+    cfg.schedule = e.sched;
+    int segments = 0;
+    for (int i = 0; i < count; ++i) {
+        const gemm_problem& p = probs[i];
+        if (p.M == 0 || p.N == 0 || p.batch == 0) continue;
+        if (segments == 0) {
+            cfg.tiles_m = (p.M + e.bm - 1) / e.bm;
+            cfg.tiles_n = (p.N + e.bn - 1) / e.bn;
+        }
+        ++segments;
+    }
+    cfg.group_m = want_group;  // 0: per problem, default_group_m
+    cfg.grid = (int32_t)best_grid;
+    cfg.max_grid = want_grid;
+    cfg.xcd_remap = want_remap >= 0 ? want_remap : ((cfg.grid % 8 == 0 && cfg.grid >= 16) ? 1 : 0);
+    cfg.tiles_total = best_tiles;
+    cfg.launches = (segments + kMaxGroupSegments - 1) / kMaxGroupSegments;
     cfg.est_cycles = best_cost;
     *out = cfg;
     return GEMM_OK;

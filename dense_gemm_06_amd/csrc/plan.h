@@ -20,4 +20,11 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
          gemm_config* out);
 int menu_entry(int index, int* variant, int* dtype, int* opb, gemm_config* out);
 
+// Validation of one grouped entry (the gemm_ex rules plus batch and strides).
+int validate_problem(int opA, int opB, int dtype, const gemm_problem& p, int index);
+// Tile-row group size the planner uses for a problem of tiles_m x tiles_n tiles.
+int default_group_m(int64_t tiles_m, int64_t tiles_n);
+int plan_grouped(int opA, int opB, int dtype, const gemm_problem* probs, int count, int num_cus, const char* arch,
+                 const gemm_config* req, gemm_config* out);
+
 }  // namespace dg

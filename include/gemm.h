@@ -92,8 +92,11 @@ typedef struct gemm_config {
                           GEMM_ERR_UNSUPPORTED); 4 ping-pong on 32x32x16 MFMAs (2-4: MFMA,
                           16-bit inputs, M and N multiples of 256, K a multiple of 32, 16-byte
                           aligned operands) */
-    int64_t tiles_m, tiles_n; /* out */
+    int64_t tiles_m, tiles_n; /* out (grouped: of the first non-empty problem) */
     double est_cycles; /* out: the heuristic's cost estimate (clock cycles) */
+    int64_t tiles_total; /* out: output tiles of the call (grouped: of all its problems) */
+    int32_t launches;    /* out: kernel launches the call makes */
+    int32_t max_grid;    /* in (grouped calls only): cap on persistent workgroups per launch, 0 = any */
 } gemm_config;
 
 /*
@@ -123,6 +126,58 @@ int gemm_ex(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A, in
 int gemm_plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
               int dtype, uintptr_t a_addr, uintptr_t b_addr, uintptr_t c_addr, int num_cus, const char* arch,
               const gemm_config* request, gemm_config* out);
+
+/*
+ * Grouped and batched products: several independent C = A @ B in one launch
+ * ("Grouped Tile Scheduler", learn-cutedsl README section 8.4: the tiles of all
+ * problems form one linear index space that a persistent grid walks, each
+ * workgroup mapping a linear tile back to its problem by searching the problems'
+ * tile offsets; section 8.1's static persistent scheduler strides every
+ * workgroup through that space by the grid size).
+ *
+ * One gemm_problem entry describes `batch` problems of one shape: problem b
+ * (0 <= b < batch) reads A + b*stride_a, B + b*stride_b and writes
+ * C + b*stride_c (strides in ELEMENTS of the operand's type, >= 0). A single
+ * problem is batch = 1 (strides ignored). Every problem follows the conventions
+ * above (row-major A, opB for B, fp32 C overwritten, degenerate shapes, the same
+ * leading-dimension rules, plus ldc < 2^31); dtype, opA and opB are common to all.
+ */
+typedef struct gemm_problem {
+    int64_t M, N, K;
+    const void* A;
+    int64_t lda, stride_a;
+    const void* B;
+    int64_t ldb, stride_b;
+    float* C;
+    int64_t ldc, stride_c;
+    int64_t batch; /* problems in this entry (0 = none) */
+} gemm_problem;
+
+/*
+ * gemm_grouped -- every problem of problems[0..count) in one kernel launch (more
+ * than 16 entries with work are split over several launches on `stream`, in
+ * order). problems is a HOST array read during the call only; the operand
+ * pointers in it are device pointers. Outputs must not overlap each other or any
+ * input (checked over each entry's whole address range, batch included:
+ * GEMM_ERR_INVALID_VALUE); within an entry with batch > 1, stride_c must be at
+ * least (M-1)*ldc + N. count == 0, or entries without output elements, are
+ * no-ops. Only the register-staged configurations (schedule 1) run grouped; cfg
+ * restricts the choice as for gemm_ex, and cfg->max_grid caps the persistent grid.
+ * Errors as for gemm_ex: everything is validated before the first launch.
+ */
+int gemm_grouped(int opA, int opB, int dtype, const gemm_problem* problems, int count, const gemm_config* cfg,
+                 void* stream);
+
+/* gemm_grouped_plan -- host-only: the configuration gemm_grouped would use (the
+ * operand pointers of `problems` are used for their alignment only). */
+int gemm_grouped_plan(int opA, int opB, int dtype, const gemm_problem* problems, int count, int num_cus,
+                      const char* arch, const gemm_config* request, gemm_config* out);
+
+/* gemm_strided_batched -- gemm_grouped of one entry: `batch` problems of one
+ * shape at fixed element strides. */
+int gemm_strided_batched(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                         int64_t stride_a, const void* B, int64_t ldb, int64_t stride_b, float* C, int64_t ldc,
+                         int64_t stride_c, int64_t batch, int dtype, const gemm_config* cfg, void* stream);
 
 /* Number of compiled kernel configurations, and entry i of that menu (GEMM_OK, or
  * GEMM_ERR_INVALID_VALUE for an index out of range). Host-only. */

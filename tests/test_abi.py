@@ -33,7 +33,8 @@ def declared_functions():
 def test_header_symbols_exported():
     names = declared_functions()
     assert set(names) == {"gemm", "gemm_ex", "gemm_plan", "gemm_menu_size", "gemm_menu_entry",
-                          "gemm_device_info", "gemm_status_string", "gemm_last_error"}
+                          "gemm_device_info", "gemm_status_string", "gemm_last_error",
+                          "gemm_grouped", "gemm_grouped_plan", "gemm_strided_batched"}
     lib = dg.library()
     for n in names:
         assert hasattr(lib, n), n
@@ -195,3 +196,110 @@ def test_gemm_rejects_before_device_access():
     with pytest.raises(dg.GemmError) as ei:
         dg.gemm(4, 4, 4, 0, 4, 0x2000, 4, 0x3000, 4, f32)
     assert ei.value.status == dg.GEMM_ERR_NULL_POINTER and "NULL operand" in str(ei.value)
+
+
+# ----------------------------------------------------------------------------- grouped calls
+def gp(M, N, K, a=1 << 20, b=1 << 24, c=1 << 28, lda=None, ldb=None, ldc=None, batch=1, sa=0, sb=0, sc=0,
+       op_b="N"):
+    lda = lda if lda is not None else max(1, K)
+    ldb = ldb if ldb is not None else (max(1, N) if op_b == "N" else max(1, K))
+    ldc = ldc if ldc is not None else max(1, N)
+    return dg.problem(M, N, K, a, lda, b, ldb, c, ldc, batch=batch, stride_a=sa, stride_b=sb, stride_c=sc)
+
+
+def distinct(shapes, dtype_size=4):
+    """Problems at far-apart fake addresses (planning uses addresses for alignment only)."""
+    return [gp(M, N, K, a=(i + 1) << 32, b=(i + 1) << 33, c=(i + 1) << 34) for i, (M, N, K) in enumerate(shapes)]
+
+
+def test_grouped_plan_counts_tiles_and_launches():
+    probs = distinct([(256, 256, 256)] * 4)
+    st, c = dg.gemm_grouped_plan(0, 0, dg.GEMM_F32, probs)
+    assert st == 0 and c.schedule == 1 and c.launches == 1
+    assert c.tiles_total == 4 * c.tiles_m * c.tiles_n and 0 < c.grid <= c.tiles_total
+    st, c = dg.gemm_grouped_plan(0, 0, dg.GEMM_F16, distinct([(100, 90, 80)] * 33))
+    assert st == 0 and c.launches == 3
+    # empty problems take no segment and no tile
+    st, c = dg.gemm_grouped_plan(0, 0, dg.GEMM_F16, distinct([(0, 90, 80), (100, 0, 80), (100, 90, 80)]))
+    assert st == 0 and c.launches == 1 and c.tiles_total == c.tiles_m * c.tiles_n
+    st, c = dg.gemm_grouped_plan(0, 0, dg.GEMM_F16, [])
+    assert st == 0 and c.launches == 0 and c.tiles_total == 0
+
+
+def test_grouped_plan_never_picks_full_tile_schedules():
+    for dt in (dg.GEMM_F16, dg.GEMM_BF16):
+        st, c = dg.gemm_grouped_plan(0, 0, dt, distinct([(4096, 4096, 4096)]))
+        assert st == 0 and c.schedule == 1 and not (c.bm == 256 and c.bn == 256 and c.waves_m * c.waves_n == 4)
+        st, _ = dg.gemm_grouped_plan(0, 0, dt, distinct([(4096, 4096, 4096)]), req=dg.request(schedule=2),
+                                     check=False)
+        assert st == dg.GEMM_ERR_UNSUPPORTED
+
+
+def test_grouped_plan_max_grid_and_vec():
+    probs = distinct([(512, 512, 64)] * 4)
+    st, c = dg.gemm_grouped_plan(0, 0, dg.GEMM_F32, probs, req=dg.request(max_grid=5))
+    assert st == 0 and c.grid == 5
+    assert dg.gemm_grouped_plan(0, 0, dg.GEMM_F32, probs)[1].vec == 1
+    # one unaligned batch stride turns the 16-byte path off for the whole call
+    odd = probs + [gp(64, 64, 64, a=1 << 40, b=1 << 41, c=1 << 42, batch=2, sa=64 * 64 + 1, sb=4096, sc=4096)]
+    assert dg.gemm_grouped_plan(0, 0, dg.GEMM_F32, odd)[1].vec == 0
+    st, _ = dg.gemm_grouped_plan(0, 0, dg.GEMM_F32, odd, req=dg.request(vec=1), check=False)
+    assert st == dg.GEMM_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(M=-1), dg.GEMM_ERR_INVALID_VALUE),
+    (dict(lda=3), dg.GEMM_ERR_INVALID_VALUE),          # lda < K
+    (dict(batch=-2), dg.GEMM_ERR_INVALID_VALUE),
+    (dict(sa=-1), dg.GEMM_ERR_INVALID_VALUE),
+    (dict(batch=2, sc=10), dg.GEMM_ERR_INVALID_VALUE),  # batch outputs would overlap
+    (dict(ldc=1 << 31), dg.GEMM_ERR_UNSUPPORTED),
+])
+def test_grouped_validation(bad, status):
+    kw = dict(M=16, N=16, K=16)
+    kw.update(bad)
+    probs = [gp(16, 16, 16)] + [gp(**kw, a=1 << 36, b=1 << 37, c=1 << 38)]
+    st, _ = dg.gemm_grouped_plan(0, 0, dg.GEMM_F32, probs, check=False)
+    assert st == status
+    assert "problem 1" in dg.gemm_last_error()
+    # the device entry point rejects the same arguments before touching any device
+    assert dg.gemm_grouped(0, 0, dg.GEMM_F32, probs, check=False) == status
+
+
+def test_grouped_rejects_without_device_access():
+    assert dg.gemm_grouped(0, 0, dg.GEMM_F32, [], check=False) == dg.GEMM_OK
+    assert dg.gemm_grouped(0, 0, dg.GEMM_F32, None, count=2, check=False) == dg.GEMM_ERR_NULL_POINTER
+    assert dg.gemm_grouped(0, 0, dg.GEMM_F32, [gp(4, 4, 4)], count=-1, check=False) == dg.GEMM_ERR_INVALID_VALUE
+    # a problem without output elements is a no-op even with NULL operands
+    assert dg.gemm_grouped(0, 0, dg.GEMM_F32, [gp(0, 4, 4, a=0, b=0, c=0)], check=False) == dg.GEMM_OK
+    assert dg.gemm_grouped(0, 0, dg.GEMM_F32, [gp(4, 4, 4, c=0)], check=False) == dg.GEMM_ERR_NULL_POINTER
+    # K = 0 needs no inputs
+    two = [gp(4, 4, 4), gp(4, 4, 0, a=0, b=0, c=0)]
+    assert dg.gemm_grouped(0, 0, dg.GEMM_F32, two, check=False) == dg.GEMM_ERR_NULL_POINTER
+
+
+@pytest.mark.parametrize("case", ["c_over_own_a", "c_over_other_b", "outputs_overlap", "batch_reaches_input"])
+def test_grouped_rejects_overlaps(case):
+    base = 1 << 30
+    p0 = gp(64, 64, 64, a=base, b=base + (1 << 20), c=base + (2 << 20))
+    if case == "c_over_own_a":
+        p0 = gp(64, 64, 64, a=base, b=base + (1 << 20), c=base + 64)
+        probs = [p0]
+    elif case == "c_over_other_b":
+        probs = [p0, gp(64, 64, 64, a=base + (3 << 20), b=base + (4 << 20), c=base + (1 << 20) + 128)]
+    elif case == "outputs_overlap":
+        probs = [p0, gp(64, 64, 64, a=base + (3 << 20), b=base + (4 << 20), c=base + (2 << 20) + 256)]
+    else:
+        # the last output of a batch reaches into the next problem's A
+        probs = [gp(64, 64, 64, a=base, b=base + (1 << 20), c=base + (2 << 20), batch=4, sc=1 << 18),
+                 gp(64, 64, 64, a=base + (2 << 20) + 3 * (1 << 18) * 4 + 100, b=base + (5 << 20), c=base + (6 << 20))]
+    assert dg.gemm_grouped(0, 0, dg.GEMM_F32, probs, check=False) == dg.GEMM_ERR_INVALID_VALUE
+    assert "overlap" in dg.gemm_last_error()
+
+
+def test_strided_batched_is_one_grouped_entry():
+    st = dg.gemm_strided_batched(0, 0, 8, 8, 8, 1 << 20, 8, 64, 1 << 24, 8, 64, 1 << 28, 8, 4, 3, dg.GEMM_F32,
+                                 check=False)
+    assert st == dg.GEMM_ERR_INVALID_VALUE and "stride_c" in dg.gemm_last_error()
+    assert dg.gemm_strided_batched(0, 0, 8, 8, 8, 0, 8, 64, 0, 8, 64, 0, 8, 64, 0, dg.GEMM_F32,
+                                   check=False) == dg.GEMM_OK
