@@ -80,8 +80,15 @@ def device_problem(name, seed=0):
     return ops, A, B, C
 
 
-def time_problem(name, steps, warmup):
-    """Warm up, then time exactly `steps` launches with HIP events on the launch stream."""
+WORKSPACE_CAP = 256 << 20   # workspace offered to split-K runs
+
+
+def time_problem(name, steps, warmup, workspace=False):
+    """Warm up, then time exactly `steps` calls with HIP events on the launch stream.
+
+    workspace=True runs gemm_ex_workspace with up to WORKSPACE_CAP bytes (the
+    heuristic may split K; a split call is two kernels, the product and the
+    reduction, both inside the timed step)."""
     import torch
     import dense_gemm_06_amd as dg
     ops, A, B, C = device_problem(name)
@@ -90,10 +97,16 @@ def time_problem(name, steps, warmup):
     args = (dg.GEMM_OP_N, dg.OP_CODE[ops.op_b], ops.M, ops.N, ops.K, A.data_ptr(), ops.lda, B.data_ptr(), ops.ldb,
             C.data_ptr(), ops.N, dg.DTYPE_CODE[ops.dtype])
     cus, arch = dg.gemm_device_info(0)
-    _, cfg = dg.gemm_plan(args[0], args[1], ops.M, ops.N, ops.K, ops.lda, ops.ldb, ops.N, args[-1],
-                          A.data_ptr(), B.data_ptr(), C.data_ptr(), cus, arch)
+    _, cfg = dg.gemm_plan_workspace(args[0], args[1], ops.M, ops.N, ops.K, ops.lda, ops.ldb, ops.N, args[-1],
+                                    A.data_ptr(), B.data_ptr(), C.data_ptr(), cus, arch,
+                                    WORKSPACE_CAP if workspace else 0)
+    if workspace and cfg.workspace_bytes > 0:
+        W = torch.empty(cfg.workspace_bytes // 4, dtype=torch.float32, device="cuda")
+        call = lambda: dg.gemm_ex_workspace(*args, None, W.data_ptr(), cfg.workspace_bytes, s)
+    else:
+        call = lambda: dg.gemm_ex(*args, None, s)
     for _ in range(warmup):
-        dg.gemm_ex(*args, None, s)
+        call()
     torch.cuda.synchronize()
     # whole job: K launches back to back between two events
     e0 = torch.cuda.Event(enable_timing=True)
@@ -101,7 +114,7 @@ def time_problem(name, steps, warmup):
     t0 = time.perf_counter()
     e0.record(stream)
     for _ in range(steps):
-        dg.gemm_ex(*args, None, s)
+        call()
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -292,6 +305,19 @@ def main():
                                      "tile": f"{v['cfg'].bm}x{v['cfg'].bn}",
                                      "variant": "mfma" if v["cfg"].variant == 2 else "lds"}
                                  for k, v in extras.items()}
+        # the under-filled problems again with a workspace (the heuristic may split K),
+        # and a long-K problem with 16 output tiles, where splitting pays
+        lk = time_problem("k1_f32_long_k", max(5, a.steps // 2), max(2, a.warmup // 2))
+        out["other_problems"]["k1_f32_long_k"] = {
+            "workload": "C=A@B 256x256x16384 f32", "tflops": round(lk["tflops"], 3),
+            "ms_per_step": round(lk["ms_per_step"], 6), "frac_of_peak": round(lk["tflops"] / lk["peak"], 4),
+            "tile": f"{lk['cfg'].bm}x{lk['cfg'].bn}", "variant": "mfma" if lk["cfg"].variant == 2 else "lds"}
+        for name in ("c1_f32_256", "c2_f32_1024", "k1_f32_long_k"):
+            r = time_problem(name, max(5, a.steps // 2), max(2, a.warmup // 2), workspace=True)
+            out["other_problems"][name]["with_workspace"] = {
+                "tflops": round(r["tflops"], 3), "ms_per_step": round(r["ms_per_step"], 6),
+                "frac_of_peak": round(r["tflops"] / r["peak"], 4), "split_k": r["cfg"].split_k,
+                "tile": f"{r['cfg'].bm}x{r['cfg'].bn}", "workspace_bytes": r["cfg"].workspace_bytes}
     if not a.no_extra and not a.only:
         grouped = {}
         for name in GROUPED:

@@ -1,7 +1,7 @@
 """Python binding of the MI355X dense GEMM library (libdensegemm.so).
 
 The functions mirror the C ABI in include/gemm.h one to one (gemm, gemm_ex,
-gemm_plan, gemm_grouped, gemm_grouped_plan, gemm_strided_batched,
+gemm_ex_workspace, gemm_plan, gemm_plan_workspace, gemm_grouped, gemm_grouped_plan, gemm_strided_batched,
 gemm_menu_size / gemm_menu_entry, gemm_device_info, gemm_status_string,
 gemm_last_error) and only marshal arguments: every step of the product runs in
 the library's HIP kernels. A nonzero status raises
@@ -48,6 +48,7 @@ class gemm_config(ctypes.Structure):
         ("tiles_m", ctypes.c_int64), ("tiles_n", ctypes.c_int64),
         ("est_cycles", ctypes.c_double),
         ("tiles_total", ctypes.c_int64), ("launches", ctypes.c_int32), ("max_grid", ctypes.c_int32),
+        ("split_k", ctypes.c_int32), ("k_chunk", ctypes.c_int32), ("workspace_bytes", ctypes.c_int64),
     ]
 
     def as_dict(self) -> dict:
@@ -56,11 +57,11 @@ class gemm_config(ctypes.Structure):
 
 def request(variant: int = GEMM_VARIANT_AUTO, bm: int = 0, bn: int = 0, vec: int = -1,
             xcd_remap: int = -1, group_m: int = 0, waves_m: int = 0, waves_n: int = 0,
-            schedule: int = 0, max_grid: int = 0) -> gemm_config:
+            schedule: int = 0, max_grid: int = 0, split_k: int = 0) -> gemm_config:
     """A gemm_config with only the "in" fields set (0 / -1: heuristic decides)."""
     c = gemm_config()
     c.variant, c.bm, c.bn, c.vec, c.xcd_remap, c.group_m = variant, bm, bn, vec, xcd_remap, group_m
-    c.waves_m, c.waves_n, c.schedule, c.max_grid = waves_m, waves_n, schedule, max_grid
+    c.waves_m, c.waves_n, c.schedule, c.max_grid, c.split_k = waves_m, waves_n, schedule, max_grid, split_k
     return c
 
 
@@ -116,6 +117,11 @@ def _load():
     lib.gemm_plan.argtypes = [i32, i32, i64, i64, i64, i64, i64, i64, i32, ctypes.c_size_t, ctypes.c_size_t,
                               ctypes.c_size_t, i32, ctypes.c_char_p, cfgp, cfgp]
     lib.gemm_plan.restype = i32
+    lib.gemm_ex_workspace.argtypes = [i32, i32, i64, i64, i64, vp, i64, vp, i64, vp, i64, i32, cfgp, vp, i64, vp]
+    lib.gemm_ex_workspace.restype = i32
+    lib.gemm_plan_workspace.argtypes = [i32, i32, i64, i64, i64, i64, i64, i64, i32, ctypes.c_size_t,
+                                        ctypes.c_size_t, ctypes.c_size_t, i32, ctypes.c_char_p, i64, cfgp, cfgp]
+    lib.gemm_plan_workspace.restype = i32
     probp = ctypes.POINTER(gemm_problem)
     lib.gemm_grouped.argtypes = [i32, i32, i32, probp, i32, cfgp, vp]
     lib.gemm_grouped.restype = i32
@@ -171,6 +177,28 @@ def gemm_ex(opA, opB, M, N, K, A, lda, B, ldb, C, ldc, dtype, cfg: gemm_config |
     if check:
         _check(st, "gemm_ex")
     return st
+
+
+def gemm_ex_workspace(opA, opB, M, N, K, A, lda, B, ldb, C, ldc, dtype, cfg: gemm_config | None = None,
+                      workspace=None, workspace_bytes=0, stream=None, check=True) -> int:
+    """gemm_ex with a device workspace (split K when it pays; see include/gemm.h)."""
+    st = _load().gemm_ex_workspace(opA, opB, M, N, K, A, lda, B, ldb, C, ldc, dtype,
+                                   ctypes.byref(cfg) if cfg is not None else None, workspace, workspace_bytes, stream)
+    if check:
+        _check(st, "gemm_ex_workspace")
+    return st
+
+
+def gemm_plan_workspace(opA, opB, M, N, K, lda, ldb, ldc, dtype, a_addr=0, b_addr=0, c_addr=0, num_cus=256,
+                        arch="gfx950", workspace_bytes=0, req: gemm_config | None = None, check=True):
+    """Host-only: the configuration gemm_ex_workspace would launch. Returns (status, gemm_config)."""
+    out = gemm_config()
+    st = _load().gemm_plan_workspace(opA, opB, M, N, K, lda, ldb, ldc, dtype, a_addr, b_addr, c_addr, num_cus,
+                                     arch.encode() if arch is not None else None, workspace_bytes,
+                                     ctypes.byref(req) if req is not None else None, ctypes.byref(out))
+    if check:
+        _check(st, "gemm_plan_workspace")
+    return st, out
 
 
 def gemm_plan(opA, opB, M, N, K, lda, ldb, ldc, dtype, a_addr=0, b_addr=0, c_addr=0, num_cus=256,

@@ -64,6 +64,22 @@ __device__ __forceinline__ void tile_coords(const GemmArgs& g, int& tm, int& tn)
     raster(bid, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
 }
 
+// Narrow the arguments to this workgroup's K slice (grid y) of a split-K launch:
+// A and B advance by the slice's first k, K becomes the slice length, and the
+// output is the slice's plane of the workspace. ES is the input element size.
+template <int ES, int OPB>
+__device__ __forceinline__ void k_slice(GemmArgs& g) {
+    if (g.k_split > 1) {
+        const int s = blockIdx.y;
+        const int kbeg = s * g.k_chunk;
+        g.A = static_cast<const char*>(g.A) + (size_t)kbeg * ES;
+        g.B = static_cast<const char*>(g.B) + (OPB == 0 ? (size_t)kbeg * (size_t)g.ldb : (size_t)kbeg) * ES;
+        g.K = min(g.K - kbeg, g.k_chunk);
+        g.C = g.work + (size_t)s * (size_t)g.work_slice;
+        g.ldc = g.work_ld;
+    }
+}
+
 // Persistent workgroup number of this workgroup: with xcd_remap the ids are
 // renumbered so that the workgroups of one XCD (hardware id mod 8) get a
 // contiguous block of numbers, hence tiles that are adjacent in linear order.
@@ -100,6 +116,7 @@ __device__ __forceinline__ void group_tile(const GroupArgs& ga, int t, GemmArgs&
     g.tiles_n = sg.tiles_n;
     g.group_m = sg.group_m;
     g.xcd_remap = 0;
+    g.k_split = 1;
 }
 
 // Load V consecutive elements starting at p into a register chunk, zero-filling

@@ -58,17 +58,17 @@ bool ranges_overlap(uintptr_t a, uint64_t alen, uintptr_t b, uint64_t blen) {
     return a < b + blen && b < a + alen;
 }
 
-int launch(int id, const dg::GemmArgs& args, unsigned grid, hipStream_t s) {
+int launch(int id, const dg::GemmArgs& args, unsigned grid, unsigned grid_y, hipStream_t s) {
     const dg::MenuEntry& e = dg::kMenu[id];
     int rc = -1;
     if (e.variant == dg::V_LDS) {
-        rc = e.dtype == dg::DT_F32 ? dg::launch_lds_f32(id, args, grid, s)
-             : e.dtype == dg::DT_F16 ? dg::launch_lds_f16(id, args, grid, s)
-                                     : dg::launch_lds_bf16(id, args, grid, s);
+        rc = e.dtype == dg::DT_F32 ? dg::launch_lds_f32(id, args, grid, grid_y, s)
+             : e.dtype == dg::DT_F16 ? dg::launch_lds_f16(id, args, grid, grid_y, s)
+                                     : dg::launch_lds_bf16(id, args, grid, grid_y, s);
     } else {
-        rc = e.dtype == dg::DT_F32 ? dg::launch_mfma_f32(id, args, grid, s)
-             : e.dtype == dg::DT_F16 ? dg::launch_mfma_f16(id, args, grid, s)
-                                     : dg::launch_mfma_bf16(id, args, grid, s);
+        rc = e.dtype == dg::DT_F32 ? dg::launch_mfma_f32(id, args, grid, grid_y, s)
+             : e.dtype == dg::DT_F16 ? dg::launch_mfma_f16(id, args, grid, grid_y, s)
+                                     : dg::launch_mfma_bf16(id, args, grid, grid_y, s);
     }
     return rc;
 }
@@ -251,11 +251,20 @@ int gemm_strided_batched(int opA, int opB, int64_t M, int64_t N, int64_t K, cons
     return gemm_grouped(opA, opB, dtype, &p, 1, cfg, stream);
 }
 
-int gemm_ex(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
-            int64_t ldb, float* C, int64_t ldc, int dtype, const gemm_config* cfg, void* stream) {
+int gemm_ex_workspace(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                      const void* B, int64_t ldb, float* C, int64_t ldc, int dtype, const gemm_config* cfg,
+                      void* workspace, int64_t workspace_bytes, void* stream) {
     dg::clear_error();
     int st = dg::validate(opA, opB, M, N, K, lda, ldb, ldc, dtype);
     if (st != GEMM_OK) return st;
+    if (workspace_bytes < 0) {
+        dg::set_error("workspace_bytes = %lld must be non-negative", (long long)workspace_bytes);
+        return GEMM_ERR_INVALID_VALUE;
+    }
+    if (workspace_bytes > 0 && workspace == nullptr) {
+        dg::set_error("workspace is NULL with workspace_bytes = %lld", (long long)workspace_bytes);
+        return GEMM_ERR_NULL_POINTER;
+    }
     if (M == 0 || N == 0) return GEMM_OK;
     if (C == nullptr || (K > 0 && (A == nullptr || B == nullptr))) {
         dg::set_error("NULL operand: A = %p, B = %p, C = %p (M = %lld, N = %lld, K = %lld)", A, B, (void*)C,
@@ -273,6 +282,23 @@ int gemm_ex(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A, in
             return GEMM_ERR_INVALID_VALUE;
         }
     }
+    if (workspace_bytes > 0) {
+        // the whole declared workspace: aligned, and disjoint from every operand
+        const uintptr_t w = (uintptr_t)workspace;
+        if ((w & 15) != 0) {
+            dg::set_error("the workspace must be 16-byte aligned (got %p)", workspace);
+            return GEMM_ERR_INVALID_VALUE;
+        }
+        const uint64_t alen = K > 0 ? ((uint64_t)(M - 1) * lda + K) * es : 0;
+        const uint64_t blen =
+            K > 0 ? (opB == GEMM_OP_N ? (uint64_t)(K - 1) * ldb + N : (uint64_t)(N - 1) * ldb + K) * es : 0;
+        if (ranges_overlap(w, (uint64_t)workspace_bytes, (uintptr_t)A, alen) ||
+            ranges_overlap(w, (uint64_t)workspace_bytes, (uintptr_t)B, blen) ||
+            ranges_overlap(w, (uint64_t)workspace_bytes, (uintptr_t)C, clen)) {
+            dg::set_error("the workspace overlaps A, B or C");
+            return GEMM_ERR_INVALID_VALUE;
+        }
+    }
     int dev = 0;
     hipError_t he = hipGetDevice(&dev);
     if (he != hipSuccess) {
@@ -284,7 +310,7 @@ int gemm_ex(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A, in
     if (st != GEMM_OK) return st;
     gemm_config plan;
     st = dg::plan(opA, opB, M, N, K, lda, ldb, ldc, dtype, (uintptr_t)A, (uintptr_t)B, (uintptr_t)C, info.num_cus,
-                  info.arch, cfg, &plan);
+                  info.arch, workspace_bytes, cfg, &plan);
     if (st != GEMM_OK) return st;
 
     dg::GemmArgs args;
@@ -301,17 +327,30 @@ int gemm_ex(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A, in
     args.tiles_n = (int)plan.tiles_n;
     args.group_m = plan.group_m;
     args.xcd_remap = plan.xcd_remap;
+    args.k_split = plan.split_k;
+    args.k_chunk = plan.k_chunk;
+    args.work = static_cast<float*>(workspace);
+    args.work_ld = (N + 3) / 4 * 4;
+    args.work_slice = M * args.work_ld;
     (void)hipGetLastError();  // clear a stale error left by earlier unrelated work
-    if (launch(plan.kernel_id, args, (unsigned)plan.grid, (hipStream_t)stream) != 0) {
+    if (launch(plan.kernel_id, args, (unsigned)plan.grid, (unsigned)plan.split_k, (hipStream_t)stream) != 0) {
         dg::set_error("internal: kernel %d has no launcher", plan.kernel_id);
         return GEMM_ERR_LAUNCH;
     }
+    if (plan.split_k > 1)
+        dg::launch_splitk_reduce(args.work, plan.split_k, args.work_slice, args.work_ld, (int)M, (int)N, C, ldc,
+                                 (hipStream_t)stream);
     he = hipGetLastError();
     if (he != hipSuccess) {
         dg::set_error("kernel launch failed: %s", hipGetErrorString(he));
         return GEMM_ERR_LAUNCH;
     }
     return GEMM_OK;
+}
+
+int gemm_ex(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+            int64_t ldb, float* C, int64_t ldc, int dtype, const gemm_config* cfg, void* stream) {
+    return gemm_ex_workspace(opA, opB, M, N, K, A, lda, B, ldb, C, ldc, dtype, cfg, nullptr, 0, stream);
 }
 
 int gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb, float* C,
@@ -327,7 +366,20 @@ int gemm_plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, in
         dg::set_error("gemm_plan: out is NULL");
         return GEMM_ERR_NULL_POINTER;
     }
-    return dg::plan(opA, opB, M, N, K, lda, ldb, ldc, dtype, a_addr, b_addr, c_addr, num_cus, arch, request, out);
+    return dg::plan(opA, opB, M, N, K, lda, ldb, ldc, dtype, a_addr, b_addr, c_addr, num_cus, arch, 0, request,
+                    out);
+}
+
+int gemm_plan_workspace(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                        int dtype, uintptr_t a_addr, uintptr_t b_addr, uintptr_t c_addr, int num_cus,
+                        const char* arch, int64_t workspace_bytes, const gemm_config* request, gemm_config* out) {
+    dg::clear_error();
+    if (out == nullptr) {
+        dg::set_error("gemm_plan_workspace: out is NULL");
+        return GEMM_ERR_NULL_POINTER;
+    }
+    return dg::plan(opA, opB, M, N, K, lda, ldb, ldc, dtype, a_addr, b_addr, c_addr, num_cus, arch,
+                    workspace_bytes, request, out);
 }
 
 int gemm_menu_size(void) { return dg::kMenuSize; }

@@ -176,6 +176,7 @@ __device__ __forceinline__ void lds_tile(const GemmArgs& g, int tm, int tn) {
 
 template <int DT, int OPB, bool VEC, int BM, int BN, int BK>
 __global__ __launch_bounds__(256) void lds_gemm(GemmArgs g) {
+    k_slice<(int)sizeof(typename Elem<DT>::type), OPB>(g);
     int tm, tn;
     tile_coords(g, tm, tn);
     lds_tile<DT, OPB, VEC, BM, BN, BK>(g, tm, tn);

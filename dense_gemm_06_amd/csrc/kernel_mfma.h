@@ -201,6 +201,7 @@ template <int DT, int OPB, bool VEC, int BM, int BN, int BK, int WM, int WN>
 __global__ __launch_bounds__(WM * WN * 64)
 __attribute__((amdgpu_waves_per_eu(1, (BM / WM) * (BN / WN) >= 128 * 128 ? 1 : 8)))
 void mfma16_gemm(GemmArgs g) {
+    k_slice<2, OPB>(g);
     int tm, tn;
     tile_coords(g, tm, tn);
     mfma16_tile<DT, OPB, VEC, BM, BN, BK, WM, WN>(g, tm, tn);
@@ -420,6 +421,7 @@ __device__ __forceinline__ void mfma32_tile(const GemmArgs& g, int tm, int tn) {
 
 template <int OPB, bool VEC, int BM, int BN, int BK, int WM, int WN>
 __global__ __launch_bounds__(WM * WN * 64) void mfma32_gemm(GemmArgs g) {
+    k_slice<4, OPB>(g);
     int tm, tn;
     tile_coords(g, tm, tn);
     mfma32_tile<OPB, VEC, BM, BN, BK, WM, WN>(g, tm, tn);

@@ -6,14 +6,15 @@
 
 namespace dg {
 
-// Enqueue kernel `id` with `grid` workgroups on `stream`. Returns 0, or -1 if
-// `id` does not belong to the family.
-int launch_lds_f32(int id, const GemmArgs& a, unsigned grid, hipStream_t stream);
-int launch_lds_f16(int id, const GemmArgs& a, unsigned grid, hipStream_t stream);
-int launch_lds_bf16(int id, const GemmArgs& a, unsigned grid, hipStream_t stream);
-int launch_mfma_f32(int id, const GemmArgs& a, unsigned grid, hipStream_t stream);
-int launch_mfma_f16(int id, const GemmArgs& a, unsigned grid, hipStream_t stream);
-int launch_mfma_bf16(int id, const GemmArgs& a, unsigned grid, hipStream_t stream);
+// Enqueue kernel `id` with grid (grid, grid_y) on `stream`; grid_y > 1 is a
+// split-K launch (register-staged kernels only). Returns 0, or -1 if `id` does
+// not belong to the family (or cannot split).
+int launch_lds_f32(int id, const GemmArgs& a, unsigned grid, unsigned grid_y, hipStream_t stream);
+int launch_lds_f16(int id, const GemmArgs& a, unsigned grid, unsigned grid_y, hipStream_t stream);
+int launch_lds_bf16(int id, const GemmArgs& a, unsigned grid, unsigned grid_y, hipStream_t stream);
+int launch_mfma_f32(int id, const GemmArgs& a, unsigned grid, unsigned grid_y, hipStream_t stream);
+int launch_mfma_f16(int id, const GemmArgs& a, unsigned grid, unsigned grid_y, hipStream_t stream);
+int launch_mfma_bf16(int id, const GemmArgs& a, unsigned grid, unsigned grid_y, hipStream_t stream);
 
 // Grouped persistent launches (schedule-1 entries only; -1 for any other id).
 int launch_lds_f32_grouped(int id, const GroupArgs& a, unsigned grid, hipStream_t stream);
@@ -22,5 +23,10 @@ int launch_lds_bf16_grouped(int id, const GroupArgs& a, unsigned grid, hipStream
 int launch_mfma_f32_grouped(int id, const GroupArgs& a, unsigned grid, hipStream_t stream);
 int launch_mfma_f16_grouped(int id, const GroupArgs& a, unsigned grid, hipStream_t stream);
 int launch_mfma_bf16_grouped(int id, const GroupArgs& a, unsigned grid, hipStream_t stream);
+
+// C[i][j] = sum over s = 0..S-1, in that order, of work[s * slice + i * work_ld + j]
+// for i < M, j < N: the fixed-order reduction of a split-K launch.
+int launch_splitk_reduce(const float* work, int S, int64_t slice, int64_t work_ld, int M, int N, float* C,
+                         int64_t ldc, hipStream_t stream);
 
 }  // namespace dg

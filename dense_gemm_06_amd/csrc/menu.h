@@ -124,6 +124,12 @@ struct GemmArgs {
     int tiles_m, tiles_n;   // ceil(M / bm), ceil(N / bn)
     int group_m;            // tile rows per raster group (L2 locality)
     int xcd_remap;          // 1: give each XCD a contiguous range of tiles
+    // Split K (register-staged kernels only): k_split > 1 slices of k_chunk
+    // elements; slice blockIdx.y writes its partial product of C to
+    // work + y * work_slice with leading dimension work_ld instead of to C.
+    int k_split, k_chunk;
+    float* work;
+    int64_t work_slice, work_ld;
 };
 
 // Grouped launches ("Grouped Tile Scheduler" of the learn-cutedsl README, section

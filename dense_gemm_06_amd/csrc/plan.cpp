@@ -130,9 +130,12 @@ static int blocks_per_cu(const MenuEntry& e) {
 
 static bool aligned16(uintptr_t a) { return (a & 15) == 0; }
 
+// Workspace of an S-slice split: one fp32 plane of M x round_up(N, 4) per slice.
+static int64_t split_workspace(int64_t S, int64_t M, int64_t N) { return S * M * ((N + 3) / 4 * 4) * 4; }
+
 int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int dtype,
-         uintptr_t a, uintptr_t b, uintptr_t c, int num_cus, const char* arch, const gemm_config* req,
-         gemm_config* out) {
+         uintptr_t a, uintptr_t b, uintptr_t c, int num_cus, const char* arch, int64_t ws_bytes,
+         const gemm_config* req, gemm_config* out) {
     (void)c;
     int st = validate(opA, opB, M, N, K, lda, ldb, ldc, dtype);
     if (st != GEMM_OK) return st;
@@ -149,8 +152,17 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
     const bool vec_ok = aligned16(a) && aligned16(b) && (lda * es) % 16 == 0 && (ldb * es) % 16 == 0;
 
     int want_variant = GEMM_VARIANT_AUTO, want_bm = 0, want_bn = 0, want_vec = -1, want_remap = -1, want_group = 0;
-    int want_wm = 0, want_wn = 0, want_sched = 0;
+    int want_wm = 0, want_wn = 0, want_sched = 0, want_split = 0;
+    if (ws_bytes < 0) {
+        set_error("workspace_bytes = %lld must be non-negative", (long long)ws_bytes);
+        return GEMM_ERR_INVALID_VALUE;
+    }
     if (req) {
+        want_split = req->split_k;
+        if (want_split < 0) {
+            set_error("split_k = %d must be non-negative", want_split);
+            return GEMM_ERR_INVALID_VALUE;
+        }
         want_variant = req->variant;
         want_bm = req->bm;
         want_bn = req->bn;
@@ -179,6 +191,7 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
 
     const MenuEntry* best = nullptr;
     double best_cost = 0;
+    int64_t best_split = 1, best_chunk = K, short_ws = -1;
     for (const MenuEntry& e : kMenu) {
         if (e.dtype != dtype || e.opb != opB) continue;
         if (want_variant != GEMM_VARIANT_AUTO && e.variant != want_variant) continue;
@@ -193,18 +206,52 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
         const int vec = want_vec >= 0 ? want_vec : (vec_ok ? 1 : 0);
         if (e.vec != vec) continue;
         const int64_t tiles = ((M + e.bm - 1) / e.bm) * ((N + e.bn - 1) / e.bn);
-        const int64_t kpad = ((K + e.bk - 1) / e.bk) * e.bk;
+        const int64_t ktiles = (K + e.bk - 1) / e.bk;
         const int occ = blocks_per_cu(e);
         const int64_t concurrent = (int64_t)num_cus * occ;
-        const int64_t rounds = (tiles + concurrent - 1) / concurrent;
-        const int64_t resident = std::min<int64_t>(occ, (tiles + num_cus - 1) / num_cus);
-        const double tile_cycles = 2.0 * e.bm * e.bn * std::max<int64_t>(kpad, e.bk) / (rate_per_cu(e) * tile_efficiency(e));
-        const double cost = (double)rounds * (double)std::max<int64_t>(resident, 1) * tile_cycles;
-        if (!best || cost < best_cost * (1 - 1e-9) ||
-            (cost <= best_cost * (1 + 1e-9) && e.bm * e.bn > best->bm * best->bn)) {
-            best = &e;
-            best_cost = cost;
+        // split candidates: none, or S slices of whole k-tiles (register-staged kernels)
+        const int cand[] = {1, 2, 4, 8, 16};
+        for (int ci = 0; ci < (want_split >= 2 ? 1 : 5); ++ci) {
+            const int S = want_split >= 2 ? want_split : cand[ci];
+            if (want_split == 1 && S != 1) continue;
+            int64_t slices = 1, chunk = K;
+            if (S > 1) {
+                if (e.sched != 1 || ktiles < 2) continue;
+                const int64_t chunk_tiles = (ktiles + S - 1) / S;
+                slices = (ktiles + chunk_tiles - 1) / chunk_tiles;
+                chunk = chunk_tiles * e.bk;
+                if (slices < 2) continue;
+                const int64_t need = split_workspace(slices, M, N);
+                if (need > ws_bytes) {
+                    if (want_split >= 2) short_ws = std::max(short_ws, need);
+                    continue;
+                }
+            }
+            const int64_t work = tiles * slices;
+            const int64_t rounds = (work + concurrent - 1) / concurrent;
+            const int64_t resident = std::min<int64_t>(occ, (work + num_cus - 1) / num_cus);
+            const int64_t kpad = ((std::min<int64_t>(chunk, K) + e.bk - 1) / e.bk) * e.bk;
+            const double tile_cycles =
+                2.0 * e.bm * e.bn * std::max<int64_t>(kpad, e.bk) / (rate_per_cu(e) * tile_efficiency(e));
+            double cost = (double)rounds * (double)std::max<int64_t>(resident, 1) * tile_cycles;
+            // the reduction reads every plane and writes C, and is a second launch;
+            // measured at 256^3 and 1024^3 fp32, a split costs about 16000 cycles
+            // beyond its traffic (about 1 KB per clock for a kernel of this size),
+            // so it pays only when few tiles face a long K
+            if (slices > 1) cost += (double)(slices + 1) * (double)M * (double)N * 4.0 / 1024.0 + 16000.0;
+            if (!best || cost < best_cost * (1 - 1e-9) ||
+                (cost <= best_cost * (1 + 1e-9) && e.bm * e.bn > best->bm * best->bn)) {
+                best = &e;
+                best_cost = cost;
+                best_split = slices;
+                best_chunk = chunk;
+            }
         }
+    }
+    if (!best && short_ws > 0) {
+        set_error("split_k = %d needs %lld bytes of workspace; %lld were given", want_split, (long long)short_ws,
+                  (long long)ws_bytes);
+        return GEMM_ERR_INVALID_VALUE;
     }
     if (!best) {
         set_error("no compiled kernel matches: dtype %s, opB %s, variant %d, bm %d, bn %d, vec %d",
@@ -235,7 +282,10 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
     const int gm = want_group ? want_group : default_group_m(cfg.tiles_m, cfg.tiles_n);
     cfg.group_m = (int32_t)std::max<int64_t>(1, std::min<int64_t>(gm, cfg.tiles_m));
     cfg.tiles_total = cfg.tiles_m * cfg.tiles_n;
-    cfg.launches = 1;
+    cfg.launches = best_split > 1 ? 2 : 1;
+    cfg.split_k = (int32_t)best_split;
+    cfg.k_chunk = (int32_t)best_chunk;
+    cfg.workspace_bytes = best_split > 1 ? split_workspace(best_split, M, N) : 0;
     cfg.xcd_remap = want_remap >= 0 ? want_remap : ((cfg.grid % 8 == 0 && cfg.grid >= 16) ? 1 : 0);
     cfg.est_cycles = best_cost;
     *out = cfg;
@@ -333,6 +383,10 @@ int plan_grouped(int opA, int opB, int dtype, const gemm_problem* probs, int cou
                       want_sched);
             return GEMM_ERR_UNSUPPORTED;
         }
+        if (req->split_k > 1) {
+            set_error("grouped calls do not split K (split_k = %d)", req->split_k);
+            return GEMM_ERR_UNSUPPORTED;
+        }
         if (want_vec == 1 && !vec_ok) {
             set_error("16-byte loads requested but some base, leading dimension or batch stride is not 16-byte "
                       "aligned");
@@ -417,6 +471,7 @@ int plan_grouped(int opA, int opB, int dtype, const gemm_problem* probs, int cou
     cfg.xcd_remap = want_remap >= 0 ? want_remap : ((cfg.grid % 8 == 0 && cfg.grid >= 16) ? 1 : 0);
     cfg.tiles_total = best_tiles;
     cfg.launches = (segments + kMaxGroupSegments - 1) / kMaxGroupSegments;
+    cfg.split_k = 1;
     cfg.est_cycles = best_cost;
     *out = cfg;
     return GEMM_OK;

@@ -15,9 +15,10 @@ const char* last_error();
 
 int validate(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
              int dtype);
+// ws_bytes: workspace available for split K (0: never split).
 int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int dtype,
-         uintptr_t a, uintptr_t b, uintptr_t c, int num_cus, const char* arch, const gemm_config* req,
-         gemm_config* out);
+         uintptr_t a, uintptr_t b, uintptr_t c, int num_cus, const char* arch, int64_t ws_bytes,
+         const gemm_config* req, gemm_config* out);
 int menu_entry(int index, int* variant, int* dtype, int* opb, gemm_config* out);
 
 // Validation of one grouped entry (the gemm_ex rules plus batch and strides).

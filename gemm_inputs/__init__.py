@@ -171,7 +171,13 @@ CONFIGS = {
     "c5_bf16_ragged": dict(M=3001, N=5003, K=1037, dtype="bf16", dist="normal", op_b="T"),
 }
 
+# Further workloads for the rows beyond the five problems: a long-K product with
+# few output tiles (the case split K is for).
+EXTRA_CONFIGS = {
+    "k1_f32_long_k": dict(M=256, N=256, K=16384, dtype="f32", dist="uniform", op_b="N"),
+}
+
 
 def make_config(name: str, seed: int = 0) -> Operands:
-    c = CONFIGS[name]
+    c = CONFIGS[name] if name in CONFIGS else EXTRA_CONFIGS[name]
     return make_operands(c["M"], c["N"], c["K"], dtype=c["dtype"], dist=c["dist"], seed=seed, op_b=c["op_b"])

@@ -97,6 +97,10 @@ typedef struct gemm_config {
     int64_t tiles_total; /* out: output tiles of the call (grouped: of all its problems) */
     int32_t launches;    /* out: kernel launches the call makes */
     int32_t max_grid;    /* in (grouped calls only): cap on persistent workgroups per launch, 0 = any */
+    int32_t split_k;     /* in/out: K slices; in: 0 = heuristic, 1 = no split, S >= 2 = S slices (fewer
+                            if K has fewer k-tiles); splitting needs a workspace (gemm_ex_workspace) */
+    int32_t k_chunk;     /* out: K elements per slice (K when not split) */
+    int64_t workspace_bytes; /* out: workspace the configuration uses (0 when not split) */
 } gemm_config;
 
 /*
@@ -126,6 +130,32 @@ int gemm_ex(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A, in
 int gemm_plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
               int dtype, uintptr_t a_addr, uintptr_t b_addr, uintptr_t c_addr, int num_cus, const char* arch,
               const gemm_config* request, gemm_config* out);
+
+/*
+ * gemm_ex_workspace -- gemm_ex with a caller-provided device workspace, which
+ * allows split K: the K range is cut into S slices that run as separate
+ * workgroups (grid y), each writing its partial product to its own plane of the
+ * workspace, and a second kernel adds the planes in slice order into C. The sum
+ * order is fixed, so results are reproducible call to call (they differ from the
+ * unsplit kernel's by rounding). This fills the machine when M x N has few tiles
+ * (the "few blocks" case of "GPU architecture and mapping kernels", section 12.9,
+ * and its exercise on a minimum block count). The heuristic splits only if the
+ * estimate improves and the workspace suffices; cfg->split_k forces a choice.
+ * workspace_bytes = 0 (workspace may be NULL) behaves as gemm_ex. Otherwise the
+ * workspace must be 16-byte aligned and its whole declared range must not overlap
+ * A, B or C (GEMM_ERR_INVALID_VALUE, checked before any launch); its contents
+ * are scratch, and calls that share a workspace must be ordered (one stream). A split needs S * M * round_up(N, 4) * 4 bytes (gemm_plan_workspace
+ * reports the amount as workspace_bytes).
+ */
+int gemm_ex_workspace(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                      const void* B, int64_t ldb, float* C, int64_t ldc, int dtype, const gemm_config* cfg,
+                      void* workspace, int64_t workspace_bytes, void* stream);
+
+/* gemm_plan_workspace -- host-only: the configuration gemm_ex_workspace would use
+ * with workspace_bytes of workspace (gemm_plan is this with 0). */
+int gemm_plan_workspace(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                        int dtype, uintptr_t a_addr, uintptr_t b_addr, uintptr_t c_addr, int num_cus,
+                        const char* arch, int64_t workspace_bytes, const gemm_config* request, gemm_config* out);
 
 /*
  * Grouped and batched products: several independent C = A @ B in one launch

@@ -34,7 +34,8 @@ def test_header_symbols_exported():
     names = declared_functions()
     assert set(names) == {"gemm", "gemm_ex", "gemm_plan", "gemm_menu_size", "gemm_menu_entry",
                           "gemm_device_info", "gemm_status_string", "gemm_last_error",
-                          "gemm_grouped", "gemm_grouped_plan", "gemm_strided_batched"}
+                          "gemm_grouped", "gemm_grouped_plan", "gemm_strided_batched",
+                          "gemm_ex_workspace", "gemm_plan_workspace"}
     lib = dg.library()
     for n in names:
         assert hasattr(lib, n), n
@@ -303,3 +304,68 @@ def test_strided_batched_is_one_grouped_entry():
     assert st == dg.GEMM_ERR_INVALID_VALUE and "stride_c" in dg.gemm_last_error()
     assert dg.gemm_strided_batched(0, 0, 8, 8, 8, 0, 8, 64, 0, 8, 64, 0, 8, 64, 0, dg.GEMM_F32,
                                    check=False) == dg.GEMM_OK
+
+
+# ----------------------------------------------------------------------------- split K
+def wplan(M, N, K, dtype="f32", ws=1 << 30, req=None, check=True):
+    return dg.gemm_plan_workspace(0, 0, M, N, K, max(1, K), max(1, N), max(1, N), dg.DTYPE_CODE[dtype], 4096, 4096,
+                                  4096, 256, "gfx950", ws, req, check=check)
+
+
+def test_split_needs_workspace():
+    """Without workspace nothing splits; with it, an under-filled problem splits."""
+    assert plan(256, 256, 16384, "f32")[1].split_k == 1
+    st, c = wplan(256, 256, 16384)
+    assert st == 0 and c.split_k > 1 and c.schedule == 1 and c.launches == 2
+    assert c.workspace_bytes == c.split_k * 256 * 256 * 4
+    assert c.k_chunk % c.bk == 0 and (c.split_k - 1) * c.k_chunk < 16384 <= c.split_k * c.k_chunk
+    # a machine-filling problem, or a short K, does not split (the reduction would cost more)
+    assert wplan(4096, 4096, 4096, "f16")[1].split_k == 1
+    assert wplan(256, 256, 256)[1].split_k == 1
+    assert wplan(1024, 1024, 1024)[1].split_k == 1
+
+
+def test_split_forced_and_clamped():
+    st, c = wplan(200, 300, 1000, req=dg.request(split_k=3))
+    assert st == 0 and c.split_k == 3
+    # more slices than k-tiles: as many slices as k-tiles
+    st, c = wplan(200, 300, 70, req=dg.request(split_k=8, bm=64, bn=64, variant=dg.GEMM_VARIANT_MFMA))
+    assert st == 0 and c.split_k == 3 and c.k_chunk == 32
+    # split_k = 1 forbids splitting even with workspace
+    assert wplan(256, 256, 256, req=dg.request(split_k=1))[1].split_k == 1
+    # workspace rows are padded to 4 floats
+    st, c = wplan(10, 6, 4096, req=dg.request(split_k=4))
+    assert st == 0 and c.workspace_bytes == 4 * 10 * 8 * 4
+
+
+def test_split_errors():
+    st, _ = wplan(256, 256, 256, ws=1000, req=dg.request(split_k=4), check=False)
+    assert st == dg.GEMM_ERR_INVALID_VALUE and "workspace" in dg.gemm_last_error()
+    st, _ = wplan(256, 256, 256, req=dg.request(split_k=-1), check=False)
+    assert st == dg.GEMM_ERR_INVALID_VALUE
+    st, _ = wplan(256, 256, 256, ws=-5, check=False)
+    assert st == dg.GEMM_ERR_INVALID_VALUE
+    # the ping-pong schedule does not split
+    st, _ = wplan(4096, 4096, 4096, "f16", req=dg.request(schedule=2, split_k=2), check=False)
+    assert st == dg.GEMM_ERR_UNSUPPORTED
+    # grouped calls do not split
+    st, _ = dg.gemm_grouped_plan(0, 0, dg.GEMM_F32, [gp(64, 64, 64)], req=dg.request(split_k=2), check=False)
+    assert st == dg.GEMM_ERR_UNSUPPORTED
+    # rejected before any device access
+    ex = dg.library().gemm_ex_workspace
+    assert ex(0, 0, 8, 8, 8, 1 << 20, 8, 1 << 21, 8, 1 << 22, 8, 0, None, None, -1, None) == dg.GEMM_ERR_INVALID_VALUE
+    assert ex(0, 0, 8, 8, 8, 1 << 20, 8, 1 << 21, 8, 1 << 22, 8, 0, None, None, 64, None) == dg.GEMM_ERR_NULL_POINTER
+    assert ex(0, 0, 0, 8, 8, 0, 8, 0, 8, 0, 8, 0, None, None, 0, None) == dg.GEMM_OK
+
+
+def test_split_workspace_rejections_before_device():
+    """Workspace checks cover the whole declared range and run before any device access."""
+    ex = dg.library().gemm_ex_workspace
+    A, B, C = 1 << 30, (1 << 30) + (1 << 22), (1 << 30) + (2 << 22)
+    args = (0, 0, 256, 256, 256, A, 256, B, 256, C, 256, 0, None)
+    W = (1 << 30) + (8 << 22)
+    assert ex(*args, W + 4, 1 << 22, None) == dg.GEMM_ERR_INVALID_VALUE
+    assert "aligned" in dg.gemm_last_error()
+    for w in (A, B + 1024 * 16, C - (1 << 20)):
+        assert ex(*args, w, 4 << 20, None) == dg.GEMM_ERR_INVALID_VALUE
+        assert "overlaps" in dg.gemm_last_error()
