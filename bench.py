@@ -87,8 +87,8 @@ def time_problem(name, steps, warmup, workspace=False):
     """Warm up, then time exactly `steps` calls with HIP events on the launch stream.
 
     workspace=True runs gemm_ex_workspace with up to WORKSPACE_CAP bytes (the
-    heuristic may split K; a split call is two kernels, the product and the
-    reduction, both inside the timed step)."""
+    heuristic may split K or pack the operands; such a call is two kernels, both
+    inside the timed step)."""
     import torch
     import dense_gemm_06_amd as dg
     ops, A, B, C = device_problem(name)
@@ -312,11 +312,13 @@ def main():
             "workload": "C=A@B 256x256x16384 f32", "tflops": round(lk["tflops"], 3),
             "ms_per_step": round(lk["ms_per_step"], 6), "frac_of_peak": round(lk["tflops"] / lk["peak"], 4),
             "tile": f"{lk['cfg'].bm}x{lk['cfg'].bn}", "variant": "mfma" if lk["cfg"].variant == 2 else "lds"}
-        for name in ("c1_f32_256", "c2_f32_1024", "k1_f32_long_k"):
+        # (and the unaligned ragged problem, which the heuristic packs into aligned whole tiles)
+        for name in ("c1_f32_256", "c2_f32_1024", "k1_f32_long_k", "c5_bf16_ragged"):
             r = time_problem(name, max(5, a.steps // 2), max(2, a.warmup // 2), workspace=True)
             out["other_problems"][name]["with_workspace"] = {
                 "tflops": round(r["tflops"], 3), "ms_per_step": round(r["ms_per_step"], 6),
                 "frac_of_peak": round(r["tflops"] / r["peak"], 4), "split_k": r["cfg"].split_k,
+                "packed": r["cfg"].pack == 2, "schedule": r["cfg"].schedule,
                 "tile": f"{r['cfg'].bm}x{r['cfg'].bn}", "workspace_bytes": r["cfg"].workspace_bytes}
     if not a.no_extra and not a.only:
         grouped = {}

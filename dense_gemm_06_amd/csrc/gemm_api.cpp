@@ -333,6 +333,22 @@ int gemm_ex_workspace(int opA, int opB, int64_t M, int64_t N, int64_t K, const v
     args.work_ld = (N + 3) / 4 * 4;
     args.work_slice = M * args.work_ld;
     (void)hipGetLastError();  // clear a stale error left by earlier unrelated work
+    if (plan.pack == 2) {
+        // zero-padded copies of A and B in the workspace, then the product on them
+        int64_t Mp, Np, Kp;
+        dg::pack_dims(M, N, K, &Mp, &Np, &Kp);
+        char* ap = static_cast<char*>(workspace);
+        char* bp = ap + dg::pack_a_bytes(dtype, M, N, K);
+        dg::PackJob ja{A, ap, lda, (int)M, (int)K, (int)Mp, (int)Kp};
+        dg::PackJob jb = opB == GEMM_OP_N ? dg::PackJob{B, bp, ldb, (int)K, (int)N, (int)Kp, (int)Np}
+                                          : dg::PackJob{B, bp, ldb, (int)N, (int)K, (int)Np, (int)Kp};
+        dg::launch_pack((int)es, ja, jb, (hipStream_t)stream);
+        args.A = ap;
+        args.B = bp;
+        args.lda = Kp;
+        args.ldb = opB == GEMM_OP_N ? Np : Kp;
+        args.K = (int)Kp;
+    }
     if (launch(plan.kernel_id, args, (unsigned)plan.grid, (unsigned)plan.split_k, (hipStream_t)stream) != 0) {
         dg::set_error("internal: kernel %d has no launcher", plan.kernel_id);
         return GEMM_ERR_LAUNCH;

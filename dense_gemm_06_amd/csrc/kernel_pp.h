@@ -206,10 +206,13 @@ __global__ __launch_bounds__(512) void mfma16_pp(GemmArgs g) {
     if (grp == 1) mma();
 
     // epilogue: lane owns C[m][n..n+3]; 16x16: one run per subtile (n = 4*lg ..);
-    // 32x32: register r of the subtile holds row n = 8(r/4) + 4*lh + r%4, so four runs
+    // 32x32: register r of the subtile holds row n = 8(r/4) + 4*lh + r%4, so four runs.
+    // The operands may be zero-padded copies larger than C (whole tiles): rows >= M
+    // and columns >= N of the padded product are not stored.
 #pragma unroll
     for (int i = 0; i < SI; ++i) {
         const int m = m0 + grp * 128 + i * MF + (MF == 16 ? l16 : l32);
+        if (m >= g.M) continue;
 #pragma unroll
         for (int j = 0; j < SJ; ++j)
 #pragma unroll
@@ -217,11 +220,12 @@ __global__ __launch_bounds__(512) void mfma16_pp(GemmArgs g) {
                 const int n = n0 + wl * 64 + j * MF + (MF == 16 ? lg * 4 : rg * 8 + lh * 4);
                 float* cp = g.C + (size_t)m * g.ldc + n;
                 const f32x4 v = {acc[i][j][4 * rg], acc[i][j][4 * rg + 1], acc[i][j][4 * rg + 2], acc[i][j][4 * rg + 3]};
-                if ((reinterpret_cast<uintptr_t>(cp) & 15) == 0) {
+                if (n + 4 <= g.N && (reinterpret_cast<uintptr_t>(cp) & 15) == 0) {
                     *reinterpret_cast<f32x4*>(cp) = v;
                 } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) cp[e] = v[e];
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < g.N) cp[e] = v[e];
                 }
             }
     }

@@ -132,6 +132,17 @@ struct GemmArgs {
     int64_t work_slice, work_ld;
 };
 
+// One operand copy of a packing launch: rows x cols elements of src (leading
+// dimension ld) into a zero-padded rows_p x cols_p destination with leading
+// dimension cols_p (a multiple of 16 bytes).
+struct PackJob {
+    const void* src;
+    void* dst;
+    int64_t ld;
+    int rows, cols;
+    int rows_p, cols_p;
+};
+
 // Grouped launches ("Grouped Tile Scheduler" of the learn-cutedsl README, section
 // 8.4): one persistent grid walks the tiles of several problems. A segment is
 // `batch` problems of one shape whose operands sit at fixed element strides

@@ -112,7 +112,13 @@ static double rate_per_cu(const MenuEntry& e) {
     if (e.variant == V_LDS) return 128.0;  // 64 lanes x 2 FLOP per FMA, one wave64 FMA per SIMD per 4 clocks x 4 SIMDs
     return e.dtype == DT_F32 ? 256.0 : 4096.0;
 }
+static double tile_efficiency_aligned(const MenuEntry& e);
+// Element-wise global loads (unaligned operands) measured about 3x slower for
+// 16-bit inputs (c5-like shapes) and are assumed 1.7x slower for fp32.
 static double tile_efficiency(const MenuEntry& e) {
+    return tile_efficiency_aligned(e) * (e.vec ? 1.0 : (e.dtype == DT_F32 ? 0.6 : 0.35));
+}
+static double tile_efficiency_aligned(const MenuEntry& e) {
     const int t = std::min(e.bm, e.bn);
     // measured at 4096^3 fp16: ping-pong 144 us, software-pipelined 164 us,
     // register-staged 256 x 256 165 us
@@ -129,6 +135,25 @@ static int blocks_per_cu(const MenuEntry& e) {
 }
 
 static bool aligned16(uintptr_t a) { return (a & 15) == 0; }
+
+void pack_dims(int64_t M, int64_t N, int64_t K, int64_t* Mp, int64_t* Np, int64_t* Kp) {
+    *Mp = (M + 255) / 256 * 256;
+    *Np = (N + 255) / 256 * 256;
+    *Kp = (K + 63) / 64 * 64;
+}
+
+int64_t pack_a_bytes(int dtype, int64_t M, int64_t N, int64_t K) {
+    int64_t Mp, Np, Kp;
+    pack_dims(M, N, K, &Mp, &Np, &Kp);
+    return (Mp * Kp * elem_size(dtype) + 255) / 256 * 256;
+}
+
+int64_t pack_workspace(int opB, int dtype, int64_t M, int64_t N, int64_t K) {
+    (void)opB;  // K x Np (row-major B) and Np x K (column-major B) hold the same count
+    int64_t Mp, Np, Kp;
+    pack_dims(M, N, K, &Mp, &Np, &Kp);
+    return pack_a_bytes(dtype, M, N, K) + Np * Kp * elem_size(dtype);
+}
 
 // Workspace of an S-slice split: one fp32 plane of M x round_up(N, 4) per slice.
 static int64_t split_workspace(int64_t S, int64_t M, int64_t N) { return S * M * ((N + 3) / 4 * 4) * 4; }
@@ -152,7 +177,7 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
     const bool vec_ok = aligned16(a) && aligned16(b) && (lda * es) % 16 == 0 && (ldb * es) % 16 == 0;
 
     int want_variant = GEMM_VARIANT_AUTO, want_bm = 0, want_bn = 0, want_vec = -1, want_remap = -1, want_group = 0;
-    int want_wm = 0, want_wn = 0, want_sched = 0, want_split = 0;
+    int want_wm = 0, want_wn = 0, want_sched = 0, want_split = 0, want_pack = 0;
     if (ws_bytes < 0) {
         set_error("workspace_bytes = %lld must be non-negative", (long long)ws_bytes);
         return GEMM_ERR_INVALID_VALUE;
@@ -183,15 +208,39 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
                       want_sched);
             return GEMM_ERR_UNSUPPORTED;
         }
-        if (want_vec == 1 && !vec_ok) {
+        want_pack = req->pack;
+        if (want_pack < 0 || want_pack > 2) {
+            set_error("pack = %d must be 0 (heuristic), 1 (never) or 2 (always)", want_pack);
+            return GEMM_ERR_INVALID_VALUE;
+        }
+        if (want_vec == 1 && !vec_ok && (ws_bytes == 0 || want_pack == 1)) {
             set_error("16-byte loads requested but A/B bases or leading dimensions are not 16-byte aligned");
             return GEMM_ERR_UNSUPPORTED;
         }
     }
 
+    // Packed operands: zero-padded, aligned copies in the workspace (whole 256 x 256
+    // tiles, K a multiple of 64), made by one extra launch whose traffic is charged.
+    int64_t Mp, Np, Kp;
+    pack_dims(M, N, K, &Mp, &Np, &Kp);
+    const int64_t pack_need = pack_workspace(opB, dtype, M, N, K);
+    const bool pack_fits = K > 0 && pack_need <= ws_bytes && Kp < ((int64_t)1 << 23) && Np < ((int64_t)1 << 23);
+    if (want_pack == 2 && !pack_fits) {
+        set_error("pack = 2 needs K > 0 and %lld bytes of workspace; %lld were given", (long long)pack_need,
+                  (long long)ws_bytes);
+        return GEMM_ERR_INVALID_VALUE;
+    }
+    const double pack_cycles =
+        (double)((M * K + K * N) + (Mp * Kp + Np * Kp)) * es / 2048.0 + 16000.0;
+
     const MenuEntry* best = nullptr;
     double best_cost = 0;
     int64_t best_split = 1, best_chunk = K, short_ws = -1;
+    bool best_packed = false;
+    for (int pass = 0; pass < 2; ++pass) {
+    const bool packed = pass == 1;
+    if (packed ? (!pack_fits || want_pack == 1 || want_split >= 2) : want_pack == 2) continue;
+    const int64_t Mx = packed ? Mp : M, Nx = packed ? Np : N, Kx = packed ? Kp : K;
     for (const MenuEntry& e : kMenu) {
         if (e.dtype != dtype || e.opb != opB) continue;
         if (want_variant != GEMM_VARIANT_AUTO && e.variant != want_variant) continue;
@@ -200,21 +249,23 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
         if (want_wm && (e.variant == V_MFMA ? e.wm : 1) != want_wm) continue;
         if (want_sched && e.sched != want_sched) continue;
         if (!schedule_enabled(e.sched)) continue;
-        // the direct-copy kernels copy whole tiles: no masking of M, N or K edges
-        if (e.sched >= 2 && (M % e.bm != 0 || N % e.bn != 0 || K % e.bk != 0 || K == 0)) continue;
+        // the direct-copy kernels copy whole tiles: no masking of M, N or K edges on
+        // the operands (the packed copies are whole tiles; C is masked at the store)
+        if (e.sched >= 2 && (Mx % e.bm != 0 || Nx % e.bn != 0 || Kx % e.bk != 0 || Kx == 0)) continue;
         if (want_wn && (e.variant == V_MFMA ? e.wn : 1) != want_wn) continue;
-        const int vec = want_vec >= 0 ? want_vec : (vec_ok ? 1 : 0);
+        const int vec = want_vec >= 0 ? want_vec : ((packed || vec_ok) ? 1 : 0);
         if (e.vec != vec) continue;
-        const int64_t tiles = ((M + e.bm - 1) / e.bm) * ((N + e.bn - 1) / e.bn);
-        const int64_t ktiles = (K + e.bk - 1) / e.bk;
+        if (e.vec && !packed && !vec_ok) continue;  // 16-byte loads need aligned operands
+        const int64_t tiles = e.sched >= 2 ? (Mx / e.bm) * (Nx / e.bn) : ((M + e.bm - 1) / e.bm) * ((N + e.bn - 1) / e.bn);
+        const int64_t ktiles = (Kx + e.bk - 1) / e.bk;
         const int occ = blocks_per_cu(e);
         const int64_t concurrent = (int64_t)num_cus * occ;
         // split candidates: none, or S slices of whole k-tiles (register-staged kernels)
         const int cand[] = {1, 2, 4, 8, 16};
         for (int ci = 0; ci < (want_split >= 2 ? 1 : 5); ++ci) {
             const int S = want_split >= 2 ? want_split : cand[ci];
-            if (want_split == 1 && S != 1) continue;
-            int64_t slices = 1, chunk = K;
+            if ((want_split == 1 || packed) && S != 1) continue;
+            int64_t slices = 1, chunk = Kx;
             if (S > 1) {
                 if (e.sched != 1 || ktiles < 2) continue;
                 const int64_t chunk_tiles = (ktiles + S - 1) / S;
@@ -230,7 +281,7 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
             const int64_t work = tiles * slices;
             const int64_t rounds = (work + concurrent - 1) / concurrent;
             const int64_t resident = std::min<int64_t>(occ, (work + num_cus - 1) / num_cus);
-            const int64_t kpad = ((std::min<int64_t>(chunk, K) + e.bk - 1) / e.bk) * e.bk;
+            const int64_t kpad = ((std::min<int64_t>(chunk, Kx) + e.bk - 1) / e.bk) * e.bk;
             const double tile_cycles =
                 2.0 * e.bm * e.bn * std::max<int64_t>(kpad, e.bk) / (rate_per_cu(e) * tile_efficiency(e));
             double cost = (double)rounds * (double)std::max<int64_t>(resident, 1) * tile_cycles;
@@ -239,14 +290,17 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
             // beyond its traffic (about 1 KB per clock for a kernel of this size),
             // so it pays only when few tiles face a long K
             if (slices > 1) cost += (double)(slices + 1) * (double)M * (double)N * 4.0 / 1024.0 + 16000.0;
+            if (packed) cost += pack_cycles;
             if (!best || cost < best_cost * (1 - 1e-9) ||
                 (cost <= best_cost * (1 + 1e-9) && e.bm * e.bn > best->bm * best->bn)) {
                 best = &e;
                 best_cost = cost;
                 best_split = slices;
                 best_chunk = chunk;
+                best_packed = packed;
             }
         }
+    }
     }
     if (!best && short_ws > 0) {
         set_error("split_k = %d needs %lld bytes of workspace; %lld were given", want_split, (long long)short_ws,
@@ -274,18 +328,19 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
     cfg.lds_bytes = e.lds_bytes;
     cfg.kernel_id = e.id;
     cfg.schedule = e.sched;
-    cfg.tiles_m = (M + e.bm - 1) / e.bm;
-    cfg.tiles_n = (N + e.bn - 1) / e.bn;
+    cfg.tiles_m = ((best_packed && e.sched >= 2 ? Mp : M) + e.bm - 1) / e.bm;
+    cfg.tiles_n = ((best_packed && e.sched >= 2 ? Np : N) + e.bn - 1) / e.bn;
     cfg.grid = (int32_t)(cfg.tiles_m * cfg.tiles_n);
     // Group enough tile rows that one XCD's share of the grid forms a compact
     // rectangle; the remap needs the grid to split evenly over the 8 XCDs.
     const int gm = want_group ? want_group : default_group_m(cfg.tiles_m, cfg.tiles_n);
     cfg.group_m = (int32_t)std::max<int64_t>(1, std::min<int64_t>(gm, cfg.tiles_m));
     cfg.tiles_total = cfg.tiles_m * cfg.tiles_n;
-    cfg.launches = best_split > 1 ? 2 : 1;
+    cfg.launches = (best_split > 1 || best_packed) ? 2 : 1;
     cfg.split_k = (int32_t)best_split;
     cfg.k_chunk = (int32_t)best_chunk;
-    cfg.workspace_bytes = best_split > 1 ? split_workspace(best_split, M, N) : 0;
+    cfg.pack = best_packed ? 2 : 1;
+    cfg.workspace_bytes = best_split > 1 ? split_workspace(best_split, M, N) : best_packed ? pack_need : 0;
     cfg.xcd_remap = want_remap >= 0 ? want_remap : ((cfg.grid % 8 == 0 && cfg.grid >= 16) ? 1 : 0);
     cfg.est_cycles = best_cost;
     *out = cfg;
@@ -383,8 +438,9 @@ int plan_grouped(int opA, int opB, int dtype, const gemm_problem* probs, int cou
                       want_sched);
             return GEMM_ERR_UNSUPPORTED;
         }
-        if (req->split_k > 1) {
-            set_error("grouped calls do not split K (split_k = %d)", req->split_k);
+        if (req->split_k > 1 || req->pack == 2) {
+            set_error("grouped calls neither split K nor pack operands (split_k = %d, pack = %d)", req->split_k,
+                      req->pack);
             return GEMM_ERR_UNSUPPORTED;
         }
         if (want_vec == 1 && !vec_ok) {
@@ -472,6 +528,7 @@ int plan_grouped(int opA, int opB, int dtype, const gemm_problem* probs, int cou
     cfg.tiles_total = best_tiles;
     cfg.launches = (segments + kMaxGroupSegments - 1) / kMaxGroupSegments;
     cfg.split_k = 1;
+    cfg.pack = 1;
     cfg.est_cycles = best_cost;
     *out = cfg;
     return GEMM_OK;

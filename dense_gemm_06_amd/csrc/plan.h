@@ -21,6 +21,13 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
          const gemm_config* req, gemm_config* out);
 int menu_entry(int index, int* variant, int* dtype, int* opb, gemm_config* out);
 
+// Packed-operand layout: A padded to Mp x Kp, B to Kp x Np (row-major) or Np x Kp
+// (column-major); Mp, Np multiples of 256, Kp of 64. A's copy starts the
+// workspace, B's follows at pack_a_bytes (a multiple of 256).
+void pack_dims(int64_t M, int64_t N, int64_t K, int64_t* Mp, int64_t* Np, int64_t* Kp);
+int64_t pack_a_bytes(int dtype, int64_t M, int64_t N, int64_t K);
+int64_t pack_workspace(int opB, int dtype, int64_t M, int64_t N, int64_t K);
+
 // Validation of one grouped entry (the gemm_ex rules plus batch and strides).
 int validate_problem(int opA, int opB, int dtype, const gemm_problem& p, int index);
 // Tile-row group size the planner uses for a problem of tiles_m x tiles_n tiles.

@@ -100,7 +100,10 @@ typedef struct gemm_config {
     int32_t split_k;     /* in/out: K slices; in: 0 = heuristic, 1 = no split, S >= 2 = S slices (fewer
                             if K has fewer k-tiles); splitting needs a workspace (gemm_ex_workspace) */
     int32_t k_chunk;     /* out: K elements per slice (K when not split) */
-    int64_t workspace_bytes; /* out: workspace the configuration uses (0 when not split) */
+    int64_t workspace_bytes; /* out: workspace the configuration uses (0 without split or packing) */
+    int32_t pack;        /* in/out: operand packing (gemm_ex_workspace); in: 0 = heuristic, 1 = never,
+                            2 = always; out: 2 if the call packs, else 1 */
+    int32_t reserved;
 } gemm_config;
 
 /*
@@ -141,6 +144,12 @@ int gemm_plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, in
  * (the "few blocks" case of "GPU architecture and mapping kernels", section 12.9,
  * and its exercise on a minimum block count). The heuristic splits only if the
  * estimate improves and the workspace suffices; cfg->split_k forces a choice.
+ * With a workspace the call may instead pack the operands: one extra kernel
+ * copies A and B into zero-padded, 16-byte aligned buffers of whole 256 x 256
+ * tiles (K padded to a multiple of 64), so unaligned or ragged operands can run
+ * on the fastest kernels; C is written only within M x N. Packing needs
+ * (Mp*Kp rounded up to 256 bytes + Np*Kp) elements of the input type, Mp, Np
+ * = M, N rounded up to 256, Kp = K rounded up to 64; cfg->pack forces a choice.
  * workspace_bytes = 0 (workspace may be NULL) behaves as gemm_ex. Otherwise the
  * workspace must be 16-byte aligned and its whole declared range must not overlap
  * A, B or C (GEMM_ERR_INVALID_VALUE, checked before any launch); its contents

@@ -369,3 +369,37 @@ def test_split_workspace_rejections_before_device():
     for w in (A, B + 1024 * 16, C - (1 << 20)):
         assert ex(*args, w, 4 << 20, None) == dg.GEMM_ERR_INVALID_VALUE
         assert "overlaps" in dg.gemm_last_error()
+
+
+# ----------------------------------------------------------------------------- packed operands
+def test_pack_plan_choices():
+    # the ragged bf16 benchmark problem packs onto the whole-tile ping-pong kernel
+    st, c = dg.gemm_plan_workspace(0, 1, 3001, 5003, 1037, 1037, 1037, 5003, dg.GEMM_BF16, 4096, 4096, 4096, 256,
+                                   "gfx950", 1 << 30)
+    assert st == 0 and c.pack == 2 and c.schedule == 2 and c.vec == 1 and c.launches == 2
+    assert (c.tiles_m, c.tiles_n) == (12, 20)
+    assert c.workspace_bytes == 3072 * 1088 * 2 + 5120 * 1088 * 2
+    # without workspace, or with pack = 1, it does not
+    assert plan(3001, 5003, 1037, "bf16", "T", lda=1037, ldb=1037, ldc=5003)[1].pack == 1
+    st, c = dg.gemm_plan_workspace(0, 1, 3001, 5003, 1037, 1037, 1037, 5003, dg.GEMM_BF16, 4096, 4096, 4096, 256,
+                                   "gfx950", 1 << 30, dg.request(pack=1))
+    assert st == 0 and c.pack == 1 and c.vec == 0
+    # an aligned whole-tile problem gains nothing from a copy
+    assert wplan(4096, 4096, 4096, "f16")[1].pack == 1
+
+
+def test_pack_errors():
+    st, _ = wplan(300, 300, 300, "f16", ws=1000, req=dg.request(pack=2), check=False)
+    assert st == dg.GEMM_ERR_INVALID_VALUE and "workspace" in dg.gemm_last_error()
+    st, _ = wplan(300, 300, 0, "f16", req=dg.request(pack=2), check=False)
+    assert st == dg.GEMM_ERR_INVALID_VALUE
+    st, _ = wplan(300, 300, 300, "f16", req=dg.request(pack=3), check=False)
+    assert st == dg.GEMM_ERR_INVALID_VALUE
+    st, _ = dg.gemm_grouped_plan(0, 0, dg.GEMM_F32, [gp(64, 64, 64)], req=dg.request(pack=2), check=False)
+    assert st == dg.GEMM_ERR_UNSUPPORTED
+    # 16-byte loads on unaligned operands: possible only by packing
+    st, _ = dg.gemm_plan(0, 0, 64, 64, 63, 63, 64, 64, dg.GEMM_F16, req=dg.request(vec=1), check=False)
+    assert st == dg.GEMM_ERR_UNSUPPORTED
+    st, c = dg.gemm_plan_workspace(0, 0, 64, 64, 63, 63, 64, 64, dg.GEMM_F16, 0, 0, 0, 256, "gfx950", 1 << 20,
+                                   dg.request(vec=1))
+    assert st == 0 and c.pack == 2 and c.vec == 1
