@@ -29,10 +29,29 @@ __global__ __launch_bounds__(256) void pack_pad(PackJob a, PackJob b, int64_t ch
         const int64_t per_row = cols_p / V;
         const int64_t r = local / per_row;
         const int c0 = (int)(local - r * per_row) * V;
-        T v[V];
+        u32x4 w;
+        if (sizeof(T) == 2 && r < rows && c0 + V <= cols) {
+            // a whole chunk of 8 16-bit elements inside the source: 4-byte loads (16-bit
+            // elements start on 2-byte boundaries, so a chunk is 4-byte aligned or 2 off)
+            const uint16_t* p = reinterpret_cast<const uint16_t*>(src + r * ld + c0);
+            if ((reinterpret_cast<uintptr_t>(p) & 3) == 0) {
+                const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+                w = u32x4{q[0], q[1], q[2], q[3]};
+            } else {
+                // elements 1..6 as three aligned words, 0 and 7 on their own: nothing
+                // outside the chunk is read
+                const uint32_t* q = reinterpret_cast<const uint32_t*>(p + 1);
+                const uint32_t d0 = q[0], d1 = q[1], d2 = q[2];
+                const uint32_t e0 = p[0], e7 = p[7];
+                w = u32x4{e0 | (d0 << 16), (d0 >> 16) | (d1 << 16), (d1 >> 16) | (d2 << 16), (d2 >> 16) | (e7 << 16)};
+            }
+        } else {
+            T v[V];
 #pragma unroll
-        for (int e = 0; e < V; ++e) v[e] = (r < rows && c0 + e < cols) ? src[r * ld + c0 + e] : T(0);
-        *reinterpret_cast<u32x4*>(dst + r * cols_p + c0) = *reinterpret_cast<const u32x4*>(v);
+            for (int e = 0; e < V; ++e) v[e] = (r < rows && c0 + e < cols) ? src[r * ld + c0 + e] : T(0);
+            w = *reinterpret_cast<const u32x4*>(v);
+        }
+        *reinterpret_cast<u32x4*>(dst + r * cols_p + c0) = w;
     }
 }
 
