@@ -132,6 +132,36 @@ def time_problem(name, steps, warmup, workspace=False):
                 peak=PEAK_TFLOPS[ops.dtype])
 
 
+def time_fused_epilogue(name, steps, warmup):
+    """The problem with a fused epilogue: C = gelu(A @ B + bias) stored as bf16."""
+    import numpy as np
+    import torch
+    import dense_gemm_06_amd as dg
+    ops, A, B, _ = device_problem(name)
+    C = torch.empty((ops.M, ops.N), dtype=torch.bfloat16, device="cuda")
+    bias = torch.from_numpy(np.random.default_rng(1).standard_normal(ops.N).astype(np.float32)).cuda()
+    epi = dg.epilogue(bias=bias.data_ptr(), activation="gelu_tanh", out_dtype="bf16")
+    stream = torch.cuda.current_stream()
+    s = stream.cuda_stream
+    args = (0, dg.OP_CODE[ops.op_b], ops.M, ops.N, ops.K, A.data_ptr(), ops.lda, B.data_ptr(), ops.ldb,
+            C.data_ptr(), ops.N, dg.DTYPE_CODE[ops.dtype], epi, None, None, 0, s)
+    cus, arch = dg.gemm_device_info(0)
+    _, cfg = dg.gemm_plan_workspace(0, args[1], ops.M, ops.N, ops.K, ops.lda, ops.ldb, ops.N, args[11],
+                                    A.data_ptr(), B.data_ptr(), C.data_ptr(), cus, arch, 0, epi=epi)
+    for _ in range(warmup):
+        dg.gemm_ex_epilogue(*args)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        dg.gemm_ex_epilogue(*args)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = 2.0 * ops.M * ops.N * ops.K
+    return dict(ms_per_step=ms, tflops=flops / (ms * 1e-3) / 1e12, cfg=cfg, peak=PEAK_TFLOPS[ops.dtype])
+
+
 # Grouped workloads: `count` independent problems of one shape, run as one grouped
 # launch (the README's grouped example: four 256^3 fp32 GEMMs).
 GROUPED = {"g4_f32_256": dict(count=4, M=256, N=256, K=256, dtype="f32")}
@@ -259,6 +289,11 @@ def main():
         return
     headline = a.only or "c4_f16_4096"
     main_res = time_problem(headline, a.steps, a.warmup)
+    # the fused-epilogue variant right after the headline, in the same thermal state
+    # (the chip's clock drifts by 10-20% over a run of heavy launches)
+    fe = None
+    if not a.no_extra and not a.only:
+        fe = time_fused_epilogue(headline, max(5, a.steps // 2), max(2, a.warmup // 2))
     extras = {}
     if not a.no_extra and not a.only:
         for name in ("c3_f32_4096", "c1_f32_256", "c2_f32_1024", "c5_bf16_ragged"):
@@ -320,6 +355,12 @@ def main():
                 "frac_of_peak": round(r["tflops"] / r["peak"], 4), "split_k": r["cfg"].split_k,
                 "packed": r["cfg"].pack == 2, "schedule": r["cfg"].schedule,
                 "tile": f"{r['cfg'].bm}x{r['cfg'].bn}", "workspace_bytes": r["cfg"].workspace_bytes}
+    if fe is not None:
+        out["fused_epilogue"] = {"workload": f"{out['config']['workload']} with C = gelu_tanh(A@B + bias) stored "
+                                             f"as bf16", "tflops": round(fe["tflops"], 3),
+                                 "ms_per_step": round(fe["ms_per_step"], 6),
+                                 "frac_of_peak": round(fe["tflops"] / fe["peak"], 4),
+                                 "kernel": kernel_name(fe["cfg"], main_res["dtype"])}
     if not a.no_extra and not a.only:
         grouped = {}
         for name in GROUPED:

@@ -1,7 +1,7 @@
 """Python binding of the MI355X dense GEMM library (libdensegemm.so).
 
 The functions mirror the C ABI in include/gemm.h one to one (gemm, gemm_ex,
-gemm_ex_workspace, gemm_plan, gemm_plan_workspace, gemm_grouped, gemm_grouped_plan, gemm_strided_batched,
+gemm_ex_workspace, gemm_ex_epilogue, gemm_plan, gemm_plan_workspace, gemm_grouped, gemm_grouped_plan, gemm_strided_batched,
 gemm_menu_size / gemm_menu_entry, gemm_device_info, gemm_status_string,
 gemm_last_error) and only marshal arguments: every step of the product runs in
 the library's HIP kernels. A nonzero status raises
@@ -67,6 +67,26 @@ def request(variant: int = GEMM_VARIANT_AUTO, bm: int = 0, bn: int = 0, vec: int
     return c
 
 
+GEMM_ACT_NONE, GEMM_ACT_RELU, GEMM_ACT_GELU_TANH = 0, 1, 2
+ACT_CODE = {"none": GEMM_ACT_NONE, "relu": GEMM_ACT_RELU, "gelu_tanh": GEMM_ACT_GELU_TANH}
+
+
+class gemm_epilogue(ctypes.Structure):
+    """C = act(alpha * (A @ B) + beta * R + bias), stored as out_dtype (see include/gemm.h)."""
+    _fields_ = [
+        ("alpha", ctypes.c_float), ("beta", ctypes.c_float), ("R", ctypes.c_void_p), ("ldr", ctypes.c_int64),
+        ("bias", ctypes.c_void_p), ("activation", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+    ]
+
+
+def epilogue(alpha=1.0, beta=0.0, R=None, ldr=0, bias=None, activation="none", out_dtype="f32") -> gemm_epilogue:
+    e = gemm_epilogue()
+    e.alpha, e.beta, e.R, e.ldr, e.bias = alpha, beta, R, ldr, bias
+    e.activation = ACT_CODE[activation] if isinstance(activation, str) else activation
+    e.out_dtype = DTYPE_CODE[out_dtype] if isinstance(out_dtype, str) else out_dtype
+    return e
+
+
 class gemm_problem(ctypes.Structure):
     """One entry of a grouped call: `batch` problems of one shape at element strides."""
     _fields_ = [
@@ -121,8 +141,13 @@ def _load():
     lib.gemm_plan.restype = i32
     lib.gemm_ex_workspace.argtypes = [i32, i32, i64, i64, i64, vp, i64, vp, i64, vp, i64, i32, cfgp, vp, i64, vp]
     lib.gemm_ex_workspace.restype = i32
+    epip = ctypes.POINTER(gemm_epilogue)
     lib.gemm_plan_workspace.argtypes = [i32, i32, i64, i64, i64, i64, i64, i64, i32, ctypes.c_size_t,
-                                        ctypes.c_size_t, ctypes.c_size_t, i32, ctypes.c_char_p, i64, cfgp, cfgp]
+                                        ctypes.c_size_t, ctypes.c_size_t, i32, ctypes.c_char_p, i64, epip, cfgp,
+                                        cfgp]
+    lib.gemm_ex_epilogue.argtypes = [i32, i32, i64, i64, i64, vp, i64, vp, i64, vp, i64, i32, epip, cfgp, vp, i64,
+                                     vp]
+    lib.gemm_ex_epilogue.restype = i32
     lib.gemm_plan_workspace.restype = i32
     probp = ctypes.POINTER(gemm_problem)
     lib.gemm_grouped.argtypes = [i32, i32, i32, probp, i32, cfgp, vp]
@@ -191,12 +216,27 @@ def gemm_ex_workspace(opA, opB, M, N, K, A, lda, B, ldb, C, ldc, dtype, cfg: gem
     return st
 
 
+def gemm_ex_epilogue(opA, opB, M, N, K, A, lda, B, ldb, C, ldc, dtype, epi: gemm_epilogue | None = None,
+                     cfg: gemm_config | None = None, workspace=None, workspace_bytes=0, stream=None,
+                     check=True) -> int:
+    """The product with a fused epilogue (C's element type is epi.out_dtype)."""
+    st = _load().gemm_ex_epilogue(opA, opB, M, N, K, A, lda, B, ldb, C, ldc, dtype,
+                                  ctypes.byref(epi) if epi is not None else None,
+                                  ctypes.byref(cfg) if cfg is not None else None, workspace, workspace_bytes, stream)
+    if check:
+        _check(st, "gemm_ex_epilogue")
+    return st
+
+
 def gemm_plan_workspace(opA, opB, M, N, K, lda, ldb, ldc, dtype, a_addr=0, b_addr=0, c_addr=0, num_cus=256,
-                        arch="gfx950", workspace_bytes=0, req: gemm_config | None = None, check=True):
-    """Host-only: the configuration gemm_ex_workspace would launch. Returns (status, gemm_config)."""
+                        arch="gfx950", workspace_bytes=0, req: gemm_config | None = None, check=True,
+                        epi: gemm_epilogue | None = None):
+    """Host-only: the configuration gemm_ex_workspace (or gemm_ex_epilogue with `epi`) would launch.
+    Returns (status, gemm_config)."""
     out = gemm_config()
     st = _load().gemm_plan_workspace(opA, opB, M, N, K, lda, ldb, ldc, dtype, a_addr, b_addr, c_addr, num_cus,
                                      arch.encode() if arch is not None else None, workspace_bytes,
+                                     ctypes.byref(epi) if epi is not None else None,
                                      ctypes.byref(req) if req is not None else None, ctypes.byref(out))
     if check:
         _check(st, "gemm_plan_workspace")

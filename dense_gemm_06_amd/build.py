@@ -1,12 +1,16 @@
 """Build the HIP library libdensegemm.so in-tree, for gfx950 only.
 
 Every translation unit is compiled with hipcc; the kernel families compile in
-parallel. Packed-fp32 VALU instructions are disabled for all device code.
+parallel. Packed-fp32 VALU instructions are disabled for all device code. The
+compiler's per-kernel resource usage (registers, scratch, spills, LDS,
+occupancy) is written to _build/resource_usage.json.
 Run as ``python -m dense_gemm_06_amd.build`` or call ``build()``.
 """
 from __future__ import annotations
 
+import json
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -23,7 +27,7 @@ HOST_SOURCES = ["plan.cpp", "gemm_api.cpp"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function"]
 DEVICE_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-                "-fno-gpu-rdc", "-munsafe-fp-atomics"]
+                "-fno-gpu-rdc", "-munsafe-fp-atomics", "-Rpass-analysis=kernel-resource-usage"]
 
 
 def hipcc() -> str:
@@ -33,11 +37,36 @@ def hipcc() -> str:
     return "hipcc"
 
 
+RESOURCE_USAGE = os.path.join(OUT_DIR, "resource_usage.json")
+_REMARK = re.compile(r"remark: (.*?) \[-Rpass-analysis=kernel-resource-usage\]")
+
+
 def _run(cmd):
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    # hipcc's host pass warns that it does not know the packed-fp32 feature: harmless
-    lines = [l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l and "not a recognized feature" not in l]
-    return r.returncode, "\n".join(lines)
+    # hipcc's host pass warns that it does not know the packed-fp32 feature: harmless;
+    # resource-usage remarks are collected separately
+    lines = [l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l and "not a recognized feature" not in l
+             and "kernel-resource-usage" not in l and not l.lstrip().startswith(("|", "^"))
+             and not re.match(r"^\s*\d+ \|", l)]
+    return r.returncode, "\n".join(lines), r.stdout
+
+
+def _resource_usage(text: str) -> dict:
+    """Per device function: the compiler's resource-usage remarks (VGPRs, AGPRs,
+    scratch bytes per lane, spills, LDS, occupancy)."""
+    out, cur = {}, None
+    for line in text.splitlines():
+        m = _REMARK.search(line)
+        if not m:
+            continue
+        t = m.group(1).strip()
+        if t.startswith("Function Name:"):
+            cur = out.setdefault(t.split(":", 1)[1].strip(), {})
+        elif cur is not None and ":" in t:
+            k, v = t.split(":", 1)
+            v = v.strip()
+            cur[k.strip()] = int(v) if v.lstrip("-").isdigit() else v
+    return out
 
 
 def build(jobs: int | None = None, verbose: bool = False) -> str:
@@ -55,15 +84,20 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     jobs = jobs or min(len(tasks), max(1, min(os.cpu_count() or 1, 8)))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         results = list(ex.map(lambda t: (t[0], *_run(t[2])), tasks))
-    failed = [(s, out) for s, rc, out in results if rc != 0]
-    for s, rc, out in results:
+    failed = [(s, out) for s, rc, out, _ in results if rc != 0]
+    for s, rc, out, _ in results:
         if verbose and out.strip():
             print(f"--- {s}\n{out}")
+    usage = {}
+    for s, rc, out, raw in results:
+        usage.update(_resource_usage(raw))
+    with open(RESOURCE_USAGE, "w") as f:
+        json.dump(usage, f, indent=1, sort_keys=True)
     if failed:
         msg = "\n".join(f"--- {s}\n{out}" for s, out in failed)
         raise RuntimeError(f"HIP build failed:\n{msg}")
     tmp = LIB + ".tmp%d" % os.getpid()
-    rc, out = _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *[t[1] for t in tasks]])
+    rc, out, _ = _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *[t[1] for t in tasks]])
     if rc != 0:
         raise RuntimeError(f"link failed:\n{out}")
     os.replace(tmp, LIB)

@@ -77,6 +77,7 @@ __device__ __forceinline__ void k_slice(GemmArgs& g) {
         g.K = min(g.K - kbeg, g.k_chunk);
         g.C = g.work + (size_t)s * (size_t)g.work_slice;
         g.ldc = g.work_ld;
+        g.ep.kind = 0;  // partial products are plain fp32; the reduction applies the epilogue
     }
 }
 
@@ -117,6 +118,149 @@ __device__ __forceinline__ void group_tile(const GroupArgs& ga, int t, GemmArgs&
     g.group_m = sg.group_m;
     g.xcd_remap = 0;
     g.k_split = 1;
+    g.ep.kind = 0;
+}
+
+// ---- epilogue and C stores
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+    const uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);  // NaN stays a quiet NaN
+    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ float load_out(const void* p, int dt, size_t i) {
+    if (dt == DT_F32) return static_cast<const float*>(p)[i];
+    const uint16_t h = static_cast<const uint16_t*>(p)[i];
+    return dt == DT_F16 ? (float)__builtin_bit_cast(_Float16, h) : __uint_as_float((uint32_t)h << 16);
+}
+
+__device__ __forceinline__ void store_out(void* p, int dt, size_t i, float x) {
+    if (dt == DT_F32) static_cast<float*>(p)[i] = x;
+    else if (dt == DT_F16) static_cast<_Float16*>(p)[i] = (_Float16)x;
+    else static_cast<uint16_t*>(p)[i] = f32_to_bf16_rne(x);
+}
+
+// GELU in its tanh form (Hendrycks and Gimpel): x/2 * (1 + tanh(u)) with
+// u = sqrt(2/pi) (x + 0.044715 x^3). Since 1 + tanh(u) = 2 / (1 + e^(-2u)), this
+// is x / (1 + e^(-2u)): a hardware exponential and reciprocal, no cancellation for
+// large negative u, and exactly x or 0 (of x's sign) where e^(-2u) under- or overflows.
+__device__ __forceinline__ float gelu_tanh(float x) {
+    const float u2 = 1.5957691216057308f * (x + 0.044715f * x * x * x);  // 2u
+    return x * __builtin_amdgcn_rcpf(1.0f + __expf(-u2));
+}
+
+__device__ __forceinline__ float epilogue_value(const Epilogue& ep, float acc, size_t ri, int n) {
+    float x = ep.alpha * acc;
+    if (ep.beta != 0.0f) x = fmaf(ep.beta, load_out(ep.R, ep.out_dt, ri), x);
+    if (ep.bias) x += ep.bias[n];
+    if (ep.act == ACT_RELU) x = x > 0.0f ? x : 0.0f;
+    else if (ep.act == ACT_GELU_TANH) x = gelu_tanh(x);
+    return x;
+}
+
+// The epilogue of one run, out of line: inlined into every run of a kernel's
+// unrolled store loop it would make the loop too large to unroll, and the
+// accumulators would then be indexed at run time (moved to scratch memory).
+// A whole, aligned run moves as one vector (16 bytes of fp32, 8 bytes of 16-bit
+// values) for both the residual read and the store.
+__device__ __forceinline__ f32x4 load_out4(const void* p, int dt, size_t i) {
+    if (dt == DT_F32) return *reinterpret_cast<const f32x4*>(static_cast<const float*>(p) + i);
+    const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p) + i);
+    f32x4 r;
+    if (dt == DT_F16) {
+        r[0] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[0] & 0xffffu));
+        r[1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[0] >> 16));
+        r[2] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[1] & 0xffffu));
+        r[3] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[1] >> 16));
+    } else {
+        r[0] = __uint_as_float(w[0] << 16);
+        r[1] = __uint_as_float(w[0] & 0xffff0000u);
+        r[2] = __uint_as_float(w[1] << 16);
+        r[3] = __uint_as_float(w[1] & 0xffff0000u);
+    }
+    return r;
+}
+
+__device__ __forceinline__ void store_out4(void* p, int dt, size_t i, f32x4 x) {
+    if (dt == DT_F32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(p) + i) = x;
+        return;
+    }
+    uint32_t h[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        h[e] = dt == DT_F16 ? (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x[e]) : (uint32_t)f32_to_bf16_rne(x[e]);
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p) + i) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+}
+
+// Wave-uniform values handed to an out-of-line function arrive in vector registers;
+// readfirstlane tells the compiler they are uniform, so branches on them are scalar
+// instead of masked. 64-bit values go through two unsigned 32-bit halves.
+__device__ __forceinline__ uint32_t uni32(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); }
+__device__ __forceinline__ uint64_t uni64(uint64_t x) {
+    return ((uint64_t)uni32((uint32_t)(x >> 32)) << 32) | (uint64_t)uni32((uint32_t)x);
+}
+__device__ __forceinline__ float unif(float x) { return __uint_as_float(uni32(__float_as_uint(x))); }
+
+__device__ __attribute__((noinline)) void epilogue_run4(const Epilogue ep_in, void* C_in, int64_t ldc_in, int N_in,
+                                                        int m, int n, f32x4 v) {
+    Epilogue ep;
+    ep.kind = (int)uni32((uint32_t)ep_in.kind);
+    ep.act = (int)uni32((uint32_t)ep_in.act);
+    ep.out_dt = (int)uni32((uint32_t)ep_in.out_dt);
+    ep.alpha = unif(ep_in.alpha);
+    ep.beta = unif(ep_in.beta);
+    ep.R = reinterpret_cast<const void*>(uni64(reinterpret_cast<uint64_t>(ep_in.R)));
+    ep.ldr = (int64_t)uni64((uint64_t)ep_in.ldr);
+    ep.bias = reinterpret_cast<const float*>(uni64(reinterpret_cast<uint64_t>(ep_in.bias)));
+    void* C = reinterpret_cast<void*>(uni64(reinterpret_cast<uint64_t>(C_in)));
+    const int64_t ldc = (int64_t)uni64((uint64_t)ldc_in);
+    const int N = (int)uni32((uint32_t)N_in);
+    const size_t ci = (size_t)m * ldc + n, ri = (size_t)m * ep.ldr + n;
+    const int vb = ep.out_dt == DT_F32 ? 16 : 8;  // bytes of a whole run
+    const int es = ep.out_dt == DT_F32 ? 4 : 2;
+    const bool whole = n + 4 <= N;
+    const bool c_vec = whole && ((reinterpret_cast<uintptr_t>(C) + ci * es) & (vb - 1)) == 0;
+    const bool r_vec = whole && ep.beta != 0.0f && ((reinterpret_cast<uintptr_t>(ep.R) + ri * es) & (vb - 1)) == 0;
+    if (c_vec && (ep.beta == 0.0f || r_vec)) {
+        const f32x4 r = ep.beta != 0.0f ? load_out4(ep.R, ep.out_dt, ri) : f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float t = ep.alpha * v[e];
+            if (ep.beta != 0.0f) t = fmaf(ep.beta, r[e], t);
+            if (ep.bias) t += ep.bias[n + e];
+            if (ep.act == ACT_RELU) t = t > 0.0f ? t : 0.0f;
+            else if (ep.act == ACT_GELU_TANH) t = gelu_tanh(t);
+            x[e] = t;
+        }
+        store_out4(C, ep.out_dt, ci, x);
+        return;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (n + e < N) store_out(C, ep.out_dt, ci + e, epilogue_value(ep, v[e], ri + e, n + e));
+}
+
+// Store the run C[m][n .. n+3] (columns >= N skipped; the caller has checked
+// m < M). The plain fp32 path uses one 16-byte store when the run is whole and
+// aligned; the epilogue path stores element by element in C's element type.
+// EPI = false compiles the plain path only (kernels that never run an epilogue).
+template <bool EPI = true>
+__device__ __forceinline__ void store_run4(const GemmArgs& g, int m, int n, f32x4 v) {
+    if (!EPI || g.ep.kind == 0) {
+        float* cp = g.C + (size_t)m * g.ldc + n;
+        if (n + 3 < g.N && (reinterpret_cast<uintptr_t>(cp) & 15) == 0) {
+            *reinterpret_cast<f32x4*>(cp) = v;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (n + e < g.N) cp[e] = v[e];
+        }
+        return;
+    }
+    epilogue_run4(g.ep, g.C, g.ldc, g.N, m, n, v);
 }
 
 // Load V consecutive elements starting at p into a register chunk, zero-filling

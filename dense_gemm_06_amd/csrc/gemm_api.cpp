@@ -251,10 +251,16 @@ int gemm_strided_batched(int opA, int opB, int64_t M, int64_t N, int64_t K, cons
     return gemm_grouped(opA, opB, dtype, &p, 1, cfg, stream);
 }
 
-int gemm_ex_workspace(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
-                      const void* B, int64_t ldb, float* C, int64_t ldc, int dtype, const gemm_config* cfg,
-                      void* workspace, int64_t workspace_bytes, void* stream) {
-    dg::clear_error();
+}  // extern "C"
+
+namespace {
+
+// The product with every option: C (element type ep.out_dt when ep.kind != 0),
+// an optional workspace (split K or packing), an optional fused epilogue. All
+// validation happens before the first launch.
+int run_product(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                int64_t ldb, void* C, int64_t ldc, int dtype, const dg::Epilogue& ep, const gemm_config* cfg,
+                void* workspace, int64_t workspace_bytes, void* stream) {
     int st = dg::validate(opA, opB, M, N, K, lda, ldb, ldc, dtype);
     if (st != GEMM_OK) return st;
     if (workspace_bytes < 0) {
@@ -267,20 +273,32 @@ int gemm_ex_workspace(int opA, int opB, int64_t M, int64_t N, int64_t K, const v
     }
     if (M == 0 || N == 0) return GEMM_OK;
     if (C == nullptr || (K > 0 && (A == nullptr || B == nullptr))) {
-        dg::set_error("NULL operand: A = %p, B = %p, C = %p (M = %lld, N = %lld, K = %lld)", A, B, (void*)C,
+        dg::set_error("NULL operand: A = %p, B = %p, C = %p (M = %lld, N = %lld, K = %lld)", A, B, C,
                       (long long)M, (long long)N, (long long)K);
         return GEMM_ERR_NULL_POINTER;
     }
     const uint64_t es = dtype == GEMM_F32 ? 4 : 2;
-    const uint64_t clen = ((uint64_t)(M - 1) * ldc + N) * 4;
-    if (K > 0) {
-        const uint64_t alen = ((uint64_t)(M - 1) * lda + K) * es;
-        const uint64_t blen = (opB == GEMM_OP_N ? (uint64_t)(K - 1) * ldb + N : (uint64_t)(N - 1) * ldb + K) * es;
-        if (ranges_overlap((uintptr_t)C, clen, (uintptr_t)A, alen) ||
-            ranges_overlap((uintptr_t)C, clen, (uintptr_t)B, blen)) {
-            dg::set_error("C overlaps A or B; the output must not alias an input");
-            return GEMM_ERR_INVALID_VALUE;
-        }
+    const uint64_t ces = (ep.kind == 0 || ep.out_dt == dg::DT_F32) ? 4 : 2;
+    const uint64_t clen = ((uint64_t)(M - 1) * ldc + N) * ces;
+    const uint64_t alen = K > 0 ? ((uint64_t)(M - 1) * lda + K) * es : 0;
+    const uint64_t blen =
+        K > 0 ? (opB == GEMM_OP_N ? (uint64_t)(K - 1) * ldb + N : (uint64_t)(N - 1) * ldb + K) * es : 0;
+    if (ranges_overlap((uintptr_t)C, clen, (uintptr_t)A, alen) ||
+        ranges_overlap((uintptr_t)C, clen, (uintptr_t)B, blen)) {
+        dg::set_error("C overlaps A or B; the output must not alias an input");
+        return GEMM_ERR_INVALID_VALUE;
+    }
+    // epilogue operands: R (C itself, or disjoint from C) and bias (disjoint from C)
+    const uint64_t rlen = (ep.kind != 0 && ep.beta != 0.0f) ? ((uint64_t)(M - 1) * ep.ldr + N) * ces : 0;
+    const uint64_t biaslen = (ep.kind != 0 && ep.bias) ? (uint64_t)N * 4 : 0;
+    if (rlen && !((uintptr_t)ep.R == (uintptr_t)C && ep.ldr == ldc) &&
+        ranges_overlap((uintptr_t)ep.R, rlen, (uintptr_t)C, clen)) {
+        dg::set_error("R overlaps C without being C itself (R == C with ldr == ldc is the in-place form)");
+        return GEMM_ERR_INVALID_VALUE;
+    }
+    if (biaslen && ranges_overlap((uintptr_t)ep.bias, biaslen, (uintptr_t)C, clen)) {
+        dg::set_error("bias overlaps C");
+        return GEMM_ERR_INVALID_VALUE;
     }
     if (workspace_bytes > 0) {
         // the whole declared workspace: aligned, and disjoint from every operand
@@ -289,13 +307,11 @@ int gemm_ex_workspace(int opA, int opB, int64_t M, int64_t N, int64_t K, const v
             dg::set_error("the workspace must be 16-byte aligned (got %p)", workspace);
             return GEMM_ERR_INVALID_VALUE;
         }
-        const uint64_t alen = K > 0 ? ((uint64_t)(M - 1) * lda + K) * es : 0;
-        const uint64_t blen =
-            K > 0 ? (opB == GEMM_OP_N ? (uint64_t)(K - 1) * ldb + N : (uint64_t)(N - 1) * ldb + K) * es : 0;
-        if (ranges_overlap(w, (uint64_t)workspace_bytes, (uintptr_t)A, alen) ||
-            ranges_overlap(w, (uint64_t)workspace_bytes, (uintptr_t)B, blen) ||
-            ranges_overlap(w, (uint64_t)workspace_bytes, (uintptr_t)C, clen)) {
-            dg::set_error("the workspace overlaps A, B or C");
+        const uint64_t wl = (uint64_t)workspace_bytes;
+        if (ranges_overlap(w, wl, (uintptr_t)A, alen) || ranges_overlap(w, wl, (uintptr_t)B, blen) ||
+            ranges_overlap(w, wl, (uintptr_t)C, clen) || ranges_overlap(w, wl, (uintptr_t)ep.R, rlen) ||
+            ranges_overlap(w, wl, (uintptr_t)ep.bias, biaslen)) {
+            dg::set_error("the workspace overlaps A, B, C or an epilogue operand");
             return GEMM_ERR_INVALID_VALUE;
         }
     }
@@ -310,13 +326,13 @@ int gemm_ex_workspace(int opA, int opB, int64_t M, int64_t N, int64_t K, const v
     if (st != GEMM_OK) return st;
     gemm_config plan;
     st = dg::plan(opA, opB, M, N, K, lda, ldb, ldc, dtype, (uintptr_t)A, (uintptr_t)B, (uintptr_t)C, info.num_cus,
-                  info.arch, workspace_bytes, cfg, &plan);
+                  info.arch, workspace_bytes, ep.kind != 0, cfg, &plan);
     if (st != GEMM_OK) return st;
 
     dg::GemmArgs args;
     args.A = A;
     args.B = B;
-    args.C = C;
+    args.C = static_cast<float*>(C);
     args.lda = lda;
     args.ldb = ldb;
     args.ldc = ldc;
@@ -332,6 +348,7 @@ int gemm_ex_workspace(int opA, int opB, int64_t M, int64_t N, int64_t K, const v
     args.work = static_cast<float*>(workspace);
     args.work_ld = (N + 3) / 4 * 4;
     args.work_slice = M * args.work_ld;
+    args.ep = ep;
     (void)hipGetLastError();  // clear a stale error left by earlier unrelated work
     if (plan.pack == 2) {
         // zero-padded copies of A and B in the workspace, then the product on them
@@ -354,7 +371,7 @@ int gemm_ex_workspace(int opA, int opB, int64_t M, int64_t N, int64_t K, const v
         return GEMM_ERR_LAUNCH;
     }
     if (plan.split_k > 1)
-        dg::launch_splitk_reduce(args.work, plan.split_k, args.work_slice, args.work_ld, (int)M, (int)N, C, ldc,
+        dg::launch_splitk_reduce(args.work, plan.split_k, args.work_slice, args.work_ld, (int)M, (int)N, C, ldc, ep,
                                  (hipStream_t)stream);
     he = hipGetLastError();
     if (he != hipSuccess) {
@@ -362,6 +379,74 @@ int gemm_ex_workspace(int opA, int opB, int64_t M, int64_t N, int64_t K, const v
         return GEMM_ERR_LAUNCH;
     }
     return GEMM_OK;
+}
+
+dg::Epilogue plain_epilogue() {
+    dg::Epilogue ep;
+    memset(&ep, 0, sizeof ep);
+    ep.alpha = 1.0f;
+    return ep;
+}
+
+// gemm_epilogue -> the kernels' descriptor; an identity epilogue (alpha 1, no
+// residual, no bias, no activation, fp32 C) becomes the plain store.
+int to_epilogue(const gemm_epilogue* e, dg::Epilogue* out) {
+    *out = plain_epilogue();
+    if (e == nullptr) return GEMM_OK;
+    if (e->out_dtype < GEMM_F32 || e->out_dtype > GEMM_BF16) {
+        dg::set_error("epilogue out_dtype %d is not GEMM_F32, GEMM_F16 or GEMM_BF16", e->out_dtype);
+        return GEMM_ERR_INVALID_VALUE;
+    }
+    if (e->activation < GEMM_ACT_NONE || e->activation > GEMM_ACT_GELU_TANH) {
+        dg::set_error("epilogue activation %d is not a gemm_activation", e->activation);
+        return GEMM_ERR_INVALID_VALUE;
+    }
+    const bool identity = e->alpha == 1.0f && e->beta == 0.0f && e->bias == nullptr &&
+                          e->activation == GEMM_ACT_NONE && e->out_dtype == GEMM_F32;
+    if (identity) return GEMM_OK;
+    out->kind = 1;
+    out->act = e->activation;
+    out->out_dt = e->out_dtype;
+    out->alpha = e->alpha;
+    out->beta = e->beta;
+    out->R = e->R;
+    out->ldr = e->ldr;
+    out->bias = e->bias;
+    return GEMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_ex_workspace(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                      const void* B, int64_t ldb, float* C, int64_t ldc, int dtype, const gemm_config* cfg,
+                      void* workspace, int64_t workspace_bytes, void* stream) {
+    dg::clear_error();
+    return run_product(opA, opB, M, N, K, A, lda, B, ldb, C, ldc, dtype, plain_epilogue(), cfg, workspace,
+                       workspace_bytes, stream);
+}
+
+int gemm_ex_epilogue(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                     int64_t ldb, void* C, int64_t ldc, int dtype, const gemm_epilogue* epilogue,
+                     const gemm_config* cfg, void* workspace, int64_t workspace_bytes, void* stream) {
+    dg::clear_error();
+    dg::Epilogue ep;
+    int st = to_epilogue(epilogue, &ep);
+    if (st != GEMM_OK) return st;
+    if (ep.kind != 0 && ep.beta != 0.0f && M > 0 && N > 0) {
+        if (ep.R == nullptr) {
+            dg::set_error("epilogue beta = %g needs R, which is NULL", (double)ep.beta);
+            return GEMM_ERR_NULL_POINTER;
+        }
+        if (ep.ldr < std::max<int64_t>(1, N)) {
+            dg::set_error("epilogue ldr = %lld is smaller than max(1, N) = %lld", (long long)ep.ldr,
+                          (long long)std::max<int64_t>(1, N));
+            return GEMM_ERR_INVALID_VALUE;
+        }
+    }
+    return run_product(opA, opB, M, N, K, A, lda, B, ldb, C, ldc, dtype, ep, cfg, workspace, workspace_bytes,
+                       stream);
 }
 
 int gemm_ex(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
@@ -382,20 +467,24 @@ int gemm_plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, in
         dg::set_error("gemm_plan: out is NULL");
         return GEMM_ERR_NULL_POINTER;
     }
-    return dg::plan(opA, opB, M, N, K, lda, ldb, ldc, dtype, a_addr, b_addr, c_addr, num_cus, arch, 0, request,
-                    out);
+    return dg::plan(opA, opB, M, N, K, lda, ldb, ldc, dtype, a_addr, b_addr, c_addr, num_cus, arch, 0, false,
+                    request, out);
 }
 
 int gemm_plan_workspace(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
                         int dtype, uintptr_t a_addr, uintptr_t b_addr, uintptr_t c_addr, int num_cus,
-                        const char* arch, int64_t workspace_bytes, const gemm_config* request, gemm_config* out) {
+                        const char* arch, int64_t workspace_bytes, const gemm_epilogue* epilogue,
+                        const gemm_config* request, gemm_config* out) {
     dg::clear_error();
     if (out == nullptr) {
         dg::set_error("gemm_plan_workspace: out is NULL");
         return GEMM_ERR_NULL_POINTER;
     }
+    dg::Epilogue ep;
+    const int st = to_epilogue(epilogue, &ep);
+    if (st != GEMM_OK) return st;
     return dg::plan(opA, opB, M, N, K, lda, ldb, ldc, dtype, a_addr, b_addr, c_addr, num_cus, arch,
-                    workspace_bytes, request, out);
+                    workspace_bytes, ep.kind != 0, request, out);
 }
 
 int gemm_menu_size(void) { return dg::kMenuSize; }

@@ -242,14 +242,8 @@ __global__ __launch_bounds__(512) void mfma16_dma(GemmArgs g) {
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
                 const int n = n0 + wn * 64 + j * 32 + rg * 8 + lh * 4;
-                float* cp = g.C + (size_t)m * g.ldc + n;
-                const f32x4 v = {acc[i][j][4 * rg], acc[i][j][4 * rg + 1], acc[i][j][4 * rg + 2], acc[i][j][4 * rg + 3]};
-                if ((reinterpret_cast<uintptr_t>(cp) & 15) == 0) {
-                    *reinterpret_cast<f32x4*>(cp) = v;
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) cp[e] = v[e];
-                }
+                store_run4<false>(g, m, n, f32x4{acc[i][j][4 * rg], acc[i][j][4 * rg + 1], acc[i][j][4 * rg + 2],
+                                                 acc[i][j][4 * rg + 3]});
             }
     }
 }

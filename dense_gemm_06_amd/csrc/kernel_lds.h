@@ -161,15 +161,8 @@ __device__ __forceinline__ void lds_tile(const GemmArgs& g, int tm, int tn) {
 #pragma unroll
             for (int qb = 0; qb < RB; ++qb) {
                 const int n = n0 + qb * 64 + tx * 4;
-                float* cp = g.C + (size_t)m * g.ldc + n;
                 const float* v = &acc[4 * q + r][4 * qb];
-                if (n + 3 < N && (reinterpret_cast<uintptr_t>(cp) & 15) == 0) {
-                    *reinterpret_cast<f32x4*>(cp) = f32x4{v[0], v[1], v[2], v[3]};
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (n + e < N) cp[e] = v[e];
-                }
+                store_run4(g, m, n, f32x4{v[0], v[1], v[2], v[3]});
             }
         }
 }

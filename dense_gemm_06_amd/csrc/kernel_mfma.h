@@ -184,15 +184,7 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs& g, int tm, int tn) {
 #pragma unroll
         for (int j = 0; j < SN; ++j) {
             const int n = n0 + wni * TWN + j * 16 + lg * 4;
-            float* cp = g.C + (size_t)m * g.ldc + n;
-            const f32x4 v = acc[i][j];
-            if (n + 3 < N && (reinterpret_cast<uintptr_t>(cp) & 15) == 0) {
-                *reinterpret_cast<f32x4*>(cp) = v;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (n + e < N) cp[e] = v[e];
-            }
+            store_run4(g, m, n, acc[i][j]);
         }
     }
 }
@@ -391,29 +383,14 @@ __device__ __forceinline__ void mfma32_tile(const GemmArgs& g, int tm, int tn) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int n = n0 + wni * TWN + q * 64 + 16 * lg + 4 * r;
-                    float* cp = g.C + (size_t)m * g.ldc + n;
-                    const f32x4 v = {acc[i][4 * q][r], acc[i][4 * q + 1][r], acc[i][4 * q + 2][r], acc[i][4 * q + 3][r]};
-                    if (n + 3 < N && (reinterpret_cast<uintptr_t>(cp) & 15) == 0) {
-                        *reinterpret_cast<f32x4*>(cp) = v;
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (n + e < N) cp[e] = v[e];
-                    }
+                    store_run4(g, m, n,
+                               f32x4{acc[i][4 * q][r], acc[i][4 * q + 1][r], acc[i][4 * q + 2][r], acc[i][4 * q + 3][r]});
                 }
         } else {
 #pragma unroll
             for (int j = 0; j < SN; ++j) {
                 const int n = n0 + wni * TWN + j * 16 + lg * 4;
-                float* cp = g.C + (size_t)m * g.ldc + n;
-                const f32x4 v = acc[i][j];
-                if (n + 3 < N && (reinterpret_cast<uintptr_t>(cp) & 15) == 0) {
-                    *reinterpret_cast<f32x4*>(cp) = v;
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (n + e < N) cp[e] = v[e];
-                }
+                store_run4(g, m, n, acc[i][j]);
             }
         }
     }

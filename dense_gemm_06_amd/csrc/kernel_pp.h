@@ -218,15 +218,9 @@ __global__ __launch_bounds__(512) void mfma16_pp(GemmArgs g) {
 #pragma unroll
             for (int rg = 0; rg < (MF == 16 ? 1 : 4); ++rg) {
                 const int n = n0 + wl * 64 + j * MF + (MF == 16 ? lg * 4 : rg * 8 + lh * 4);
-                float* cp = g.C + (size_t)m * g.ldc + n;
-                const f32x4 v = {acc[i][j][4 * rg], acc[i][j][4 * rg + 1], acc[i][j][4 * rg + 2], acc[i][j][4 * rg + 3]};
-                if (n + 4 <= g.N && (reinterpret_cast<uintptr_t>(cp) & 15) == 0) {
-                    *reinterpret_cast<f32x4*>(cp) = v;
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (n + e < g.N) cp[e] = v[e];
-                }
+                // the 32x32 form keeps to plain stores: its epilogue branch runs out of registers
+                store_run4<MF == 16>(g, m, n, f32x4{acc[i][j][4 * rg], acc[i][j][4 * rg + 1], acc[i][j][4 * rg + 2],
+                                                    acc[i][j][4 * rg + 3]});
             }
     }
 }

@@ -24,12 +24,13 @@ int launch_mfma_f32_grouped(int id, const GroupArgs& a, unsigned grid, hipStream
 int launch_mfma_f16_grouped(int id, const GroupArgs& a, unsigned grid, hipStream_t stream);
 int launch_mfma_bf16_grouped(int id, const GroupArgs& a, unsigned grid, hipStream_t stream);
 
-// C[i][j] = sum over s = 0..S-1, in that order, of work[s * slice + i * work_ld + j]
-// for i < M, j < N: the fixed-order reduction of a split-K launch.
 // Zero-padded copies of A and B in one launch (elem_size 2 or 4).
 int launch_pack(int elem_size, const PackJob& a, const PackJob& b, hipStream_t stream);
 
-int launch_splitk_reduce(const float* work, int S, int64_t slice, int64_t work_ld, int M, int N, float* C,
-                         int64_t ldc, hipStream_t stream);
+// C[i][j] = sum over s = 0..S-1, in that order, of work[s * slice + i * work_ld + j]
+// for i < M, j < N: the fixed-order reduction of a split-K launch, followed by the
+// fused epilogue when ep.kind != 0 (C then has element type ep.out_dt).
+int launch_splitk_reduce(const float* work, int S, int64_t slice, int64_t work_ld, int M, int N, void* C,
+                         int64_t ldc, const Epilogue& ep, hipStream_t stream);
 
 }  // namespace dg

@@ -36,6 +36,11 @@ struct MenuEntry {
 // passed its parity tests on the device.
 constexpr bool schedule_enabled(int sched) { return sched != 3; }
 
+// Configurations whose kernel applies a fused epilogue (every other one stores the
+// plain fp32 accumulator only): all but the 32x32x16 ping-pong and the
+// software-pipelined kernels.
+constexpr bool epilogue_capable(int sched) { return sched != 3 && sched != 4; }
+
 // Configurations that also have a grouped (persistent) form: the register-staged
 // schedule, which masks every edge, except the 4-wave 256 x 256 tiles (their
 // grouped form runs out of registers).
@@ -114,6 +119,21 @@ constexpr bool grouped_capable(int sched, int bm, int bn, int wm, int wn) {
 
 constexpr int kMenuSize = 80;
 
+// Fused epilogue ("Shared memory and tensor cores", section 13.10: bias,
+// activation, residual add or type cast applied to the accumulator before the
+// store). kind = 0: plain fp32 store of the accumulator. Otherwise
+//   C[m][n] = act(alpha * acc + beta * R[m][n] + bias[n])   (beta = 0: R unread)
+// stored as out_dt (DT_F32, DT_F16 or DT_BF16, round to nearest even); R has
+// C's element type and may be C itself.
+enum Activation { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU_TANH = 2 };
+struct Epilogue {
+    int kind, act, out_dt, pad;
+    float alpha, beta;
+    const void* R;
+    int64_t ldr;
+    const float* bias;
+};
+
 // Arguments every kernel receives (by value).
 struct GemmArgs {
     const void* A;
@@ -130,6 +150,7 @@ struct GemmArgs {
     int k_split, k_chunk;
     float* work;
     int64_t work_slice, work_ld;
+    Epilogue ep;            // C's element type is ep.out_dt when ep.kind != 0
 };
 
 // One operand copy of a packing launch: rows x cols elements of src (leading

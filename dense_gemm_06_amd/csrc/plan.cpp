@@ -160,7 +160,7 @@ static int64_t split_workspace(int64_t S, int64_t M, int64_t N) { return S * M *
 
 int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int dtype,
          uintptr_t a, uintptr_t b, uintptr_t c, int num_cus, const char* arch, int64_t ws_bytes,
-         const gemm_config* req, gemm_config* out) {
+         bool fused_epilogue, const gemm_config* req, gemm_config* out) {
     (void)c;
     int st = validate(opA, opB, M, N, K, lda, ldb, ldc, dtype);
     if (st != GEMM_OK) return st;
@@ -249,6 +249,7 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
         if (want_wm && (e.variant == V_MFMA ? e.wm : 1) != want_wm) continue;
         if (want_sched && e.sched != want_sched) continue;
         if (!schedule_enabled(e.sched)) continue;
+        if (fused_epilogue && !epilogue_capable(e.sched)) continue;
         // the direct-copy kernels copy whole tiles: no masking of M, N or K edges on
         // the operands (the packed copies are whole tiles; C is masked at the store)
         if (e.sched >= 2 && (Mx % e.bm != 0 || Nx % e.bn != 0 || Kx % e.bk != 0 || Kx == 0)) continue;

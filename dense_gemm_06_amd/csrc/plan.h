@@ -15,10 +15,11 @@ const char* last_error();
 
 int validate(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
              int dtype);
-// ws_bytes: workspace available for split K (0: never split).
+// ws_bytes: workspace available for split K or packing (0: neither).
+// fused_epilogue: the call applies an epilogue (only epilogue_capable kernels).
 int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int dtype,
          uintptr_t a, uintptr_t b, uintptr_t c, int num_cus, const char* arch, int64_t ws_bytes,
-         const gemm_config* req, gemm_config* out);
+         bool fused_epilogue, const gemm_config* req, gemm_config* out);
 int menu_entry(int index, int* variant, int* dtype, int* opb, gemm_config* out);
 
 // Packed-operand layout: A padded to Mp x Kp, B to Kp x Np (row-major) or Np x Kp

@@ -16,8 +16,8 @@ namespace dg {
 // one aligned 16-byte load; columns N..work_ld-1 of a plane are read (never
 // written by the slices) but not stored.
 __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ work, int S, int64_t slice,
-                                                     int64_t work_ld, int M, int N, float* __restrict__ C,
-                                                     int64_t ldc) {
+                                                     int64_t work_ld, int M, int N, void* __restrict__ Cv,
+                                                     int64_t ldc, Epilogue ep) {
     const int quads = (N + 3) >> 2;
     const int64_t total = (int64_t)M * quads;
     for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < total; q += (int64_t)gridDim.x * 256) {
@@ -26,7 +26,15 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ w
         const float* w = work + (size_t)i * (size_t)work_ld + j;
         f32x4 acc = *reinterpret_cast<const f32x4*>(w);
         for (int s = 1; s < S; ++s) acc += *reinterpret_cast<const f32x4*>(w + (size_t)s * (size_t)slice);
-        float* c = C + (size_t)i * (size_t)ldc + j;
+        if (ep.kind != 0) {
+            // the fused epilogue applies to the complete sum
+            for (int e = 0; e < 4; ++e)
+                if (j + e < N)
+                    store_out(Cv, ep.out_dt, (size_t)i * (size_t)ldc + j + e,
+                              epilogue_value(ep, acc[e], (size_t)i * (size_t)ep.ldr + j + e, j + e));
+            continue;
+        }
+        float* c = static_cast<float*>(Cv) + (size_t)i * (size_t)ldc + j;
         if (j + 4 <= N && (reinterpret_cast<uintptr_t>(c) & 15) == 0) {
             *reinterpret_cast<f32x4*>(c) = acc;
         } else {
@@ -36,11 +44,11 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ w
     }
 }
 
-int launch_splitk_reduce(const float* work, int S, int64_t slice, int64_t work_ld, int M, int N, float* C,
-                         int64_t ldc, hipStream_t stream) {
+int launch_splitk_reduce(const float* work, int S, int64_t slice, int64_t work_ld, int M, int N, void* C,
+                         int64_t ldc, const Epilogue& ep, hipStream_t stream) {
     const int64_t total = (int64_t)M * ((N + 3) / 4);
     const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>((total + 255) / 256, 4096));
-    hipLaunchKernelGGL(splitk_reduce, dim3(grid), dim3(256), 0, stream, work, S, slice, work_ld, M, N, C, ldc);
+    hipLaunchKernelGGL(splitk_reduce, dim3(grid), dim3(256), 0, stream, work, S, slice, work_ld, M, N, C, ldc, ep);
     return 0;
 }
 

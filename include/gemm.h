@@ -23,7 +23,8 @@
  *    Column-major B is the layout the learn-cutedsl README's naive kernel reads
  *    (B indexed as [column, k]) and the one its layout section calls typical.
  *  - dtype gives the element type of A and B: GEMM_F32 (IEEE binary32),
- *    GEMM_F16 (IEEE binary16), GEMM_BF16 (bfloat16). C is always fp32.
+ *    GEMM_F16 (IEEE binary16), GEMM_BF16 (bfloat16). C is fp32 (a fused
+ *    epilogue, gemm_ex_epilogue, may store it as fp16 or bf16).
  *  - Pointers A, B, C are DEVICE pointers (memory the caller allocated on the
  *    current HIP device); the caller owns them and the stream. A and B must not
  *    overlap C (the kernels read them through restrict-qualified pointers);
@@ -160,11 +161,50 @@ int gemm_ex_workspace(int opA, int opB, int64_t M, int64_t N, int64_t K, const v
                       const void* B, int64_t ldb, float* C, int64_t ldc, int dtype, const gemm_config* cfg,
                       void* workspace, int64_t workspace_bytes, void* stream);
 
-/* gemm_plan_workspace -- host-only: the configuration gemm_ex_workspace would use
- * with workspace_bytes of workspace (gemm_plan is this with 0). */
+/*
+ * Fused epilogue ("Shared memory and tensor cores", section 13.10: apply a bias,
+ * an activation, a residual add or a type cast to the accumulator before the
+ * store, saving a kernel and its memory round trip). gemm_ex_epilogue computes
+ *     C[i][j] = act(alpha * (A @ B)[i][j] + beta * R[i][j] + bias[j])
+ * with the product accumulated in fp32, the epilogue in fp32, and C stored in
+ * out_dtype (round to nearest even). R is read only when beta != 0; it has C's
+ * element type and leading dimension ldr, and may be C itself (R == C with
+ * ldr == ldc: the in-place BLAS form C = alpha A B + beta C); otherwise it must
+ * not overlap C. bias (NULL = none) holds N fp32 values and must not overlap C.
+ * GEMM_ACT_GELU_TANH is GELU in its tanh form, x/2 (1 + tanh(sqrt(2/pi) (x +
+ * 0.044715 x^3))). An identity epilogue (alpha 1, beta 0, no bias, no
+ * activation, fp32 C) is the plain store.
+ */
+typedef enum { GEMM_ACT_NONE = 0, GEMM_ACT_RELU = 1, GEMM_ACT_GELU_TANH = 2 } gemm_activation;
+
+typedef struct gemm_epilogue {
+    float alpha, beta;
+    const void* R;      /* residual (device pointer), element type out_dtype */
+    int64_t ldr;        /* leading dimension of R in elements (>= N when beta != 0) */
+    const float* bias;  /* NULL or N fp32 values (device pointer) */
+    int32_t activation; /* gemm_activation, applied last */
+    int32_t out_dtype;  /* GEMM_F32, GEMM_F16 or GEMM_BF16: element type of C and R */
+} gemm_epilogue;
+
+/*
+ * gemm_ex_epilogue -- gemm_ex_workspace with a fused epilogue; C's element type
+ * is epilogue->out_dtype (epilogue = NULL: plain fp32 C). Errors as for
+ * gemm_ex_workspace, plus GEMM_ERR_INVALID_VALUE for a bad out_dtype or
+ * activation, a short ldr, or overlaps of R or bias with C; GEMM_ERR_NULL_POINTER
+ * for a NULL R with beta != 0. Split K applies the epilogue once, to the
+ * complete sum; packing applies it in the product kernel.
+ */
+int gemm_ex_epilogue(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                     int64_t ldb, void* C, int64_t ldc, int dtype, const gemm_epilogue* epilogue,
+                     const gemm_config* cfg, void* workspace, int64_t workspace_bytes, void* stream);
+
+/* gemm_plan_workspace -- host-only: the configuration gemm_ex_epilogue (or, with
+ * epilogue = NULL, gemm_ex_workspace) would use with workspace_bytes of workspace
+ * (gemm_plan is this with 0 and NULL). */
 int gemm_plan_workspace(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
                         int dtype, uintptr_t a_addr, uintptr_t b_addr, uintptr_t c_addr, int num_cus,
-                        const char* arch, int64_t workspace_bytes, const gemm_config* request, gemm_config* out);
+                        const char* arch, int64_t workspace_bytes, const gemm_epilogue* epilogue,
+                        const gemm_config* request, gemm_config* out);
 
 /*
  * Grouped and batched products: several independent C = A @ B in one launch

@@ -28,3 +28,35 @@ def normalized_error(C, Cref, D) -> float:
     with np.errstate(divide="ignore", invalid="ignore"):
         r = np.where(zero, 0.0, diff / np.where(zero, 1.0, D))
     return float(r.max())
+
+
+# Rounding unit of a stored output type (half an ulp relative, round to nearest even).
+OUT_UNIT = {"f32": 0.0, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+# Smallest positive subnormal spacing of the output type (absolute floor of its rounding).
+OUT_TINY = {"f32": 0.0, "f16": 2.0 ** -25, "bf16": 2.0 ** -134}
+
+
+def epilogue_error(C, ref, Dp, in_dtype: str, out_dtype: str) -> float:
+    """Largest ratio |C - ref| / bound over all entries; <= 1 passes.
+
+    bound = 1.2 TOL[in] Dp + 1e-6 Dp + OUT_UNIT[out] |ref| + OUT_TINY[out]:
+    the product's normalized tolerance scaled through alpha, the fp32 rounding of
+    the epilogue's own operations (a few units of 2^-24 of Dp), the activation's
+    Lipschitz constant (1 for ReLU, under 1.13 for GELU) and its fp32 evaluation,
+    and the rounding of the stored value to the output type. Non-finite C fails.
+    """
+    C = np.asarray(C, dtype=np.float64)
+    if C.shape != ref.shape:
+        raise ValueError(f"shape mismatch {C.shape} vs {ref.shape}")
+    if C.size == 0:
+        return 0.0
+    if not np.all(np.isfinite(C)):
+        return float("inf")
+    bound = (1.2 * TOL[in_dtype] + 1e-6) * Dp + OUT_UNIT[out_dtype] * np.abs(ref) + OUT_TINY[out_dtype]
+    diff = np.abs(C - ref)
+    zero = bound == 0
+    if np.any(diff[zero] != 0):
+        return float("inf")
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(zero, 0.0, diff / np.where(zero, 1.0, bound))
+    return float(r.max())

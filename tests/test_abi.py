@@ -35,7 +35,7 @@ def test_header_symbols_exported():
     assert set(names) == {"gemm", "gemm_ex", "gemm_plan", "gemm_menu_size", "gemm_menu_entry",
                           "gemm_device_info", "gemm_status_string", "gemm_last_error",
                           "gemm_grouped", "gemm_grouped_plan", "gemm_strided_batched",
-                          "gemm_ex_workspace", "gemm_plan_workspace"}
+                          "gemm_ex_workspace", "gemm_plan_workspace", "gemm_ex_epilogue"}
     lib = dg.library()
     for n in names:
         assert hasattr(lib, n), n
@@ -307,9 +307,9 @@ def test_strided_batched_is_one_grouped_entry():
 
 
 # ----------------------------------------------------------------------------- split K
-def wplan(M, N, K, dtype="f32", ws=1 << 30, req=None, check=True):
+def wplan(M, N, K, dtype="f32", ws=1 << 30, req=None, check=True, epi=None):
     return dg.gemm_plan_workspace(0, 0, M, N, K, max(1, K), max(1, N), max(1, N), dg.DTYPE_CODE[dtype], 4096, 4096,
-                                  4096, 256, "gfx950", ws, req, check=check)
+                                  4096, 256, "gfx950", ws, req, check=check, epi=epi)
 
 
 def test_split_needs_workspace():
@@ -403,3 +403,46 @@ def test_pack_errors():
     st, c = dg.gemm_plan_workspace(0, 0, 64, 64, 63, 63, 64, 64, dg.GEMM_F16, 0, 0, 0, 256, "gfx950", 1 << 20,
                                    dg.request(vec=1))
     assert st == 0 and c.pack == 2 and c.vec == 1
+
+
+# ----------------------------------------------------------------------------- fused epilogue
+def test_epilogue_plan_avoids_plain_only_kernels():
+    gelu = dg.epilogue(alpha=2.0, activation="gelu_tanh")
+    st, _ = wplan(4096, 4096, 4096, "f16", req=dg.request(schedule=4), epi=gelu, check=False)
+    assert st == dg.GEMM_ERR_UNSUPPORTED
+    # the identity epilogue is the plain store: any kernel
+    assert wplan(4096, 4096, 4096, "f16", req=dg.request(schedule=4), epi=dg.epilogue())[1].schedule == 4
+    # the headline configuration keeps its ping-pong kernel with an epilogue
+    assert wplan(4096, 4096, 4096, "f16", epi=gelu)[1].schedule == 2
+    st, _ = wplan(64, 64, 64, epi=dg.epilogue(out_dtype=7), check=False)
+    assert st == dg.GEMM_ERR_INVALID_VALUE
+
+
+def test_epilogue_rejections_before_device():
+    ex = dg.gemm_ex_epilogue
+    A, B, C = 1 << 30, (1 << 30) + (1 << 22), (1 << 30) + (2 << 22)
+    R, bias = (1 << 30) + (4 << 22), (1 << 30) + (5 << 22)
+    args = (0, 0, 64, 64, 64, A, 64, B, 64, C, 64, dg.GEMM_F32)
+
+    def call(epi, ws=None, wsb=0):
+        return ex(*args, epi, None, ws, wsb, None, check=False)
+    assert call(dg.epilogue(out_dtype=5)) == dg.GEMM_ERR_INVALID_VALUE
+    assert call(dg.epilogue(activation=9, alpha=2.0)) == dg.GEMM_ERR_INVALID_VALUE
+    assert call(dg.epilogue(beta=1.0, R=None, ldr=64)) == dg.GEMM_ERR_NULL_POINTER
+    assert call(dg.epilogue(beta=1.0, R=R, ldr=10)) == dg.GEMM_ERR_INVALID_VALUE
+    # R overlapping C without being C
+    assert call(dg.epilogue(beta=1.0, R=C + 256, ldr=64)) == dg.GEMM_ERR_INVALID_VALUE
+    assert "R overlaps C" in dg.gemm_last_error()
+    # R == C with another leading dimension is not the in-place form
+    assert call(dg.epilogue(beta=1.0, R=C, ldr=65)) == dg.GEMM_ERR_INVALID_VALUE
+    assert call(dg.epilogue(bias=C + 64, alpha=2.0)) == dg.GEMM_ERR_INVALID_VALUE
+    assert "bias" in dg.gemm_last_error()
+    # the workspace must not overlap the epilogue operands either
+    assert call(dg.epilogue(beta=1.0, R=R, ldr=64), ws=R, wsb=1 << 16) == dg.GEMM_ERR_INVALID_VALUE
+    # C in a 16-bit output type overlapping A is caught with C's own element size
+    args16 = (0, 0, 64, 64, 64, A, 64, B, 64, A - 64 * 64 * 2 + 64, 64, dg.GEMM_F32)
+    assert ex(*args16, dg.epilogue(out_dtype="f16", alpha=2.0), None, None, 0, None, check=False) == \
+        dg.GEMM_ERR_INVALID_VALUE
+    # empty output: nothing to check, nothing launched
+    assert ex(0, 0, 0, 64, 64, 0, 64, 0, 64, 0, 64, 0, dg.epilogue(beta=1.0), None, None, 0, None,
+              check=False) == dg.GEMM_OK
