@@ -203,6 +203,42 @@ __device__ __forceinline__ uint64_t uni64(uint64_t x) {
 }
 __device__ __forceinline__ float unif(float x) { return __uint_as_float(uni32(__float_as_uint(x))); }
 
+// The epilogue of the run C[m][n .. n+3] (columns >= N skipped). A whole run at
+// aligned addresses moves as one vector for R and for C, and reads bias as one
+// 16-byte load when aligned.
+__device__ __forceinline__ void epilogue_run4_body(const Epilogue& ep, void* C, int64_t ldc, int N, int m, int n,
+                                                   f32x4 v) {
+    const size_t ci = (size_t)m * ldc + n, ri = (size_t)m * ep.ldr + n;
+    const int vb = ep.out_dt == DT_F32 ? 16 : 8;  // bytes of a whole run
+    const int es = ep.out_dt == DT_F32 ? 4 : 2;
+    const bool whole = n + 4 <= N;
+    const bool c_vec = whole && ((reinterpret_cast<uintptr_t>(C) + ci * es) & (vb - 1)) == 0;
+    const bool r_vec = whole && ep.beta != 0.0f && ((reinterpret_cast<uintptr_t>(ep.R) + ri * es) & (vb - 1)) == 0;
+    if (c_vec && (ep.beta == 0.0f || r_vec)) {
+        const f32x4 r = ep.beta != 0.0f ? load_out4(ep.R, ep.out_dt, ri) : f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 b = {0.f, 0.f, 0.f, 0.f};
+        if (ep.bias) {
+            if ((reinterpret_cast<uintptr_t>(ep.bias + n) & 15) == 0) b = *reinterpret_cast<const f32x4*>(ep.bias + n);
+            else b = f32x4{ep.bias[n], ep.bias[n + 1], ep.bias[n + 2], ep.bias[n + 3]};
+        }
+        f32x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float t = ep.alpha * v[e];
+            if (ep.beta != 0.0f) t = fmaf(ep.beta, r[e], t);
+            t += b[e];
+            if (ep.act == ACT_RELU) t = t > 0.0f ? t : 0.0f;
+            else if (ep.act == ACT_GELU_TANH) t = gelu_tanh(t);
+            x[e] = t;
+        }
+        store_out4(C, ep.out_dt, ci, x);
+        return;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (n + e < N) store_out(C, ep.out_dt, ci + e, epilogue_value(ep, v[e], ri + e, n + e));
+}
+
 __device__ __attribute__((noinline)) void epilogue_run4(const Epilogue ep_in, void* C_in, int64_t ldc_in, int N_in,
                                                         int m, int n, f32x4 v) {
     Epilogue ep;
@@ -217,30 +253,7 @@ __device__ __attribute__((noinline)) void epilogue_run4(const Epilogue ep_in, vo
     void* C = reinterpret_cast<void*>(uni64(reinterpret_cast<uint64_t>(C_in)));
     const int64_t ldc = (int64_t)uni64((uint64_t)ldc_in);
     const int N = (int)uni32((uint32_t)N_in);
-    const size_t ci = (size_t)m * ldc + n, ri = (size_t)m * ep.ldr + n;
-    const int vb = ep.out_dt == DT_F32 ? 16 : 8;  // bytes of a whole run
-    const int es = ep.out_dt == DT_F32 ? 4 : 2;
-    const bool whole = n + 4 <= N;
-    const bool c_vec = whole && ((reinterpret_cast<uintptr_t>(C) + ci * es) & (vb - 1)) == 0;
-    const bool r_vec = whole && ep.beta != 0.0f && ((reinterpret_cast<uintptr_t>(ep.R) + ri * es) & (vb - 1)) == 0;
-    if (c_vec && (ep.beta == 0.0f || r_vec)) {
-        const f32x4 r = ep.beta != 0.0f ? load_out4(ep.R, ep.out_dt, ri) : f32x4{0.f, 0.f, 0.f, 0.f};
-        f32x4 x;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            float t = ep.alpha * v[e];
-            if (ep.beta != 0.0f) t = fmaf(ep.beta, r[e], t);
-            if (ep.bias) t += ep.bias[n + e];
-            if (ep.act == ACT_RELU) t = t > 0.0f ? t : 0.0f;
-            else if (ep.act == ACT_GELU_TANH) t = gelu_tanh(t);
-            x[e] = t;
-        }
-        store_out4(C, ep.out_dt, ci, x);
-        return;
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-        if (n + e < N) store_out(C, ep.out_dt, ci + e, epilogue_value(ep, v[e], ri + e, n + e));
+    epilogue_run4_body(ep, C, ldc, N, m, n, v);
 }
 
 // Store the run C[m][n .. n+3] (columns >= N skipped; the caller has checked

@@ -205,6 +205,43 @@ __global__ __launch_bounds__(512) void mfma16_pp(GemmArgs g) {
     }
     if (grp == 1) mma();
 
+    if constexpr (MF == 16) {
+        if (g.ep.kind != 0) {
+            // Fused epilogue, staged through LDS (free once every wave's last fragment
+            // reads are done): each wave writes half of its 128 x 64 fp32 tile into its
+            // own 16 KB slot (chunk c of row r at c ^ (r & 15): conflict-free writes of the
+            // fragment layout and reads of whole rows), then reads back whole rows,
+            // 4 columns per lane, and applies the epilogue with coalesced row stores.
+            // Only this wave touches its slot; the wave barrier keeps the compiler from
+            // moving LDS accesses across the write/read phases, which the hardware
+            // executes in order within a wave.
+            __syncthreads();
+            char* slot = reinterpret_cast<char*>(grp == 0 ? &sA[0][0] : &sB[0][0]) + wl * 16384;
+            const int cm0 = m0 + grp * 128, cn0 = n0 + wl * 64;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    const int row = ii * 16 + l16;
+#pragma unroll
+                    for (int j = 0; j < SJ; ++j) {
+                        const int chunk = j * 4 + lg;
+                        *reinterpret_cast<f32x4*>(slot + row * 256 + ((chunk ^ (row & 15)) << 4)) = acc[h * 4 + ii][j];
+                    }
+                }
+                __builtin_amdgcn_wave_barrier();
+                for (int it = 0; it < 16; ++it) {
+                    const int row = it * 4 + (lane >> 4), chunk = lane & 15;
+                    const f32x4 v = *reinterpret_cast<const f32x4*>(slot + row * 256 + ((chunk ^ (row & 15)) << 4));
+                    const int m = cm0 + h * 64 + row;
+                    if (m < g.M) epilogue_run4_body(g.ep, g.C, g.ldc, g.N, m, cn0 + chunk * 4, v);
+                }
+                __builtin_amdgcn_wave_barrier();
+            }
+            return;
+        }
+    }
+
     // epilogue: lane owns C[m][n..n+3]; 16x16: one run per subtile (n = 4*lg ..);
     // 32x32: register r of the subtile holds row n = 8(r/4) + 4*lh + r%4, so four runs.
     // The operands may be zero-padded copies larger than C (whole tiles): rows >= M
@@ -218,9 +255,10 @@ __global__ __launch_bounds__(512) void mfma16_pp(GemmArgs g) {
 #pragma unroll
             for (int rg = 0; rg < (MF == 16 ? 1 : 4); ++rg) {
                 const int n = n0 + wl * 64 + j * MF + (MF == 16 ? lg * 4 : rg * 8 + lh * 4);
-                // the 32x32 form keeps to plain stores: its epilogue branch runs out of registers
-                store_run4<MF == 16>(g, m, n, f32x4{acc[i][j][4 * rg], acc[i][j][4 * rg + 1], acc[i][j][4 * rg + 2],
-                                                    acc[i][j][4 * rg + 3]});
+                // plain stores (the 16x16 form runs its epilogue staged above; the 32x32
+                // form is plain-store only)
+                store_run4<false>(g, m, n, f32x4{acc[i][j][4 * rg], acc[i][j][4 * rg + 1], acc[i][j][4 * rg + 2],
+                                                 acc[i][j][4 * rg + 3]});
             }
     }
 }
