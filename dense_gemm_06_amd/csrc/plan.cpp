@@ -125,6 +125,7 @@ static double tile_efficiency_aligned(const MenuEntry& e) {
     if (e.sched == 2) return 0.97;
     if (e.sched == 4) return 0.96;
     if (e.sched == 3) return 0.85;
+    if (e.sched == 5) return 0.90;  // problem-dependent: see plan()
     if (e.variant == V_LDS) return t >= 128 ? 0.6 : 0.35;
     return t >= 256 ? 0.85 : t >= 128 ? 0.7 : 0.45;
 }
@@ -197,7 +198,7 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
         want_wm = req->waves_m;
         want_wn = req->waves_n;
         want_sched = req->schedule;
-        if (want_sched < 0 || want_sched > 4 || want_wm < 0 || want_wn < 0 || want_variant < 0 || want_variant > 2 || want_vec < -1 || want_vec > 1 || want_remap < -1 ||
+        if (want_sched < 0 || want_sched > 5 || want_wm < 0 || want_wn < 0 || want_variant < 0 || want_variant > 2 || want_vec < -1 || want_vec > 1 || want_remap < -1 ||
             want_remap > 1 || want_group < 0 || want_bm < 0 || want_bn < 0) {
             set_error("invalid requested configuration (variant %d, bm %d, bn %d, vec %d, xcd_remap %d, group_m %d)",
                       want_variant, want_bm, want_bn, want_vec, want_remap, want_group);
@@ -283,8 +284,15 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
             const int64_t rounds = (work + concurrent - 1) / concurrent;
             const int64_t resident = std::min<int64_t>(occ, (work + num_cus - 1) / num_cus);
             const int64_t kpad = ((std::min<int64_t>(chunk, Kx) + e.bk - 1) / e.bk) * e.bk;
-            const double tile_cycles =
-                2.0 * e.bm * e.bn * std::max<int64_t>(kpad, e.bk) / (rate_per_cu(e) * tile_efficiency(e));
+            // The four-wave kernel (schedule 5) was measured faster than the ping-pong
+            // kernel when one round of tiles covers the machine, B is row-major and K
+            // spans at least 64 k-tiles (4096 x 4096 x K, K = 2048..8192: 3-10% less
+            // time; bf16 4096^3: 10%); with several rounds (8192^3: 10% slower), short K
+            // (K = 1024: equal; the packed 3001 x 5003 x 1037 problem: 15% slower) or
+            // column-major B (within 3% either way) the ping-pong kernel stays.
+            double eff = tile_efficiency(e);
+            if (e.sched == 5) eff = (e.opb == 0 && rounds == 1 && ktiles >= 64) ? 0.99 : 0.90;
+            const double tile_cycles = 2.0 * e.bm * e.bn * std::max<int64_t>(kpad, e.bk) / (rate_per_cu(e) * eff);
             double cost = (double)rounds * (double)std::max<int64_t>(resident, 1) * tile_cycles;
             // the reduction reads every plane and writes C, and is a second launch;
             // measured at 256^3 and 1024^3 fp32, a split costs about 16000 cycles

@@ -35,7 +35,7 @@ def _lib_built():
 MENU = _menu()
 MENU_IDS = [f"k{e['kernel_id']}-{'lds' if e['variant'] == 1 else 'mfma'}-{DT_NAME[e['dtype']]}-"
             f"op{'NT'[e['opb']]}-{'v16' if e['vec'] else 'v1'}-{e['bm']}x{e['bn']}-w{e['waves_m']}x{e['waves_n']}"
-            f"{ {1: '', 2: '-pp', 3: '-dma', 4: '-pp32'}[e['schedule']] }"
+            f"{ {1: '', 2: '-pp', 3: '-dma', 4: '-pp32', 5: '-w4'}[e['schedule']] }"
             for e in MENU]
 
 
@@ -104,7 +104,7 @@ def test_kernel_random_ragged(e):
     assert err <= TOL[ops.dtype], err
 
 
-@pytest.mark.parametrize("schedule", [2, pytest.param(3, marks=pytest.mark.skip(reason=SCHED3_OFF)), 4])
+@pytest.mark.parametrize("schedule", [2, pytest.param(3, marks=pytest.mark.skip(reason=SCHED3_OFF)), 4, 5])
 @pytest.mark.parametrize("k_tiles", [1, 2, 3, 4, 5, 6, 130])
 @pytest.mark.parametrize("dtype,op_b", [("f16", "N"), ("bf16", "N"), ("f16", "T"), ("bf16", "T")])
 def test_full_tile_kernels_k_tile_counts(schedule, k_tiles, dtype, op_b):
