@@ -64,6 +64,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="time only the headline problem")
     p.add_argument("--only", default=None, help="time only this benchmark problem, or grouped workload (for profiling)")
+    p.add_argument("--with-workspace", action="store_true",
+                   help="with --only: pass a workspace (the heuristic may split K or pack the operands)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="instead of GEMMs, run 5 plain device copies of MIB MiB (calibrates HBM counters)")
     return p.parse_args()
@@ -208,6 +210,66 @@ def time_grouped(name, steps, warmup):
                 separate_tflops=flops / (ms_sep * 1e-3) / 1e12, cfg=cfg, peak=PEAK_TFLOPS[spec["dtype"]])
 
 
+def time_distribution(name, n=100, warmup=10, n_cold=10, cold_bytes=512 << 20):
+    """Per-launch durations: n launches back to back with an event pair around each
+    (median, min, max), and n_cold launches each preceded by a write of cold_bytes
+    of scratch, which evicts the inputs from the 256 MB MALL ("cold")."""
+    import torch
+    import dense_gemm_06_amd as dg
+    ops, A, B, C = device_problem(name)
+    stream = torch.cuda.current_stream()
+    s = stream.cuda_stream
+    call = lambda: dg.gemm_ex(0, dg.OP_CODE[ops.op_b], ops.M, ops.N, ops.K, A.data_ptr(), ops.lda, B.data_ptr(),
+                              ops.ldb, C.data_ptr(), ops.N, dg.DTYPE_CODE[ops.dtype], None, s)
+    for _ in range(warmup):
+        call()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(n):
+        call()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    warm = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(n))
+    scratch = torch.empty(cold_bytes // 4, dtype=torch.float32, device="cuda")
+    cold = []
+    for i in range(n_cold):
+        scratch.fill_(float(i))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1) * 1e3)
+    cold.sort()
+    del scratch, A, B, C
+    flops = 2.0 * ops.M * ops.N * ops.K
+    med = lambda v: v[len(v) // 2] if len(v) % 2 else 0.5 * (v[len(v) // 2 - 1] + v[len(v) // 2])
+    return {"warm": {"launches": n, "median_us": round(med(warm), 2), "min_us": round(warm[0], 2),
+                     "max_us": round(warm[-1], 2), "tflops_at_median": round(flops / (med(warm) * 1e-6) / 1e12, 1),
+                     "tflops_at_min": round(flops / (warm[0] * 1e-6) / 1e12, 1)},
+            "cold": {"launches": n_cold, "evict_bytes": cold_bytes, "median_us": round(med(cold), 2),
+                     "min_us": round(cold[0], 2), "tflops_at_median": round(flops / (med(cold) * 1e-6) / 1e12, 1)}}
+
+
+def cpu_small(name, rows=None):
+    """The oracle on c1 / c2 with all host threads and with one thread (GFLOP/s); a
+    bounded row sample for the larger one."""
+    import gemm_inputs as gi
+    import oracle
+    ops = gi.make_config(name)
+    oracle.build(force=False)
+    rows = list(range(rows or ops.M))
+    out = {}
+    cores = oracle.max_threads()
+    for label, nt in (("all_threads", 0), ("one_thread", 1)):
+        _, t = oracle.timed_gemm_ref(ops, rows=rows, nthreads=nt)
+        out[label] = round(2.0 * len(rows) * ops.N * ops.K / t / 1e9, 3)
+    out.update(unit="GFLOP/s", cores=cores, kind="oracle",
+               sample=f"rows 0..{len(rows) - 1} of {ops.M}x{ops.N}x{ops.K} {ops.dtype}")
+    return out
+
+
 def cpu_baseline(name, target_s):
     """The oracle on the first r rows of `name`, r chosen for about target_s seconds."""
     import gemm_inputs as gi
@@ -291,7 +353,7 @@ def main():
         print(json.dumps({k: (v.as_dict() if k == "cfg" else v) for k, v in r.items()}), flush=True)
         return
     headline = a.only or "c4_f16_4096"
-    main_res = time_problem(headline, a.steps, a.warmup)
+    main_res = time_problem(headline, a.steps, a.warmup, workspace=bool(a.only and a.with_workspace))
     # the fused-epilogue variant right after the headline, in the same thermal state
     # (the chip's clock drifts by 10-20% over a run of heavy launches)
     fe = None
@@ -299,7 +361,7 @@ def main():
         fe = time_fused_epilogue(headline, max(5, a.steps // 2), max(2, a.warmup // 2))
     extras = {}
     if not a.no_extra and not a.only:
-        for name in ("c3_f32_4096", "c1_f32_256", "c2_f32_1024", "c5_bf16_ragged"):
+        for name in ("c3_f32_4096", "c1_f32_256", "c2_f32_1024", "c5_bf16_ragged", "m8_f16_shard", "m8_f32_shard"):
             extras[name] = time_problem(name, max(5, a.steps // 2), max(2, a.warmup // 2))
 
     cfg = main_res["cfg"]
@@ -351,7 +413,7 @@ def main():
             "ms_per_step": round(lk["ms_per_step"], 6), "frac_of_peak": round(lk["tflops"] / lk["peak"], 4),
             "tile": f"{lk['cfg'].bm}x{lk['cfg'].bn}", "variant": "mfma" if lk["cfg"].variant == 2 else "lds"}
         # (and the unaligned ragged problem, which the heuristic packs into aligned whole tiles)
-        for name in ("c1_f32_256", "c2_f32_1024", "k1_f32_long_k", "c5_bf16_ragged"):
+        for name in ("c1_f32_256", "c2_f32_1024", "k1_f32_long_k", "c5_bf16_ragged", "m8_f16_shard", "m8_f32_shard"):
             r = time_problem(name, max(5, a.steps // 2), max(2, a.warmup // 2), workspace=True)
             out["other_problems"][name]["with_workspace"] = {
                 "tflops": round(r["tflops"], 3), "ms_per_step": round(r["ms_per_step"], 6),
@@ -375,8 +437,17 @@ def main():
                              "separate_launches_ms": round(r["separate_ms"], 6),
                              "tile": f"{r['cfg'].bm}x{r['cfg'].bn}", "grid": r["cfg"].grid}
         out["grouped"] = grouped
+    if not a.no_extra and not a.only:
+        # per-launch distribution (median / min) and MALL-cold launches of the two 4096^3 problems
+        out["launch_distribution"] = {name: time_distribution(name, n=100 if name.startswith("c4") else 30)
+                                      for name in (headline, "c3_f32_4096")}
+        for name in ("m8_f16_shard", "m8_f32_shard"):
+            if name in out.get("other_problems", {}):
+                out["other_problems"][name]["workload"] = ("one GPU's share of the 4096^3 problem split 8 ways by "
+                                                           "rows: C=A@B 512x4096x4096 " + name[3:6])
     if not a.no_cpu_baseline and not a.only:
         out["cpu_baseline"] = cpu_baseline(headline, a.cpu_seconds)
+        out["cpu_small"] = {"c1_f32_256": cpu_small("c1_f32_256"), "c2_f32_1024": cpu_small("c2_f32_1024", rows=128)}
     print(json.dumps(out), flush=True)
 
 

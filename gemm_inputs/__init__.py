@@ -175,6 +175,9 @@ CONFIGS = {
 # few output tiles (the case split K is for).
 EXTRA_CONFIGS = {
     "k1_f32_long_k": dict(M=256, N=256, K=16384, dtype="f32", dist="uniform", op_b="N"),
+    # one GPU's share of the 4096^3 problems split 8 ways by rows of A and C
+    "m8_f16_shard": dict(M=512, N=4096, K=4096, dtype="f16", dist="uniform", op_b="N"),
+    "m8_f32_shard": dict(M=512, N=4096, K=4096, dtype="f32", dist="uniform", op_b="N"),
 }
 
 

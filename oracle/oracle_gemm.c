@@ -102,11 +102,15 @@ int oracle_gemm(int opA, int opB, int64_t M, int64_t N, int64_t K,
                 Bd[k * N + j] = oracle_load(B, opB == 0 ? k * ldb + j : j * ldb + k, dtype);
     }
 
+    /* the thread count applies to this call only (a num_threads clause, not the
+       process-wide setting, so a later call with nthreads <= 0 gets the default) */
+    int nt = 1;
 #ifdef _OPENMP
-    if (nthreads > 0) omp_set_num_threads(nthreads);
+    nt = nthreads > 0 ? nthreads : omp_get_max_threads();
 #endif
+    (void)nt;
     int bad = 0;
-#pragma omp parallel for schedule(dynamic, 1)
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
     for (int64_t r = 0; r < nrows; ++r) {
         int64_t i = rows ? rows[r] : r;
         double* c = Cref + r * N;

@@ -147,9 +147,10 @@ def checksum_property(C, ops, tol):
     assert np.all(np.abs(got - ref) <= tol * dsum * 1.0001 + 1e-300)
 
 
-@pytest.mark.parametrize("name", list(gi.CONFIGS))
+@pytest.mark.parametrize("name", list(gi.CONFIGS) + ["m8_f16_shard", "m8_f32_shard"])
 def test_benchmark_config_heuristic(name):
-    """The five benchmark problems at full size, in the configuration the heuristic picks."""
+    """The five benchmark problems, and one GPU's row share of the 4096^3 problems, at
+    full size in the configuration the heuristic picks."""
     ops = gi.make_config(name)
     ldc = ops.N
     print(f"case config {name}", flush=True)

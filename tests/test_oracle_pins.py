@@ -321,3 +321,14 @@ def test_check_criterion():
     C = Cref.copy()
     C[1, 1] = np.nan
     assert normalized_error(C, Cref, D) == float("inf")
+
+
+def test_thread_count_applies_to_one_call():
+    """A call with an explicit thread count leaves later default calls on all threads,
+    and the result does not depend on the thread count."""
+    ops = gi.make_operands(40, 30, 20, "f32", "uniform", seed=5)
+    before = oracle.max_threads()
+    C1, D1 = oracle.gemm_ref(ops, nthreads=1)
+    assert oracle.max_threads() == before
+    C0, D0 = oracle.gemm_ref(ops)
+    assert np.array_equal(C1, C0) and np.array_equal(D1, D0)
