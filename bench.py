@@ -43,7 +43,7 @@ def kernel_sources(cfg) -> list[str]:
     if cfg.schedule == 3:
         return common + ["kernel_dma.h"]
     if cfg.schedule == 5:
-        return common + ["kernel_w4.h"]
+        return common + ["kernel_sp.h"]
     return common + ["kernel_mfma.h"]
 
 
@@ -308,7 +308,7 @@ def kernel_name(cfg, dtype):
         base = "mfma32_gemm"
     else:
         base = {1: "mfma16_gemm", 2: "mfma16_pp (16x16x32)", 3: "mfma16_dma", 4: "mfma16_pp (32x32x16)",
-                5: "mfma32_w4 (32x32x16)"}[cfg.schedule]
+                5: "mfma32_sp (32x32x16)"}[cfg.schedule]
     return f"{base} {cfg.bm}x{cfg.bn}x{cfg.bk} waves {cfg.waves_m}x{cfg.waves_n}"
 
 

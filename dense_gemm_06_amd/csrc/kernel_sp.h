@@ -1,0 +1,319 @@
+// kernel_sp.h -- software-pipelined 32x32x16 MFMA kernel with direct LDS copies.
+#pragma once
+#include <type_traits>
+
+#include "lds_layout.h"
+
+// An LDS pointer made from a byte address (an integer): it carries no link to the
+// LDS variable the address falls in.
+#define DG_LDS_AT(a) ((__attribute__((address_space(3))) void*)(uintptr_t)(uint32_t)(a))
+
+namespace dg {
+
+// Wait until at most N of this wave's vector memory operations are in flight.
+template <int N>
+__device__ __forceinline__ void vm_wait_n() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// The same for a run-time even n in 0..24 (larger values wait for everything).
+__device__ __forceinline__ void vm_wait(int n) {
+    switch (n) {
+        case 0: vm_wait_n<0>(); break;
+        case 2: vm_wait_n<2>(); break;
+        case 4: vm_wait_n<4>(); break;
+        case 6: vm_wait_n<6>(); break;
+        case 8: vm_wait_n<8>(); break;
+        case 10: vm_wait_n<10>(); break;
+        case 12: vm_wait_n<12>(); break;
+        case 16: vm_wait_n<16>(); break;
+        case 20: vm_wait_n<20>(); break;
+        case 24: vm_wait_n<24>(); break;
+        default: vm_wait_n<0>(); break;
+    }
+}
+
+// Software-pipelined MFMA kernel for 16-bit inputs on full 256 x 256 tiles (M and
+// N multiples of 256, K a multiple of 32, 16-byte aligned operands).
+//
+// NW = 4: four waves, one per SIMD, each owning a 128 x 128 quarter of the tile with
+// its 16 v_mfma_f32_32x32x16 accumulators (256 registers) in the accumulation
+// registers. NW = 8: eight waves, two per SIMD, each owning 128 x 64 (8
+// accumulators). A 128 x 128 wave reads 64 bytes of LDS fragments per 32x32x16
+// MFMA, a 128 x 64 wave 96; a single wave issues this instruction at about 87% of
+// the matrix unit's rate, two waves per SIMD near 100%.
+//
+// The k loop runs in steps of 16. Each wave holds two fragment sets: while the
+// MFMAs of step s run from one set, the fragment reads of step s+1 fill the other,
+// interleaved with the MFMAs. Tiles of k = 32 (two steps) arrive by direct global
+// -> LDS copies (global_load_lds_dwordx4) into a ring of 4 stages, issued three
+// tiles ahead: each wave copies its share of the A tile during the first step of a
+// tile and of the B tile during the second. One barrier per tile, between its two
+// steps, makes the next tile visible (each wave first waits for its own copies of
+// it) and retires the stage the refill of the current iteration overwrites.
+//
+// Tile t sits in stage t mod 4. Step (t, 0)'s fragments are read during step
+// (t-1, 1), step (t, 1)'s during step (t, 0). The last reads of stage t mod 4 are
+// therefore done (lgkmcnt(0)) before the barrier of iteration t, and iteration
+// t+1 refills that stage with tile t+4.
+//
+// LDS layouts and the fragment maps are those of the 32x32x16 ping-pong form:
+// k-major 64-byte rows with chunk swizzle kmaj32_swz, row-major B with nmaj32_swz,
+// read through ds_read_b64_tr_b16. Both swizzles depend on the lane only for the
+// rows a wave reads, so every fragment read is a per-lane base plus an immediate.
+//
+// Epilogue: the accumulators go through the LDS the k loop no longer needs, half
+// a wave tile at a time (64 rows), and leave as whole rows: each store instruction
+// writes 2 (NW = 4) or 4 (NW = 8) rows of the wave tile, contiguous in C. A fused
+// epilogue (ep.kind != 0) is applied on the way out.
+template <int DT, int OPB, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void mfma32_sp(
+    GemmArgs g) {
+    static_assert(NW == 4 || NW == 8, "waves");
+    constexpr int BM = 256, BN = 256, BK = 32, S = 4, D = S - 1;  // D: copy distance in tiles
+    constexpr int SA = BM * BK, SB = BN * BK;                     // halfs per stage
+    constexpr int STAGE_BYTES = SA * 2;                           // 16 KB for each of A and B
+    constexpr int WNN = NW / 2;                                   // waves along n
+    constexpr int SJ = 8 / WNN;                                   // 32-column subtiles per wave
+    constexpr int CPB = 16 / NW;                                  // 1 KB copies per wave and operand
+    __shared__ __attribute__((aligned(1024))) uint16_t sA[S][SA];
+    __shared__ __attribute__((aligned(1024))) uint16_t sB[S][SB];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WNN, wn = wave % WNN;
+    const int l32 = lane & 31, lh = lane >> 5;
+    const int l16 = lane & 15, lg = lane >> 4;
+    int tm, tn;
+    tile_coords(g, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int nk = g.K / BK;
+    const uint16_t* __restrict__ A = static_cast<const uint16_t*>(g.A);
+    const uint16_t* __restrict__ B = static_cast<const uint16_t*>(g.B);
+
+    // ---- direct copies: wave w moves blocks CPB*w .. CPB*w+CPB-1 (1 KB each) of the A
+    // tile and of the B tile. Lane L of block b lands at LDS byte b*1024 + 16L, a fixed
+    // swizzled position, and loads the logical 16-byte chunk that belongs there.
+    const uint16_t* srcA[CPB];
+    const uint16_t* srcB[CPB];
+#pragma unroll
+    for (int i = 0; i < CPB; ++i) {
+        const int b = wave * CPB + i;
+        const int row = b * 16 + (lane >> 2);
+        srcA[i] = A + (size_t)(m0 + row) * g.lda + (((lane & 3) ^ kmaj32_swz(row)) << 3);
+        if (OPB == 1) {
+            srcB[i] = B + (size_t)(n0 + row) * g.ldb + (((lane & 3) ^ kmaj32_swz(row)) << 3);
+        } else {
+            const int krow = b * 2 + (lane >> 5);
+            srcB[i] = B + (size_t)krow * g.ldb + n0 + (((lane & 31) ^ nmaj32_swz(krow)) << 3);
+        }
+    }
+    const size_t kstepB = OPB == 0 ? (size_t)BK * g.ldb : (size_t)BK;  // elements per k-tile
+    // LDS destinations as plain wave-uniform numbers (M0 takes them directly). Built
+    // from an integer, a copy's LDS pointer carries no link to sA / sB, so the
+    // compiler does not make every later LDS read wait for all copies in flight
+    // (vmcnt(0)); the explicit waits below order them instead.
+    const uint32_t wave_u = (uint32_t)__builtin_amdgcn_readfirstlane(wave);
+    const uint32_t dstA = (uint32_t)reinterpret_cast<uintptr_t>(DG_LDSV(&sA[0][0])) + wave_u * (CPB * 1024u);
+    const uint32_t dstB = (uint32_t)reinterpret_cast<uintptr_t>(DG_LDSV(&sB[0][0])) + wave_u * (CPB * 1024u);
+    auto copy_a = [&](int t, int i) {
+        __builtin_amdgcn_global_load_lds(DG_GLB(srcA[i] + (size_t)t * BK),
+                                         DG_LDS_AT(dstA + (uint32_t)(t & 3) * STAGE_BYTES + i * 1024u), 16, 0, 0);
+    };
+    auto copy_b = [&](int t, int i) {
+        __builtin_amdgcn_global_load_lds(DG_GLB(srcB[i] + (size_t)t * kstepB),
+                                         DG_LDS_AT(dstB + (uint32_t)(t & 3) * STAGE_BYTES + i * 1024u), 16, 0, 0);
+    };
+
+    // ---- fragment addresses (bytes within a stage).
+    // Q (A rows wm*128 + 32i + l32), P of column-major B (B rows wn*32*SJ + 32j + l32):
+    // lane holds k 8*lh .. 8*lh+7 of the step, chunk (2ks + lh) ^ ((l32 >> 2) & 3);
+    // a subtile adds 32 rows = 2048 bytes.
+    const int qsw = (l32 >> 2) & 3;
+    int qoff[2], poff[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        qoff[ks] = (wm * 128 + l32) * 64 + (((ks * 2 + lh) ^ qsw) << 4);
+        poff[ks] = (wn * 32 * SJ + l32) * 64 + (((ks * 2 + lh) ^ qsw) << 4);
+    }
+    // P of row-major B (transpose reads): in each 16-lane group, lane i addresses k row
+    // kb + i/4 at columns nb + 4(i%4) and receives column nb + i of rows kb..kb+3.
+    // Lane groups 0/1 (2/3) cover columns 0-15 / 16-31 of k rows 0-7 (8-15) of the
+    // step; step ks and half hh add (16 ks + 4 hh) rows of 512 bytes as immediates.
+    int toff[SJ];
+#pragma unroll
+    for (int j = 0; j < SJ; ++j) {
+        const int col = wn * 32 * SJ + j * 32 + (lg & 1) * 16 + ((l16 & 3) << 2);
+        const int krow = (lg >> 1) * 8 + (l16 >> 2);
+        toff[j] = krow * 512 + (((col >> 3) ^ nmaj32_swz(krow)) << 4) + (col & 7) * 2;
+    }
+    const uint32_t sB_base = (uint32_t)reinterpret_cast<uintptr_t>(DG_LDSV(&sB[0][0]));
+
+    // One fragment set: q[i] (A), p[j] (B) as 8 halfs per lane; ph[j][hh] are the two
+    // transpose-read halves of p[j] for row-major B.
+    struct Frags {
+        u32x4 q[4];
+        u32x4 p[SJ];
+        u32x2 ph[SJ][2];
+    };
+    Frags f0, f1;
+
+    // Read number r of step ks of the tile in stage st into f: 4 Q reads, then 2*SJ
+    // (row-major B) or SJ (column-major B) P reads.
+    auto read_one = [&](Frags& f, int st, int ks, int r) {
+        if (r < 4) {
+            f.q[r] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(&sA[0][0]) + st * STAGE_BYTES +
+                                                     qoff[ks] + r * 2048);
+        } else if (OPB == 1) {
+            f.p[r - 4] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(&sB[0][0]) +
+                                                        st * STAGE_BYTES + poff[ks] + (r - 4) * 2048);
+        } else {
+            const int j = (r - 4) >> 1, hh = (r - 4) & 1;
+            const uint32_t addr = sB_base + (uint32_t)(st * STAGE_BYTES + toff[j] + (ks * 16 + hh * 4) * 512);
+            asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(f.ph[j][hh]) : "v"(addr));
+        }
+    };
+    constexpr int NREAD = 4 + (OPB == 0 ? 2 * SJ : SJ);
+    // After the lgkmcnt(0) wait that ends a step: the transpose halves (asm outputs the
+    // compiler cannot see being written late) pass through an empty asm placed after
+    // the wait, so their uses cannot move above it; then they are joined into p[j].
+    auto settle = [&](Frags& f) {
+        if (OPB == 0) {
+#pragma unroll
+            for (int j = 0; j < SJ; ++j) {
+                asm volatile("" : "+v"(f.ph[j][0]), "+v"(f.ph[j][1]));
+                f.p[j] = u32x4{f.ph[j][0][0], f.ph[j][0][1], f.ph[j][1][0], f.ph[j][1][1]};
+            }
+        }
+    };
+
+    f32x16 acc[4][SJ];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < SJ; ++j) acc[i][j] = f32x16{};
+
+    auto mfma = [&](const Frags& f, int i, int j) {
+        if (DT == DT_F16)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, f.p[j]),
+                                                               __builtin_bit_cast(f16x8, f.q[i]), acc[i][j], 0, 0, 0);
+        else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f.p[j]),
+                                                                __builtin_bit_cast(bf16x8, f.q[i]), acc[i][j], 0, 0, 0);
+    };
+
+    // One step: 4*SJ MFMAs from `cur`, each followed by at most two other instructions
+    // in a fixed order: the fragment reads of `nxt` two at a time after the first
+    // MFMAs (early, so they are done by the wait that ends the step), then this wave's
+    // CPB copies of tile `ct` (half `half`: 0 = A, 1 = B) after every other MFMA of the
+    // second half of the step.
+    constexpr int NM = 4 * SJ;  // MFMAs per step
+    auto step = [&](const Frags& cur, Frags& nxt, int rst, int rks, bool do_copy, int ct, int half) {
+#pragma unroll
+        for (int k = 0; k < NM; ++k) {
+            mfma(cur, k / SJ, k % SJ);
+            if (2 * k < NREAD) read_one(nxt, rst, rks, 2 * k);
+            if (2 * k + 1 < NREAD) read_one(nxt, rst, rks, 2 * k + 1);
+            const int c = (k - NM / 2) >> 1;
+            if (do_copy && k >= NM / 2 && (k & 1) == 0 && c < CPB) {
+                if (half == 0) copy_a(ct, c);
+                else copy_b(ct, c);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // prologue: tiles 0 .. D-1 in flight (A then B of each); tile 0 complete; step
+    // (0, 0) fragments read.
+    for (int t = 0; t < D && t < nk; ++t) {
+#pragma unroll
+        for (int i = 0; i < CPB; ++i) copy_a(t, i);
+#pragma unroll
+        for (int i = 0; i < CPB; ++i) copy_b(t, i);
+    }
+    vm_wait(2 * CPB * (min(D, nk) - 1));
+    asm volatile("s_barrier" ::: "memory");
+#pragma unroll
+    for (int r = 0; r < NREAD; ++r) read_one(f0, 0, 0, r);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    settle(f0);
+
+    // One iteration (tile t). REFILL: tile t+D exists and is copied. The reads of step
+    // (t+1, 0) in the last iteration fetch a stage nobody writes any more; their values
+    // are never used (this keeps the step free of branches).
+    auto iteration = [&](int t, auto refill_tag) {
+        constexpr bool REFILL = decltype(refill_tag)::value;
+        const int st = t & 3;
+        // step (t, 0): MFMAs from f0; read step (t, 1) into f1; copy A of tile t+D
+        step(f0, f1, st, 1, REFILL, t + D, 0);
+        // own reads done; own copies of tile t+1 done (those of tiles t+2 .. t+D-1 and
+        // the A half of tile t+D may still be in flight); then the barrier
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (REFILL) vm_wait_n<2 * CPB * (D - 2) + CPB>();
+        else vm_wait(2 * CPB * max(0, nk - t - 2));
+        asm volatile("s_barrier" ::: "memory");
+        settle(f1);
+        // step (t, 1): MFMAs from f1; read step (t+1, 0) into f0; copy B of tile t+D
+        step(f1, f0, (t + 1) & 3, 0, REFILL, t + D, 1);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        settle(f0);
+    };
+    int t = 0;
+    for (; t + D < nk; ++t) iteration(t, std::true_type{});
+    for (; t < nk; ++t) iteration(t, std::false_type{});
+
+    // ---- epilogue through LDS. Every wave's last reads are done (lgkmcnt(0) above);
+    // the barrier makes sure all of them are before any wave overwrites a stage. The
+    // empty asm in the write loop stands between the MFMAs and the reads of their
+    // results, so the compiler's hazard padding does not see the MFMA as the last
+    // writer: the 18 wait states a 16-pass MFMA result needs are given here.
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
+    __syncthreads();
+    // Each wave owns a slot of 64 rows x WT bytes (WT = 32*SJ fp32 = 512 or 256 bytes):
+    // NW = 4: 32 KB, waves 0-1 in sA, 2-3 in sB; NW = 8: 16 KB, waves 0-3 in sA, 4-7
+    // in sB. Register r of subtile (i, j) holds row 32i + l32 of the wave tile and
+    // columns 32j + 8(r/4) + 4*lh + r%4: chunk c = 8j + 2(r/4) + lh of 16 bytes, stored
+    // at position c ^ (row & 15) of its row, which keeps both the writes (16 rows per
+    // lane phase) and the whole-row reads free of bank conflicts.
+    constexpr int WT = 32 * SJ * 4;           // bytes per wave-tile row
+    constexpr int CPR = WT / 16;              // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;             // rows per read instruction
+    constexpr int SLOT = 64 * WT;
+    char* slot = reinterpret_cast<char*>(wave < NW / 2 ? &sA[0][0] : &sB[0][0]) + (wave % (NW / 2)) * SLOT;
+    const int cm0 = m0 + wm * 128, cn0 = n0 + wn * 32 * SJ;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+            const int i = 2 * h + ii;
+            const int row = ii * 32 + l32;
+#pragma unroll
+            for (int j = 0; j < SJ; ++j) {
+                // one subtile at a time: the empty asm pins acc[i][j] in the accumulation
+                // registers until here (otherwise all accumulators are copied out at once,
+                // which needs more registers than exist)
+                asm volatile("" : "+a"(acc[i][j]));
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) {
+                    const int c = j * 8 + rg * 2 + lh;
+                    *reinterpret_cast<f32x4*>(slot + row * WT + ((c ^ (row & 15)) << 4)) =
+                        f32x4{acc[i][j][4 * rg], acc[i][j][4 * rg + 1], acc[i][j][4 * rg + 2], acc[i][j][4 * rg + 3]};
+                }
+            }
+        }
+        // only this wave touches its slot; the wave barrier keeps the compiler from
+        // moving LDS accesses across the write / read phases, which the hardware runs
+        // in order within a wave
+        __builtin_amdgcn_wave_barrier();
+        for (int it = 0; it < 64 / RPI; ++it) {
+            const int row = it * RPI + lane / CPR, c = lane % CPR;
+            const f32x4 v = *reinterpret_cast<const f32x4*>(slot + row * WT + ((c ^ (row & 15)) << 4));
+            const int m = cm0 + h * 64 + row;
+            if (m < g.M) {
+                if (g.ep.kind == 0) store_run4<false>(g, m, cn0 + c * 4, v);
+                else epilogue_run4_body(g.ep, g.C, g.ldc, g.N, m, cn0 + c * 4, v);
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+}  // namespace dg

@@ -33,4 +33,4 @@
 #include "kernel_mfma.h"
 #include "kernel_pp.h"
 #include "kernel_dma.h"
-#include "kernel_w4.h"
+#include "kernel_sp.h"

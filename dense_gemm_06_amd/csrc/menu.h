@@ -20,8 +20,9 @@ enum Dtype { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
 //   bm, bn, bk : block tile; wm x wn : wave grid (MFMA); tm x tn : thread tile (LDS)
 //   sched   : 1 = register-staged double buffer (any shape), 2 = ping-pong with
 //             direct global->LDS copies on 16x16x32 MFMAs, 3 = software-pipelined
-//             with direct copies, 4 = ping-pong on 32x32x16 MFMAs, 5 = four waves
-//             of 128 x 128, software-pipelined, with direct copies (2-5: full tiles
+//             with direct copies, 4 = ping-pong on 32x32x16 MFMAs, 5 = software-
+//             pipelined 32x32x16 with direct copies, 4 waves of 128 x 128 or 8 of
+//             128 x 64 (2-5: full tiles
 //             only -- M, N multiples of bm, bn, K a multiple of bk, 16-byte aligned
 //             operands)
 struct MenuEntry {
@@ -38,9 +39,9 @@ struct MenuEntry {
 constexpr bool schedule_enabled(int sched) { return sched != 3; }
 
 // Configurations whose kernel applies a fused epilogue (every other one stores the
-// plain fp32 accumulator only): all but the 32x32x16 ping-pong and the
-// software-pipelined kernels.
-constexpr bool epilogue_capable(int sched) { return sched != 3 && sched != 4 && sched != 5; }
+// plain fp32 accumulator only): all but the 32x32x16 ping-pong kernel and the
+// switched-off schedule 3.
+constexpr bool epilogue_capable(int sched) { return sched != 3 && sched != 4; }
 
 // Configurations that also have a grouped (persistent) form: the register-staged
 // schedule, which masks every edge, except the 4-wave 256 x 256 tiles (their
@@ -102,11 +103,13 @@ constexpr bool grouped_capable(int sched, int bm, int bn, int wm, int wn) {
     X(base + 0, V_MFMA, dt, 0, 1, 256, 256, 32, 2, 4, 0, 0, 512, 4 * 2 * 32 * 512, 3)      \
     X(base + 1, V_MFMA, dt, 1, 1, 256, 256, 32, 2, 4, 0, 0, 512, 4 * 2 * 32 * 512, 3)
 
-// Four-wave software-pipelined kernels (16-bit inputs, full tiles, 4 LDS stages of
-// k = 32, 128 x 128 per wave on 32x32x16 MFMAs).
-#define DG_MFMA_W4(X, base, dt)                                                          \
+// Software-pipelined kernels (16-bit inputs, full tiles, 4 LDS stages of k = 32,
+// 32x32x16 MFMAs): 4 waves of 128 x 128 and 8 waves of 128 x 64.
+#define DG_MFMA_SP(X, base, dt)                                                          \
     X(base + 0, V_MFMA, dt, 0, 1, 256, 256, 32, 2, 2, 0, 0, 256, 4 * 2 * 32 * 512, 5)      \
-    X(base + 1, V_MFMA, dt, 1, 1, 256, 256, 32, 2, 2, 0, 0, 256, 4 * 2 * 32 * 512, 5)
+    X(base + 1, V_MFMA, dt, 1, 1, 256, 256, 32, 2, 2, 0, 0, 256, 4 * 2 * 32 * 512, 5)      \
+    X(base + 2, V_MFMA, dt, 0, 1, 256, 256, 32, 2, 4, 0, 0, 512, 4 * 2 * 32 * 512, 5)      \
+    X(base + 3, V_MFMA, dt, 1, 1, 256, 256, 32, 2, 4, 0, 0, 512, 4 * 2 * 32 * 512, 5)
 
 #define DG_MENU(X)                                              \
     DG_LDS_ENTRIES(X, 0, DT_F32, 16)            \
@@ -123,10 +126,10 @@ constexpr bool grouped_capable(int sched, int bm, int bn, int wm, int wn) {
     DG_MFMA_DMA(X, 74, DT_BF16)                                  \
     DG_MFMA_PP32(X, 76, DT_F16)                                  \
     DG_MFMA_PP32(X, 78, DT_BF16)                                 \
-    DG_MFMA_W4(X, 80, DT_F16)                                    \
-    DG_MFMA_W4(X, 82, DT_BF16)
+    DG_MFMA_SP(X, 80, DT_F16)                                    \
+    DG_MFMA_SP(X, 84, DT_BF16)
 
-constexpr int kMenuSize = 84;
+constexpr int kMenuSize = 88;
 
 // Fused epilogue ("Shared memory and tensor cores", section 13.10: bias,
 // activation, residual add or type cast applied to the accumulator before the

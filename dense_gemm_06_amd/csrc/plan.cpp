@@ -284,14 +284,15 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
             const int64_t rounds = (work + concurrent - 1) / concurrent;
             const int64_t resident = std::min<int64_t>(occ, (work + num_cus - 1) / num_cus);
             const int64_t kpad = ((std::min<int64_t>(chunk, Kx) + e.bk - 1) / e.bk) * e.bk;
-            // The four-wave kernel (schedule 5) was measured faster than the ping-pong
-            // kernel when one round of tiles covers the machine, B is row-major and K
-            // spans at least 64 k-tiles (4096 x 4096 x K, K = 2048..8192: 3-10% less
-            // time; bf16 4096^3: 10%); with several rounds (8192^3: 10% slower), short K
-            // (K = 1024: equal; the packed 3001 x 5003 x 1037 problem: 15% slower) or
-            // column-major B (within 3% either way) the ping-pong kernel stays.
+            // The software-pipelined kernel (schedule 5) in its 8-wave form was measured
+            // faster than the ping-pong kernel for row-major B and K of at least 64
+            // k-tiles (4096^3 fp16: 124-130 us against 133-147; 8192^3: 917 against 997;
+            // bf16 4096^3: 115 against 126; with the fused GELU epilogue: equal), and
+            // equal at K = 1024; with column-major B it is 9-12% slower, and its 4-wave
+            // form is slower than the 8-wave one throughout (and 16% slower than the
+            // ping-pong kernel with a fused epilogue), so those stay off by default.
             double eff = tile_efficiency(e);
-            if (e.sched == 5) eff = (e.opb == 0 && rounds == 1 && ktiles >= 64) ? 0.99 : 0.90;
+            if (e.sched == 5) eff = (e.wm * e.wn == 8 && e.opb == 0 && ktiles >= 64) ? 0.99 : 0.90;
             const double tile_cycles = 2.0 * e.bm * e.bn * std::max<int64_t>(kpad, e.bk) / (rate_per_cu(e) * eff);
             double cost = (double)rounds * (double)std::max<int64_t>(resident, 1) * tile_cycles;
             // the reduction reads every plane and writes C, and is a second launch;

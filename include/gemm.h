@@ -90,10 +90,10 @@ typedef struct gemm_config {
     int32_t schedule;  /* in/out: 0 any; 1 register-staged double buffer (any shape); 2 ping-pong
                           with direct global->LDS copies on 16x16x32 MFMAs; 3 software-pipelined
                           with direct global->LDS copies (switched off: requests for it return
-                          GEMM_ERR_UNSUPPORTED); 4 ping-pong on 32x32x16 MFMAs; 5 four waves
-                          of 128 x 128 on 32x32x16 MFMAs, software-pipelined, with direct
-                          global->LDS copies (2-5: MFMA, 16-bit inputs, M and N multiples of
-                          256, K a multiple of 32, 16-byte aligned operands; 4 and 5 store the
+                          GEMM_ERR_UNSUPPORTED); 4 ping-pong on 32x32x16 MFMAs; 5 software-
+                          pipelined 32x32x16 with direct global->LDS copies, 4 waves of 128 x
+                          128 or 8 of 128 x 64 (2-5: MFMA, 16-bit inputs, M and N multiples of
+                          256, K a multiple of 32, 16-byte aligned operands; 4 stores the
                           plain fp32 accumulator only) */
     int64_t tiles_m, tiles_n; /* out (grouped: of the first non-empty problem) */
     double est_cycles; /* out: the heuristic's cost estimate (clock cycles) */

@@ -51,7 +51,7 @@ def test_status_strings():
 
 def test_menu_is_complete():
     menu = dg.gemm_menu()
-    assert len(menu) == dg.library().gemm_menu_size() == 84
+    assert len(menu) == dg.library().gemm_menu_size() == 88
     seen = set()
     for e in menu:
         assert e["lds_bytes"] <= 160 * 1024
@@ -65,7 +65,7 @@ def test_menu_is_complete():
                 for vec in (0, 1):
                     tiles = {(bm, bn) for (v, d, o, ve, bm, bn) in seen if (v, d, o, ve) == (variant, dtype, opb, vec)}
                     assert len(tiles) >= 2, (variant, dtype, opb, vec)
-    assert dg.library().gemm_menu_entry(84, None, None, None, None) == dg.GEMM_ERR_INVALID_VALUE
+    assert dg.library().gemm_menu_entry(88, None, None, None, None) == dg.GEMM_ERR_INVALID_VALUE
 
 
 def plan(M, N, K, dtype="f32", op_b="N", lda=None, ldb=None, ldc=None, a=0, b=0, c=0, cus=256, arch="gfx950",
@@ -80,7 +80,7 @@ def plan(M, N, K, dtype="f32", op_b="N", lda=None, ldb=None, ldc=None, a=0, b=0,
 def test_plan_benchmark_configs():
     st, c = plan(4096, 4096, 4096, "f16")
     assert st == 0 and c.variant == dg.GEMM_VARIANT_MFMA and (c.bm, c.bn) == (256, 256) and c.grid == 256
-    assert c.vec == 1 and c.schedule == 5 and c.threads == 256 and (c.waves_m, c.waves_n) == (2, 2)
+    assert c.vec == 1 and c.schedule == 5 and c.threads == 512 and (c.waves_m, c.waves_n) == (2, 4)
     st, c = plan(4096, 4096, 4096, "f32")
     assert st == 0 and c.variant == dg.GEMM_VARIANT_MFMA and c.vec == 1
     # ragged bf16 with column-major B and odd leading dimensions: element-wise loads
@@ -89,19 +89,21 @@ def test_plan_benchmark_configs():
     assert c.tiles_m == -(-3001 // c.bm) and c.tiles_n == -(-5003 // c.bn)
 
 
-def test_plan_four_wave_kernel_where_measured_faster():
-    """Schedule 5 for one round of whole tiles, row-major B and K of 64 k-tiles or
-    more; the ping-pong kernel otherwise (several rounds of tiles, short K,
-    column-major B, or a fused epilogue, which schedule 5 does not apply)."""
-    assert plan(4096, 4096, 4096, "f16")[1].schedule == 5
-    assert plan(4096, 4096, 4096, "bf16")[1].schedule == 5
-    assert plan(4096, 4096, 2048, "f16")[1].schedule == 5
+def test_plan_software_pipelined_kernel_where_measured_faster():
+    """Schedule 5 (8 waves) for whole tiles with row-major B and K of 64 k-tiles or
+    more, with or without a fused epilogue; the ping-pong kernel for short K and for
+    column-major B; the 4-wave form only when asked for."""
+    for m, n, k, dt in ((4096, 4096, 4096, "f16"), (4096, 4096, 4096, "bf16"), (4096, 4096, 2048, "f16"),
+                        (8192, 8192, 8192, "f16")):
+        c = plan(m, n, k, dt)[1]
+        assert c.schedule == 5 and (c.waves_m, c.waves_n) == (2, 4), (m, n, k, dt)
     assert plan(4096, 4096, 1024, "f16")[1].schedule == 2
-    assert plan(8192, 8192, 8192, "f16")[1].schedule == 2
     assert plan(4096, 4096, 4096, "f16", "T")[1].schedule == 2
     st, c = dg.gemm_plan_workspace(0, 0, 4096, 4096, 4096, 4096, 4096, 4096, dg.GEMM_F16, 0, 0, 0, 256, "gfx950", 0,
                                    None, epi=dg.epilogue(activation="relu"))
-    assert st == 0 and c.schedule == 2
+    assert st == 0 and c.schedule == 5 and c.waves_n == 4
+    c = plan(4096, 4096, 4096, "f16", req=dg.request(schedule=5, waves_n=2))[1]
+    assert c.schedule == 5 and c.threads == 256
 
 
 def test_plan_ping_pong_eligibility():
@@ -423,13 +425,12 @@ def test_pack_errors():
 # ----------------------------------------------------------------------------- fused epilogue
 def test_epilogue_plan_avoids_plain_only_kernels():
     gelu = dg.epilogue(alpha=2.0, activation="gelu_tanh")
-    for sched in (4, 5):
-        st, _ = wplan(4096, 4096, 4096, "f16", req=dg.request(schedule=sched), epi=gelu, check=False)
-        assert st == dg.GEMM_ERR_UNSUPPORTED
+    st, _ = wplan(4096, 4096, 4096, "f16", req=dg.request(schedule=4), epi=gelu, check=False)
+    assert st == dg.GEMM_ERR_UNSUPPORTED
     # the identity epilogue is the plain store: any kernel
     assert wplan(4096, 4096, 4096, "f16", req=dg.request(schedule=4), epi=dg.epilogue())[1].schedule == 4
-    # the headline configuration keeps its ping-pong kernel with an epilogue
-    assert wplan(4096, 4096, 4096, "f16", epi=gelu)[1].schedule == 2
+    # the headline configuration keeps its software-pipelined kernel with an epilogue
+    assert wplan(4096, 4096, 4096, "f16", epi=gelu)[1].schedule == 5
     st, _ = wplan(64, 64, 64, epi=dg.epilogue(out_dtype=7), check=False)
     assert st == dg.GEMM_ERR_INVALID_VALUE
 

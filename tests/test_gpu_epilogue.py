@@ -145,12 +145,15 @@ def test_epilogue_paths(path, dtype, out, act):
     assert epilogue_error(got, ref, Dp, dtype, out) <= 1.0
 
 
+@pytest.mark.parametrize("schedule,waves_n", [(2, 0), (5, 2), (5, 4)])
 @pytest.mark.parametrize("dtype,op_b", [("f16", "N"), ("bf16", "T")])
-@pytest.mark.parametrize("out", ["f32", "bf16"])
-def test_epilogue_ping_pong_whole_tiles(dtype, op_b, out):
+@pytest.mark.parametrize("out", ["f32", "bf16", "f16"])
+def test_epilogue_whole_tile_kernels(schedule, waves_n, dtype, op_b, out):
+    """The LDS-staged epilogues of the ping-pong and software-pipelined kernels."""
     ops = gi.make_operands(512, 256, 96, dtype, "normal", seed=8, op_b=op_b)
-    got, ref, Dp, plan = run_epi(ops, out, act="gelu_tanh", cfg=dg.request(schedule=2))
-    assert plan.schedule == 2
+    got, ref, Dp, plan = run_epi(ops, out, act="gelu_tanh",
+                                 cfg=dg.request(schedule=schedule, waves_n=waves_n))
+    assert plan.schedule == schedule
     assert epilogue_error(got, ref, Dp, dtype, out) <= 1.0
 
 

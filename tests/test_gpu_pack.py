@@ -50,7 +50,7 @@ CASES = [(600, 300, 200), (257, 513, 95), (1, 256, 64), (300, 1, 33), (512, 256,
 
 
 @pytest.mark.parametrize("dtype,op_b", [("f16", "N"), ("bf16", "T"), ("f16", "T"), ("bf16", "N")])
-@pytest.mark.parametrize("schedule", [2, 4, 5, 1])
+@pytest.mark.parametrize("schedule", [2, 4, 5, 1])  # schedule 5: the planner's 4- or 8-wave choice
 @pytest.mark.parametrize("shape", CASES, ids=[f"{m}x{n}x{k}" for m, n, k in CASES])
 def test_pack_onto_each_schedule(dtype, op_b, schedule, shape):
     """Odd leading dimensions and a base one element off 16 bytes: packing is the

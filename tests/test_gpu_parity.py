@@ -35,7 +35,7 @@ def _lib_built():
 MENU = _menu()
 MENU_IDS = [f"k{e['kernel_id']}-{'lds' if e['variant'] == 1 else 'mfma'}-{DT_NAME[e['dtype']]}-"
             f"op{'NT'[e['opb']]}-{'v16' if e['vec'] else 'v1'}-{e['bm']}x{e['bn']}-w{e['waves_m']}x{e['waves_n']}"
-            f"{ {1: '', 2: '-pp', 3: '-dma', 4: '-pp32', 5: '-w4'}[e['schedule']] }"
+            f"{ {1: '', 2: '-pp', 3: '-dma', 4: '-pp32', 5: '-sp'}[e['schedule']] }"
             for e in MENU]
 
 
@@ -104,13 +104,14 @@ def test_kernel_random_ragged(e):
     assert err <= TOL[ops.dtype], err
 
 
-@pytest.mark.parametrize("schedule", [2, pytest.param(3, marks=pytest.mark.skip(reason=SCHED3_OFF)), 4, 5])
+@pytest.mark.parametrize("schedule,waves_n", [(2, 0), pytest.param(3, 0, marks=pytest.mark.skip(reason=SCHED3_OFF)),
+                                              (4, 0), (5, 2), (5, 4)])
 @pytest.mark.parametrize("k_tiles", [1, 2, 3, 4, 5, 6, 130])
 @pytest.mark.parametrize("dtype,op_b", [("f16", "N"), ("bf16", "N"), ("f16", "T"), ("bf16", "T")])
-def test_full_tile_kernels_k_tile_counts(schedule, k_tiles, dtype, op_b):
+def test_full_tile_kernels_k_tile_counts(schedule, waves_n, k_tiles, dtype, op_b):
     """Prologue and tail of the direct-copy kernels for every small k-tile count, and a long K."""
     ops = gi.make_operands(256, 512, 32 * k_tiles, dtype, "normal", seed=k_tiles, op_b=op_b)
-    C = run_ops(ops, cfg=dg.request(schedule=schedule), ldc=ops.N + 4)
+    C = run_ops(ops, cfg=dg.request(schedule=schedule, waves_n=waves_n), ldc=ops.N + 4)
     check_untouched(C, ops.M, ops.N)
     Cref, D = oracle.gemm_ref(ops)
     assert normalized_error(C[:ops.M, :ops.N], Cref, D) <= TOL[dtype]
