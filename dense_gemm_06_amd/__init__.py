@@ -58,12 +58,12 @@ class gemm_config(ctypes.Structure):
 
 def request(variant: int = GEMM_VARIANT_AUTO, bm: int = 0, bn: int = 0, vec: int = -1,
             xcd_remap: int = -1, group_m: int = 0, waves_m: int = 0, waves_n: int = 0,
-            schedule: int = 0, max_grid: int = 0, split_k: int = 0, pack: int = 0) -> gemm_config:
+            schedule: int = 0, max_grid: int = 0, split_k: int = 0, pack: int = 0, threads: int = 0) -> gemm_config:
     """A gemm_config with only the "in" fields set (0 / -1: heuristic decides)."""
     c = gemm_config()
     c.variant, c.bm, c.bn, c.vec, c.xcd_remap, c.group_m = variant, bm, bn, vec, xcd_remap, group_m
     c.waves_m, c.waves_n, c.schedule, c.max_grid, c.split_k = waves_m, waves_n, schedule, max_grid, split_k
-    c.pack = pack
+    c.pack, c.threads = pack, threads
     return c
 
 

@@ -1,5 +1,7 @@
 // kernel_mfma.h -- register-staged MFMA kernels (any shape, masked edges).
 #pragma once
+#include <type_traits>
+
 #include "lds_layout.h"
 
 namespace dg {
@@ -223,9 +225,17 @@ void mfma16_gemm_grouped(GroupArgs ga) {
 // Row-major B: a lane reads a float4 along n instead; P subtile u of a 64-wide
 // group holds the columns n = 4(l%16) + u, so the four subtiles share one read
 // and, at the store, a lane owns 16 consecutive n of one row of C.
-template <int OPB, bool VEC, int BM, int BN, int BK, int WM, int WN>
+//
+// KG = 2 splits K inside the workgroup: two groups of WM x WN waves, each with its
+// own LDS stages, take the even and the odd k-tiles; at the end group 1 hands its
+// accumulators to group 0 through LDS and group 0 adds them (group 0's sum first,
+// a fixed order) and stores. With one wave per SIMD a matrix instruction stream
+// issues well below the unit's rate; the second group doubles the waves per SIMD
+// for tiles too small to hold more waves.
+template <int OPB, bool VEC, int BM, int BN, int BK, int WM, int WN, int KG = 1>
 __device__ __forceinline__ void mfma32_tile(const GemmArgs& g, int tm, int tn) {
-    constexpr int NT = WM * WN * 64;
+    static_assert(KG == 1 || KG == 2, "k groups");
+    constexpr int NT = WM * WN * 64;  // threads of one k group
     constexpr int TWM = BM / WM, TWN = BN / WN;
     constexpr int SM = TWM / 16, SN = TWN / 16, QN = TWN / 64;
     constexpr int KC = BK / 4;  // 16-byte chunks per k-row
@@ -236,10 +246,13 @@ __device__ __forceinline__ void mfma32_tile(const GemmArgs& g, int tm, int tn) {
     static_assert(OPB == 1 || TWN % 64 == 0, "row-major B needs 64-wide wave tiles");
     static_assert(LA >= 1 && LB >= 1 && (BM * KC) % NT == 0, "tile does not divide the thread count");
 
-    __shared__ __attribute__((aligned(16))) float sA[2][BM * BK];
-    __shared__ __attribute__((aligned(16))) float sB[2][BN * BK];
+    __shared__ __attribute__((aligned(16))) float sAg[KG][2][BM * BK];
+    __shared__ __attribute__((aligned(16))) float sBg[KG][2][BN * BK];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int kg = KG == 1 ? 0 : (int)threadIdx.x / NT;  // uniform per wave
+    float(&sA)[2][BM * BK] = sAg[kg];
+    float(&sB)[2][BN * BK] = sBg[kg];
+    const int tid = (int)threadIdx.x - kg * NT, lane = tid & 63, wave = tid >> 6;
     const int wmi = wave / WN, wni = wave % WN;
     const int l16 = lane & 15, lg = lane >> 4;
     const int m0 = tm * BM, n0 = tn * BN;
@@ -319,15 +332,11 @@ __device__ __forceinline__ void mfma32_tile(const GemmArgs& g, int tm, int tn) {
 #pragma unroll
         for (int j = 0; j < SN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // group kg takes k-tiles kg, kg + KG, ...: nkg of them; every group runs the same
+    // number of iterations (nl) so that all threads reach every barrier
     const int nk = (K + BK - 1) / BK;
-    if (nk > 0) {
-        load_tiles(0);
-        store_tiles(0);
-    }
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) load_tiles(kt + 1);
+    const int nkg = (nk - kg + KG - 1) / KG, nl = (nk + KG - 1) / KG;
+    auto compute = [&](int cur) {
 #pragma unroll
         for (int kk = 0; kk < BK; kk += 16) {
             f32x4 qa[SM];
@@ -369,8 +378,40 @@ __device__ __forceinline__ void mfma32_tile(const GemmArgs& g, int tm, int tn) {
                             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(pb[j][s], qa[i][s], acc[i][j], 0, 0, 0);
             }
         }
-        if (kt + 1 < nk) store_tiles(cur ^ 1);
+    };
+    if (nkg > 0) {
+        load_tiles(kg);
+        store_tiles(0);
+    }
+    __syncthreads();
+    for (int lt = 0; lt < nl; ++lt) {
+        const int cur = lt & 1;
+        if (lt + 1 < nkg) load_tiles((lt + 1) * KG + kg);
+        if (lt < nkg) compute(cur);
+        if (lt + 1 < nkg) store_tiles(cur ^ 1);
         __syncthreads();
+    }
+    if constexpr (KG == 2) {
+        // group 1's accumulators through LDS (its own A stages, free after the last
+        // barrier), lane-major so that consecutive lanes touch consecutive words
+        static_assert(BM * BN <= 2 * BM * BK, "reduction buffer");
+        float* red = &sAg[1][0][0];
+        if (kg == 1) {
+#pragma unroll
+            for (int i = 0; i < SM; ++i)
+#pragma unroll
+                for (int j = 0; j < SN; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) red[(((wave * SM + i) * SN + j) * 4 + e) * 64 + lane] = acc[i][j][e];
+        }
+        __syncthreads();
+        if (kg == 1) return;
+#pragma unroll
+        for (int i = 0; i < SM; ++i)
+#pragma unroll
+            for (int j = 0; j < SN; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[i][j][e] += red[(((wave * SM + i) * SN + j) * 4 + e) * 64 + lane];
     }
 
 #pragma unroll
@@ -396,12 +437,12 @@ __device__ __forceinline__ void mfma32_tile(const GemmArgs& g, int tm, int tn) {
     }
 }
 
-template <int OPB, bool VEC, int BM, int BN, int BK, int WM, int WN>
-__global__ __launch_bounds__(WM * WN * 64) void mfma32_gemm(GemmArgs g) {
+template <int OPB, bool VEC, int BM, int BN, int BK, int WM, int WN, int KG = 1>
+__global__ __launch_bounds__(WM * WN * 64 * KG) void mfma32_gemm(GemmArgs g) {
     k_slice<4, OPB>(g);
     int tm, tn;
     tile_coords(g, tm, tn);
-    mfma32_tile<OPB, VEC, BM, BN, BK, WM, WN>(g, tm, tn);
+    mfma32_tile<OPB, VEC, BM, BN, BK, WM, WN, KG>(g, tm, tn);
 }
 
 template <int OPB, bool VEC, int BM, int BN, int BK, int WM, int WN>

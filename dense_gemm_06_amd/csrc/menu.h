@@ -45,9 +45,10 @@ constexpr bool epilogue_capable(int sched) { return sched != 3 && sched != 4; }
 
 // Configurations that also have a grouped (persistent) form: the register-staged
 // schedule, which masks every edge, except the 4-wave 256 x 256 tiles (their
-// grouped form runs out of registers).
-constexpr bool grouped_capable(int sched, int bm, int bn, int wm, int wn) {
-    return sched == 1 && !(bm == 256 && bn == 256 && wm * wn == 4);
+// grouped form runs out of registers) and the MFMA tiles that split K between two
+// wave grids (threads = 2 x 64 x wm x wn).
+constexpr bool grouped_capable(int variant, int sched, int bm, int bn, int wm, int wn, int threads) {
+    return sched == 1 && !(bm == 256 && bn == 256 && wm * wn == 4) && (variant != V_MFMA || threads == wm * wn * 64);
 }
 
 // X(id, variant, dtype, opb, vec, bm, bn, bk, wm, wn, tm, tn, threads, lds_bytes, sched)
@@ -111,6 +112,15 @@ constexpr bool grouped_capable(int sched, int bm, int bn, int wm, int wn) {
     X(base + 2, V_MFMA, dt, 0, 1, 256, 256, 32, 2, 4, 0, 0, 512, 4 * 2 * 32 * 512, 5)      \
     X(base + 3, V_MFMA, dt, 1, 1, 256, 256, 32, 2, 4, 0, 0, 512, 4 * 2 * 32 * 512, 5)
 
+// fp32 64 x 64 tiles with K split between two groups of 4 waves inside the
+// workgroup (8 waves: two per SIMD for a tile that holds four); LDS: two stages
+// per group.
+#define DG_MFMA_KG2(X, base)                                                             \
+    X(base + 0, V_MFMA, DT_F32, 0, 1, 64, 64, 32, 4, 1, 0, 0, 512, 2 * 2 * 4 * 32 * 128, 1)   \
+    X(base + 1, V_MFMA, DT_F32, 1, 1, 64, 64, 32, 4, 1, 0, 0, 512, 2 * 2 * 4 * 32 * 128, 1)   \
+    X(base + 2, V_MFMA, DT_F32, 0, 0, 64, 64, 32, 4, 1, 0, 0, 512, 2 * 2 * 4 * 32 * 128, 1)   \
+    X(base + 3, V_MFMA, DT_F32, 1, 0, 64, 64, 32, 4, 1, 0, 0, 512, 2 * 2 * 4 * 32 * 128, 1)
+
 #define DG_MENU(X)                                              \
     DG_LDS_ENTRIES(X, 0, DT_F32, 16)            \
     DG_LDS_ENTRIES(X, 8, DT_F16, 32)            \
@@ -127,9 +137,10 @@ constexpr bool grouped_capable(int sched, int bm, int bn, int wm, int wn) {
     DG_MFMA_PP32(X, 76, DT_F16)                                  \
     DG_MFMA_PP32(X, 78, DT_BF16)                                 \
     DG_MFMA_SP(X, 80, DT_F16)                                    \
-    DG_MFMA_SP(X, 84, DT_BF16)
+    DG_MFMA_SP(X, 84, DT_BF16)                                   \
+    DG_MFMA_KG2(X, 88)
 
-constexpr int kMenuSize = 88;
+constexpr int kMenuSize = 92;
 
 // Fused epilogue ("Shared memory and tensor cores", section 13.10: bias,
 // activation, residual add or type cast applied to the accumulator before the

@@ -127,6 +127,10 @@ static double tile_efficiency_aligned(const MenuEntry& e) {
     if (e.sched == 3) return 0.85;
     if (e.sched == 5) return 0.90;  // problem-dependent: see plan()
     if (e.variant == V_LDS) return t >= 128 ? 0.6 : 0.35;
+    // the fp32 64 x 64 tile with K split between two wave grids measured 7-9% faster
+    // than with one (1024^3: 27.3-27.8 us against 29.6-29.8; 256^3: 8.4-8.6 against
+    // 9.0-9.1; 512 x 4096 x 4096: 162-169 against 177-180)
+    if (e.threads > e.wm * e.wn * 64) return 0.49;
     return t >= 256 ? 0.85 : t >= 128 ? 0.7 : 0.45;
 }
 static int blocks_per_cu(const MenuEntry& e) {
@@ -178,7 +182,7 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
     const bool vec_ok = aligned16(a) && aligned16(b) && (lda * es) % 16 == 0 && (ldb * es) % 16 == 0;
 
     int want_variant = GEMM_VARIANT_AUTO, want_bm = 0, want_bn = 0, want_vec = -1, want_remap = -1, want_group = 0;
-    int want_wm = 0, want_wn = 0, want_sched = 0, want_split = 0, want_pack = 0;
+    int want_wm = 0, want_wn = 0, want_sched = 0, want_split = 0, want_pack = 0, want_threads = 0;
     if (ws_bytes < 0) {
         set_error("workspace_bytes = %lld must be non-negative", (long long)ws_bytes);
         return GEMM_ERR_INVALID_VALUE;
@@ -198,6 +202,11 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
         want_wm = req->waves_m;
         want_wn = req->waves_n;
         want_sched = req->schedule;
+        want_threads = req->threads;
+        if (want_threads < 0) {
+            set_error("threads = %d must be non-negative", want_threads);
+            return GEMM_ERR_INVALID_VALUE;
+        }
         if (want_sched < 0 || want_sched > 5 || want_wm < 0 || want_wn < 0 || want_variant < 0 || want_variant > 2 || want_vec < -1 || want_vec > 1 || want_remap < -1 ||
             want_remap > 1 || want_group < 0 || want_bm < 0 || want_bn < 0) {
             set_error("invalid requested configuration (variant %d, bm %d, bn %d, vec %d, xcd_remap %d, group_m %d)",
@@ -249,6 +258,7 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
         if (want_bn && e.bn != want_bn) continue;
         if (want_wm && (e.variant == V_MFMA ? e.wm : 1) != want_wm) continue;
         if (want_sched && e.sched != want_sched) continue;
+        if (want_threads && e.threads != want_threads) continue;
         if (!schedule_enabled(e.sched)) continue;
         if (fused_epilogue && !epilogue_capable(e.sched)) continue;
         // the direct-copy kernels copy whole tiles: no masking of M, N or K edges on
@@ -284,15 +294,20 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
             const int64_t rounds = (work + concurrent - 1) / concurrent;
             const int64_t resident = std::min<int64_t>(occ, (work + num_cus - 1) / num_cus);
             const int64_t kpad = ((std::min<int64_t>(chunk, Kx) + e.bk - 1) / e.bk) * e.bk;
-            // The software-pipelined kernel (schedule 5) in its 8-wave form was measured
-            // faster than the ping-pong kernel for row-major B and K of at least 64
-            // k-tiles (4096^3 fp16: 124-130 us against 133-147; 8192^3: 917 against 997;
-            // bf16 4096^3: 115 against 126; with the fused GELU epilogue: equal), and
-            // equal at K = 1024; with column-major B it is 9-12% slower, and its 4-wave
-            // form is slower than the 8-wave one throughout (and 16% slower than the
-            // ping-pong kernel with a fused epilogue), so those stay off by default.
+            // The software-pipelined kernel (schedule 5), as measured against the
+            // ping-pong kernel: 8 waves win for row-major B and K of at least 64 k-tiles
+            // (4096^3 fp16: 124-130 us against 133-147; 8192^3: 917 against 997; bf16
+            // 4096^3: 115 against 126; with the fused GELU epilogue: equal); 4 waves win
+            // for short K, where the C store weighs more (the packed 3001 x 5003 x 1037
+            // problem, 34 k-tiles, column-major B: 62 us against 72; 4096^2 x 1024: equal);
+            // with column-major B and long K the ping-pong kernel is 9-12% faster, and the
+            // 4-wave form is 16% slower than it with a fused epilogue.
             double eff = tile_efficiency(e);
-            if (e.sched == 5) eff = (e.wm * e.wn == 8 && e.opb == 0 && ktiles >= 64) ? 0.99 : 0.90;
+            if (e.sched == 5) {
+                const bool eight = e.wm * e.wn == 8;
+                eff = (eight && e.opb == 0 && ktiles >= 64) || (!eight && ktiles < 64 && !fused_epilogue) ? 0.99
+                                                                                                         : 0.90;
+            }
             const double tile_cycles = 2.0 * e.bm * e.bn * std::max<int64_t>(kpad, e.bk) / (rate_per_cu(e) * eff);
             double cost = (double)rounds * (double)std::max<int64_t>(resident, 1) * tile_cycles;
             // the reduction reads every plane and writes C, and is a second launch;
@@ -424,7 +439,7 @@ int plan_grouped(int opA, int opB, int dtype, const gemm_problem* probs, int cou
                  (p.ldb * es) % 16 == 0 && (!strided || ((p.stride_a * es) % 16 == 0 && (p.stride_b * es) % 16 == 0));
     }
     int want_variant = GEMM_VARIANT_AUTO, want_bm = 0, want_bn = 0, want_vec = -1, want_remap = -1, want_group = 0;
-    int want_wm = 0, want_wn = 0, want_sched = 0, want_grid = 0;
+    int want_wm = 0, want_wn = 0, want_sched = 0, want_grid = 0, want_threads = 0;
     if (req) {
         want_variant = req->variant;
         want_bm = req->bm;
@@ -436,9 +451,10 @@ int plan_grouped(int opA, int opB, int dtype, const gemm_problem* probs, int cou
         want_wn = req->waves_n;
         want_sched = req->schedule;
         want_grid = req->max_grid;
+        want_threads = req->threads;
         if (want_variant < 0 || want_variant > 2 || want_vec < -1 || want_vec > 1 || want_remap < -1 || want_remap > 1 ||
             want_group < 0 || want_bm < 0 || want_bn < 0 || want_wm < 0 || want_wn < 0 || want_sched < 0 ||
-            want_grid < 0) {
+            want_grid < 0 || want_threads < 0) {
             set_error("invalid requested configuration (variant %d, bm %d, bn %d, vec %d, xcd_remap %d, group_m %d, "
                       "max_grid %d)", want_variant, want_bm, want_bn, want_vec, want_remap, want_group, want_grid);
             return GEMM_ERR_INVALID_VALUE;
@@ -464,7 +480,8 @@ int plan_grouped(int opA, int opB, int dtype, const gemm_problem* probs, int cou
     int64_t best_tiles = 0, best_grid = 0;
     for (const MenuEntry& e : kMenu) {
         if (e.dtype != dtype || e.opb != opB) continue;
-        if (!grouped_capable(e.sched, e.bm, e.bn, e.wm, e.wn)) continue;
+        if (!grouped_capable(e.variant, e.sched, e.bm, e.bn, e.wm, e.wn, e.threads)) continue;
+        if (want_threads && e.threads != want_threads) continue;
         if (want_variant != GEMM_VARIANT_AUTO && e.variant != want_variant) continue;
         if (want_bm && e.bm != want_bm) continue;
         if (want_bn && e.bn != want_bn) continue;

@@ -83,7 +83,8 @@ typedef struct gemm_config {
     int32_t group_m;   /* in/out: 0 auto; tile rows per raster group */
     int32_t waves_m, waves_n;   /* in/out: wave grid of an MFMA workgroup (1 x 1 for LDS); 0 = any */
     int32_t thread_m, thread_n; /* out: per-thread micro-tile of the LDS kernel (0 for MFMA) */
-    int32_t threads;   /* out: workgroup size */
+    int32_t threads;   /* in/out: 0 any; workgroup size (64 x waves_m x waves_n, or twice that for
+                          the fp32 64 x 64 configurations that split K between two wave grids) */
     int32_t lds_bytes; /* out: LDS per workgroup */
     int32_t grid;      /* out: workgroups launched (tiles_m * tiles_n) */
     int32_t kernel_id; /* out: index into the library's kernel menu */

@@ -51,21 +51,24 @@ def test_status_strings():
 
 def test_menu_is_complete():
     menu = dg.gemm_menu()
-    assert len(menu) == dg.library().gemm_menu_size() == 88
+    assert len(menu) == dg.library().gemm_menu_size() == 92
     seen = set()
     for e in menu:
         assert e["lds_bytes"] <= 160 * 1024
         assert e["threads"] in (256, 512)
         seen.add((e["variant"], e["dtype"], e["opb"], e["vec"], e["bm"], e["bn"]))
         if e["variant"] == dg.GEMM_VARIANT_MFMA:
-            assert e["waves_m"] * e["waves_n"] * 64 == e["threads"]
+            # one wave grid per workgroup, or two that split K (fp32 64 x 64 only)
+            k_groups = e["threads"] // (e["waves_m"] * e["waves_n"] * 64)
+            assert k_groups * e["waves_m"] * e["waves_n"] * 64 == e["threads"] and k_groups in (1, 2)
+            assert k_groups == 1 or (e["dtype"] == 0 and (e["bm"], e["bn"]) == (64, 64) and e["schedule"] == 1)
     for variant in (1, 2):
         for dtype in (0, 1, 2):
             for opb in (0, 1):
                 for vec in (0, 1):
                     tiles = {(bm, bn) for (v, d, o, ve, bm, bn) in seen if (v, d, o, ve) == (variant, dtype, opb, vec)}
                     assert len(tiles) >= 2, (variant, dtype, opb, vec)
-    assert dg.library().gemm_menu_entry(88, None, None, None, None) == dg.GEMM_ERR_INVALID_VALUE
+    assert dg.library().gemm_menu_entry(92, None, None, None, None) == dg.GEMM_ERR_INVALID_VALUE
 
 
 def plan(M, N, K, dtype="f32", op_b="N", lda=None, ldb=None, ldc=None, a=0, b=0, c=0, cus=256, arch="gfx950",
@@ -97,8 +100,13 @@ def test_plan_software_pipelined_kernel_where_measured_faster():
                         (8192, 8192, 8192, "f16")):
         c = plan(m, n, k, dt)[1]
         assert c.schedule == 5 and (c.waves_m, c.waves_n) == (2, 4), (m, n, k, dt)
-    assert plan(4096, 4096, 1024, "f16")[1].schedule == 2
+    c = plan(4096, 4096, 1024, "f16")[1]   # short K: the 4-wave form
+    assert c.schedule == 5 and c.threads == 256
     assert plan(4096, 4096, 4096, "f16", "T")[1].schedule == 2
+    # the ragged column-major problem, packed into whole tiles of K = 1088: 4 waves
+    st, c = dg.gemm_plan_workspace(0, 1, 3001, 5003, 1037, 1037, 1037, 5003, dg.GEMM_BF16, 0x10002, 0x200002,
+                                   0x400000, 256, "gfx950", 64 << 20, None)
+    assert st == 0 and c.pack == 2 and c.schedule == 5 and c.threads == 256
     st, c = dg.gemm_plan_workspace(0, 0, 4096, 4096, 4096, 4096, 4096, 4096, dg.GEMM_F16, 0, 0, 0, 256, "gfx950", 0,
                                    None, epi=dg.epilogue(activation="relu"))
     assert st == 0 and c.schedule == 5 and c.waves_n == 4
@@ -390,10 +398,11 @@ def test_split_workspace_rejections_before_device():
 
 # ----------------------------------------------------------------------------- packed operands
 def test_pack_plan_choices():
-    # the ragged bf16 benchmark problem packs onto the whole-tile ping-pong kernel
+    # the ragged bf16 benchmark problem packs onto a whole-tile kernel (the 4-wave
+    # software-pipelined one for its short K)
     st, c = dg.gemm_plan_workspace(0, 1, 3001, 5003, 1037, 1037, 1037, 5003, dg.GEMM_BF16, 4096, 4096, 4096, 256,
                                    "gfx950", 1 << 30)
-    assert st == 0 and c.pack == 2 and c.schedule == 2 and c.vec == 1 and c.launches == 2
+    assert st == 0 and c.pack == 2 and c.schedule == 5 and c.vec == 1 and c.launches == 2
     assert (c.tiles_m, c.tiles_n) == (12, 20)
     assert c.workspace_bytes == 3072 * 1088 * 2 + 5120 * 1088 * 2
     # without workspace, or with pack = 1, it does not
@@ -463,3 +472,28 @@ def test_epilogue_rejections_before_device():
     # empty output: nothing to check, nothing launched
     assert ex(0, 0, 0, 64, 64, 0, 64, 0, 64, 0, 64, 0, dg.epilogue(beta=1.0), None, None, 0, None,
               check=False) == dg.GEMM_OK
+
+
+def test_threads_request_selects_k_split_kernels():
+    """The fp32 64 x 64 tile exists with one wave grid (256 threads) and with two that
+    split K (512 threads); the requested workgroup size picks between them."""
+    for threads in (256, 512):
+        st, c = plan(1024, 1024, 1024, "f32", req=dg.request(bm=64, bn=64, threads=threads))
+        assert st == 0 and c.threads == threads and (c.bm, c.bn) == (64, 64)
+    st, _ = plan(1024, 1024, 1024, "f32", req=dg.request(threads=-1))
+    assert st == dg.GEMM_ERR_INVALID_VALUE
+    st, _ = plan(1024, 1024, 1024, "f32", req=dg.request(bm=64, bn=64, threads=384))
+    assert st == dg.GEMM_ERR_UNSUPPORTED
+    # grouped calls have no K-split form
+    st, _ = dg.gemm_grouped_plan(0, 0, dg.GEMM_F32, [dg.problem(64, 64, 64, 0x10000, 64, 0x100000, 64, 0x200000, 64)],
+                                 req=dg.request(bm=64, bn=64, threads=512), check=False)
+    assert st == dg.GEMM_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_grouped_plan_every_variant(dtype):
+    """Both kernel families have grouped forms for every input type."""
+    probs = [dg.problem(100, 90, 80, 0x10000, 80, 0x100000, 90, 0x200000, 90)]
+    for variant in (dg.GEMM_VARIANT_LDS, dg.GEMM_VARIANT_MFMA):
+        st, c = dg.gemm_grouped_plan(0, 0, dg.DTYPE_CODE[dtype], probs, req=dg.request(variant=variant), check=False)
+        assert st == 0 and c.variant == variant, (dtype, variant, dg.gemm_last_error())

@@ -54,7 +54,7 @@ def menu_params():
 
 def forced(e):
     return dg.request(variant=e["variant"], bm=e["bm"], bn=e["bn"], vec=e["vec"], waves_m=e["waves_m"],
-                      waves_n=e["waves_n"], schedule=e["schedule"])
+                      waves_n=e["waves_n"], threads=e["threads"], schedule=e["schedule"])
 
 
 def ragged_shape(e):

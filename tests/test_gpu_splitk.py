@@ -63,7 +63,7 @@ def run_split(ops: gi.Operands, cfg, ws_bytes=1 << 26, ldc=None, ws_fill=float("
 
 def forced(e, split):
     return dg.request(variant=e["variant"], bm=e["bm"], bn=e["bn"], vec=e["vec"], waves_m=e["waves_m"],
-                      waves_n=e["waves_n"], schedule=1, split_k=split)
+                      waves_n=e["waves_n"], threads=e["threads"], schedule=1, split_k=split)
 
 
 def shape_for(e):
