@@ -12,6 +12,29 @@
 
 namespace dg {
 
+// Eight consecutive 16-bit elements from a 2-byte aligned address p, reading only
+// those 16 bytes, as four 32-bit words: a chunk that starts 4-byte aligned is four
+// aligned words; one that starts 2 bytes off is elements 1..6 as three aligned words
+// plus elements 0 and 7 as halves. The three middle words are one load instruction
+// for both kinds of lane (only the address differs), so a wave whose lanes mix the
+// two alignments (rows of odd length) issues six loads where element-wise loading
+// issues eight. (In the GEMM kernels' own loaders this measured slower than
+// element-wise loads on the ragged 3001 x 5003 x 1037 problem, 130 us against 112.)
+__device__ __forceinline__ u32x4 load8_u16(const uint16_t* p) {
+    const bool odd = (reinterpret_cast<uintptr_t>(p) & 2) != 0;
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(p + (odd ? 1 : 2));  // 4-byte aligned either way
+    const uint32_t m0 = q[0], m1 = q[1], m2 = q[2];  // elements 2..7 (aligned) or 1..6 (odd)
+    uint32_t first, last = 0;
+    if (odd) {
+        first = p[0];
+        last = p[7];
+    } else {
+        first = *reinterpret_cast<const uint32_t*>(p);  // elements 0, 1
+    }
+    if (!odd) return u32x4{first, m0, m1, m2};
+    return u32x4{first | (m0 << 16), (m0 >> 16) | (m1 << 16), (m1 >> 16) | (m2 << 16), (m2 >> 16) | (last << 16)};
+}
+
 // One thread per 16-byte chunk of a destination, grid-stride over the chunks of
 // both destinations (A's first, then B's). Source elements outside rows x cols
 // are never read.
@@ -33,18 +56,7 @@ __global__ __launch_bounds__(256) void pack_pad(PackJob a, PackJob b, int64_t ch
         if (sizeof(T) == 2 && r < rows && c0 + V <= cols) {
             // a whole chunk of 8 16-bit elements inside the source: 4-byte loads (16-bit
             // elements start on 2-byte boundaries, so a chunk is 4-byte aligned or 2 off)
-            const uint16_t* p = reinterpret_cast<const uint16_t*>(src + r * ld + c0);
-            if ((reinterpret_cast<uintptr_t>(p) & 3) == 0) {
-                const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
-                w = u32x4{q[0], q[1], q[2], q[3]};
-            } else {
-                // elements 1..6 as three aligned words, 0 and 7 on their own: nothing
-                // outside the chunk is read
-                const uint32_t* q = reinterpret_cast<const uint32_t*>(p + 1);
-                const uint32_t d0 = q[0], d1 = q[1], d2 = q[2];
-                const uint32_t e0 = p[0], e7 = p[7];
-                w = u32x4{e0 | (d0 << 16), (d0 >> 16) | (d1 << 16), (d1 >> 16) | (d2 << 16), (d2 >> 16) | (e7 << 16)};
-            }
+            w = load8_u16(reinterpret_cast<const uint16_t*>(src + r * ld + c0));
         } else {
             T v[V];
 #pragma unroll
