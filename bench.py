@@ -366,6 +366,10 @@ def main():
 
     cfg = main_res["cfg"]
     traffic = load_traffic(headline, cfg)
+    import gemm_inputs as gi
+    spec = gi.CONFIGS.get(headline) or gi.EXTRA_CONFIGS[headline]
+    dist_text = "uniform[-1,1)" if spec["dist"] == "uniform" else "normal N(0,1)"
+    b_text = "row-major" if spec["op_b"] == "N" else "column-major"
     roof = {"bound": "mfma", "achieved": main_res["kernel_tflops"], "peak": main_res["peak"], "unit": "TFLOP/s",
             "frac": main_res["kernel_tflops"] / main_res["peak"], "traffic": traffic,
             "kernel": kernel_name(cfg, main_res["dtype"]),
@@ -382,9 +386,9 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": main_res["dtype"],
-        "data": "synthetic (seeded uniform[-1,1) rounded to the input dtype)",
+        "data": f"synthetic (seeded {dist_text} rounded to the input dtype)",
         "config": {"workload": f"C=A@B {main_res['M']}x{main_res['N']}x{main_res['K']} {main_res['dtype']} in, "
-                               f"fp32 acc/out, row-major A,B", "M": main_res["M"], "N": main_res["N"],
+                               f"fp32 acc/out, row-major A, {b_text} B", "M": main_res["M"], "N": main_res["N"],
                    "K": main_res["K"], "kernel_cfg": {k: v for k, v in cfg.as_dict().items() if k != "est_cycles"},
                    "cus": main_res["cus"], "arch": main_res["arch"]},
         "pct_of_peak": round(100 * main_res["tflops"] / main_res["peak"], 2),

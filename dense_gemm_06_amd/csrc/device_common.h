@@ -279,11 +279,18 @@ __device__ __forceinline__ void store_run4(const GemmArgs& g, int m, int n, f32x
 // Load V consecutive elements starting at p into a register chunk, zero-filling
 // the elements at index >= valid (valid <= 0 means the whole chunk is outside
 // the matrix and nothing is read). VEC selects one 16-byte load when the chunk
-// is complete; the caller guarantees 16-byte alignment in that case.
+// is complete. The address need only be aligned to the element: gfx950 under the
+// HSA runtime serves under-aligned global vector loads (the compiler itself emits
+// global_load_dwordx4 for a 16-byte copy from a 2-byte-aligned address there).
+template <typename T, int V>
+__device__ __forceinline__ void load16(T (&r)[V], const T* p) {
+    static_assert(sizeof(T) * V == 16, "a chunk is 16 bytes");
+    __builtin_memcpy(r, p, 16);
+}
 template <typename T, int V, bool VEC>
 __device__ __forceinline__ void load_chunk(T (&r)[V], const T* p, int valid) {
     if (VEC && valid >= V) {
-        *reinterpret_cast<u32x4*>(r) = *reinterpret_cast<const u32x4*>(p);
+        load16(r, p);
     } else {
 #pragma unroll
         for (int e = 0; e < V; ++e) r[e] = (e < valid) ? p[e] : T(0);
@@ -294,7 +301,7 @@ __device__ __forceinline__ void load_chunk(T (&r)[V], const T* p, int valid) {
 template <typename T, int V, bool VEC>
 __device__ __forceinline__ void load_chunk_full(T (&r)[V], const T* p) {
     if (VEC) {
-        *reinterpret_cast<u32x4*>(r) = *reinterpret_cast<const u32x4*>(p);
+        load16(r, p);
     } else {
 #pragma unroll
         for (int e = 0; e < V; ++e) r[e] = p[e];

@@ -113,10 +113,17 @@ static double rate_per_cu(const MenuEntry& e) {
     return e.dtype == DT_F32 ? 256.0 : 4096.0;
 }
 static double tile_efficiency_aligned(const MenuEntry& e);
-// Element-wise global loads (unaligned operands) measured about 3x slower for
-// 16-bit inputs (c5-like shapes) and are assumed 1.7x slower for fp32.
-static double tile_efficiency(const MenuEntry& e) {
-    return tile_efficiency_aligned(e) * (e.vec ? 1.0 : (e.dtype == DT_F32 ? 0.6 : 0.35));
+// Load-path factor. 16-byte loads from rows that are not 16-byte aligned, on the
+// register-staged 256 x 256 kernels, as measured against the same kernel on a
+// 16-byte-aligned problem of the same tile counts: 16-bit 3001 x 5003 x 1037 with
+// column-major B 69-75 us against 54-57 (3008 x 5008 x 1040), 4095^3 f16 310-321
+// us against 165 (4096^3); fp32 4095^3 1303 us against 1032. Element-wise loads
+// (bases not aligned to the element) measured about 3x slower for 16-bit inputs
+// and are assumed 1.7x slower for fp32.
+static double tile_efficiency(const MenuEntry& e, bool rows16) {
+    const bool f32 = e.dtype == DT_F32;
+    const double load = !e.vec ? (f32 ? 0.6 : 0.35) : rows16 ? 1.0 : (f32 ? 0.8 : 0.55);
+    return tile_efficiency_aligned(e) * load;
 }
 static double tile_efficiency_aligned(const MenuEntry& e) {
     const int t = std::min(e.bm, e.bn);
@@ -140,6 +147,7 @@ static int blocks_per_cu(const MenuEntry& e) {
 }
 
 static bool aligned16(uintptr_t a) { return (a & 15) == 0; }
+static bool elem_aligned(uintptr_t a, int es) { return (a & (uintptr_t)(es - 1)) == 0; }
 
 void pack_dims(int64_t M, int64_t N, int64_t K, int64_t* Mp, int64_t* Np, int64_t* Kp) {
     *Mp = (M + 255) / 256 * 256;
@@ -179,7 +187,11 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
         return GEMM_ERR_INVALID_VALUE;
     }
     const int es = elem_size(dtype);
-    const bool vec_ok = aligned16(a) && aligned16(b) && (lda * es) % 16 == 0 && (ldb * es) % 16 == 0;
+    // Register-staged kernels read 16-byte chunks with under-aligned vector loads,
+    // which need only element-aligned bases; the direct global -> LDS copies of the
+    // whole-tile kernels need 16-byte-aligned bases and rows.
+    const bool vec_ok = elem_aligned(a, es) && elem_aligned(b, es);
+    const bool dma_ok = aligned16(a) && aligned16(b) && (lda * es) % 16 == 0 && (ldb * es) % 16 == 0;
 
     int want_variant = GEMM_VARIANT_AUTO, want_bm = 0, want_bn = 0, want_vec = -1, want_remap = -1, want_group = 0;
     int want_wm = 0, want_wn = 0, want_sched = 0, want_split = 0, want_pack = 0, want_threads = 0;
@@ -224,7 +236,7 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
             return GEMM_ERR_INVALID_VALUE;
         }
         if (want_vec == 1 && !vec_ok && (ws_bytes == 0 || want_pack == 1)) {
-            set_error("16-byte loads requested but A/B bases or leading dimensions are not 16-byte aligned");
+            set_error("16-byte loads requested but the A/B bases are not aligned to the element size");
             return GEMM_ERR_UNSUPPORTED;
         }
     }
@@ -267,7 +279,8 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
         if (want_wn && (e.variant == V_MFMA ? e.wn : 1) != want_wn) continue;
         const int vec = want_vec >= 0 ? want_vec : ((packed || vec_ok) ? 1 : 0);
         if (e.vec != vec) continue;
-        if (e.vec && !packed && !vec_ok) continue;  // 16-byte loads need aligned operands
+        if (e.vec && !packed && !vec_ok) continue;          // 16-byte loads need element-aligned bases
+        if (e.sched >= 2 && !packed && !dma_ok) continue;   // direct LDS copies need 16-byte alignment
         const int64_t tiles = e.sched >= 2 ? (Mx / e.bm) * (Nx / e.bn) : ((M + e.bm - 1) / e.bm) * ((N + e.bn - 1) / e.bn);
         const int64_t ktiles = (Kx + e.bk - 1) / e.bk;
         const int occ = blocks_per_cu(e);
@@ -302,7 +315,7 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
             // problem, 34 k-tiles, column-major B: 62 us against 72; 4096^2 x 1024: equal);
             // with column-major B and long K the ping-pong kernel is 9-12% faster, and the
             // 4-wave form is 16% slower than it with a fused epilogue.
-            double eff = tile_efficiency(e);
+            double eff = tile_efficiency(e, packed || dma_ok);
             if (e.sched == 5) {
                 const bool eight = e.wm * e.wn == 8;
                 eff = (eight && e.opb == 0 && ktiles >= 64) || (!eight && ktiles < 64 && !fused_epilogue) ? 0.99
@@ -430,13 +443,15 @@ int plan_grouped(int opA, int opB, int dtype, const gemm_problem* probs, int cou
         return GEMM_ERR_INVALID_VALUE;
     }
     const int es = elem_size(dtype);
-    bool vec_ok = true;
+    bool vec_ok = true, rows16 = true;
     for (int i = 0; i < count; ++i) {
         const gemm_problem& p = probs[i];
         if (p.M == 0 || p.N == 0 || p.batch == 0) continue;
-        const bool strided = p.batch > 1;
-        vec_ok = vec_ok && aligned16((uintptr_t)p.A) && aligned16((uintptr_t)p.B) && (p.lda * es) % 16 == 0 &&
-                 (p.ldb * es) % 16 == 0 && (!strided || ((p.stride_a * es) % 16 == 0 && (p.stride_b * es) % 16 == 0));
+        // batch strides are in elements, so every batch stays element-aligned
+        vec_ok = vec_ok && elem_aligned((uintptr_t)p.A, es) && elem_aligned((uintptr_t)p.B, es);
+        rows16 = rows16 && aligned16((uintptr_t)p.A) && aligned16((uintptr_t)p.B) && (p.lda * es) % 16 == 0 &&
+                 (p.ldb * es) % 16 == 0 &&
+                 (p.batch <= 1 || ((p.stride_a * es) % 16 == 0 && (p.stride_b * es) % 16 == 0));
     }
     int want_variant = GEMM_VARIANT_AUTO, want_bm = 0, want_bn = 0, want_vec = -1, want_remap = -1, want_group = 0;
     int want_wm = 0, want_wn = 0, want_sched = 0, want_grid = 0, want_threads = 0;
@@ -470,8 +485,7 @@ int plan_grouped(int opA, int opB, int dtype, const gemm_problem* probs, int cou
             return GEMM_ERR_UNSUPPORTED;
         }
         if (want_vec == 1 && !vec_ok) {
-            set_error("16-byte loads requested but some base, leading dimension or batch stride is not 16-byte "
-                      "aligned");
+            set_error("16-byte loads requested but some A/B base is not aligned to the element size");
             return GEMM_ERR_UNSUPPORTED;
         }
     }
@@ -496,7 +510,7 @@ int plan_grouped(int opA, int opB, int dtype, const gemm_problem* probs, int cou
             if (p.M == 0 || p.N == 0 || p.batch == 0) continue;
             const int64_t t = p.batch * ((p.M + e.bm - 1) / e.bm) * ((p.N + e.bn - 1) / e.bn);
             const int64_t kpad = std::max<int64_t>(((p.K + e.bk - 1) / e.bk) * e.bk, e.bk);
-            const double tc = 2.0 * e.bm * e.bn * (double)kpad / (rate_per_cu(e) * tile_efficiency(e));
+            const double tc = 2.0 * e.bm * e.bn * (double)kpad / (rate_per_cu(e) * tile_efficiency(e, rows16));
             tiles += t;
             work += (double)t * tc;
             longest = std::max(longest, tc);

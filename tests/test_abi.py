@@ -86,9 +86,11 @@ def test_plan_benchmark_configs():
     assert c.vec == 1 and c.schedule == 5 and c.threads == 512 and (c.waves_m, c.waves_n) == (2, 4)
     st, c = plan(4096, 4096, 4096, "f32")
     assert st == 0 and c.variant == dg.GEMM_VARIANT_MFMA and c.vec == 1
-    # ragged bf16 with column-major B and odd leading dimensions: element-wise loads
+    # ragged bf16 with column-major B and odd leading dimensions: 16-byte loads from
+    # 2-byte-aligned rows on the register-staged 256 x 256 kernel
     st, c = plan(3001, 5003, 1037, "bf16", "T", lda=1037, ldb=1037, ldc=5003)
-    assert st == 0 and c.variant == dg.GEMM_VARIANT_MFMA and c.vec == 0 and c.schedule == 1
+    assert st == 0 and c.variant == dg.GEMM_VARIANT_MFMA and c.vec == 1 and c.schedule == 1
+    assert (c.bm, c.bn) == (256, 256)
     assert c.tiles_m == -(-3001 // c.bm) and c.tiles_n == -(-5003 // c.bn)
 
 
@@ -150,14 +152,25 @@ def test_plan_fills_the_machine():
 
 
 def test_plan_alignment_rules():
-    # misaligned base pointer or leading dimension -> element-wise loads
-    assert plan(512, 512, 512, "f16", a=2)[1].vec == 0
-    assert plan(512, 512, 512, "f16", lda=516)[1].vec == 0     # 1032 bytes per row
+    # element-aligned bases: 16-byte loads, whatever the row alignment
+    assert plan(512, 512, 512, "f16", a=2)[1].vec == 1
+    assert plan(512, 512, 512, "f16", lda=516)[1].vec == 1     # 1032 bytes per row
     assert plan(512, 512, 512, "f16", lda=520)[1].vec == 1     # 1040 bytes = 65 x 16
-    assert plan(512, 512, 512, "f32", ldb=514)[1].vec == 0
-    # forcing 16-byte loads on misaligned data is refused
-    st, _ = plan(512, 512, 512, "f16", a=2, req=dg.request(vec=1))
+    assert plan(512, 512, 512, "f32", ldb=514)[1].vec == 1
+    # a base not aligned to the element: element-wise loads
+    assert plan(512, 512, 512, "f16", a=1)[1].vec == 0
+    assert plan(512, 512, 512, "f32", b=6)[1].vec == 0
+    # the direct global -> LDS copies of the whole-tile kernels need 16-byte rows
+    assert plan(4096, 4096, 4096, "f16")[1].schedule == 5
+    for kw in (dict(a=2), dict(lda=4100), dict(b=8), dict(ldb=4100)):
+        st, c = plan(4096, 4096, 4096, "f16", **kw)
+        assert st == 0 and c.schedule == 1 and c.vec == 1, kw
+        st, _ = plan(4096, 4096, 4096, "f16", req=dg.request(schedule=5), **kw)
+        assert st == dg.GEMM_ERR_UNSUPPORTED, kw
+    # forcing 16-byte loads on bases not aligned to the element is refused
+    st, _ = plan(512, 512, 512, "f16", a=1, req=dg.request(vec=1))
     assert st == dg.GEMM_ERR_UNSUPPORTED
+    assert plan(512, 512, 512, "f16", a=2, req=dg.request(vec=1))[0] == 0
 
 
 def test_plan_forced_configurations():
@@ -266,10 +279,13 @@ def test_grouped_plan_max_grid_and_vec():
     st, c = dg.gemm_grouped_plan(0, 0, dg.GEMM_F32, probs, req=dg.request(max_grid=5))
     assert st == 0 and c.grid == 5
     assert dg.gemm_grouped_plan(0, 0, dg.GEMM_F32, probs)[1].vec == 1
-    # one unaligned batch stride turns the 16-byte path off for the whole call
+    # batch strides are in elements: an odd one keeps the 16-byte path
     odd = probs + [gp(64, 64, 64, a=1 << 40, b=1 << 41, c=1 << 42, batch=2, sa=64 * 64 + 1, sb=4096, sc=4096)]
-    assert dg.gemm_grouped_plan(0, 0, dg.GEMM_F32, odd)[1].vec == 0
-    st, _ = dg.gemm_grouped_plan(0, 0, dg.GEMM_F32, odd, req=dg.request(vec=1), check=False)
+    assert dg.gemm_grouped_plan(0, 0, dg.GEMM_F32, odd)[1].vec == 1
+    # one base not aligned to the element turns it off for the whole call
+    bad = probs + [gp(64, 64, 64, a=(1 << 40) + 2, b=1 << 41, c=1 << 42)]
+    assert dg.gemm_grouped_plan(0, 0, dg.GEMM_F32, bad)[1].vec == 0
+    st, _ = dg.gemm_grouped_plan(0, 0, dg.GEMM_F32, bad, req=dg.request(vec=1), check=False)
     assert st == dg.GEMM_ERR_UNSUPPORTED
 
 
@@ -409,7 +425,7 @@ def test_pack_plan_choices():
     assert plan(3001, 5003, 1037, "bf16", "T", lda=1037, ldb=1037, ldc=5003)[1].pack == 1
     st, c = dg.gemm_plan_workspace(0, 1, 3001, 5003, 1037, 1037, 1037, 5003, dg.GEMM_BF16, 4096, 4096, 4096, 256,
                                    "gfx950", 1 << 30, dg.request(pack=1))
-    assert st == 0 and c.pack == 1 and c.vec == 0
+    assert st == 0 and c.pack == 1 and c.vec == 1 and c.schedule == 1
     # an aligned whole-tile problem gains nothing from a copy
     assert wplan(4096, 4096, 4096, "f16")[1].pack == 1
 
@@ -423,10 +439,10 @@ def test_pack_errors():
     assert st == dg.GEMM_ERR_INVALID_VALUE
     st, _ = dg.gemm_grouped_plan(0, 0, dg.GEMM_F32, [gp(64, 64, 64)], req=dg.request(pack=2), check=False)
     assert st == dg.GEMM_ERR_UNSUPPORTED
-    # 16-byte loads on unaligned operands: possible only by packing
-    st, _ = dg.gemm_plan(0, 0, 64, 64, 63, 63, 64, 64, dg.GEMM_F16, req=dg.request(vec=1), check=False)
+    # 16-byte loads on a base not aligned to the element: possible only by packing
+    st, _ = dg.gemm_plan(0, 0, 64, 64, 63, 63, 64, 64, dg.GEMM_F16, 1, 0, 0, req=dg.request(vec=1), check=False)
     assert st == dg.GEMM_ERR_UNSUPPORTED
-    st, c = dg.gemm_plan_workspace(0, 0, 64, 64, 63, 63, 64, 64, dg.GEMM_F16, 0, 0, 0, 256, "gfx950", 1 << 20,
+    st, c = dg.gemm_plan_workspace(0, 0, 64, 64, 63, 63, 64, 64, dg.GEMM_F16, 1, 0, 0, 256, "gfx950", 1 << 20,
                                    dg.request(vec=1))
     assert st == 0 and c.pack == 2 and c.vec == 1
 

@@ -194,7 +194,8 @@ def test_strided_batched_shared_b(dtype, op_b):
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
 def test_grouped_vector_path(dtype):
     """16-byte aligned bases, leading dimensions and strides give the 16-byte load path;
-    one unaligned stride falls back to element-wise loads for the whole call."""
+    so does an odd batch stride (16-byte loads from element-aligned addresses); the
+    element-wise loads, forced, give the same result."""
     q = 4 if dtype == "f32" else 8
     aligned = [rand_entry(192, 160, 96, dtype, "N", 70, batch=2, stride_a=192 * 96 + 4 * q, stride_b=96 * 160 + q),
                rand_entry(64, 128, 64, dtype, "N", 71)]
@@ -203,8 +204,9 @@ def test_grouped_vector_path(dtype):
     run(aligned, dtype, "N")
     for e in aligned:
         e.check()
-    unaligned = [rand_entry(192, 160, 96, dtype, "N", 72, batch=2, stride_a=192 * 96 + 1)]
-    _, cfg = dg.gemm_grouped_plan(0, 0, dg.DTYPE_CODE[dtype], [e.problem() for e in unaligned])
-    assert cfg.vec == 0
-    run(unaligned, dtype, "N")
-    unaligned[0].check()
+    for vec in (-1, 0):
+        unaligned = [rand_entry(192, 160, 93, dtype, "N", 72, batch=2, ld_pad=(1, 3, 0))]  # odd strides and lds
+        _, cfg = dg.gemm_grouped_plan(0, 0, dg.DTYPE_CODE[dtype], [e.problem() for e in unaligned])
+        assert cfg.vec == 1
+        run(unaligned, dtype, "N", cfg=dg.request(vec=vec))
+        unaligned[0].check()

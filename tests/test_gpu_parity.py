@@ -225,13 +225,25 @@ def test_small_and_degenerate_shapes(dtype, op_b, shape):
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("op_b", ["N", "T"])
-def test_misaligned_bases(dtype, op_b):
-    """Operands starting 1 element past a 16-byte boundary run the element-wise path correctly."""
-    ops = gi.make_operands(300, 200, 150, dtype, "normal", seed=9, op_b=op_b)
-    C = run_ops(ops, a_off=1, b_off=1, c_off=1, ldc=201)
-    check_untouched(C, ops.M, ops.N)
+@pytest.mark.parametrize("off", [1, 3])
+@pytest.mark.parametrize("vec", [1, 0])
+def test_misaligned_bases(dtype, op_b, off, vec):
+    """Operands starting `off` elements past a 16-byte boundary, with leading
+    dimensions that move every row to another offset within 16 bytes: the 16-byte
+    loads from element-aligned addresses (the heuristic's choice) and the
+    element-wise loads both give the oracle's result, including the partial
+    chunks at the K edge."""
+    M, N, K = 300, 200, 150
+    ldb = N + 5 if op_b == "N" else K + 5
+    ops = gi.make_operands(M, N, K, dtype, "normal", seed=9 + off, op_b=op_b, lda=K + 3, ldb=ldb)
+    es = 4 if dtype == "f32" else 2
+    _, cfg = dg.gemm_plan(0, dg.OP_CODE[op_b], M, N, K, ops.lda, ops.ldb, 201, dg.DTYPE_CODE[dtype],
+                          (1 << 20) + off * es, (1 << 21) + off * es, 1 << 22)
+    assert cfg.vec == 1 and cfg.schedule == 1
+    C = run_ops(ops, cfg=dg.request(vec=vec), a_off=off, b_off=off, c_off=off, ldc=201)
+    check_untouched(C, M, N)
     Cref, D = oracle.gemm_ref(ops)
-    assert normalized_error(C[:ops.M, :ops.N], Cref, D) <= TOL[dtype]
+    assert normalized_error(C[:M, :N], Cref, D) <= TOL[dtype]
 
 
 @pytest.mark.parametrize("dtype,op_b", [("f32", "N"), ("f16", "N"), ("bf16", "T")])
