@@ -305,7 +305,7 @@ def kernel_name(cfg, dtype):
     if cfg.variant == 1:
         base = "lds_gemm"
     elif dtype == "f32":
-        base = "mfma32_gemm"
+        base = "mfma32_gemm, three LDS stages" if cfg.schedule == 6 else "mfma32_gemm"
     else:
         base = {1: "mfma16_gemm", 2: "mfma16_pp (16x16x32)", 3: "mfma16_dma", 4: "mfma16_pp (32x32x16)",
                 5: "mfma32_sp (32x32x16)"}[cfg.schedule]

@@ -232,9 +232,17 @@ void mfma16_gemm_grouped(GroupArgs ga) {
 // a fixed order) and stores. With one wave per SIMD a matrix instruction stream
 // issues well below the unit's rate; the second group doubles the waves per SIMD
 // for tiles too small to hold more waves.
-template <int OPB, bool VEC, int BM, int BN, int BK, int WM, int WN, int KG = 1>
+//
+// ST = 3 keeps three LDS stages instead of two, so that the fragments of the next
+// k-tile can be read before the barrier that ends the current one: tile t + 1 was
+// stored one iteration earlier, and the stage being filled (t + 2) is the one
+// every wave finished reading before the previous barrier. Fragments are double-
+// buffered by halves of the k-tile: each half's reads are issued while the other
+// half's MFMAs run, so no MFMA waits on an LDS read that was issued just before it.
+template <int OPB, bool VEC, int BM, int BN, int BK, int WM, int WN, int KG = 1, int ST = 2>
 __device__ __forceinline__ void mfma32_tile(const GemmArgs& g, int tm, int tn) {
     static_assert(KG == 1 || KG == 2, "k groups");
+    static_assert(ST == 2 || (ST == 3 && KG == 1 && BK == 32), "three stages: one k group, k-tiles of 32");
     constexpr int NT = WM * WN * 64;  // threads of one k group
     constexpr int TWM = BM / WM, TWN = BN / WN;
     constexpr int SM = TWM / 16, SN = TWN / 16, QN = TWN / 64;
@@ -246,12 +254,12 @@ __device__ __forceinline__ void mfma32_tile(const GemmArgs& g, int tm, int tn) {
     static_assert(OPB == 1 || TWN % 64 == 0, "row-major B needs 64-wide wave tiles");
     static_assert(LA >= 1 && LB >= 1 && (BM * KC) % NT == 0, "tile does not divide the thread count");
 
-    __shared__ __attribute__((aligned(16))) float sAg[KG][2][BM * BK];
-    __shared__ __attribute__((aligned(16))) float sBg[KG][2][BN * BK];
+    __shared__ __attribute__((aligned(16))) float sAg[KG][ST][BM * BK];
+    __shared__ __attribute__((aligned(16))) float sBg[KG][ST][BN * BK];
 
     const int kg = KG == 1 ? 0 : (int)threadIdx.x / NT;  // uniform per wave
-    float(&sA)[2][BM * BK] = sAg[kg];
-    float(&sB)[2][BN * BK] = sBg[kg];
+    float(&sA)[ST][BM * BK] = sAg[kg];
+    float(&sB)[ST][BN * BK] = sBg[kg];
     const int tid = (int)threadIdx.x - kg * NT, lane = tid & 63, wave = tid >> 6;
     const int wmi = wave / WN, wni = wave % WN;
     const int l16 = lane & 15, lg = lane >> 4;
@@ -266,7 +274,7 @@ __device__ __forceinline__ void mfma32_tile(const GemmArgs& g, int tm, int tn) {
     const int mlim = M - m0, nlim = N - n0;
     const bool interior = mlim >= BM && nlim >= BN;  // uniform: no row/column masking needed
     float ra[LA][4], rb[LB][4];
-    auto load_tiles = [&](int kt) {
+    auto load_into = [&](float (&da)[LA][4], float (&db)[LB][4], int kt) {
         const int k0 = kt * BK;
         const float* Ak = Ablk + k0;
         const float* Bk = OPB == 0 ? Bblk + (size_t)k0 * g.ldb : Bblk + k0;
@@ -274,13 +282,13 @@ __device__ __forceinline__ void mfma32_tile(const GemmArgs& g, int tm, int tn) {
 #pragma unroll
             for (int p = 0; p < LA; ++p) {
                 const int idx = tid + NT * p, row = idx / KC, c = idx % KC;
-                load_chunk_full<float, 4, VEC>(ra[p], Ak + (row * lda + c * 4));
+                load_chunk_full<float, 4, VEC>(da[p], Ak + (row * lda + c * 4));
             }
 #pragma unroll
             for (int p = 0; p < LB; ++p) {
                 const int idx = tid + NT * p;
                 const int row = OPB == 0 ? idx / NC : idx / KC, c = OPB == 0 ? idx % NC : idx % KC;
-                load_chunk_full<float, 4, VEC>(rb[p], Bk + (row * ldb + c * 4));
+                load_chunk_full<float, 4, VEC>(db[p], Bk + (row * ldb + c * 4));
             }
             return;
         }
@@ -288,7 +296,7 @@ __device__ __forceinline__ void mfma32_tile(const GemmArgs& g, int tm, int tn) {
         for (int p = 0; p < LA; ++p) {
             const int idx = tid + NT * p, row = idx / KC, c = idx % KC;
             const int valid = row < mlim ? min(4, K - k0 - c * 4) : 0;
-            load_chunk<float, 4, VEC>(ra[p], Ak + (row * lda + c * 4), valid);
+            load_chunk<float, 4, VEC>(da[p], Ak + (row * lda + c * 4), valid);
         }
 #pragma unroll
         for (int p = 0; p < LB; ++p) {
@@ -296,14 +304,15 @@ __device__ __forceinline__ void mfma32_tile(const GemmArgs& g, int tm, int tn) {
             if (OPB == 0) {
                 const int row = idx / NC, c = idx % NC;
                 const int valid = k0 + row < K ? min(4, nlim - c * 4) : 0;
-                load_chunk<float, 4, VEC>(rb[p], Bk + (row * ldb + c * 4), valid);
+                load_chunk<float, 4, VEC>(db[p], Bk + (row * ldb + c * 4), valid);
             } else {
                 const int row = idx / KC, c = idx % KC;
                 const int valid = row < nlim ? min(4, K - k0 - c * 4) : 0;
-                load_chunk<float, 4, VEC>(rb[p], Bk + (row * ldb + c * 4), valid);
+                load_chunk<float, 4, VEC>(db[p], Bk + (row * ldb + c * 4), valid);
             }
         }
     };
+    auto load_tiles = [&](int kt) { load_into(ra, rb, kt); };
     auto store_tiles = [&](int buf) {
 #pragma unroll
         for (int p = 0; p < LA; ++p) {
@@ -379,17 +388,152 @@ __device__ __forceinline__ void mfma32_tile(const GemmArgs& g, int tm, int tn) {
             }
         }
     };
-    if (nkg > 0) {
-        load_tiles(kg);
-        store_tiles(0);
-    }
-    __syncthreads();
-    for (int lt = 0; lt < nl; ++lt) {
-        const int cur = lt & 1;
-        if (lt + 1 < nkg) load_tiles((lt + 1) * KG + kg);
-        if (lt < nkg) compute(cur);
-        if (lt + 1 < nkg) store_tiles(cur ^ 1);
+    if constexpr (ST == 3) {
+        // one half k-tile (16 k) of fragments: A as in compute(); B as four k-rows
+        // (row-major) or SN column subtiles (column-major)
+        struct Frag {
+            f32x4 a[SM];
+            f32x4 b[OPB == 0 ? 4 * QN : SN];
+        };
+        auto read_frag = [&](Frag& f, int buf, int kk) {
+#pragma unroll
+            for (int i = 0; i < SM; ++i) {
+                const int r = wmi * TWM + i * 16 + l16;
+                f.a[i] = *reinterpret_cast<const f32x4*>(&sA[buf][r * BK + ((((kk >> 2) + lg) ^ kmaj_swz(r)) << 2)]);
+            }
+            if (OPB == 0) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+#pragma unroll
+                    for (int q = 0; q < QN; ++q)
+                        f.b[s * QN + q] = *reinterpret_cast<const f32x4*>(
+                            &sB[buf][(kk + 4 * lg + s) * BN + wni * TWN + q * 64 + 4 * l16]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < SN; ++j) {
+                    const int r = wni * TWN + j * 16 + l16;
+                    f.b[j] = *reinterpret_cast<const f32x4*>(&sB[buf][r * BK + ((((kk >> 2) + lg) ^ kmaj_swz(r)) << 2)]);
+                }
+            }
+        };
+        // store chunk p (A's LA chunks, then B's LB) of the staged k-tile into stage buf
+        auto store_chunk = [&](const float (&da)[LA][4], const float (&db)[LB][4], int buf, int p) {
+            if (p < LA) {
+                const int idx = tid + NT * p, row = idx / KC, c = idx % KC;
+                *reinterpret_cast<f32x4*>(&sA[buf][row * BK + ((c ^ kmaj_swz(row)) << 2)]) =
+                    f32x4{da[p][0], da[p][1], da[p][2], da[p][3]};
+            } else {
+                const int q = p - LA, idx = tid + NT * q;
+                if (OPB == 0) {
+                    const int row = idx / NC, c = idx % NC;
+                    *reinterpret_cast<f32x4*>(&sB[buf][row * BN + (c << 2)]) =
+                        f32x4{db[q][0], db[q][1], db[q][2], db[q][3]};
+                } else {
+                    const int row = idx / KC, c = idx % KC;
+                    *reinterpret_cast<f32x4*>(&sB[buf][row * BK + ((c ^ kmaj_swz(row)) << 2)]) =
+                        f32x4{db[q][0], db[q][1], db[q][2], db[q][3]};
+                }
+            }
+        };
+        // the MFMAs of step s (one k of each lane's float4) of a half k-tile
+        auto mma_step = [&](const Frag& f, int s) {
+#pragma unroll
+            for (int i = 0; i < SM; ++i) {
+                if (OPB == 0) {
+#pragma unroll
+                    for (int q = 0; q < QN; ++q)
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            acc[i][4 * q + u] =
+                                __builtin_amdgcn_mfma_f32_16x16x4f32(f.b[s * QN + q][u], f.a[i][s], acc[i][4 * q + u], 0, 0, 0);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < SN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(f.b[j][s], f.a[i][s], acc[i][j], 0, 0, 0);
+                }
+            }
+        };
+        auto mma = [&](const Frag& f) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int i = 0; i < SM; ++i) {
+                    if (OPB == 0) {
+#pragma unroll
+                        for (int q = 0; q < QN; ++q)
+#pragma unroll
+                            for (int u = 0; u < 4; ++u)
+                                acc[i][4 * q + u] = __builtin_amdgcn_mfma_f32_16x16x4f32(f.b[s * QN + q][u], f.a[i][s],
+                                                                                         acc[i][4 * q + u], 0, 0, 0);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < SN; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(f.b[j][s], f.a[i][s], acc[i][j], 0, 0, 0);
+                    }
+                }
+        };
+        Frag f0, f1;
+        if (nk > 0) {
+            load_tiles(0);
+            store_tiles(0);
+        }
+        if (nk > 1) {
+            load_tiles(1);
+            store_tiles(1);
+        }
         __syncthreads();
+        if (nk > 0) read_frag(f0, 0, 0);
+        // accumulators in the accumulation registers (measured 0.6% faster than in
+        // the vector registers at 4096^3 and 8192^3)
+#pragma unroll
+        for (int i = 0; i < SM; ++i)
+#pragma unroll
+            for (int j = 0; j < SN; ++j) asm volatile("" : "+a"(acc[i][j]));
+        int cur = 0;  // lt % 3
+        for (int lt = 0; lt < nk; ++lt) {
+            const int nxt = cur == 2 ? 0 : cur + 1, far = nxt == 2 ? 0 : nxt + 1;
+            if (lt + 2 < nk) load_tiles(lt + 2);
+            read_frag(f1, cur, 16);
+            // the compiler would sink the reads below the MFMAs that should hide them
+            __builtin_amdgcn_sched_barrier(0);
+            mma(f0);
+            __builtin_amdgcn_sched_barrier(0);
+            // unconditional: after the last k-tile this reads a stage whose values go
+            // unused, and a branch here would make the compiler wait for these reads
+            // before the MFMAs below
+            read_frag(f0, nxt, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            // The LDS writes of tile t + 2 go between the MFMA steps of this half
+            // rather than all at once before the barrier. Stage `far` is free for the
+            // whole iteration; without a new tile (the last two iterations) the stale
+            // registers land in a stage that is never read again.
+            constexpr int NCH = LA + LB, PER = (NCH + 2) / 3;
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                mma_step(f1, st);
+                __builtin_amdgcn_sched_barrier(0);
+                if (st < 3) {
+#pragma unroll
+                    for (int p = st * PER; p < NCH && p < (st + 1) * PER; ++p) store_chunk(ra, rb, far, p);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            __syncthreads();
+            cur = nxt;
+        }
+    } else {
+        if (nkg > 0) {
+            load_tiles(kg);
+            store_tiles(0);
+        }
+        __syncthreads();
+        for (int lt = 0; lt < nl; ++lt) {
+            const int cur = lt & 1;
+            if (lt + 1 < nkg) load_tiles((lt + 1) * KG + kg);
+            if (lt < nkg) compute(cur);
+            if (lt + 1 < nkg) store_tiles(cur ^ 1);
+            __syncthreads();
+        }
     }
     if constexpr (KG == 2) {
         // group 1's accumulators through LDS (its own A stages, free after the last
@@ -437,12 +581,12 @@ __device__ __forceinline__ void mfma32_tile(const GemmArgs& g, int tm, int tn) {
     }
 }
 
-template <int OPB, bool VEC, int BM, int BN, int BK, int WM, int WN, int KG = 1>
+template <int OPB, bool VEC, int BM, int BN, int BK, int WM, int WN, int KG = 1, int ST = 2>
 __global__ __launch_bounds__(WM * WN * 64 * KG) void mfma32_gemm(GemmArgs g) {
     k_slice<4, OPB>(g);
     int tm, tn;
     tile_coords(g, tm, tn);
-    mfma32_tile<OPB, VEC, BM, BN, BK, WM, WN, KG>(g, tm, tn);
+    mfma32_tile<OPB, VEC, BM, BN, BK, WM, WN, KG, ST>(g, tm, tn);
 }
 
 template <int OPB, bool VEC, int BM, int BN, int BK, int WM, int WN>

@@ -24,7 +24,8 @@ enum Dtype { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
 //             pipelined 32x32x16 with direct copies, 4 waves of 128 x 128 or 8 of
 //             128 x 64 (2-5: full tiles
 //             only -- M, N multiples of bm, bn, K a multiple of bk, 16-byte aligned
-//             operands)
+//             operands), 6 = register-staged with three LDS stages and fragments
+//             read a half k-tile ahead (fp32, any shape)
 struct MenuEntry {
     int id, variant, dtype, opb, vec, bm, bn, bk, wm, wn, tm, tn, threads, lds_bytes, sched;
 };
@@ -37,6 +38,10 @@ struct MenuEntry {
 // Both are corrected in the kernel; it stays off until the corrected kernel has
 // passed its parity tests on the device.
 constexpr bool schedule_enabled(int sched) { return sched != 3; }
+
+// Schedules whose kernels copy whole tiles straight into LDS: M, N and K must be
+// whole tiles (or packed into them) and the operands 16-byte aligned.
+constexpr bool whole_tile(int sched) { return sched >= 2 && sched <= 5; }
 
 // Configurations whose kernel applies a fused epilogue (every other one stores the
 // plain fp32 accumulator only): all but the 32x32x16 ping-pong kernel and the
@@ -121,6 +126,11 @@ constexpr bool grouped_capable(int variant, int sched, int bm, int bn, int wm, i
     X(base + 2, V_MFMA, DT_F32, 0, 0, 64, 64, 32, 4, 1, 0, 0, 512, 2 * 2 * 4 * 32 * 128, 1)   \
     X(base + 3, V_MFMA, DT_F32, 1, 0, 64, 64, 32, 4, 1, 0, 0, 512, 2 * 2 * 4 * 32 * 128, 1)
 
+// fp32 256 x 128 tiles on the three-stage schedule (6): LDS holds three stages.
+#define DG_MFMA_F32S3(X, base)                                                           \
+    X(base + 0, V_MFMA, DT_F32, 0, 1, 256, 128, 32, 4, 2, 0, 0, 512, 3 * 4 * 32 * 384, 6)     \
+    X(base + 1, V_MFMA, DT_F32, 1, 1, 256, 128, 32, 4, 2, 0, 0, 512, 3 * 4 * 32 * 384, 6)
+
 #define DG_MENU(X)                                              \
     DG_LDS_ENTRIES(X, 0, DT_F32, 16)            \
     DG_LDS_ENTRIES(X, 8, DT_F16, 32)            \
@@ -138,9 +148,10 @@ constexpr bool grouped_capable(int variant, int sched, int bm, int bn, int wm, i
     DG_MFMA_PP32(X, 78, DT_BF16)                                 \
     DG_MFMA_SP(X, 80, DT_F16)                                    \
     DG_MFMA_SP(X, 84, DT_BF16)                                   \
-    DG_MFMA_KG2(X, 88)
+    DG_MFMA_KG2(X, 88)                                           \
+    DG_MFMA_F32S3(X, 92)
 
-constexpr int kMenuSize = 92;
+constexpr int kMenuSize = 94;
 
 // Fused epilogue ("Shared memory and tensor cores", section 13.10: bias,
 // activation, residual add or type cast applied to the accumulator before the

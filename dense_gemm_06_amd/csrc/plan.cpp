@@ -133,6 +133,10 @@ static double tile_efficiency_aligned(const MenuEntry& e) {
     if (e.sched == 4) return 0.96;
     if (e.sched == 3) return 0.85;
     if (e.sched == 5) return 0.90;  // problem-dependent: see plan()
+    // the fp32 three-stage 256 x 128 tile against the register-staged one, alternated
+    // in one run at 4096^3: 1027.5-1029.9 us against 1036.0-1038.4 (row-major B),
+    // 1021.4-1022.6 against 1046.7-1046.9 (column-major B); it does not split K
+    if (e.sched == 6) return 0.71;
     if (e.variant == V_LDS) return t >= 128 ? 0.6 : 0.35;
     // the fp32 64 x 64 tile with K split between two wave grids measured 7-9% faster
     // than with one (1024^3: 27.3-27.8 us against 29.6-29.8; 256^3: 8.4-8.6 against
@@ -219,7 +223,7 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
             set_error("threads = %d must be non-negative", want_threads);
             return GEMM_ERR_INVALID_VALUE;
         }
-        if (want_sched < 0 || want_sched > 5 || want_wm < 0 || want_wn < 0 || want_variant < 0 || want_variant > 2 || want_vec < -1 || want_vec > 1 || want_remap < -1 ||
+        if (want_sched < 0 || want_sched > 6 || want_wm < 0 || want_wn < 0 || want_variant < 0 || want_variant > 2 || want_vec < -1 || want_vec > 1 || want_remap < -1 ||
             want_remap > 1 || want_group < 0 || want_bm < 0 || want_bn < 0) {
             set_error("invalid requested configuration (variant %d, bm %d, bn %d, vec %d, xcd_remap %d, group_m %d)",
                       want_variant, want_bm, want_bn, want_vec, want_remap, want_group);
@@ -275,13 +279,13 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
         if (fused_epilogue && !epilogue_capable(e.sched)) continue;
         // the direct-copy kernels copy whole tiles: no masking of M, N or K edges on
         // the operands (the packed copies are whole tiles; C is masked at the store)
-        if (e.sched >= 2 && (Mx % e.bm != 0 || Nx % e.bn != 0 || Kx % e.bk != 0 || Kx == 0)) continue;
+        if (whole_tile(e.sched) && (Mx % e.bm != 0 || Nx % e.bn != 0 || Kx % e.bk != 0 || Kx == 0)) continue;
         if (want_wn && (e.variant == V_MFMA ? e.wn : 1) != want_wn) continue;
         const int vec = want_vec >= 0 ? want_vec : ((packed || vec_ok) ? 1 : 0);
         if (e.vec != vec) continue;
         if (e.vec && !packed && !vec_ok) continue;          // 16-byte loads need element-aligned bases
-        if (e.sched >= 2 && !packed && !dma_ok) continue;   // direct LDS copies need 16-byte alignment
-        const int64_t tiles = e.sched >= 2 ? (Mx / e.bm) * (Nx / e.bn) : ((M + e.bm - 1) / e.bm) * ((N + e.bn - 1) / e.bn);
+        if (whole_tile(e.sched) && !packed && !dma_ok) continue;   // direct LDS copies need 16-byte alignment
+        const int64_t tiles = whole_tile(e.sched) ? (Mx / e.bm) * (Nx / e.bn) : ((M + e.bm - 1) / e.bm) * ((N + e.bn - 1) / e.bn);
         const int64_t ktiles = (Kx + e.bk - 1) / e.bk;
         const int occ = blocks_per_cu(e);
         const int64_t concurrent = (int64_t)num_cus * occ;
@@ -366,8 +370,8 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
     cfg.lds_bytes = e.lds_bytes;
     cfg.kernel_id = e.id;
     cfg.schedule = e.sched;
-    cfg.tiles_m = ((best_packed && e.sched >= 2 ? Mp : M) + e.bm - 1) / e.bm;
-    cfg.tiles_n = ((best_packed && e.sched >= 2 ? Np : N) + e.bn - 1) / e.bn;
+    cfg.tiles_m = ((best_packed && whole_tile(e.sched) ? Mp : M) + e.bm - 1) / e.bm;
+    cfg.tiles_n = ((best_packed && whole_tile(e.sched) ? Np : N) + e.bn - 1) / e.bn;
     cfg.grid = (int32_t)(cfg.tiles_m * cfg.tiles_n);
     // Group enough tile rows that one XCD's share of the grid forms a compact
     // rectangle; the remap needs the grid to split evenly over the 8 XCDs.

@@ -95,7 +95,9 @@ typedef struct gemm_config {
                           pipelined 32x32x16 with direct global->LDS copies, 4 waves of 128 x
                           128 or 8 of 128 x 64 (2-5: MFMA, 16-bit inputs, M and N multiples of
                           256, K a multiple of 32, 16-byte aligned operands; 4 stores the
-                          plain fp32 accumulator only) */
+                          plain fp32 accumulator only); 6 register-staged with three LDS
+                          stages and fragments read half a k-tile ahead (fp32 256 x 128
+                          tiles, any shape, K not split) */
     int64_t tiles_m, tiles_n; /* out (grouped: of the first non-empty problem) */
     double est_cycles; /* out: the heuristic's cost estimate (clock cycles) */
     int64_t tiles_total; /* out: output tiles of the call (grouped: of all its problems) */

@@ -51,7 +51,7 @@ def test_status_strings():
 
 def test_menu_is_complete():
     menu = dg.gemm_menu()
-    assert len(menu) == dg.library().gemm_menu_size() == 92
+    assert len(menu) == dg.library().gemm_menu_size() == 94
     seen = set()
     for e in menu:
         assert e["lds_bytes"] <= 160 * 1024
@@ -68,7 +68,7 @@ def test_menu_is_complete():
                 for vec in (0, 1):
                     tiles = {(bm, bn) for (v, d, o, ve, bm, bn) in seen if (v, d, o, ve) == (variant, dtype, opb, vec)}
                     assert len(tiles) >= 2, (variant, dtype, opb, vec)
-    assert dg.library().gemm_menu_entry(92, None, None, None, None) == dg.GEMM_ERR_INVALID_VALUE
+    assert dg.library().gemm_menu_entry(94, None, None, None, None) == dg.GEMM_ERR_INVALID_VALUE
 
 
 def plan(M, N, K, dtype="f32", op_b="N", lda=None, ldb=None, ldc=None, a=0, b=0, c=0, cus=256, arch="gfx950",
@@ -123,8 +123,26 @@ def test_plan_ping_pong_eligibility():
     assert plan(4096, 4096, 4096 + 16, "f16")[1].schedule == 1
     assert plan(4096 + 8, 4096, 4096, "f16")[1].schedule == 1
     assert plan(4096, 4096, 4096, "f16", a=2)[1].schedule == 1
-    assert plan(4096, 4096, 4096, "f32")[1].schedule == 1
+    assert plan(4096, 4096, 4096, "f32")[1].schedule not in (2, 3, 4, 5)
     st, _ = plan(4000, 4096, 4096, "f16", req=dg.request(schedule=2))
+    assert st == dg.GEMM_ERR_UNSUPPORTED
+
+
+def test_plan_three_stage_fp32():
+    """Schedule 6 (fp32 256 x 128, three LDS stages) where the grid fills the machine,
+    either B layout, ragged shapes included; never for 16-bit inputs, never split."""
+    for op_b in "NT":
+        for shape in ((4096, 4096, 4096), (8192, 8192, 8192), (4000, 4096, 3001)):
+            st, c = plan(*shape, "f32", op_b)
+            assert st == 0 and c.schedule == 6 and (c.bm, c.bn) == (256, 128) and c.threads == 512, (shape, op_b)
+    # few tiles: the register-staged kernels, which may split K with a workspace
+    assert plan(1024, 1024, 1024, "f32")[1].schedule == 1
+    st, c = wplan(512, 512, 8192, "f32")
+    assert st == 0 and c.schedule == 1 and c.split_k > 1
+    # forced, with a K split: refused (schedule 6 has no sliced form)
+    st, _ = wplan(4096, 4096, 4096, "f32", req=dg.request(schedule=6, split_k=2), check=False)
+    assert st != 0
+    st, _ = plan(4096, 4096, 4096, "f16", req=dg.request(schedule=6))
     assert st == dg.GEMM_ERR_UNSUPPORTED
 
 

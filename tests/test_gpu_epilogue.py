@@ -157,6 +157,16 @@ def test_epilogue_whole_tile_kernels(schedule, waves_n, dtype, op_b, out):
     assert epilogue_error(got, ref, Dp, dtype, out) <= 1.0
 
 
+@pytest.mark.parametrize("op_b", ["N", "T"])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_epilogue_three_stage_fp32(op_b, out):
+    """The fp32 three-stage schedule with a fused epilogue, ragged tiles."""
+    ops = gi.make_operands(300, 200, 150, "f32", "normal", seed=9, op_b=op_b)
+    got, ref, Dp, plan = run_epi(ops, out, act="gelu_tanh", cfg=dg.request(schedule=6))
+    assert plan.schedule == 6
+    assert epilogue_error(got, ref, Dp, "f32", out) <= 1.0
+
+
 @pytest.mark.parametrize("out", ["f32", "f16", "bf16"])
 def test_epilogue_in_place(out):
     """R == C: the BLAS form C = alpha A B + beta C."""

@@ -35,7 +35,7 @@ def _lib_built():
 MENU = _menu()
 MENU_IDS = [f"k{e['kernel_id']}-{'lds' if e['variant'] == 1 else 'mfma'}-{DT_NAME[e['dtype']]}-"
             f"op{'NT'[e['opb']]}-{'v16' if e['vec'] else 'v1'}-{e['bm']}x{e['bn']}-w{e['waves_m']}x{e['waves_n']}"
-            f"{ {1: '', 2: '-pp', 3: '-dma', 4: '-pp32', 5: '-sp'}[e['schedule']] }"
+            f"{ {1: '', 2: '-pp', 3: '-dma', 4: '-pp32', 5: '-sp', 6: '-s3'}[e['schedule']] }"
             for e in MENU]
 
 
@@ -52,6 +52,9 @@ def menu_params():
             else pytest.param(e, id=i) for e, i in zip(MENU, MENU_IDS)]
 
 
+WHOLE_TILE = (2, 3, 4, 5)   # schedules that copy whole tiles straight into LDS
+
+
 def forced(e):
     return dg.request(variant=e["variant"], bm=e["bm"], bn=e["bn"], vec=e["vec"], waves_m=e["waves_m"],
                       waves_n=e["waves_n"], threads=e["threads"], schedule=e["schedule"])
@@ -62,7 +65,7 @@ def ragged_shape(e):
 
     Ping-pong kernels take only whole tiles: 2 x 3 tiles and 9 k-tiles (an odd
     count, so both LDS-stage parities and the prefetch tail are exercised)."""
-    if e["schedule"] >= 2:
+    if e["schedule"] in WHOLE_TILE:
         return 2 * e["bm"], 3 * e["bn"], 9 * e["bk"]
     return 2 * e["bm"] + 37, 2 * e["bn"] + 19, 3 * e["bk"] + 13
 
@@ -115,6 +118,20 @@ def test_full_tile_kernels_k_tile_counts(schedule, waves_n, k_tiles, dtype, op_b
     check_untouched(C, ops.M, ops.N)
     Cref, D = oracle.gemm_ref(ops)
     assert normalized_error(C[:ops.M, :ops.N], Cref, D) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("k_tiles", [1, 2, 3, 4, 5, 7, 130])
+@pytest.mark.parametrize("op_b", ["N", "T"])
+def test_three_stage_fp32_k_tile_counts(k_tiles, op_b):
+    """Prologue (one or two k-tiles), steady state and tail of the fp32 three-stage
+    schedule, with a ragged last k-tile for odd counts, on ragged M and N."""
+    K = 32 * k_tiles - (13 if k_tiles % 2 else 0)
+    ops = gi.make_operands(300, 200, K, "f32", "normal", seed=k_tiles, op_b=op_b)
+    print(f"case three-stage fp32 K={K} op {op_b}", flush=True)
+    C = run_ops(ops, cfg=dg.request(schedule=6), ldc=ops.N + 4)
+    check_untouched(C, ops.M, ops.N)
+    Cref, D = oracle.gemm_ref(ops)
+    assert normalized_error(C[:ops.M, :ops.N], Cref, D) <= TOL["f32"]
 
 
 @pytest.mark.parametrize("e", menu_params())
