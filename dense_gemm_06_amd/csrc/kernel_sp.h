@@ -92,18 +92,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     // ---- direct copies: wave w moves blocks CPB*w .. CPB*w+CPB-1 (1 KB each) of the A
     // tile and of the B tile. Lane L of block b lands at LDS byte b*1024 + 16L, a fixed
     // swizzled position, and loads the logical 16-byte chunk that belongs there.
+    // Edge tiles (M or N not a multiple of 256): rows of A, and of a column-major B,
+    // at or beyond M (N) copy row M - 1 (N - 1) instead, and 16-byte column chunks of
+    // a row-major B that start at or beyond N copy columns 0..7 (N is then a multiple
+    // of 8, so no chunk straddles N); what they bring in only reaches rows and
+    // columns of C that the epilogue does not store.
     const uint16_t* srcA[CPB];
     const uint16_t* srcB[CPB];
 #pragma unroll
     for (int i = 0; i < CPB; ++i) {
         const int b = wave * CPB + i;
         const int row = b * 16 + (lane >> 2);
-        srcA[i] = A + (size_t)(m0 + row) * g.lda + (((lane & 3) ^ kmaj32_swz(row)) << 3);
+        srcA[i] = A + (size_t)min(m0 + row, g.M - 1) * g.lda + (((lane & 3) ^ kmaj32_swz(row)) << 3);
         if (OPB == 1) {
-            srcB[i] = B + (size_t)(n0 + row) * g.ldb + (((lane & 3) ^ kmaj32_swz(row)) << 3);
+            srcB[i] = B + (size_t)min(n0 + row, g.N - 1) * g.ldb + (((lane & 3) ^ kmaj32_swz(row)) << 3);
         } else {
             const int krow = b * 2 + (lane >> 5);
-            srcB[i] = B + (size_t)krow * g.ldb + n0 + (((lane & 31) ^ nmaj32_swz(krow)) << 3);
+            const int col = n0 + (((lane & 31) ^ nmaj32_swz(krow)) << 3);
+            srcB[i] = B + (size_t)krow * g.ldb + (col < g.N ? col : 0);
         }
     }
     const size_t kstepB = OPB == 0 ? (size_t)BK * g.ldb : (size_t)BK;  // elements per k-tile

@@ -278,14 +278,21 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
         if (!schedule_enabled(e.sched)) continue;
         if (fused_epilogue && !epilogue_capable(e.sched)) continue;
         // the direct-copy kernels copy whole tiles: no masking of M, N or K edges on
-        // the operands (the packed copies are whole tiles; C is masked at the store)
-        if (whole_tile(e.sched) && (Mx % e.bm != 0 || Nx % e.bn != 0 || Kx % e.bk != 0 || Kx == 0)) continue;
+        // the operands (the packed copies are whole tiles; C is masked at the store).
+        // The software-pipelined kernel also takes edge tiles in M and N, copying
+        // clamped rows and columns (row-major B: N a multiple of 8, so that no 16-byte
+        // chunk reaches past the end of a row).
+        if (whole_tile(e.sched) && (Kx % e.bk != 0 || Kx == 0)) continue;
+        if (whole_tile(e.sched) && (Mx % e.bm != 0 || Nx % e.bn != 0) &&
+            !(e.sched == 5 && (e.opb == 1 || Nx % 8 == 0)))
+            continue;
         if (want_wn && (e.variant == V_MFMA ? e.wn : 1) != want_wn) continue;
         const int vec = want_vec >= 0 ? want_vec : ((packed || vec_ok) ? 1 : 0);
         if (e.vec != vec) continue;
         if (e.vec && !packed && !vec_ok) continue;          // 16-byte loads need element-aligned bases
         if (whole_tile(e.sched) && !packed && !dma_ok) continue;   // direct LDS copies need 16-byte alignment
-        const int64_t tiles = whole_tile(e.sched) ? (Mx / e.bm) * (Nx / e.bn) : ((M + e.bm - 1) / e.bm) * ((N + e.bn - 1) / e.bn);
+        const int64_t tiles = whole_tile(e.sched) ? ((Mx + e.bm - 1) / e.bm) * ((Nx + e.bn - 1) / e.bn)
+                                                  : ((M + e.bm - 1) / e.bm) * ((N + e.bn - 1) / e.bn);
         const int64_t ktiles = (Kx + e.bk - 1) / e.bk;
         const int occ = blocks_per_cu(e);
         const int64_t concurrent = (int64_t)num_cus * occ;

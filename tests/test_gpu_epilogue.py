@@ -157,6 +157,16 @@ def test_epilogue_whole_tile_kernels(schedule, waves_n, dtype, op_b, out):
     assert epilogue_error(got, ref, Dp, dtype, out) <= 1.0
 
 
+@pytest.mark.parametrize("waves_n", [2, 4])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_epilogue_software_pipelined_edge_tiles(waves_n, out):
+    """The staged epilogue of schedule 5 on edge tiles (M, N not multiples of 256)."""
+    ops = gi.make_operands(300, 264, 96, "f16", "normal", seed=10)
+    got, ref, Dp, plan = run_epi(ops, out, act="gelu_tanh", cfg=dg.request(schedule=5, waves_n=waves_n))
+    assert plan.schedule == 5
+    assert epilogue_error(got, ref, Dp, "f16", out) <= 1.0
+
+
 @pytest.mark.parametrize("op_b", ["N", "T"])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_epilogue_three_stage_fp32(op_b, out):

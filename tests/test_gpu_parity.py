@@ -120,6 +120,27 @@ def test_full_tile_kernels_k_tile_counts(schedule, waves_n, k_tiles, dtype, op_b
     assert normalized_error(C[:ops.M, :ops.N], Cref, D) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("waves_n", [2, 4])
+@pytest.mark.parametrize("shape,op_b", [((300, 264, 64), "N"), ((513, 777, 96), "T"), ((257, 512, 4160), "N"),
+                                        ((40, 8, 32), "N"), ((600, 1, 128), "T"), ((256, 300, 32 * 130), "T")])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_software_pipelined_edge_tiles(waves_n, shape, op_b, dtype):
+    """Schedule 5 on M and N that are not multiples of 256 (row-major B: N a multiple
+    of 8), with copies of clamped rows and columns in the edge tiles; K a multiple of
+    32 from one k-tile to 130."""
+    M, N, K = shape
+    ops = gi.make_operands(M, N, K, dtype, "normal", seed=M + N + K, op_b=op_b)
+    print(f"case sp edge tiles {shape} {dtype} op {op_b} waves_n {waves_n}", flush=True)
+    req = dg.request(schedule=5, waves_n=waves_n)
+    st, plan = dg.gemm_plan(0, dg.OP_CODE[op_b], M, N, K, ops.lda, ops.ldb, N + 3, dg.DTYPE_CODE[dtype],
+                            1 << 30, 1 << 40, 1 << 41, 256, "gfx950", req)
+    assert plan.schedule == 5 and plan.tiles_m == -(-M // 256) and plan.tiles_n == -(-N // 256)
+    C = run_ops(ops, cfg=req, ldc=N + 3)
+    check_untouched(C, M, N)
+    Cref, D = oracle.gemm_ref(ops)
+    assert normalized_error(C[:M, :N], Cref, D) <= TOL[dtype]
+
+
 @pytest.mark.parametrize("k_tiles", [1, 2, 3, 4, 5, 7, 130])
 @pytest.mark.parametrize("op_b", ["N", "T"])
 def test_three_stage_fp32_k_tile_counts(k_tiles, op_b):
