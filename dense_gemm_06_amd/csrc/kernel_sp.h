@@ -32,8 +32,9 @@ __device__ __forceinline__ void vm_wait(int n) {
     }
 }
 
-// Software-pipelined MFMA kernel for 16-bit inputs on full 256 x 256 tiles (M and
-// N multiples of 256, K a multiple of 32, 16-byte aligned operands).
+// Software-pipelined MFMA kernel for 16-bit inputs on 256 x 256 tiles (K a multiple
+// of 8, 16-byte aligned operands; edge tiles in M, and in N for column-major B or for
+// N a multiple of 8, and a partial last k-tile, are handled as described below).
 //
 // NW = 4: four waves, one per SIMD, each owning a 128 x 128 quarter of the tile with
 // its 16 v_mfma_f32_32x32x16 accumulators (256 registers) in the accumulation
@@ -85,7 +86,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     int tm, tn;
     tile_coords(g, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const int nk = g.K / BK;
+    // K a multiple of 8: the last k-tile may be partial (krem of its 32 k valid); its
+    // copies clamp the chunks at or beyond K and the LDS chunks past K are zeroed
+    // before any fragment of that tile is read
+    const int nk = (g.K + BK - 1) / BK;
+    const int krem = g.K - (nk - 1) * BK;
+    const bool ktail = krem < BK;
     const uint16_t* __restrict__ A = static_cast<const uint16_t*>(g.A);
     const uint16_t* __restrict__ B = static_cast<const uint16_t*>(g.B);
 
@@ -97,18 +103,25 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     // a row-major B that start at or beyond N copy columns 0..7 (N is then a multiple
     // of 8, so no chunk straddles N); what they bring in only reaches rows and
     // columns of C that the epilogue does not store.
+    // kcA / kcB: the k offset of a lane's chunk within the k-tile (k-major copies);
+    // krB: the k row of a lane's chunk (row-major B). A lane whose chunk of the last
+    // tile starts at or beyond K copies the chunk at k = 0 of its row instead.
     const uint16_t* srcA[CPB];
     const uint16_t* srcB[CPB];
+    int kcA[CPB], kcB[CPB];
 #pragma unroll
     for (int i = 0; i < CPB; ++i) {
         const int b = wave * CPB + i;
         const int row = b * 16 + (lane >> 2);
-        srcA[i] = A + (size_t)min(m0 + row, g.M - 1) * g.lda + (((lane & 3) ^ kmaj32_swz(row)) << 3);
+        kcA[i] = ((lane & 3) ^ kmaj32_swz(row)) << 3;
+        srcA[i] = A + (size_t)min(m0 + row, g.M - 1) * g.lda + kcA[i];
         if (OPB == 1) {
-            srcB[i] = B + (size_t)min(n0 + row, g.N - 1) * g.ldb + (((lane & 3) ^ kmaj32_swz(row)) << 3);
+            kcB[i] = kcA[i];
+            srcB[i] = B + (size_t)min(n0 + row, g.N - 1) * g.ldb + kcB[i];
         } else {
             const int krow = b * 2 + (lane >> 5);
             const int col = n0 + (((lane & 31) ^ nmaj32_swz(krow)) << 3);
+            kcB[i] = krow;
             srcB[i] = B + (size_t)krow * g.ldb + (col < g.N ? col : 0);
         }
     }
@@ -120,13 +133,41 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     const uint32_t wave_u = (uint32_t)__builtin_amdgcn_readfirstlane(wave);
     const uint32_t dstA = (uint32_t)reinterpret_cast<uintptr_t>(DG_LDSV(&sA[0][0])) + wave_u * (CPB * 1024u);
     const uint32_t dstB = (uint32_t)reinterpret_cast<uintptr_t>(DG_LDSV(&sB[0][0])) + wave_u * (CPB * 1024u);
-    auto copy_a = [&](int t, int i) {
-        __builtin_amdgcn_global_load_lds(DG_GLB(srcA[i] + (size_t)t * BK),
-                                         DG_LDS_AT(dstA + (uint32_t)(t & 3) * STAGE_BYTES + i * 1024u), 16, 0, 0);
+    // TAIL: t is the partial last k-tile
+    auto copy_a = [&](int t, int i, auto tail_tag) {
+        const uint16_t* src = srcA[i] + (size_t)t * BK;
+        if (decltype(tail_tag)::value && kcA[i] >= krem) src = srcA[i] - kcA[i];
+        __builtin_amdgcn_global_load_lds(DG_GLB(src), DG_LDS_AT(dstA + (uint32_t)(t & 3) * STAGE_BYTES + i * 1024u),
+                                         16, 0, 0);
     };
-    auto copy_b = [&](int t, int i) {
-        __builtin_amdgcn_global_load_lds(DG_GLB(srcB[i] + (size_t)t * kstepB),
-                                         DG_LDS_AT(dstB + (uint32_t)(t & 3) * STAGE_BYTES + i * 1024u), 16, 0, 0);
+    auto copy_b = [&](int t, int i, auto tail_tag) {
+        const uint16_t* src = srcB[i] + (size_t)t * kstepB;
+        if (decltype(tail_tag)::value && kcB[i] >= krem)
+            src = OPB == 1 ? srcB[i] - kcB[i] : srcB[i] - (size_t)kcB[i] * g.ldb;
+        __builtin_amdgcn_global_load_lds(DG_GLB(src), DG_LDS_AT(dstB + (uint32_t)(t & 3) * STAGE_BYTES + i * 1024u),
+                                         16, 0, 0);
+    };
+    // Zero the chunks of stage st that lie at or beyond K (the partial last tile), then
+    // wait for this wave's writes; the caller's barrier publishes them.
+    auto zero_tail = [&](int st) {
+        char* sa = reinterpret_cast<char*>(&sA[st][0]);
+        char* sb = reinterpret_cast<char*>(&sB[st][0]);
+        for (int idx = tid; idx < BM * 4; idx += NW * 64) {
+            const int r = idx >> 2, c = idx & 3;
+            if (c * 8 >= krem) *reinterpret_cast<u32x4*>(sa + r * 64 + ((c ^ kmaj32_swz(r)) << 4)) = u32x4{0, 0, 0, 0};
+        }
+        if (OPB == 1) {
+            for (int idx = tid; idx < BN * 4; idx += NW * 64) {
+                const int r = idx >> 2, c = idx & 3;
+                if (c * 8 >= krem)
+                    *reinterpret_cast<u32x4*>(sb + r * 64 + ((c ^ kmaj32_swz(r)) << 4)) = u32x4{0, 0, 0, 0};
+            }
+        } else {
+            // k rows krem .. 31 of 512 bytes each (the swizzle only permutes chunks within a row)
+            for (int idx = krem * 32 + tid; idx < BK * 32; idx += NW * 64)
+                *reinterpret_cast<u32x4*>(sb + idx * 16) = u32x4{0, 0, 0, 0};
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     };
 
     // ---- fragment addresses (bytes within a stage).
@@ -212,7 +253,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     // CPB copies of tile `ct` (half `half`: 0 = A, 1 = B) after every other MFMA of the
     // second half of the step.
     constexpr int NM = 4 * SJ;  // MFMAs per step
-    auto step = [&](const Frags& cur, Frags& nxt, int rst, int rks, bool do_copy, int ct, int half) {
+    auto step = [&](const Frags& cur, Frags& nxt, int rst, int rks, bool do_copy, int ct, int half, auto tail_tag) {
 #pragma unroll
         for (int k = 0; k < NM; ++k) {
             mfma(cur, k / SJ, k % SJ);
@@ -220,8 +261,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
             if (2 * k + 1 < NREAD) read_one(nxt, rst, rks, 2 * k + 1);
             const int c = (k - NM / 2) >> 1;
             if (do_copy && k >= NM / 2 && (k & 1) == 0 && c < CPB) {
-                if (half == 0) copy_a(ct, c);
-                else copy_b(ct, c);
+                if (half == 0) copy_a(ct, c, tail_tag);
+                else copy_b(ct, c, tail_tag);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -230,41 +271,67 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     // prologue: tiles 0 .. D-1 in flight (A then B of each); tile 0 complete; step
     // (0, 0) fragments read.
     for (int t = 0; t < D && t < nk; ++t) {
+        if (ktail && t == nk - 1) {
 #pragma unroll
-        for (int i = 0; i < CPB; ++i) copy_a(t, i);
+            for (int i = 0; i < CPB; ++i) copy_a(t, i, std::true_type{});
 #pragma unroll
-        for (int i = 0; i < CPB; ++i) copy_b(t, i);
+            for (int i = 0; i < CPB; ++i) copy_b(t, i, std::true_type{});
+        } else {
+#pragma unroll
+            for (int i = 0; i < CPB; ++i) copy_a(t, i, std::false_type{});
+#pragma unroll
+            for (int i = 0; i < CPB; ++i) copy_b(t, i, std::false_type{});
+        }
     }
     vm_wait(2 * CPB * (min(D, nk) - 1));
     asm volatile("s_barrier" ::: "memory");
+    if (ktail && nk == 1) {
+        zero_tail(0);
+        asm volatile("s_barrier" ::: "memory");
+    }
 #pragma unroll
     for (int r = 0; r < NREAD; ++r) read_one(f0, 0, 0, r);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     settle(f0);
 
-    // One iteration (tile t). REFILL: tile t+D exists and is copied. The reads of step
-    // (t+1, 0) in the last iteration fetch a stage nobody writes any more; their values
-    // are never used (this keeps the step free of branches).
-    auto iteration = [&](int t, auto refill_tag) {
+    // One iteration (tile t). REFILL: tile t+D exists and is copied (TAIL: it is the
+    // partial last tile). FIX: tile t+1 is the partial last tile, whose chunks past K
+    // are zeroed between the barrier that completes its copies and the first reads of
+    // it. The reads of step (t+1, 0) in the last iteration fetch a stage nobody writes
+    // any more; their values are never used (this keeps the step free of branches).
+    auto iteration = [&](int t, auto refill_tag, auto tail_tag, auto fix_tag) {
         constexpr bool REFILL = decltype(refill_tag)::value;
         const int st = t & 3;
         // step (t, 0): MFMAs from f0; read step (t, 1) into f1; copy A of tile t+D
-        step(f0, f1, st, 1, REFILL, t + D, 0);
+        step(f0, f1, st, 1, REFILL, t + D, 0, tail_tag);
         // own reads done; own copies of tile t+1 done (those of tiles t+2 .. t+D-1 and
         // the A half of tile t+D may still be in flight); then the barrier
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (REFILL) vm_wait_n<2 * CPB * (D - 2) + CPB>();
         else vm_wait(2 * CPB * max(0, nk - t - 2));
         asm volatile("s_barrier" ::: "memory");
+        if (decltype(fix_tag)::value) {
+            zero_tail((t + 1) & 3);
+            asm volatile("s_barrier" ::: "memory");
+        }
         settle(f1);
         // step (t, 1): MFMAs from f1; read step (t+1, 0) into f0; copy B of tile t+D
-        step(f1, f0, (t + 1) & 3, 0, REFILL, t + D, 1);
+        step(f1, f0, (t + 1) & 3, 0, REFILL, t + D, 1, tail_tag);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         settle(f0);
     };
+    constexpr std::true_type yes{};
+    constexpr std::false_type no{};
+    // straight runs of one variant each (a branch between two inlined variants inside
+    // a loop leaves the register allocator unable to keep the fragments in registers)
+    const int nfull = ktail ? nk - 1 : nk;  // tiles t + D copied by the plain variant
     int t = 0;
-    for (; t + D < nk; ++t) iteration(t, std::true_type{});
-    for (; t < nk; ++t) iteration(t, std::false_type{});
+    for (; t + D < nfull; ++t) iteration(t, yes, no, no);
+    for (; ktail && t + D == nk - 1; ++t) iteration(t, yes, yes, no);  // copies the partial tile
+    const int nfix = ktail ? nk - 2 : nk;   // the iteration before the partial tile
+    for (; t < nfix; ++t) iteration(t, no, no, no);
+    for (; ktail && t == nk - 2; ++t) iteration(t, no, no, yes);
+    for (; t < nk; ++t) iteration(t, no, no, no);
 
     // ---- epilogue through LDS. Every wave's last reads are done (lgkmcnt(0) above);
     // the barrier makes sure all of them are before any wave overwrites a stage. The

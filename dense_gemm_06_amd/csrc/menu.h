@@ -22,8 +22,8 @@ enum Dtype { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
 //             direct global->LDS copies on 16x16x32 MFMAs, 3 = software-pipelined
 //             with direct copies, 4 = ping-pong on 32x32x16 MFMAs, 5 = software-
 //             pipelined 32x32x16 with direct copies, 4 waves of 128 x 128 or 8 of
-//             128 x 64 (2-5: K a multiple of bk and 16-byte aligned operands;
-//             2-4: M, N multiples of bm, bn; 5: edge tiles in M, and in N for
+//             128 x 64 (2-5: 16-byte aligned operands; 2-4: M, N, K multiples of
+//             bm, bn, bk; 5: K a multiple of 8, edge tiles in M, and in N for
 //             column-major B or N a multiple of 8), 6 = register-staged with three LDS stages and fragments
 //             read a half k-tile ahead (fp32, any shape)
 struct MenuEntry {
@@ -39,9 +39,9 @@ struct MenuEntry {
 // passed its parity tests on the device.
 constexpr bool schedule_enabled(int sched) { return sched != 3; }
 
-// Schedules whose kernels copy whole tiles straight into LDS: K must be whole
-// k-tiles and the operands 16-byte aligned; M and N whole tiles too, except for
-// schedule 5, which clamps the copies of its edge tiles.
+// Schedules whose kernels copy whole tiles straight into LDS: the operands must be
+// 16-byte aligned and M, N, K whole tiles, except for schedule 5, which clamps the
+// copies of its edge tiles and zeroes a partial last k-tile past K.
 constexpr bool whole_tile(int sched) { return sched >= 2 && sched <= 5; }
 
 // Configurations whose kernel applies a fused epilogue (every other one stores the

@@ -121,7 +121,10 @@ def test_plan_ping_pong_eligibility():
     tiles in M and N go to the software-pipelined kernel)."""
     assert plan(4096, 4096, 4096, "bf16")[1].schedule >= 2
     assert plan(4096, 4096, 4096, "f16", "T")[1].schedule >= 2
-    assert plan(4096, 4096, 4096 + 16, "f16")[1].schedule == 1
+    assert plan(4096, 4096, 4096 + 16, "f16")[1].schedule == 5   # the software-pipelined kernel's K tail
+    for sched in (2, 4):
+        st, _ = plan(4096, 4096, 4096 + 16, "f16", req=dg.request(schedule=sched))
+        assert st == dg.GEMM_ERR_UNSUPPORTED
     assert plan(4096 + 8, 4096, 4096, "f16")[1].schedule == 5
     for sched in (2, 4):
         st, _ = plan(4096 + 8, 4096, 4096, "f16", req=dg.request(schedule=sched))
@@ -144,7 +147,9 @@ def test_plan_software_pipelined_edge_tiles():
     assert st == dg.GEMM_ERR_UNSUPPORTED
     st, c = plan(4000, 4001, 4096, "f16", "T")
     assert st == 0 and c.schedule == 5
-    assert plan(4000, 4000, 4000 + 8, "f16")[1].schedule == 1   # K not a multiple of 32
+    assert plan(4000, 4000, 4000 + 8, "f16")[1].schedule == 5   # a partial last k-tile
+    st, c = plan(4000, 4000, 4004, "f16", lda=4008)             # K not a multiple of 8
+    assert st == 0 and c.schedule == 1
     assert plan(4000, 4000, 4000, "f16", lda=4004)[1].schedule == 1   # rows not 16-byte aligned
 
 

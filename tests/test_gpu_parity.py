@@ -122,12 +122,16 @@ def test_full_tile_kernels_k_tile_counts(schedule, waves_n, k_tiles, dtype, op_b
 
 @pytest.mark.parametrize("waves_n", [2, 4])
 @pytest.mark.parametrize("shape,op_b", [((300, 264, 64), "N"), ((513, 777, 96), "T"), ((257, 512, 4160), "N"),
-                                        ((40, 8, 32), "N"), ((600, 1, 128), "T"), ((256, 300, 32 * 130), "T")])
+                                        ((40, 8, 32), "N"), ((600, 1, 128), "T"), ((256, 300, 32 * 130), "T"),
+                                        ((300, 264, 40), "N"), ((513, 777, 1000), "T"), ((40, 8, 8), "N"),
+                                        ((256, 256, 24), "T"), ((257, 512, 4168), "N"), ((512, 256, 56), "T"),
+                                        ((256, 512, 80), "N"), ((300, 300, 16), "T")])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_software_pipelined_edge_tiles(waves_n, shape, op_b, dtype):
     """Schedule 5 on M and N that are not multiples of 256 (row-major B: N a multiple
-    of 8), with copies of clamped rows and columns in the edge tiles; K a multiple of
-    32 from one k-tile to 130."""
+    of 8), with copies of clamped rows and columns in the edge tiles, and on K that is
+    a multiple of 8 but not of 32: the partial last k-tile (1 to 131 k-tiles, so that
+    it falls in the prologue, in the last refill and after it) is zeroed past K."""
     M, N, K = shape
     ops = gi.make_operands(M, N, K, dtype, "normal", seed=M + N + K, op_b=op_b)
     print(f"case sp edge tiles {shape} {dtype} op {op_b} waves_n {waves_n}", flush=True)
