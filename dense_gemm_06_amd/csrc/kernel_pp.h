@@ -6,8 +6,9 @@
 
 namespace dg {
 
-// Ping-pong MFMA kernel for 16-bit inputs on full 256 x 256 tiles (M and N
-// multiples of 256, K a multiple of 32, 16-byte aligned operands).
+// Ping-pong MFMA kernel for 16-bit inputs on 256 x 256 tiles (K a multiple of 32,
+// 16-byte aligned operands; edge tiles in M, and in N for column-major B or for N a
+// multiple of 8, copy clamped rows and columns).
 //
 // The register-staged kernel runs every wave through the same sequence (load,
 // wait, MFMA, store, barrier), so the matrix unit idles whenever all waves wait
@@ -55,7 +56,10 @@ __global__ __launch_bounds__(512) void mfma16_pp(GemmArgs g) {
 
     // Direct copies: each wave issues 4 copies of 1 KB (64 lanes x 16 B) per tile.
     // Lane L of block b lands at LDS byte b*1024 + 16L, i.e. at a fixed swizzled
-    // position; it loads the logical chunk that belongs there.
+    // position; it loads the logical chunk that belongs there. Edge tiles (M or N not
+    // a multiple of 256): rows at or beyond M (N) copy row M - 1 (N - 1), and column
+    // chunks of a row-major B at or beyond N copy columns 0..7 (N is then a multiple
+    // of 8); the masked epilogue never stores what they produce.
     const uint16_t* src[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -63,11 +67,13 @@ __global__ __launch_bounds__(512) void mfma16_pp(GemmArgs g) {
         if (grp == 0 || OPB == 1) {
             const int row = b * 16 + (lane >> 2);
             const int c = (lane & 3) ^ kswz(row);
-            src[i] = grp == 0 ? A + (size_t)(m0 + row) * g.lda + c * 8 : B + (size_t)(n0 + row) * g.ldb + c * 8;
+            src[i] = grp == 0 ? A + (size_t)min(m0 + row, g.M - 1) * g.lda + c * 8
+                              : B + (size_t)min(n0 + row, g.N - 1) * g.ldb + c * 8;
         } else {
             const int row = b * 2 + (lane >> 5);
             const int c = (lane & 31) ^ nswz(row);
-            src[i] = B + (size_t)row * g.ldb + n0 + c * 8;
+            const int col = n0 + c * 8;
+            src[i] = B + (size_t)row * g.ldb + (col < g.N ? col : 0);
         }
     }
     const size_t kstep = (grp == 1 && OPB == 0) ? (size_t)BK * g.ldb : (size_t)BK;  // elements per k-tile

@@ -22,9 +22,9 @@ enum Dtype { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
 //             direct global->LDS copies on 16x16x32 MFMAs, 3 = software-pipelined
 //             with direct copies, 4 = ping-pong on 32x32x16 MFMAs, 5 = software-
 //             pipelined 32x32x16 with direct copies, 4 waves of 128 x 128 or 8 of
-//             128 x 64 (2-5: 16-byte aligned operands; 2-4: M, N, K multiples of
-//             bm, bn, bk; 5: K a multiple of 8, edge tiles in M, and in N for
-//             column-major B or N a multiple of 8), 6 = register-staged with three LDS stages and fragments
+//             128 x 64 (2-5: 16-byte aligned operands, edge tiles in M, and in N
+//             for column-major B or N a multiple of 8; 2-4: K a multiple of bk;
+//             5: K a multiple of 8), 6 = register-staged with three LDS stages and fragments
 //             read a half k-tile ahead (fp32, any shape)
 struct MenuEntry {
     int id, variant, dtype, opb, vec, bm, bn, bk, wm, wn, tm, tn, threads, lds_bytes, sched;
@@ -39,9 +39,10 @@ struct MenuEntry {
 // passed its parity tests on the device.
 constexpr bool schedule_enabled(int sched) { return sched != 3; }
 
-// Schedules whose kernels copy whole tiles straight into LDS: the operands must be
-// 16-byte aligned and M, N, K whole tiles, except for schedule 5, which clamps the
-// copies of its edge tiles and zeroes a partial last k-tile past K.
+// Schedules whose kernels copy tiles straight into LDS: the operands must be 16-byte
+// aligned and K whole k-tiles (schedule 5: K a multiple of 8, a partial last k-tile
+// zeroed past K); edge tiles in M and N copy clamped rows and columns (schedule 3,
+// switched off: whole tiles only).
 constexpr bool whole_tile(int sched) { return sched >= 2 && sched <= 5; }
 
 // Configurations whose kernel applies a fused epilogue (every other one stores the

@@ -279,13 +279,13 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
         if (fused_epilogue && !epilogue_capable(e.sched)) continue;
         // the direct-copy kernels copy whole tiles: no masking of M, N or K edges on
         // the operands (the packed copies are whole tiles; C is masked at the store).
-        // The software-pipelined kernel also takes edge tiles in M and N, copying
-        // clamped rows and columns (row-major B: N a multiple of 8, so that no 16-byte
-        // chunk reaches past the end of a row), and a partial last k-tile (K a
-        // multiple of 8, zeroed past K in LDS).
+        // The software-pipelined and ping-pong kernels also take edge tiles in M and N,
+        // copying clamped rows and columns (row-major B: N a multiple of 8, so that no
+        // 16-byte chunk reaches past the end of a row); the software-pipelined kernel
+        // also a partial last k-tile (K a multiple of 8, zeroed past K in LDS).
         if (whole_tile(e.sched) && (Kx == 0 || (Kx % e.bk != 0 && !(e.sched == 5 && Kx % 8 == 0)))) continue;
         if (whole_tile(e.sched) && (Mx % e.bm != 0 || Nx % e.bn != 0) &&
-            !(e.sched == 5 && (e.opb == 1 || Nx % 8 == 0)))
+            !((e.sched == 5 || e.sched == 2 || e.sched == 4) && (e.opb == 1 || Nx % 8 == 0)))
             continue;
         if (want_wn && (e.variant == V_MFMA ? e.wn : 1) != want_wn) continue;
         const int vec = want_vec >= 0 ? want_vec : ((packed || vec_ok) ? 1 : 0);

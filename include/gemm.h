@@ -94,9 +94,8 @@ typedef struct gemm_config {
                           GEMM_ERR_UNSUPPORTED); 4 ping-pong on 32x32x16 MFMAs; 5 software-
                           pipelined 32x32x16 with direct global->LDS copies, 4 waves of 128 x
                           128 or 8 of 128 x 64 (2-5: MFMA, 16-bit inputs, 16-byte aligned
-                          operands; 2-4: M and N multiples of 256, K of 32; 5: K a multiple
-                          of 8, any M, and any N for column-major B, N a multiple of 8 for
-                          row-major B;
+                          operands, any M, and any N for column-major B or N a multiple of
+                          8 for row-major B; 2-4: K a multiple of 32; 5: K a multiple of 8;
                           4 stores the plain fp32 accumulator only); 6 register-staged with three LDS
                           stages and fragments read half a k-tile ahead (fp32 256 x 128
                           tiles, any shape, K not split) */

@@ -127,26 +127,28 @@ def test_plan_ping_pong_eligibility():
         assert st == dg.GEMM_ERR_UNSUPPORTED
     assert plan(4096 + 8, 4096, 4096, "f16")[1].schedule == 5
     for sched in (2, 4):
-        st, _ = plan(4096 + 8, 4096, 4096, "f16", req=dg.request(schedule=sched))
+        # edge tiles in M and N: yes; row-major B with N not a multiple of 8: no
+        assert plan(4096 + 8, 4096, 4096, "f16", req=dg.request(schedule=sched))[0] == 0
+        st, _ = plan(4096, 4001, 4096, "f16", ldb=4008, req=dg.request(schedule=sched))
         assert st == dg.GEMM_ERR_UNSUPPORTED
     assert plan(4096, 4096, 4096, "f16", a=2)[1].schedule == 1
     assert plan(4096, 4096, 4096, "f32")[1].schedule not in (2, 3, 4, 5)
-    st, _ = plan(4000, 4096, 4096, "f16", req=dg.request(schedule=2))
+    st, _ = plan(4096, 4096, 4000 + 8, "f16", req=dg.request(schedule=2))   # K not a multiple of 32
     assert st == dg.GEMM_ERR_UNSUPPORTED
 
 
 def test_plan_software_pipelined_edge_tiles():
     """Schedule 5 takes M and N that are not multiples of 256 (row-major B only with N a
     multiple of 8); K must stay a multiple of 32 and the operands 16-byte aligned."""
-    for op_b in "NT":
+    for op_b, sched in (("N", 5), ("T", 2)):   # column-major B: the ping-pong kernel, as for whole tiles
         st, c = plan(4000, 4000, 4000, "f16", op_b)
-        assert st == 0 and c.schedule == 5 and (c.tiles_m, c.tiles_n) == (16, 16), op_b
+        assert st == 0 and c.schedule == sched and (c.tiles_m, c.tiles_n) == (16, 16), op_b
     st, c = plan(4000, 4001, 4096, "f16", "N", ldb=4008)     # a 16-byte chunk would straddle N
     assert st == 0 and c.schedule == 1
     st, _ = plan(4000, 4001, 4096, "f16", "N", ldb=4008, req=dg.request(schedule=5))
     assert st == dg.GEMM_ERR_UNSUPPORTED
     st, c = plan(4000, 4001, 4096, "f16", "T")
-    assert st == 0 and c.schedule == 5
+    assert st == 0 and c.schedule in (2, 5)
     assert plan(4000, 4000, 4000 + 8, "f16")[1].schedule == 5   # a partial last k-tile
     st, c = plan(4000, 4000, 4004, "f16", lda=4008)             # K not a multiple of 8
     assert st == 0 and c.schedule == 1

@@ -145,6 +145,23 @@ def test_software_pipelined_edge_tiles(waves_n, shape, op_b, dtype):
     assert normalized_error(C[:M, :N], Cref, D) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("schedule", [2, 4])
+@pytest.mark.parametrize("shape,op_b", [((300, 264, 64), "N"), ((513, 777, 96), "T"), ((257, 512, 4160), "N"),
+                                        ((40, 8, 32), "N"), ((600, 1, 128), "T"), ((256, 300, 32 * 9), "T")])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_ping_pong_edge_tiles(schedule, shape, op_b, dtype):
+    """The ping-pong kernels on M and N that are not multiples of 256 (row-major B: N
+    a multiple of 8), K a multiple of 32."""
+    M, N, K = shape
+    ops = gi.make_operands(M, N, K, dtype, "normal", seed=M + 2 * N + K, op_b=op_b)
+    print(f"case pp edge tiles {shape} {dtype} op {op_b} schedule {schedule}", flush=True)
+    req = dg.request(schedule=schedule)
+    C = run_ops(ops, cfg=req, ldc=N + 3)
+    check_untouched(C, M, N)
+    Cref, D = oracle.gemm_ref(ops)
+    assert normalized_error(C[:M, :N], Cref, D) <= TOL[dtype]
+
+
 @pytest.mark.parametrize("k_tiles", [1, 2, 3, 4, 5, 7, 130])
 @pytest.mark.parametrize("op_b", ["N", "T"])
 def test_three_stage_fp32_k_tile_counts(k_tiles, op_b):
