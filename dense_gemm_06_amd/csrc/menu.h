@@ -43,7 +43,7 @@ constexpr bool schedule_enabled(int sched) { return sched != 3; }
 // aligned and K whole k-tiles (schedule 5: K a multiple of 8, a partial last k-tile
 // zeroed past K); edge tiles in M and N copy clamped rows and columns (schedule 3,
 // switched off: whole tiles only).
-constexpr bool whole_tile(int sched) { return sched >= 2 && sched <= 5; }
+constexpr bool direct_copy(int sched) { return sched >= 2 && sched <= 5; }
 
 // Configurations whose kernel applies a fused epilogue (every other one stores the
 // plain fp32 accumulator only): all but the 32x32x16 ping-pong kernel and the

@@ -283,16 +283,16 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
         // copying clamped rows and columns (row-major B: N a multiple of 8, so that no
         // 16-byte chunk reaches past the end of a row); the software-pipelined kernel
         // also a partial last k-tile (K a multiple of 8, zeroed past K in LDS).
-        if (whole_tile(e.sched) && (Kx == 0 || (Kx % e.bk != 0 && !(e.sched == 5 && Kx % 8 == 0)))) continue;
-        if (whole_tile(e.sched) && (Mx % e.bm != 0 || Nx % e.bn != 0) &&
+        if (direct_copy(e.sched) && (Kx == 0 || (Kx % e.bk != 0 && !(e.sched == 5 && Kx % 8 == 0)))) continue;
+        if (direct_copy(e.sched) && (Mx % e.bm != 0 || Nx % e.bn != 0) &&
             !((e.sched == 5 || e.sched == 2 || e.sched == 4) && (e.opb == 1 || Nx % 8 == 0)))
             continue;
         if (want_wn && (e.variant == V_MFMA ? e.wn : 1) != want_wn) continue;
         const int vec = want_vec >= 0 ? want_vec : ((packed || vec_ok) ? 1 : 0);
         if (e.vec != vec) continue;
         if (e.vec && !packed && !vec_ok) continue;          // 16-byte loads need element-aligned bases
-        if (whole_tile(e.sched) && !packed && !dma_ok) continue;   // direct LDS copies need 16-byte alignment
-        const int64_t tiles = whole_tile(e.sched) ? ((Mx + e.bm - 1) / e.bm) * ((Nx + e.bn - 1) / e.bn)
+        if (direct_copy(e.sched) && !packed && !dma_ok) continue;   // direct LDS copies need 16-byte alignment
+        const int64_t tiles = direct_copy(e.sched) ? ((Mx + e.bm - 1) / e.bm) * ((Nx + e.bn - 1) / e.bn)
                                                   : ((M + e.bm - 1) / e.bm) * ((N + e.bn - 1) / e.bn);
         const int64_t ktiles = (Kx + e.bk - 1) / e.bk;
         const int occ = blocks_per_cu(e);
@@ -378,8 +378,8 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
     cfg.lds_bytes = e.lds_bytes;
     cfg.kernel_id = e.id;
     cfg.schedule = e.sched;
-    cfg.tiles_m = ((best_packed && whole_tile(e.sched) ? Mp : M) + e.bm - 1) / e.bm;
-    cfg.tiles_n = ((best_packed && whole_tile(e.sched) ? Np : N) + e.bn - 1) / e.bn;
+    cfg.tiles_m = ((best_packed && direct_copy(e.sched) ? Mp : M) + e.bm - 1) / e.bm;
+    cfg.tiles_n = ((best_packed && direct_copy(e.sched) ? Np : N) + e.bn - 1) / e.bn;
     cfg.grid = (int32_t)(cfg.tiles_m * cfg.tiles_n);
     // Group enough tile rows that one XCD's share of the grid forms a compact
     // rectangle; the remap needs the grid to split evenly over the 8 XCDs.

@@ -104,7 +104,7 @@ static void check_plan(int opB, int64_t M, int64_t N, int64_t K, int64_t lda, in
         CHECK((int64_t)c.grid == c.tiles_m * c.tiles_n, "grid %d", c.grid);
     }
     if (e.vec && !packed) CHECK(a % es == 0 && b % es == 0, "16-byte loads on bases not aligned to the element");
-    if (whole_tile(e.sched) && !packed) {
+    if (direct_copy(e.sched) && !packed) {
         CHECK(a % 16 == 0 && b % 16 == 0 && (lda * es) % 16 == 0 && (ldb * es) % 16 == 0,
               "direct copies on unaligned operands");
         CHECK(K > 0 && K % 8 == 0, "direct copies with K = %lld", (long long)K);
