@@ -210,6 +210,51 @@ def time_grouped(name, steps, warmup):
                 separate_tflops=flops / (ms_sep * 1e-3) / 1e12, cfg=cfg, peak=PEAK_TFLOPS[spec["dtype"]])
 
 
+def sclk_under_load(name, seconds=2.0):
+    """The graphics clock while the problem's kernel runs back to back: launches in
+    batches for about `seconds`, while a child amd-smi process reads the clock of
+    every XCD once, half-way through. Reported as not measured when amd-smi is
+    missing or its output cannot be read."""
+    import shutil
+    import subprocess
+    import threading
+    import torch
+    import dense_gemm_06_amd as dg
+    exe = shutil.which("amd-smi")
+    if exe is None:
+        return {"measured": False, "reason": "amd-smi not found"}
+    ops, A, B, C = device_problem(name)
+    s = torch.cuda.current_stream().cuda_stream
+    call = lambda: dg.gemm_ex(0, dg.OP_CODE[ops.op_b], ops.M, ops.N, ops.K, A.data_ptr(), ops.lda, B.data_ptr(),
+                              ops.ldb, C.data_ptr(), ops.N, dg.DTYPE_CODE[ops.dtype], None, s)
+    result = {}
+
+    def probe():
+        time.sleep(seconds / 2)
+        try:
+            r = subprocess.run([exe, "metric", "-c", "--json"], capture_output=True, text=True, timeout=30)
+            data = json.loads(r.stdout)
+            gpu = data["gpu_data"][0] if isinstance(data, dict) else data[0]
+            clocks = {k: v["clk"]["value"] for k, v in gpu["clock"].items() if k.startswith("gfx_")}
+            result.update(measured=True, source="amd-smi metric -c", workload=name, mhz_per_xcd=list(clocks.values()),
+                          mhz_mean=round(sum(clocks.values()) / len(clocks), 1),
+                          mhz_max_rated=max(v["max_clk"]["value"] for k, v in gpu["clock"].items()
+                                            if k.startswith("gfx_")))
+        except Exception as exc:  # the clock is context; the run goes on without it
+            result.update(measured=False, reason=f"{type(exc).__name__}: {str(exc)[:160]}")
+
+    t = threading.Thread(target=probe)
+    t.start()
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end or t.is_alive():
+        for _ in range(50):
+            call()
+        torch.cuda.synchronize()
+    t.join()
+    del A, B, C
+    return result
+
+
 def time_distribution(name, n=100, warmup=10, n_cold=10, cold_bytes=512 << 20):
     """Per-launch durations: n launches back to back with an event pair around each
     (median, min, max), and n_cold launches each preceded by a write of cold_bytes
@@ -445,6 +490,7 @@ def main():
         # per-launch distribution (median / min) and MALL-cold launches of the two 4096^3 problems
         out["launch_distribution"] = {name: time_distribution(name, n=100 if name.startswith("c4") else 30)
                                       for name in (headline, "c3_f32_4096")}
+        out["sclk"] = sclk_under_load(headline)
         for name in ("m8_f16_shard", "m8_f32_shard"):
             if name in out.get("other_problems", {}):
                 out["other_problems"][name]["workload"] = ("one GPU's share of the 4096^3 problem split 8 ways by "
