@@ -232,16 +232,30 @@ def sclk_under_load(name, seconds=2.0):
     def probe():
         time.sleep(seconds / 2)
         try:
-            r = subprocess.run([exe, "metric", "-c", "--json"], capture_output=True, text=True, timeout=30)
+            r = subprocess.run([exe, "metric", "-c", "-p", "--json"], capture_output=True, text=True, timeout=30)
             data = json.loads(r.stdout)
             gpu = data["gpu_data"][0] if isinstance(data, dict) else data[0]
             clocks = {k: v["clk"]["value"] for k, v in gpu["clock"].items() if k.startswith("gfx_")}
-            result.update(measured=True, source="amd-smi metric -c", workload=name, mhz_per_xcd=list(clocks.values()),
-                          mhz_mean=round(sum(clocks.values()) / len(clocks), 1),
+            result.update(measured=True, source="amd-smi metric -c -p", workload=name,
+                          mhz_per_xcd=list(clocks.values()), mhz_mean=round(sum(clocks.values()) / len(clocks), 1),
                           mhz_max_rated=max(v["max_clk"]["value"] for k, v in gpu["clock"].items()
                                             if k.startswith("gfx_")))
+            try:
+                result["socket_power_w"] = gpu["power"]["socket_power"]["value"]
+            except (KeyError, TypeError):
+                pass
         except Exception as exc:  # the clock is context; the run goes on without it
             result.update(measured=False, reason=f"{type(exc).__name__}: {str(exc)[:160]}")
+        smi = shutil.which("rocm-smi")
+        if smi:
+            try:  # the board's power cap, when the tool reports it
+                r = subprocess.run([smi, "--showmaxpower", "--json"], capture_output=True, text=True, timeout=30)
+                card = next(iter(json.loads(r.stdout).values()))
+                cap = [v for k, v in card.items() if "power" in k.lower()]
+                if cap:
+                    result["power_cap_w"] = float(str(cap[0]).split()[0])
+            except Exception:
+                pass
 
     t = threading.Thread(target=probe)
     t.start()
