@@ -123,11 +123,12 @@ __device__ __forceinline__ void group_tile(const GroupArgs& ga, int t, GemmArgs&
 
 // ---- epilogue and C stores
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
-    const uint32_t u = __float_as_uint(x);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);  // NaN stays a quiet NaN
-    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-}
+// fp32 -> bf16, round to nearest even: the hardware conversion (v_cvt_pk_bf16_f32,
+// two values per instruction), which on gfx950 gives the same bits as the integer
+// round-to-nearest-even (add 0x7fff plus the kept lowest bit, keep the high half) for
+// every one of the 2^32 fp32 patterns except NaNs, which stay NaNs (checked
+// exhaustively on the device).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
 
 __device__ __forceinline__ float load_out(const void* p, int dt, size_t i) {
     if (dt == DT_F32) return static_cast<const float*>(p)[i];
