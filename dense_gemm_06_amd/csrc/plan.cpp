@@ -133,16 +133,29 @@ static double tile_efficiency_aligned(const MenuEntry& e) {
     if (e.sched == 4) return 0.96;
     if (e.sched == 3) return 0.85;
     if (e.sched == 5) return 0.90;  // problem-dependent: see plan()
-    // the fp32 three-stage 256 x 128 tile against the register-staged one, alternated
-    // in one run at 4096^3: 1027.5-1029.9 us against 1036.0-1038.4 (row-major B),
-    // 1021.4-1022.6 against 1046.7-1046.9 (column-major B); it does not split K
-    if (e.sched == 6) return 0.71;
+    // the fp32 three-stage 256 x 128 tile: 2.8% faster per k than two resident 128 x 128
+    // register-staged tiles per CU (fitted from 8192^2 x K, K = 256, 512 and 8192,
+    // alternated: 31.2 against 32.1 us per round and 256 k), with a larger fixed cost
+    // per round (fp32_round_overhead); it does not split K
+    if (e.sched == 6) return 0.72;
     if (e.variant == V_LDS) return t >= 128 ? 0.6 : 0.35;
     // the fp32 64 x 64 tile with K split between two wave grids measured 7-9% faster
     // than with one (1024^3: 27.3-27.8 us against 29.6-29.8; 256^3: 8.4-8.6 against
     // 9.0-9.1; 512 x 4096 x 4096: 162-169 against 177-180)
     if (e.threads > e.wm * e.wn * 64) return 0.49;
     return t >= 256 ? 0.85 : t >= 128 ? 0.7 : 0.45;
+}
+// fp32 tiles: cycles per round of tiles beyond the k loop (the first copies and the
+// C store), fitted from the same 8192^2 x K runs: a lone 256 x 128 tile per CU
+// (three-stage or register-staged) exposes about 13-14 us per round (128 KB of C),
+// two resident 128 x 128 tiles about 6 us (the same C bytes; one tile's store and
+// first copies overlap the other's k loop). In the model's cycles (about 2.9 per ns
+// at the fp32 rates above): 0.29 cycles per byte of C alone, 0.134 with two or
+// more resident tiles. Without this term the three-stage tile won at short K and
+// measured 18% slower than 128 x 128 tiles at 8192^2 x 256 (360.8 us against 305.0).
+static double fp32_round_overhead(const MenuEntry& e, int64_t resident) {
+    const double c_bytes = 4.0 * e.bm * e.bn * (double)resident;
+    return c_bytes * (resident >= 2 ? 0.134 : 0.29);
 }
 static int blocks_per_cu(const MenuEntry& e) {
     const int by_lds = (160 * 1024) / e.lds_bytes;
@@ -319,22 +332,26 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
             const int64_t rounds = (work + concurrent - 1) / concurrent;
             const int64_t resident = std::min<int64_t>(occ, (work + num_cus - 1) / num_cus);
             const int64_t kpad = ((std::min<int64_t>(chunk, Kx) + e.bk - 1) / e.bk) * e.bk;
-            // The software-pipelined kernel (schedule 5), as measured against the
-            // ping-pong kernel: 8 waves win for row-major B and K of at least 64 k-tiles
-            // (4096^3 fp16: 124-130 us against 133-147; 8192^3: 917 against 997; bf16
-            // 4096^3: 115 against 126; with the fused GELU epilogue: equal); 4 waves win
-            // for short K, where the C store weighs more (the packed 3001 x 5003 x 1037
-            // problem, 34 k-tiles, column-major B: 62 us against 72; 4096^2 x 1024: equal);
-            // with column-major B and long K the ping-pong kernel is 9-12% faster, and the
-            // 4-wave form is 16% slower than it with a fused epilogue.
+            // The software-pipelined kernel (schedule 5) against the ping-pong kernel and
+            // its own 4-wave form, medians of three alternated passes: 8 waves are best or
+            // within 1% on both B layouts (column-major B: 4096^3 bf16 113.6 us against
+            // 119.1 ping-pong and 118.1 four waves, 8192^3 bf16 862 against 876, 8192^2 x
+            // 256 fp16 85.8 against 90.3 and 88.2; row-major B: 8192^2 x 512 fp16 108.2
+            // against 116.2 and 115.9, 8192^2 x 256 85.5 against 89.2 and 90.8), except
+            // for one round of tiles with at most 32 k-tiles, where the ping-pong kernel
+            // is 2-5% faster (4096^2 x 1024 bf16, column-major B: 36.7 against 38.7;
+            // 4096^2 x 512 bf16: 25.8 against 26.4). With a fused epilogue: 8 waves equal
+            // to the ping-pong kernel at 4096^3 fp16; 4 waves with column-major B 16% slower.
             double eff = tile_efficiency(e, packed || dma_ok);
             if (e.sched == 5) {
                 const bool eight = e.wm * e.wn == 8;
-                eff = (eight && e.opb == 0 && ktiles >= 64) || (!eight && ktiles < 64 && !fused_epilogue) ? 0.99
-                                                                                                         : 0.90;
+                if (fused_epilogue) eff = eight && e.opb == 0 && ktiles >= 64 ? 0.99 : 0.90;
+                else eff = !eight ? 0.90 : (tiles <= num_cus && ktiles <= 32) ? 0.96 : 0.99;
             }
             const double tile_cycles = 2.0 * e.bm * e.bn * std::max<int64_t>(kpad, e.bk) / (rate_per_cu(e) * eff);
             double cost = (double)rounds * (double)std::max<int64_t>(resident, 1) * tile_cycles;
+            if (e.dtype == DT_F32 && e.variant == V_MFMA)
+                cost += (double)rounds * fp32_round_overhead(e, std::max<int64_t>(resident, 1));
             // the reduction reads every plane and writes C, and is a second launch;
             // measured at 256^3 and 1024^3 fp32, a split costs about 16000 cycles
             // beyond its traffic (about 1 KB per clock for a kernel of this size),

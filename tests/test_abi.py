@@ -95,20 +95,23 @@ def test_plan_benchmark_configs():
 
 
 def test_plan_software_pipelined_kernel_where_measured_faster():
-    """Schedule 5 (8 waves) for whole tiles with row-major B and K of 64 k-tiles or
-    more, with or without a fused epilogue; the ping-pong kernel for short K and for
-    column-major B; the 4-wave form only when asked for."""
-    for m, n, k, dt in ((4096, 4096, 4096, "f16"), (4096, 4096, 4096, "bf16"), (4096, 4096, 2048, "f16"),
-                        (8192, 8192, 8192, "f16")):
-        c = plan(m, n, k, dt)[1]
-        assert c.schedule == 5 and (c.waves_m, c.waves_n) == (2, 4), (m, n, k, dt)
-    c = plan(4096, 4096, 1024, "f16")[1]   # short K: the 4-wave form
-    assert c.schedule == 5 and c.threads == 256
-    assert plan(4096, 4096, 4096, "f16", "T")[1].schedule == 2
-    # the ragged column-major problem, packed into whole tiles of K = 1088: 4 waves
+    """Schedule 5 with 8 waves for both B layouts; the ping-pong kernel for one round of
+    tiles with at most 32 k-tiles; with a fused epilogue, 8 waves for row-major B and
+    K of 64 k-tiles or more; the 4-wave form only when asked for."""
+    for m, n, k, dt, op_b in ((4096, 4096, 4096, "f16", "N"), (4096, 4096, 4096, "bf16", "N"),
+                              (4096, 4096, 2048, "f16", "N"), (8192, 8192, 8192, "f16", "N"),
+                              (8192, 8192, 256, "f16", "N"), (8192, 8192, 512, "f16", "N"),
+                              (4096, 4096, 4096, "f16", "T"), (4096, 4096, 4096, "bf16", "T"),
+                              (8192, 8192, 256, "f16", "T"), (5000, 5000, 5000, "f16", "T")):
+        c = plan(m, n, k, dt, op_b)[1]
+        assert c.schedule == 5 and (c.waves_m, c.waves_n) == (2, 4), (m, n, k, dt, op_b)
+    # one round of 256 tiles and at most 32 k-tiles: the ping-pong kernel
+    for k, dt, op_b in ((1024, "f16", "N"), (512, "bf16", "N"), (1024, "bf16", "T")):
+        assert plan(4096, 4096, k, dt, op_b)[1].schedule == 2, (k, dt, op_b)
+    # the ragged column-major problem, packed into whole tiles of K = 1088 (34 k-tiles)
     st, c = dg.gemm_plan_workspace(0, 1, 3001, 5003, 1037, 1037, 1037, 5003, dg.GEMM_BF16, 0x10002, 0x200002,
                                    0x400000, 256, "gfx950", 64 << 20, None)
-    assert st == 0 and c.pack == 2 and c.schedule == 5 and c.threads == 256
+    assert st == 0 and c.pack == 2 and c.schedule == 5 and c.threads == 512
     st, c = dg.gemm_plan_workspace(0, 0, 4096, 4096, 4096, 4096, 4096, 4096, dg.GEMM_F16, 0, 0, 0, 256, "gfx950", 0,
                                    None, epi=dg.epilogue(activation="relu"))
     assert st == 0 and c.schedule == 5 and c.waves_n == 4
@@ -140,7 +143,7 @@ def test_plan_ping_pong_eligibility():
 def test_plan_software_pipelined_edge_tiles():
     """Schedule 5 takes M and N that are not multiples of 256 (row-major B only with N a
     multiple of 8); K must stay a multiple of 32 and the operands 16-byte aligned."""
-    for op_b, sched in (("N", 5), ("T", 2)):   # column-major B: the ping-pong kernel, as for whole tiles
+    for op_b, sched in (("N", 5), ("T", 5)):
         st, c = plan(4000, 4000, 4000, "f16", op_b)
         assert st == 0 and c.schedule == sched and (c.tiles_m, c.tiles_n) == (16, 16), op_b
     st, c = plan(4000, 4001, 4096, "f16", "N", ldb=4008)     # a 16-byte chunk would straddle N
@@ -164,6 +167,11 @@ def test_plan_three_stage_fp32():
             assert st == 0 and c.schedule == 6 and (c.bm, c.bn) == (256, 128) and c.threads == 512, (shape, op_b)
     # few tiles: the register-staged kernels, which may split K with a workspace
     assert plan(1024, 1024, 1024, "f32")[1].schedule == 1
+    # short K: the three-stage tile's fixed cost per round of tiles outweighs its faster
+    # k loop; two resident 128 x 128 register-staged tiles per CU
+    for shape in ((8192, 8192, 256), (8192, 8192, 512), (4096, 4096, 1024)):
+        st, c = plan(*shape, "f32")
+        assert st == 0 and c.schedule == 1 and (c.bm, c.bn) == (128, 128), shape
     st, c = wplan(512, 512, 8192, "f32")
     assert st == 0 and c.schedule == 1 and c.split_k > 1
     # forced, with a K split: refused (schedule 6 has no sliced form)
