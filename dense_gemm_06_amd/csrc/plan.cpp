@@ -340,12 +340,16 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
             // against 116.2 and 115.9, 8192^2 x 256 85.5 against 89.2 and 90.8), except
             // for one round of tiles with at most 32 k-tiles, where the ping-pong kernel
             // is 2-5% faster (4096^2 x 1024 bf16, column-major B: 36.7 against 38.7;
-            // 4096^2 x 512 bf16: 25.8 against 26.4). With a fused epilogue: 8 waves equal
-            // to the ping-pong kernel at 4096^3 fp16; 4 waves with column-major B 16% slower.
+            // 4096^2 x 512 bf16: 25.8 against 26.4). With a fused epilogue (bias, GELU,
+            // bf16 out) 8 waves win from 32 k-tiles on, either B layout (column-major B
+            // 4096^3 fp16 140.9 against 147.3, bf16 127.1 against 131.0; row-major B
+            // 4096^2 x 1024 53.0 against 54.7), the ping-pong kernel at 8 and 16 k-tiles
+            // (8192^2 x 256 124.4 against 127.2; 8192^2 x 512 column-major B 150.6
+            // against 155.2); 4 waves are 12-60% slower there.
             double eff = tile_efficiency(e, packed || dma_ok);
             if (e.sched == 5) {
                 const bool eight = e.wm * e.wn == 8;
-                if (fused_epilogue) eff = eight && e.opb == 0 && ktiles >= 64 ? 0.99 : 0.90;
+                if (fused_epilogue) eff = eight && ktiles >= 32 ? 0.99 : 0.90;
                 else eff = !eight ? 0.90 : (tiles <= num_cus && ktiles <= 32) ? 0.96 : 0.99;
             }
             const double tile_cycles = 2.0 * e.bm * e.bn * std::max<int64_t>(kpad, e.bk) / (rate_per_cu(e) * eff);

@@ -112,9 +112,12 @@ def test_plan_software_pipelined_kernel_where_measured_faster():
     st, c = dg.gemm_plan_workspace(0, 1, 3001, 5003, 1037, 1037, 1037, 5003, dg.GEMM_BF16, 0x10002, 0x200002,
                                    0x400000, 256, "gfx950", 64 << 20, None)
     assert st == 0 and c.pack == 2 and c.schedule == 5 and c.threads == 512
-    st, c = dg.gemm_plan_workspace(0, 0, 4096, 4096, 4096, 4096, 4096, 4096, dg.GEMM_F16, 0, 0, 0, 256, "gfx950", 0,
-                                   None, epi=dg.epilogue(activation="relu"))
-    assert st == 0 and c.schedule == 5 and c.waves_n == 4
+    # with a fused epilogue: 8 waves from 32 k-tiles on, either B layout; the ping-pong
+    # kernel below that
+    for op_b, k, sched in ((0, 4096, 5), (1, 4096, 5), (0, 1024, 5), (0, 256, 2), (1, 512, 2)):
+        st, c = dg.gemm_plan_workspace(0, op_b, 4096, 4096, k, k, 4096 if op_b == 0 else k, 4096, dg.GEMM_F16, 0, 0,
+                                       0, 256, "gfx950", 0, None, epi=dg.epilogue(activation="relu"))
+        assert st == 0 and c.schedule == sched and (sched == 2 or c.waves_n == 4), (op_b, k)
     c = plan(4096, 4096, 4096, "f16", req=dg.request(schedule=5, waves_n=2))[1]
     assert c.schedule == 5 and c.threads == 256
 
