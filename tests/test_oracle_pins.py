@@ -332,3 +332,24 @@ def test_thread_count_applies_to_one_call():
     assert oracle.max_threads() == before
     C0, D0 = oracle.gemm_ref(ops)
     assert np.array_equal(C1, C0) and np.array_equal(D1, D0)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("op_b", ["N", "T"])
+def test_oracle_non_finite_inputs(dtype, op_b):
+    """IEEE classes of sums of products with NaN and infinite factors, worked by hand:
+    an infinity times zero is NaN, infinities of both signs in one sum give NaN, one
+    infinite product makes the sum infinite with its sign, a NaN factor makes NaN."""
+    inf, nan = np.inf, np.nan
+    a = np.array([[inf, 1.0], [nan, 0.0], [1.0, 2.0], [-inf, 1.0], [3.0, -1.0]])
+    b = np.array([[0.0, 1.0, 2.0], [1.0, -inf, 4.0]])
+    want = np.array([[nan, nan, inf],       # inf*0 + 1;  inf*1 + (-inf);  inf*2 + 4
+                     [nan, nan, nan],       # a NaN factor in every sum
+                     [2.0, -inf, 10.0],     # 0 + 2;  1 + 2*(-inf);  2 + 8
+                     [nan, -inf, -inf],     # -inf*0 + 1;  -inf*1 + (-inf);  -inf*2 + 4
+                     [-1.0, inf, 2.0]])     # 0 - 1;  3 + (-1)(-inf);  6 - 4
+    ops = gi.from_values(a, b, dtype, op_b)
+    C, _ = oracle.gemm_ref(ops)
+    assert np.array_equal(np.isnan(C), np.isnan(want))
+    fin = ~np.isnan(want)
+    assert np.array_equal(C[fin], want[fin])
