@@ -40,8 +40,6 @@ def kernel_sources(cfg) -> list[str]:
         return common + ["kernel_lds.h"]
     if cfg.schedule in (2, 4):
         return common + ["kernel_pp.h"]
-    if cfg.schedule == 3:
-        return common + ["kernel_dma.h"]
     if cfg.schedule == 5:
         return common + ["kernel_sp.h"]
     return common + ["kernel_mfma.h"]
@@ -66,8 +64,13 @@ def parse():
     p.add_argument("--only", default=None, help="time only this benchmark problem, or grouped workload (for profiling)")
     p.add_argument("--with-workspace", action="store_true",
                    help="with --only: pass a workspace (the heuristic may split K or pack the operands)")
-    p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
-                   help="instead of GEMMs, run 5 plain device copies of MIB MiB (calibrates HBM counters)")
+    p.add_argument("--extended", action="store_true",
+                   help="also time the fused epilogue, the per-launch distribution and the clock under load "
+                        "(more launches of the headline kernel, so a kernel trace of such a run averages "
+                        "over more than the timed steps)")
+    p.add_argument("--traffic-probe", type=int, default=0, metavar="MIB",
+                   help="instead of GEMMs, run the counter-calibration kernels over MIB MiB each (direct LDS "
+                        "copies of 64-byte row segments, 16-byte loads, 16-byte stores)")
     return p.parse_args()
 
 
@@ -366,7 +369,7 @@ def kernel_name(cfg, dtype):
     elif dtype == "f32":
         base = "mfma32_gemm, three LDS stages" if cfg.schedule == 6 else "mfma32_gemm"
     else:
-        base = {1: "mfma16_gemm", 2: "mfma16_pp (16x16x32)", 3: "mfma16_dma", 4: "mfma16_pp (32x32x16)",
+        base = {1: "mfma16_gemm", 2: "mfma16_pp (16x16x32)", 4: "mfma16_pp (32x32x16)",
                 5: "mfma32_sp (32x32x16)"}[cfg.schedule]
     return f"{base} {cfg.bm}x{cfg.bn}x{cfg.bk} waves {cfg.waves_m}x{cfg.waves_n}"
 
@@ -384,6 +387,34 @@ def load_traffic(problem, cfg):
     return rec.get("hbm_bytes_per_launch")
 
 
+def traffic_probe(mib):
+    """One launch of each calibration kernel of libdgprobe.so over `mib` MiB: the bytes
+    each moves are known, so a counter run over this command gives the counter-to-bytes
+    factor of each memory form (probe_read_lds, probe_read_vec, probe_write)."""
+    import ctypes
+    import torch
+    from dense_gemm_06_amd import build as b
+    lib = ctypes.CDLL(b.PROBE_LIB)
+    lib.dg_probe_traffic.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.dg_probe_out_bytes.argtypes = [ctypes.c_int, ctypes.c_int64]
+    lib.dg_probe_out_bytes.restype = ctypes.c_int64
+    nbytes = mib << 20
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").uniform_()
+    dst = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    out = torch.zeros(max(lib.dg_probe_out_bytes(k, nbytes) for k in (0, 1)) // 4 + 1, dtype=torch.int32,
+                      device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    torch.cuda.synchronize()
+    res = {}
+    for kind, name in ((0, "probe_read_lds"), (1, "probe_read_vec"), (2, "probe_write")):
+        rc = lib.dg_probe_traffic(kind, src.data_ptr(), dst.data_ptr() if kind == 2 else out.data_ptr(), nbytes, s)
+        torch.cuda.synchronize()
+        if rc != 0:
+            raise RuntimeError(f"{name}: status {rc}")
+        res[name] = {"bytes_read" if kind < 2 else "bytes_written": nbytes}
+    print(json.dumps({"traffic_probe": res}), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -394,15 +425,8 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
-    if a.copy_probe:
-        n = a.copy_probe * (1 << 20) // 4
-        src = torch.rand(n, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "copies": 5}))
+    if a.traffic_probe:
+        traffic_probe(a.traffic_probe)
         return
     import dense_gemm_06_amd as dg
     dg.library()   # fail loudly if the HIP library is missing
@@ -416,7 +440,7 @@ def main():
     # the fused-epilogue variant right after the headline, in the same thermal state
     # (the chip's clock drifts by 10-20% over a run of heavy launches)
     fe = None
-    if not a.no_extra and not a.only:
+    if a.extended and not a.only:
         fe = time_fused_epilogue(headline, max(5, a.steps // 2), max(2, a.warmup // 2))
     extras = {}
     if not a.no_extra and not a.only:
@@ -500,7 +524,7 @@ def main():
                              "separate_launches_ms": round(r["separate_ms"], 6),
                              "tile": f"{r['cfg'].bm}x{r['cfg'].bn}", "grid": r["cfg"].grid}
         out["grouped"] = grouped
-    if not a.no_extra and not a.only:
+    if a.extended and not a.only:
         # per-launch distribution (median / min) and MALL-cold launches of the two 4096^3 problems
         out["launch_distribution"] = {name: time_distribution(name, n=100 if name.startswith("c4") else 30)
                                       for name in (headline, "c3_f32_4096")}

@@ -19,6 +19,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdensegemm.so")
+# Calibration kernels for the HBM traffic counters (a measurement tool, linked apart
+# from the GEMM library).
+PROBE_LIB = os.path.join(HERE, "libdgprobe.so")
 ARCH = "gfx950"
 
 DEVICE_SOURCES = ["inst_lds_f32.hip", "inst_lds_f16.hip", "inst_lds_bf16.hip",
@@ -101,6 +104,11 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     if rc != 0:
         raise RuntimeError(f"link failed:\n{out}")
     os.replace(tmp, LIB)
+    tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    rc, out, _ = _run([cc, *COMMON, *DEVICE_FLAGS, "-shared", os.path.join(CSRC, "probe.hip"), "-o", tmp])
+    if rc != 0:
+        raise RuntimeError(f"probe library build failed:\n{out}")
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

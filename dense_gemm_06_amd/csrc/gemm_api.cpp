@@ -16,6 +16,7 @@
 #include "../../include/gemm.h"
 #include "launch.h"
 #include "plan.h"
+#include "product.h"
 
 namespace {
 
@@ -83,6 +84,15 @@ int launch_grouped(int id, const dg::GroupArgs& args, unsigned grid, hipStream_t
     return e.dtype == dg::DT_F32 ? dg::launch_mfma_f32_grouped(id, args, grid, s)
            : e.dtype == dg::DT_F16 ? dg::launch_mfma_f16_grouped(id, args, grid, s)
                                    : dg::launch_mfma_bf16_grouped(id, args, grid, s);
+}
+
+// A launcher's result as a gemm_status: -1 means the kernel id has no launcher
+// (an internal inconsistency), a positive value is the hipError_t of the launch.
+int launch_result(int rc, const char* what, int id) {
+    if (rc == 0) return GEMM_OK;
+    if (rc < 0) dg::set_error("internal: %s %d has no launcher", what, id);
+    else dg::set_error("%s %d: launch failed: %s", what, id, hipGetErrorString((hipError_t)rc));
+    return GEMM_ERR_LAUNCH;
 }
 
 // Byte extent of `batch` matrices of rows x cols (leading dimension ld) placed
@@ -204,19 +214,12 @@ int gemm_grouped(int opA, int opB, int dtype, const gemm_problem* problems, int 
         sg.tile_begin = a.total_tiles;
         a.total_tiles += sg.batch * sg.tiles_m * sg.tiles_n;  // < 2^31 in total (checked by the planner)
     }
-    (void)hipGetLastError();  // clear a stale error left by earlier unrelated work
     for (dg::GroupArgs& a : launches) {
         const unsigned grid = (unsigned)std::min<int64_t>(a.total_tiles, plan.grid);
         a.xcd_remap = plan.xcd_remap;
-        if (launch_grouped(plan.kernel_id, a, grid, (hipStream_t)stream) != 0) {
-            dg::set_error("internal: kernel %d has no grouped launcher", plan.kernel_id);
-            return GEMM_ERR_LAUNCH;
-        }
-        he = hipGetLastError();
-        if (he != hipSuccess) {
-            dg::set_error("grouped kernel launch failed: %s", hipGetErrorString(he));
-            return GEMM_ERR_LAUNCH;
-        }
+        st = launch_result(launch_grouped(plan.kernel_id, a, grid, (hipStream_t)stream), "grouped kernel",
+                           plan.kernel_id);
+        if (st != GEMM_OK) return st;
     }
     return GEMM_OK;
 }
@@ -253,11 +256,8 @@ int gemm_strided_batched(int opA, int opB, int64_t M, int64_t N, int64_t K, cons
 
 }  // extern "C"
 
-namespace {
+namespace dg {
 
-// The product with every option: C (element type ep.out_dt when ep.kind != 0),
-// an optional workspace (split K or packing), an optional fused epilogue. All
-// validation happens before the first launch.
 int run_product(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
                 int64_t ldb, void* C, int64_t ldc, int dtype, const dg::Epilogue& ep, const gemm_config* cfg,
                 void* workspace, int64_t workspace_bytes, void* stream) {
@@ -349,7 +349,6 @@ int run_product(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A
     args.work_ld = (N + 3) / 4 * 4;
     args.work_slice = M * args.work_ld;
     args.ep = ep;
-    (void)hipGetLastError();  // clear a stale error left by earlier unrelated work
     if (plan.pack == 2) {
         // zero-padded copies of A and B in the workspace, then the product on them
         int64_t Mp, Np, Kp;
@@ -359,34 +358,37 @@ int run_product(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A
         dg::PackJob ja{A, ap, lda, (int)M, (int)K, (int)Mp, (int)Kp};
         dg::PackJob jb = opB == GEMM_OP_N ? dg::PackJob{B, bp, ldb, (int)K, (int)N, (int)Kp, (int)Np}
                                           : dg::PackJob{B, bp, ldb, (int)N, (int)K, (int)Np, (int)Kp};
-        dg::launch_pack((int)es, ja, jb, (hipStream_t)stream);
+        st = launch_result(dg::launch_pack((int)es, ja, jb, (hipStream_t)stream), "packing kernel", 0);
+        if (st != GEMM_OK) return st;
         args.A = ap;
         args.B = bp;
         args.lda = Kp;
         args.ldb = opB == GEMM_OP_N ? Np : Kp;
         args.K = (int)Kp;
     }
-    if (launch(plan.kernel_id, args, (unsigned)plan.grid, (unsigned)plan.split_k, (hipStream_t)stream) != 0) {
-        dg::set_error("internal: kernel %d has no launcher", plan.kernel_id);
-        return GEMM_ERR_LAUNCH;
-    }
+    st = launch_result(launch(plan.kernel_id, args, (unsigned)plan.grid, (unsigned)plan.split_k, (hipStream_t)stream),
+                       "kernel", plan.kernel_id);
+    if (st != GEMM_OK) return st;
     if (plan.split_k > 1)
-        dg::launch_splitk_reduce(args.work, plan.split_k, args.work_slice, args.work_ld, (int)M, (int)N, C, ldc, ep,
-                                 (hipStream_t)stream);
-    he = hipGetLastError();
-    if (he != hipSuccess) {
-        dg::set_error("kernel launch failed: %s", hipGetErrorString(he));
-        return GEMM_ERR_LAUNCH;
-    }
+        return launch_result(dg::launch_splitk_reduce(args.work, plan.split_k, args.work_slice, args.work_ld, (int)M,
+                                                      (int)N, C, ldc, ep, (hipStream_t)stream),
+                             "split-K reduction kernel", 0);
     return GEMM_OK;
 }
 
-dg::Epilogue plain_epilogue() {
-    dg::Epilogue ep;
+Epilogue plain_epilogue() {
+    Epilogue ep;
     memset(&ep, 0, sizeof ep);
     ep.alpha = 1.0f;
     return ep;
 }
+
+}  // namespace dg
+
+namespace {
+
+using dg::plain_epilogue;
+using dg::run_product;
 
 // gemm_epilogue -> the kernels' descriptor; an identity epilogue (alpha 1, no
 // residual, no bias, no activation, fp32 C) becomes the plain store.
@@ -442,6 +444,11 @@ int gemm_ex_epilogue(int opA, int opB, int64_t M, int64_t N, int64_t K, const vo
         if (ep.ldr < std::max<int64_t>(1, N)) {
             dg::set_error("epilogue ldr = %lld is smaller than max(1, N) = %lld", (long long)ep.ldr,
                           (long long)std::max<int64_t>(1, N));
+            return GEMM_ERR_INVALID_VALUE;
+        }
+        if (!dg::extent_fits(M, N, ep.ldr)) {
+            dg::set_error("epilogue ldr = %lld: R's extent (M - 1) * ldr + N (M = %lld, N = %lld) does not fit in "
+                          "the address space", (long long)ep.ldr, (long long)M, (long long)N);
             return GEMM_ERR_INVALID_VALUE;
         }
     }

@@ -32,5 +32,4 @@
 #include "kernel_lds.h"
 #include "kernel_mfma.h"
 #include "kernel_pp.h"
-#include "kernel_dma.h"
 #include "kernel_sp.h"

@@ -6,9 +6,23 @@
 
 namespace dg {
 
+template <typename T> struct same_type { typedef T type; };
+
+// Enqueue kernel `fn` with the given by-value arguments and return this launch's
+// own status: 0, or the hipError_t the launch reported. A status left over from
+// earlier, unrelated work of the calling thread is neither read nor cleared.
+template <typename... P>
+int launch_status(void (*fn)(P...), dim3 grid, dim3 block, hipStream_t stream, typename same_type<P>::type... a) {
+    void* args[] = {static_cast<void*>(&a)...};
+    return (int)hipLaunchKernel(reinterpret_cast<const void*>(fn), grid, block, args, 0, stream);
+}
+
+// The family launchers return 0 after enqueueing, -1 if the kernel id has no
+// launcher there (it does not belong to the family or cannot split), or the
+// positive hipError_t of a launch the runtime refused.
+
 // Enqueue kernel `id` with grid (grid, grid_y) on `stream`; grid_y > 1 is a
-// split-K launch (register-staged kernels only). Returns 0, or -1 if `id` does
-// not belong to the family (or cannot split).
+// split-K launch (register-staged kernels only).
 int launch_lds_f32(int id, const GemmArgs& a, unsigned grid, unsigned grid_y, hipStream_t stream);
 int launch_lds_f16(int id, const GemmArgs& a, unsigned grid, unsigned grid_y, hipStream_t stream);
 int launch_lds_bf16(int id, const GemmArgs& a, unsigned grid, unsigned grid_y, hipStream_t stream);

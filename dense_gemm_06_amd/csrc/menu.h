@@ -19,36 +19,31 @@ enum Dtype { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
 //             0 = element-wise loads (any alignment)
 //   bm, bn, bk : block tile; wm x wn : wave grid (MFMA); tm x tn : thread tile (LDS)
 //   sched   : 1 = register-staged double buffer (any shape), 2 = ping-pong with
-//             direct global->LDS copies on 16x16x32 MFMAs, 3 = software-pipelined
-//             with direct copies, 4 = ping-pong on 32x32x16 MFMAs, 5 = software-
+//             direct global->LDS copies on 16x16x32 MFMAs, 3 = not used (an earlier
+//             kernel, removed), 4 = ping-pong on 32x32x16 MFMAs, 5 = software-
 //             pipelined 32x32x16 with direct copies, 4 waves of 128 x 128 or 8 of
-//             128 x 64 (2-5: 16-byte aligned operands, edge tiles in M, and in N
-//             for column-major B or N a multiple of 8; 2-4: K a multiple of bk;
+//             128 x 64 (2, 4, 5: 16-byte aligned operands, edge tiles in M, and in N
+//             for column-major B or N a multiple of 8; 2, 4: K a multiple of bk;
 //             5: K a multiple of 8), 6 = register-staged with three LDS stages and fragments
 //             read a half k-tile ahead (fp32, any shape)
 struct MenuEntry {
     int id, variant, dtype, opb, vec, bm, bn, bk, wm, wn, tm, tn, threads, lds_bytes, sched;
 };
 
-// Schedules the planner may choose and the launcher will run. Schedule 3 is
-// compiled but switched off: its copy code had two defects that made it address
-// memory it does not own (an M0 write read by the next LDS DMA without the wait
-// state the GFX9 family requires, and a copy base address built from a signed
-// readfirstlane result, which sign-extends when bit 31 of the low word is set).
-// Both are corrected in the kernel; it stays off until the corrected kernel has
-// passed its parity tests on the device.
+// Schedules the planner may choose and the launcher will run. Schedule 3 (a
+// software-pipelined kernel whose copies were issued from inline assembly) faulted
+// on the device and was removed from the library; the number stays unused so that
+// configurations keep their meaning, and requests for it are refused.
 constexpr bool schedule_enabled(int sched) { return sched != 3; }
 
 // Schedules whose kernels copy tiles straight into LDS: the operands must be 16-byte
 // aligned and K whole k-tiles (schedule 5: K a multiple of 8, a partial last k-tile
-// zeroed past K); edge tiles in M and N copy clamped rows and columns (schedule 3,
-// switched off: whole tiles only).
-constexpr bool direct_copy(int sched) { return sched >= 2 && sched <= 5; }
+// zeroed past K); edge tiles in M and N copy clamped rows and columns.
+constexpr bool direct_copy(int sched) { return sched == 2 || sched == 4 || sched == 5; }
 
 // Configurations whose kernel applies a fused epilogue (every other one stores the
-// plain fp32 accumulator only): all but the 32x32x16 ping-pong kernel and the
-// switched-off schedule 3.
-constexpr bool epilogue_capable(int sched) { return sched != 3 && sched != 4; }
+// plain fp32 accumulator only): all but the 32x32x16 ping-pong kernel.
+constexpr bool epilogue_capable(int sched) { return sched != 4; }
 
 // Configurations that also have a grouped (persistent) form: the register-staged
 // schedule, which masks every edge, except the 4-wave 256 x 256 tiles (their
@@ -106,11 +101,6 @@ constexpr bool grouped_capable(int variant, int sched, int bm, int bn, int wm, i
     X(base + 0, V_MFMA, dt, 0, 1, 256, 256, 32, 2, 4, 0, 0, 512, 4 * 2 * 32 * 512, 4)      \
     X(base + 1, V_MFMA, dt, 1, 1, 256, 256, 32, 2, 4, 0, 0, 512, 4 * 2 * 32 * 512, 4)
 
-// Software-pipelined kernels with direct LDS copies (16-bit inputs, full tiles).
-#define DG_MFMA_DMA(X, base, dt)                                                         \
-    X(base + 0, V_MFMA, dt, 0, 1, 256, 256, 32, 2, 4, 0, 0, 512, 4 * 2 * 32 * 512, 3)      \
-    X(base + 1, V_MFMA, dt, 1, 1, 256, 256, 32, 2, 4, 0, 0, 512, 4 * 2 * 32 * 512, 3)
-
 // Software-pipelined kernels (16-bit inputs, full tiles, 4 LDS stages of k = 32,
 // 32x32x16 MFMAs): 4 waves of 128 x 128 and 8 waves of 128 x 64.
 #define DG_MFMA_SP(X, base, dt)                                                          \
@@ -144,16 +134,14 @@ constexpr bool grouped_capable(int variant, int sched, int bm, int bn, int wm, i
     DG_MFMA_WIDE(X, 64, DT_BF16)                                 \
     DG_MFMA_PP(X, 68, DT_F16)                                    \
     DG_MFMA_PP(X, 70, DT_BF16)                                   \
-    DG_MFMA_DMA(X, 72, DT_F16)                                   \
-    DG_MFMA_DMA(X, 74, DT_BF16)                                  \
-    DG_MFMA_PP32(X, 76, DT_F16)                                  \
-    DG_MFMA_PP32(X, 78, DT_BF16)                                 \
-    DG_MFMA_SP(X, 80, DT_F16)                                    \
-    DG_MFMA_SP(X, 84, DT_BF16)                                   \
-    DG_MFMA_KG2(X, 88)                                           \
-    DG_MFMA_F32S3(X, 92)
+    DG_MFMA_PP32(X, 72, DT_F16)                                  \
+    DG_MFMA_PP32(X, 74, DT_BF16)                                 \
+    DG_MFMA_SP(X, 76, DT_F16)                                    \
+    DG_MFMA_SP(X, 80, DT_BF16)                                   \
+    DG_MFMA_KG2(X, 84)                                           \
+    DG_MFMA_F32S3(X, 88)
 
-constexpr int kMenuSize = 94;
+constexpr int kMenuSize = 90;
 
 // Fused epilogue ("Shared memory and tensor cores", section 13.10: bias,
 // activation, residual add or type cast applied to the accumulator before the

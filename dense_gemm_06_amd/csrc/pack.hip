@@ -64,11 +64,8 @@ int launch_pack(int elem_size, const PackJob& a, const PackJob& b, hipStream_t s
     const int64_t chunks_a = (int64_t)a.rows_p * a.cols_p / V;
     const int64_t total = chunks_a + (int64_t)b.rows_p * b.cols_p / V;
     const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>((total + 255) / 256, 8192));
-    if (elem_size == 2)
-        hipLaunchKernelGGL(pack_pad<uint16_t>, dim3(grid), dim3(256), 0, stream, a, b, chunks_a, total);
-    else
-        hipLaunchKernelGGL(pack_pad<float>, dim3(grid), dim3(256), 0, stream, a, b, chunks_a, total);
-    return 0;
+    if (elem_size == 2) return launch_status(pack_pad<uint16_t>, dim3(grid), dim3(256), stream, a, b, chunks_a, total);
+    return launch_status(pack_pad<float>, dim3(grid), dim3(256), stream, a, b, chunks_a, total);
 }
 
 }  // namespace dg

@@ -45,6 +45,12 @@ const MenuEntry kMenu[kMenuSize] = {
 #undef DG_ENTRY
 };
 
+bool extent_fits(int64_t rows, int64_t cols, int64_t ld) {
+    if (rows <= 0 || cols <= 0) return true;
+    const unsigned __int128 n = (unsigned __int128)(uint64_t)(rows - 1) * (uint64_t)ld + (uint64_t)cols;
+    return (n * 4) >> 62 == 0;
+}
+
 static const char* dtype_name(int dt) { return dt == 0 ? "fp32" : dt == 1 ? "fp16" : "bf16"; }
 static int elem_size(int dt) { return dt == DT_F32 ? 4 : 2; }
 
@@ -77,6 +83,13 @@ int validate(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int
     }
     if (ldc < minldc) {
         set_error("ldc = %lld is smaller than max(1, N) = %lld", (long long)ldc, (long long)minldc);
+        return GEMM_ERR_INVALID_VALUE;
+    }
+    // C's element range, (M - 1) * ldc + N elements of up to 4 bytes, must be
+    // representable (the overlap checks and the kernels' 64-bit offsets rely on it)
+    if (!extent_fits(M, N, ldc)) {
+        set_error("ldc = %lld: C's extent (M - 1) * ldc + N (M = %lld, N = %lld) does not fit in the address space",
+                  (long long)ldc, (long long)M, (long long)N);
         return GEMM_ERR_INVALID_VALUE;
     }
     if (opA == GEMM_OP_T) {
@@ -131,7 +144,6 @@ static double tile_efficiency_aligned(const MenuEntry& e) {
     // register-staged 256 x 256 165 us
     if (e.sched == 2) return 0.97;
     if (e.sched == 4) return 0.96;
-    if (e.sched == 3) return 0.85;
     if (e.sched == 5) return 0.90;  // problem-dependent: see plan()
     // the fp32 three-stage 256 x 128 tile: 2.8% faster per k than two resident 128 x 128
     // register-staged tiles per CU (fitted from 8192^2 x K, K = 256, 512 and 8192,
@@ -243,8 +255,7 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
             return GEMM_ERR_INVALID_VALUE;
         }
         if (want_sched && !schedule_enabled(want_sched)) {
-            set_error("schedule %d is switched off in this library (its kernel has not passed parity on the device)",
-                      want_sched);
+            set_error("schedule %d is not available: its kernel was removed from this library", want_sched);
             return GEMM_ERR_UNSUPPORTED;
         }
         want_pack = req->pack;

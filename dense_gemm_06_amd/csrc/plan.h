@@ -13,6 +13,9 @@ void set_error(const char* fmt, ...);
 void clear_error();
 const char* last_error();
 
+// True when a rows x cols matrix with leading dimension ld (elements of up to 4
+// bytes) spans fewer than 2^62 bytes, so 64-bit extents and offsets cannot overflow.
+bool extent_fits(int64_t rows, int64_t cols, int64_t ld);
 int validate(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
              int dtype);
 // ws_bytes: workspace available for split K or packing (0: neither).

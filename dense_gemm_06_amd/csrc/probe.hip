@@ -1,0 +1,103 @@
+// probe.hip -- calibration kernels for the HBM traffic counters (libdgprobe.so).
+//
+// Each kernel moves a known number of bytes with one of the memory forms the GEMM
+// kernels use, so that the value a profiler's FETCH_SIZE or WRITE_SIZE reports for
+// it gives the factor from counter to bytes for that form:
+//   kind 0  reads with global_load_lds_dwordx4 in the pattern of the software-
+//           pipelined kernel's A copies: 64-byte row segments (k-tiles of 32
+//           16-bit elements) of 256-row panels, four lanes per segment, 16 rows per
+//           1 KB copy, the k-tiles of a panel walked in order;
+//   kind 1  reads with global_load_dwordx4, 64 lanes covering 1 KB contiguously;
+//   kind 2  writes with global_store_dwordx4, 64 lanes covering 1 KB contiguously
+//           (the staged epilogue's whole-row stores).
+// Every byte is touched exactly once. This library is a measurement tool: the GEMM
+// library neither links nor calls it.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "launch.h"
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kRowElems = 4096;               // 16-bit elements per source row (8 KB)
+constexpr int64_t kPanelBytes = 256LL * 8192;  // one workgroup's 256 rows
+
+__global__ __launch_bounds__(256) void probe_read_lds(const uint16_t* __restrict__ src, uint32_t* __restrict__ out) {
+    __shared__ __attribute__((aligned(1024))) uint16_t tile[256 * 32];  // 16 KB: one k-tile of the panel
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint16_t* panel = src + (size_t)blockIdx.x * 256 * kRowElems;
+    const uint32_t base = (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)tile);
+    uint32_t acc = 0;
+    for (int kt = 0; kt < kRowElems / 32; ++kt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int b = wave * 4 + i;                 // 1 KB copy number 0..15
+            const int row = b * 16 + (lane >> 2);       // 16 rows of 64 bytes per copy
+            const uint16_t* p = panel + (size_t)row * kRowElems + kt * 32 + (lane & 3) * 8;
+            __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)p,
+                                             (__attribute__((address_space(3))) void*)(uintptr_t)(base + b * 1024u),
+                                             16, 0, 0);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        acc ^= reinterpret_cast<const uint32_t*>(tile)[tid * 16 + (kt & 15)];
+        __syncthreads();
+    }
+    if (acc == 0x9E3779B9u) out[blockIdx.x] = acc;  // keeps the loads; out has one slot per workgroup
+}
+
+__global__ __launch_bounds__(256) void probe_read_vec(const u32x4* __restrict__ src, int64_t n16,
+                                                      uint32_t* __restrict__ out) {
+    uint32_t acc = 0;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256) {
+        const u32x4 v = src[i];
+        acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
+    if (acc == 0x9E3779B9u) out[blockIdx.x] = acc;
+}
+
+__global__ __launch_bounds__(256) void probe_write(u32x4* __restrict__ dst, int64_t n16) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256)
+        dst[i] = u32x4{(uint32_t)i, 1u, 2u, 3u};
+}
+
+}  // namespace
+
+extern "C" {
+
+// Launch probe `kind` over `bytes` on `stream`. kind 0: src holds bytes / 8192 rows of
+// 4096 16-bit elements and bytes must be a positive multiple of 2 MiB (256 rows); kind
+// 1: bytes a positive multiple of 4096; both need dst to hold 4 bytes per workgroup
+// (dg_probe_out_bytes). kind 2: writes bytes (a positive multiple of 4096) to dst; src
+// is unused. Returns 0, 1 for invalid arguments, or the hipError_t of the launch.
+int64_t dg_probe_out_bytes(int kind, int64_t bytes) {
+    if (kind == 0) return bytes / kPanelBytes * 4;
+    if (kind == 1) return 4 * std::min<int64_t>(bytes / 4096, 16384);
+    return 0;
+}
+
+int dg_probe_traffic(int kind, const void* src, void* dst, int64_t bytes, void* stream) {
+    hipStream_t s = (hipStream_t)stream;
+    if (bytes <= 0 || dst == nullptr) return 1;
+    if (kind == 0) {
+        if (bytes % kPanelBytes != 0 || src == nullptr || bytes / kPanelBytes >= (1 << 30)) return 1;
+        return dg::launch_status(probe_read_lds, dim3((unsigned)(bytes / kPanelBytes)), dim3(256), s,
+                                 static_cast<const uint16_t*>(src), static_cast<uint32_t*>(dst));
+    } else if (kind == 1) {
+        if (bytes % 4096 != 0 || src == nullptr) return 1;
+        const unsigned grid = (unsigned)std::min<int64_t>(bytes / 4096, 16384);
+        return dg::launch_status(probe_read_vec, dim3(grid), dim3(256), s, static_cast<const u32x4*>(src), bytes / 16,
+                                 static_cast<uint32_t*>(dst));
+    } else if (kind == 2) {
+        if (bytes % 4096 != 0) return 1;
+        const unsigned grid = (unsigned)std::min<int64_t>(bytes / 4096, 16384);
+        return dg::launch_status(probe_write, dim3(grid), dim3(256), s, static_cast<u32x4*>(dst), bytes / 16);
+    }
+    return 1;
+}
+
+}  // extern "C"

@@ -48,8 +48,7 @@ int launch_splitk_reduce(const float* work, int S, int64_t slice, int64_t work_l
                          int64_t ldc, const Epilogue& ep, hipStream_t stream) {
     const int64_t total = (int64_t)M * ((N + 3) / 4);
     const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>((total + 255) / 256, 4096));
-    hipLaunchKernelGGL(splitk_reduce, dim3(grid), dim3(256), 0, stream, work, S, slice, work_ld, M, N, C, ldc, ep);
-    return 0;
+    return launch_status(splitk_reduce, dim3(grid), dim3(256), stream, work, S, slice, work_ld, M, N, C, ldc, ep);
 }
 
 }  // namespace dg

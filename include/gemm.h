@@ -89,13 +89,12 @@ typedef struct gemm_config {
     int32_t grid;      /* out: workgroups launched (tiles_m * tiles_n) */
     int32_t kernel_id; /* out: index into the library's kernel menu */
     int32_t schedule;  /* in/out: 0 any; 1 register-staged double buffer (any shape); 2 ping-pong
-                          with direct global->LDS copies on 16x16x32 MFMAs; 3 software-pipelined
-                          with direct global->LDS copies (switched off: requests for it return
-                          GEMM_ERR_UNSUPPORTED); 4 ping-pong on 32x32x16 MFMAs; 5 software-
-                          pipelined 32x32x16 with direct global->LDS copies, 4 waves of 128 x
-                          128 or 8 of 128 x 64 (2-5: MFMA, 16-bit inputs, 16-byte aligned
-                          operands, any M, and any N for column-major B or N a multiple of
-                          8 for row-major B; 2-4: K a multiple of 32; 5: K a multiple of 8;
+                          with direct global->LDS copies on 16x16x32 MFMAs; 3 not available
+                          (requests for it return GEMM_ERR_UNSUPPORTED); 4 ping-pong on 32x32x16
+                          MFMAs; 5 software-pipelined 32x32x16 with direct global->LDS copies,
+                          4 waves of 128 x 128 or 8 of 128 x 64 (2, 4, 5: MFMA, 16-bit inputs,
+                          16-byte aligned operands, any M, and any N for column-major B or N a
+                          multiple of 8 for row-major B; 2, 4: K a multiple of 32; 5: K a multiple of 8;
                           4 stores the plain fp32 accumulator only); 6 register-staged with three LDS
                           stages and fragments read half a k-tile ahead (fp32 256 x 128
                           tiles, any shape, K not split) */
@@ -116,6 +115,15 @@ typedef struct gemm_config {
 /*
  * gemm -- C = A @ B with row-major A (M x K), row-major B (K x N), row-major fp32 C.
  * Exactly gemm_ex(GEMM_OP_N, GEMM_OP_N, ..., cfg = NULL, stream).
+ *
+ * The operation is the one "Shared memory and tensor cores" sets up in section
+ * 13.1 (C = A @ B for a square problem, whose DRAM traffic the block tiling of
+ * sections 13.2-13.3 cuts) with the tensor-core contract of section 13.8 and the
+ * WMMA template of section 13.9 (16-bit inputs, products exact, sums in fp32,
+ * a float C). Arguments: M, N, K >= 0 (elements); A, B, C device pointers owned
+ * by the caller; lda, ldb, ldc leading dimensions in elements; dtype a
+ * gemm_dtype; stream a hipStream_t (NULL: the default stream). Returns GEMM_OK
+ * after enqueueing, or a gemm_status with nothing enqueued.
  */
 int gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
          float* C, int64_t ldc, int dtype, void* stream);
@@ -126,6 +134,13 @@ int gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void
  * opB = GEMM_OP_T reads B column-major (B(k,j) = B[j*ldb + k]). cfg = NULL runs
  * the heuristic; otherwise its "in" fields restrict the choice (a request no
  * compiled kernel satisfies returns GEMM_ERR_UNSUPPORTED).
+ *
+ * The operand layouts follow the learn-cutedsl README, section 2.4 "Layout and
+ * Linear indexing": row-major storage has strides (ld, 1), column-major (1, ld),
+ * and GEMM libraries commonly take B column-major (B stored row-major but
+ * transposed), the NN / NT / TN / TT naming. cfg (host memory, read during the
+ * call only, may be NULL) plays the role of the option / Opts a caller of the
+ * pages' launch helpers passes to pick a kernel. Errors as for gemm.
  */
 int gemm_ex(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
             int64_t ldb, float* C, int64_t ldc, int dtype, const gemm_config* cfg, void* stream);
@@ -136,6 +151,16 @@ int gemm_ex(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A, in
  * operand addresses (only their alignment is used), num_cus the compute-unit
  * count and arch the device architecture name (e.g. "gfx950"). Applies the same
  * validation as gemm_ex except pointer checks; fills *out on success.
+ *
+ * This is the launch heuristic in the role of gpu_opt_choice, "GPU architecture
+ * and mapping kernels", section 12.9 "Choosing a launch configuration" (and its
+ * exercise that asks for a minimum block count that fills the machine): a pure
+ * function of the shape, layouts, alignment and device, so it can be tested
+ * without a GPU. request (host memory, may be NULL) restricts the choice as
+ * gemm_ex's cfg does; out (host memory) receives the launch. Returns
+ * GEMM_ERR_NULL_POINTER for out == NULL, else the status gemm_ex would return
+ * for these arguments before launching (GEMM_ERR_DEVICE for an arch other than
+ * gfx950).
  */
 int gemm_plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
               int dtype, uintptr_t a_addr, uintptr_t b_addr, uintptr_t c_addr, int num_cus, const char* arch,
@@ -273,10 +298,23 @@ int gemm_menu_entry(int index, int* variant, int* dtype, int* opb, gemm_config* 
  * of HIP device `device`. Returns GEMM_ERR_DEVICE if it cannot be queried. */
 int gemm_device_info(int device, int* num_cus, char* arch, int len);
 
-/* Static description of a gemm_status value. */
+/*
+ * Status reporting in the manner of the pages' GPU runtime, "GPU architecture
+ * and mapping kernels", section 12.11 "Running on a real GPU: cuda.py": every
+ * runtime status is checked and a nonzero one is turned into an error that says
+ * what failed; and in the spirit of "Shared memory and tensor cores", section
+ * 13.5, where an error is to say what is unsupported and why.
+ *
+ * gemm_status_string -- a static, NUL-terminated description of a gemm_status
+ * value ("unknown gemm_status" for any other int); never NULL, owned by the
+ * library, valid for the life of the process.
+ */
 const char* gemm_status_string(int status);
 
-/* Thread-local description of the last failure on this thread ("" after success). */
+/* gemm_last_error -- a description of the last failure of a call made on this
+ * thread: which argument or runtime call was refused and why ("" after a call
+ * that succeeded). The string is thread-local and owned by the library; it stays
+ * valid until the next library call on the same thread. */
 const char* gemm_last_error(void);
 
 #ifdef __cplusplus

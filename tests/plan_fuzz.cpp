@@ -109,10 +109,7 @@ static void check_plan(int opB, int64_t M, int64_t N, int64_t K, int64_t lda, in
               "direct copies on unaligned operands");
         CHECK(K > 0 && K % 8 == 0, "direct copies with K = %lld", (long long)K);
         if (e.sched != 5) CHECK(K % e.bk == 0, "schedule %d with K = %lld", e.sched, (long long)K);
-        if (e.sched == 3)
-            CHECK(M % e.bm == 0 && N % e.bn == 0, "whole-tile schedule %d on %lld x %lld", e.sched, (long long)M,
-                  (long long)N);
-        else if (opB == 0)
+        if (opB == 0)
             CHECK(N % e.bn == 0 || N % 8 == 0, "row-major B edge tile with N = %lld", (long long)N);
     }
     if (req) {

@@ -51,7 +51,7 @@ def test_status_strings():
 
 def test_menu_is_complete():
     menu = dg.gemm_menu()
-    assert len(menu) == dg.library().gemm_menu_size() == 94
+    assert len(menu) == dg.library().gemm_menu_size() == 90
     seen = set()
     for e in menu:
         assert e["lds_bytes"] <= 160 * 1024
@@ -68,7 +68,7 @@ def test_menu_is_complete():
                 for vec in (0, 1):
                     tiles = {(bm, bn) for (v, d, o, ve, bm, bn) in seen if (v, d, o, ve) == (variant, dtype, opb, vec)}
                     assert len(tiles) >= 2, (variant, dtype, opb, vec)
-    assert dg.library().gemm_menu_entry(94, None, None, None, None) == dg.GEMM_ERR_INVALID_VALUE
+    assert dg.library().gemm_menu_entry(90, None, None, None, None) == dg.GEMM_ERR_INVALID_VALUE
 
 
 def plan(M, N, K, dtype="f32", op_b="N", lda=None, ldb=None, ldc=None, a=0, b=0, c=0, cus=256, arch="gfx950",
@@ -184,8 +184,10 @@ def test_plan_three_stage_fp32():
     assert st == dg.GEMM_ERR_UNSUPPORTED
 
 
-def test_plan_never_selects_switched_off_schedule():
-    """Schedule 3 is compiled but switched off: never chosen, and a forced request is refused."""
+def test_plan_never_selects_removed_schedule():
+    """Schedule 3 (a kernel that faulted on the device) was removed: no menu entry has it,
+    it is never chosen, and a forced request is refused."""
+    assert all(e["schedule"] != 3 for e in dg.gemm_menu())
     for dtype in ("f16", "bf16"):
         for op_b in "NT":
             for shape in ((4096, 4096, 4096), (256, 512, 32), (8192, 8192, 8192)):
@@ -193,7 +195,7 @@ def test_plan_never_selects_switched_off_schedule():
                 assert st == 0 and c.schedule != 3
             st, _ = plan(4096, 4096, 4096, dtype, op_b, req=dg.request(schedule=3))
             assert st == dg.GEMM_ERR_UNSUPPORTED
-    assert "switched off" in dg.gemm_last_error()
+    assert "removed" in dg.gemm_last_error()
 
 
 def test_plan_fills_the_machine():
@@ -248,6 +250,9 @@ def test_plan_forced_configurations():
     (dict(M=4, N=4, K=4, ldb=3), dg.GEMM_ERR_INVALID_VALUE, "ldb"),
     (dict(M=4, N=4, K=8, op_b="T", ldb=7), dg.GEMM_ERR_INVALID_VALUE, "column-major"),
     (dict(M=4, N=4, K=4, ldc=3), dg.GEMM_ERR_INVALID_VALUE, "ldc"),
+    (dict(M=4, N=4, K=4, ldc=1 << 61), dg.GEMM_ERR_INVALID_VALUE, "extent"),
+    (dict(M=1 << 29, N=4, K=4, ldc=(1 << 62) // (1 << 29)), dg.GEMM_ERR_INVALID_VALUE, "extent"),
+    (dict(M=4, N=4, K=4, ldc=(1 << 63) - 1), dg.GEMM_ERR_INVALID_VALUE, "extent"),
     (dict(M=4, N=4, K=4, arch="gfx942"), dg.GEMM_ERR_DEVICE, "gfx942"),
     (dict(M=4, N=4, K=4, cus=0), dg.GEMM_ERR_INVALID_VALUE, "compute-unit"),
     (dict(M=1 << 30, N=4, K=4), dg.GEMM_ERR_UNSUPPORTED, "2^30"),
@@ -533,6 +538,11 @@ def test_epilogue_rejections_before_device():
     assert "R overlaps C" in dg.gemm_last_error()
     # R == C with another leading dimension is not the in-place form
     assert call(dg.epilogue(beta=1.0, R=C, ldr=65)) == dg.GEMM_ERR_INVALID_VALUE
+    # a leading dimension of R whose extent overflows 64 bits is refused, not wrapped
+    # into a range that could slip past the overlap checks
+    for ldr in ((1 << 63) - 1, 1 << 57):
+        assert call(dg.epilogue(beta=1.0, R=R, ldr=ldr)) == dg.GEMM_ERR_INVALID_VALUE
+        assert "extent" in dg.gemm_last_error()
     assert call(dg.epilogue(bias=C + 64, alpha=2.0)) == dg.GEMM_ERR_INVALID_VALUE
     assert "bias" in dg.gemm_last_error()
     # the workspace must not overlap the epilogue operands either

@@ -167,6 +167,21 @@ def test_epilogue_software_pipelined_edge_tiles(waves_n, out):
     assert epilogue_error(got, ref, Dp, "f16", out) <= 1.0
 
 
+@pytest.mark.parametrize("shape,dtype,op_b", [((300, 264, 96), "f16", "N"), ((513, 777, 96), "bf16", "T"),
+                                              ((40, 8, 32), "bf16", "N"), ((600, 1, 128), "f16", "T")])
+@pytest.mark.parametrize("out", ["f32", "f16", "bf16"])
+def test_epilogue_ping_pong_edge_tiles(shape, dtype, op_b, out):
+    """The LDS-staged epilogue of the ping-pong kernel (schedule 2) on edge tiles (M
+    and N not multiples of 256; row-major B with N a multiple of 8): rows >= M and
+    columns >= N of the staged tile must not be stored, with bias, GELU, a residual
+    (beta != 0) and every output type."""
+    M, N, K = shape
+    ops = gi.make_operands(M, N, K, dtype, "normal", seed=M + N, op_b=op_b)
+    got, ref, Dp, plan = run_epi(ops, out, act="gelu_tanh", cfg=dg.request(schedule=2))
+    assert plan.schedule == 2 and plan.tiles_m == -(-M // 256) and plan.tiles_n == -(-N // 256)
+    assert epilogue_error(got, ref, Dp, dtype, out) <= 1.0
+
+
 @pytest.mark.parametrize("op_b", ["N", "T"])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_epilogue_three_stage_fp32(op_b, out):
