@@ -13,6 +13,11 @@ launch stream around the K launches. One kernel runs per step and the launches
 follow each other with no gap, so the step time is also the kernel's average
 duration (the roofline figure). Inputs are resident in HBM before timing starts.
 
+Only the W + K headline launches run the headline kernel in the default command
+(the fused epilogue, the per-launch distribution and the clock probe, which
+launch it many more times, run only with --extended), so a kernel trace of the
+default command averages exactly those launches.
+
 CPU baseline: the oracle (plain fp64 triple loop, OpenMP) timed on the host
 cores on a bounded sample of the same problem (its first r rows; about 10-20 s
 of CPU work), reported as TFLOP/s of the sample.
@@ -62,6 +67,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="time only the headline problem")
     p.add_argument("--only", default=None, help="time only this benchmark problem, or grouped workload (for profiling)")
+    p.add_argument("--force", default=None, metavar="KEY=V,...",
+                   help="with --only: force a configuration (gemm_config input fields, e.g. variant=1 or "
+                        "schedule=5,waves_n=2), for profiling a kernel the heuristic does not pick")
     p.add_argument("--with-workspace", action="store_true",
                    help="with --only: pass a workspace (the heuristic may split K or pack the operands)")
     p.add_argument("--extended", action="store_true",
@@ -90,7 +98,7 @@ def device_problem(name, seed=0):
 WORKSPACE_CAP = 256 << 20   # workspace offered to split-K runs
 
 
-def time_problem(name, steps, warmup, workspace=False):
+def time_problem(name, steps, warmup, workspace=False, force=None):
     """Warm up, then time exactly `steps` calls with HIP events on the launch stream.
 
     workspace=True runs gemm_ex_workspace with up to WORKSPACE_CAP bytes (the
@@ -104,14 +112,15 @@ def time_problem(name, steps, warmup, workspace=False):
     args = (dg.GEMM_OP_N, dg.OP_CODE[ops.op_b], ops.M, ops.N, ops.K, A.data_ptr(), ops.lda, B.data_ptr(), ops.ldb,
             C.data_ptr(), ops.N, dg.DTYPE_CODE[ops.dtype])
     cus, arch = dg.gemm_device_info(0)
+    req = dg.request(**force) if force else None
     _, cfg = dg.gemm_plan_workspace(args[0], args[1], ops.M, ops.N, ops.K, ops.lda, ops.ldb, ops.N, args[-1],
                                     A.data_ptr(), B.data_ptr(), C.data_ptr(), cus, arch,
-                                    WORKSPACE_CAP if workspace else 0)
+                                    WORKSPACE_CAP if workspace else 0, req)
     if workspace and cfg.workspace_bytes > 0:
         W = torch.empty(cfg.workspace_bytes // 4, dtype=torch.float32, device="cuda")
-        call = lambda: dg.gemm_ex_workspace(*args, None, W.data_ptr(), cfg.workspace_bytes, s)
+        call = lambda: dg.gemm_ex_workspace(*args, req, W.data_ptr(), cfg.workspace_bytes, s)
     else:
-        call = lambda: dg.gemm_ex(*args, None, s)
+        call = lambda: dg.gemm_ex(*args, req, s)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -436,7 +445,13 @@ def main():
         print(json.dumps({k: (v.as_dict() if k == "cfg" else v) for k, v in r.items()}), flush=True)
         return
     headline = a.only or "c4_f16_4096"
-    main_res = time_problem(headline, a.steps, a.warmup, workspace=bool(a.only and a.with_workspace))
+    force = None
+    if a.force:
+        if not a.only:
+            print("--force needs --only", file=sys.stderr)
+            sys.exit(2)
+        force = {k: int(v) for k, v in (kv.split("=") for kv in a.force.split(","))}
+    main_res = time_problem(headline, a.steps, a.warmup, workspace=bool(a.only and a.with_workspace), force=force)
     # the fused-epilogue variant right after the headline, in the same thermal state
     # (the chip's clock drifts by 10-20% over a run of heavy launches)
     fe = None
