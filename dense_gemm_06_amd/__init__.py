@@ -1,7 +1,7 @@
 """Python binding of the MI355X dense GEMM library (libdensegemm.so).
 
 The functions mirror the C ABI in include/gemm.h one to one (gemm, gemm_ex,
-gemm_ex_workspace, gemm_ex_epilogue, gemm_plan, gemm_plan_workspace, gemm_grouped, gemm_grouped_plan, gemm_strided_batched,
+gemm_ex_workspace, gemm_ex_noalloc, gemm_ex_epilogue, gemm_plan, gemm_plan_workspace, gemm_grouped, gemm_grouped_plan, gemm_strided_batched,
 gemm_menu_size / gemm_menu_entry, gemm_device_info, gemm_status_string,
 gemm_last_error) and only marshal arguments: every step of the product runs in
 the library's HIP kernels. A nonzero status raises
@@ -32,6 +32,7 @@ GEMM_ERR_UNSUPPORTED = 3
 GEMM_ERR_DEVICE = 4
 GEMM_ERR_LAUNCH = 5
 GEMM_VARIANT_AUTO, GEMM_VARIANT_LDS, GEMM_VARIANT_MFMA = 0, 1, 2
+GEMM_NOALLOC_SCRATCH_BYTES = 32 << 20   # the fixed scratch of gemm_ex_noalloc (include/gemm.h)
 
 DTYPE_CODE = {"f32": GEMM_F32, "f16": GEMM_F16, "bf16": GEMM_BF16}
 OP_CODE = {"N": GEMM_OP_N, "T": GEMM_OP_T}
@@ -141,6 +142,8 @@ def _load():
     lib.gemm_plan.restype = i32
     lib.gemm_ex_workspace.argtypes = [i32, i32, i64, i64, i64, vp, i64, vp, i64, vp, i64, i32, cfgp, vp, i64, vp]
     lib.gemm_ex_workspace.restype = i32
+    lib.gemm_ex_noalloc.argtypes = [i32, i32, i64, i64, i64, vp, i64, vp, i64, vp, i64, i32, cfgp, vp]
+    lib.gemm_ex_noalloc.restype = i32
     epip = ctypes.POINTER(gemm_epilogue)
     lib.gemm_plan_workspace.argtypes = [i32, i32, i64, i64, i64, i64, i64, i64, i32, ctypes.c_size_t,
                                         ctypes.c_size_t, ctypes.c_size_t, i32, ctypes.c_char_p, i64, epip, cfgp,
@@ -213,6 +216,17 @@ def gemm_ex_workspace(opA, opB, M, N, K, A, lda, B, ldb, C, ldc, dtype, cfg: gem
                                    ctypes.byref(cfg) if cfg is not None else None, workspace, workspace_bytes, stream)
     if check:
         _check(st, "gemm_ex_workspace")
+    return st
+
+
+def gemm_ex_noalloc(opA, opB, M, N, K, A, lda, B, ldb, C, ldc, dtype, cfg: gemm_config | None = None,
+                    stream=None, check=True) -> int:
+    """gemm_ex_workspace on the library's fixed scratch array (no allocation; calls that
+    overlap on one GPU race on it)."""
+    st = _load().gemm_ex_noalloc(opA, opB, M, N, K, A, lda, B, ldb, C, ldc, dtype,
+                                 ctypes.byref(cfg) if cfg is not None else None, stream)
+    if check:
+        _check(st, "gemm_ex_noalloc")
     return st
 
 

@@ -25,7 +25,8 @@ PROBE_LIB = os.path.join(HERE, "libdgprobe.so")
 ARCH = "gfx950"
 
 DEVICE_SOURCES = ["inst_lds_f32.hip", "inst_lds_f16.hip", "inst_lds_bf16.hip",
-                  "inst_mfma_f32.hip", "inst_mfma_f16.hip", "inst_mfma_bf16.hip", "reduce.hip", "pack.hip"]
+                  "inst_mfma_f32.hip", "inst_mfma_f16.hip", "inst_mfma_bf16.hip", "reduce.hip", "pack.hip",
+                  "noalloc.hip"]
 HOST_SOURCES = ["plan.cpp", "gemm_api.cpp"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function"]

@@ -41,7 +41,8 @@
  *    no C++ exception crosses this interface.
  *  - State: the library allocates no device memory and keeps no workspace; the
  *    only state is a per-device cache of (compute-unit count, architecture)
- *    filled on first use. All entry points are thread-safe.
+ *    filled on first use, and the fixed scratch array of gemm_ex_noalloc. All
+ *    entry points are thread-safe (gemm_ex_noalloc: see its own rule).
  */
 #ifndef DENSE_GEMM_06_AMD_GEMM_H
 #define DENSE_GEMM_06_AMD_GEMM_H
@@ -191,6 +192,25 @@ int gemm_plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, in
 int gemm_ex_workspace(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                       const void* B, int64_t ldb, float* C, int64_t ldc, int dtype, const gemm_config* cfg,
                       void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * gemm_ex_noalloc -- gemm_ex_workspace for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the workspace is a fixed scratch array of
+ * GEMM_NOALLOC_SCRATCH_BYTES inside the library, one copy per GPU, held until the
+ * process ends. The call allocates and frees nothing. Plans, results and errors
+ * are those of gemm_ex_workspace with a workspace of that size (split K or
+ * packing only when they fit in it); a forced split or packing that needs more
+ * returns GEMM_ERR_INVALID_VALUE with a message that says so. Every call on one
+ * GPU shares that GPU's array and the array keeps the last call's contents, so
+ * calls that overlap in time on one GPU (several streams, or threads without an
+ * order between their calls) race and must not be made; calls ordered on one
+ * stream are safe.
+ */
+#define GEMM_NOALLOC_SCRATCH_BYTES ((int64_t)32 << 20)
+
+int gemm_ex_noalloc(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                    int64_t ldb, float* C, int64_t ldc, int dtype, const gemm_config* cfg, void* stream);
 
 /*
  * Fused epilogue ("Shared memory and tensor cores", section 13.10: apply a bias,

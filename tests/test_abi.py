@@ -35,7 +35,8 @@ def test_header_symbols_exported():
     assert set(names) == {"gemm", "gemm_ex", "gemm_plan", "gemm_menu_size", "gemm_menu_entry",
                           "gemm_device_info", "gemm_status_string", "gemm_last_error",
                           "gemm_grouped", "gemm_grouped_plan", "gemm_strided_batched",
-                          "gemm_ex_workspace", "gemm_plan_workspace", "gemm_ex_epilogue"}
+                          "gemm_ex_workspace", "gemm_plan_workspace", "gemm_ex_epilogue",
+                          "gemm_ex_noalloc"}
     lib = dg.library()
     for n in names:
         assert hasattr(lib, n), n
