@@ -32,6 +32,25 @@ __device__ __forceinline__ void vm_wait(int n) {
     }
 }
 
+// The first v (0..8) of a chunk of eight 16-bit elements, the rest zero, from w =
+// the 8 elements that END at the chunk's last valid one (element j of w is element
+// j - (8 - v) of the chunk): w shifted down by 8 - v elements as a 128-bit value.
+__device__ __forceinline__ u32x4 keep_first8(u32x4 w, int v) {
+    if (v >= 8) return w;
+    if (v <= 0) return u32x4{0, 0, 0, 0};
+    const uint64_t lo = ((uint64_t)w[1] << 32) | w[0], hi = ((uint64_t)w[3] << 32) | w[2];
+    const int s = 16 * (8 - v);  // 16 .. 112 bits
+    uint64_t olo, ohi;
+    if (s >= 64) {
+        olo = hi >> (s - 64);
+        ohi = 0;
+    } else {
+        olo = (lo >> s) | (hi << (64 - s));
+        ohi = hi >> s;
+    }
+    return u32x4{(uint32_t)olo, (uint32_t)(olo >> 32), (uint32_t)ohi, (uint32_t)(ohi >> 32)};
+}
+
 // Software-pipelined MFMA kernel for 16-bit inputs on 256 x 256 tiles (K a multiple
 // of 8, 16-byte aligned operands; edge tiles in M, and in N for column-major B or for
 // N a multiple of 8, and a partial last k-tile, are handled as described below).
@@ -66,7 +85,20 @@ __device__ __forceinline__ void vm_wait(int n) {
 // a wave tile at a time (64 rows), and leave as whole rows: each store instruction
 // writes 2 (NW = 4) or 4 (NW = 8) rows of the wave tile, contiguous in C. A fused
 // epilogue (ep.kind != 0) is applied on the way out.
-template <int DT, int OPB, int NW>
+//
+// REG = true is the same kernel for operands that are only aligned to their element
+// (rows at any 2-byte offset) and for any K >= 8 and any N >= 8: each 16-byte chunk
+// a lane owns goes global -> registers -> LDS instead of straight into LDS. Every
+// chunk is exactly one 16-byte load, from an address inside the row (a chunk that
+// straddles K, or N for a row-major B, is loaded as the 8 elements that end at the
+// row's last valid one and shifted into place, zero-filled, when written; a chunk
+// wholly past the end is loaded from the row start and written as zeros), so the
+// load counter always counts 2*CPB loads per tile and wave. Tile t+1 is written to
+// its stage during step (t, 0), before the barrier that publishes it, from registers
+// loaded one iteration earlier; the load of tile t+2 then reuses them. The LDS
+// layout, the fragment reads, the MFMAs and the epilogue are those of the direct-copy
+// form.
+template <int DT, int OPB, int NW, bool REG>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void mfma32_sp(
     GemmArgs g) {
     static_assert(NW == 4 || NW == 8, "waves");
@@ -109,6 +141,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     const uint16_t* srcA[CPB];
     const uint16_t* srcB[CPB];
     int kcA[CPB], kcB[CPB];
+    int nvB[CPB];  // REG, row-major B: columns of the lane's chunk inside N (0..8)
 #pragma unroll
     for (int i = 0; i < CPB; ++i) {
         const int b = wave * CPB + i;
@@ -122,7 +155,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
             const int krow = b * 2 + (lane >> 5);
             const int col = n0 + (((lane & 31) ^ nmaj32_swz(krow)) << 3);
             kcB[i] = krow;
-            srcB[i] = B + (size_t)krow * g.ldb + (col < g.N ? col : 0);
+            if constexpr (REG) {
+                // a chunk that straddles N is read from the row's last 8 columns, one
+                // wholly past N from column 0 (N >= 8); the write shifts or zeroes it
+                const int v = g.N - col;
+                nvB[i] = v < 0 ? 0 : (v > 8 ? 8 : v);
+                srcB[i] = B + (size_t)krow * g.ldb + (v >= 8 ? col : v > 0 ? g.N - 8 : 0);
+            } else {
+                srcB[i] = B + (size_t)krow * g.ldb + (col < g.N ? col : 0);
+            }
         }
     }
     const size_t kstepB = OPB == 0 ? (size_t)BK * g.ldb : (size_t)BK;  // elements per k-tile
@@ -168,6 +209,62 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
                 *reinterpret_cast<u32x4*>(sb + idx * 16) = u32x4{0, 0, 0, 0};
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    };
+
+    // ---- register staging (REG). Tile t's chunks: ra (A) and rb (B), one 16-byte load
+    // each; written to stage t & 3 at the LDS position the direct copy would fill.
+    u32x4 ra[CPB], rb[CPB];
+    const bool nedge = OPB == 0 && n0 + BN > g.N;  // a row-major B tile that crosses N
+    auto ld16 = [](const uint16_t* p) {
+        u32x4 r;
+        __builtin_memcpy(&r, p, 16);  // one global_load_dwordx4; gfx950 serves under-aligned ones
+        return r;
+    };
+    // chunk c of tile t: c < CPB is A chunk c, else B chunk c - CPB. TAIL: t is the
+    // partial last k-tile.
+    auto load_reg = [&](int t, int c, auto tail_tag) {
+        constexpr bool TAIL = decltype(tail_tag)::value;
+        if (c < CPB) {
+            const uint16_t* src = srcA[c] + (size_t)t * BK;
+            if (TAIL) {
+                const int v = g.K - (t * BK + kcA[c]);
+                if (v < 8) src = srcA[c] - kcA[c] + (v > 0 ? g.K - 8 : 0);
+            }
+            ra[c] = ld16(src);
+        } else {
+            const int i = c - CPB;
+            const uint16_t* src = srcB[i] + (size_t)t * kstepB;
+            if (TAIL) {
+                if (OPB == 1) {
+                    const int v = g.K - (t * BK + kcB[i]);
+                    if (v < 8) src = srcB[i] - kcB[i] + (v > 0 ? g.K - 8 : 0);
+                } else if (t * BK + kcB[i] >= g.K) {
+                    src = srcB[i] + (size_t)(g.K - 1 - kcB[i]) * g.ldb;  // row K - 1, written as zeros
+                }
+            }
+            rb[i] = ld16(src);
+        }
+    };
+    auto write_reg = [&](int t, int c, auto tail_tag) {
+        constexpr bool TAIL = decltype(tail_tag)::value;
+        u32x4 v;
+        uint32_t addr;
+        if (c < CPB) {
+            v = ra[c];
+            if (TAIL) v = keep_first8(v, g.K - (t * BK + kcA[c]));
+            addr = dstA + (uint32_t)(t & 3) * STAGE_BYTES + (uint32_t)c * 1024u;
+        } else {
+            const int i = c - CPB;
+            v = rb[i];
+            if (OPB == 1) {
+                if (TAIL) v = keep_first8(v, g.K - (t * BK + kcB[i]));
+            } else {
+                if (nedge) v = keep_first8(v, nvB[i]);
+                if (TAIL && t * BK + kcB[i] >= g.K) v = u32x4{0, 0, 0, 0};
+            }
+            addr = dstB + (uint32_t)(t & 3) * STAGE_BYTES + (uint32_t)i * 1024u;
+        }
+        *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(DG_LDS_AT(addr + (uint32_t)lane * 16u)) = v;
     };
 
     // ---- fragment addresses (bytes within a stage).
@@ -268,6 +365,86 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
         }
     };
 
+    constexpr std::true_type yes{};
+    constexpr std::false_type no{};
+    if constexpr (REG) {
+    // One step of the register-staged form: as `step`, with no copies; with a write
+    // tag (tile wt exists), the second half of the step first waits for this wave's
+    // loads of tile wt, then writes one chunk of it after each MFMA and, with a load
+    // tag (tile lt exists), loads the same chunk of tile lt into the freed registers.
+    auto step_reg = [&](const Frags& cur, Frags& nxt, int rst, int rks, int wt, int lt, auto write_tag,
+                        auto load_tag) {
+        constexpr int W = decltype(write_tag)::value, L = decltype(load_tag)::value;  // 0 none, 1 full, 2 tail
+#pragma unroll
+        for (int k = 0; k < NM; ++k) {
+            mfma(cur, k / SJ, k % SJ);
+            if (2 * k < NREAD) read_one(nxt, rst, rks, 2 * k);
+            if (2 * k + 1 < NREAD) read_one(nxt, rst, rks, 2 * k + 1);
+            if constexpr (W != 0) {
+                if (k >= NM / 2) {
+                    const int c = k - NM / 2;  // chunk 0 .. 2*CPB - 1
+                    if (c == 0) vm_wait_n<0>();
+                    write_reg(wt, c, std::integral_constant<bool, W == 2>{});
+                    if constexpr (L != 0) load_reg(lt, c, std::integral_constant<bool, L == 2>{});
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    constexpr std::integral_constant<int, 0> none{};
+    constexpr std::integral_constant<int, 1> full{};
+    constexpr std::integral_constant<int, 2> part{};
+    // prologue: tile 0 loaded, written to stage 0; tile 1 loaded; step (0, 0)
+    // fragments read.
+    if (ktail && nk == 1) {
+#pragma unroll
+        for (int c = 0; c < 2 * CPB; ++c) load_reg(0, c, yes);
+        vm_wait_n<0>();
+#pragma unroll
+        for (int c = 0; c < 2 * CPB; ++c) write_reg(0, c, yes);
+    } else {
+#pragma unroll
+        for (int c = 0; c < 2 * CPB; ++c) load_reg(0, c, no);
+        vm_wait_n<0>();
+#pragma unroll
+        for (int c = 0; c < 2 * CPB; ++c) write_reg(0, c, no);
+    }
+    if (nk > 1) {
+        if (ktail && nk == 2) {
+#pragma unroll
+            for (int c = 0; c < 2 * CPB; ++c) load_reg(1, c, yes);
+        } else {
+#pragma unroll
+            for (int c = 0; c < 2 * CPB; ++c) load_reg(1, c, no);
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    asm volatile("s_barrier" ::: "memory");
+#pragma unroll
+    for (int r = 0; r < NREAD; ++r) read_one(f0, 0, 0, r);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    settle(f0);
+    // One iteration (tile t): step (t, 0) writes tile t+1 (tag W) and loads tile t+2
+    // (tag L); the barrier publishes tile t+1; step (t, 1) reads step (t+1, 0).
+    auto iteration_reg = [&](int t, auto write_tag, auto load_tag) {
+        step_reg(f0, f1, t & 3, 1, t + 1, t + 2, write_tag, load_tag);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        asm volatile("s_barrier" ::: "memory");
+        settle(f1);
+        step_reg(f1, f0, (t + 1) & 3, 0, 0, 0, none, none);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        settle(f0);
+    };
+    // straight runs of one variant each, as in the direct-copy form
+    const int nfull = ktail ? nk - 1 : nk;  // whole k-tiles
+    int t = 0;
+    for (; t + 2 < nfull; ++t) iteration_reg(t, full, full);
+    for (; ktail && t + 2 == nk - 1; ++t) iteration_reg(t, full, part);  // loads the partial tile
+    for (; t + 2 < nk; ++t) iteration_reg(t, full, none);
+    for (; ktail && t + 2 == nk; ++t) iteration_reg(t, part, none);      // writes the partial tile
+    for (; t + 1 < nk; ++t) iteration_reg(t, full, none);
+    for (; t < nk; ++t) iteration_reg(t, none, none);
+    } else {
     // prologue: tiles 0 .. D-1 in flight (A then B of each); tile 0 complete; step
     // (0, 0) fragments read.
     for (int t = 0; t < D && t < nk; ++t) {
@@ -320,8 +497,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         settle(f0);
     };
-    constexpr std::true_type yes{};
-    constexpr std::false_type no{};
     // straight runs of one variant each (a branch between two inlined variants inside
     // a loop leaves the register allocator unable to keep the fragments in registers)
     const int nfull = ktail ? nk - 1 : nk;  // tiles t + D copied by the plain variant
@@ -332,6 +507,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     for (; t < nfix; ++t) iteration(t, no, no, no);
     for (; ktail && t == nk - 2; ++t) iteration(t, no, no, yes);
     for (; t < nk; ++t) iteration(t, no, no, no);
+    }
 
     // ---- epilogue through LDS. Every wave's last reads are done (lgkmcnt(0) above);
     // the barrier makes sure all of them are before any wave overwrites a stage. The

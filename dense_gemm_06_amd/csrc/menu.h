@@ -25,7 +25,9 @@ enum Dtype { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
 //             128 x 64 (2, 4, 5: 16-byte aligned operands, edge tiles in M, and in N
 //             for column-major B or N a multiple of 8; 2, 4: K a multiple of bk;
 //             5: K a multiple of 8), 6 = register-staged with three LDS stages and fragments
-//             read a half k-tile ahead (fp32, any shape)
+//             read a half k-tile ahead (fp32, any shape), 7 = the software-pipelined
+//             32x32x16 kernel of schedule 5 with register-staged loads (16-bit inputs,
+//             bases aligned to the element, any M, K >= 8, N >= 8 for row-major B)
 struct MenuEntry {
     int id, variant, dtype, opb, vec, bm, bn, bk, wm, wn, tm, tn, threads, lds_bytes, sched;
 };
@@ -109,6 +111,15 @@ constexpr bool grouped_capable(int variant, int sched, int bm, int bn, int wm, i
     X(base + 2, V_MFMA, dt, 0, 1, 256, 256, 32, 2, 4, 0, 0, 512, 4 * 2 * 32 * 512, 5)      \
     X(base + 3, V_MFMA, dt, 1, 1, 256, 256, 32, 2, 4, 0, 0, 512, 4 * 2 * 32 * 512, 5)
 
+// The software-pipelined kernels with register-staged loads (schedule 7): 16-byte
+// loads from element-aligned rows, so no alignment or divisibility beyond K >= 8 (and
+// N >= 8 for row-major B).
+#define DG_MFMA_SPR(X, base, dt)                                                         \
+    X(base + 0, V_MFMA, dt, 0, 1, 256, 256, 32, 2, 2, 0, 0, 256, 4 * 2 * 32 * 512, 7)      \
+    X(base + 1, V_MFMA, dt, 1, 1, 256, 256, 32, 2, 2, 0, 0, 256, 4 * 2 * 32 * 512, 7)      \
+    X(base + 2, V_MFMA, dt, 0, 1, 256, 256, 32, 2, 4, 0, 0, 512, 4 * 2 * 32 * 512, 7)      \
+    X(base + 3, V_MFMA, dt, 1, 1, 256, 256, 32, 2, 4, 0, 0, 512, 4 * 2 * 32 * 512, 7)
+
 // fp32 64 x 64 tiles with K split between two groups of 4 waves inside the
 // workgroup (8 waves: two per SIMD for a tile that holds four); LDS: two stages
 // per group.
@@ -139,9 +150,11 @@ constexpr bool grouped_capable(int variant, int sched, int bm, int bn, int wm, i
     DG_MFMA_SP(X, 76, DT_F16)                                    \
     DG_MFMA_SP(X, 80, DT_BF16)                                   \
     DG_MFMA_KG2(X, 84)                                           \
-    DG_MFMA_F32S3(X, 88)
+    DG_MFMA_F32S3(X, 88)                                         \
+    DG_MFMA_SPR(X, 90, DT_F16)                                   \
+    DG_MFMA_SPR(X, 94, DT_BF16)
 
-constexpr int kMenuSize = 90;
+constexpr int kMenuSize = 98;
 
 // Fused epilogue ("Shared memory and tensor cores", section 13.10: bias,
 // activation, residual add or type cast applied to the accumulator before the

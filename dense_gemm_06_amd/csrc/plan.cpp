@@ -135,7 +135,7 @@ static double tile_efficiency_aligned(const MenuEntry& e);
 // and are assumed 1.7x slower for fp32.
 static double tile_efficiency(const MenuEntry& e, bool rows16) {
     const bool f32 = e.dtype == DT_F32;
-    const double load = !e.vec ? (f32 ? 0.6 : 0.35) : rows16 ? 1.0 : (f32 ? 0.8 : 0.55);
+    const double load = !e.vec ? (f32 ? 0.6 : 0.35) : (rows16 || e.sched == 7) ? 1.0 : (f32 ? 0.8 : 0.55);
     return tile_efficiency_aligned(e) * load;
 }
 static double tile_efficiency_aligned(const MenuEntry& e) {
@@ -144,7 +144,7 @@ static double tile_efficiency_aligned(const MenuEntry& e) {
     // register-staged 256 x 256 165 us
     if (e.sched == 2) return 0.97;
     if (e.sched == 4) return 0.96;
-    if (e.sched == 5) return 0.90;  // problem-dependent: see plan()
+    if (e.sched == 5 || e.sched == 7) return 0.90;  // problem-dependent: see plan()
     // the fp32 three-stage 256 x 128 tile: 2.8% faster per k than two resident 128 x 128
     // register-staged tiles per CU (fitted from 8192^2 x K, K = 256, 512 and 8192,
     // alternated: 31.2 against 32.1 us per round and 256 k), with a larger fixed cost
@@ -248,7 +248,7 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
             set_error("threads = %d must be non-negative", want_threads);
             return GEMM_ERR_INVALID_VALUE;
         }
-        if (want_sched < 0 || want_sched > 6 || want_wm < 0 || want_wn < 0 || want_variant < 0 || want_variant > 2 || want_vec < -1 || want_vec > 1 || want_remap < -1 ||
+        if (want_sched < 0 || want_sched > 7 || want_wm < 0 || want_wn < 0 || want_variant < 0 || want_variant > 2 || want_vec < -1 || want_vec > 1 || want_remap < -1 ||
             want_remap > 1 || want_group < 0 || want_bm < 0 || want_bn < 0) {
             set_error("invalid requested configuration (variant %d, bm %d, bn %d, vec %d, xcd_remap %d, group_m %d)",
                       want_variant, want_bm, want_bn, want_vec, want_remap, want_group);
@@ -311,6 +311,9 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
         if (direct_copy(e.sched) && (Mx % e.bm != 0 || Nx % e.bn != 0) &&
             !((e.sched == 5 || e.sched == 2 || e.sched == 4) && (e.opb == 1 || Nx % 8 == 0)))
             continue;
+        // the register-staged software-pipelined kernel reads whole 16-byte chunks
+        // inside each row: K >= 8, and N >= 8 for a row-major B
+        if (e.sched == 7 && (Kx < 8 || (e.opb == 0 && Nx < 8))) continue;
         if (want_wn && (e.variant == V_MFMA ? e.wn : 1) != want_wn) continue;
         const int vec = want_vec >= 0 ? want_vec : ((packed || vec_ok) ? 1 : 0);
         if (e.vec != vec) continue;
@@ -357,11 +360,21 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
             // 4096^2 x 1024 53.0 against 54.7), the ping-pong kernel at 8 and 16 k-tiles
             // (8192^2 x 256 124.4 against 127.2; 8192^2 x 512 column-major B 150.6
             // against 155.2); 4 waves are 12-60% slower there.
+            //
+            // The register-staged form (schedule 7) follows the same rules, about 10%
+            // slower than the direct copies on the same data (medians of three
+            // alternated passes, 8 waves: 4096^3 fp16 134.5 against 123.1 us, 3072 x
+            // 5120 x 1088 bf16 41.3 against 40.7); it is the kernel for rows that are
+            // not 16-byte aligned: 3001 x 5003 x 1037 bf16 with column-major B 58.3 us
+            // against 73 on the register-staged 256 x 256 tile and 62.2 packed, 2000 x
+            // 3000 x 1001 fp16 36.4 against 39.2, 4095^3 fp16 156.1 against 161.8 for
+            // 4 waves; 8192^2 x 1037 bf16 193.2 against 183.3 packed.
             double eff = tile_efficiency(e, packed || dma_ok);
-            if (e.sched == 5) {
+            if (e.sched == 5 || e.sched == 7) {
                 const bool eight = e.wm * e.wn == 8;
                 if (fused_epilogue) eff = eight && ktiles >= 32 ? 0.99 : 0.90;
                 else eff = !eight ? 0.90 : (tiles <= num_cus && ktiles <= 32) ? 0.96 : 0.99;
+                if (e.sched == 7) eff *= 0.9;
             }
             const double tile_cycles = 2.0 * e.bm * e.bn * std::max<int64_t>(kpad, e.bk) / (rate_per_cu(e) * eff);
             double cost = (double)rounds * (double)std::max<int64_t>(resident, 1) * tile_cycles;

@@ -98,7 +98,10 @@ typedef struct gemm_config {
                           multiple of 8 for row-major B; 2, 4: K a multiple of 32; 5: K a multiple of 8;
                           4 stores the plain fp32 accumulator only); 6 register-staged with three LDS
                           stages and fragments read half a k-tile ahead (fp32 256 x 128
-                          tiles, any shape, K not split) */
+                          tiles, any shape, K not split); 7 the software-pipelined kernel
+                          of schedule 5 with register-staged 16-byte loads (16-bit inputs,
+                          bases aligned to the element, rows at any offset, any M, K >= 8,
+                          any N for column-major B or N >= 8 for row-major B) */
     int64_t tiles_m, tiles_n; /* out (grouped: of the first non-empty problem) */
     double est_cycles; /* out: the heuristic's cost estimate (clock cycles) */
     int64_t tiles_total; /* out: output tiles of the call (grouped: of all its problems) */

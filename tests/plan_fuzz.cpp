@@ -112,6 +112,12 @@ static void check_plan(int opB, int64_t M, int64_t N, int64_t K, int64_t lda, in
         if (opB == 0)
             CHECK(N % e.bn == 0 || N % 8 == 0, "row-major B edge tile with N = %lld", (long long)N);
     }
+    if (e.sched == 7) {
+        // whole 16-byte chunks inside every row: K >= 8, N >= 8 for a row-major B, and
+        // 16-byte loads (element-aligned bases unless packed)
+        CHECK(e.vec == 1 && K >= 8 && (opB == 1 || N >= 8 || (packed && N > 0)),
+              "register-staged software-pipelined kernel with K = %lld, N = %lld", (long long)K, (long long)N);
+    }
     if (req) {
         if (req->bm) CHECK(c.bm == req->bm, "bm %d requested %d", c.bm, req->bm);
         if (req->bn) CHECK(c.bn == req->bn, "bn %d requested %d", c.bn, req->bn);

@@ -52,7 +52,7 @@ def test_status_strings():
 
 def test_menu_is_complete():
     menu = dg.gemm_menu()
-    assert len(menu) == dg.library().gemm_menu_size() == 90
+    assert len(menu) == dg.library().gemm_menu_size() == 98
     seen = set()
     for e in menu:
         assert e["lds_bytes"] <= 160 * 1024
@@ -69,7 +69,7 @@ def test_menu_is_complete():
                 for vec in (0, 1):
                     tiles = {(bm, bn) for (v, d, o, ve, bm, bn) in seen if (v, d, o, ve) == (variant, dtype, opb, vec)}
                     assert len(tiles) >= 2, (variant, dtype, opb, vec)
-    assert dg.library().gemm_menu_entry(90, None, None, None, None) == dg.GEMM_ERR_INVALID_VALUE
+    assert dg.library().gemm_menu_entry(98, None, None, None, None) == dg.GEMM_ERR_INVALID_VALUE
 
 
 def plan(M, N, K, dtype="f32", op_b="N", lda=None, ldb=None, ldc=None, a=0, b=0, c=0, cus=256, arch="gfx950",
@@ -88,9 +88,10 @@ def test_plan_benchmark_configs():
     st, c = plan(4096, 4096, 4096, "f32")
     assert st == 0 and c.variant == dg.GEMM_VARIANT_MFMA and c.vec == 1
     # ragged bf16 with column-major B and odd leading dimensions: 16-byte loads from
-    # 2-byte-aligned rows on the register-staged 256 x 256 kernel
+    # 2-byte-aligned rows on the register-staged software-pipelined kernel, 8 waves
     st, c = plan(3001, 5003, 1037, "bf16", "T", lda=1037, ldb=1037, ldc=5003)
-    assert st == 0 and c.variant == dg.GEMM_VARIANT_MFMA and c.vec == 1 and c.schedule == 1
+    assert st == 0 and c.variant == dg.GEMM_VARIANT_MFMA and c.vec == 1 and c.schedule == 7
+    assert (c.waves_m, c.waves_n) == (2, 4)
     assert (c.bm, c.bn) == (256, 256)
     assert c.tiles_m == -(-3001 // c.bm) and c.tiles_n == -(-5003 // c.bn)
 
@@ -109,10 +110,11 @@ def test_plan_software_pipelined_kernel_where_measured_faster():
     # one round of 256 tiles and at most 32 k-tiles: the ping-pong kernel
     for k, dt, op_b in ((1024, "f16", "N"), (512, "bf16", "N"), (1024, "bf16", "T")):
         assert plan(4096, 4096, k, dt, op_b)[1].schedule == 2, (k, dt, op_b)
-    # the ragged column-major problem, packed into whole tiles of K = 1088 (34 k-tiles)
+    # the ragged column-major problem: the register-staged form runs it directly, even
+    # with a workspace that would allow packing (58 us against 62 packed)
     st, c = dg.gemm_plan_workspace(0, 1, 3001, 5003, 1037, 1037, 1037, 5003, dg.GEMM_BF16, 0x10002, 0x200002,
                                    0x400000, 256, "gfx950", 64 << 20, None)
-    assert st == 0 and c.pack == 2 and c.schedule == 5 and c.threads == 512
+    assert st == 0 and c.pack == 1 and c.schedule == 7 and c.threads == 512
     # with a fused epilogue: 8 waves from 32 k-tiles on, either B layout; the ping-pong
     # kernel below that
     for op_b, k, sched in ((0, 4096, 5), (1, 4096, 5), (0, 1024, 5), (0, 256, 2), (1, 512, 2)):
@@ -138,8 +140,8 @@ def test_plan_ping_pong_eligibility():
         assert plan(4096 + 8, 4096, 4096, "f16", req=dg.request(schedule=sched))[0] == 0
         st, _ = plan(4096, 4001, 4096, "f16", ldb=4008, req=dg.request(schedule=sched))
         assert st == dg.GEMM_ERR_UNSUPPORTED
-    assert plan(4096, 4096, 4096, "f16", a=2)[1].schedule == 1
-    assert plan(4096, 4096, 4096, "f32")[1].schedule not in (2, 3, 4, 5)
+    assert plan(4096, 4096, 4096, "f16", a=2)[1].schedule == 7    # A not 16-byte aligned
+    assert plan(4096, 4096, 4096, "f32")[1].schedule not in (2, 3, 4, 5, 7)
     st, _ = plan(4096, 4096, 4000 + 8, "f16", req=dg.request(schedule=2))   # K not a multiple of 32
     assert st == dg.GEMM_ERR_UNSUPPORTED
 
@@ -151,15 +153,15 @@ def test_plan_software_pipelined_edge_tiles():
         st, c = plan(4000, 4000, 4000, "f16", op_b)
         assert st == 0 and c.schedule == sched and (c.tiles_m, c.tiles_n) == (16, 16), op_b
     st, c = plan(4000, 4001, 4096, "f16", "N", ldb=4008)     # a 16-byte chunk would straddle N
-    assert st == 0 and c.schedule == 1
+    assert st == 0 and c.schedule == 7
     st, _ = plan(4000, 4001, 4096, "f16", "N", ldb=4008, req=dg.request(schedule=5))
     assert st == dg.GEMM_ERR_UNSUPPORTED
     st, c = plan(4000, 4001, 4096, "f16", "T")
     assert st == 0 and c.schedule in (2, 5)
     assert plan(4000, 4000, 4000 + 8, "f16")[1].schedule == 5   # a partial last k-tile
     st, c = plan(4000, 4000, 4004, "f16", lda=4008)             # K not a multiple of 8
-    assert st == 0 and c.schedule == 1
-    assert plan(4000, 4000, 4000, "f16", lda=4004)[1].schedule == 1   # rows not 16-byte aligned
+    assert st == 0 and c.schedule == 7
+    assert plan(4000, 4000, 4000, "f16", lda=4004)[1].schedule == 7   # rows not 16-byte aligned
 
 
 def test_plan_three_stage_fp32():
@@ -221,9 +223,10 @@ def test_plan_alignment_rules():
     assert plan(512, 512, 512, "f32", b=6)[1].vec == 0
     # the direct global -> LDS copies of the whole-tile kernels need 16-byte rows
     assert plan(4096, 4096, 4096, "f16")[1].schedule == 5
+    # (otherwise the register-staged form of the software-pipelined kernel runs)
     for kw in (dict(a=2), dict(lda=4100), dict(b=8), dict(ldb=4100)):
         st, c = plan(4096, 4096, 4096, "f16", **kw)
-        assert st == 0 and c.schedule == 1 and c.vec == 1, kw
+        assert st == 0 and c.schedule == 7 and c.vec == 1, kw
         st, _ = plan(4096, 4096, 4096, "f16", req=dg.request(schedule=5), **kw)
         assert st == dg.GEMM_ERR_UNSUPPORTED, kw
     # forcing 16-byte loads on bases not aligned to the element is refused
@@ -476,18 +479,22 @@ def test_split_workspace_rejections_before_device():
 
 # ----------------------------------------------------------------------------- packed operands
 def test_pack_plan_choices():
-    # the ragged bf16 benchmark problem packs onto a whole-tile kernel (the 4-wave
-    # software-pipelined one for its short K)
+    # the ragged bf16 benchmark problem runs directly on the register-staged
+    # software-pipelined kernel; forced packing puts it on the direct-copy one, whole
+    # tiles of K = 1088
     st, c = dg.gemm_plan_workspace(0, 1, 3001, 5003, 1037, 1037, 1037, 5003, dg.GEMM_BF16, 4096, 4096, 4096, 256,
                                    "gfx950", 1 << 30)
+    assert st == 0 and c.pack == 1 and c.schedule == 7 and c.launches == 1
+    st, c = dg.gemm_plan_workspace(0, 1, 3001, 5003, 1037, 1037, 1037, 5003, dg.GEMM_BF16, 4096, 4096, 4096, 256,
+                                   "gfx950", 1 << 30, dg.request(pack=2))
     assert st == 0 and c.pack == 2 and c.schedule == 5 and c.vec == 1 and c.launches == 2
     assert (c.tiles_m, c.tiles_n) == (12, 20)
     assert c.workspace_bytes == 3072 * 1088 * 2 + 5120 * 1088 * 2
-    # without workspace, or with pack = 1, it does not
-    assert plan(3001, 5003, 1037, "bf16", "T", lda=1037, ldb=1037, ldc=5003)[1].pack == 1
-    st, c = dg.gemm_plan_workspace(0, 1, 3001, 5003, 1037, 1037, 1037, 5003, dg.GEMM_BF16, 4096, 4096, 4096, 256,
-                                   "gfx950", 1 << 30, dg.request(pack=1))
-    assert st == 0 and c.pack == 1 and c.vec == 1 and c.schedule == 1
+    # a 16-bit problem with misaligned rows and no room for the register-staged kernel's
+    # 16-byte chunks (K < 8) still packs when a workspace is given
+    st, c = dg.gemm_plan_workspace(0, 0, 4096, 4096, 7, 7, 4097, 4096, dg.GEMM_F16, 4096, 4096, 4096, 256,
+                                   "gfx950", 1 << 30)
+    assert st == 0 and c.schedule != 7
     # an aligned whole-tile problem gains nothing from a copy
     assert wplan(4096, 4096, 4096, "f16")[1].pack == 1
 

@@ -145,7 +145,7 @@ def test_epilogue_paths(path, dtype, out, act):
     assert epilogue_error(got, ref, Dp, dtype, out) <= 1.0
 
 
-@pytest.mark.parametrize("schedule,waves_n", [(2, 0), (5, 2), (5, 4)])
+@pytest.mark.parametrize("schedule,waves_n", [(2, 0), (5, 2), (5, 4), (7, 2), (7, 4)])
 @pytest.mark.parametrize("dtype,op_b", [("f16", "N"), ("bf16", "T")])
 @pytest.mark.parametrize("out", ["f32", "bf16", "f16"])
 def test_epilogue_whole_tile_kernels(schedule, waves_n, dtype, op_b, out):
@@ -180,6 +180,17 @@ def test_epilogue_ping_pong_edge_tiles(shape, dtype, op_b, out):
     got, ref, Dp, plan = run_epi(ops, out, act="gelu_tanh", cfg=dg.request(schedule=2))
     assert plan.schedule == 2 and plan.tiles_m == -(-M // 256) and plan.tiles_n == -(-N // 256)
     assert epilogue_error(got, ref, Dp, dtype, out) <= 1.0
+
+
+@pytest.mark.parametrize("waves_n", [2, 4])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_epilogue_register_staged_sp_unaligned(waves_n, out):
+    """Schedule 7's staged epilogue on an unaligned ragged problem (rows at 2-byte
+    offsets, K and N not multiples of 8)."""
+    ops = gi.make_operands(300, 263, 99, "bf16", "normal", seed=12, lda=101, ldb=267)
+    got, ref, Dp, plan = run_epi(ops, out, act="gelu_tanh", cfg=dg.request(schedule=7, waves_n=waves_n))
+    assert plan.schedule == 7
+    assert epilogue_error(got, ref, Dp, "bf16", out) <= 1.0
 
 
 @pytest.mark.parametrize("op_b", ["N", "T"])

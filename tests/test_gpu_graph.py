@@ -59,16 +59,17 @@ def run_case(make_call, inputs, outputs):
         assert torch.isfinite(outputs[0].float()).all()
 
 
-@pytest.mark.parametrize("case", ["pipelined_f16", "three_stage_f32", "register_staged_bf16_T"])
+@pytest.mark.parametrize("case", ["pipelined_f16", "pipelined_reg_bf16", "three_stage_f32", "register_staged_bf16_T"])
 def test_plain_call_in_graph(case):
     torch = _torch()
     dtype, op_b, shape, req = {
         "pipelined_f16": ("f16", "N", (1000, 1024, 1064), dg.request(schedule=5)),
+        "pipelined_reg_bf16": ("bf16", "T", (1001, 1023, 1037), dg.request(schedule=7)),
         "three_stage_f32": ("f32", "N", (600, 500, 300), dg.request(schedule=6)),
         "register_staged_bf16_T": ("bf16", "T", (301, 257, 103), None),
     }[case]
     M, N, K = shape
-    A, lda, B, ldb = operands(torch, M, N, K, dtype, op_b, pad=(0, 0) if case != "register_staged_bf16_T" else (3, 5))
+    A, lda, B, ldb = operands(torch, M, N, K, dtype, op_b, pad=(3, 5) if case in ("register_staged_bf16_T", "pipelined_reg_bf16") else (0, 0))
     C = [torch.zeros(M * N, dtype=torch.float32, device="cuda") for _ in range(2)]
     print(f"graph case {case}: {shape} {dtype} op {op_b}", flush=True)
 

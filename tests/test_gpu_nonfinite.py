@@ -90,6 +90,8 @@ PLAIN = [
     ("ping-pong-bf16-T", "bf16", "T", (300, 260, 224), dict(schedule=2)),
     ("pipelined8-f16", "f16", "N", (300, 264, 200), dict(schedule=5, threads=512)),
     ("pipelined4-bf16-T", "bf16", "T", (300, 260, 200), dict(schedule=5, threads=256)),
+    ("pipelined-reg8-f16", "f16", "N", (300, 263, 203), dict(schedule=7, threads=512)),
+    ("pipelined-reg4-bf16-T", "bf16", "T", (300, 261, 203), dict(schedule=7, threads=256)),
 ]
 
 

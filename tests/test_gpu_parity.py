@@ -35,7 +35,7 @@ def _lib_built():
 MENU = _menu()
 MENU_IDS = [f"k{e['kernel_id']}-{'lds' if e['variant'] == 1 else 'mfma'}-{DT_NAME[e['dtype']]}-"
             f"op{'NT'[e['opb']]}-{'v16' if e['vec'] else 'v1'}-{e['bm']}x{e['bn']}-w{e['waves_m']}x{e['waves_n']}"
-            f"{ {1: '', 2: '-pp', 3: '-dma', 4: '-pp32', 5: '-sp', 6: '-s3'}[e['schedule']] }"
+            f"{ {1: '', 2: '-pp', 4: '-pp32', 5: '-sp', 6: '-s3', 7: '-spr'}[e['schedule']] }"
             for e in MENU]
 
 
@@ -142,6 +142,80 @@ def test_software_pipelined_edge_tiles(waves_n, shape, op_b, dtype):
     check_untouched(C, M, N)
     Cref, D = oracle.gemm_ref(ops)
     assert normalized_error(C[:M, :N], Cref, D) <= TOL[dtype]
+
+
+SPR_SHAPES = [((300, 264, 64), "N"), ((513, 777, 96), "T"), ((257, 512, 4160), "N"), ((40, 8, 32), "N"),
+              ((600, 1, 128), "T"), ((256, 300, 32 * 130), "T"), ((300, 264, 40), "N"), ((513, 777, 1000), "T"),
+              ((40, 8, 8), "N"), ((256, 256, 24), "T"), ((257, 512, 4168), "N"), ((512, 256, 56), "T"),
+              # K not a multiple of 8, N not a multiple of 8 (row-major B straddling N), N = 9
+              ((300, 264, 37), "N"), ((513, 777, 1037), "T"), ((100, 9, 13), "N"), ((257, 263, 71), "N"),
+              ((64, 1000, 8), "T"), ((65, 65, 9), "N"), ((255, 257, 263), "T"), ((777, 300, 99), "N")]
+
+
+@pytest.mark.parametrize("waves_n", [2, 4])
+@pytest.mark.parametrize("shape,op_b", SPR_SHAPES)
+@pytest.mark.parametrize("dtype,offset", [("f16", 0), ("bf16", 1)])
+def test_register_staged_sp(waves_n, shape, op_b, dtype, offset):
+    """Schedule 7 (the software-pipelined kernel with register-staged loads) on rows at
+    any 2-byte offset: leading dimensions K + 3 and N + 5 (or K + 5), bases 0 or 1
+    element past a 16-byte boundary, ragged M and N, K and (row-major B) N that are
+    not multiples of 8, so that partial chunks are loaded from the row's last 8
+    elements and shifted into place."""
+    M, N, K = shape
+    ldb = (N if op_b == "N" else K) + 5
+    ops = gi.make_operands(M, N, K, dtype, "normal", seed=M + N + K, op_b=op_b, lda=K + 3, ldb=ldb)
+    print(f"case spr {shape} {dtype} op {op_b} waves_n {waves_n} offset {offset}", flush=True)
+    req = dg.request(schedule=7, waves_n=waves_n)
+    es = 2
+    st, plan = dg.gemm_plan(0, dg.OP_CODE[op_b], M, N, K, ops.lda, ops.ldb, N + 3, dg.DTYPE_CODE[dtype],
+                            (1 << 30) + offset * es, (1 << 40) + offset * es, 1 << 41, 256, "gfx950", req)
+    assert plan.schedule == 7 and plan.tiles_m == -(-M // 256) and plan.tiles_n == -(-N // 256)
+    C = run_ops(ops, cfg=req, ldc=N + 3, a_off=offset, b_off=offset, c_off=offset)
+    check_untouched(C, M, N)
+    Cref, D = oracle.gemm_ref(ops)
+    assert normalized_error(C[:M, :N], Cref, D) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("waves_n", [2, 4])
+@pytest.mark.parametrize("k_tiles", [1, 2, 3, 4, 5, 6, 130])
+@pytest.mark.parametrize("dtype,op_b", [("f16", "N"), ("bf16", "N"), ("f16", "T"), ("bf16", "T")])
+def test_register_staged_sp_k_tile_counts(waves_n, k_tiles, dtype, op_b):
+    """Prologue, steady state and tail of schedule 7 for every small k-tile count and a
+    long K, with a partial last k-tile of 27 k (odd k-tile counts) or a whole one."""
+    K = 32 * k_tiles - (5 if k_tiles % 2 else 0)
+    ops = gi.make_operands(300, 520, K, dtype, "normal", seed=k_tiles, op_b=op_b, lda=K + 1,
+                           ldb=(520 if op_b == "N" else K) + 3)
+    C = run_ops(ops, cfg=dg.request(schedule=7, waves_n=waves_n), ldc=ops.N + 4)
+    check_untouched(C, ops.M, ops.N)
+    Cref, D = oracle.gemm_ref(ops)
+    assert normalized_error(C[:ops.M, :ops.N], Cref, D) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("waves_n", [2, 4])
+@pytest.mark.parametrize("op_b", ["N", "T"])
+def test_register_staged_sp_integer_exact(waves_n, op_b):
+    """Integer data through schedule 7 on an unaligned ragged shape: bit-exact."""
+    M, N, K = 301, 263, 1037
+    i = np.arange(M)[:, None]
+    k = np.arange(K)[None, :]
+    a = (((7 * i + 3 * k) % 7) - 3).astype(np.float32)
+    b = (((5 * np.arange(K)[:, None] + 2 * np.arange(N)[None, :] + 1) % 7) - 3).astype(np.float32)
+    ops = gi.from_values(a, b, "bf16", op_b, lda=K + 1, ldb=(N if op_b == "N" else K) + 1)
+    C = run_ops(ops, cfg=dg.request(schedule=7, waves_n=waves_n), ldc=N + 1, a_off=1, b_off=1)
+    check_untouched(C, M, N)
+    Cref, _ = oracle.gemm_ref(ops, want_d=False)
+    assert np.array_equal(C[:M, :N].astype(np.float64), Cref)
+
+
+@pytest.mark.parametrize("waves_n", [2, 4])
+def test_register_staged_sp_c5_full_size(waves_n):
+    """The 3001 x 5003 x 1037 bf16 problem with column-major B (rows at 2-byte
+    offsets) on schedule 7, every entry against the oracle."""
+    ops = gi.make_config("c5_bf16_ragged")
+    C = run_ops(ops, cfg=dg.request(schedule=7, waves_n=waves_n), ldc=ops.N, extra_rows=1)
+    check_untouched(C, ops.M, ops.N)
+    Cref, D = oracle.gemm_ref(ops)
+    assert normalized_error(C[:ops.M, :ops.N], Cref, D) <= TOL[ops.dtype]
 
 
 @pytest.mark.parametrize("schedule", [2, 4])

@@ -47,7 +47,8 @@ def _run(ops, noalloc: bool, cfg=None):
 
 
 CASES = {
-    # rows that are not 16-byte aligned: the planner packs both operands into the scratch
+    # rows that are not 16-byte aligned, packing forced: both operands are copied into
+    # the scratch
     "packed": lambda: [gi.make_operands(3001, 5003, 1037, "bf16", "normal", seed=1, op_b="T", lda=1037, ldb=1037),
                        gi.make_operands(2500, 4000, 1037, "bf16", "normal", seed=2, op_b="T", lda=1039, ldb=1041)],
     # 16 output tiles facing a long K: split K into partial planes in the scratch
@@ -63,8 +64,9 @@ CASES = {
 def test_noalloc_matches_workspace_call(name):
     for i, ops in enumerate(CASES[name]()):
         print(f"noalloc case {name} call {i}: M={ops.M} N={ops.N} K={ops.K} {ops.dtype} op {ops.op_b}", flush=True)
-        got, plan = _run(ops, noalloc=True)
-        ref, plan_ws = _run(ops, noalloc=False)
+        cfg = dg.request(pack=2) if name == "packed" else None
+        got, plan = _run(ops, noalloc=True, cfg=cfg)
+        ref, plan_ws = _run(ops, noalloc=False, cfg=cfg)
         assert plan.as_dict() == plan_ws.as_dict()
         if name == "packed":
             assert plan.pack == 2
