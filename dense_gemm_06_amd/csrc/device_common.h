@@ -163,11 +163,17 @@ __device__ __forceinline__ float epilogue_value(const Epilogue& ep, float acc, s
 // The epilogue of one run, out of line: inlined into every run of a kernel's
 // unrolled store loop it would make the loop too large to unroll, and the
 // accumulators would then be indexed at run time (moved to scratch memory).
-// A whole, aligned run moves as one vector (16 bytes of fp32, 8 bytes of 16-bit
-// values) for both the residual read and the store.
+// A whole run moves as one vector (16 bytes of fp32, 8 bytes of 16-bit values)
+// for both the residual read and the store, at any element-aligned address:
+// gfx950 serves under-aligned vector stores as it serves under-aligned loads.
 __device__ __forceinline__ f32x4 load_out4(const void* p, int dt, size_t i) {
-    if (dt == DT_F32) return *reinterpret_cast<const f32x4*>(static_cast<const float*>(p) + i);
-    const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p) + i);
+    if (dt == DT_F32) {
+        f32x4 r;
+        __builtin_memcpy(&r, static_cast<const float*>(p) + i, 16);
+        return r;
+    }
+    u32x2 w;
+    __builtin_memcpy(&w, static_cast<const uint16_t*>(p) + i, 8);
     f32x4 r;
     if (dt == DT_F16) {
         r[0] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[0] & 0xffffu));
@@ -185,14 +191,15 @@ __device__ __forceinline__ f32x4 load_out4(const void* p, int dt, size_t i) {
 
 __device__ __forceinline__ void store_out4(void* p, int dt, size_t i, f32x4 x) {
     if (dt == DT_F32) {
-        *reinterpret_cast<f32x4*>(static_cast<float*>(p) + i) = x;
+        __builtin_memcpy(static_cast<float*>(p) + i, &x, 16);
         return;
     }
     uint32_t h[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
         h[e] = dt == DT_F16 ? (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x[e]) : (uint32_t)f32_to_bf16_rne(x[e]);
-    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p) + i) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+    const u32x2 w = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+    __builtin_memcpy(static_cast<uint16_t*>(p) + i, &w, 8);
 }
 
 // Wave-uniform values handed to an out-of-line function arrive in vector registers;
@@ -204,24 +211,15 @@ __device__ __forceinline__ uint64_t uni64(uint64_t x) {
 }
 __device__ __forceinline__ float unif(float x) { return __uint_as_float(uni32(__float_as_uint(x))); }
 
-// The epilogue of the run C[m][n .. n+3] (columns >= N skipped). A whole run at
-// aligned addresses moves as one vector for R and for C, and reads bias as one
-// 16-byte load when aligned.
+// The epilogue of the run C[m][n .. n+3] (columns >= N skipped). A whole run
+// moves as one vector for R and for C, and reads bias as one 16-byte load.
 __device__ __forceinline__ void epilogue_run4_body(const Epilogue& ep, void* C, int64_t ldc, int N, int m, int n,
                                                    f32x4 v) {
     const size_t ci = (size_t)m * ldc + n, ri = (size_t)m * ep.ldr + n;
-    const int vb = ep.out_dt == DT_F32 ? 16 : 8;  // bytes of a whole run
-    const int es = ep.out_dt == DT_F32 ? 4 : 2;
-    const bool whole = n + 4 <= N;
-    const bool c_vec = whole && ((reinterpret_cast<uintptr_t>(C) + ci * es) & (vb - 1)) == 0;
-    const bool r_vec = whole && ep.beta != 0.0f && ((reinterpret_cast<uintptr_t>(ep.R) + ri * es) & (vb - 1)) == 0;
-    if (c_vec && (ep.beta == 0.0f || r_vec)) {
+    if (n + 4 <= N) {
         const f32x4 r = ep.beta != 0.0f ? load_out4(ep.R, ep.out_dt, ri) : f32x4{0.f, 0.f, 0.f, 0.f};
         f32x4 b = {0.f, 0.f, 0.f, 0.f};
-        if (ep.bias) {
-            if ((reinterpret_cast<uintptr_t>(ep.bias + n) & 15) == 0) b = *reinterpret_cast<const f32x4*>(ep.bias + n);
-            else b = f32x4{ep.bias[n], ep.bias[n + 1], ep.bias[n + 2], ep.bias[n + 3]};
-        }
+        if (ep.bias) __builtin_memcpy(&b, ep.bias + n, 16);
         f32x4 x;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -258,15 +256,17 @@ __device__ __attribute__((noinline)) void epilogue_run4(const Epilogue ep_in, vo
 }
 
 // Store the run C[m][n .. n+3] (columns >= N skipped; the caller has checked
-// m < M). The plain fp32 path uses one 16-byte store when the run is whole and
-// aligned; the epilogue path stores element by element in C's element type.
-// EPI = false compiles the plain path only (kernels that never run an epilogue).
+// m < M). The plain fp32 path uses one 16-byte store when the run is whole, at any
+// element-aligned address (gfx950 serves under-aligned vector stores; rows of C
+// with an odd leading dimension start at 4-byte offsets); the epilogue path runs
+// the out-of-line epilogue. EPI = false compiles the plain path only (kernels
+// that never run an epilogue).
 template <bool EPI = true>
 __device__ __forceinline__ void store_run4(const GemmArgs& g, int m, int n, f32x4 v) {
     if (!EPI || g.ep.kind == 0) {
         float* cp = g.C + (size_t)m * g.ldc + n;
-        if (n + 3 < g.N && (reinterpret_cast<uintptr_t>(cp) & 15) == 0) {
-            *reinterpret_cast<f32x4*>(cp) = v;
+        if (n + 3 < g.N) {
+            __builtin_memcpy(cp, &v, 16);
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)

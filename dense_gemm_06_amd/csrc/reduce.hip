@@ -35,8 +35,8 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ w
             continue;
         }
         float* c = static_cast<float*>(Cv) + (size_t)i * (size_t)ldc + j;
-        if (j + 4 <= N && (reinterpret_cast<uintptr_t>(c) & 15) == 0) {
-            *reinterpret_cast<f32x4*>(c) = acc;
+        if (j + 4 <= N) {
+            __builtin_memcpy(c, &acc, 16);  // one 16-byte store, at any element-aligned address
         } else {
             for (int e = 0; e < 4; ++e)
                 if (j + e < N) c[e] = acc[e];
