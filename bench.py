@@ -45,7 +45,7 @@ def kernel_sources(cfg) -> list[str]:
         return common + ["kernel_lds.h"]
     if cfg.schedule in (2, 4):
         return common + ["kernel_pp.h"]
-    if cfg.schedule == 5:
+    if cfg.schedule in (5, 7):
         return common + ["kernel_sp.h"]
     return common + ["kernel_mfma.h"]
 
@@ -379,7 +379,7 @@ def kernel_name(cfg, dtype):
         base = "mfma32_gemm, three LDS stages" if cfg.schedule == 6 else "mfma32_gemm"
     else:
         base = {1: "mfma16_gemm", 2: "mfma16_pp (16x16x32)", 4: "mfma16_pp (32x32x16)",
-                5: "mfma32_sp (32x32x16)"}[cfg.schedule]
+                5: "mfma32_sp (32x32x16)", 7: "mfma32_sp, register-staged (32x32x16)"}[cfg.schedule]
     return f"{base} {cfg.bm}x{cfg.bn}x{cfg.bk} waves {cfg.waves_m}x{cfg.waves_n}"
 
 
