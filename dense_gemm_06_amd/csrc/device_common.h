@@ -81,6 +81,24 @@ __device__ __forceinline__ void k_slice(GemmArgs& g) {
     }
 }
 
+// Tile of workgroup blockIdx.x in round r of a grid of G workgroups that walks
+// `total` tiles in rounds of G (round r holds tiles r*G .. r*G + R - 1, R = min(G,
+// total - r*G)), or -1 when the round has none for it. With xcd_remap (G a multiple
+// of 8) the round's tiles are split into 8 contiguous runs of as equal a length as
+// possible, run x going to the workgroups of XCD x (hardware id mod 8), so that a
+// partial last round still spreads over every XCD and each XCD's tiles stay
+// adjacent in raster order. A full round (R = G) gives XCD x the tiles x*G/8 ..
+// x*G/8 + G/8 - 1.
+__device__ __forceinline__ int round_tile(int r, int total, int xcd_remap) {
+    const int G = gridDim.x, bid = blockIdx.x;
+    const int base = r * G;
+    const int R = min(G, total - base);
+    if (!xcd_remap || (G & 7) != 0) return bid < R ? base + bid : -1;
+    const int x = bid & 7, local = bid >> 3;
+    const int q = R >> 3, rem = R & 7;
+    return local < q + (x < rem ? 1 : 0) ? base + x * q + min(x, rem) + local : -1;
+}
+
 // Persistent workgroup number of this workgroup: with xcd_remap the ids are
 // renumbered so that the workgroups of one XCD (hardware id mod 8) get a
 // contiguous block of numbers, hence tiles that are adjacent in linear order.

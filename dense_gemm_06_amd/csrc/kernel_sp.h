@@ -98,7 +98,7 @@ __device__ __forceinline__ u32x4 keep_first8(u32x4 w, int v) {
 // loaded one iteration earlier; the load of tile t+2 then reuses them. The LDS
 // layout, the fragment reads, the MFMAs and the epilogue are those of the direct-copy
 // form.
-template <int DT, int OPB, int NW, bool REG>
+template <int DT, int OPB, int NW, bool REG, bool PERSIST = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void mfma32_sp(
     GemmArgs g) {
     static_assert(NW == 4 || NW == 8, "waves");
@@ -115,9 +115,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     const int wm = wave / WNN, wn = wave % WNN;
     const int l32 = lane & 31, lh = lane >> 5;
     const int l16 = lane & 15, lg = lane >> 4;
-    int tm, tn;
-    tile_coords(g, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
+    // Output tiles: one per workgroup (grid = tiles) or, for the direct-copy form, a
+    // persistent grid that takes them in rounds of its size (the tile loop below).
+    // With xcd_remap each XCD's workgroups take a contiguous run of each round.
+    const int tiles_total = g.tiles_m * g.tiles_n;
+    int round = 0;
+    int tile = round_tile(0, tiles_total, g.xcd_remap);
     // K a multiple of 8: the last k-tile may be partial (krem of its 32 k valid); its
     // copies clamp the chunks at or beyond K and the LDS chunks past K are zeroed
     // before any fragment of that tile is read
@@ -138,34 +141,50 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     // kcA / kcB: the k offset of a lane's chunk within the k-tile (k-major copies);
     // krB: the k row of a lane's chunk (row-major B). A lane whose chunk of the last
     // tile starts at or beyond K copies the chunk at k = 0 of its row instead.
-    const uint16_t* srcA[CPB];
-    const uint16_t* srcB[CPB];
     int kcA[CPB], kcB[CPB];
-    int nvB[CPB];  // REG, row-major B: columns of the lane's chunk inside N (0..8)
 #pragma unroll
     for (int i = 0; i < CPB; ++i) {
         const int b = wave * CPB + i;
         const int row = b * 16 + (lane >> 2);
         kcA[i] = ((lane & 3) ^ kmaj32_swz(row)) << 3;
-        srcA[i] = A + (size_t)min(m0 + row, g.M - 1) * g.lda + kcA[i];
-        if (OPB == 1) {
-            kcB[i] = kcA[i];
-            srcB[i] = B + (size_t)min(n0 + row, g.N - 1) * g.ldb + kcB[i];
-        } else {
-            const int krow = b * 2 + (lane >> 5);
-            const int col = n0 + (((lane & 31) ^ nmaj32_swz(krow)) << 3);
-            kcB[i] = krow;
-            if constexpr (REG) {
-                // a chunk that straddles N is read from the row's last 8 columns, one
-                // wholly past N from column 0 (N >= 8); the write shifts or zeroes it
-                const int v = g.N - col;
-                nvB[i] = v < 0 ? 0 : (v > 8 ? 8 : v);
-                srcB[i] = B + (size_t)krow * g.ldb + (v >= 8 ? col : v > 0 ? g.N - 8 : 0);
+        kcB[i] = OPB == 1 ? kcA[i] : b * 2 + (lane >> 5);
+    }
+    // A lane's chunk sources for one output tile, and the tile's origin.
+    struct Src {
+        const uint16_t* a[CPB];
+        const uint16_t* b[CPB];
+        int nv[CPB];  // REG, row-major B: columns of the lane's chunk inside N (0..8)
+        int m0, n0;
+    };
+    auto make_src = [&](int t, Src& s) {
+        int tm, tn;
+        raster(t, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
+        s.m0 = tm * BM;
+        s.n0 = tn * BN;
+#pragma unroll
+        for (int i = 0; i < CPB; ++i) {
+            const int b = wave * CPB + i;
+            const int row = b * 16 + (lane >> 2);
+            s.a[i] = A + (size_t)min(s.m0 + row, g.M - 1) * g.lda + kcA[i];
+            if (OPB == 1) {
+                s.b[i] = B + (size_t)min(s.n0 + row, g.N - 1) * g.ldb + kcB[i];
             } else {
-                srcB[i] = B + (size_t)krow * g.ldb + (col < g.N ? col : 0);
+                const int krow = kcB[i];
+                const int col = s.n0 + (((lane & 31) ^ nmaj32_swz(krow)) << 3);
+                if constexpr (REG) {
+                    // a chunk that straddles N is read from the row's last 8 columns, one
+                    // wholly past N from column 0 (N >= 8); the write shifts or zeroes it
+                    const int v = g.N - col;
+                    s.nv[i] = v < 0 ? 0 : (v > 8 ? 8 : v);
+                    s.b[i] = B + (size_t)krow * g.ldb + (v >= 8 ? col : v > 0 ? g.N - 8 : 0);
+                } else {
+                    s.b[i] = B + (size_t)krow * g.ldb + (col < g.N ? col : 0);
+                }
             }
         }
-    }
+    };
+    Src cur;  // the tile being computed
+    make_src(tile, cur);
     const size_t kstepB = OPB == 0 ? (size_t)BK * g.ldb : (size_t)BK;  // elements per k-tile
     // LDS destinations as plain wave-uniform numbers (M0 takes them directly). Built
     // from an integer, a copy's LDS pointer carries no link to sA / sB, so the
@@ -174,19 +193,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     const uint32_t wave_u = (uint32_t)__builtin_amdgcn_readfirstlane(wave);
     const uint32_t dstA = (uint32_t)reinterpret_cast<uintptr_t>(DG_LDSV(&sA[0][0])) + wave_u * (CPB * 1024u);
     const uint32_t dstB = (uint32_t)reinterpret_cast<uintptr_t>(DG_LDSV(&sB[0][0])) + wave_u * (CPB * 1024u);
-    // TAIL: t is the partial last k-tile
-    auto copy_a = [&](int t, int i, auto tail_tag) {
-        const uint16_t* src = srcA[i] + (size_t)t * BK;
-        if (decltype(tail_tag)::value && kcA[i] >= krem) src = srcA[i] - kcA[i];
-        __builtin_amdgcn_global_load_lds(DG_GLB(src), DG_LDS_AT(dstA + (uint32_t)(t & 3) * STAGE_BYTES + i * 1024u),
-                                         16, 0, 0);
+    // Copy chunk i of k-tile t of the tile whose sources are s into stage st (0..3).
+    // TAIL: t is the partial last k-tile.
+    auto copy_a = [&](const Src& s, int t, uint32_t st, int i, auto tail_tag) {
+        const uint16_t* src = s.a[i] + (size_t)t * BK;
+        if (decltype(tail_tag)::value && kcA[i] >= krem) src = s.a[i] - kcA[i];
+        __builtin_amdgcn_global_load_lds(DG_GLB(src), DG_LDS_AT(dstA + st * STAGE_BYTES + i * 1024u), 16, 0, 0);
     };
-    auto copy_b = [&](int t, int i, auto tail_tag) {
-        const uint16_t* src = srcB[i] + (size_t)t * kstepB;
+    auto copy_b = [&](const Src& s, int t, uint32_t st, int i, auto tail_tag) {
+        const uint16_t* src = s.b[i] + (size_t)t * kstepB;
         if (decltype(tail_tag)::value && kcB[i] >= krem)
-            src = OPB == 1 ? srcB[i] - kcB[i] : srcB[i] - (size_t)kcB[i] * g.ldb;
-        __builtin_amdgcn_global_load_lds(DG_GLB(src), DG_LDS_AT(dstB + (uint32_t)(t & 3) * STAGE_BYTES + i * 1024u),
-                                         16, 0, 0);
+            src = OPB == 1 ? s.b[i] - kcB[i] : s.b[i] - (size_t)kcB[i] * g.ldb;
+        __builtin_amdgcn_global_load_lds(DG_GLB(src), DG_LDS_AT(dstB + st * STAGE_BYTES + i * 1024u), 16, 0, 0);
     };
     // Zero the chunks of stage st that lie at or beyond K (the partial last tile), then
     // wait for this wave's writes; the caller's barrier publishes them.
@@ -214,7 +232,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     // ---- register staging (REG). Tile t's chunks: ra (A) and rb (B), one 16-byte load
     // each; written to stage t & 3 at the LDS position the direct copy would fill.
     u32x4 ra[CPB], rb[CPB];
-    const bool nedge = OPB == 0 && n0 + BN > g.N;  // a row-major B tile that crosses N
+    const bool nedge = OPB == 0 && cur.n0 + BN > g.N;  // a row-major B tile that crosses N
     auto ld16 = [](const uint16_t* p) {
         u32x4 r;
         __builtin_memcpy(&r, p, 16);  // one global_load_dwordx4; gfx950 serves under-aligned ones
@@ -225,21 +243,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     auto load_reg = [&](int t, int c, auto tail_tag) {
         constexpr bool TAIL = decltype(tail_tag)::value;
         if (c < CPB) {
-            const uint16_t* src = srcA[c] + (size_t)t * BK;
+            const uint16_t* src = cur.a[c] + (size_t)t * BK;
             if (TAIL) {
                 const int v = g.K - (t * BK + kcA[c]);
-                if (v < 8) src = srcA[c] - kcA[c] + (v > 0 ? g.K - 8 : 0);
+                if (v < 8) src = cur.a[c] - kcA[c] + (v > 0 ? g.K - 8 : 0);
             }
             ra[c] = ld16(src);
         } else {
             const int i = c - CPB;
-            const uint16_t* src = srcB[i] + (size_t)t * kstepB;
+            const uint16_t* src = cur.b[i] + (size_t)t * kstepB;
             if (TAIL) {
                 if (OPB == 1) {
                     const int v = g.K - (t * BK + kcB[i]);
-                    if (v < 8) src = srcB[i] - kcB[i] + (v > 0 ? g.K - 8 : 0);
+                    if (v < 8) src = cur.b[i] - kcB[i] + (v > 0 ? g.K - 8 : 0);
                 } else if (t * BK + kcB[i] >= g.K) {
-                    src = srcB[i] + (size_t)(g.K - 1 - kcB[i]) * g.ldb;  // row K - 1, written as zeros
+                    src = cur.b[i] + (size_t)(g.K - 1 - kcB[i]) * g.ldb;  // row K - 1, written as zeros
                 }
             }
             rb[i] = ld16(src);
@@ -259,7 +277,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
             if (OPB == 1) {
                 if (TAIL) v = keep_first8(v, g.K - (t * BK + kcB[i]));
             } else {
-                if (nedge) v = keep_first8(v, nvB[i]);
+                if (nedge) v = keep_first8(v, cur.nv[i]);
                 if (TAIL && t * BK + kcB[i] >= g.K) v = u32x4{0, 0, 0, 0};
             }
             addr = dstB + (uint32_t)(t & 3) * STAGE_BYTES + (uint32_t)i * 1024u;
@@ -347,21 +365,85 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     // One step: 4*SJ MFMAs from `cur`, each followed by at most two other instructions
     // in a fixed order: the fragment reads of `nxt` two at a time after the first
     // MFMAs (early, so they are done by the wait that ends the step), then this wave's
-    // CPB copies of tile `ct` (half `half`: 0 = A, 1 = B) after every other MFMA of the
-    // second half of the step.
+    // CPB copies of k-tile `ct` of the tile with sources `cs` into stage `cst` (half
+    // `half`: 0 = A, 1 = B) after every other MFMA of the second half of the step.
     constexpr int NM = 4 * SJ;  // MFMAs per step
-    auto step = [&](const Frags& cur, Frags& nxt, int rst, int rks, bool do_copy, int ct, int half, auto tail_tag) {
+    auto step = [&](const Frags& cur_f, Frags& nxt_f, int rst, int rks, bool do_copy, const Src& cs, int ct,
+                    uint32_t cst, int half, auto tail_tag) {
 #pragma unroll
         for (int k = 0; k < NM; ++k) {
-            mfma(cur, k / SJ, k % SJ);
-            if (2 * k < NREAD) read_one(nxt, rst, rks, 2 * k);
-            if (2 * k + 1 < NREAD) read_one(nxt, rst, rks, 2 * k + 1);
+            mfma(cur_f, k / SJ, k % SJ);
+            if (2 * k < NREAD) read_one(nxt_f, rst, rks, 2 * k);
+            if (2 * k + 1 < NREAD) read_one(nxt_f, rst, rks, 2 * k + 1);
             const int c = (k - NM / 2) >> 1;
             if (do_copy && k >= NM / 2 && (k & 1) == 0 && c < CPB) {
-                if (half == 0) copy_a(ct, c, tail_tag);
-                else copy_b(ct, c, tail_tag);
+                if (half == 0) copy_a(cs, ct, cst, c, tail_tag);
+                else copy_b(cs, ct, cst, c, tail_tag);
             }
             __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // ---- epilogues. Before either, every wave's last fragment reads are done
+    // (lgkmcnt(0) at the end of the last iteration) and a barrier makes sure all of
+    // them are before any wave overwrites a stage. The empty asm before that barrier
+    // stands between the MFMAs and the reads of their results, so the compiler's hazard
+    // padding does not see the MFMA as the last writer: the 18 wait states a 16-pass
+    // MFMA result needs are given here.
+    const int wrow0 = wm * 128, wcol0 = wn * 32 * SJ;  // the wave's tile within the output tile
+    auto store4 = [&](int m, int n, f32x4 v) {
+        if (m < g.M) {
+            if (g.ep.kind == 0) store_run4<false>(g, m, n, v);
+            else epilogue_run4_body(g.ep, g.C, g.ldc, g.N, m, n, v);
+        }
+    };
+    // The whole LDS, 64 rows of the wave tile at a time: each wave owns a slot of 64
+    // rows x WT bytes (WT = 32*SJ fp32 = 512 or 256 bytes): NW = 4: 32 KB, waves 0-1 in
+    // sA, 2-3 in sB; NW = 8: 16 KB, waves 0-3 in sA, 4-7 in sB. Register r of subtile
+    // (i, j) holds row 32i + l32 of the wave tile and columns 32j + 8(r/4) + 4*lh + r%4:
+    // chunk c = 8j + 2(r/4) + lh of 16 bytes, stored at position c ^ (row & 15) of its
+    // row, which keeps both the writes (16 rows per lane phase) and the whole-row reads
+    // free of bank conflicts; each store instruction writes 2 (NW = 4) or 4 (NW = 8)
+    // whole rows of the wave tile, contiguous in C.
+    auto full_epilogue = [&](const Src& s) {
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
+        __syncthreads();
+        constexpr int WT = 32 * SJ * 4;           // bytes per wave-tile row
+        constexpr int CPR = WT / 16;              // 16-byte chunks per row
+        constexpr int RPI = 64 / CPR;             // rows per read instruction
+        constexpr int SLOT = 64 * WT;
+        char* slot = reinterpret_cast<char*>(wave < NW / 2 ? &sA[0][0] : &sB[0][0]) + (wave % (NW / 2)) * SLOT;
+        const int cm0 = s.m0 + wrow0, cn0 = s.n0 + wcol0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int ii = 0; ii < 2; ++ii) {
+                const int i = 2 * h + ii;
+                const int row = ii * 32 + l32;
+#pragma unroll
+                for (int j = 0; j < SJ; ++j) {
+                    // one subtile at a time: the empty asm pins acc[i][j] in the accumulation
+                    // registers until here (otherwise all accumulators are copied out at
+                    // once, which needs more registers than exist)
+                    asm volatile("" : "+a"(acc[i][j]));
+#pragma unroll
+                    for (int rg = 0; rg < 4; ++rg) {
+                        const int c = j * 8 + rg * 2 + lh;
+                        *reinterpret_cast<f32x4*>(slot + row * WT + ((c ^ (row & 15)) << 4)) =
+                            f32x4{acc[i][j][4 * rg], acc[i][j][4 * rg + 1], acc[i][j][4 * rg + 2], acc[i][j][4 * rg + 3]};
+                    }
+                }
+            }
+            // only this wave touches its slot; the wave barrier keeps the compiler from
+            // moving LDS accesses across the write / read phases, which the hardware runs
+            // in order within a wave
+            __builtin_amdgcn_wave_barrier();
+            for (int it = 0; it < 64 / RPI; ++it) {
+                const int row = it * RPI + lane / CPR, c = lane % CPR;
+                const f32x4 v = *reinterpret_cast<const f32x4*>(slot + row * WT + ((c ^ (row & 15)) << 4));
+                store4(cm0 + h * 64 + row, cn0 + c * 4, v);
+            }
+            __builtin_amdgcn_wave_barrier();
         }
     };
 
@@ -444,20 +526,22 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     for (; ktail && t + 2 == nk; ++t) iteration_reg(t, part, none);      // writes the partial tile
     for (; t + 1 < nk; ++t) iteration_reg(t, full, none);
     for (; t < nk; ++t) iteration_reg(t, none, none);
-    } else {
-    // prologue: tiles 0 .. D-1 in flight (A then B of each); tile 0 complete; step
+    full_epilogue(cur);
+    } else if constexpr (!PERSIST) {
+    // ---- the direct-copy form, one output tile per workgroup.
+    // prologue: k-tiles 0 .. D-1 in flight (A then B of each); k-tile 0 complete; step
     // (0, 0) fragments read.
     for (int t = 0; t < D && t < nk; ++t) {
         if (ktail && t == nk - 1) {
 #pragma unroll
-            for (int i = 0; i < CPB; ++i) copy_a(t, i, std::true_type{});
+            for (int i = 0; i < CPB; ++i) copy_a(cur, t, (uint32_t)t, i, yes);
 #pragma unroll
-            for (int i = 0; i < CPB; ++i) copy_b(t, i, std::true_type{});
+            for (int i = 0; i < CPB; ++i) copy_b(cur, t, (uint32_t)t, i, yes);
         } else {
 #pragma unroll
-            for (int i = 0; i < CPB; ++i) copy_a(t, i, std::false_type{});
+            for (int i = 0; i < CPB; ++i) copy_a(cur, t, (uint32_t)t, i, no);
 #pragma unroll
-            for (int i = 0; i < CPB; ++i) copy_b(t, i, std::false_type{});
+            for (int i = 0; i < CPB; ++i) copy_b(cur, t, (uint32_t)t, i, no);
         }
     }
     vm_wait(2 * CPB * (min(D, nk) - 1));
@@ -471,18 +555,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     settle(f0);
 
-    // One iteration (tile t). REFILL: tile t+D exists and is copied (TAIL: it is the
-    // partial last tile). FIX: tile t+1 is the partial last tile, whose chunks past K
-    // are zeroed between the barrier that completes its copies and the first reads of
-    // it. The reads of step (t+1, 0) in the last iteration fetch a stage nobody writes
-    // any more; their values are never used (this keeps the step free of branches).
+    // One iteration (k-tile t, in stage t & 3). REFILL: k-tile t+D exists and is copied
+    // (TAIL: it is the partial last k-tile). FIX: k-tile t+1 is the partial last tile,
+    // whose chunks past K are zeroed between the barrier that completes its copies and
+    // the first reads of it. The reads of step (t+1, 0) in the last iteration fetch a
+    // stage nobody writes any more; their values are never used (this keeps the step
+    // free of branches).
     auto iteration = [&](int t, auto refill_tag, auto tail_tag, auto fix_tag) {
         constexpr bool REFILL = decltype(refill_tag)::value;
         const int st = t & 3;
-        // step (t, 0): MFMAs from f0; read step (t, 1) into f1; copy A of tile t+D
-        step(f0, f1, st, 1, REFILL, t + D, 0, tail_tag);
-        // own reads done; own copies of tile t+1 done (those of tiles t+2 .. t+D-1 and
-        // the A half of tile t+D may still be in flight); then the barrier
+        // step (t, 0): MFMAs from f0; read step (t, 1) into f1; copy A of k-tile t+D
+        step(f0, f1, st, 1, REFILL, cur, t + D, (uint32_t)((t + D) & 3), 0, tail_tag);
+        // own reads done; own copies of k-tile t+1 done (those of k-tiles t+2 .. t+D-1
+        // and the A half of k-tile t+D may still be in flight); then the barrier
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (REFILL) vm_wait_n<2 * CPB * (D - 2) + CPB>();
         else vm_wait(2 * CPB * max(0, nk - t - 2));
@@ -492,14 +577,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
             asm volatile("s_barrier" ::: "memory");
         }
         settle(f1);
-        // step (t, 1): MFMAs from f1; read step (t+1, 0) into f0; copy B of tile t+D
-        step(f1, f0, (t + 1) & 3, 0, REFILL, t + D, 1, tail_tag);
+        // step (t, 1): MFMAs from f1; read step (t+1, 0) into f0; copy B of k-tile t+D
+        step(f1, f0, (t + 1) & 3, 0, REFILL, cur, t + D, (uint32_t)((t + D) & 3), 1, tail_tag);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         settle(f0);
     };
     // straight runs of one variant each (a branch between two inlined variants inside
     // a loop leaves the register allocator unable to keep the fragments in registers)
-    const int nfull = ktail ? nk - 1 : nk;  // tiles t + D copied by the plain variant
+    const int nfull = ktail ? nk - 1 : nk;  // k-tiles t + D copied by the plain variant
     int t = 0;
     for (; t + D < nfull; ++t) iteration(t, yes, no, no);
     for (; ktail && t + D == nk - 1; ++t) iteration(t, yes, yes, no);  // copies the partial tile
@@ -507,61 +592,114 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     for (; t < nfix; ++t) iteration(t, no, no, no);
     for (; ktail && t == nk - 2; ++t) iteration(t, no, no, yes);
     for (; t < nk; ++t) iteration(t, no, no, no);
-    }
-
-    // ---- epilogue through LDS. Every wave's last reads are done (lgkmcnt(0) above);
-    // the barrier makes sure all of them are before any wave overwrites a stage. The
-    // empty asm in the write loop stands between the MFMAs and the reads of their
-    // results, so the compiler's hazard padding does not see the MFMA as the last
-    // writer: the 18 wait states a 16-pass MFMA result needs are given here.
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
-    __syncthreads();
-    // Each wave owns a slot of 64 rows x WT bytes (WT = 32*SJ fp32 = 512 or 256 bytes):
-    // NW = 4: 32 KB, waves 0-1 in sA, 2-3 in sB; NW = 8: 16 KB, waves 0-3 in sA, 4-7
-    // in sB. Register r of subtile (i, j) holds row 32i + l32 of the wave tile and
-    // columns 32j + 8(r/4) + 4*lh + r%4: chunk c = 8j + 2(r/4) + lh of 16 bytes, stored
-    // at position c ^ (row & 15) of its row, which keeps both the writes (16 rows per
-    // lane phase) and the whole-row reads free of bank conflicts.
-    constexpr int WT = 32 * SJ * 4;           // bytes per wave-tile row
-    constexpr int CPR = WT / 16;              // 16-byte chunks per row
-    constexpr int RPI = 64 / CPR;             // rows per read instruction
-    constexpr int SLOT = 64 * WT;
-    char* slot = reinterpret_cast<char*>(wave < NW / 2 ? &sA[0][0] : &sB[0][0]) + (wave % (NW / 2)) * SLOT;
-    const int cm0 = m0 + wm * 128, cn0 = n0 + wn * 32 * SJ;
+    full_epilogue(cur);
+    } else {
+    // ---- the direct-copy form on a persistent grid: each workgroup takes one tile of
+    // each round of `grid` tiles until a round has none for it (K a multiple of 32
+    // with more than D k-tiles, checked by the host). The stream of k-tile copies runs on across tiles: the last D iterations of
+    // a tile, which have no k-tile of their own left to copy, copy k-tiles 0 .. D-1 of
+    // the workgroup's next tile into the stages that follow, so the next tile starts
+    // with its first D k-tiles in LDS and no pipeline fill. The finished tile's
+    // epilogue goes through the one stage the next tile does not yet occupy (that of
+    // the finished tile's last k-tile), one 32 x 32 subtile (4 KB per wave) at a time.
+    // Before its first global store each wave waits for all of its copies (only loads
+    // are in flight then, and loads complete in order), so the next tile's first two
+    // iterations need no memory wait and no later wait for a copy is counted across a
+    // store issued after that copy: gfx950 counts stores and loads on one counter and
+    // may complete them out of order.
+    Src nxt;              // the next tile's sources
+    uint32_t sb = 0;      // stage of the current tile's k-tile 0
+    bool primed = false;  // k-tiles 0 .. D-1 of the current tile are complete in LDS
+    for (;;) {
+        const int ntile = round_tile(round + 1, tiles_total, g.xcd_remap);
+        const bool has_next = ntile >= 0;
+        if (has_next) make_src(ntile, nxt);
+        if (!primed) {
+            for (int t = 0; t < D; ++t) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+                for (int i = 0; i < CPB; ++i) copy_a(cur, t, (uint32_t)t, i, no);
 #pragma unroll
-        for (int ii = 0; ii < 2; ++ii) {
-            const int i = 2 * h + ii;
-            const int row = ii * 32 + l32;
+                for (int i = 0; i < CPB; ++i) copy_b(cur, t, (uint32_t)t, i, no);
+            }
+            vm_wait_n<2 * CPB * (D - 1)>();
+            asm volatile("s_barrier" ::: "memory");
+        }
+#pragma unroll
+        for (int r = 0; r < NREAD; ++r) read_one(f0, (int)(sb & 3u), 0, r);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        settle(f0);
+        // One iteration (k-tile t, stage (sb + t) & 3). LAST: one of the last D, which
+        // copies k-tile t + D - nk of the next tile when there is one (a uniform branch
+        // around the copies) and otherwise nothing. A primed tile's first two
+        // iterations skip the memory wait: their k-tiles 1 and 2 are complete.
+        auto iteration = [&](int t, auto last_tag) {
+            constexpr bool LAST = decltype(last_tag)::value;
+            const uint32_t st = (sb + (uint32_t)t) & 3u;
+            const uint32_t cst = (sb + (uint32_t)(t + D)) & 3u;
+            const bool copy = !LAST || has_next;
+            const Src& cs = LAST ? nxt : cur;
+            const int ct = LAST ? t + D - nk : t + D;
+            step(f0, f1, (int)st, 1, copy, cs, ct, cst, 0, no);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if (!(primed && t < 2)) {
+                if (!LAST) vm_wait_n<2 * CPB * (D - 2) + CPB>();
+                else vm_wait(copy ? 2 * CPB * (D - 2) + CPB : 2 * CPB * max(0, nk - t - 2));
+            }
+            asm volatile("s_barrier" ::: "memory");
+            settle(f1);
+            step(f1, f0, (int)((st + 1) & 3u), 0, copy, cs, ct, cst, 1, no);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            settle(f0);
+        };
+        int t = 0;
+        for (; t + D < nk; ++t) iteration(t, no);
+        for (; t < nk; ++t) iteration(t, yes);
+        // epilogue through the stage of this tile's last k-tile, (sb + nk - 1) & 3: 4 KB
+        // per wave, one 32 x 32 subtile at a time (32 rows of 128 bytes, chunk c of row r
+        // at c ^ ((r >> 1) & 7), free of bank conflicts for the fragment-layout writes and
+        // for the whole-row reads); each store instruction writes 8 rows of 128 bytes.
+        // The row loop stays rolled, so that the store code (with a fused epilogue's
+        // arithmetic) exists once per subtile.
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
+        __syncthreads();
+        const uint32_t es = (sb + (uint32_t)(nk - 1)) & 3u;
+        char* slot = reinterpret_cast<char*>(wave < NW / 2 ? &sA[es][0] : &sB[es][0]) + (wave % (NW / 2)) * 4096;
+        const int cm0 = cur.m0 + wrow0, cn0 = cur.n0 + wcol0;
+        vm_wait_n<0>();  // the next tile's first k-tiles, before any store
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
 #pragma unroll
             for (int j = 0; j < SJ; ++j) {
-                // one subtile at a time: the empty asm pins acc[i][j] in the accumulation
-                // registers until here (otherwise all accumulators are copied out at once,
-                // which needs more registers than exist)
                 asm volatile("" : "+a"(acc[i][j]));
 #pragma unroll
                 for (int rg = 0; rg < 4; ++rg) {
-                    const int c = j * 8 + rg * 2 + lh;
-                    *reinterpret_cast<f32x4*>(slot + row * WT + ((c ^ (row & 15)) << 4)) =
+                    const int c = rg * 2 + lh;
+                    *reinterpret_cast<f32x4*>(slot + l32 * 128 + ((c ^ ((l32 >> 1) & 7)) << 4)) =
                         f32x4{acc[i][j][4 * rg], acc[i][j][4 * rg + 1], acc[i][j][4 * rg + 2], acc[i][j][4 * rg + 3]};
                 }
+                __builtin_amdgcn_wave_barrier();
+#pragma clang loop unroll(disable)
+                for (int it = 0; it < 4; ++it) {
+                    const int row = it * 8 + (lane >> 3), c = lane & 7;
+                    const f32x4 v = *reinterpret_cast<const f32x4*>(slot + row * 128 + ((c ^ ((row >> 1) & 7)) << 4));
+                    store4(cm0 + 32 * i + row, cn0 + 32 * j + c * 4, v);
+                }
+                __builtin_amdgcn_wave_barrier();
             }
         }
-        // only this wave touches its slot; the wave barrier keeps the compiler from
-        // moving LDS accesses across the write / read phases, which the hardware runs
-        // in order within a wave
-        __builtin_amdgcn_wave_barrier();
-        for (int it = 0; it < 64 / RPI; ++it) {
-            const int row = it * RPI + lane / CPR, c = lane % CPR;
-            const f32x4 v = *reinterpret_cast<const f32x4*>(slot + row * WT + ((c ^ (row & 15)) << 4));
-            const int m = cm0 + h * 64 + row;
-            if (m < g.M) {
-                if (g.ep.kind == 0) store_run4<false>(g, m, cn0 + c * 4, v);
-                else epilogue_run4_body(g.ep, g.C, g.ldc, g.N, m, cn0 + c * 4, v);
-            }
-        }
-        __builtin_amdgcn_wave_barrier();
+        if (!has_next) break;
+        // every wave's slot reads are done before the next tile refills this stage
+        __syncthreads();
+        primed = true;
+        sb = (sb + (uint32_t)nk) & 3u;
+        cur = nxt;
+        tile = ntile;
+        ++round;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < SJ; ++j) acc[i][j] = f32x16{};
+    }
     }
 }
 

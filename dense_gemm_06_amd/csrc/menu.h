@@ -43,6 +43,15 @@ constexpr bool schedule_enabled(int sched) { return sched != 3; }
 // zeroed past K); edge tiles in M and N copy clamped rows and columns.
 constexpr bool direct_copy(int sched) { return sched == 2 || sched == 4 || sched == 5; }
 
+// Configurations with a persistent single-problem form (a grid below the tile count,
+// each workgroup striding through the tiles): the 8-wave software-pipelined
+// direct-copy kernel, with K (padded K when packed) whole k-tiles of 32, more than
+// three of them. (The 4-wave form's 256 accumulators do not stay in registers
+// across its tile loop.)
+constexpr bool persistent_capable(int sched, int threads, int64_t K) {
+    return sched == 5 && threads == 512 && K % 32 == 0 && K / 32 > 3;
+}
+
 // Configurations whose kernel applies a fused epilogue (every other one stores the
 // plain fp32 accumulator only): all but the 32x32x16 ping-pong kernel.
 constexpr bool epilogue_capable(int sched) { return sched != 4; }

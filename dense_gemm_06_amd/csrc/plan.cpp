@@ -223,7 +223,7 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
     const bool dma_ok = aligned16(a) && aligned16(b) && (lda * es) % 16 == 0 && (ldb * es) % 16 == 0;
 
     int want_variant = GEMM_VARIANT_AUTO, want_bm = 0, want_bn = 0, want_vec = -1, want_remap = -1, want_group = 0;
-    int want_wm = 0, want_wn = 0, want_sched = 0, want_split = 0, want_pack = 0, want_threads = 0;
+    int want_wm = 0, want_wn = 0, want_sched = 0, want_split = 0, want_pack = 0, want_threads = 0, want_grid = 0;
     if (ws_bytes < 0) {
         set_error("workspace_bytes = %lld must be non-negative", (long long)ws_bytes);
         return GEMM_ERR_INVALID_VALUE;
@@ -246,6 +246,11 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
         want_threads = req->threads;
         if (want_threads < 0) {
             set_error("threads = %d must be non-negative", want_threads);
+            return GEMM_ERR_INVALID_VALUE;
+        }
+        want_grid = req->max_grid;
+        if (want_grid < 0) {
+            set_error("max_grid = %d must be non-negative", want_grid);
             return GEMM_ERR_INVALID_VALUE;
         }
         if (want_sched < 0 || want_sched > 7 || want_wm < 0 || want_wn < 0 || want_variant < 0 || want_variant > 2 || want_vec < -1 || want_vec > 1 || want_remap < -1 ||
@@ -285,7 +290,7 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
 
     const MenuEntry* best = nullptr;
     double best_cost = 0;
-    int64_t best_split = 1, best_chunk = K, short_ws = -1;
+    int64_t best_split = 1, best_chunk = K, short_ws = -1, best_grid = 0;
     bool best_packed = false;
     for (int pass = 0; pass < 2; ++pass) {
     const bool packed = pass == 1;
@@ -324,6 +329,25 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
         const int64_t ktiles = (Kx + e.bk - 1) / e.bk;
         const int occ = blocks_per_cu(e);
         const int64_t concurrent = (int64_t)num_cus * occ;
+        // A grid capped below the tile count: the persistent form of the
+        // software-pipelined direct-copy kernel (whole k-tiles, more than the three
+        // its copy stream runs ahead), each workgroup taking one tile per round.
+        // Without a cap it is the default where it applies and the tiles outnumber
+        // the workgroups the machine holds at once: one workgroup per slot, whose
+        // copies of a tile's first k-tiles overlap the previous tile's last ones.
+        // Medians of five alternated passes against one workgroup per tile (8 waves):
+        // 8192^2 x 512 fp16 98.8 against 104.1 us, 8192^2 x 2048 fp16 255.5 against
+        // 271.9, 16384 x 8192 x 1024 fp16 302.0 against 340.1, 6144^2 x 2048 bf16
+        // 162.2 against 166.0, 8192^3 bf16 892.8 against 906.1; with bias, GELU and
+        // bf16 output 8192^2 x 1024 fp16 198.5 against 203.6, 8192^2 x 4096 523.0
+        // against 533.2.
+        int64_t grid_e = tiles;
+        if (want_grid > 0 && tiles > want_grid) {
+            if (!persistent_capable(e.sched, e.threads, Kx)) continue;
+            grid_e = want_grid;
+        } else if (want_grid == 0 && tiles > concurrent && persistent_capable(e.sched, e.threads, Kx)) {
+            grid_e = concurrent;
+        }
         // split candidates: none, or S slices of whole k-tiles (register-staged kernels)
         const int cand[] = {1, 2, 4, 8, 16};
         for (int ci = 0; ci < (want_split >= 2 ? 1 : 5); ++ci) {
@@ -342,9 +366,15 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
                     continue;
                 }
             }
+            if (grid_e < tiles && S != 1) continue;
             const int64_t work = tiles * slices;
-            const int64_t rounds = (work + concurrent - 1) / concurrent;
-            const int64_t resident = std::min<int64_t>(occ, (work + num_cus - 1) / num_cus);
+            // persistent: ceil(tiles / grid) tiles per workgroup, the grid in waves of
+            // `concurrent` workgroups
+            const int64_t rounds = grid_e < tiles ? ((grid_e + concurrent - 1) / concurrent) *
+                                                        ((tiles + grid_e - 1) / grid_e)
+                                                  : (work + concurrent - 1) / concurrent;
+            const int64_t resident =
+                std::min<int64_t>(occ, ((grid_e < tiles ? grid_e : work) + num_cus - 1) / num_cus);
             const int64_t kpad = ((std::min<int64_t>(chunk, Kx) + e.bk - 1) / e.bk) * e.bk;
             // The software-pipelined kernel (schedule 5) against the ping-pong kernel and
             // its own 4-wave form, medians of three alternated passes: 8 waves are best or
@@ -393,6 +423,7 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
                 best_split = slices;
                 best_chunk = chunk;
                 best_packed = packed;
+                best_grid = grid_e;
             }
         }
     }
@@ -403,8 +434,11 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
         return GEMM_ERR_INVALID_VALUE;
     }
     if (!best) {
-        set_error("no compiled kernel matches: dtype %s, opB %s, variant %d, bm %d, bn %d, vec %d",
-                  dtype_name(dtype), opB == GEMM_OP_N ? "N" : "T", want_variant, want_bm, want_bn, want_vec);
+        set_error("no compiled kernel matches: dtype %s, opB %s, variant %d, bm %d, bn %d, vec %d%s",
+                  dtype_name(dtype), opB == GEMM_OP_N ? "N" : "T", want_variant, want_bm, want_bn, want_vec,
+                  want_grid > 0 ? " (a max_grid below the tile count needs the 8-wave schedule-5 kernel: 16-byte "
+                                  "aligned operands or packing, K a multiple of 32 and at least 128, no split)"
+                                : "");
         return GEMM_ERR_UNSUPPORTED;
     }
     const MenuEntry& e = *best;
@@ -425,7 +459,8 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
     cfg.schedule = e.sched;
     cfg.tiles_m = ((best_packed && direct_copy(e.sched) ? Mp : M) + e.bm - 1) / e.bm;
     cfg.tiles_n = ((best_packed && direct_copy(e.sched) ? Np : N) + e.bn - 1) / e.bn;
-    cfg.grid = (int32_t)(cfg.tiles_m * cfg.tiles_n);
+    cfg.grid = (int32_t)std::min<int64_t>(cfg.tiles_m * cfg.tiles_n, best_grid);
+    cfg.max_grid = want_grid;
     // Group enough tile rows that one XCD's share of the grid forms a compact
     // rectangle; the remap needs the grid to split evenly over the 8 XCDs.
     const int gm = want_group ? want_group : default_group_m(cfg.tiles_m, cfg.tiles_n);

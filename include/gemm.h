@@ -106,7 +106,14 @@ typedef struct gemm_config {
     double est_cycles; /* out: the heuristic's cost estimate (clock cycles) */
     int64_t tiles_total; /* out: output tiles of the call (grouped: of all its problems) */
     int32_t launches;    /* out: kernel launches the call makes */
-    int32_t max_grid;    /* in (grouped calls only): cap on persistent workgroups per launch, 0 = any */
+    int32_t max_grid;    /* in/out: cap on the workgroups of a launch, 0 = heuristic. Grouped calls:
+                            the persistent grid. Single calls: a cap below the output tile
+                            count selects the persistent form of schedule 5 with 8 waves (each
+                            workgroup takes one tile per round of `grid` tiles; K, padded K
+                            when packed, a multiple of 32 and at least 128; no split), the only
+                            kernel that has one; 0 lets the heuristic use that form with one
+                            workgroup per compute unit when the tiles outnumber the compute
+                            units; a cap at or above the tile count means one workgroup per tile */
     int32_t split_k;     /* in/out: K slices; in: 0 = heuristic, 1 = no split, S >= 2 = S slices (fewer
                             if K has fewer k-tiles); splitting needs a workspace (gemm_ex_workspace) */
     int32_t k_chunk;     /* out: K elements per slice (K when not split) */

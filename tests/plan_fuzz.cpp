@@ -80,7 +80,7 @@ static void random_request(gemm_config* r) {
 }
 
 static void check_plan(int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int dtype, uintptr_t a,
-                       uintptr_t b, int64_t ws, bool epi, const gemm_config* req, const gemm_config& c) {
+                       uintptr_t b, int64_t ws, bool epi, const gemm_config* req, const gemm_config& c, int cus) {
     CHECK(c.kernel_id >= 0 && c.kernel_id < kMenuSize, "kernel %d", c.kernel_id);
     if (c.kernel_id < 0 || c.kernel_id >= kMenuSize) return;
     const MenuEntry& e = kMenu[c.kernel_id];
@@ -101,7 +101,18 @@ static void check_plan(int opB, int64_t M, int64_t N, int64_t K, int64_t lda, in
         CHECK(c.tiles_m >= 1 && c.tiles_n >= 1 && c.tiles_m * c.bm >= M && c.tiles_n * c.bn >= N,
               "tiles %lld x %lld of %d x %d for %lld x %lld", (long long)c.tiles_m, (long long)c.tiles_n, c.bm, c.bn,
               (long long)M, (long long)N);
-        CHECK((int64_t)c.grid == c.tiles_m * c.tiles_n, "grid %d", c.grid);
+        // one workgroup per tile, or a persistent grid of the 8-wave software-pipelined
+        // kernel on whole k-tiles (padded K when packed), no split: the requested cap,
+        // or without one a workgroup per compute unit (one fits per unit)
+        const int64_t tiles = c.tiles_m * c.tiles_n;
+        const int64_t Kx = packed ? (K + 63) / 64 * 64 : K;
+        const bool capped = req && req->max_grid > 0;
+        CHECK((int64_t)c.grid == tiles ||
+                  (c.grid < tiles && persistent_capable(e.sched, e.threads, Kx) && c.split_k == 1 &&
+                   c.grid == (capped ? req->max_grid : cus)),
+              "grid %d for %lld tiles (max_grid %d, schedule %d, K %lld)", c.grid, (long long)tiles,
+              req ? req->max_grid : 0, e.sched, (long long)K);
+        if (req && req->max_grid > 0) CHECK(c.grid <= req->max_grid, "grid %d above max_grid %d", c.grid, req->max_grid);
     }
     if (e.vec && !packed) CHECK(a % es == 0 && b % es == 0, "16-byte loads on bases not aligned to the element");
     if (direct_copy(e.sched) && !packed) {
@@ -159,7 +170,7 @@ int main(int argc, char** argv) {
         CHECK(st >= GEMM_OK && st <= GEMM_ERR_LAUNCH, "status %d", st);
         if (st == GEMM_OK) {
             ++ok;
-            check_plan(opB, M, N, K, lda, ldb, dtype, a, b, ws, epi, with_req ? &req : nullptr, out);
+            check_plan(opB, M, N, K, lda, ldb, dtype, a, b, ws, epi, with_req ? &req : nullptr, out, cus);
         } else {
             ++rejected;
             CHECK(last_error() && last_error()[0], "status %d without a message", st);

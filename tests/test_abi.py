@@ -201,6 +201,50 @@ def test_plan_never_selects_removed_schedule():
     assert "removed" in dg.gemm_last_error()
 
 
+def test_plan_persistent_grid():
+    """max_grid below the tile count on a single call: the persistent form of the
+    8-wave schedule-5 kernel (whole k-tiles of 32, at least four, no split); a cap at
+    or above the tile count changes nothing; shapes the persistent form cannot take
+    are refused with the reason."""
+    for dtype in ("f16", "bf16"):
+        for op_b in "NT":
+            st, c = plan(8192, 8192, 1024, dtype, op_b, req=dg.request(max_grid=256))
+            assert st == 0 and c.grid == 256 and c.schedule == 5 and c.threads == 512 and c.max_grid == 256
+            assert c.tiles_m * c.tiles_n == 1024 and c.xcd_remap == 1
+            st, c = plan(1000, 1304, 256, dtype, op_b, req=dg.request(max_grid=3))
+            assert st == 0 and c.grid == 3 and c.schedule == 5 and c.xcd_remap == 0
+    # without a cap: the persistent grid of one workgroup per compute unit where the
+    # tiles outnumber the compute units, one workgroup per tile otherwise
+    for dtype, op_b in (("f16", "N"), ("bf16", "T")):
+        st, c = plan(8192, 8192, 1024, dtype, op_b)
+        assert st == 0 and c.schedule == 5 and c.threads == 512 and c.grid == 256 and c.xcd_remap == 1
+        st, c = plan(8192, 8192, 1024, dtype, op_b, cus=304)
+        assert st == 0 and c.schedule == 5 and c.grid == 304
+        st, c = plan(8192, 8192, 1024, dtype, op_b, req=dg.request(max_grid=1 << 20))
+        assert st == 0 and c.grid == 1024
+    st, c = plan(8192, 8192, 1000, "f16")   # partial last k-tile: no persistent form
+    assert st == 0 and c.grid == c.tiles_m * c.tiles_n
+    st, c = plan(4096, 4096, 4096, "f16", req=dg.request(max_grid=256))
+    assert st == 0 and c.grid == 256 and c.schedule == 5
+    st, c = plan(4096, 4096, 4096, "f16", req=dg.request(max_grid=100000))
+    assert st == 0 and c.grid == 256
+    # the persistent form needs at least four whole k-tiles of 32
+    for K in (96, 1000, 1036):
+        st, c = plan(8192, 8192, K, "f16", req=dg.request(max_grid=256))
+        assert st == dg.GEMM_ERR_UNSUPPORTED and "max_grid" in dg.gemm_last_error(), K
+    # the 4-wave form, a split and the other schedules have no persistent single-call form
+    st, c = plan(8192, 8192, 1024, "f16", req=dg.request(max_grid=256, waves_n=2, schedule=5))
+    assert st == dg.GEMM_ERR_UNSUPPORTED
+    st, c = plan(8192, 8192, 1024, "f16", req=dg.request(max_grid=256, schedule=7))
+    assert st == dg.GEMM_ERR_UNSUPPORTED
+    st, c = plan(8192, 8192, 1024, "f32", req=dg.request(max_grid=256))
+    assert st == dg.GEMM_ERR_UNSUPPORTED
+    st, c = plan(512, 512, 1024, "f32", req=dg.request(max_grid=256))
+    assert st == 0 and c.grid <= 256
+    st, c = plan(64, 64, 64, "f16", req=dg.request(max_grid=-1))
+    assert st == dg.GEMM_ERR_INVALID_VALUE
+
+
 def test_plan_fills_the_machine():
     """A smaller problem gets smaller tiles so that the grid covers the compute units."""
     st, c = plan(1024, 1024, 1024, "f32")
