@@ -380,6 +380,8 @@ def kernel_name(cfg, dtype):
     else:
         base = {1: "mfma16_gemm", 2: "mfma16_pp (16x16x32)", 4: "mfma16_pp (32x32x16)",
                 5: "mfma32_sp (32x32x16)", 7: "mfma32_sp, register-staged (32x32x16)"}[cfg.schedule]
+    if cfg.grid < cfg.tiles_total:
+        base += f", persistent grid of {cfg.grid}"
     return f"{base} {cfg.bm}x{cfg.bn}x{cfg.bk} waves {cfg.waves_m}x{cfg.waves_n}"
 
 
@@ -459,8 +461,12 @@ def main():
         fe = time_fused_epilogue(headline, max(5, a.steps // 2), max(2, a.warmup // 2))
     extras = {}
     if not a.no_extra and not a.only:
-        for name in ("c3_f32_4096", "c1_f32_256", "c2_f32_1024", "c5_bf16_ragged", "m8_f16_shard", "m8_f32_shard"):
+        for name in ("c3_f32_4096", "c1_f32_256", "c2_f32_1024", "c5_bf16_ragged", "m8_f16_shard", "m8_f32_shard",
+                     "r4_f16_8192x8192x2048"):
             extras[name] = time_problem(name, max(5, a.steps // 2), max(2, a.warmup // 2))
+        # the same four-round problem with one workgroup per tile (no persistent grid)
+        one_per_tile = time_problem("r4_f16_8192x8192x2048", max(5, a.steps // 2), max(2, a.warmup // 2),
+                                    force={"max_grid": 1 << 30})
 
     cfg = main_res["cfg"]
     traffic = load_traffic(headline, cfg)
@@ -507,6 +513,13 @@ def main():
                                      "tile": f"{v['cfg'].bm}x{v['cfg'].bn}",
                                      "variant": "mfma" if v["cfg"].variant == 2 else "lds"}
                                  for k, v in extras.items()}
+        for k, v in extras.items():
+            out["other_problems"][k]["grid"] = v["cfg"].grid
+        r = one_per_tile
+        out["other_problems"]["r4_f16_8192x8192x2048"].update(
+            workload="C=A@B 8192x8192x2048 f16: four rounds of 256 tiles on the persistent grid",
+            one_workgroup_per_tile={"tflops": round(r["tflops"], 3), "ms_per_step": round(r["ms_per_step"], 6),
+                                    "grid": r["cfg"].grid})
         # the under-filled problems again with a workspace (the heuristic may split K),
         # and a long-K problem with 16 output tiles, where splitting pays
         lk = time_problem("k1_f32_long_k", max(5, a.steps // 2), max(2, a.warmup // 2))

@@ -656,8 +656,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
         for (; t < nk; ++t) iteration(t, yes);
         // epilogue through the stage of this tile's last k-tile, (sb + nk - 1) & 3: 4 KB
         // per wave, one 32 x 32 subtile at a time (32 rows of 128 bytes, chunk c of row r
-        // at c ^ ((r >> 1) & 7), free of bank conflicts for the fragment-layout writes and
-        // for the whole-row reads); each store instruction writes 8 rows of 128 bytes.
+        // at c ^ (r & 7); the bank-conflict counter reads zero for both the
+        // fragment-layout writes and the whole-row reads, where c ^ ((r >> 1) & 7) made
+        // every write take two passes); each store instruction writes 8 rows of 128 bytes.
         // The row loop stays rolled, so that the store code (with a fused epilogue's
         // arithmetic) exists once per subtile.
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
@@ -674,14 +675,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 #pragma unroll
                 for (int rg = 0; rg < 4; ++rg) {
                     const int c = rg * 2 + lh;
-                    *reinterpret_cast<f32x4*>(slot + l32 * 128 + ((c ^ ((l32 >> 1) & 7)) << 4)) =
+                    *reinterpret_cast<f32x4*>(slot + l32 * 128 + ((c ^ (l32 & 7)) << 4)) =
                         f32x4{acc[i][j][4 * rg], acc[i][j][4 * rg + 1], acc[i][j][4 * rg + 2], acc[i][j][4 * rg + 3]};
                 }
                 __builtin_amdgcn_wave_barrier();
 #pragma clang loop unroll(disable)
                 for (int it = 0; it < 4; ++it) {
                     const int row = it * 8 + (lane >> 3), c = lane & 7;
-                    const f32x4 v = *reinterpret_cast<const f32x4*>(slot + row * 128 + ((c ^ ((row >> 1) & 7)) << 4));
+                    const f32x4 v = *reinterpret_cast<const f32x4*>(slot + row * 128 + ((c ^ (row & 7)) << 4));
                     store4(cm0 + 32 * i + row, cn0 + 32 * j + c * 4, v);
                 }
                 __builtin_amdgcn_wave_barrier();

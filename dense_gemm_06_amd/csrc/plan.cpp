@@ -335,12 +335,14 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
         // Without a cap it is the default where it applies and the tiles outnumber
         // the workgroups the machine holds at once: one workgroup per slot, whose
         // copies of a tile's first k-tiles overlap the previous tile's last ones.
-        // Medians of five alternated passes against one workgroup per tile (8 waves):
-        // 8192^2 x 512 fp16 98.8 against 104.1 us, 8192^2 x 2048 fp16 255.5 against
-        // 271.9, 16384 x 8192 x 1024 fp16 302.0 against 340.1, 6144^2 x 2048 bf16
-        // 162.2 against 166.0, 8192^3 bf16 892.8 against 906.1; with bias, GELU and
-        // bf16 output 8192^2 x 1024 fp16 198.5 against 203.6, 8192^2 x 4096 523.0
-        // against 533.2.
+        // Medians of five alternated passes against one workgroup per tile (8 waves,
+        // one box): 8192^2 x 512 fp16 85.1 against 96.6 us, 8192^2 x 2048 fp16 238.3
+        // against 259.9, 16384 x 8192 x 1024 fp16 288.6 against 327.6, 12288^2 x 512
+        // bf16 213.3 against 232.7, 6144^2 x 2048 bf16 151.6 against 156.2, 4608^2 x
+        // 1024 fp16 56.7 against 59.3, 4352^2 x 256 fp16 27.1 against 28.8, 8192^3
+        // bf16 852.6 against 859.2; with bias, GELU and bf16 output 8192^2 x 1024 fp16
+        // 181.2 against 189.5, 8192^2 x 512 bf16 121.3 against 128.1, 8192^2 x 4096
+        // 497.0 against 508.8.
         int64_t grid_e = tiles;
         if (want_grid > 0 && tiles > want_grid) {
             if (!persistent_capable(e.sched, e.threads, Kx)) continue;

@@ -178,6 +178,8 @@ EXTRA_CONFIGS = {
     # one GPU's share of the 4096^3 problems split 8 ways by rows of A and C
     "m8_f16_shard": dict(M=512, N=4096, K=4096, dtype="f16", dist="uniform", op_b="N"),
     "m8_f32_shard": dict(M=512, N=4096, K=4096, dtype="f32", dist="uniform", op_b="N"),
+    # four rounds of 256 output tiles of 256 x 256 (the persistent grid's case)
+    "r4_f16_8192x8192x2048": dict(M=8192, N=8192, K=2048, dtype="f16", dist="uniform", op_b="N"),
 }
 
 

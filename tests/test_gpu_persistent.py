@@ -109,3 +109,19 @@ def test_persistent_c4_integer_exact(grid):
     Cref, _ = oracle.gemm_ref(ops, want_d=False)
     bad = np.argwhere(C.astype(np.float64) != Cref)
     assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:5].tolist()}"
+
+
+def test_persistent_benchmark_problem_full_size():
+    """The 8192 x 8192 x 2048 fp16 problem (four rounds of 256 tiles) in the
+    configuration the heuristic picks, which is the persistent grid of 256 that the
+    benchmark times: every entry of C against the oracle."""
+    ops = gi.make_config("r4_f16_8192x8192x2048")
+    plan = plan_of(ops, None, ops.N)
+    print(f"persistent benchmark problem: grid {plan.grid}, schedule {plan.schedule}", flush=True)
+    assert plan.schedule == 5 and plan.grid == 256 and plan.tiles_m * plan.tiles_n == 1024
+    C = run_ops(ops, ldc=ops.N, extra_rows=1)
+    check_untouched(C, ops.M, ops.N)
+    Cref, D = oracle.gemm_ref(ops)
+    err = normalized_error(C[:ops.M, :ops.N], Cref, D)
+    print(f"normalized error {err:.3e} over all {ops.M} x {ops.N} entries", flush=True)
+    assert err <= TOL[ops.dtype], err
