@@ -226,12 +226,13 @@ void mfma16_gemm_grouped(GroupArgs ga) {
 // group holds the columns n = 4(l%16) + u, so the four subtiles share one read
 // and, at the store, a lane owns 16 consecutive n of one row of C.
 //
-// KG = 2 splits K inside the workgroup: two groups of WM x WN waves, each with its
-// own LDS stages, take the even and the odd k-tiles; at the end group 1 hands its
-// accumulators to group 0 through LDS and group 0 adds them (group 0's sum first,
-// a fixed order) and stores. With one wave per SIMD a matrix instruction stream
-// issues well below the unit's rate; the second group doubles the waves per SIMD
-// for tiles too small to hold more waves.
+// KG = 2 or 4 splits K inside the workgroup: KG groups of WM x WN waves, each with
+// its own LDS stages, take k-tiles kg, kg + KG, ...; at the end groups 1 .. KG-1
+// hand their accumulators to group 0 through LDS and group 0 adds them in group
+// order (group 0's sum first, a fixed order) and stores. With one wave per SIMD a
+// matrix instruction stream issues well below the unit's rate; the extra groups add
+// waves per SIMD for tiles too small to hold more waves, and shorten each wave's
+// chain of k-tiles where K is short.
 //
 // ST = 3 keeps three LDS stages instead of two, so that the fragments of the next
 // k-tile can be read before the barrier that ends the current one: tile t + 1 was
@@ -241,8 +242,8 @@ void mfma16_gemm_grouped(GroupArgs ga) {
 // half's MFMAs run, so no MFMA waits on an LDS read that was issued just before it.
 template <int OPB, bool VEC, int BM, int BN, int BK, int WM, int WN, int KG = 1, int ST = 2>
 __device__ __forceinline__ void mfma32_tile(const GemmArgs& g, int tm, int tn) {
-    static_assert(KG == 1 || KG == 2, "k groups");
-    static_assert(ST == 2 || (ST == 3 && KG == 1 && BK == 32), "three stages: one k group, k-tiles of 32");
+    static_assert(KG == 1 || KG == 2 || KG == 4, "k groups");
+    static_assert(ST == 2 || (ST == 3 && BK == 32), "three stages: k-tiles of 32");
     constexpr int NT = WM * WN * 64;  // threads of one k group
     constexpr int TWM = BM / WM, TWN = BN / WN;
     constexpr int SM = TWM / 16, SN = TWN / 16, QN = TWN / 64;
@@ -345,6 +346,9 @@ __device__ __forceinline__ void mfma32_tile(const GemmArgs& g, int tm, int tn) {
     // number of iterations (nl) so that all threads reach every barrier
     const int nk = (K + BK - 1) / BK;
     const int nkg = (nk - kg + KG - 1) / KG, nl = (nk + KG - 1) / KG;
+    // k-tile of iteration lt for this group (at or past nk for a group with fewer
+    // k-tiles than nl: the masked loads then bring zeros, which add nothing)
+    auto ktile = [&](int lt) { return lt * KG + kg; };
     auto compute = [&](int cur) {
 #pragma unroll
         for (int kk = 0; kk < BK; kk += 16) {
@@ -473,16 +477,16 @@ __device__ __forceinline__ void mfma32_tile(const GemmArgs& g, int tm, int tn) {
                 }
         };
         Frag f0, f1;
-        if (nk > 0) {
-            load_tiles(0);
+        if (nl > 0) {
+            load_tiles(ktile(0));
             store_tiles(0);
         }
-        if (nk > 1) {
-            load_tiles(1);
+        if (nl > 1) {
+            load_tiles(ktile(1));
             store_tiles(1);
         }
         __syncthreads();
-        if (nk > 0) read_frag(f0, 0, 0);
+        if (nl > 0) read_frag(f0, 0, 0);
         // accumulators in the accumulation registers (measured 0.6% faster than in
         // the vector registers at 4096^3 and 8192^3)
 #pragma unroll
@@ -490,9 +494,9 @@ __device__ __forceinline__ void mfma32_tile(const GemmArgs& g, int tm, int tn) {
 #pragma unroll
             for (int j = 0; j < SN; ++j) asm volatile("" : "+a"(acc[i][j]));
         int cur = 0;  // lt % 3
-        for (int lt = 0; lt < nk; ++lt) {
+        for (int lt = 0; lt < nl; ++lt) {
             const int nxt = cur == 2 ? 0 : cur + 1, far = nxt == 2 ? 0 : nxt + 1;
-            if (lt + 2 < nk) load_tiles(lt + 2);
+            if (lt + 2 < nl) load_tiles(ktile(lt + 2));
             read_frag(f1, cur, 16);
             // the compiler would sink the reads below the MFMAs that should hide them
             __builtin_amdgcn_sched_barrier(0);
@@ -535,12 +539,13 @@ __device__ __forceinline__ void mfma32_tile(const GemmArgs& g, int tm, int tn) {
             __syncthreads();
         }
     }
-    if constexpr (KG == 2) {
-        // group 1's accumulators through LDS (its own A stages, free after the last
-        // barrier), lane-major so that consecutive lanes touch consecutive words
-        static_assert(BM * BN <= 2 * BM * BK, "reduction buffer");
-        float* red = &sAg[1][0][0];
-        if (kg == 1) {
+    if constexpr (KG > 1) {
+        // the accumulators of groups 1 .. KG-1 through LDS (each group's own A stages,
+        // free after the last barrier), lane-major so that consecutive lanes touch
+        // consecutive words; group 0 adds them in group order
+        static_assert(BM * BN <= ST * BM * BK, "reduction buffer");
+        if (kg != 0) {
+            float* red = &sAg[kg][0][0];
 #pragma unroll
             for (int i = 0; i < SM; ++i)
 #pragma unroll
@@ -549,13 +554,17 @@ __device__ __forceinline__ void mfma32_tile(const GemmArgs& g, int tm, int tn) {
                     for (int e = 0; e < 4; ++e) red[(((wave * SM + i) * SN + j) * 4 + e) * 64 + lane] = acc[i][j][e];
         }
         __syncthreads();
-        if (kg == 1) return;
+        if (kg != 0) return;
 #pragma unroll
-        for (int i = 0; i < SM; ++i)
+        for (int q = 1; q < KG; ++q) {
+            const float* red = &sAg[q][0][0];
 #pragma unroll
-            for (int j = 0; j < SN; ++j)
+            for (int i = 0; i < SM; ++i)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[i][j][e] += red[(((wave * SM + i) * SN + j) * 4 + e) * 64 + lane];
+                for (int j = 0; j < SN; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[i][j][e] += red[(((wave * SM + i) * SN + j) * 4 + e) * 64 + lane];
+        }
     }
 
 #pragma unroll

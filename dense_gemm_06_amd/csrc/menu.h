@@ -143,6 +143,19 @@ constexpr bool grouped_capable(int variant, int sched, int bm, int bn, int wm, i
     X(base + 0, V_MFMA, DT_F32, 0, 1, 256, 128, 32, 4, 2, 0, 0, 512, 3 * 4 * 32 * 384, 6)     \
     X(base + 1, V_MFMA, DT_F32, 1, 1, 256, 128, 32, 4, 2, 0, 0, 512, 3 * 4 * 32 * 384, 6)
 
+// Small fp32 tiles. 16 x 64 with K split over four groups of one wave (256 threads,
+// two LDS stages per group): 64 workgroups at 256^3, where 64 x 64 tiles give 16.
+// 64 x 64 with K split over two groups of four waves on the three-stage schedule
+// (6): the next k-tile's fragments read before the barrier, copies two k-tiles
+// ahead.
+#define DG_MFMA_F32SMALL(X, base)                                                        \
+    X(base + 0, V_MFMA, DT_F32, 0, 1, 16, 64, 32, 1, 1, 0, 0, 256, 4 * 2 * 4 * 32 * 80, 1)     \
+    X(base + 1, V_MFMA, DT_F32, 1, 1, 16, 64, 32, 1, 1, 0, 0, 256, 4 * 2 * 4 * 32 * 80, 1)     \
+    X(base + 2, V_MFMA, DT_F32, 0, 0, 16, 64, 32, 1, 1, 0, 0, 256, 4 * 2 * 4 * 32 * 80, 1)     \
+    X(base + 3, V_MFMA, DT_F32, 1, 0, 16, 64, 32, 1, 1, 0, 0, 256, 4 * 2 * 4 * 32 * 80, 1)     \
+    X(base + 4, V_MFMA, DT_F32, 0, 1, 64, 64, 32, 4, 1, 0, 0, 512, 2 * 3 * 4 * 32 * 128, 6)    \
+    X(base + 5, V_MFMA, DT_F32, 1, 1, 64, 64, 32, 4, 1, 0, 0, 512, 2 * 3 * 4 * 32 * 128, 6)
+
 #define DG_MENU(X)                                              \
     DG_LDS_ENTRIES(X, 0, DT_F32, 16)            \
     DG_LDS_ENTRIES(X, 8, DT_F16, 32)            \
@@ -161,9 +174,10 @@ constexpr bool grouped_capable(int variant, int sched, int bm, int bn, int wm, i
     DG_MFMA_KG2(X, 84)                                           \
     DG_MFMA_F32S3(X, 88)                                         \
     DG_MFMA_SPR(X, 90, DT_F16)                                   \
-    DG_MFMA_SPR(X, 94, DT_BF16)
+    DG_MFMA_SPR(X, 94, DT_BF16)                                  \
+    DG_MFMA_F32SMALL(X, 98)
 
-constexpr int kMenuSize = 98;
+constexpr int kMenuSize = 104;
 
 // Fused epilogue ("Shared memory and tensor cores", section 13.10: bias,
 // activation, residual add or type cast applied to the accumulator before the

@@ -15,6 +15,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include <algorithm>
 #include <cmath>
 #include <string>
@@ -149,12 +151,17 @@ static double tile_efficiency_aligned(const MenuEntry& e) {
     // register-staged tiles per CU (fitted from 8192^2 x K, K = 256, 512 and 8192,
     // alternated: 31.2 against 32.1 us per round and 256 k), with a larger fixed cost
     // per round (fp32_round_overhead); it does not split K
-    if (e.sched == 6) return 0.72;
+    if (e.sched == 6) return e.bm >= 256 ? 0.72 : 0.40;  // 64 x 64: see plan()
     if (e.variant == V_LDS) return t >= 128 ? 0.6 : 0.35;
     // the fp32 64 x 64 tile with K split between two wave grids measured 7-9% faster
     // than with one (1024^3: 27.3-27.8 us against 29.6-29.8; 256^3: 8.4-8.6 against
     // 9.0-9.1; 512 x 4096 x 4096: 162-169 against 177-180)
-    if (e.threads > e.wm * e.wn * 64) return 0.49;
+    // The 16 x 64 tile with K split over four one-wave groups: two resident per CU;
+    // against the 64 x 64 tile with two K groups, 256^3 5.4 us against 8.2 (64
+    // workgroups against 16), 512^3 8.1 against 13.4, 128 x 1024 x 1024 12.6 against
+    // 23.5, 256 x 256 x 16384 153 against 326; slower once 64 x 64 tiles fill the
+    // machine (1024^3 32.0 against 24.7, 1024^2 x 256 12.6 against 9.4)
+    if (e.threads > e.wm * e.wn * 64) return e.bm < 64 ? 0.30 : 0.49;
     return t >= 256 ? 0.85 : t >= 128 ? 0.7 : 0.45;
 }
 // fp32 tiles: cycles per round of tiles beyond the k loop (the first copies and the
@@ -200,10 +207,9 @@ int64_t pack_workspace(int opB, int dtype, int64_t M, int64_t N, int64_t K) {
 // Workspace of an S-slice split: one fp32 plane of M x round_up(N, 4) per slice.
 static int64_t split_workspace(int64_t S, int64_t M, int64_t N) { return S * M * ((N + 3) / 4 * 4) * 4; }
 
-int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int dtype,
-         uintptr_t a, uintptr_t b, uintptr_t c, int num_cus, const char* arch, int64_t ws_bytes,
-         bool fused_epilogue, const gemm_config* req, gemm_config* out) {
-    (void)c;
+static int plan_uncached(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                         int dtype, uintptr_t a, uintptr_t b, int num_cus, const char* arch, int64_t ws_bytes,
+                         bool fused_epilogue, const gemm_config* req, gemm_config* out) {
     int st = validate(opA, opB, M, N, K, lda, ldb, ldc, dtype);
     if (st != GEMM_OK) return st;
     if (arch == nullptr || strncmp(arch, "gfx950", 6) != 0) {
@@ -408,6 +414,12 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
                 else eff = !eight ? 0.90 : (tiles <= num_cus && ktiles <= 32) ? 0.96 : 0.99;
                 if (e.sched == 7) eff *= 0.9;
             }
+            // the fp32 64 x 64 tile with two K groups on the three-stage schedule:
+            // 1.5-6% faster than on the two-stage one for one round of tiles (1024^3
+            // 23.7-24.3 us against 24.7-25.2, both B layouts), 10-13% slower over
+            // several rounds (2048^3 171.1 against 150.7; 512 x 4096 x 4096 165.0
+            // against 149.7)
+            if (e.dtype == DT_F32 && e.sched == 6 && e.bm < 256) eff = rounds == 1 ? 0.50 : 0.40;
             const double tile_cycles = 2.0 * e.bm * e.bn * std::max<int64_t>(kpad, e.bk) / (rate_per_cu(e) * eff);
             double cost = (double)rounds * (double)std::max<int64_t>(resident, 1) * tile_cycles;
             if (e.dtype == DT_F32 && e.variant == V_MFMA)
@@ -477,6 +489,99 @@ int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
     cfg.est_cycles = best_cost;
     *out = cfg;
     return GEMM_OK;
+}
+
+// ---- plan cache. A plan depends on the problem (operand flags, sizes, leading
+// dimensions, dtype), on A's and B's addresses only through their offsets mod 16,
+// on the device (CU count, architecture), the workspace size, whether an epilogue
+// is fused, and the request's input fields. Successful plans are kept in a small
+// direct-mapped table keyed on exactly those, so that a repeated call skips the
+// cost model (a few microseconds of host time, as much as a small product takes on
+// the device). Failed plans are not kept: each failure sets its message anew.
+namespace {
+
+struct PlanKey {
+    int64_t M, N, K, lda, ldb, ldc, ws;
+    int32_t opA, opB, dtype, num_cus, a16, b16, fused, has_req;
+    int32_t req[13];
+    char arch[32];
+};
+
+struct PlanSlot {
+    bool used;
+    PlanKey key;
+    gemm_config cfg;
+};
+
+constexpr int kPlanSlots = 256;
+std::mutex g_plan_mutex;
+PlanSlot g_plan_cache[kPlanSlots];
+
+bool make_key(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int dtype,
+              uintptr_t a, uintptr_t b, int num_cus, const char* arch, int64_t ws_bytes, bool fused,
+              const gemm_config* req, PlanKey* k) {
+    if (arch == nullptr || strlen(arch) >= sizeof k->arch) return false;
+    memset(k, 0, sizeof *k);  // padding included, so that keys compare with memcmp
+    k->M = M;
+    k->N = N;
+    k->K = K;
+    k->lda = lda;
+    k->ldb = ldb;
+    k->ldc = ldc;
+    k->ws = ws_bytes;
+    k->opA = opA;
+    k->opB = opB;
+    k->dtype = dtype;
+    k->num_cus = num_cus;
+    k->a16 = (int32_t)(a & 15);
+    k->b16 = (int32_t)(b & 15);
+    k->fused = fused ? 1 : 0;
+    k->has_req = req != nullptr;
+    if (req) {
+        const int32_t in[13] = {req->variant, req->bm,       req->bn,      req->vec,     req->xcd_remap,
+                                req->group_m, req->waves_m,  req->waves_n, req->schedule, req->max_grid,
+                                req->split_k, req->pack,     req->threads};
+        memcpy(k->req, in, sizeof in);
+    }
+    memcpy(k->arch, arch, strlen(arch));
+    return true;
+}
+
+uint32_t key_hash(const PlanKey& k) {
+    const unsigned char* p = reinterpret_cast<const unsigned char*>(&k);
+    uint32_t h = 2166136261u;  // FNV-1a
+    for (size_t i = 0; i < sizeof k; ++i) h = (h ^ p[i]) * 16777619u;
+    return h;
+}
+
+}  // namespace
+
+int plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int dtype,
+         uintptr_t a, uintptr_t b, uintptr_t c, int num_cus, const char* arch, int64_t ws_bytes,
+         bool fused_epilogue, const gemm_config* req, gemm_config* out) {
+    (void)c;
+    PlanKey key;
+    const bool cacheable = make_key(opA, opB, M, N, K, lda, ldb, ldc, dtype, a, b, num_cus, arch, ws_bytes,
+                                    fused_epilogue, req, &key);
+    const uint32_t slot = cacheable ? key_hash(key) % kPlanSlots : 0;
+    if (cacheable) {
+        std::lock_guard<std::mutex> lock(g_plan_mutex);
+        const PlanSlot& e = g_plan_cache[slot];
+        if (e.used && memcmp(&e.key, &key, sizeof key) == 0) {
+            *out = e.cfg;
+            return GEMM_OK;
+        }
+    }
+    const int st = plan_uncached(opA, opB, M, N, K, lda, ldb, ldc, dtype, a, b, num_cus, arch, ws_bytes,
+                                 fused_epilogue, req, out);
+    if (st == GEMM_OK && cacheable) {
+        std::lock_guard<std::mutex> lock(g_plan_mutex);
+        PlanSlot& e = g_plan_cache[slot];
+        e.used = true;
+        e.key = key;
+        e.cfg = *out;
+    }
+    return st;
 }
 
 int default_group_m(int64_t tiles_m, int64_t tiles_n) {

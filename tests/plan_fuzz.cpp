@@ -171,6 +171,13 @@ int main(int argc, char** argv) {
         if (st == GEMM_OK) {
             ++ok;
             check_plan(opB, M, N, K, lda, ldb, dtype, a, b, ws, epi, with_req ? &req : nullptr, out, cus);
+            // the same call again (now answered by the plan cache, or after another
+            // entry took its slot) gives the same plan
+            gemm_config again;
+            memset(&again, 0x33, sizeof again);
+            const int st2 = plan(opA, opB, M, N, K, lda, ldb, ldc, dtype, a, b, cp, cus, arch, ws, epi,
+                                 with_req ? &req : nullptr, &again);
+            CHECK(st2 == GEMM_OK && memcmp(&again, &out, sizeof out) == 0, "repeated plan differs (status %d)", st2);
         } else {
             ++rejected;
             CHECK(last_error() && last_error()[0], "status %d without a message", st);

@@ -52,24 +52,27 @@ def test_status_strings():
 
 def test_menu_is_complete():
     menu = dg.gemm_menu()
-    assert len(menu) == dg.library().gemm_menu_size() == 98
+    assert len(menu) == dg.library().gemm_menu_size() == 104
     seen = set()
     for e in menu:
         assert e["lds_bytes"] <= 160 * 1024
         assert e["threads"] in (256, 512)
         seen.add((e["variant"], e["dtype"], e["opb"], e["vec"], e["bm"], e["bn"]))
         if e["variant"] == dg.GEMM_VARIANT_MFMA:
-            # one wave grid per workgroup, or two that split K (fp32 64 x 64 only)
+            # one wave grid per workgroup, or two or four that split K (fp32 64 x 64 on
+            # either fp32 schedule, 16 x 64 with four groups)
             k_groups = e["threads"] // (e["waves_m"] * e["waves_n"] * 64)
-            assert k_groups * e["waves_m"] * e["waves_n"] * 64 == e["threads"] and k_groups in (1, 2)
-            assert k_groups == 1 or (e["dtype"] == 0 and (e["bm"], e["bn"]) == (64, 64) and e["schedule"] == 1)
+            assert k_groups * e["waves_m"] * e["waves_n"] * 64 == e["threads"] and k_groups in (1, 2, 4)
+            assert k_groups == 1 or (e["dtype"] == 0 and (
+                ((e["bm"], e["bn"]) == (64, 64) and k_groups == 2 and e["schedule"] in (1, 6)) or
+                ((e["bm"], e["bn"]) == (16, 64) and k_groups == 4 and e["schedule"] == 1)))
     for variant in (1, 2):
         for dtype in (0, 1, 2):
             for opb in (0, 1):
                 for vec in (0, 1):
                     tiles = {(bm, bn) for (v, d, o, ve, bm, bn) in seen if (v, d, o, ve) == (variant, dtype, opb, vec)}
                     assert len(tiles) >= 2, (variant, dtype, opb, vec)
-    assert dg.library().gemm_menu_entry(98, None, None, None, None) == dg.GEMM_ERR_INVALID_VALUE
+    assert dg.library().gemm_menu_entry(104, None, None, None, None) == dg.GEMM_ERR_INVALID_VALUE
 
 
 def plan(M, N, K, dtype="f32", op_b="N", lda=None, ldb=None, ldc=None, a=0, b=0, c=0, cus=256, arch="gfx950",
@@ -166,13 +169,15 @@ def test_plan_software_pipelined_edge_tiles():
 
 def test_plan_three_stage_fp32():
     """Schedule 6 (fp32 256 x 128, three LDS stages) where the grid fills the machine,
-    either B layout, ragged shapes included; never for 16-bit inputs, never split."""
+    either B layout, ragged shapes included, and its 64 x 64 form for one round of
+    tiles; never for 16-bit inputs, never split."""
     for op_b in "NT":
         for shape in ((4096, 4096, 4096), (8192, 8192, 8192), (4000, 4096, 3001)):
             st, c = plan(*shape, "f32", op_b)
             assert st == 0 and c.schedule == 6 and (c.bm, c.bn) == (256, 128) and c.threads == 512, (shape, op_b)
-    # few tiles: the register-staged kernels, which may split K with a workspace
-    assert plan(1024, 1024, 1024, "f32")[1].schedule == 1
+    # one round of 64 x 64 tiles: the same schedule with two K groups on that tile
+    st, c = plan(1024, 1024, 1024, "f32")
+    assert st == 0 and c.schedule == 6 and (c.bm, c.bn) == (64, 64)
     # short K: the three-stage tile's fixed cost per round of tiles outweighs its faster
     # k loop; two resident 128 x 128 register-staged tiles per CU
     for shape in ((8192, 8192, 256), (8192, 8192, 512), (4096, 4096, 1024)):
@@ -245,12 +250,72 @@ def test_plan_persistent_grid():
     assert st == dg.GEMM_ERR_INVALID_VALUE
 
 
+def test_plan_cache_returns_the_uncached_plan():
+    """The planner keeps successful plans in a cache keyed on everything a plan
+    depends on. Repeated and interleaved calls must give what a first call gives:
+    same problem twice, then the alignment class, a request field, the workspace and
+    the CU count changed one at a time (each changes the plan here), and a failing
+    call between them (failures are not cached and keep their message)."""
+    fields = [f for f, _ in dg.gemm_config._fields_ if f != "est_cycles"]
+
+    def snap(c):
+        return tuple(getattr(c, f) for f in fields)
+
+    cases = [
+        dict(M=3001, N=5003, K=1037, dtype="bf16", op_b="T", a=0, b=0),        # aligned bases, odd lds
+        dict(M=3001, N=5003, K=1037, dtype="bf16", op_b="T", a=1, b=1),        # not element-aligned
+        dict(M=4096, N=4096, K=4096, dtype="f16", op_b="N", a=0, b=0),
+        dict(M=4096, N=4096, K=4096, dtype="f16", op_b="N", a=8, b=0),         # not 16-byte aligned
+        dict(M=8192, N=8192, K=1024, dtype="f16", op_b="N", a=0, b=0),         # persistent grid
+        dict(M=8192, N=8192, K=1024, dtype="f16", op_b="N", a=0, b=0, cus=128),
+        dict(M=4096, N=4096, K=4096, dtype="f16", op_b="N", a=0, b=0, req=dict(schedule=2)),
+        dict(M=4096, N=4096, K=4096, dtype="f16", op_b="N", a=0, b=0, req=dict(waves_n=2)),
+        dict(M=256, N=256, K=16384, dtype="f32", op_b="N", a=0, b=0),
+    ]
+
+    def run(cs):
+        kw = dict(cs)
+        req = kw.pop("req", None)
+        cus = kw.pop("cus", 256)
+        st, c = plan(kw["M"], kw["N"], kw["K"], kw["dtype"], kw["op_b"], a=kw["a"], b=kw["b"], cus=cus,
+                     req=dg.request(**req) if req else None)
+        assert st == 0
+        return snap(c)
+
+    first = [run(cs) for cs in cases]
+    assert len(set(first)) == len(first), "each case changes the plan"
+    for _ in range(3):
+        for i, cs in enumerate(cases):
+            assert run(cs) == first[i]
+            st, _ = plan(4096, 4096, 4096, "f16", req=dg.request(schedule=3))
+            assert st == dg.GEMM_ERR_UNSUPPORTED and "removed" in dg.gemm_last_error()
+    # workspace: split K appears only with one (gemm_plan_workspace)
+    st, c0 = dg.gemm_plan_workspace(0, 0, 256, 256, 16384, 16384, 256, 256, dg.GEMM_F32, 0, 0, 1 << 40, 256,
+                                    "gfx950", 0, None, check=False)
+    st1, c1 = dg.gemm_plan_workspace(0, 0, 256, 256, 16384, 16384, 256, 256, dg.GEMM_F32, 0, 0, 1 << 40, 256,
+                                     "gfx950", 1 << 26, None, check=False)
+    st2, c2 = dg.gemm_plan_workspace(0, 0, 256, 256, 16384, 16384, 256, 256, dg.GEMM_F32, 0, 0, 1 << 40, 256,
+                                     "gfx950", 0, None, check=False)
+    assert st == st1 == st2 == 0 and c0.split_k == 1 and c1.split_k > 1 and snap(c2) == snap(c0)
+
+
 def test_plan_fills_the_machine():
     """A smaller problem gets smaller tiles so that the grid covers the compute units."""
     st, c = plan(1024, 1024, 1024, "f32")
     assert st == 0 and c.grid >= 256
-    st, c = plan(256, 256, 256, "f32")
-    assert st == 0 and (c.bm, c.bn) == (64, 64)
+    # 256^3: the 16 x 64 tile with K over four wave groups (64 workgroups; 64 x 64
+    # tiles would give 16)
+    for op_b in "NT":
+        st, c = plan(256, 256, 256, "f32", op_b)
+        assert st == 0 and (c.bm, c.bn) == (16, 64) and c.grid == 64 and c.threads == 256
+    st, c = plan(512, 512, 512, "f32")
+    assert st == 0 and (c.bm, c.bn) == (16, 64) and c.grid == 256
+    # 1024^3: 64 x 64 tiles fill the machine; one round of them on the three-stage
+    # schedule with two K groups
+    st, c = plan(1024, 1024, 1024, "f32")
+    assert st == 0 and (c.bm, c.bn) == (64, 64) and c.schedule == 6 and c.threads == 512 and c.grid == 256
+    st, c = plan(2048, 2048, 2048, "f32")
+    assert st == 0 and c.schedule != 6 or c.bm == 256
     # a tall-skinny problem still picks a tile count close to the CU count or more
     st, c = plan(8192, 64, 4096, "f16")
     assert st == 0 and c.grid >= 64
