@@ -12,6 +12,11 @@ torch.cuda.synchronize(); the duration is taken from HIP events recorded on the
 launch stream around the K launches. One kernel runs per step and the launches
 follow each other with no gap, so the step time is also the kernel's average
 duration (the roofline figure). Inputs are resident in HBM before timing starts.
+The other problems are timed the same way over K/2 steps or more, after a
+warm-up of about 20 ms of their launches (the clock rises over the first
+milliseconds of sustained work): a small problem gets enough steps for about 5 ms
+of launches (reported as `steps`), so that the start of the idle queue, paid once
+per timed window, does not weigh on its step time.
 
 Only the W + K headline launches run the headline kernel in the default command
 (the fused epilogue, the per-launch distribution and the clock probe, which
@@ -98,12 +103,19 @@ def device_problem(name, seed=0):
 WORKSPACE_CAP = 256 << 20   # workspace offered to split-K runs
 
 
-def time_problem(name, steps, warmup, workspace=False, force=None):
+def time_problem(name, steps, warmup, workspace=False, force=None, min_window_ms=0.0, min_warm_ms=0.0):
     """Warm up, then time exactly `steps` calls with HIP events on the launch stream.
 
     workspace=True runs gemm_ex_workspace with up to WORKSPACE_CAP bytes (the
     heuristic may split K or pack the operands; such a call is two kernels, both
-    inside the timed step)."""
+    inside the timed step). min_window_ms > 0 raises `steps` until the timed
+    launches span about that long (estimated from the warm-up), so that the start of
+    an idle queue, paid once per timed window, is spread over enough launches of a
+    small problem. min_warm_ms > 0 extends the untimed warm-up to about that long:
+    the chip raises its clock over the first milliseconds of sustained work (a
+    1024^3 fp32 launch measured 24.6 us over the first 20 launches and 22.6 over
+    launches 320-420 of one run), which a warm-up of a few short launches does not
+    cover."""
     import torch
     import dense_gemm_06_amd as dg
     ops, A, B, C = device_problem(name)
@@ -121,9 +133,17 @@ def time_problem(name, steps, warmup, workspace=False, force=None):
         call = lambda: dg.gemm_ex_workspace(*args, req, W.data_ptr(), cfg.workspace_bytes, s)
     else:
         call = lambda: dg.gemm_ex(*args, req, s)
+    t0 = time.perf_counter()
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
+    if (min_window_ms > 0 or min_warm_ms > 0) and warmup > 0:
+        per_call_ms = (time.perf_counter() - t0) * 1e3 / warmup
+        steps = max(steps, min(4000, int(min_window_ms / max(per_call_ms, 1e-4)) + 1))
+        more = min(20000, int(min_warm_ms / max(per_call_ms, 1e-4)) - warmup)
+        for _ in range(max(0, more)):
+            call()
+        torch.cuda.synchronize()
     # whole job: K launches back to back between two events
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -142,7 +162,7 @@ def time_problem(name, steps, warmup, workspace=False, force=None):
     launch_ms = ms
     flops = 2.0 * ops.M * ops.N * ops.K
     del A, B, C
-    return dict(problem=name, ms_per_step=ms, launch_ms=launch_ms, tflops=flops / (ms * 1e-3) / 1e12,
+    return dict(problem=name, steps=steps, ms_per_step=ms, launch_ms=launch_ms, tflops=flops / (ms * 1e-3) / 1e12,
                 kernel_tflops=flops / (launch_ms * 1e-3) / 1e12, wall_s=wall, dtype=ops.dtype,
                 M=ops.M, N=ops.N, K=ops.K, op_b=ops.op_b, flops=flops, cfg=cfg, cus=cus, arch=arch,
                 peak=PEAK_TFLOPS[ops.dtype])
@@ -463,10 +483,10 @@ def main():
     if not a.no_extra and not a.only:
         for name in ("c3_f32_4096", "c1_f32_256", "c2_f32_1024", "c5_bf16_ragged", "m8_f16_shard", "m8_f32_shard",
                      "r4_f16_8192x8192x2048"):
-            extras[name] = time_problem(name, max(5, a.steps // 2), max(2, a.warmup // 2))
+            extras[name] = time_problem(name, max(5, a.steps // 2), max(2, a.warmup // 2), min_window_ms=5.0, min_warm_ms=20.0)
         # the same four-round problem with one workgroup per tile (no persistent grid)
         one_per_tile = time_problem("r4_f16_8192x8192x2048", max(5, a.steps // 2), max(2, a.warmup // 2),
-                                    force={"max_grid": 1 << 30})
+                                    force={"max_grid": 1 << 30}, min_window_ms=5.0, min_warm_ms=20.0)
 
     cfg = main_res["cfg"]
     traffic = load_traffic(headline, cfg)
@@ -509,6 +529,7 @@ def main():
                        "kernel_cfg": {k: v for k, v in r["cfg"].as_dict().items() if k != "est_cycles"}}
     if extras:
         out["other_problems"] = {k: {"tflops": round(v["tflops"], 3), "ms_per_step": round(v["ms_per_step"], 6),
+                                     "steps": v["steps"],
                                      "frac_of_peak": round(v["tflops"] / v["peak"], 4),
                                      "tile": f"{v['cfg'].bm}x{v['cfg'].bn}",
                                      "variant": "mfma" if v["cfg"].variant == 2 else "lds"}
@@ -522,14 +543,14 @@ def main():
                                     "grid": r["cfg"].grid})
         # the under-filled problems again with a workspace (the heuristic may split K),
         # and a long-K problem with 16 output tiles, where splitting pays
-        lk = time_problem("k1_f32_long_k", max(5, a.steps // 2), max(2, a.warmup // 2))
+        lk = time_problem("k1_f32_long_k", max(5, a.steps // 2), max(2, a.warmup // 2), min_window_ms=5.0, min_warm_ms=20.0)
         out["other_problems"]["k1_f32_long_k"] = {
             "workload": "C=A@B 256x256x16384 f32", "tflops": round(lk["tflops"], 3),
             "ms_per_step": round(lk["ms_per_step"], 6), "frac_of_peak": round(lk["tflops"] / lk["peak"], 4),
             "tile": f"{lk['cfg'].bm}x{lk['cfg'].bn}", "variant": "mfma" if lk["cfg"].variant == 2 else "lds"}
         # (and the unaligned ragged problem, which the heuristic packs into aligned whole tiles)
         for name in ("c1_f32_256", "c2_f32_1024", "k1_f32_long_k", "c5_bf16_ragged", "m8_f16_shard", "m8_f32_shard"):
-            r = time_problem(name, max(5, a.steps // 2), max(2, a.warmup // 2), workspace=True)
+            r = time_problem(name, max(5, a.steps // 2), max(2, a.warmup // 2), workspace=True, min_window_ms=5.0, min_warm_ms=20.0)
             out["other_problems"][name]["with_workspace"] = {
                 "tflops": round(r["tflops"], 3), "ms_per_step": round(r["ms_per_step"], 6),
                 "frac_of_peak": round(r["tflops"] / r["peak"], 4), "split_k": r["cfg"].split_k,

@@ -1,0 +1,227 @@
+// kernel_f32dc.h -- fp32 64 x 64 tiles with direct global -> LDS copies several
+// k-tiles ahead (schedule 8).
+#pragma once
+#include "kernel_sp.h"
+
+namespace dg {
+
+// fp32 inputs on v_mfma_f32_16x16x4_f32, one 64 x 64 tile of C per workgroup, K split
+// over KG groups of four waves (group kg takes k-tiles kg, kg + KG, ...; K is a
+// multiple of KG * 32, checked by the host). Each wave owns a 16 x 64 slice of the
+// tile, as in the register-staged 64 x 64 tile (fragments, MFMA order and store are
+// that kernel's), but the operands reach LDS by direct copies (global_load_lds, 16
+// bytes per lane: one instruction fills 1 KB of LDS) into S stages per group, issued
+// S - 1 k-tiles ahead. Nothing passes through registers, so a copy can be in flight
+// for S - 2 whole k-tiles before its data is needed, and the k loop carries no
+// address or store arithmetic for the staging.
+//
+// Iteration lt (stage lt % S): copy k-tile lt + S - 1 into the stage of k-tile lt - 1
+// (whose reads ended before the previous barrier); read the second half of k-tile
+// lt's fragments; MFMAs on the first half; read the first half of k-tile lt + 1
+// (complete and published by the previous barrier); MFMAs on the second half; wait
+// until this wave's copies of k-tile lt + 2 have landed; barrier. Only copies are in
+// flight in the loop (no stores), so the vector-memory counter counts copies alone
+// and they complete in order.
+//
+// LDS layouts (those of the register-staged fp32 tile): A, and B when column-major,
+// k-major rows of 32 floats, chunk c of row r at position c ^ (r & 7); a row-major B
+// as k-rows of 64 floats, unswizzled. Copy block b of A fills rows 8b .. 8b + 7: lane
+// L lands at byte 16 L of the block, position L & 7 of row 8b + (L >> 3), and loads
+// the logical chunk that belongs there. Edge tiles: rows of A (and of a
+// column-major B) at or beyond M (N) copy row M - 1 (N - 1); 16-byte column chunks of
+// a row-major B at or beyond N (a multiple of 4) copy columns 0 .. 3. What they bring
+// in reaches only rows and columns of C that are not stored.
+template <int OPB, int KG, int S>
+__global__ __launch_bounds__(256 * KG) void mfma32_dc(GemmArgs g) {
+    constexpr int BM = 64, BN = 64, BK = 32;
+    constexpr int NT = 256;                  // threads per K group
+    constexpr int STAGE = BM * BK;           // floats per operand and stage (B: BK x BN, the same)
+    constexpr int STAGE_BYTES = STAGE * 4;   // 8 KB
+    static_assert(KG == 1 || KG == 2, "k groups");
+    static_assert(S >= 3 && KG * S * 2 * STAGE_BYTES <= 160 * 1024, "stages");
+    __shared__ __attribute__((aligned(1024))) float sAg[KG][S][STAGE];
+    __shared__ __attribute__((aligned(1024))) float sBg[KG][S][STAGE];
+
+    const int kg = KG == 1 ? 0 : (int)threadIdx.x / NT;  // uniform per wave
+    const int tid = (int)threadIdx.x - kg * NT, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lg = lane >> 4;
+    int tm, tn;
+    tile_coords(g, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const float* __restrict__ A = static_cast<const float*>(g.A);
+    const float* __restrict__ B = static_cast<const float*>(g.B);
+    const int nl = g.K / (BK * KG);  // k-tiles per group
+
+    // Copy sources at this group's first k-tile, and the step between its k-tiles.
+    // Wave w copies blocks 2w and 2w + 1 of A and of B.
+    const float* srcA[2];
+    const float* srcB[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int b = 2 * wave + i;
+        const int row = b * 8 + (lane >> 3), c = (lane & 7) ^ kmaj_swz(row);
+        srcA[i] = A + (size_t)min(m0 + row, g.M - 1) * g.lda + kg * BK + 4 * c;
+        if (OPB == 1) {
+            srcB[i] = B + (size_t)min(n0 + row, g.N - 1) * g.ldb + kg * BK + 4 * c;
+        } else {
+            const int krow = b * 4 + (lane >> 4), col = n0 + 4 * (lane & 15);
+            srcB[i] = B + (size_t)(kg * BK + krow) * g.ldb + (col < g.N ? col : 0);
+        }
+    }
+    const size_t stepA = (size_t)KG * BK;
+    const size_t stepB = OPB == 0 ? (size_t)KG * BK * g.ldb : (size_t)KG * BK;
+    const uint32_t wave_u = (uint32_t)__builtin_amdgcn_readfirstlane(wave);
+    const uint32_t dstA = (uint32_t)reinterpret_cast<uintptr_t>(DG_LDSV(&sAg[kg][0][0])) + wave_u * 2048u;
+    const uint32_t dstB = (uint32_t)reinterpret_cast<uintptr_t>(DG_LDSV(&sBg[kg][0][0])) + wave_u * 2048u;
+    auto issue = [&](int lt, uint32_t st) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            __builtin_amdgcn_global_load_lds(DG_GLB(srcA[i] + (size_t)lt * stepA),
+                                             DG_LDS_AT(dstA + st * STAGE_BYTES + i * 1024u), 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            __builtin_amdgcn_global_load_lds(DG_GLB(srcB[i] + (size_t)lt * stepB),
+                                             DG_LDS_AT(dstB + st * STAGE_BYTES + i * 1024u), 16, 0, 0);
+    };
+
+    // Fragments of one half k-tile (16 k): A rows wave*16 + l16 as a float4 along k;
+    // B as four k-rows (row-major: a float4 along n) or four 16-column subtiles
+    // (column-major: a float4 along k).
+    struct Frag {
+        f32x4 a;
+        f32x4 b[4];
+    };
+    const int ra = wave * 16 + l16;
+    auto read_frag = [&](Frag& f, uint32_t st, int kk) {
+        const float* sa = &sAg[kg][0][0] + st * STAGE;
+        const float* sb = &sBg[kg][0][0] + st * STAGE;
+        f.a = *reinterpret_cast<const f32x4*>(sa + ra * BK + ((((kk >> 2) + lg) ^ kmaj_swz(ra)) << 2));
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            if (OPB == 0) {
+                f.b[s] = *reinterpret_cast<const f32x4*>(sb + (kk + 4 * lg + s) * BN + 4 * l16);
+            } else {
+                const int r = s * 16 + l16;
+                f.b[s] = *reinterpret_cast<const f32x4*>(sb + r * BK + ((((kk >> 2) + lg) ^ kmaj_swz(r)) << 2));
+            }
+        }
+    };
+    f32x4 acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto read_one = [&](Frag& f, uint32_t st, int kk, int r) {
+        const float* sa = &sAg[kg][0][0] + st * STAGE;
+        const float* sb = &sBg[kg][0][0] + st * STAGE;
+        if (r == 0) {
+            f.a = *reinterpret_cast<const f32x4*>(sa + ra * BK + ((((kk >> 2) + lg) ^ kmaj_swz(ra)) << 2));
+        } else if (OPB == 0) {
+            f.b[r - 1] = *reinterpret_cast<const f32x4*>(sb + (kk + 4 * lg + r - 1) * BN + 4 * l16);
+        } else {
+            const int rb = (r - 1) * 16 + l16;
+            f.b[r - 1] = *reinterpret_cast<const f32x4*>(sb + rb * BK + ((((kk >> 2) + lg) ^ kmaj_swz(rb)) << 2));
+        }
+    };
+    // The 16 MFMAs of one half, with the five fragment reads of another half after the
+    // MFMAs at positions rpos .. rpos + 4 and, with a copy tag, this wave's four copies
+    // of k-tile ct into stage cst after MFMAs 1, 3, 5 and 7, so that the matrix unit
+    // starts right after the barrier and the other instructions issue in its shadow.
+    auto mma_mixed = [&](const Frag& f, Frag& nf, uint32_t nst, int nkk, int rpos, bool copy, int ct, uint32_t cst) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int k = 4 * s + j;
+                if (OPB == 0)
+                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(f.b[s][j], f.a[s], acc[j], 0, 0, 0);
+                else
+                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(f.b[j][s], f.a[s], acc[j], 0, 0, 0);
+                if (k >= rpos && k < rpos + 5) read_one(nf, nst, nkk, k - rpos);
+                if (copy && (k & 1) && k < 8) {
+                    const int i = (k >> 1) & 1;
+                    if (k < 4)
+                        __builtin_amdgcn_global_load_lds(DG_GLB(srcA[i] + (size_t)ct * stepA),
+                                                         DG_LDS_AT(dstA + cst * STAGE_BYTES + i * 1024u), 16, 0, 0);
+                    else
+                        __builtin_amdgcn_global_load_lds(DG_GLB(srcB[i] + (size_t)ct * stepB),
+                                                         DG_LDS_AT(dstB + cst * STAGE_BYTES + i * 1024u), 16, 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+    };
+    auto settle = [&](Frag& f) {
+        asm volatile("" : "+v"(f.a), "+v"(f.b[0]), "+v"(f.b[1]), "+v"(f.b[2]), "+v"(f.b[3]));
+    };
+
+    // prologue: k-tiles 0 .. S - 2 in flight; k-tiles 0 and 1 complete
+    for (int t = 0; t < S - 1 && t < nl; ++t) issue(t, (uint32_t)t);
+    vm_wait(4 * max(0, min(S - 2, nl - 1) - 1));
+    asm volatile("s_barrier" ::: "memory");
+    Frag f0, f1;
+    if (nl > 0) read_frag(f0, 0, 0);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    settle(f0);
+    uint32_t st = 0;  // lt % S
+    // One iteration; COPY: k-tile lt + S - 1 exists and is copied, and then the wait
+    // leaves the copies of k-tiles lt + 3 .. lt + S - 1 in flight.
+    auto iteration = [&](int lt, auto copy_tag) {
+        constexpr bool COPY = decltype(copy_tag)::value;
+        const uint32_t nst = st + 1 == S ? 0 : st + 1;
+        const uint32_t cst = st == 0 ? S - 1 : st - 1;  // (lt + S - 1) % S
+        // first half: the second half's fragments read after its first MFMAs
+        mma_mixed(f0, f1, st, 16, 0, false, 0, 0);
+        // second half: the copies of k-tile lt + S - 1 (into the stage of k-tile lt - 1)
+        // and the first half of k-tile lt + 1 (unconditional: after the last k-tile it
+        // reads a stage whose values go unused)
+        mma_mixed(f1, f0, nst, 0, 8, COPY, lt + S - 1, cst);
+        // this wave's copies of k-tile lt + 2 landed (those of later k-tiles may be in
+        // flight), its own LDS reads done; then the barrier publishes k-tile lt + 2 and
+        // frees stage st for the copies of the next iteration
+        if (COPY) vm_wait_n<4 * (S - 3)>();
+        else vm_wait(4 * max(0, nl - 1 - (lt + 2)));
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        asm volatile("s_barrier" ::: "memory");
+        settle(f0);
+        st = nst;
+    };
+    constexpr std::true_type yes{};
+    constexpr std::false_type no{};
+    int lt = 0;
+    for (; lt + S - 1 < nl; ++lt) iteration(lt, yes);
+    for (; lt < nl; ++lt) iteration(lt, no);
+
+    if constexpr (KG == 2) {
+        // group 1's accumulators through LDS (its own A stages: every copy has landed
+        // and every read of them is done), lane-major; group 0 adds them after its own
+        // (a fixed order)
+        static_assert(4 * 4 * 64 * 4 <= S * STAGE, "reduction buffer");
+        float* red = &sAg[1][0][0];
+        if (kg == 1) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) red[((wave * 4 + j) * 4 + e) * 64 + lane] = acc[j][e];
+        }
+        __syncthreads();
+        if (kg == 1) return;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[j][e] += red[((wave * 4 + j) * 4 + e) * 64 + lane];
+    }
+
+    const int m = m0 + ra;
+    if (m >= g.M) return;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        if (OPB == 0) {
+            // subtile j holds columns 4 l16 + j: lane owns 16 consecutive n of row m
+            const int n = n0 + 16 * lg + 4 * r;
+            store_run4(g, m, n, f32x4{acc[0][r], acc[1][r], acc[2][r], acc[3][r]});
+        } else {
+            const int n = n0 + r * 16 + lg * 4;
+            store_run4(g, m, n, acc[r]);
+        }
+    }
+}
+
+}  // namespace dg

@@ -33,3 +33,4 @@
 #include "kernel_mfma.h"
 #include "kernel_pp.h"
 #include "kernel_sp.h"
+#include "kernel_f32dc.h"

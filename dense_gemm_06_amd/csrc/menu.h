@@ -27,7 +27,9 @@ enum Dtype { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
 //             5: K a multiple of 8), 6 = register-staged with three LDS stages and fragments
 //             read a half k-tile ahead (fp32, any shape), 7 = the software-pipelined
 //             32x32x16 kernel of schedule 5 with register-staged loads (16-bit inputs,
-//             bases aligned to the element, any M, K >= 8, N >= 8 for row-major B)
+//             bases aligned to the element, any M, K >= 8, N >= 8 for row-major B),
+//             8 = fp32 64 x 64 tiles with direct copies three k-tiles ahead (16-byte
+//             aligned operands, K a multiple of 64, N a multiple of 4 for row-major B)
 struct MenuEntry {
     int id, variant, dtype, opb, vec, bm, bn, bk, wm, wn, tm, tn, threads, lds_bytes, sched;
 };
@@ -41,7 +43,7 @@ constexpr bool schedule_enabled(int sched) { return sched != 3; }
 // Schedules whose kernels copy tiles straight into LDS: the operands must be 16-byte
 // aligned and K whole k-tiles (schedule 5: K a multiple of 8, a partial last k-tile
 // zeroed past K); edge tiles in M and N copy clamped rows and columns.
-constexpr bool direct_copy(int sched) { return sched == 2 || sched == 4 || sched == 5; }
+constexpr bool direct_copy(int sched) { return sched == 2 || sched == 4 || sched == 5 || sched == 8; }
 
 // Configurations with a persistent single-problem form (a grid below the tile count,
 // each workgroup striding through the tiles): the 8-wave software-pipelined
@@ -156,6 +158,13 @@ constexpr bool grouped_capable(int variant, int sched, int bm, int bn, int wm, i
     X(base + 4, V_MFMA, DT_F32, 0, 1, 64, 64, 32, 4, 1, 0, 0, 512, 2 * 3 * 4 * 32 * 128, 6)    \
     X(base + 5, V_MFMA, DT_F32, 1, 1, 64, 64, 32, 4, 1, 0, 0, 512, 2 * 3 * 4 * 32 * 128, 6)
 
+// fp32 64 x 64 tiles with direct copies (schedule 8): two K groups of four waves,
+// four LDS stages per group (16-byte aligned operands, K a multiple of 64, row-major
+// B with N a multiple of 4).
+#define DG_MFMA_F32DC(X, base)                                                           \
+    X(base + 0, V_MFMA, DT_F32, 0, 1, 64, 64, 32, 4, 1, 0, 0, 512, 2 * 4 * 2 * 8192, 8)        \
+    X(base + 1, V_MFMA, DT_F32, 1, 1, 64, 64, 32, 4, 1, 0, 0, 512, 2 * 4 * 2 * 8192, 8)
+
 #define DG_MENU(X)                                              \
     DG_LDS_ENTRIES(X, 0, DT_F32, 16)            \
     DG_LDS_ENTRIES(X, 8, DT_F16, 32)            \
@@ -175,9 +184,10 @@ constexpr bool grouped_capable(int variant, int sched, int bm, int bn, int wm, i
     DG_MFMA_F32S3(X, 88)                                         \
     DG_MFMA_SPR(X, 90, DT_F16)                                   \
     DG_MFMA_SPR(X, 94, DT_BF16)                                  \
-    DG_MFMA_F32SMALL(X, 98)
+    DG_MFMA_F32SMALL(X, 98)                                      \
+    DG_MFMA_F32DC(X, 104)
 
-constexpr int kMenuSize = 104;
+constexpr int kMenuSize = 106;
 
 // Fused epilogue ("Shared memory and tensor cores", section 13.10: bias,
 // activation, residual add or type cast applied to the accumulator before the

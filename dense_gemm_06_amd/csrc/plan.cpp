@@ -152,6 +152,7 @@ static double tile_efficiency_aligned(const MenuEntry& e) {
     // alternated: 31.2 against 32.1 us per round and 256 k), with a larger fixed cost
     // per round (fp32_round_overhead); it does not split K
     if (e.sched == 6) return e.bm >= 256 ? 0.72 : 0.40;  // 64 x 64: see plan()
+    if (e.sched == 8) return 0.50;  // see plan()
     if (e.variant == V_LDS) return t >= 128 ? 0.6 : 0.35;
     // the fp32 64 x 64 tile with K split between two wave grids measured 7-9% faster
     // than with one (1024^3: 27.3-27.8 us against 29.6-29.8; 256^3: 8.4-8.6 against
@@ -259,7 +260,7 @@ static int plan_uncached(int opA, int opB, int64_t M, int64_t N, int64_t K, int6
             set_error("max_grid = %d must be non-negative", want_grid);
             return GEMM_ERR_INVALID_VALUE;
         }
-        if (want_sched < 0 || want_sched > 7 || want_wm < 0 || want_wn < 0 || want_variant < 0 || want_variant > 2 || want_vec < -1 || want_vec > 1 || want_remap < -1 ||
+        if (want_sched < 0 || want_sched > 8 || want_wm < 0 || want_wn < 0 || want_variant < 0 || want_variant > 2 || want_vec < -1 || want_vec > 1 || want_remap < -1 ||
             want_remap > 1 || want_group < 0 || want_bm < 0 || want_bn < 0) {
             set_error("invalid requested configuration (variant %d, bm %d, bn %d, vec %d, xcd_remap %d, group_m %d)",
                       want_variant, want_bm, want_bn, want_vec, want_remap, want_group);
@@ -320,8 +321,11 @@ static int plan_uncached(int opA, int opB, int64_t M, int64_t N, int64_t K, int6
         // also a partial last k-tile (K a multiple of 8, zeroed past K in LDS).
         if (direct_copy(e.sched) && (Kx == 0 || (Kx % e.bk != 0 && !(e.sched == 5 && Kx % 8 == 0)))) continue;
         if (direct_copy(e.sched) && (Mx % e.bm != 0 || Nx % e.bn != 0) &&
-            !((e.sched == 5 || e.sched == 2 || e.sched == 4) && (e.opb == 1 || Nx % 8 == 0)))
+            !((e.sched == 5 || e.sched == 2 || e.sched == 4) && (e.opb == 1 || Nx % 8 == 0)) &&
+            !(e.sched == 8 && (e.opb == 1 || Nx % 4 == 0)))
             continue;
+        // the fp32 direct-copy tile: K in whole k-tiles for each of its two K groups
+        if (e.sched == 8 && Kx % 64 != 0) continue;
         // the register-staged software-pipelined kernel reads whole 16-byte chunks
         // inside each row: K >= 8, and N >= 8 for a row-major B
         if (e.sched == 7 && (Kx < 8 || (e.opb == 0 && Nx < 8))) continue;
@@ -420,6 +424,15 @@ static int plan_uncached(int opA, int opB, int64_t M, int64_t N, int64_t K, int6
             // several rounds (2048^3 171.1 against 150.7; 512 x 4096 x 4096 165.0
             // against 149.7)
             if (e.dtype == DT_F32 && e.sched == 6 && e.bm < 256) eff = rounds == 1 ? 0.50 : 0.40;
+            // the fp32 64 x 64 direct-copy tile (one resident per CU), against the
+            // heuristic's choice before it, medians of five alternated passes: 1024^3
+            // 21.5 us against 24.6 (row-major B) and 20.7 against 23.4, 1024^2 x 4096
+            // 70.5 against 82.7, 768^2 x 1024 20.7 against 23.7, 2048^3 147.7 against
+            // 150.1, 512 x 4096 x 4096 140.9 against 148.0; one round of its tiles
+            // gains most (each further round exposes its first copies and its store
+            // again), and 4096^3 (1113 against 1026 for the 256 x 128 tile) or 256^3
+            // (7.3 against 5.4 for the 16 x 64 tile) go to the other tiles
+            if (e.sched == 8) eff = rounds == 1 ? 0.57 : 0.50;
             const double tile_cycles = 2.0 * e.bm * e.bn * std::max<int64_t>(kpad, e.bk) / (rate_per_cu(e) * eff);
             double cost = (double)rounds * (double)std::max<int64_t>(resident, 1) * tile_cycles;
             if (e.dtype == DT_F32 && e.variant == V_MFMA)

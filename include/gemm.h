@@ -87,7 +87,7 @@ typedef struct gemm_config {
     int32_t threads;   /* in/out: 0 any; workgroup size (64 x waves_m x waves_n, or twice that for
                           the fp32 64 x 64 configurations that split K between two wave grids) */
     int32_t lds_bytes; /* out: LDS per workgroup */
-    int32_t grid;      /* out: workgroups launched (tiles_m * tiles_n) */
+    int32_t grid;      /* out: workgroups launched (tiles_m * tiles_n, or a persistent grid) */
     int32_t kernel_id; /* out: index into the library's kernel menu */
     int32_t schedule;  /* in/out: 0 any; 1 register-staged double buffer (any shape); 2 ping-pong
                           with direct global->LDS copies on 16x16x32 MFMAs; 3 not available
@@ -98,10 +98,14 @@ typedef struct gemm_config {
                           multiple of 8 for row-major B; 2, 4: K a multiple of 32; 5: K a multiple of 8;
                           4 stores the plain fp32 accumulator only); 6 register-staged with three LDS
                           stages and fragments read half a k-tile ahead (fp32 256 x 128
-                          tiles, any shape, K not split); 7 the software-pipelined kernel
-                          of schedule 5 with register-staged 16-byte loads (16-bit inputs,
-                          bases aligned to the element, rows at any offset, any M, K >= 8,
-                          any N for column-major B or N >= 8 for row-major B) */
+                          tiles, and 64 x 64 tiles with K over two wave groups; any shape,
+                          K not split); 7 the software-pipelined kernel of schedule 5 with
+                          register-staged 16-byte loads (16-bit inputs, bases aligned to the
+                          element, rows at any offset, any M, K >= 8, any N for column-major
+                          B or N >= 8 for row-major B); 8 fp32 64 x 64 tiles with direct
+                          global->LDS copies three k-tiles ahead, K over two wave groups
+                          (16-byte aligned operands, any M, K a multiple of 64, any N for
+                          column-major B or N a multiple of 4 for row-major B, K not split) */
     int64_t tiles_m, tiles_n; /* out (grouped: of the first non-empty problem) */
     double est_cycles; /* out: the heuristic's cost estimate (clock cycles) */
     int64_t tiles_total; /* out: output tiles of the call (grouped: of all its problems) */

@@ -120,8 +120,10 @@ static void check_plan(int opB, int64_t M, int64_t N, int64_t K, int64_t lda, in
               "direct copies on unaligned operands");
         CHECK(K > 0 && K % 8 == 0, "direct copies with K = %lld", (long long)K);
         if (e.sched != 5) CHECK(K % e.bk == 0, "schedule %d with K = %lld", e.sched, (long long)K);
+        if (e.sched == 8) CHECK(K % 64 == 0, "schedule 8 with K = %lld", (long long)K);
         if (opB == 0)
-            CHECK(N % e.bn == 0 || N % 8 == 0, "row-major B edge tile with N = %lld", (long long)N);
+            CHECK(N % e.bn == 0 || N % (e.sched == 8 ? 4 : 8) == 0, "row-major B edge tile with N = %lld",
+                  (long long)N);
     }
     if (e.sched == 7) {
         // whole 16-byte chunks inside every row: K >= 8, N >= 8 for a row-major B, and

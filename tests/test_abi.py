@@ -52,7 +52,7 @@ def test_status_strings():
 
 def test_menu_is_complete():
     menu = dg.gemm_menu()
-    assert len(menu) == dg.library().gemm_menu_size() == 104
+    assert len(menu) == dg.library().gemm_menu_size() == 106
     seen = set()
     for e in menu:
         assert e["lds_bytes"] <= 160 * 1024
@@ -64,7 +64,7 @@ def test_menu_is_complete():
             k_groups = e["threads"] // (e["waves_m"] * e["waves_n"] * 64)
             assert k_groups * e["waves_m"] * e["waves_n"] * 64 == e["threads"] and k_groups in (1, 2, 4)
             assert k_groups == 1 or (e["dtype"] == 0 and (
-                ((e["bm"], e["bn"]) == (64, 64) and k_groups == 2 and e["schedule"] in (1, 6)) or
+                ((e["bm"], e["bn"]) == (64, 64) and k_groups == 2 and e["schedule"] in (1, 6, 8)) or
                 ((e["bm"], e["bn"]) == (16, 64) and k_groups == 4 and e["schedule"] == 1)))
     for variant in (1, 2):
         for dtype in (0, 1, 2):
@@ -72,7 +72,7 @@ def test_menu_is_complete():
                 for vec in (0, 1):
                     tiles = {(bm, bn) for (v, d, o, ve, bm, bn) in seen if (v, d, o, ve) == (variant, dtype, opb, vec)}
                     assert len(tiles) >= 2, (variant, dtype, opb, vec)
-    assert dg.library().gemm_menu_entry(104, None, None, None, None) == dg.GEMM_ERR_INVALID_VALUE
+    assert dg.library().gemm_menu_entry(106, None, None, None, None) == dg.GEMM_ERR_INVALID_VALUE
 
 
 def plan(M, N, K, dtype="f32", op_b="N", lda=None, ldb=None, ldc=None, a=0, b=0, c=0, cus=256, arch="gfx950",
@@ -175,8 +175,9 @@ def test_plan_three_stage_fp32():
         for shape in ((4096, 4096, 4096), (8192, 8192, 8192), (4000, 4096, 3001)):
             st, c = plan(*shape, "f32", op_b)
             assert st == 0 and c.schedule == 6 and (c.bm, c.bn) == (256, 128) and c.threads == 512, (shape, op_b)
-    # one round of 64 x 64 tiles: the same schedule with two K groups on that tile
-    st, c = plan(1024, 1024, 1024, "f32")
+    # one round of 64 x 64 tiles on unaligned rows: the same schedule with two K
+    # groups on that tile
+    st, c = plan(1024, 1024, 1024, "f32", lda=1025)
     assert st == 0 and c.schedule == 6 and (c.bm, c.bn) == (64, 64)
     # short K: the three-stage tile's fixed cost per round of tiles outweighs its faster
     # k loop; two resident 128 x 128 register-staged tiles per CU
@@ -310,10 +311,16 @@ def test_plan_fills_the_machine():
         assert st == 0 and (c.bm, c.bn) == (16, 64) and c.grid == 64 and c.threads == 256
     st, c = plan(512, 512, 512, "f32")
     assert st == 0 and (c.bm, c.bn) == (16, 64) and c.grid == 256
-    # 1024^3: 64 x 64 tiles fill the machine; one round of them on the three-stage
-    # schedule with two K groups
-    st, c = plan(1024, 1024, 1024, "f32")
-    assert st == 0 and (c.bm, c.bn) == (64, 64) and c.schedule == 6 and c.threads == 512 and c.grid == 256
+    # 1024^3: 64 x 64 tiles fill the machine; one round of them on the direct-copy
+    # tile with two K groups (schedule 8), or on the three-stage schedule where the
+    # operands are not 16-byte aligned
+    for op_b in "NT":
+        st, c = plan(1024, 1024, 1024, "f32", op_b)
+        assert st == 0 and (c.bm, c.bn) == (64, 64) and c.schedule == 8 and c.threads == 512 and c.grid == 256
+    st, c = plan(1024, 1024, 1024, "f32", lda=1025)
+    assert st == 0 and (c.bm, c.bn) == (64, 64) and c.schedule == 6
+    st, c = plan(1024, 1024, 1000, "f32")   # K not a multiple of 64
+    assert st == 0 and c.schedule != 8
     st, c = plan(2048, 2048, 2048, "f32")
     assert st == 0 and c.schedule != 6 or c.bm == 256
     # a tall-skinny problem still picks a tile count close to the CU count or more

@@ -194,6 +194,16 @@ def test_epilogue_register_staged_sp_unaligned(waves_n, out):
 
 
 @pytest.mark.parametrize("op_b", ["N", "T"])
+@pytest.mark.parametrize("out", ["f32", "bf16", "f16"])
+def test_epilogue_f32_direct_copy(op_b, out):
+    """The fp32 direct-copy tile (schedule 8) with a fused epilogue on edge tiles."""
+    ops = gi.make_operands(300, 264 if op_b == "N" else 263, 128, "f32", "normal", seed=13, op_b=op_b)
+    got, ref, Dp, plan = run_epi(ops, out, act="gelu_tanh", cfg=dg.request(schedule=8))
+    assert plan.schedule == 8
+    assert epilogue_error(got, ref, Dp, "f32", out) <= 1.0
+
+
+@pytest.mark.parametrize("op_b", ["N", "T"])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_epilogue_three_stage_fp32(op_b, out):
     """The fp32 three-stage schedule with a fused epilogue, ragged tiles."""

@@ -35,7 +35,7 @@ def _lib_built():
 MENU = _menu()
 MENU_IDS = [f"k{e['kernel_id']}-{'lds' if e['variant'] == 1 else 'mfma'}-{DT_NAME[e['dtype']]}-"
             f"op{'NT'[e['opb']]}-{'v16' if e['vec'] else 'v1'}-{e['bm']}x{e['bn']}-w{e['waves_m']}x{e['waves_n']}"
-            f"{ {1: '', 2: '-pp', 4: '-pp32', 5: '-sp', 6: '-s3', 7: '-spr'}[e['schedule']] }"
+            f"{ {1: '', 2: '-pp', 4: '-pp32', 5: '-sp', 6: '-s3', 7: '-spr', 8: '-dc'}[e['schedule']] }"
             for e in MENU]
 
 
@@ -63,9 +63,13 @@ def ragged_shape(e):
 
     The direct-copy kernels (schedules 2, 4 and 5) get whole tiles here: 2 x 3 tiles
     and 9 k-tiles (an odd count, so both LDS-stage parities and the prefetch tail are
-    exercised); their edge tiles and partial k-tiles have cases of their own below."""
+    exercised); their edge tiles and partial k-tiles have cases of their own below.
+    The fp32 direct-copy tile (schedule 8) gets ragged M and N and ten k-tiles (five
+    per K group)."""
     if e["schedule"] in WHOLE_TILE:
         return 2 * e["bm"], 3 * e["bn"], 9 * e["bk"]
+    if e["schedule"] == 8:  # ragged M and N (a multiple of 4 for row-major B); K a multiple of 64
+        return 2 * e["bm"] + 37, 2 * e["bn"] + (20 if e["opb"] == 0 else 19), 10 * e["bk"]
     return 2 * e["bm"] + 37, 2 * e["bn"] + 19, 3 * e["bk"] + 13
 
 
@@ -216,6 +220,46 @@ def test_register_staged_sp_c5_full_size(waves_n):
     check_untouched(C, ops.M, ops.N)
     Cref, D = oracle.gemm_ref(ops)
     assert normalized_error(C[:ops.M, :ops.N], Cref, D) <= TOL[ops.dtype]
+
+
+@pytest.mark.parametrize("k_groups_tiles", [1, 2, 3, 4, 5, 8, 32])
+@pytest.mark.parametrize("op_b", ["N", "T"])
+def test_f32_direct_copy_k_tile_counts(k_groups_tiles, op_b):
+    """Schedule 8 (fp32 64 x 64 with direct copies, two K groups, four stages) for
+    every small count of k-tiles per group (the prologue issues three, so 1-3 never
+    enter the steady state) and a long K, on ragged M and N."""
+    K = 64 * k_groups_tiles
+    N = 300 if op_b == "N" else 301
+    ops = gi.make_operands(333, N, K, "f32", "normal", seed=k_groups_tiles, op_b=op_b)
+    C = run_ops(ops, cfg=dg.request(schedule=8), ldc=N + 4)
+    check_untouched(C, ops.M, ops.N)
+    Cref, D = oracle.gemm_ref(ops)
+    assert normalized_error(C[:ops.M, :ops.N], Cref, D) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("shape,op_b", [((1024, 1024, 1024), "N"), ((1024, 1024, 1024), "T"), ((65, 4, 64), "N"),
+                                        ((100, 1, 128), "T"), ((1000, 1000, 192), "N"), ((64, 64, 64), "T")])
+def test_f32_direct_copy_integer_exact(shape, op_b):
+    """Integer data through schedule 8, edge tiles included: bit-exact."""
+    M, N, K = shape
+    i = np.arange(M)[:, None]
+    k = np.arange(K)[None, :]
+    a = (((7 * i + 3 * k) % 7) - 3).astype(np.float32)
+    b = (((5 * np.arange(K)[:, None] + 2 * np.arange(N)[None, :] + 1) % 7) - 3).astype(np.float32)
+    ops = gi.from_values(a, b, "f32", op_b)
+    C = run_ops(ops, cfg=dg.request(schedule=8), ldc=N + 1)
+    check_untouched(C, M, N)
+    Cref, _ = oracle.gemm_ref(ops, want_d=False)
+    assert np.array_equal(C[:M, :N].astype(np.float64), Cref)
+
+
+def test_f32_direct_copy_refusals():
+    """Schedule 8 needs K a multiple of 64, 16-byte aligned operands and, for a
+    row-major B, N a multiple of 4: other problems are refused when it is forced."""
+    for (M, N, K, op_b, lda) in ((128, 128, 96, "N", 96), (128, 130, 128, "N", 128), (128, 128, 128, "N", 130)):
+        st, _ = dg.gemm_plan(0, dg.OP_CODE[op_b], M, N, K, lda, N, N, dg.GEMM_F32, 0, 0, 1 << 40, 256, "gfx950",
+                             dg.request(schedule=8), check=False)
+        assert st == dg.GEMM_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("schedule", [2, 4])
