@@ -52,6 +52,8 @@ def kernel_sources(cfg) -> list[str]:
         return common + ["kernel_pp.h"]
     if cfg.schedule in (5, 7):
         return common + ["kernel_sp.h"]
+    if cfg.schedule == 8:
+        return common + ["kernel_sp.h", "kernel_f32dc.h"]
     return common + ["kernel_mfma.h"]
 
 
@@ -78,9 +80,9 @@ def parse():
     p.add_argument("--with-workspace", action="store_true",
                    help="with --only: pass a workspace (the heuristic may split K or pack the operands)")
     p.add_argument("--extended", action="store_true",
-                   help="also time the fused epilogue, the per-launch distribution and the clock under load "
-                        "(more launches of the headline kernel, so a kernel trace of such a run averages "
-                        "over more than the timed steps)")
+                   help="also time the fused epilogue, the per-launch distribution, the clock under load and the "
+                        "four-round problem with one workgroup per tile (more launches of the headline kernel, so a "
+                        "kernel trace of such a run averages over more than the timed steps)")
     p.add_argument("--traffic-probe", type=int, default=0, metavar="MIB",
                    help="instead of GEMMs, run the counter-calibration kernels over MIB MiB each (direct LDS "
                         "copies of 64-byte row segments, 16-byte loads, 16-byte stores)")
@@ -396,7 +398,8 @@ def kernel_name(cfg, dtype):
     if cfg.variant == 1:
         base = "lds_gemm"
     elif dtype == "f32":
-        base = "mfma32_gemm, three LDS stages" if cfg.schedule == 6 else "mfma32_gemm"
+        base = ("mfma32_gemm, three LDS stages" if cfg.schedule == 6 else
+                "mfma32_dc, direct copies" if cfg.schedule == 8 else "mfma32_gemm")
     else:
         base = {1: "mfma16_gemm", 2: "mfma16_pp (16x16x32)", 4: "mfma16_pp (32x32x16)",
                 5: "mfma32_sp (32x32x16)", 7: "mfma32_sp, register-staged (32x32x16)"}[cfg.schedule]
@@ -484,9 +487,13 @@ def main():
         for name in ("c3_f32_4096", "c1_f32_256", "c2_f32_1024", "c5_bf16_ragged", "m8_f16_shard", "m8_f32_shard",
                      "r4_f16_8192x8192x2048"):
             extras[name] = time_problem(name, max(5, a.steps // 2), max(2, a.warmup // 2), min_window_ms=5.0, min_warm_ms=20.0)
-        # the same four-round problem with one workgroup per tile (no persistent grid)
-        one_per_tile = time_problem("r4_f16_8192x8192x2048", max(5, a.steps // 2), max(2, a.warmup // 2),
-                                    force={"max_grid": 1 << 30}, min_window_ms=5.0, min_warm_ms=20.0)
+        # the same four-round problem with one workgroup per tile (no persistent grid):
+        # the headline's kernel, so only with --extended (the default command runs the
+        # headline kernel for the headline's steps alone)
+        one_per_tile = None
+        if a.extended:
+            one_per_tile = time_problem("r4_f16_8192x8192x2048", max(5, a.steps // 2), max(2, a.warmup // 2),
+                                        force={"max_grid": 1 << 30}, min_window_ms=5.0, min_warm_ms=20.0)
 
     cfg = main_res["cfg"]
     traffic = load_traffic(headline, cfg)
@@ -536,11 +543,12 @@ def main():
                                  for k, v in extras.items()}
         for k, v in extras.items():
             out["other_problems"][k]["grid"] = v["cfg"].grid
-        r = one_per_tile
-        out["other_problems"]["r4_f16_8192x8192x2048"].update(
-            workload="C=A@B 8192x8192x2048 f16: four rounds of 256 tiles on the persistent grid",
-            one_workgroup_per_tile={"tflops": round(r["tflops"], 3), "ms_per_step": round(r["ms_per_step"], 6),
-                                    "grid": r["cfg"].grid})
+        out["other_problems"]["r4_f16_8192x8192x2048"]["workload"] = (
+            "C=A@B 8192x8192x2048 f16: four rounds of 256 tiles on the persistent grid")
+        if one_per_tile is not None:
+            r = one_per_tile
+            out["other_problems"]["r4_f16_8192x8192x2048"]["one_workgroup_per_tile"] = {
+                "tflops": round(r["tflops"], 3), "ms_per_step": round(r["ms_per_step"], 6), "grid": r["cfg"].grid}
         # the under-filled problems again with a workspace (the heuristic may split K),
         # and a long-K problem with 16 output tiles, where splitting pays
         lk = time_problem("k1_f32_long_k", max(5, a.steps // 2), max(2, a.warmup // 2), min_window_ms=5.0, min_warm_ms=20.0)
