@@ -98,10 +98,16 @@ __device__ __forceinline__ u32x4 keep_first8(u32x4 w, int v) {
 // loaded one iteration earlier; the load of tile t+2 then reuses them. The LDS
 // layout, the fragment reads, the MFMAs and the epilogue are those of the direct-copy
 // form.
-template <int DT, int OPB, int NW, bool REG, bool PERSIST = false>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void mfma32_sp(
-    GemmArgs g) {
+//
+// GROUPED (persistent direct-copy form only): the tiles are those of a grouped call's
+// problems, in the linear order of its segment table (each problem, batch member and
+// tile raster as for the register-staged grouped kernels); each tile carries its own
+// operands, leading dimensions, M, N, K and C, and the copy stream runs on across
+// problems as across tiles. g then holds only xcd_remap (and no fused epilogue).
+template <int DT, int OPB, int NW, bool REG, bool PERSIST, bool GROUPED>
+__device__ __forceinline__ void mfma32_sp_body(GemmArgs& g, const GroupArgs* ga) {
     static_assert(NW == 4 || NW == 8, "waves");
+    static_assert(!GROUPED || (PERSIST && !REG && NW == 8), "grouped: the persistent direct-copy form");
     constexpr int BM = 256, BN = 256, BK = 32, S = 4, D = S - 1;  // D: copy distance in tiles
     constexpr int SA = BM * BK, SB = BN * BK;                     // halfs per stage
     constexpr int STAGE_BYTES = SA * 2;                           // 16 KB for each of A and B
@@ -118,7 +124,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     // Output tiles: one per workgroup (grid = tiles) or, for the direct-copy form, a
     // persistent grid that takes them in rounds of its size (the tile loop below).
     // With xcd_remap each XCD's workgroups take a contiguous run of each round.
-    const int tiles_total = g.tiles_m * g.tiles_n;
+    int tiles_total;
+    if constexpr (GROUPED) tiles_total = ga->total_tiles;
+    else tiles_total = g.tiles_m * g.tiles_n;
     int round = 0;
     int tile = round_tile(0, tiles_total, g.xcd_remap);
     // K a multiple of 8: the last k-tile may be partial (krem of its 32 k valid); its
@@ -127,8 +135,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     const int nk = (g.K + BK - 1) / BK;
     const int krem = g.K - (nk - 1) * BK;
     const bool ktail = krem < BK;
-    const uint16_t* __restrict__ A = static_cast<const uint16_t*>(g.A);
-    const uint16_t* __restrict__ B = static_cast<const uint16_t*>(g.B);
 
     // ---- direct copies: wave w moves blocks CPB*w .. CPB*w+CPB-1 (1 KB each) of the A
     // tile and of the B tile. Lane L of block b lands at LDS byte b*1024 + 16L, a fixed
@@ -149,43 +155,89 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
         kcA[i] = ((lane & 3) ^ kmaj32_swz(row)) << 3;
         kcB[i] = OPB == 1 ? kcA[i] : b * 2 + (lane >> 5);
     }
-    // A lane's chunk sources for one output tile, and the tile's origin.
+    // A lane's chunk sources for one output tile, the tile's origin, and what the tile
+    // needs of its problem: the k-tile count, the step between k-tiles of B, and C
+    // with its leading dimension and bounds (the call's, or the tile's problem's in a
+    // grouped call).
     struct Src {
         const uint16_t* a[CPB];
         const uint16_t* b[CPB];
         int nv[CPB];  // REG, row-major B: columns of the lane's chunk inside N (0..8)
         int m0, n0;
+        int M, N, nk;
+        size_t kstep_b;  // elements per k-tile of B
+        float* C;
+        int64_t ldc;
+    };
+    // The problem of tile t: operands, leading dimensions, sizes and tile coordinates.
+    struct Prob {
+        const uint16_t* A;
+        const uint16_t* B;
+        float* C;
+        int64_t lda, ldb, ldc;
+        int M, N, K, tm, tn;
+    };
+    auto prob_of = [&](int t, Prob& p) {
+        if constexpr (GROUPED) {
+            GemmArgs gt;
+            group_tile<2>(*ga, t, gt, p.tm, p.tn);
+            p.A = static_cast<const uint16_t*>(gt.A);
+            p.B = static_cast<const uint16_t*>(gt.B);
+            p.C = gt.C;
+            p.lda = gt.lda;
+            p.ldb = gt.ldb;
+            p.ldc = gt.ldc;
+            p.M = gt.M;
+            p.N = gt.N;
+            p.K = gt.K;
+        } else {
+            raster(t, g.tiles_m, g.tiles_n, g.group_m, p.tm, p.tn);
+            p.A = static_cast<const uint16_t*>(g.A);
+            p.B = static_cast<const uint16_t*>(g.B);
+            p.C = g.C;
+            p.lda = g.lda;
+            p.ldb = g.ldb;
+            p.ldc = g.ldc;
+            p.M = g.M;
+            p.N = g.N;
+            p.K = g.K;
+        }
     };
     auto make_src = [&](int t, Src& s) {
-        int tm, tn;
-        raster(t, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
-        s.m0 = tm * BM;
-        s.n0 = tn * BN;
+        Prob p;
+        prob_of(t, p);
+        s.m0 = p.tm * BM;
+        s.n0 = p.tn * BN;
+        s.M = p.M;
+        s.N = p.N;
+        s.nk = (p.K + BK - 1) / BK;
+        s.kstep_b = OPB == 0 ? (size_t)BK * p.ldb : (size_t)BK;
+        s.C = p.C;
+        s.ldc = p.ldc;
 #pragma unroll
         for (int i = 0; i < CPB; ++i) {
             const int b = wave * CPB + i;
             const int row = b * 16 + (lane >> 2);
-            s.a[i] = A + (size_t)min(s.m0 + row, g.M - 1) * g.lda + kcA[i];
+            s.a[i] = p.A + (size_t)min(s.m0 + row, p.M - 1) * p.lda + kcA[i];
             if (OPB == 1) {
-                s.b[i] = B + (size_t)min(s.n0 + row, g.N - 1) * g.ldb + kcB[i];
+                s.b[i] = p.B + (size_t)min(s.n0 + row, p.N - 1) * p.ldb + kcB[i];
             } else {
                 const int krow = kcB[i];
                 const int col = s.n0 + (((lane & 31) ^ nmaj32_swz(krow)) << 3);
                 if constexpr (REG) {
                     // a chunk that straddles N is read from the row's last 8 columns, one
                     // wholly past N from column 0 (N >= 8); the write shifts or zeroes it
-                    const int v = g.N - col;
+                    const int v = p.N - col;
                     s.nv[i] = v < 0 ? 0 : (v > 8 ? 8 : v);
-                    s.b[i] = B + (size_t)krow * g.ldb + (v >= 8 ? col : v > 0 ? g.N - 8 : 0);
+                    s.b[i] = p.B + (size_t)krow * p.ldb + (v >= 8 ? col : v > 0 ? p.N - 8 : 0);
                 } else {
-                    s.b[i] = B + (size_t)krow * g.ldb + (col < g.N ? col : 0);
+                    s.b[i] = p.B + (size_t)krow * p.ldb + (col < p.N ? col : 0);
                 }
             }
         }
     };
     Src cur;  // the tile being computed
     make_src(tile, cur);
-    const size_t kstepB = OPB == 0 ? (size_t)BK * g.ldb : (size_t)BK;  // elements per k-tile
     // LDS destinations as plain wave-uniform numbers (M0 takes them directly). Built
     // from an integer, a copy's LDS pointer carries no link to sA / sB, so the
     // compiler does not make every later LDS read wait for all copies in flight
@@ -201,7 +253,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
         __builtin_amdgcn_global_load_lds(DG_GLB(src), DG_LDS_AT(dstA + st * STAGE_BYTES + i * 1024u), 16, 0, 0);
     };
     auto copy_b = [&](const Src& s, int t, uint32_t st, int i, auto tail_tag) {
-        const uint16_t* src = s.b[i] + (size_t)t * kstepB;
+        const uint16_t* src = s.b[i] + (size_t)t * s.kstep_b;
         if (decltype(tail_tag)::value && kcB[i] >= krem)
             src = OPB == 1 ? s.b[i] - kcB[i] : s.b[i] - (size_t)kcB[i] * g.ldb;
         __builtin_amdgcn_global_load_lds(DG_GLB(src), DG_LDS_AT(dstB + st * STAGE_BYTES + i * 1024u), 16, 0, 0);
@@ -251,7 +303,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
             ra[c] = ld16(src);
         } else {
             const int i = c - CPB;
-            const uint16_t* src = cur.b[i] + (size_t)t * kstepB;
+            const uint16_t* src = cur.b[i] + (size_t)t * cur.kstep_b;
             if (TAIL) {
                 if (OPB == 1) {
                     const int v = g.K - (t * BK + kcB[i]);
@@ -395,6 +447,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
         if (m < g.M) {
             if (g.ep.kind == 0) store_run4<false>(g, m, n, v);
             else epilogue_run4_body(g.ep, g.C, g.ldc, g.N, m, n, v);
+        }
+    };
+    // The same for the persistent form, with C, its leading dimension and bounds from
+    // the tile's sources (its own problem's in a grouped call, which has no fused
+    // epilogue)
+    auto store4p = [&](const Src& s, int m, int n, f32x4 v) {
+        if (m >= s.M) return;
+        if (GROUPED || g.ep.kind == 0) {
+            float* cp = s.C + (size_t)m * s.ldc + n;
+            if (n + 3 < s.N) {
+                __builtin_memcpy(cp, &v, 16);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (n + e < s.N) cp[e] = v[e];
+            }
+        } else {
+            epilogue_run4_body(g.ep, g.C, g.ldc, g.N, m, n, v);
         }
     };
     // The whole LDS, 64 rows of the wave tile at a time: each wave owns a slot of 64
@@ -629,7 +699,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         settle(f0);
         // One iteration (k-tile t, stage (sb + t) & 3). LAST: one of the last D, which
-        // copies k-tile t + D - nk of the next tile when there is one (a uniform branch
+        // copies k-tile t + D - nk of the next tile (nk: this tile's k-tiles) when there is one (a uniform branch
         // around the copies) and otherwise nothing. A primed tile's first two
         // iterations skip the memory wait: their k-tiles 1 and 2 are complete.
         auto iteration = [&](int t, auto last_tag) {
@@ -638,12 +708,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
             const uint32_t cst = (sb + (uint32_t)(t + D)) & 3u;
             const bool copy = !LAST || has_next;
             const Src& cs = LAST ? nxt : cur;
-            const int ct = LAST ? t + D - nk : t + D;
+            const int ct = LAST ? t + D - cur.nk : t + D;
             step(f0, f1, (int)st, 1, copy, cs, ct, cst, 0, no);
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             if (!(primed && t < 2)) {
                 if (!LAST) vm_wait_n<2 * CPB * (D - 2) + CPB>();
-                else vm_wait(copy ? 2 * CPB * (D - 2) + CPB : 2 * CPB * max(0, nk - t - 2));
+                else vm_wait(copy ? 2 * CPB * (D - 2) + CPB : 2 * CPB * max(0, cur.nk - t - 2));
             }
             asm volatile("s_barrier" ::: "memory");
             settle(f1);
@@ -652,8 +722,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
             settle(f0);
         };
         int t = 0;
-        for (; t + D < nk; ++t) iteration(t, no);
-        for (; t < nk; ++t) iteration(t, yes);
+        for (; t + D < cur.nk; ++t) iteration(t, no);
+        for (; t < cur.nk; ++t) iteration(t, yes);
         // epilogue through the stage of this tile's last k-tile, (sb + nk - 1) & 3: 4 KB
         // per wave, one 32 x 32 subtile at a time (32 rows of 128 bytes, chunk c of row r
         // at c ^ (r & 7); the bank-conflict counter reads zero for both the
@@ -663,7 +733,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
         // arithmetic) exists once per subtile.
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
         __syncthreads();
-        const uint32_t es = (sb + (uint32_t)(nk - 1)) & 3u;
+        const uint32_t es = (sb + (uint32_t)(cur.nk - 1)) & 3u;
         char* slot = reinterpret_cast<char*>(wave < NW / 2 ? &sA[es][0] : &sB[es][0]) + (wave % (NW / 2)) * 4096;
         const int cm0 = cur.m0 + wrow0, cn0 = cur.n0 + wcol0;
         vm_wait_n<0>();  // the next tile's first k-tiles, before any store
@@ -683,7 +753,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
                 for (int it = 0; it < 4; ++it) {
                     const int row = it * 8 + (lane >> 3), c = lane & 7;
                     const f32x4 v = *reinterpret_cast<const f32x4*>(slot + row * 128 + ((c ^ (row & 7)) << 4));
-                    store4(cm0 + 32 * i + row, cn0 + 32 * j + c * 4, v);
+                    store4p(cur, cm0 + 32 * i + row, cn0 + 32 * j + c * 4, v);
                 }
                 __builtin_amdgcn_wave_barrier();
             }
@@ -692,7 +762,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
         // every wave's slot reads are done before the next tile refills this stage
         __syncthreads();
         primed = true;
-        sb = (sb + (uint32_t)nk) & 3u;
+        sb = (sb + (uint32_t)cur.nk) & 3u;
         cur = nxt;
         tile = ntile;
         ++round;
@@ -702,6 +772,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
             for (int j = 0; j < SJ; ++j) acc[i][j] = f32x16{};
     }
     }
+}
+
+template <int DT, int OPB, int NW, bool REG, bool PERSIST = false>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void mfma32_sp(
+    GemmArgs g) {
+    mfma32_sp_body<DT, OPB, NW, REG, PERSIST, false>(g, nullptr);
+}
+
+// Grouped calls on the persistent direct-copy form (8 waves; every problem 16-byte
+// aligned with K a multiple of 32 and at least 128, row-major B with N a multiple of
+// 8: checked by the host).
+template <int DT, int OPB>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void mfma32_sp_grouped(GroupArgs ga) {
+    GemmArgs g = {};
+    g.xcd_remap = ga.xcd_remap;
+    g.ep.kind = 0;
+    mfma32_sp_body<DT, OPB, 8, false, true, true>(g, &ga);
 }
 
 }  // namespace dg

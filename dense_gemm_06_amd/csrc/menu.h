@@ -60,10 +60,14 @@ constexpr bool epilogue_capable(int sched) { return sched != 4; }
 
 // Configurations that also have a grouped (persistent) form: the register-staged
 // schedule, which masks every edge, except the 4-wave 256 x 256 tiles (their
-// grouped form runs out of registers) and the MFMA tiles that split K between two
-// wave grids (threads = 2 x 64 x wm x wn).
+// grouped form runs out of registers) and the MFMA tiles that split K between wave
+// groups (threads = KG x 64 x wm x wn); and the 8-wave software-pipelined
+// direct-copy kernel on its persistent form (every problem 16-byte aligned with K a
+// multiple of 32 and at least 128, row-major B with N a multiple of 8).
 constexpr bool grouped_capable(int variant, int sched, int bm, int bn, int wm, int wn, int threads) {
-    return sched == 1 && !(bm == 256 && bn == 256 && wm * wn == 4) && (variant != V_MFMA || threads == wm * wn * 64);
+    return (sched == 1 && !(bm == 256 && bn == 256 && wm * wn == 4) &&
+            (variant != V_MFMA || threads == wm * wn * 64)) ||
+           (sched == 5 && threads == 512);
 }
 
 // X(id, variant, dtype, opb, vec, bm, bn, bk, wm, wn, tm, tn, threads, lds_bytes, sched)

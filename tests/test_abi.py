@@ -446,13 +446,36 @@ def test_grouped_plan_counts_tiles_and_launches():
     assert st == 0 and c.launches == 0 and c.tiles_total == 0
 
 
-def test_grouped_plan_never_picks_full_tile_schedules():
+def test_grouped_plan_schedules():
+    """Grouped calls run the register-staged schedule (1) or, where every problem is
+    16-byte aligned with K a multiple of 32 and at least 128 (row-major B: N a multiple
+    of 8), the persistent software-pipelined kernel (schedule 5, 8 waves); never the
+    other whole-tile schedules."""
     for dt in (dg.GEMM_F16, dg.GEMM_BF16):
-        st, c = dg.gemm_grouped_plan(0, 0, dt, distinct([(4096, 4096, 4096)]))
-        assert st == 0 and c.schedule == 1 and not (c.bm == 256 and c.bn == 256 and c.waves_m * c.waves_n == 4)
-        st, _ = dg.gemm_grouped_plan(0, 0, dt, distinct([(4096, 4096, 4096)]), req=dg.request(schedule=2),
-                                     check=False)
-        assert st == dg.GEMM_ERR_UNSUPPORTED
+        for op_b in "NT":
+            st, c = dg.gemm_grouped_plan(0, dg.OP_CODE[op_b], dt, [gp(4096, 4096, 1024, op_b=op_b)] * 1 +
+                                         [gp(2048, 1000, 512, a=1 << 36, b=1 << 37, c=1 << 38, op_b=op_b)])
+            assert st == 0 and c.schedule == 5 and c.threads == 512 and c.grid == 256 and c.xcd_remap == 1
+        # a batch at 16-byte strides keeps it; an odd stride, K not a multiple of 32,
+        # K below 128, N not a multiple of 8 for row-major B, or fp32 do not
+        # (16 members of 16 tiles: enough 256 x 256 tiles to fill the machine)
+        ok = gp(1024, 1024, 256, batch=16, sa=1024 * 256 + 8, sb=256 * 1024 + 8, sc=1024 * 1024)
+        assert dg.gemm_grouped_plan(0, 0, dt, [ok])[1].schedule == 5
+        for bad in (gp(1024, 1024, 256, batch=16, sa=1024 * 256 + 1, sb=256 * 1024, sc=1024 * 1024),
+                    gp(4096, 4096, 1000), gp(4096, 4096, 96), gp(4096, 4092, 256),
+                    gp(4096, 4096, 256, a=(1 << 20) + 2)):
+            st, c = dg.gemm_grouped_plan(0, 0, dt, [bad])
+            assert st == 0 and c.schedule == 1, bad
+            st, _ = dg.gemm_grouped_plan(0, 0, dt, [bad], req=dg.request(schedule=5), check=False)
+            assert st == dg.GEMM_ERR_UNSUPPORTED
+        for sched in (2, 4, 6, 7):
+            st, _ = dg.gemm_grouped_plan(0, 0, dt, distinct([(4096, 4096, 4096)]), req=dg.request(schedule=sched),
+                                         check=False)
+            assert st == dg.GEMM_ERR_UNSUPPORTED
+        st, c = dg.gemm_grouped_plan(0, 0, dt, distinct([(4096, 4096, 4096)]), req=dg.request(schedule=1))
+        assert st == 0 and c.schedule == 1
+    st, c = dg.gemm_grouped_plan(0, 0, dg.GEMM_F32, distinct([(4096, 4096, 4096)]))
+    assert st == 0 and c.schedule == 1
 
 
 def test_grouped_plan_max_grid_and_vec():

@@ -210,3 +210,87 @@ def test_grouped_vector_path(dtype):
         assert cfg.vec == 1
         run(unaligned, dtype, "N", cfg=dg.request(vec=vec))
         unaligned[0].check()
+
+
+# ---- grouped calls on the persistent software-pipelined kernel (schedule 5)
+
+def aligned_entry(M, N, K, dtype, op_b, seed, batch=1, gap=8):
+    """Rows and batch strides that are multiples of 16 bytes (8 elements)."""
+    ldb = N if op_b == "N" else K
+    members = [gi.make_operands(M, N, K, dtype, "normal", seed=seed * 100 + i, op_b=op_b, lda=K, ldb=ldb)
+               for i in range(batch)]
+    la, lb = len(members[0].A), len(members[0].B)
+    up = lambda n: -(-n // 8) * 8 + gap
+    return Entry(members, ldc=N + 3, stride_a=up(la), stride_b=up(lb))
+
+
+SP = dg.request(schedule=5)  # forced: these are tests of the kernel, on shapes of any size
+
+
+def sp_plan(entries, dtype, op_b, cfg=None):
+    _, plan = dg.gemm_grouped_plan(0, dg.OP_CODE[op_b], dg.DTYPE_CODE[dtype], [e.problem() for e in entries],
+                                   req=cfg)
+    print(f"grouped plan: schedule {plan.schedule}, grid {plan.grid}, tiles {plan.tiles_total}", flush=True)
+    return plan
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("op_b", ["N", "T"])
+def test_grouped_software_pipelined_mixed(dtype, op_b):
+    """Aligned problems of different M, N and K (whole k-tiles, four or more) in one
+    persistent launch of the software-pipelined kernel: edge tiles, a batch, K from 128
+    to 1056, the copy stream running on across problems."""
+    entries = [
+        aligned_entry(300, 264, 128, dtype, op_b, 1),
+        aligned_entry(512, 512, 1056, dtype, op_b, 2),
+        aligned_entry(257, 776, 160, dtype, op_b, 3, batch=3),
+        aligned_entry(64, 8, 256, dtype, op_b, 4),
+        aligned_entry(1000, 520, 224, dtype, op_b, 5),
+    ]
+    plan = sp_plan(entries, dtype, op_b, SP)
+    assert plan.schedule == 5 and plan.threads == 512
+    run(entries, dtype, op_b, cfg=SP)
+    for e in entries:
+        e.check()
+
+
+@pytest.mark.parametrize("max_grid", [1, 3, 8, 16])
+def test_grouped_software_pipelined_grids(max_grid):
+    """Capped grids: each workgroup walks many tiles of several problems."""
+    entries = [aligned_entry(512, 512, 256, "bf16", "T", 80 + s) for s in range(3)] + \
+              [aligned_entry(300, 600, 128, "bf16", "T", 84, batch=2)]
+    req = dg.request(schedule=5, max_grid=max_grid)
+    plan = sp_plan(entries, "bf16", "T", req)
+    assert plan.schedule == 5 and plan.grid == max_grid
+    run(entries, "bf16", "T", cfg=req)
+    for e in entries:
+        e.check()
+
+
+@pytest.mark.parametrize("op_b", ["N", "T"])
+def test_grouped_software_pipelined_integer_exact(op_b):
+    entries = []
+    for s, (M, N, K) in enumerate([(300, 264, 256), (513, 520, 128), (256, 256, 512)]):
+        i = np.arange(M)[:, None]
+        k = np.arange(K)[None, :]
+        a = (((7 * i + 3 * k + s) % 7) - 3).astype(np.float32)
+        b = (((5 * np.arange(K)[:, None] + 2 * np.arange(N)[None, :] + s + 1) % 7) - 3).astype(np.float32)
+        entries.append(Entry([gi.from_values(a, b, "f16", op_b)], ldc=N + 1))
+    plan = sp_plan(entries, "f16", op_b, SP)
+    assert plan.schedule == 5
+    run(entries, "f16", op_b, cfg=SP)
+    for e in entries:
+        e.check(exact=True)
+
+
+def test_strided_batched_software_pipelined():
+    """Eight 768 x 1024 x 512 bf16 products with column-major B at padded strides."""
+    torch = _torch()
+    e = aligned_entry(768, 1024, 512, "bf16", "T", 90, batch=8, gap=64)
+    m0 = e.members[0]
+    plan = sp_plan([e], "bf16", "T", SP)
+    assert plan.schedule == 5
+    dg.gemm_strided_batched(0, dg.GEMM_OP_T, e.M, e.N, e.K, e.a_ptr, m0.lda, e.sa, e.b_ptr, m0.ldb, e.sb, e.c_ptr,
+                            e.ldc, e.sc, e.batch, dg.GEMM_BF16, SP, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    e.check()
