@@ -152,7 +152,7 @@ static double tile_efficiency_aligned(const MenuEntry& e) {
     // alternated: 31.2 against 32.1 us per round and 256 k), with a larger fixed cost
     // per round (fp32_round_overhead); it does not split K
     if (e.sched == 6) return e.bm >= 256 ? 0.72 : 0.40;  // 64 x 64: see plan()
-    if (e.sched == 8) return 0.50;  // see plan()
+    if (e.sched == 8) return 0.50;  // not used: plan() costs it from a fit of its own
     if (e.variant == V_LDS) return t >= 128 ? 0.6 : 0.35;
     // the fp32 64 x 64 tile with K split between two wave grids measured 7-9% faster
     // than with one (1024^3: 27.3-27.8 us against 29.6-29.8; 256^3: 8.4-8.6 against
@@ -424,19 +424,23 @@ static int plan_uncached(int opA, int opB, int64_t M, int64_t N, int64_t K, int6
             // several rounds (2048^3 171.1 against 150.7; 512 x 4096 x 4096 165.0
             // against 149.7)
             if (e.dtype == DT_F32 && e.sched == 6 && e.bm < 256) eff = rounds == 1 ? 0.50 : 0.40;
-            // the fp32 64 x 64 direct-copy tile (one resident per CU), against the
-            // heuristic's choice before it, medians of five alternated passes: 1024^3
-            // 21.5 us against 24.6 (row-major B) and 20.7 against 23.4, 1024^2 x 4096
-            // 70.5 against 82.7, 768^2 x 1024 20.7 against 23.7, 2048^3 147.7 against
-            // 150.1, 512 x 4096 x 4096 140.9 against 148.0; one round of its tiles
-            // gains most (each further round exposes its first copies and its store
-            // again), and 4096^3 (1113 against 1026 for the 256 x 128 tile) or 256^3
-            // (7.3 against 5.4 for the 16 x 64 tile) go to the other tiles
-            if (e.sched == 8) eff = rounds == 1 ? 0.57 : 0.50;
+            // (the fp32 64 x 64 direct-copy tile, schedule 8, is costed below)
             const double tile_cycles = 2.0 * e.bm * e.bn * std::max<int64_t>(kpad, e.bk) / (rate_per_cu(e) * eff);
             double cost = (double)rounds * (double)std::max<int64_t>(resident, 1) * tile_cycles;
-            if (e.dtype == DT_F32 && e.variant == V_MFMA)
+            if (e.dtype == DT_F32 && e.variant == V_MFMA && e.sched != 8)
                 cost += (double)rounds * fp32_round_overhead(e, std::max<int64_t>(resident, 1));
+            // The direct-copy tile's time, fitted per round of its tiles (one resident per
+            // CU) from 1024^3 21.2 us (one round), 1536^3 86.3 (three), 2048^3 147.7
+            // (four), 2560^3 316.8 (seven) and 1024^2 x 256 8.7: about 4.5 us per round
+            // (the launch's share, the first copies, the K-group reduction and the
+            // store) and 15.8 us per 1024 of K, in the model's cycles (2400 per us). It
+            // loses to larger tiles once the rounds pile up their fixed cost (4096^3 1113
+            // us against 1026 for the 256 x 128 tile, 6144^2 x 512 403 against 323 for
+            // 128 x 128 tiles, 8192^2 x 1024 1568 against 1066): not past nine rounds.
+            if (e.sched == 8) {
+                if (rounds > 9) continue;
+                cost = (double)rounds * (10800.0 + 37.0 * (double)kpad);
+            }
             // the reduction reads every plane and writes C, and is a second launch;
             // measured at 256^3 and 1024^3 fp32, a split costs about 16000 cycles
             // beyond its traffic (about 1 KB per clock for a kernel of this size),

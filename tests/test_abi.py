@@ -300,6 +300,25 @@ def test_plan_cache_returns_the_uncached_plan():
     assert st == st1 == st2 == 0 and c0.split_k == 1 and c1.split_k > 1 and snap(c2) == snap(c0)
 
 
+def test_plan_fp32_choices_follow_measurements():
+    """fp32 tile choices on shapes where each kernel was timed against the others on
+    the device (the fastest of the alternatives in medians of five alternated passes):
+    the direct-copy 64 x 64 tile for one to a few rounds of its tiles, 128 x 128 tiles
+    or the 256 x 128 three-stage tile once its rounds pile up, 16 x 64 tiles for few
+    tiles."""
+    cases = {(1536, 1536, 1536, "N"): 8, (2560, 2560, 2560, "N"): 8, (3072, 3072, 1024, "T"): 8,
+             (1024, 4096, 4096, "N"): 8, (2048, 2048, 2048, "N"): 8, (768, 768, 1024, "N"): 8,
+             (4096, 4096, 4096, "N"): 6, (6144, 6144, 512, "N"): (1, 128), (8192, 8192, 1024, "N"): (1, 128),
+             (512, 512, 512, "N"): (1, 16), (256, 256, 16384, "N"): (1, 16)}
+    for (M, N, K, op_b), want in cases.items():
+        st, c = plan(M, N, K, "f32", op_b)
+        assert st == 0
+        if isinstance(want, tuple):
+            assert (c.schedule, c.bm) == want, ((M, N, K), c.schedule, c.bm)
+        else:
+            assert c.schedule == want, ((M, N, K), c.schedule)
+
+
 def test_plan_fills_the_machine():
     """A smaller problem gets smaller tiles so that the grid covers the compute units."""
     st, c = plan(1024, 1024, 1024, "f32")
