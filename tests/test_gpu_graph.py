@@ -59,7 +59,8 @@ def run_case(make_call, inputs, outputs):
         assert torch.isfinite(outputs[0].float()).all()
 
 
-@pytest.mark.parametrize("case", ["pipelined_f16", "pipelined_reg_bf16", "three_stage_f32", "register_staged_bf16_T"])
+@pytest.mark.parametrize("case", ["pipelined_f16", "pipelined_reg_bf16", "three_stage_f32", "register_staged_bf16_T",
+                                  "persistent_f16", "direct_copy_f32", "small_tile_f32"])
 def test_plain_call_in_graph(case):
     torch = _torch()
     dtype, op_b, shape, req = {
@@ -67,6 +68,9 @@ def test_plain_call_in_graph(case):
         "pipelined_reg_bf16": ("bf16", "T", (1001, 1023, 1037), dg.request(schedule=7)),
         "three_stage_f32": ("f32", "N", (600, 500, 300), dg.request(schedule=6)),
         "register_staged_bf16_T": ("bf16", "T", (301, 257, 103), None),
+        "persistent_f16": ("f16", "N", (1000, 1304, 256), dg.request(schedule=5, waves_n=4, max_grid=7)),
+        "direct_copy_f32": ("f32", "T", (1000, 900, 384), dg.request(schedule=8)),
+        "small_tile_f32": ("f32", "N", (256, 256, 256), dg.request(bm=16, bn=64, threads=256, schedule=1)),
     }[case]
     M, N, K = shape
     A, lda, B, ldb = operands(torch, M, N, K, dtype, op_b, pad=(3, 5) if case in ("register_staged_bf16_T", "pipelined_reg_bf16") else (0, 0))
@@ -119,19 +123,23 @@ def test_epilogue_call_in_graph():
     run_case(call, [A, B, bias], C)
 
 
-def test_grouped_call_in_graph():
+@pytest.mark.parametrize("case", ["register_staged_f32", "software_pipelined_f16"])
+def test_grouped_call_in_graph(case):
     torch = _torch()
-    shapes = [(256, 256, 256), (100, 130, 70), (64, 512, 33)]
-    ops = [operands(torch, M, N, K, "f32", "N") for (M, N, K) in shapes]
+    if case == "register_staged_f32":
+        dtype, req, shapes = "f32", None, [(256, 256, 256), (100, 130, 70), (64, 512, 33)]
+    else:  # the persistent software-pipelined grouped kernel: aligned, whole k-tiles
+        dtype, req, shapes = "f16", dg.request(schedule=5), [(512, 512, 256), (300, 264, 128), (257, 776, 512)]
+    ops = [operands(torch, M, N, K, dtype, "N") for (M, N, K) in shapes]
     C = [[torch.zeros(M * N, dtype=torch.float32, device="cuda") for (M, N, K) in shapes] for _ in range(2)]
-    print("graph case grouped", flush=True)
+    print(f"graph case grouped {case}", flush=True)
 
     def probs(i):
         return [dg.problem(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C[i][j].data_ptr(), N)
                 for j, ((M, N, K), (A, lda, B, ldb)) in enumerate(zip(shapes, ops))]
 
     def call(i, s):
-        dg.gemm_grouped(0, 0, dg.GEMM_F32, probs(i), None, s)
+        dg.gemm_grouped(0, 0, dg.DTYPE_CODE[dtype], probs(i), req, s)
 
     inputs = [t for (A, _, B, _) in ops for t in (A, B)]
     for i, t in enumerate(inputs):
