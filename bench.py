@@ -52,7 +52,7 @@ def kernel_sources(cfg) -> list[str]:
         return common + ["kernel_pp.h"]
     if cfg.schedule in (5, 7):
         return common + ["kernel_sp.h"]
-    if cfg.schedule == 8:
+    if cfg.schedule in (8, 9):
         return common + ["kernel_sp.h", "kernel_f32dc.h"]
     return common + ["kernel_mfma.h"]
 
@@ -399,7 +399,8 @@ def kernel_name(cfg, dtype):
         base = "lds_gemm"
     elif dtype == "f32":
         base = ("mfma32_gemm, three LDS stages" if cfg.schedule == 6 else
-                "mfma32_dc, direct copies" if cfg.schedule == 8 else "mfma32_gemm")
+                "mfma32_dc, direct copies" if cfg.schedule == 8 else
+                "mfma32_dcl, direct copies" if cfg.schedule == 9 else "mfma32_gemm")
     else:
         base = {1: "mfma16_gemm", 2: "mfma16_pp (16x16x32)", 4: "mfma16_pp (32x32x16)",
                 5: "mfma32_sp (32x32x16)", 7: "mfma32_sp, register-staged (32x32x16)"}[cfg.schedule]

@@ -225,3 +225,201 @@ __global__ __launch_bounds__(256 * KG) void mfma32_dc(GemmArgs g) {
 }
 
 }  // namespace dg
+
+namespace dg {
+
+// fp32 inputs on v_mfma_f32_16x16x4_f32, BM x BN tiles (256 x 128 or 128 x 128) on
+// eight waves (schedule 9): a WM x WN grid of wave tiles of (BM / WM) x 64, operands
+// copied straight into S LDS stages of k = 32 (global_load_lds, 16 bytes per lane,
+// 1 KB per instruction). Each wave holds FA = BM / WM / 16 row blocks of A and, per
+// k-step, 64 columns of B as four strided 16-column blocks (row-major B: column
+// 4 l16 + j of the wave tile in block j, one float4 read along n per k-row;
+// column-major B: four contiguous 16-column blocks, a float4 along k each).
+//
+// Iteration lt (stage lt % S): the copies of k-tile lt + S - 1 (into the stage of
+// k-tile lt - 1, whose reads ended before the previous barrier) and the reads of
+// k-tile lt's second half go out between the first half's MFMAs; the second half's
+// MFMAs carry the reads of k-tile lt + 1's first half (published by the previous
+// barrier); then this wave's copies of k-tile lt + 2 must have landed, and a barrier
+// publishes it. With three stages the copies of k-tile lt + 2 are waited for at the
+// end of the iteration that issues them, a whole iteration (128 MFMAs per wave for
+// a 256 x 128 tile) after they went out; with four, one iteration later.
+//
+// LDS layouts are those of the 64 x 64 direct-copy tile: A (and a column-major B)
+// as k-major rows of 32 floats, chunk c of row r at c ^ (r & 7); a row-major B as
+// k-rows of BN floats, unswizzled (the fragment reads of a 16-lane phase cover the
+// 64 banks once: rows are whole multiples of 256 bytes apart). Edge tiles: rows
+// past M (N) copy row M - 1 (N - 1); 16-byte column chunks of a row-major B at or
+// past N (a multiple of 4) copy columns 0 .. 3; neither reaches a stored element.
+template <int OPB, int BM, int BN, int S>
+__global__ __launch_bounds__(512) void mfma32_dcl(GemmArgs g) {
+    constexpr int BK = 32, NW = 8;
+    constexpr int WN = BN / 64, WM = NW / WN, WTM = BM / WM, FA = WTM / 16;
+    static_assert(BN % 64 == 0 && NW % WN == 0 && WTM % 16 == 0 && FA >= 1 && FA <= 4, "wave grid");
+    constexpr int SA = BM * BK, SB = BK * BN;  // floats per stage
+    constexpr int CA = BM / 64, CB = BN / 64;  // 1 KB copies per wave and k-tile
+    constexpr int CPW = CA + CB;
+    constexpr int NR = FA + 4;                 // fragment reads per half k-tile
+    static_assert(S >= 3 && S * (SA + SB) * 4 <= 160 * 1024, "stages");
+    static_assert(2 * CPW <= 16 * FA && NR + 8 <= 16 * FA, "interleave slots");
+    __shared__ __attribute__((aligned(1024))) float sA[S * SA];
+    __shared__ __attribute__((aligned(1024))) float sB[S * SB];
+
+    const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, lg = lane >> 4;
+    const int wm = wave / WN, wn = wave % WN;
+    int tm, tn;
+    tile_coords(g, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const float* __restrict__ A = static_cast<const float*>(g.A);
+    const float* __restrict__ B = static_cast<const float*>(g.B);
+    const int nl = g.K / BK;
+
+    // Copy sources at k-tile 0: wave w copies blocks w CA .. w CA + CA - 1 of A (8 rows
+    // each) and w CB .. w CB + CB - 1 of B.
+    const float* srcA[CA];
+    const float* srcB[CB];
+#pragma unroll
+    for (int i = 0; i < CA; ++i) {
+        const int row = (wave * CA + i) * 8 + (lane >> 3), c = (lane & 7) ^ kmaj_swz(row);
+        srcA[i] = A + (size_t)min(m0 + row, g.M - 1) * g.lda + 4 * c;
+    }
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+        const int b = wave * CB + i;
+        if (OPB == 1) {
+            const int row = b * 8 + (lane >> 3), c = (lane & 7) ^ kmaj_swz(row);
+            srcB[i] = B + (size_t)min(n0 + row, g.N - 1) * g.ldb + 4 * c;
+        } else {
+            // block b: k-rows 4a .. 4a + 3 (a = b % 8) of the 64-column segment b / 8; its
+            // 256-byte window q holds their 64-byte quads q (columns 16 q .. 16 q + 15),
+            // k-row 4a + t at slot t ^ q. Lane L fills window L / 16, slot (L / 4) % 4,
+            // chunk L % 4.
+            const int seg = b >> 3, a = b & 7, q = lane >> 4, t = (lane >> 2) & 3, e = lane & 3;
+            const int krow = 4 * a + (t ^ q), col = n0 + seg * 64 + 16 * q + 4 * e;
+            srcB[i] = B + (size_t)krow * g.ldb + (col < g.N ? col : 0);
+        }
+    }
+    const size_t stepB = OPB == 0 ? (size_t)BK * g.ldb : (size_t)BK;
+    const uint32_t wave_u = (uint32_t)__builtin_amdgcn_readfirstlane(wave);
+    const uint32_t dstA = (uint32_t)reinterpret_cast<uintptr_t>(DG_LDSV(&sA[0])) + wave_u * (CA * 1024u);
+    const uint32_t dstB = (uint32_t)reinterpret_cast<uintptr_t>(DG_LDSV(&sB[0])) + wave_u * (CB * 1024u);
+    // copy q (0 .. CPW - 1) of this wave's share of k-tile lt into stage st
+    auto copy_one = [&](int q, int lt, uint32_t st) {
+        if (q < CA)
+            __builtin_amdgcn_global_load_lds(DG_GLB(srcA[q] + (size_t)lt * BK),
+                                             DG_LDS_AT(dstA + st * (SA * 4u) + q * 1024u), 16, 0, 0);
+        else
+            __builtin_amdgcn_global_load_lds(DG_GLB(srcB[q - CA] + (size_t)lt * stepB),
+                                             DG_LDS_AT(dstB + st * (SB * 4u) + (q - CA) * 1024u), 16, 0, 0);
+    };
+
+    struct Frag {
+        f32x4 a[FA];
+        f32x4 b[4];
+    };
+    const int ra0 = wm * WTM + l16;
+    // read r (0 .. NR - 1) of the fragments of the half k-tile at kk of stage st
+    auto read_one = [&](Frag& f, uint32_t st, int kk, int r) {
+        const float* sa = sA + st * SA;
+        const float* sb = sB + st * SB;
+        if (r < FA) {
+            const int ra = ra0 + 16 * r;
+            f.a[r] = *reinterpret_cast<const f32x4*>(sa + ra * BK + ((((kk >> 2) + lg) ^ kmaj_swz(ra)) << 2));
+        } else if (OPB == 0) {
+            const int kr = kk + 4 * lg + r - FA, q = l16 >> 2;
+            f.b[r - FA] = *reinterpret_cast<const f32x4*>(sb + wn * (BK * 64) + (kr >> 2) * 256 + q * 64 +
+                                                          (((kr & 3) ^ q) << 4) + 4 * (l16 & 3));
+        } else {
+            const int rb = wn * 64 + (r - FA) * 16 + l16;
+            f.b[r - FA] = *reinterpret_cast<const f32x4*>(sb + rb * BK + ((((kk >> 2) + lg) ^ kmaj_swz(rb)) << 2));
+        }
+    };
+    f32x4 acc[FA][4];
+#pragma unroll
+    for (int i = 0; i < FA; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // The 16 FA MFMAs of one half, with the NR reads of another half after the MFMAs
+    // at positions rpos .. rpos + NR - 1 and, with a copy tag, this wave's CPW copies
+    // of k-tile ct into stage cst after MFMAs 1, 3, 5, ...
+    auto mma_mixed = [&](const Frag& f, Frag& nf, uint32_t nst, int nkk, int rpos, bool copy, int ct, uint32_t cst) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int i = 0; i < FA; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int k = (s * FA + i) * 4 + j;
+                    if (OPB == 0)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(f.b[s][j], f.a[i][s], acc[i][j], 0, 0, 0);
+                    else
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(f.b[j][s], f.a[i][s], acc[i][j], 0, 0, 0);
+                    if (k >= rpos && k < rpos + NR) read_one(nf, nst, nkk, k - rpos);
+                    if (copy && (k & 1) && (k >> 1) < CPW) copy_one(k >> 1, ct, cst);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+    };
+    auto settle = [&](Frag& f) {
+#pragma unroll
+        for (int i = 0; i < FA; ++i) asm volatile("" : "+v"(f.a[i]));
+#pragma unroll
+        for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(f.b[s]));
+    };
+
+    // prologue: k-tiles 0 .. S - 2 in flight; k-tiles 0 and 1 complete
+    for (int t = 0; t < S - 1 && t < nl; ++t)
+#pragma unroll
+        for (int q = 0; q < CPW; ++q) copy_one(q, t, (uint32_t)t);
+    vm_wait(CPW * max(0, min(S - 2, nl - 1) - 1));
+    asm volatile("s_barrier" ::: "memory");
+    Frag f0, f1;
+    if (nl > 0)
+#pragma unroll
+        for (int r = 0; r < NR; ++r) read_one(f0, 0, 0, r);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    settle(f0);
+    uint32_t st = 0;  // lt % S
+    // One iteration; COPY: k-tile lt + S - 1 exists and is copied, and the wait then
+    // leaves the copies of k-tiles lt + 3 .. lt + S - 1 in flight.
+    auto iteration = [&](int lt, auto copy_tag) {
+        constexpr bool COPY = decltype(copy_tag)::value;
+        const uint32_t nst = st + 1 == S ? 0 : st + 1;
+        const uint32_t cst = st == 0 ? S - 1 : st - 1;  // (lt + S - 1) % S
+        // first half: the copies of k-tile lt + S - 1 and the second half's fragments
+        mma_mixed(f0, f1, st, 16, 0, COPY, lt + S - 1, cst);
+        // second half: the first half of k-tile lt + 1 (unconditional: after the last
+        // k-tile it reads a stage whose values go unused)
+        mma_mixed(f1, f0, nst, 0, 8, false, 0, 0);
+        if (COPY) vm_wait_n<CPW * (S - 3)>();
+        else vm_wait(CPW * max(0, nl - 1 - (lt + 2)));
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        asm volatile("s_barrier" ::: "memory");
+        settle(f0);
+        st = nst;
+    };
+    constexpr std::true_type yes{};
+    constexpr std::false_type no{};
+    int lt = 0;
+    for (; lt + S - 1 < nl; ++lt) iteration(lt, yes);
+    for (; lt < nl; ++lt) iteration(lt, no);
+
+#pragma unroll
+    for (int i = 0; i < FA; ++i) {
+        const int m = m0 + ra0 + 16 * i;
+        if (m >= g.M) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            if (OPB == 0) {
+                // block j holds wave-tile columns 4 l16 + j: the lane owns 16 consecutive n
+                const int n = n0 + wn * 64 + 16 * lg + 4 * r;
+                store_run4(g, m, n, f32x4{acc[i][0][r], acc[i][1][r], acc[i][2][r], acc[i][3][r]});
+            } else {
+                const int n = n0 + wn * 64 + r * 16 + lg * 4;
+                store_run4(g, m, n, acc[i][r]);
+            }
+        }
+    }
+}
+
+}  // namespace dg

@@ -29,7 +29,10 @@ enum Dtype { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
 //             32x32x16 kernel of schedule 5 with register-staged loads (16-bit inputs,
 //             bases aligned to the element, any M, K >= 8, N >= 8 for row-major B),
 //             8 = fp32 64 x 64 tiles with direct copies three k-tiles ahead (16-byte
-//             aligned operands, K a multiple of 64, N a multiple of 4 for row-major B)
+//             aligned operands, K a multiple of 64, N a multiple of 4 for row-major B),
+//             9 = fp32 256 x 128 and 128 x 128 tiles on eight waves with direct copies
+//             two (three LDS stages) or three (four) k-tiles ahead (16-byte aligned
+//             operands, K a multiple of 32, N a multiple of 4 for row-major B)
 struct MenuEntry {
     int id, variant, dtype, opb, vec, bm, bn, bk, wm, wn, tm, tn, threads, lds_bytes, sched;
 };
@@ -43,7 +46,9 @@ constexpr bool schedule_enabled(int sched) { return sched != 3; }
 // Schedules whose kernels copy tiles straight into LDS: the operands must be 16-byte
 // aligned and K whole k-tiles (schedule 5: K a multiple of 8, a partial last k-tile
 // zeroed past K); edge tiles in M and N copy clamped rows and columns.
-constexpr bool direct_copy(int sched) { return sched == 2 || sched == 4 || sched == 5 || sched == 8; }
+constexpr bool direct_copy(int sched) {
+    return sched == 2 || sched == 4 || sched == 5 || sched == 8 || sched == 9;
+}
 
 // Configurations with a persistent single-problem form (a grid below the tile count,
 // each workgroup striding through the tiles): the 8-wave software-pipelined
@@ -169,6 +174,15 @@ constexpr bool grouped_capable(int variant, int sched, int bm, int bn, int wm, i
     X(base + 0, V_MFMA, DT_F32, 0, 1, 64, 64, 32, 4, 1, 0, 0, 512, 2 * 4 * 2 * 8192, 8)        \
     X(base + 1, V_MFMA, DT_F32, 1, 1, 64, 64, 32, 4, 1, 0, 0, 512, 2 * 4 * 2 * 8192, 8)
 
+// fp32 tiles with direct copies on eight waves (schedule 9): 256 x 128 (4 x 2 waves of
+// 64 x 64, three LDS stages of 48 KB) and 128 x 128 (4 x 2 waves of 32 x 64, four
+// stages of 32 KB).
+#define DG_MFMA_F32DCL(X, base)                                                          \
+    X(base + 0, V_MFMA, DT_F32, 0, 1, 256, 128, 32, 4, 2, 0, 0, 512, 3 * 4 * 32 * 384, 9)     \
+    X(base + 1, V_MFMA, DT_F32, 1, 1, 256, 128, 32, 4, 2, 0, 0, 512, 3 * 4 * 32 * 384, 9)     \
+    X(base + 2, V_MFMA, DT_F32, 0, 1, 128, 128, 32, 4, 2, 0, 0, 512, 5 * 4 * 32 * 256, 9)     \
+    X(base + 3, V_MFMA, DT_F32, 1, 1, 128, 128, 32, 4, 2, 0, 0, 512, 5 * 4 * 32 * 256, 9)
+
 #define DG_MENU(X)                                              \
     DG_LDS_ENTRIES(X, 0, DT_F32, 16)            \
     DG_LDS_ENTRIES(X, 8, DT_F16, 32)            \
@@ -189,9 +203,10 @@ constexpr bool grouped_capable(int variant, int sched, int bm, int bn, int wm, i
     DG_MFMA_SPR(X, 90, DT_F16)                                   \
     DG_MFMA_SPR(X, 94, DT_BF16)                                  \
     DG_MFMA_F32SMALL(X, 98)                                      \
-    DG_MFMA_F32DC(X, 104)
+    DG_MFMA_F32DC(X, 104)                                        \
+    DG_MFMA_F32DCL(X, 106)
 
-constexpr int kMenuSize = 106;
+constexpr int kMenuSize = 110;
 
 // Fused epilogue ("Shared memory and tensor cores", section 13.10: bias,
 // activation, residual add or type cast applied to the accumulator before the

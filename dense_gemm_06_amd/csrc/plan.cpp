@@ -260,7 +260,7 @@ static int plan_uncached(int opA, int opB, int64_t M, int64_t N, int64_t K, int6
             set_error("max_grid = %d must be non-negative", want_grid);
             return GEMM_ERR_INVALID_VALUE;
         }
-        if (want_sched < 0 || want_sched > 8 || want_wm < 0 || want_wn < 0 || want_variant < 0 || want_variant > 2 || want_vec < -1 || want_vec > 1 || want_remap < -1 ||
+        if (want_sched < 0 || want_sched > 9 || want_wm < 0 || want_wn < 0 || want_variant < 0 || want_variant > 2 || want_vec < -1 || want_vec > 1 || want_remap < -1 ||
             want_remap > 1 || want_group < 0 || want_bm < 0 || want_bn < 0) {
             set_error("invalid requested configuration (variant %d, bm %d, bn %d, vec %d, xcd_remap %d, group_m %d)",
                       want_variant, want_bm, want_bn, want_vec, want_remap, want_group);
@@ -322,7 +322,7 @@ static int plan_uncached(int opA, int opB, int64_t M, int64_t N, int64_t K, int6
         if (direct_copy(e.sched) && (Kx == 0 || (Kx % e.bk != 0 && !(e.sched == 5 && Kx % 8 == 0)))) continue;
         if (direct_copy(e.sched) && (Mx % e.bm != 0 || Nx % e.bn != 0) &&
             !((e.sched == 5 || e.sched == 2 || e.sched == 4) && (e.opb == 1 || Nx % 8 == 0)) &&
-            !(e.sched == 8 && (e.opb == 1 || Nx % 4 == 0)))
+            !((e.sched == 8 || e.sched == 9) && (e.opb == 1 || Nx % 4 == 0)))
             continue;
         // the fp32 direct-copy tile: K in whole k-tiles for each of its two K groups
         if (e.sched == 8 && Kx % 64 != 0) continue;
@@ -425,21 +425,47 @@ static int plan_uncached(int opA, int opB, int64_t M, int64_t N, int64_t K, int6
             // against 149.7)
             if (e.dtype == DT_F32 && e.sched == 6 && e.bm < 256) eff = rounds == 1 ? 0.50 : 0.40;
             // (the fp32 64 x 64 direct-copy tile, schedule 8, is costed below)
+            // the fp32 128 x 128 register-staged tile is costed for two resident per CU,
+            // each hiding the other's copies and store; alone on a CU it measured 12%
+            // slower (2048^3 153.9 us, 1024 x 4096 x 4096 298.6: 256 tiles, one round)
+            if (e.dtype == DT_F32 && e.sched == 1 && e.bm == 128 && e.threads == 256 &&
+                std::min<int64_t>(occ, ((grid_e < tiles ? grid_e : work) + num_cus - 1) / num_cus) < 2)
+                eff *= 0.88;
             const double tile_cycles = 2.0 * e.bm * e.bn * std::max<int64_t>(kpad, e.bk) / (rate_per_cu(e) * eff);
             double cost = (double)rounds * (double)std::max<int64_t>(resident, 1) * tile_cycles;
             if (e.dtype == DT_F32 && e.variant == V_MFMA && e.sched != 8)
                 cost += (double)rounds * fp32_round_overhead(e, std::max<int64_t>(resident, 1));
             // The direct-copy tile's time, fitted per round of its tiles (one resident per
             // CU) from 1024^3 21.2 us (one round), 1536^3 86.3 (three), 2048^3 147.7
-            // (four), 2560^3 316.8 (seven) and 1024^2 x 256 8.7: about 4.5 us per round
-            // (the launch's share, the first copies, the K-group reduction and the
-            // store) and 15.8 us per 1024 of K, in the model's cycles (2400 per us). It
+            // (four), 2560^3 315 (seven), 3072^3 490 (nine) and 1024 x 4096 x 4096 285.6
+            // (four): about 3.0 us per round (the launch's share, the first copies, the
+            // K-group reduction and the store) and 16.7 us per 1024 of K, in the model's
+            // cycles (2900 per us). It
             // loses to larger tiles once the rounds pile up their fixed cost (4096^3 1113
             // us against 1026 for the 256 x 128 tile, 6144^2 x 512 403 against 323 for
             // 128 x 128 tiles, 8192^2 x 1024 1568 against 1066): not past nine rounds.
             if (e.sched == 8) {
                 if (rounds > 9) continue;
-                cost = (double)rounds * (10800.0 + 37.0 * (double)kpad);
+                cost = (double)rounds * (8700.0 + 47.3 * (double)kpad);
+            }
+            // The large direct-copy tiles (schedule 9), fitted the same way over 24 shapes
+            // of 256 to 12288 (medians of five alternated passes, one box): per round of
+            // tiles a fixed time plus a time per k, in us: 256 x 128 with row-major B 12.1
+            // + 0.1192 K, column-major B 8.8 + 0.1227 K; 128 x 128 (one resident per CU)
+            // 9.3 + 0.0608 K and 5.9 + 0.059 K, and 7.5% more for a single round. Against
+            // the three-stage tile's 14.3 + 0.1212 K (8.4 + 0.1215 K) this makes the
+            // 256 x 128 tile the faster for row-major B and the 128 x 128 tile for
+            // column-major B once K is long (4096^3 1013 and 989 us against 1032 and
+            // 1017; 8192^3 7911 and 7803 against 8057 and 8029), and the 128 x 128 tile
+            // for one round of long K (2048^3 143 and 137 against 148 and 144 for 64 x
+            // 64 tiles; 1024 x 4096 x 4096 278 and 266 against 281 and 277), while two
+            // resident 128 x 128 register-staged tiles keep short K (8192^2 x 256 306
+            // against 347). The model's cycles: 2900 per us.
+            if (e.sched == 9) {
+                const bool wide = e.bm == 256;
+                const double a = wide ? (e.opb == 0 ? 12.1 : 8.8) : (e.opb == 0 ? 9.3 : 5.9);
+                const double b = wide ? (e.opb == 0 ? 0.1192 : 0.1227) : (e.opb == 0 ? 0.0608 : 0.059);
+                cost = (double)rounds * (a + b * (double)kpad) * 2900.0 * (rounds == 1 && !wide ? 1.075 : 1.0);
             }
             // the reduction reads every plane and writes C, and is a second launch;
             // measured at 256^3 and 1024^3 fp32, a split costs about 16000 cycles

@@ -73,7 +73,7 @@ static void random_request(gemm_config* r) {
     r->waves_m = (int32_t)(coin(70) ? 0 : pick(-1, 5));
     r->waves_n = (int32_t)(coin(70) ? 0 : pick(-1, 5));
     r->threads = (int32_t)(coin(70) ? 0 : pick(-1, 3) * 256);
-    r->schedule = (int32_t)(coin(60) ? 0 : pick(-1, 7));
+    r->schedule = (int32_t)(coin(60) ? 0 : pick(-1, 10));
     r->split_k = (int32_t)(coin(60) ? 0 : pick(-1, 20));
     r->pack = (int32_t)(coin(60) ? 0 : pick(-1, 3));
     r->max_grid = (int32_t)(coin(70) ? 0 : pick(-1, 600));
@@ -122,7 +122,7 @@ static void check_plan(int opB, int64_t M, int64_t N, int64_t K, int64_t lda, in
         if (e.sched != 5) CHECK(K % e.bk == 0, "schedule %d with K = %lld", e.sched, (long long)K);
         if (e.sched == 8) CHECK(K % 64 == 0, "schedule 8 with K = %lld", (long long)K);
         if (opB == 0)
-            CHECK(N % e.bn == 0 || N % (e.sched == 8 ? 4 : 8) == 0, "row-major B edge tile with N = %lld",
+            CHECK(N % e.bn == 0 || N % (e.sched == 8 || e.sched == 9 ? 4 : 8) == 0, "row-major B edge tile with N = %lld",
                   (long long)N);
     }
     if (e.sched == 7) {

@@ -52,7 +52,7 @@ def test_status_strings():
 
 def test_menu_is_complete():
     menu = dg.gemm_menu()
-    assert len(menu) == dg.library().gemm_menu_size() == 106
+    assert len(menu) == dg.library().gemm_menu_size() == 110
     seen = set()
     for e in menu:
         assert e["lds_bytes"] <= 160 * 1024
@@ -72,7 +72,7 @@ def test_menu_is_complete():
                 for vec in (0, 1):
                     tiles = {(bm, bn) for (v, d, o, ve, bm, bn) in seen if (v, d, o, ve) == (variant, dtype, opb, vec)}
                     assert len(tiles) >= 2, (variant, dtype, opb, vec)
-    assert dg.library().gemm_menu_entry(106, None, None, None, None) == dg.GEMM_ERR_INVALID_VALUE
+    assert dg.library().gemm_menu_entry(110, None, None, None, None) == dg.GEMM_ERR_INVALID_VALUE
 
 
 def plan(M, N, K, dtype="f32", op_b="N", lda=None, ldb=None, ldc=None, a=0, b=0, c=0, cus=256, arch="gfx950",
@@ -168,20 +168,21 @@ def test_plan_software_pipelined_edge_tiles():
 
 
 def test_plan_three_stage_fp32():
-    """Schedule 6 (fp32 256 x 128, three LDS stages) where the grid fills the machine,
-    either B layout, ragged shapes included, and its 64 x 64 form for one round of
-    tiles; never for 16-bit inputs, never split."""
+    """Schedule 6 (fp32 256 x 128, three LDS stages) where the grid fills the machine
+    and the direct-copy tiles do not apply (K not a multiple of 32, or rows not 16-byte
+    aligned), either B layout, and its 64 x 64 form for one round of tiles; never for
+    16-bit inputs, never split."""
     for op_b in "NT":
-        for shape in ((4096, 4096, 4096), (8192, 8192, 8192), (4000, 4096, 3001)):
-            st, c = plan(*shape, "f32", op_b)
+        for shape, lda in (((4000, 4096, 3001), None), ((4096, 4096, 4096), 4097), ((8192, 8192, 8192), 8194)):
+            st, c = plan(*shape, "f32", op_b, lda=lda)
             assert st == 0 and c.schedule == 6 and (c.bm, c.bn) == (256, 128) and c.threads == 512, (shape, op_b)
     # one round of 64 x 64 tiles on unaligned rows: the same schedule with two K
     # groups on that tile
     st, c = plan(1024, 1024, 1024, "f32", lda=1025)
     assert st == 0 and c.schedule == 6 and (c.bm, c.bn) == (64, 64)
-    # short K: the three-stage tile's fixed cost per round of tiles outweighs its faster
+    # short K: the large tiles' fixed cost per round of tiles outweighs their faster
     # k loop; two resident 128 x 128 register-staged tiles per CU
-    for shape in ((8192, 8192, 256), (8192, 8192, 512), (4096, 4096, 1024)):
+    for shape in ((8192, 8192, 256), (8192, 8192, 512), (12288, 12288, 512)):
         st, c = plan(*shape, "f32")
         assert st == 0 and c.schedule == 1 and (c.bm, c.bn) == (128, 128), shape
     st, c = wplan(512, 512, 8192, "f32")
@@ -303,12 +304,17 @@ def test_plan_cache_returns_the_uncached_plan():
 def test_plan_fp32_choices_follow_measurements():
     """fp32 tile choices on shapes where each kernel was timed against the others on
     the device (the fastest of the alternatives in medians of five alternated passes):
-    the direct-copy 64 x 64 tile for one to a few rounds of its tiles, 128 x 128 tiles
-    or the 256 x 128 three-stage tile once its rounds pile up, 16 x 64 tiles for few
-    tiles."""
+    the direct-copy 64 x 64 tile for one to a few rounds of its tiles, the large
+    direct-copy tiles for long K (256 x 128 with row-major B, 128 x 128 with
+    column-major B or for a single round), two resident 128 x 128 register-staged
+    tiles for short K, 16 x 64 tiles for few tiles."""
     cases = {(1536, 1536, 1536, "N"): 8, (2560, 2560, 2560, "N"): 8, (3072, 3072, 1024, "T"): 8,
-             (1024, 4096, 4096, "N"): 8, (2048, 2048, 2048, "N"): 8, (768, 768, 1024, "N"): 8,
-             (4096, 4096, 4096, "N"): 6, (6144, 6144, 512, "N"): (1, 128), (8192, 8192, 1024, "N"): (1, 128),
+             (3072, 3072, 3072, "T"): 8, (768, 768, 1024, "N"): 8,
+             (1024, 4096, 4096, "N"): (9, 128), (1024, 4096, 4096, "T"): (9, 128), (2048, 2048, 2048, "N"): (9, 128),
+             (2048, 2048, 2048, "T"): (9, 128), (4096, 4096, 4096, "N"): (9, 256), (4096, 4096, 4096, "T"): (9, 128),
+             (8192, 8192, 8192, "N"): (9, 256), (8192, 8192, 8192, "T"): (9, 128), (4096, 8192, 2048, "N"): (9, 256),
+             (4096, 8192, 2048, "T"): (9, 128), (8192, 8192, 1024, "T"): (9, 128),
+             (6144, 6144, 512, "N"): (1, 128), (8192, 8192, 256, "T"): (1, 128), (12288, 12288, 512, "N"): (1, 128),
              (512, 512, 512, "N"): (1, 16), (256, 256, 16384, "N"): (1, 16)}
     for (M, N, K, op_b), want in cases.items():
         st, c = plan(M, N, K, "f32", op_b)

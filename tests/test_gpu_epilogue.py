@@ -203,6 +203,17 @@ def test_epilogue_f32_direct_copy(op_b, out):
     assert epilogue_error(got, ref, Dp, "f32", out) <= 1.0
 
 
+@pytest.mark.parametrize("bm", [256, 128])
+@pytest.mark.parametrize("op_b", ["N", "T"])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_epilogue_f32_large_direct_copy(bm, op_b, out):
+    """The fp32 large direct-copy tiles (schedule 9) with a fused epilogue on edge tiles."""
+    ops = gi.make_operands(300, 264 if op_b == "N" else 263, 160, "f32", "normal", seed=17, op_b=op_b)
+    got, ref, Dp, plan = run_epi(ops, out, act="gelu_tanh", cfg=dg.request(schedule=9, bm=bm))
+    assert plan.schedule == 9 and plan.bm == bm
+    assert epilogue_error(got, ref, Dp, "f32", out) <= 1.0
+
+
 @pytest.mark.parametrize("op_b", ["N", "T"])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_epilogue_three_stage_fp32(op_b, out):

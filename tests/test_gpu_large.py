@@ -97,8 +97,15 @@ def test_whole_tile_kernel_a_beyond_2_31_elements():
 
 
 def test_three_stage_fp32_a_beyond_2_31_elements():
-    """The fp32 three-stage tile: 2^20 + 100 rows of 2048 (2.1e9 elements of A)."""
-    check_large_a((1 << 20) + 100, 256, 2048, "f32", 2048, seed=33, expect_schedule=6)
+    """The fp32 three-stage tile (requested): 2^20 + 100 rows of 2048 (2.1e9 elements of A)."""
+    check_large_a((1 << 20) + 100, 256, 2048, "f32", 2048, seed=33, expect_schedule=6,
+                  req=dg.request(schedule=6))
+
+
+def test_large_direct_copy_fp32_a_beyond_2_31_elements():
+    """The fp32 256 x 128 direct-copy tile, the heuristic's choice here: 2^20 + 100
+    rows of 2048 (2.1e9 elements of A), copy sources past 2^31 elements."""
+    check_large_a((1 << 20) + 100, 256, 2048, "f32", 2048, seed=34, expect_schedule=9)
 
 
 @pytest.mark.parametrize("dtype,op_b", [("f16", "N"), ("f32", "T")])

@@ -35,7 +35,7 @@ def _lib_built():
 MENU = _menu()
 MENU_IDS = [f"k{e['kernel_id']}-{'lds' if e['variant'] == 1 else 'mfma'}-{DT_NAME[e['dtype']]}-"
             f"op{'NT'[e['opb']]}-{'v16' if e['vec'] else 'v1'}-{e['bm']}x{e['bn']}-w{e['waves_m']}x{e['waves_n']}"
-            f"{ {1: '', 2: '-pp', 4: '-pp32', 5: '-sp', 6: '-s3', 7: '-spr', 8: '-dc'}[e['schedule']] }"
+            f"{ {1: '', 2: '-pp', 4: '-pp32', 5: '-sp', 6: '-s3', 7: '-spr', 8: '-dc', 9: '-dcl'}[e['schedule']] }"
             for e in MENU]
 
 
@@ -64,11 +64,11 @@ def ragged_shape(e):
     The direct-copy kernels (schedules 2, 4 and 5) get whole tiles here: 2 x 3 tiles
     and 9 k-tiles (an odd count, so both LDS-stage parities and the prefetch tail are
     exercised); their edge tiles and partial k-tiles have cases of their own below.
-    The fp32 direct-copy tile (schedule 8) gets ragged M and N and ten k-tiles (five
+    The fp32 direct-copy tiles get ragged M and N and ten k-tiles (schedule 8: five
     per K group)."""
     if e["schedule"] in WHOLE_TILE:
         return 2 * e["bm"], 3 * e["bn"], 9 * e["bk"]
-    if e["schedule"] == 8:  # ragged M and N (a multiple of 4 for row-major B); K a multiple of 64
+    if e["schedule"] in (8, 9):  # ragged M and N (a multiple of 4 for row-major B); K in whole k-tiles
         return 2 * e["bm"] + 37, 2 * e["bn"] + (20 if e["opb"] == 0 else 19), 10 * e["bk"]
     return 2 * e["bm"] + 37, 2 * e["bn"] + 19, 3 * e["bk"] + 13
 
@@ -251,6 +251,51 @@ def test_f32_direct_copy_integer_exact(shape, op_b):
     check_untouched(C, M, N)
     Cref, _ = oracle.gemm_ref(ops, want_d=False)
     assert np.array_equal(C[:M, :N].astype(np.float64), Cref)
+
+
+@pytest.mark.parametrize("bm", [256, 128])
+@pytest.mark.parametrize("k_tiles", [1, 2, 3, 4, 5, 6, 9, 130])
+@pytest.mark.parametrize("op_b", ["N", "T"])
+def test_f32_large_direct_copy_k_tile_counts(bm, k_tiles, op_b):
+    """Schedule 9 (fp32 256 x 128 on three LDS stages, 128 x 128 on four, direct
+    copies) for every small k-tile count (the prologue issues two or three, so the
+    shortest never enter the steady state) and a long K, on ragged M and N spanning
+    several tiles."""
+    K = 32 * k_tiles
+    M, N = 2 * bm + 77, (300 if op_b == "N" else 301)
+    ops = gi.make_operands(M, N, K, "f32", "normal", seed=k_tiles + bm, op_b=op_b)
+    print(f"case fp32 large direct copy {bm}x128 K={K} op {op_b}", flush=True)
+    C = run_ops(ops, cfg=dg.request(schedule=9, bm=bm), ldc=N + 4)
+    check_untouched(C, ops.M, ops.N)
+    Cref, D = oracle.gemm_ref(ops)
+    assert normalized_error(C[:ops.M, :ops.N], Cref, D) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("bm", [256, 128])
+@pytest.mark.parametrize("shape,op_b", [((1024, 1024, 1024), "N"), ((1024, 1024, 1024), "T"), ((65, 4, 64), "N"),
+                                        ((100, 1, 128), "T"), ((1000, 1000, 192), "N"), ((257, 129, 96), "T")])
+def test_f32_large_direct_copy_integer_exact(bm, shape, op_b):
+    """Integer data through schedule 9, edge tiles included: bit-exact."""
+    M, N, K = shape
+    i = np.arange(M)[:, None]
+    k = np.arange(K)[None, :]
+    a = (((7 * i + 3 * k) % 7) - 3).astype(np.float32)
+    b = (((5 * np.arange(K)[:, None] + 2 * np.arange(N)[None, :] + 1) % 7) - 3).astype(np.float32)
+    ops = gi.from_values(a, b, "f32", op_b)
+    print(f"case fp32 large direct copy integer {bm}x128 {shape} op {op_b}", flush=True)
+    C = run_ops(ops, cfg=dg.request(schedule=9, bm=bm), ldc=N + 1)
+    check_untouched(C, M, N)
+    Cref, _ = oracle.gemm_ref(ops, want_d=False)
+    assert np.array_equal(C[:M, :N].astype(np.float64), Cref)
+
+
+def test_f32_large_direct_copy_refusals():
+    """Schedule 9 needs K a multiple of 32, 16-byte aligned operands and, for a
+    row-major B, N a multiple of 4: other problems are refused when it is forced."""
+    for (M, N, K, op_b, lda) in ((128, 128, 80, "N", 80), (128, 130, 128, "N", 128), (128, 128, 128, "N", 130)):
+        st, _ = dg.gemm_plan(0, dg.OP_CODE[op_b], M, N, K, lda, N, N, dg.GEMM_F32, 0, 0, 1 << 40, 256, "gfx950",
+                             dg.request(schedule=9), check=False)
+        assert st == dg.GEMM_ERR_UNSUPPORTED
 
 
 def test_f32_direct_copy_refusals():
