@@ -105,7 +105,11 @@ typedef struct gemm_config {
                           B or N >= 8 for row-major B); 8 fp32 64 x 64 tiles with direct
                           global->LDS copies three k-tiles ahead, K over two wave groups
                           (16-byte aligned operands, any M, K a multiple of 64, any N for
-                          column-major B or N a multiple of 4 for row-major B, K not split) */
+                          column-major B or N a multiple of 4 for row-major B, K not split);
+                          9 fp32 256 x 128 (three LDS stages) or 128 x 128 (five) tiles on
+                          eight waves with direct global->LDS copies (16-byte aligned
+                          operands, any M, K a multiple of 32, any N for column-major B or N
+                          a multiple of 4 for row-major B, K not split) */
     int64_t tiles_m, tiles_n; /* out (grouped: of the first non-empty problem) */
     double est_cycles; /* out: the heuristic's cost estimate (clock cycles) */
     int64_t tiles_total; /* out: output tiles of the call (grouped: of all its problems) */
