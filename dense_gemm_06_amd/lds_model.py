@@ -82,10 +82,13 @@ def gfx950_passes(byte_addr_of_lane: Callable[[int], int], width: int) -> int:
 # direct-copy kernel's row-major B fragment reads, conflict-free 16-byte reads of
 # four k-rows per phase, took 1264-1277 us at 4096^3 with every phase in one window,
 # 1187-1196 with two windows of eight lanes and 1017 with four lanes in each window.
-# (The 8-byte transpose reads of the 16-bit kernels, two windows per 32-lane phase,
-# measured the same with four: 116.3 against 116.0 us at 4096^3.) The measure below
-# is the worst phase's load of its busiest window relative to an even spread: 1 = a
-# quarter of the phase in each window, 2 = two windows, 4 = one window.
+# It is not a general law: the 8-byte transpose reads of the 16-bit kernels (two
+# windows per 32-lane phase) measured the same with four (116.3 against 116.0 us at
+# 4096^3), and the fp32 64 x 64 direct-copy tile, whose wave tiles hold one row block,
+# measured 0-5% slower with the four-window layout (1024^3 22.1 against 21.3 us), so
+# each layout is kept where it measured faster. The measure below is the worst phase's
+# load of its busiest window relative to an even spread: 1 = a quarter of the phase in
+# each window, 2 = two windows, 4 = one window.
 def gfx950_window_load(byte_addr_of_lane: Callable[[int], int], width: int) -> int:
     if width == 16:
         groups: dict = {}
