@@ -774,9 +774,14 @@ __device__ __forceinline__ void mfma32_sp_body(GemmArgs& g, const GroupArgs* ga)
     }
 }
 
+// One tile per workgroup (grid x), or the persistent form. A split-K launch of the
+// one-tile form (grid y = slices; not the persistent form) narrows A, B, K and C to
+// the slice first: the slice's partial product goes to its workspace plane as plain
+// fp32, and the fixed-order reduction applies any epilogue.
 template <int DT, int OPB, int NW, bool REG, bool PERSIST = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void mfma32_sp(
     GemmArgs g) {
+    if constexpr (!PERSIST) k_slice<2, OPB>(g);
     mfma32_sp_body<DT, OPB, NW, REG, PERSIST, false>(g, nullptr);
 }
 

@@ -177,6 +177,50 @@ static double fp32_round_overhead(const MenuEntry& e, int64_t resident) {
     const double c_bytes = 4.0 * e.bm * e.bn * (double)resident;
     return c_bytes * (resident >= 2 ? 0.134 : 0.29);
 }
+// Time model of the 16-bit MFMA tile families on 16-byte loads (fitted, in us, to
+// 1290 medians of five alternated passes over 26 shapes of 512 to 8192 and 120 more
+// between 512^2 x 256 and 8192^2 x 16384, both B layouts, one box, splits included;
+// median error 1.6-6.8% per family): the larger of a per-CU bound, rounds of
+// tiles of `resident` tiles each at a per-CU rate min(resident r1, rcap) TFLOP/s
+// plus a fixed a per round, and a chip bound c + 2MNK / R (the board's power limit:
+// a problem that keeps every CU busy runs at R TFLOP/s whatever its tile). The
+// per-CU bound is what makes few tiles of long K slow, and R what makes the largest
+// tiles win once the machine is full.
+struct Fit16 {
+    double a, r1, rcap, c, R;
+};
+static const Fit16* fit16(const MenuEntry& e) {
+    static const Fit16 rs64{3.25, 1.12, 2.90, 4.52, 537.4}, rs128{5.97, 2.77, 4.00, 4.46, 834.0},
+        rs256{14.79, 5.18, 5.18, 6.12, 900.4}, wide{15.34, 4.16, 4.16, 7.10, 802.7},
+        pp16{14.61, 6.84, 6.84, 6.34, 1065.8}, pp32{16.96, 6.39, 6.39, 5.09, 927.8},
+        sp4{17.35, 8.72, 8.72, 11.69, 1086.0}, sp8{13.36, 9.23, 9.23, 8.18, 1108.1},
+        spr8{14.69, 7.65, 7.65, 11.31, 1011.2};
+    if (e.variant != V_MFMA || e.dtype == DT_F32 || !e.vec) return nullptr;
+    switch (e.sched) {
+        case 1:
+            if (e.bm == 64 && e.bn == 64 && e.threads == 256) return &rs64;
+            if (e.bm == 128 && e.bn == 128 && e.threads == 256) return &rs128;
+            if (e.bm == 256 && e.bn == 256) return e.threads == 512 ? &rs256 : &wide;
+            return nullptr;
+        case 2: return &pp16;
+        case 4: return &pp32;
+        case 5: return e.threads == 512 ? &sp8 : &sp4;
+        case 7: return e.threads == 512 ? &spr8 : &sp4;  // the 4-wave form: sp4, 10% slower
+        default: return nullptr;
+    }
+}
+// kslow stretches the k loop only (slower loads), not the fixed costs.
+static double fit16_us(const Fit16& f, const MenuEntry& e, int64_t rounds, int64_t resident, int64_t kt,
+                       double flops, double kslow) {
+    const double w = 2.0 * e.bm * e.bn * e.bk / 1e6;  // MFLOP per k-tile of one tile
+    const double rate = std::min((double)resident * f.r1, f.rcap);
+    const double per_cu = (double)rounds * (f.a + kslow * (double)kt * (double)resident * w / rate);
+    return std::max(per_cu, f.c + kslow * flops / (f.R * 1e6));
+}
+// The 16-bit model's cycles per us (the software-pipelined 4096^3 kernel's cost
+// against its time), to set fitted times beside the families the fit does not cover.
+constexpr double kCycles16PerUs = 1141.0;
+
 static int blocks_per_cu(const MenuEntry& e) {
     const int by_lds = (160 * 1024) / e.lds_bytes;
     const int by_waves = 32 / (e.threads / 64);  // 8 waves per SIMD x 4 SIMDs
@@ -367,11 +411,16 @@ static int plan_uncached(int opA, int opB, int64_t M, int64_t N, int64_t K, int6
             if ((want_split == 1 || packed) && S != 1) continue;
             int64_t slices = 1, chunk = Kx;
             if (S > 1) {
-                if (e.sched != 1 || ktiles < 2) continue;
+                // the register-staged kernels and the one-tile form of the
+                // software-pipelined kernels take K slices of whole k-tiles
+                if ((e.sched != 1 && e.sched != 5 && e.sched != 7) || ktiles < 2) continue;
                 const int64_t chunk_tiles = (ktiles + S - 1) / S;
                 slices = (ktiles + chunk_tiles - 1) / chunk_tiles;
                 chunk = chunk_tiles * e.bk;
                 if (slices < 2) continue;
+                // the register-staged software-pipelined kernel reads 16-byte chunks inside
+                // its slice: the last slice holds at least 8 k
+                if (e.sched == 7 && Kx - (slices - 1) * chunk < 8) continue;
                 const int64_t need = split_workspace(slices, M, N);
                 if (need > ws_bytes) {
                     if (want_split >= 2) short_ws = std::max(short_ws, need);
@@ -413,9 +462,12 @@ static int plan_uncached(int opA, int opB, int64_t M, int64_t N, int64_t K, int6
             // 4 waves; 8192^2 x 1037 bf16 193.2 against 183.3 packed.
             double eff = tile_efficiency(e, packed || dma_ok);
             if (e.sched == 5 || e.sched == 7) {
+                // k-tiles of one workgroup's work (a slice when K is split; the slices'
+                // partial products are plain stores, the reduction applies the epilogue)
+                const int64_t kt_unit = (std::min<int64_t>(chunk, Kx) + e.bk - 1) / e.bk;
                 const bool eight = e.wm * e.wn == 8;
-                if (fused_epilogue) eff = eight && ktiles >= 32 ? 0.99 : 0.90;
-                else eff = !eight ? 0.90 : (tiles <= num_cus && ktiles <= 32) ? 0.96 : 0.99;
+                if (fused_epilogue && slices == 1) eff = eight && ktiles >= 32 ? 0.99 : 0.90;
+                else eff = !eight ? 0.90 : (work <= num_cus && kt_unit <= 32) ? 0.96 : 0.99;
                 if (e.sched == 7) eff *= 0.9;
             }
             // the fp32 64 x 64 tile with two K groups on the three-stage schedule:
@@ -467,12 +519,60 @@ static int plan_uncached(int opA, int opB, int64_t M, int64_t N, int64_t K, int6
                 const double b = wide ? (e.opb == 0 ? 0.1192 : 0.1227) : (e.opb == 0 ? 0.0608 : 0.059);
                 cost = (double)rounds * (a + b * (double)kpad) * 2900.0 * (rounds == 1 && !wide ? 1.075 : 1.0);
             }
-            // the reduction reads every plane and writes C, and is a second launch;
-            // measured at 256^3 and 1024^3 fp32, a split costs about 16000 cycles
-            // beyond its traffic (about 1 KB per clock for a kernel of this size),
-            // so it pays only when few tiles face a long K
-            if (slices > 1) cost += (double)(slices + 1) * (double)M * (double)N * 4.0 / 1024.0 + 16000.0;
-            if (packed) cost += pack_cycles;
+            // 16-bit families with a fitted time: the persistent grid measured 2-12%
+            // faster than one workgroup per tile over several rounds (0.94 on average),
+            // a split adds its reduction (every plane read and C written: 5.5 TB/s
+            // fitted on 434 split runs, and 4 us for the second launch, which small
+            // problems measured: 768^2 x 512 split four ways 12.1 us against 5.9),
+            // packing its copy (3.5 TB/s, plus 3 us for its launch);
+            // 16-byte loads from rows that are not 16-byte aligned cost the
+            // register-staged kernels 1.8x in the k loop (the load factor above)
+            const Fit16* f16 = fit16(e);
+            if (f16) {
+                const int64_t kt_unit = (std::min<int64_t>(chunk, Kx) + e.bk - 1) / e.bk;
+                const double kslow = e.sched == 1 && !(packed || dma_ok) ? 1.0 / 0.55 : 1.0;
+                double t = fit16_us(*f16, e, rounds, std::max<int64_t>(resident, 1), kt_unit,
+                                    2.0 * (double)Mx * (double)Nx * (double)Kx, kslow);
+                if (e.sched == 7 && e.threads != 512) t *= 1.1;
+                // where the direct-copy kernels can take the problem (16-byte aligned
+                // operands, K a multiple of 8, row-major B with N a multiple of 8), the
+                // register-staged software-pipelined form measured about 10% slower
+                // than they do (4096^2 x 256 fp16: 21.7 us against 19.4 on the ping-pong
+                // kernel)
+                if (e.sched == 7 && (packed || dma_ok) && Kx % 8 == 0 && (e.opb == 1 || Nx % 8 == 0)) t *= 1.15;
+                // the ping-pong kernel against the 8-wave software-pipelined one, beyond
+                // what the fit resolves: past 32 k-tiles 3-16% slower with row-major B
+                // (4096^2 x 2048 fp16 70.6 us against 67.3, bf16 67.3 against 62.5;
+                // 3072 x 4096 x 2048 62.8 against 53.6), 1% faster with column-major B
+                // (67.7 against 68.5); for one full round of at most 32 k-tiles 3-5%
+                // faster (4096^2 x 512 fp16 25.8 against 27.0, bf16 25.0 against 26.0;
+                // 4096^2 x 1024 39 against 40, bf16 37 against 39); with a fused
+                // epilogue the 8-wave kernel is the faster from 32 k-tiles on (4096^2 x
+                // 1024, bias, GELU and bf16 out: 53.0 against 54.7)
+                if (e.sched == 2) {
+                    const bool one_round = rounds == 1 && work * 10 >= (int64_t)num_cus * 9;
+                    // (with an epilogue below 32 k-tiles the ping-pong kernel measured
+                    // 2-3% faster, 8192^2 x 256 124.4 against 127.2 and 8192^2 x 512
+                    // column-major B 150.6 against 155.2, where the fit puts it 10-15%
+                    // behind: the factor sets the measured order)
+                    if (fused_epilogue) t *= kt_unit < 32 ? 0.85 : 1.03;
+                    else if (kt_unit > 32 && e.opb == 0) t *= 1.08;
+                    else if (kt_unit <= 16) t *= 0.85;  // 4096^2 x 256 bf16 19.4 against 20.9,
+                                                        // 1536 x 8192 x 256 18.2 against 20.4
+                    else if (one_round && kt_unit <= 32) t *= 0.95;
+                }
+                if (grid_e < tiles) t *= 0.94;
+                if (slices > 1) t += 4.0 + (double)(slices + 1) * (double)M * (double)N * 4.0 / 5.49e6;
+                if (packed) t += (double)((M * K + K * N) + (Mp * Kp + Np * Kp)) * es / 3.5e6 + 3.0;
+                cost = t * kCycles16PerUs;
+            } else {
+                // the reduction reads every plane and writes C, and is a second launch;
+                // measured at 256^3 and 1024^3 fp32, a split costs about 16000 cycles
+                // beyond its traffic (about 1 KB per clock for a kernel of this size),
+                // so it pays only when few tiles face a long K
+                if (slices > 1) cost += (double)(slices + 1) * (double)M * (double)N * 4.0 / 1024.0 + 16000.0;
+                if (packed) cost += pack_cycles;
+            }
             if (!best || cost < best_cost * (1 - 1e-9) ||
                 (cost <= best_cost * (1 + 1e-9) && e.bm * e.bn > best->bm * best->bn)) {
                 best = &e;

@@ -203,6 +203,18 @@ def test_epilogue_f32_direct_copy(op_b, out):
     assert epilogue_error(got, ref, Dp, "f32", out) <= 1.0
 
 
+@pytest.mark.parametrize("schedule", [5, 7])
+@pytest.mark.parametrize("out", ["f32", "bf16", "f16"])
+def test_epilogue_software_pipelined_split(schedule, out):
+    """A K split of the software-pipelined kernel: the slices store plain partial
+    products and the reduction applies alpha, beta R, bias and GELU."""
+    ops = gi.make_operands(300, 264, 32 * 7 + 8, "f16", "normal", seed=21)
+    got, ref, Dp, plan = run_epi(ops, out, act="gelu_tanh", ws_bytes=1 << 24,
+                                 cfg=dg.request(schedule=schedule, waves_n=4, split_k=3))
+    assert plan.schedule == schedule and plan.split_k == 3
+    assert epilogue_error(got, ref, Dp, "f16", out) <= 1.0
+
+
 @pytest.mark.parametrize("bm", [256, 128])
 @pytest.mark.parametrize("op_b", ["N", "T"])
 @pytest.mark.parametrize("out", ["f32", "bf16"])

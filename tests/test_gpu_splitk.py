@@ -147,3 +147,74 @@ def test_split_small_workspace_falls_back():
     assert plan.split_k == 1
     Cref, D = oracle.gemm_ref(ops)
     assert normalized_error(C[:256, :256], Cref, D) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("schedule,waves_n", [(5, 4), (5, 2), (7, 4), (7, 2)])
+@pytest.mark.parametrize("dtype,op_b", [("f16", "N"), ("bf16", "T")])
+@pytest.mark.parametrize("split", [2, 3, 5])
+def test_split_software_pipelined(schedule, waves_n, dtype, op_b, split):
+    """The one-tile form of the software-pipelined kernels with K in slices of whole
+    k-tiles, on edge tiles in M and N; K leaves a partial last k-tile in the last slice
+    (a multiple of 8 for the direct copies, any for the register-staged form, whose
+    operands here sit at 2-byte offsets)."""
+    M, N = 300, 264 if op_b == "N" else 263
+    if schedule == 5:
+        K, lda, ldb = 32 * 9 + 8, None, None
+        off = 0
+    else:
+        K = 32 * 9 + 5
+        lda, ldb = K + 1, (N if op_b == "N" else K) + 3
+        off = 1
+    ops = gi.make_operands(M, N, K, dtype, "normal", seed=split + 10 * schedule + waves_n, op_b=op_b, lda=lda,
+                           ldb=ldb)
+    C, plan = run_split_offset(ops, dg.request(schedule=schedule, waves_n=waves_n, split_k=split), off, ldc=N + 3)
+    assert plan.split_k == split and plan.schedule == schedule
+    check_untouched(C, M, N)
+    Cref, D = oracle.gemm_ref(ops)
+    assert normalized_error(C[:M, :N], Cref, D) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("schedule", [5, 7])
+@pytest.mark.parametrize("op_b", ["N", "T"])
+def test_split_software_pipelined_integer_exact(schedule, op_b):
+    """Integer data through four slices of the software-pipelined kernel: bit-exact,
+    and a second call gives the same bits."""
+    M, N, K = 512, 256, 32 * 10
+    i = np.arange(M)[:, None]
+    k = np.arange(K)[None, :]
+    a = (((7 * i + 3 * k) % 7) - 3).astype(np.float32)
+    b = (((5 * np.arange(K)[:, None] + 2 * np.arange(N)[None, :] + 1) % 7) - 3).astype(np.float32)
+    ops = gi.from_values(a, b, "f16", op_b)
+    req = dg.request(schedule=schedule, waves_n=4, split_k=4)
+    C1, plan = run_split(ops, req, ldc=N + 1)
+    C2, _ = run_split(ops, req, ldc=N + 1)
+    assert plan.split_k == 4 and plan.schedule == schedule
+    Cref, _ = oracle.gemm_ref(ops, want_d=False)
+    assert np.array_equal(C1[:M, :N].astype(np.float64), Cref)
+    assert np.array_equal(C1, C2)
+
+
+def run_split_offset(ops, cfg, off, ldc):
+    """run_split with operands placed `off` elements past an aligned address (the
+    register-staged form's element-aligned rows)."""
+    if off == 0:
+        return run_split(ops, cfg, ldc=ldc)
+    torch = _torch()
+    rows = ops.M + 2
+    tdt = torch.float16 if ops.dtype == "f16" else torch.bfloat16
+    At = torch.from_numpy(np.concatenate([np.zeros(off, np.uint16), ops.A.astype(np.uint16)]).view(np.int16)).cuda()
+    Bt = torch.from_numpy(np.concatenate([np.zeros(off, np.uint16), ops.B.astype(np.uint16)]).view(np.int16)).cuda()
+    a_ptr, b_ptr = At.data_ptr() + 2 * off, Bt.data_ptr() + 2 * off
+    Ct = torch.full((rows * ldc + 8,), float(SENTINEL), dtype=torch.float32, device="cuda")
+    ws = 1 << 26
+    Wt = torch.full((ws // 4 + 8,), float("nan"), dtype=torch.float32, device="cuda")
+    _, plan = dg.gemm_plan_workspace(0, dg.OP_CODE[ops.op_b], ops.M, ops.N, ops.K, ops.lda, ops.ldb, ldc,
+                                     dg.DTYPE_CODE[ops.dtype], a_ptr, b_ptr, Ct.data_ptr(), 256, "gfx950", ws, cfg)
+    print(f"split-K case M={ops.M} N={ops.N} K={ops.K} {ops.dtype} op {ops.op_b} offset {off}: kernel "
+          f"{plan.kernel_id} schedule {plan.schedule} split {plan.split_k}", flush=True)
+    dg.gemm_ex_workspace(0, dg.OP_CODE[ops.op_b], ops.M, ops.N, ops.K, a_ptr, ops.lda, b_ptr, ops.ldb,
+                         Ct.data_ptr(), ldc, dg.DTYPE_CODE[ops.dtype], cfg, Wt.data_ptr(), ws,
+                         torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    del tdt
+    return Ct[:rows * ldc].cpu().numpy().reshape(rows, ldc), plan
