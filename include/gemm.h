@@ -123,7 +123,9 @@ typedef struct gemm_config {
                             workgroup per compute unit when the tiles outnumber the compute
                             units; a cap at or above the tile count means one workgroup per tile */
     int32_t split_k;     /* in/out: K slices; in: 0 = heuristic, 1 = no split, S >= 2 = S slices (fewer
-                            if K has fewer k-tiles); splitting needs a workspace (gemm_ex_workspace) */
+                            if K has fewer k-tiles); splitting needs a workspace (gemm_ex_workspace)
+                            and one of schedules 1, 5 (not on a persistent grid) and 7 (the last
+                            slice at least 8 elements of K) */
     int32_t k_chunk;     /* out: K elements per slice (K when not split) */
     int64_t workspace_bytes; /* out: workspace the configuration uses (0 without split or packing) */
     int32_t pack;        /* in/out: operand packing (gemm_ex_workspace); in: 0 = heuristic, 1 = never,
@@ -187,9 +189,11 @@ int gemm_plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, in
 
 /*
  * gemm_ex_workspace -- gemm_ex with a caller-provided device workspace, which
- * allows split K: the K range is cut into S slices that run as separate
- * workgroups (grid y), each writing its partial product to its own plane of the
- * workspace, and a second kernel adds the planes in slice order into C. The sum
+ * allows split K: the K range is cut into S slices of whole k-tiles that run as
+ * separate workgroups (grid y; the register-staged kernels and the one-tile form
+ * of the software-pipelined ones), each writing its partial product to its own
+ * plane of the workspace, and a second kernel adds the planes in slice order into
+ * C, applying any epilogue. The sum
  * order is fixed, so results are reproducible call to call (they differ from the
  * unsplit kernel's by rounding). This fills the machine when M x N has few tiles
  * (the "few blocks" case of "GPU architecture and mapping kernels", section 12.9,
