@@ -325,6 +325,30 @@ def test_plan_fp32_choices_follow_measurements():
             assert c.schedule == want, ((M, N, K), c.schedule)
 
 
+def test_plan_16bit_choices_follow_measurements():
+    """16-bit choices with a workspace on shapes where the choice was timed against the
+    previous model's (medians of five alternated passes, one box): few tiles facing a
+    long K split on the 256 x 256 software-pipelined kernel or on smaller register-staged
+    tiles, which the previous model left unsplit on 64 x 64 or 128 x 128 tiles."""
+    cases = {  # (M, N, K), dtype, opB: (schedule, bm, split)   time against the previous choice
+        ((768, 1024, 16384), "f16", 0): (5, 256, 16),   # 46.0 us against 129.7
+        ((1536, 1536, 8192), "f16", 0): (5, 256, 4),    # 56.2 against 102.3
+        ((512, 3072, 8192), "bf16", 1): (5, 256, 8),    # 43.5 against 68.5
+        ((2048, 3072, 16384), "bf16", 1): (5, 256, 2),  # 188.3 against 280.6
+        ((768, 1024, 8192), "f16", 0): (1, 128, 8),     # 32.2 against 66.1
+        ((512, 768, 4096), "f16", 0): (1, 64, 4),       # 16.6 against 33.8
+    }
+    for ((M, N, K), dt, op_b), want in cases.items():
+        st, c = dg.gemm_plan_workspace(0, op_b, M, N, K, K, N if op_b == 0 else K, N, dg.DTYPE_CODE[dt], 4096, 4096,
+                                       4096, 256, "gfx950", 1 << 30, None)
+        assert st == 0 and (c.schedule, c.bm, c.split_k) == want, ((M, N, K), dt, c.schedule, c.bm, c.split_k)
+        assert c.grid == c.tiles_total and c.workspace_bytes == c.split_k * M * ((N + 3) // 4 * 4) * 4
+    # without a workspace nothing splits, and the same problems keep one launch
+    st, c = dg.gemm_plan_workspace(0, 0, 768, 1024, 16384, 16384, 1024, 1024, dg.GEMM_F16, 4096, 4096, 4096, 256,
+                                   "gfx950", 0, None)
+    assert st == 0 and c.split_k == 1 and c.launches == 1
+
+
 def test_plan_fills_the_machine():
     """A smaller problem gets smaller tiles so that the grid covers the compute units."""
     st, c = plan(1024, 1024, 1024, "f32")
