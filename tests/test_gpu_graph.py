@@ -84,11 +84,15 @@ def test_plain_call_in_graph(case):
     run_case(call, [A, B], C)
 
 
-@pytest.mark.parametrize("case", ["split_k", "packed"])
+@pytest.mark.parametrize("case", ["split_k", "split_k_pipelined_f16", "split_k_pipelined_reg_bf16", "packed"])
 def test_workspace_call_in_graph(case):
     torch = _torch()
     if case == "split_k":
         dtype, op_b, (M, N, K), req, pad = "f32", "N", (256, 256, 8192), dg.request(split_k=8), (0, 0)
+    elif case == "split_k_pipelined_f16":
+        dtype, op_b, (M, N, K), req, pad = "f16", "N", (512, 768, 4096), dg.request(schedule=5, split_k=4), (0, 0)
+    elif case == "split_k_pipelined_reg_bf16":
+        dtype, op_b, (M, N, K), req, pad = "bf16", "T", (300, 500, 2053), dg.request(schedule=7, split_k=3), (3, 5)
     else:
         dtype, op_b, (M, N, K), req, pad = "bf16", "T", (301, 257, 103), dg.request(pack=2), (3, 5)
     A, lda, B, ldb = operands(torch, M, N, K, dtype, op_b, pad)
