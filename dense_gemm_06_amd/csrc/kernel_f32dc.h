@@ -33,6 +33,7 @@ namespace dg {
 // in reaches only rows and columns of C that are not stored.
 template <int OPB, int KG, int S>
 __global__ __launch_bounds__(256 * KG) void mfma32_dc(GemmArgs g) {
+    k_slice<4, OPB>(g);  // a split-K launch: this workgroup's slice (whole pairs of k-tiles)
     constexpr int BM = 64, BN = 64, BK = 32;
     constexpr int NT = 256;                  // threads per K group
     constexpr int STAGE = BM * BK;           // floats per operand and stage (B: BK x BN, the same)
@@ -259,6 +260,7 @@ namespace dg {
 // columns 0 .. 3; neither reaches a stored element.
 template <int OPB, int BM, int BN, int S>
 __global__ __launch_bounds__(512) void mfma32_dcl(GemmArgs g) {
+    k_slice<4, OPB>(g);  // a split-K launch: this workgroup's slice (whole k-tiles)
     constexpr int BK = 32, NW = 8;
     constexpr int WN = BN / 64, WM = NW / WN, WTM = BM / WM, FA = WTM / 16;
     static_assert(BN % 64 == 0 && NW % WN == 0 && WTM % 16 == 0 && FA >= 1 && FA <= 4, "wave grid");

@@ -411,10 +411,13 @@ static int plan_uncached(int opA, int opB, int64_t M, int64_t N, int64_t K, int6
             if ((want_split == 1 || packed) && S != 1) continue;
             int64_t slices = 1, chunk = Kx;
             if (S > 1) {
-                // the register-staged kernels and the one-tile form of the
-                // software-pipelined kernels take K slices of whole k-tiles
-                if ((e.sched != 1 && e.sched != 5 && e.sched != 7) || ktiles < 2) continue;
-                const int64_t chunk_tiles = (ktiles + S - 1) / S;
+                // the register-staged kernels, the one-tile form of the software-
+                // pipelined kernels and the fp32 direct-copy tiles take K slices of whole
+                // k-tiles (the 64 x 64 direct-copy tile: whole pairs, one per K group)
+                if ((e.sched != 1 && e.sched != 5 && e.sched != 7 && e.sched != 8 && e.sched != 9) || ktiles < 2)
+                    continue;
+                int64_t chunk_tiles = (ktiles + S - 1) / S;
+                if (e.sched == 8) chunk_tiles = (chunk_tiles + 1) & ~(int64_t)1;
                 slices = (ktiles + chunk_tiles - 1) / chunk_tiles;
                 chunk = chunk_tiles * e.bk;
                 if (slices < 2) continue;

@@ -105,11 +105,12 @@ typedef struct gemm_config {
                           B or N >= 8 for row-major B); 8 fp32 64 x 64 tiles with direct
                           global->LDS copies three k-tiles ahead, K over two wave groups
                           (16-byte aligned operands, any M, K a multiple of 64, any N for
-                          column-major B or N a multiple of 4 for row-major B, K not split);
+                          column-major B or N a multiple of 4 for row-major B; K slices of
+                          whole pairs of k-tiles);
                           9 fp32 256 x 128 (three LDS stages) or 128 x 128 (five) tiles on
                           eight waves with direct global->LDS copies (16-byte aligned
                           operands, any M, K a multiple of 32, any N for column-major B or N
-                          a multiple of 4 for row-major B, K not split) */
+                          a multiple of 4 for row-major B) */
     int64_t tiles_m, tiles_n; /* out (grouped: of the first non-empty problem) */
     double est_cycles; /* out: the heuristic's cost estimate (clock cycles) */
     int64_t tiles_total; /* out: output tiles of the call (grouped: of all its problems) */
@@ -124,8 +125,9 @@ typedef struct gemm_config {
                             units; a cap at or above the tile count means one workgroup per tile */
     int32_t split_k;     /* in/out: K slices; in: 0 = heuristic, 1 = no split, S >= 2 = S slices (fewer
                             if K has fewer k-tiles); splitting needs a workspace (gemm_ex_workspace)
-                            and one of schedules 1, 5 (not on a persistent grid) and 7 (the last
-                            slice at least 8 elements of K) */
+                            and one of schedules 1, 5 (not on a persistent grid), 7 (the last
+                            slice at least 8 elements of K), 8 (slices of whole pairs of
+                            k-tiles, so fewer slices than asked where that rounds up) and 9 */
     int32_t k_chunk;     /* out: K elements per slice (K when not split) */
     int64_t workspace_bytes; /* out: workspace the configuration uses (0 without split or packing) */
     int32_t pack;        /* in/out: operand packing (gemm_ex_workspace); in: 0 = heuristic, 1 = never,
@@ -190,8 +192,8 @@ int gemm_plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, in
 /*
  * gemm_ex_workspace -- gemm_ex with a caller-provided device workspace, which
  * allows split K: the K range is cut into S slices of whole k-tiles that run as
- * separate workgroups (grid y; the register-staged kernels and the one-tile form
- * of the software-pipelined ones), each writing its partial product to its own
+ * separate workgroups (grid y; the register-staged kernels, the one-tile form of
+ * the software-pipelined ones and the fp32 direct-copy tiles), each writing its partial product to its own
  * plane of the workspace, and a second kernel adds the planes in slice order into
  * C, applying any epilogue. The sum
  * order is fixed, so results are reproducible call to call (they differ from the

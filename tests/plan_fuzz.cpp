@@ -91,7 +91,8 @@ static void check_plan(int opB, int64_t M, int64_t N, int64_t K, int64_t lda, in
           "config does not match entry %d", e.id);
     CHECK(schedule_enabled(e.sched), "switched-off schedule %d chosen", e.sched);
     CHECK(!epi || epilogue_capable(e.sched), "schedule %d with an epilogue", e.sched);
-    CHECK(c.split_k >= 1 && (c.split_k == 1 || e.sched == 1 || e.sched == 5 || e.sched == 7), "split %d on schedule %d", c.split_k, e.sched);
+    CHECK(c.split_k >= 1 && (c.split_k == 1 || e.sched == 1 || e.sched == 5 || e.sched == 7 || e.sched == 8 || e.sched == 9), "split %d on schedule %d", c.split_k, e.sched);
+    CHECK(c.split_k == 1 || e.sched != 8 || c.k_chunk % 64 == 0, "schedule 8 slice of %lld", (long long)c.k_chunk);
     CHECK(c.split_k == 1 || c.grid == c.tiles_m * c.tiles_n, "split %d on a persistent grid", c.split_k);
     CHECK(!(c.split_k > 1 && packed), "split and packed");
     CHECK(c.workspace_bytes >= 0 && c.workspace_bytes <= (ws > 0 ? ws : 0), "workspace %lld of %lld",

@@ -218,3 +218,37 @@ def run_split_offset(ops, cfg, off, ldc):
     torch.cuda.synchronize()
     del tdt
     return Ct[:rows * ldc].cpu().numpy().reshape(rows, ldc), plan
+
+
+@pytest.mark.parametrize("schedule,bm", [(8, 64), (9, 256), (9, 128)])
+@pytest.mark.parametrize("op_b", ["N", "T"])
+@pytest.mark.parametrize("split", [2, 3, 5])
+def test_split_f32_direct_copy(schedule, bm, op_b, split):
+    """The fp32 direct-copy tiles with K in slices of whole k-tiles (pairs for the 64 x 64
+    tile, whose two K groups share each slice), on edge tiles in M and N."""
+    M, N = 2 * bm + 37, 300 if op_b == "N" else 301
+    K = 64 * 11
+    ops = gi.make_operands(M, N, K, "f32", "normal", seed=split + schedule + bm, op_b=op_b)
+    C, plan = run_split(ops, dg.request(schedule=schedule, bm=bm, split_k=split), ldc=N + 3)
+    # slices of whole k-tile pairs on the 64 x 64 tile: 22 k-tiles asked for in five
+    # slices become four of six
+    assert (plan.split_k == split or (schedule == 8 and 2 <= plan.split_k < split)) and plan.schedule == schedule
+    assert plan.bm == bm and (schedule != 8 or plan.k_chunk % 64 == 0)
+    check_untouched(C, M, N)
+    Cref, D = oracle.gemm_ref(ops)
+    assert normalized_error(C[:M, :N], Cref, D) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("schedule,bm", [(8, 64), (9, 256), (9, 128)])
+def test_split_f32_direct_copy_integer_exact(schedule, bm):
+    """Integer data through four slices of the fp32 direct-copy tiles: bit-exact."""
+    M, N, K = 300, 260, 64 * 12
+    i = np.arange(M)[:, None]
+    k = np.arange(K)[None, :]
+    a = (((7 * i + 3 * k) % 7) - 3).astype(np.float32)
+    b = (((5 * np.arange(K)[:, None] + 2 * np.arange(N)[None, :] + 1) % 7) - 3).astype(np.float32)
+    ops = gi.from_values(a, b, "f32", "N")
+    C, plan = run_split(ops, dg.request(schedule=schedule, bm=bm, split_k=4), ldc=N + 1)
+    assert plan.split_k == 4 and plan.schedule == schedule
+    Cref, _ = oracle.gemm_ref(ops, want_d=False)
+    assert np.array_equal(C[:M, :N].astype(np.float64), Cref)
