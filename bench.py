@@ -58,7 +58,10 @@ def kernel_sources(cfg) -> list[str]:
 
 
 def kernel_source_hash(cfg) -> str:
-    h = hashlib.sha256()
+    """Hash of a configuration's kernel sources and the device compiler flags (code
+    placement alone has changed a kernel's speed)."""
+    from dense_gemm_06_amd.build import DEVICE_FLAGS
+    h = hashlib.sha256(" ".join(DEVICE_FLAGS).encode())
     for f in kernel_sources(cfg):
         with open(os.path.join(ROOT, "dense_gemm_06_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
