@@ -128,13 +128,14 @@ static double rate_per_cu(const MenuEntry& e) {
     return e.dtype == DT_F32 ? 256.0 : 4096.0;
 }
 static double tile_efficiency_aligned(const MenuEntry& e);
-// Load-path factor. 16-byte loads from rows that are not 16-byte aligned, on the
-// register-staged 256 x 256 kernels, as measured against the same kernel on a
-// 16-byte-aligned problem of the same tile counts: 16-bit 3001 x 5003 x 1037 with
-// column-major B 69-75 us against 54-57 (3008 x 5008 x 1040), 4095^3 f16 310-321
-// us against 165 (4096^3); fp32 4095^3 1303 us against 1032. Element-wise loads
-// (bases not aligned to the element) measured about 3x slower for 16-bit inputs
-// and are assumed 1.7x slower for fp32.
+// Per-tile efficiency of the kernels without a fitted time (the SIMT kernels, the
+// grouped kernels and 16-bit element-wise loads) and a load-path factor: 16-byte
+// loads from rows that are not 16-byte aligned, on the register-staged 256 x 256
+// kernels, as measured against the same kernel on a 16-byte-aligned problem of the
+// same tile counts: 16-bit 3001 x 5003 x 1037 with column-major B 69-75 us against
+// 54-57 (3008 x 5008 x 1040), 4095^3 f16 310-321 us against 165 (4096^3).
+// Element-wise loads (bases not aligned to the element) measured about 3x slower
+// for 16-bit inputs and are assumed 1.7x slower for fp32.
 static double tile_efficiency(const MenuEntry& e, bool rows16) {
     const bool f32 = e.dtype == DT_F32;
     const double load = !e.vec ? (f32 ? 0.6 : 0.35) : (rows16 || e.sched == 7) ? 1.0 : (f32 ? 0.8 : 0.55);
@@ -147,55 +148,81 @@ static double tile_efficiency_aligned(const MenuEntry& e) {
     if (e.sched == 2) return 0.97;
     if (e.sched == 4) return 0.96;
     if (e.sched == 5 || e.sched == 7) return 0.90;  // problem-dependent: see plan()
-    // the fp32 three-stage 256 x 128 tile: 2.8% faster per k than two resident 128 x 128
-    // register-staged tiles per CU (fitted from 8192^2 x K, K = 256, 512 and 8192,
-    // alternated: 31.2 against 32.1 us per round and 256 k), with a larger fixed cost
-    // per round (fp32_round_overhead); it does not split K
-    if (e.sched == 6) return e.bm >= 256 ? 0.72 : 0.40;  // 64 x 64: see plan()
-    if (e.sched == 8) return 0.50;  // not used: plan() costs it from a fit of its own
     if (e.variant == V_LDS) return t >= 128 ? 0.6 : 0.35;
-    // the fp32 64 x 64 tile with K split between two wave grids measured 7-9% faster
-    // than with one (1024^3: 27.3-27.8 us against 29.6-29.8; 256^3: 8.4-8.6 against
-    // 9.0-9.1; 512 x 4096 x 4096: 162-169 against 177-180)
-    // The 16 x 64 tile with K split over four one-wave groups: two resident per CU;
-    // against the 64 x 64 tile with two K groups, 256^3 5.4 us against 8.2 (64
-    // workgroups against 16), 512^3 8.1 against 13.4, 128 x 1024 x 1024 12.6 against
-    // 23.5, 256 x 256 x 16384 153 against 326; slower once 64 x 64 tiles fill the
-    // machine (1024^3 32.0 against 24.7, 1024^2 x 256 12.6 against 9.4)
-    if (e.threads > e.wm * e.wn * 64) return e.bm < 64 ? 0.30 : 0.49;
     return t >= 256 ? 0.85 : t >= 128 ? 0.7 : 0.45;
 }
-// fp32 tiles: cycles per round of tiles beyond the k loop (the first copies and the
-// C store), fitted from the same 8192^2 x K runs: a lone 256 x 128 tile per CU
-// (three-stage or register-staged) exposes about 13-14 us per round (128 KB of C),
-// two resident 128 x 128 tiles about 6 us (the same C bytes; one tile's store and
-// first copies overlap the other's k loop). In the model's cycles (about 2.9 per ns
-// at the fp32 rates above): 0.29 cycles per byte of C alone, 0.134 with two or
-// more resident tiles. Without this term the three-stage tile won at short K and
-// measured 18% slower than 128 x 128 tiles at 8192^2 x 256 (360.8 us against 305.0).
-static double fp32_round_overhead(const MenuEntry& e, int64_t resident) {
-    const double c_bytes = 4.0 * e.bm * e.bn * (double)resident;
-    return c_bytes * (resident >= 2 ? 0.134 : 0.29);
-}
-// Time model of the 16-bit MFMA tile families on 16-byte loads (fitted, in us, to
-// 1290 medians of five alternated passes over 26 shapes of 512 to 8192 and 120 more
-// between 512^2 x 256 and 8192^2 x 16384, both B layouts, one box, splits included;
-// median error 1.6-6.8% per family): the larger of a per-CU bound, rounds of
-// tiles of `resident` tiles each at a per-CU rate min(resident r1, rcap) TFLOP/s
-// plus a fixed a per round, and a chip bound c + 2MNK / R (the board's power limit:
-// a problem that keeps every CU busy runs at R TFLOP/s whatever its tile). The
+// Time model of the MFMA tile families (fitted, in us, per family): the larger of a
+// per-CU bound, rounds of tiles of `resident` tiles each at a per-CU rate (16-bit:
+// min(resident r1, rcap) TFLOP/s; fp32: a rate per resident count) plus a fixed a
+// per round, and a chip bound c + 2MNK / R (for 16-bit inputs the board's power
+// limit: a problem that keeps every CU busy runs at R TFLOP/s whatever its tile). The
 // per-CU bound is what makes few tiles of long K slow, and R what makes the largest
-// tiles win once the machine is full.
-struct Fit16 {
-    double a, r1, rcap, c, R;
+// tiles win once the machine is full. ks stretches the k loop for rows that are not
+// 16-byte aligned (fp32; the 16-bit register-staged kernels take a fixed factor, see
+// plan()).
+//
+// 16-bit families on 16-byte loads: 1290 medians of five alternated passes over 26
+// shapes of 512 to 8192 and 120 more between 512^2 x 256 and 8192^2 x 16384, both B
+// layouts, one box, splits included; median error 1.6-6.8% per family.
+//
+// fp32 families, per B layout: 1694 medians of five passes in shuffled order over 28
+// shapes of 256^2 x 4096 to 8192^2 x 512, both B layouts, every tile with and without
+// K split 2-16 ways, and 8 shapes with A rows one element off 16-byte alignment, and
+// 180 medians of seven passes on 90 shapes drawn at random (log-uniform 256-8192, a
+// third of them ragged); median error 0.3-3.3% per family and layout (the per-tile
+// efficiency model used before: 3-47%). A partial tile in M or N stretches the
+// register-staged tiles' k loop by 4-33% (edge): an edge tile's masked loads run at
+// up to half speed and, a round of tiles ending together, set the launch's time
+// (1024 x 1028 x 4096 on 64 x 64 tiles 228 us, against 160 for 1024 x 1088). The 64 x 64 four-wave tile runs its k loop at 0.35, 0.43, 0.46 and
+// 0.47 TFLOP/s per CU with one to four resident (a shared cap reached at two
+// resident had it 35% off at 1280^2 x 8192), and the chip bound takes over at five;
+// the direct-copy 256 x 128 tile's k loop is the faster with row-major B (0.562
+// against 0.543), the 128 x 128 tile's with column-major B (0.560 against 0.545);
+// rows that are not 16-byte aligned cost the register-staged fp32 tiles 2-5% (not
+// the 25% assumed before).
+struct TimeFit {
+    double a, r1, rcap, c, R, ks;
+    double edge;     // k-loop stretch when M or N leaves a partial tile (register-staged fp32 tiles)
+    double rate[5];  // if set: the per-CU rate with 1, 2, ... resident tiles (fp32)
 };
-static const Fit16* fit16(const MenuEntry& e) {
-    static const Fit16 rs64{3.25, 1.12, 2.90, 4.52, 537.4}, rs128{5.97, 2.77, 4.00, 4.46, 834.0},
-        rs256{14.79, 5.18, 5.18, 6.12, 900.4}, wide{15.34, 4.16, 4.16, 7.10, 802.7},
-        pp16{14.61, 6.84, 6.84, 6.34, 1065.8}, pp32{16.96, 6.39, 6.39, 5.09, 927.8},
-        sp4{17.35, 8.72, 8.72, 11.69, 1086.0}, sp8{13.36, 9.23, 9.23, 8.18, 1108.1},
-        spr8{14.69, 7.65, 7.65, 11.31, 1011.2};
-    if (e.variant != V_MFMA || e.dtype == DT_F32 || !e.vec) return nullptr;
+static const TimeFit* time_fit(const MenuEntry& e) {
+    static const TimeFit rs64{3.25, 1.12, 2.90, 4.52, 537.4, 1, 1}, rs128{5.97, 2.77, 4.00, 4.46, 834.0, 1, 1},
+        rs256{14.79, 5.18, 5.18, 6.12, 900.4, 1, 1}, wide{15.34, 4.16, 4.16, 7.10, 802.7, 1, 1},
+        pp16{14.61, 6.84, 6.84, 6.34, 1065.8, 1, 1}, pp32{16.96, 6.39, 6.39, 5.09, 927.8, 1, 1},
+        sp4{17.35, 8.72, 8.72, 11.69, 1086.0, 1, 1}, sp8{13.36, 9.23, 9.23, 8.18, 1108.1, 1, 1},
+        spr8{14.69, 7.65, 7.65, 11.31, 1011.2, 1, 1};
+    // fp32, per B layout (row-major, column-major): register-staged 64 x 64 on four
+    // waves (five resident per CU) and on two K groups (two), 128 x 128 (two), 256 x 128
+    // (one), 16 x 64 with four K groups (two); the three-stage 256 x 128 and 64 x 64
+    // tiles; the direct-copy 64 x 64, 256 x 128 and 128 x 128 tiles (one resident
+    // each). The unaligned runs had row-major B; both layouts take their ks.
+    static const TimeFit f_rs64[2]{{2.75, 0, 0, 6.37, 120.7, 1.031, 1.223, {0.3497, 0.4330, 0.4562, 0.4656, 0.6140}}, {2.41, 0, 0, 5.53, 119.3, 1.031, 1.165, {0.3615, 0.4437, 0.4748, 0.4678, 0.6140}}},
+        f_kg2[2]{{2.56, 0, 0, 6.74, 117.1, 1.034, 1.213, {0.3985, 0.5001}}, {2.11, 0, 0, 5.72, 115.0, 1.034, 1.163, {0.3868, 0.4823}}},
+        f_rs128[2]{{7.52, 0, 0, 10.71, 129.0, 1.021, 1.335, {0.4865, 0.5930}}, {5.30, 0, 0, 7.15, 130.0, 1.021, 1.191, {0.4893, 0.5780}}},
+        f_rs256[2]{{13.07, 0, 0, 32.25, 138.1, 1.041, 1.186, {0.5553}}, {7.40, 0, 0, 15.55, 133.2, 1.041, 1.070, {0.5338}}},
+        f_s3[2]{{13.94, 0, 0, 33.74, 138.3, 1.028, 1.200, {0.5577}}, {8.46, 0, 0, 18.29, 136.7, 1.028, 1.065, {0.5427}}},
+        f_s3_64[2]{{4.57, 0, 0, 4.77, 106.0, 1.021, 1.089, {0.4365}}, {2.47, 0, 0, 10.07, 150.5, 1.021, 1.035, {0.4175}}},
+        f_small[2]{{2.14, 0, 0, 5.86, 83.0, 1.051, 1.614, {0.2144, 0.3372}}, {2.18, 0, 0, 5.51, 80.6, 1.051, 1.000, {0.2141, 0.3261}}},
+        f_d[2]{{3.45, 0, 0, 5.45, 125.7, 1.000, 1.000, {0.4998}}, {2.85, 0, 0, 4.74, 124.0, 1.000, 1.000, {0.5010}}},
+        f_w[2]{{12.69, 0, 0, 14.07, 135.0, 1.000, 1.000, {0.5621}}, {8.15, 0, 0, 8.17, 134.2, 1.000, 1.000, {0.5430}}},
+        f_n[2]{{7.25, 0, 0, 10.92, 133.9, 1.000, 1.000, {0.5444}}, {5.58, 0, 0, 8.52, 139.6, 1.000, 1.000, {0.5588}}};
+    if (e.variant != V_MFMA) return nullptr;
+    if (e.dtype == DT_F32) {
+        const int b = e.opb;
+        switch (e.sched) {
+            case 1:
+                if (e.bm == 64 && e.bn == 64) return e.threads == 256 ? &f_rs64[b] : &f_kg2[b];
+                if (e.bm == 128 && e.bn == 128) return &f_rs128[b];
+                if (e.bm == 256 && e.bn == 128) return &f_rs256[b];
+                if (e.bm == 16 && e.bn == 64) return &f_small[b];
+                return nullptr;
+            case 6: return e.bm == 256 ? &f_s3[b] : &f_s3_64[b];
+            case 8: return &f_d[b];
+            case 9: return e.bm == 256 ? &f_w[b] : &f_n[b];
+            default: return nullptr;
+        }
+    }
+    if (!e.vec) return nullptr;
     switch (e.sched) {
         case 1:
             if (e.bm == 64 && e.bn == 64 && e.threads == 256) return &rs64;
@@ -210,16 +237,18 @@ static const Fit16* fit16(const MenuEntry& e) {
     }
 }
 // kslow stretches the k loop only (slower loads), not the fixed costs.
-static double fit16_us(const Fit16& f, const MenuEntry& e, int64_t rounds, int64_t resident, int64_t kt,
-                       double flops, double kslow) {
+static double fit_us(const TimeFit& f, const MenuEntry& e, int64_t rounds, int64_t resident, int64_t kt,
+                     double flops, double kslow) {
     const double w = 2.0 * e.bm * e.bn * e.bk / 1e6;  // MFLOP per k-tile of one tile
-    const double rate = std::min((double)resident * f.r1, f.rcap);
+    const double rate = f.rate[0] > 0 ? f.rate[std::min<int64_t>(resident, 5) - 1] : std::min((double)resident * f.r1, f.rcap);
     const double per_cu = (double)rounds * (f.a + kslow * (double)kt * (double)resident * w / rate);
     return std::max(per_cu, f.c + kslow * flops / (f.R * 1e6));
 }
-// The 16-bit model's cycles per us (the software-pipelined 4096^3 kernel's cost
-// against its time), to set fitted times beside the families the fit does not cover.
+// Model cycles per us: the 16-bit model's (the software-pipelined 4096^3 kernel's cost
+// against its time) and the fp32 model's, to set fitted times beside the families the
+// fits do not cover (the SIMT kernels).
 constexpr double kCycles16PerUs = 1141.0;
+constexpr double kCycles32PerUs = 2900.0;
 
 static int blocks_per_cu(const MenuEntry& e) {
     const int by_lds = (160 * 1024) / e.lds_bytes;
@@ -374,6 +403,17 @@ static int plan_uncached(int opA, int opB, int64_t M, int64_t N, int64_t K, int6
         // inside each row: K >= 8, and N >= 8 for a row-major B
         if (e.sched == 7 && (Kx < 8 || (e.opb == 0 && Nx < 8))) continue;
         if (want_wn && (e.variant == V_MFMA ? e.wn : 1) != want_wn) continue;
+        // fp32 tiles that the direct-copy tiles of the same shape dominate where those
+        // can run (unless asked for by schedule): the three-stage 64 x 64 tile measured
+        // 10-40% slower than the direct-copy one on all 44 shapes timed with both
+        // (median 17%), the three-stage and register-staged 256 x 128 tiles within 1-2%
+        // of the direct-copy 256 x 128 tile (medians 0.6% and 1.6% slower, at most 4%
+        // faster), which leaves their ranking to noise in the fitted times
+        if (e.dtype == DT_F32 && e.variant == V_MFMA && !want_sched && (packed || dma_ok) &&
+            (e.opb == 1 || Nx % 4 == 0)) {
+            if (e.sched == 6 && e.bm == 64 && Kx % 64 == 0 && Kx > 0) continue;
+            if ((e.sched == 6 || e.sched == 1) && e.bm == 256 && e.bn == 128 && Kx % 32 == 0 && Kx > 0) continue;
+        }
         const int vec = want_vec >= 0 ? want_vec : ((packed || vec_ok) ? 1 : 0);
         if (e.vec != vec) continue;
         if (e.vec && !packed && !vec_ok) continue;          // 16-byte loads need element-aligned bases
@@ -473,55 +513,8 @@ static int plan_uncached(int opA, int opB, int64_t M, int64_t N, int64_t K, int6
                 else eff = !eight ? 0.90 : (work <= num_cus && kt_unit <= 32) ? 0.96 : 0.99;
                 if (e.sched == 7) eff *= 0.9;
             }
-            // the fp32 64 x 64 tile with two K groups on the three-stage schedule:
-            // 1.5-6% faster than on the two-stage one for one round of tiles (1024^3
-            // 23.7-24.3 us against 24.7-25.2, both B layouts), 10-13% slower over
-            // several rounds (2048^3 171.1 against 150.7; 512 x 4096 x 4096 165.0
-            // against 149.7)
-            if (e.dtype == DT_F32 && e.sched == 6 && e.bm < 256) eff = rounds == 1 ? 0.50 : 0.40;
-            // (the fp32 64 x 64 direct-copy tile, schedule 8, is costed below)
-            // the fp32 128 x 128 register-staged tile is costed for two resident per CU,
-            // each hiding the other's copies and store; alone on a CU it measured 12%
-            // slower (2048^3 153.9 us, 1024 x 4096 x 4096 298.6: 256 tiles, one round)
-            if (e.dtype == DT_F32 && e.sched == 1 && e.bm == 128 && e.threads == 256 &&
-                std::min<int64_t>(occ, ((grid_e < tiles ? grid_e : work) + num_cus - 1) / num_cus) < 2)
-                eff *= 0.88;
             const double tile_cycles = 2.0 * e.bm * e.bn * std::max<int64_t>(kpad, e.bk) / (rate_per_cu(e) * eff);
             double cost = (double)rounds * (double)std::max<int64_t>(resident, 1) * tile_cycles;
-            if (e.dtype == DT_F32 && e.variant == V_MFMA && e.sched != 8)
-                cost += (double)rounds * fp32_round_overhead(e, std::max<int64_t>(resident, 1));
-            // The direct-copy tile's time, fitted per round of its tiles (one resident per
-            // CU) from 1024^3 21.2 us (one round), 1536^3 86.3 (three), 2048^3 147.7
-            // (four), 2560^3 315 (seven), 3072^3 490 (nine) and 1024 x 4096 x 4096 285.6
-            // (four): about 3.0 us per round (the launch's share, the first copies, the
-            // K-group reduction and the store) and 16.7 us per 1024 of K, in the model's
-            // cycles (2900 per us). It
-            // loses to larger tiles once the rounds pile up their fixed cost (4096^3 1113
-            // us against 1026 for the 256 x 128 tile, 6144^2 x 512 403 against 323 for
-            // 128 x 128 tiles, 8192^2 x 1024 1568 against 1066): not past nine rounds.
-            if (e.sched == 8) {
-                if (rounds > 9) continue;
-                cost = (double)rounds * (8700.0 + 47.3 * (double)kpad);
-            }
-            // The large direct-copy tiles (schedule 9), fitted the same way over 24 shapes
-            // of 256 to 12288 (medians of five alternated passes, one box): per round of
-            // tiles a fixed time plus a time per k, in us: 256 x 128 with row-major B 12.1
-            // + 0.1192 K, column-major B 8.8 + 0.1227 K; 128 x 128 (one resident per CU)
-            // 9.3 + 0.0608 K and 5.9 + 0.059 K, and 7.5% more for a single round. Against
-            // the three-stage tile's 14.3 + 0.1212 K (8.4 + 0.1215 K) this makes the
-            // 256 x 128 tile the faster for row-major B and the 128 x 128 tile for
-            // column-major B once K is long (4096^3 1013 and 989 us against 1032 and
-            // 1017; 8192^3 7911 and 7803 against 8057 and 8029), and the 128 x 128 tile
-            // for one round of long K (2048^3 143 and 137 against 148 and 144 for 64 x
-            // 64 tiles; 1024 x 4096 x 4096 278 and 266 against 281 and 277), while two
-            // resident 128 x 128 register-staged tiles keep short K (8192^2 x 256 306
-            // against 347). The model's cycles: 2900 per us.
-            if (e.sched == 9) {
-                const bool wide = e.bm == 256;
-                const double a = wide ? (e.opb == 0 ? 12.1 : 8.8) : (e.opb == 0 ? 9.3 : 5.9);
-                const double b = wide ? (e.opb == 0 ? 0.1192 : 0.1227) : (e.opb == 0 ? 0.0608 : 0.059);
-                cost = (double)rounds * (a + b * (double)kpad) * 2900.0 * (rounds == 1 && !wide ? 1.075 : 1.0);
-            }
             // 16-bit families with a fitted time: the persistent grid measured 2-12%
             // faster than one workgroup per tile over several rounds (0.94 on average),
             // a split adds its reduction (every plane read and C written: 5.5 TB/s
@@ -530,12 +523,21 @@ static int plan_uncached(int opA, int opB, int64_t M, int64_t N, int64_t K, int6
             // packing its copy (3.5 TB/s, plus 3 us for its launch);
             // 16-byte loads from rows that are not 16-byte aligned cost the
             // register-staged kernels 1.8x in the k loop (the load factor above)
-            const Fit16* f16 = fit16(e);
-            if (f16) {
-                const int64_t kt_unit = (std::min<int64_t>(chunk, Kx) + e.bk - 1) / e.bk;
+            const TimeFit* fit = time_fit(e);
+            const int64_t kt_unit = (std::min<int64_t>(chunk, Kx) + e.bk - 1) / e.bk;
+            const double flops = 2.0 * (double)Mx * (double)Nx * (double)Kx;
+            if (fit && e.dtype == DT_F32) {
+                // fp32 tiles with a fitted time; element-wise loads (bases not aligned
+                // to the element) are assumed 1.7x slower in the k loop. The split's
+                // reduction and the packing copy as below and for 16-bit inputs.
+                const double kslow = (!e.vec ? 1.7 : (packed || dma_ok) ? 1.0 : fit->ks) *
+                                     (Mx % e.bm != 0 || Nx % e.bn != 0 ? fit->edge : 1.0);
+                double t = fit_us(*fit, e, rounds, std::max<int64_t>(resident, 1), kt_unit, flops, kslow);
+                if (slices > 1) t += 4.0 + (double)(slices + 1) * (double)M * (double)N * 4.0 / 5.49e6;
+                cost = t * kCycles32PerUs + (packed ? pack_cycles : 0.0);
+            } else if (fit) {
                 const double kslow = e.sched == 1 && !(packed || dma_ok) ? 1.0 / 0.55 : 1.0;
-                double t = fit16_us(*f16, e, rounds, std::max<int64_t>(resident, 1), kt_unit,
-                                    2.0 * (double)Mx * (double)Nx * (double)Kx, kslow);
+                double t = fit_us(*fit, e, rounds, std::max<int64_t>(resident, 1), kt_unit, flops, kslow);
                 if (e.sched == 7 && e.threads != 512) t *= 1.1;
                 // where the direct-copy kernels can take the problem (16-byte aligned
                 // operands, K a multiple of 8, row-major B with N a multiple of 8), the
@@ -569,10 +571,8 @@ static int plan_uncached(int opA, int opB, int64_t M, int64_t N, int64_t K, int6
                 if (packed) t += (double)((M * K + K * N) + (Mp * Kp + Np * Kp)) * es / 3.5e6 + 3.0;
                 cost = t * kCycles16PerUs;
             } else {
-                // the reduction reads every plane and writes C, and is a second launch;
-                // measured at 256^3 and 1024^3 fp32, a split costs about 16000 cycles
-                // beyond its traffic (about 1 KB per clock for a kernel of this size),
-                // so it pays only when few tiles face a long K
+                // the SIMT kernels: the reduction reads every plane and writes C, and is a
+                // second launch (about 16000 cycles beyond its traffic at 1 KB per clock)
                 if (slices > 1) cost += (double)(slices + 1) * (double)M * (double)N * 4.0 / 1024.0 + 16000.0;
                 if (packed) cost += pack_cycles;
             }
