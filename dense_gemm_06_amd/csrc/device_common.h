@@ -310,11 +310,26 @@ template <typename T, int V, bool VEC>
 __device__ __forceinline__ void load_chunk(T (&r)[V], const T* p, int valid) {
     if (VEC && valid >= V) {
         load16(r, p);
+    } else if (valid <= 0) {
+        // outside the matrix: a branch of its own, so that only lanes whose chunk
+        // the edge cuts take the element loads below (and, for 16-bit elements, the
+        // wait that packing them needs)
+#pragma unroll
+        for (int e = 0; e < V; ++e) r[e] = T(0);
     } else {
 #pragma unroll
         for (int e = 0; e < V; ++e) r[e] = (e < valid) ? p[e] : T(0);
     }
 }
+
+// An s_waitcnt vmcnt(0) (the other counters untouched) placed where no vector memory
+// load is in flight, so that it waits for nothing and tells the compiler's wait
+// tracking so. The register-staged kernels call it before an edge k-tile's masked
+// loads: their interior and edge load paths meet in one block, the tracking then
+// counts the interior path's loads as pending on the edge path as well, and the edge
+// path, which reuses those loads' registers as temporaries, waited chunk by chunk for
+// its own loads (an edge tile took twice an interior tile's time).
+__device__ __forceinline__ void vm_settled() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // As load_chunk for a chunk known to lie inside the matrix: no guards.
 template <typename T, int V, bool VEC>

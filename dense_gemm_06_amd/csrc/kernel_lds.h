@@ -62,6 +62,7 @@ __device__ __forceinline__ void lds_tile(const GemmArgs& g, int tm, int tn) {
             }
             return;
         }
+        vm_settled();  // nothing in flight here: the previous loads were stored
 #pragma unroll
         for (int p = 0; p < LA; ++p) {
             const int idx = tid + 256 * p, row = idx / CA, c = idx % CA;

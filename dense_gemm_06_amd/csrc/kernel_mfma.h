@@ -69,6 +69,7 @@ __device__ __forceinline__ void mfma16_tile(const GemmArgs& g, int tm, int tn) {
             }
             return;
         }
+        vm_settled();  // nothing in flight here: the previous loads were stored
 #pragma unroll
         for (int p = 0; p < LA; ++p) {
             const int idx = tid + NT * p, row = idx / KC, c = idx % KC;
@@ -293,6 +294,7 @@ __device__ __forceinline__ void mfma32_tile(const GemmArgs& g, int tm, int tn) {
             }
             return;
         }
+        vm_settled();  // nothing in flight here: the previous loads were stored
 #pragma unroll
         for (int p = 0; p < LA; ++p) {
             const int idx = tid + NT * p, row = idx / KC, c = idx % KC;
