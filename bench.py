@@ -489,7 +489,7 @@ def main():
     extras = {}
     if not a.no_extra and not a.only:
         for name in ("c3_f32_4096", "c1_f32_256", "c2_f32_1024", "c5_bf16_ragged", "m8_f16_shard", "m8_f32_shard",
-                     "r4_f16_8192x8192x2048"):
+                     "r4_f16_8192x8192x2048", "t33_f16_4352x4352x2048"):
             extras[name] = time_problem(name, max(5, a.steps // 2), max(2, a.warmup // 2), min_window_ms=5.0, min_warm_ms=20.0)
         # the same four-round problem with one workgroup per tile (no persistent grid):
         # the headline's kernel, so only with --extended (the default command runs the
@@ -549,6 +549,8 @@ def main():
             out["other_problems"][k]["grid"] = v["cfg"].grid
         out["other_problems"]["r4_f16_8192x8192x2048"]["workload"] = (
             "C=A@B 8192x8192x2048 f16: four rounds of 256 tiles on the persistent grid")
+        out["other_problems"]["t33_f16_4352x4352x2048"]["workload"] = (
+            "C=A@B 4352x4352x2048 f16: a round of 256 tiles and a tail of 33 (with a workspace: stream-K)")
         if one_per_tile is not None:
             r = one_per_tile
             out["other_problems"]["r4_f16_8192x8192x2048"]["one_workgroup_per_tile"] = {
@@ -561,12 +563,13 @@ def main():
             "ms_per_step": round(lk["ms_per_step"], 6), "frac_of_peak": round(lk["tflops"] / lk["peak"], 4),
             "tile": f"{lk['cfg'].bm}x{lk['cfg'].bn}", "variant": "mfma" if lk["cfg"].variant == 2 else "lds"}
         # (and the unaligned ragged problem, which the heuristic packs into aligned whole tiles)
-        for name in ("c1_f32_256", "c2_f32_1024", "k1_f32_long_k", "c5_bf16_ragged", "m8_f16_shard", "m8_f32_shard"):
+        for name in ("c1_f32_256", "c2_f32_1024", "k1_f32_long_k", "c5_bf16_ragged", "m8_f16_shard", "m8_f32_shard",
+                     "t33_f16_4352x4352x2048"):
             r = time_problem(name, max(5, a.steps // 2), max(2, a.warmup // 2), workspace=True, min_window_ms=5.0, min_warm_ms=20.0)
             out["other_problems"][name]["with_workspace"] = {
                 "tflops": round(r["tflops"], 3), "ms_per_step": round(r["ms_per_step"], 6),
                 "frac_of_peak": round(r["tflops"] / r["peak"], 4), "split_k": r["cfg"].split_k,
-                "packed": r["cfg"].pack == 2, "schedule": r["cfg"].schedule,
+                "packed": r["cfg"].pack == 2, "stream_k_width": r["cfg"].sk_width, "schedule": r["cfg"].schedule,
                 "tile": f"{r['cfg'].bm}x{r['cfg'].bn}", "workspace_bytes": r["cfg"].workspace_bytes}
     if fe is not None:
         out["fused_epilogue"] = {"workload": f"{out['config']['workload']} with C = gelu_tanh(A@B + bias) stored "

@@ -50,7 +50,8 @@ class gemm_config(ctypes.Structure):
         ("est_cycles", ctypes.c_double),
         ("tiles_total", ctypes.c_int64), ("launches", ctypes.c_int32), ("max_grid", ctypes.c_int32),
         ("split_k", ctypes.c_int32), ("k_chunk", ctypes.c_int32), ("workspace_bytes", ctypes.c_int64),
-        ("pack", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("pack", ctypes.c_int32), ("stream_k", ctypes.c_int32), ("sk_width", ctypes.c_int32),
+        ("reserved", ctypes.c_int32), ("reserved2", ctypes.c_int32),
     ]
 
     def as_dict(self) -> dict:
@@ -59,12 +60,13 @@ class gemm_config(ctypes.Structure):
 
 def request(variant: int = GEMM_VARIANT_AUTO, bm: int = 0, bn: int = 0, vec: int = -1,
             xcd_remap: int = -1, group_m: int = 0, waves_m: int = 0, waves_n: int = 0,
-            schedule: int = 0, max_grid: int = 0, split_k: int = 0, pack: int = 0, threads: int = 0) -> gemm_config:
+            schedule: int = 0, max_grid: int = 0, split_k: int = 0, pack: int = 0, threads: int = 0,
+            stream_k: int = 0, sk_width: int = 0) -> gemm_config:
     """A gemm_config with only the "in" fields set (0 / -1: heuristic decides)."""
     c = gemm_config()
     c.variant, c.bm, c.bn, c.vec, c.xcd_remap, c.group_m = variant, bm, bn, vec, xcd_remap, group_m
     c.waves_m, c.waves_n, c.schedule, c.max_grid, c.split_k = waves_m, waves_n, schedule, max_grid, split_k
-    c.pack, c.threads = pack, threads
+    c.pack, c.threads, c.stream_k, c.sk_width = pack, threads, stream_k, sk_width
     return c
 
 

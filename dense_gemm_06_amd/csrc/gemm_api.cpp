@@ -349,6 +349,11 @@ int run_product(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A
     args.work_ld = (N + 3) / 4 * 4;
     args.work_slice = M * args.work_ld;
     args.ep = ep;
+    // stream-K: the tiles past the last whole round of the grid (all of them when
+    // there are fewer tiles than workgroups)
+    const int64_t tiles_total = plan.tiles_m * plan.tiles_n;
+    args.sk_tiles = plan.stream_k == 2 ? (int)(tiles_total > plan.grid ? tiles_total % plan.grid : tiles_total) : 0;
+    args.sk_width = plan.stream_k == 2 ? plan.sk_width : 0;
     if (plan.pack == 2) {
         // zero-padded copies of A and B in the workspace, then the product on them
         int64_t Mp, Np, Kp;
@@ -373,6 +378,11 @@ int run_product(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A
         return launch_result(dg::launch_splitk_reduce(args.work, plan.split_k, args.work_slice, args.work_ld, (int)M,
                                                       (int)N, C, ldc, ep, (hipStream_t)stream),
                              "split-K reduction kernel", 0);
+    if (args.sk_tiles > 0)
+        return launch_result(dg::launch_streamk_fixup(args.work, args.sk_width, args.sk_tiles, args.K / plan.bk,
+                                                      (int)(tiles_total - args.sk_tiles), args.tiles_m, args.tiles_n,
+                                                      args.group_m, (int)M, (int)N, C, ldc, ep, (hipStream_t)stream),
+                             "stream-K fixup kernel", 0);
     return GEMM_OK;
 }
 

@@ -3,6 +3,7 @@
 #include <type_traits>
 
 #include "lds_layout.h"
+#include "streamk.h"
 
 // An LDS pointer made from a byte address (an integer): it carries no link to the
 // LDS variable the address falls in.
@@ -99,6 +100,13 @@ __device__ __forceinline__ u32x4 keep_first8(u32x4 w, int v) {
 // layout, the fragment reads, the MFMAs and the epilogue are those of the direct-copy
 // form.
 //
+// STREAM-K (persistent direct-copy form, g.sk_tiles > 0): after its whole rounds of
+// tiles each of the first g.sk_width workgroups takes its share of the tail tiles'
+// k-tiles (streamk.h), as at most two pieces, each a tile with its own k range and
+// k-tile count (at least 4, so the copy stream carries over between pieces as
+// between tiles). A piece that does not cover its tile stores its partial sum, as
+// plain fp32, to its workspace slot; the fixup launch completes those tiles.
+//
 // GROUPED (persistent direct-copy form only): the tiles are those of a grouped call's
 // problems, in the linear order of its segment table (each problem, batch member and
 // tile raster as for the register-staged grouped kernels); each tile carries its own
@@ -127,8 +135,47 @@ __device__ __forceinline__ void mfma32_sp_body(GemmArgs& g, const GroupArgs* ga)
     int tiles_total;
     if constexpr (GROUPED) tiles_total = ga->total_tiles;
     else tiles_total = g.tiles_m * g.tiles_n;
+    // A unit of work: tile `tile` over k-tiles kb .. kb + nk - 1 (nk < 0: all of its
+    // problem's K), its sum stored to C (slot < 0) or to workspace slot `slot`.
+    struct Unit {
+        int tile, kb, nk, slot;
+    };
+    // Unit u of this workgroup: round u of the whole tiles, then (stream-K) the pieces
+    // of its share of the tail; false past the last one.
+    const int sk_tiles = (PERSIST && !GROUPED) ? g.sk_tiles : 0;
+    const int dp_total = tiles_total - sk_tiles;  // a multiple of the grid when sk_tiles > 0
+    const int dp_rounds = sk_tiles > 0 ? dp_total / (int)gridDim.x : 0;
+    auto unit_at = [&](int u, Unit& un) -> bool {
+        un.kb = 0;
+        un.nk = -1;
+        un.slot = -1;
+        if (sk_tiles == 0 || u < dp_rounds) {
+            un.tile = round_tile(u, sk_tiles > 0 ? dp_total : tiles_total, g.xcd_remap);
+            return un.tile >= 0;
+        }
+        // the shares go to hardware ids 0 .. sk_width - 1, which the dispatcher
+        // spreads round-robin over the XCDs
+        const int kt = (g.K + BK - 1) / BK;
+        const int w = (int)blockIdx.x, p = u - dp_rounds;
+        int t, kb, nk;
+        if (w >= g.sk_width || p > 1 || !sk_piece(w, p, g.sk_width, sk_tiles, kt, t, kb, nk)) return false;
+        un.tile = dp_total + t;
+        un.kb = kb;
+        un.nk = nk;
+        un.slot = nk == kt ? -1 : 2 * w + p;
+        return true;
+    };
     int round = 0;
-    int tile = round_tile(0, tiles_total, g.xcd_remap);
+    Unit first;
+    if constexpr (PERSIST) {
+        // a stream-K share can be empty: the whole workgroup leaves before its first barrier
+        if (!unit_at(0, first)) return;
+    } else {
+        first.tile = round_tile(0, tiles_total, g.xcd_remap);
+        first.kb = 0;
+        first.nk = -1;
+        first.slot = -1;
+    }
     // K a multiple of 8: the last k-tile may be partial (krem of its 32 k valid); its
     // copies clamp the chunks at or beyond K and the LDS chunks past K are zeroed
     // before any fragment of that tile is read
@@ -166,8 +213,9 @@ __device__ __forceinline__ void mfma32_sp_body(GemmArgs& g, const GroupArgs* ga)
         int m0, n0;
         int M, N, nk;
         size_t kstep_b;  // elements per k-tile of B
-        float* C;
+        float* C;        // element (m, n) at C[m * ldc + n]
         int64_t ldc;
+        bool plain;      // a partial sum for the workspace: no fused epilogue
     };
     // The problem of tile t: operands, leading dimensions, sizes and tile coordinates.
     struct Prob {
@@ -203,41 +251,52 @@ __device__ __forceinline__ void mfma32_sp_body(GemmArgs& g, const GroupArgs* ga)
             p.K = g.K;
         }
     };
-    auto make_src = [&](int t, Src& s) {
+    auto make_src = [&](const Unit& un, Src& s) {
         Prob p;
-        prob_of(t, p);
+        prob_of(un.tile, p);
         s.m0 = p.tm * BM;
         s.n0 = p.tn * BN;
         s.M = p.M;
         s.N = p.N;
-        s.nk = (p.K + BK - 1) / BK;
+        s.nk = un.nk < 0 ? (p.K + BK - 1) / BK : un.nk;
         s.kstep_b = OPB == 0 ? (size_t)BK * p.ldb : (size_t)BK;
-        s.C = p.C;
-        s.ldc = p.ldc;
+        s.plain = un.slot >= 0;
+        if (un.slot >= 0) {
+            // the slot holds the tile at leading dimension BN: element (m, n) of C
+            // lands at slot[(m - m0) * BN + n - n0]
+            s.C = g.work + ((ptrdiff_t)un.slot * (BM * BN) - ((ptrdiff_t)s.m0 * BN + s.n0));
+            s.ldc = BN;
+        } else {
+            s.C = p.C;
+            s.ldc = p.ldc;
+        }
+        // the unit's first k (0 unless it is a stream-K piece)
+        const size_t k0 = (size_t)un.kb * BK;
 #pragma unroll
         for (int i = 0; i < CPB; ++i) {
             const int b = wave * CPB + i;
             const int row = b * 16 + (lane >> 2);
-            s.a[i] = p.A + (size_t)min(s.m0 + row, p.M - 1) * p.lda + kcA[i];
+            s.a[i] = p.A + (size_t)min(s.m0 + row, p.M - 1) * p.lda + k0 + kcA[i];
             if (OPB == 1) {
-                s.b[i] = p.B + (size_t)min(s.n0 + row, p.N - 1) * p.ldb + kcB[i];
+                s.b[i] = p.B + (size_t)min(s.n0 + row, p.N - 1) * p.ldb + k0 + kcB[i];
             } else {
-                const int krow = kcB[i];
+                const int krow = kcB[i];  // k row within the k-tile
                 const int col = s.n0 + (((lane & 31) ^ nmaj32_swz(krow)) << 3);
+                const size_t kr = k0 + (size_t)krow;
                 if constexpr (REG) {
                     // a chunk that straddles N is read from the row's last 8 columns, one
                     // wholly past N from column 0 (N >= 8); the write shifts or zeroes it
                     const int v = p.N - col;
                     s.nv[i] = v < 0 ? 0 : (v > 8 ? 8 : v);
-                    s.b[i] = p.B + (size_t)krow * p.ldb + (v >= 8 ? col : v > 0 ? p.N - 8 : 0);
+                    s.b[i] = p.B + kr * p.ldb + (v >= 8 ? col : v > 0 ? p.N - 8 : 0);
                 } else {
-                    s.b[i] = p.B + (size_t)krow * p.ldb + (col < p.N ? col : 0);
+                    s.b[i] = p.B + kr * p.ldb + (col < p.N ? col : 0);
                 }
             }
         }
     };
     Src cur;  // the tile being computed
-    make_src(tile, cur);
+    make_src(first, cur);
     // LDS destinations as plain wave-uniform numbers (M0 takes them directly). Built
     // from an integer, a copy's LDS pointer carries no link to sA / sB, so the
     // compiler does not make every later LDS read wait for all copies in flight
@@ -454,7 +513,7 @@ __device__ __forceinline__ void mfma32_sp_body(GemmArgs& g, const GroupArgs* ga)
     // epilogue)
     auto store4p = [&](const Src& s, int m, int n, f32x4 v) {
         if (m >= s.M) return;
-        if (GROUPED || g.ep.kind == 0) {
+        if (GROUPED || g.ep.kind == 0 || s.plain) {
             float* cp = s.C + (size_t)m * s.ldc + n;
             if (n + 3 < s.N) {
                 __builtin_memcpy(cp, &v, 16);
@@ -681,9 +740,9 @@ __device__ __forceinline__ void mfma32_sp_body(GemmArgs& g, const GroupArgs* ga)
     uint32_t sb = 0;      // stage of the current tile's k-tile 0
     bool primed = false;  // k-tiles 0 .. D-1 of the current tile are complete in LDS
     for (;;) {
-        const int ntile = round_tile(round + 1, tiles_total, g.xcd_remap);
-        const bool has_next = ntile >= 0;
-        if (has_next) make_src(ntile, nxt);
+        Unit nu;
+        const bool has_next = unit_at(round + 1, nu);
+        if (has_next) make_src(nu, nxt);
         if (!primed) {
             for (int t = 0; t < D; ++t) {
 #pragma unroll
@@ -764,7 +823,6 @@ __device__ __forceinline__ void mfma32_sp_body(GemmArgs& g, const GroupArgs* ga)
         primed = true;
         sb = (sb + (uint32_t)cur.nk) & 3u;
         cur = nxt;
-        tile = ntile;
         ++round;
 #pragma unroll
         for (int i = 0; i < 4; ++i)

@@ -47,4 +47,11 @@ int launch_pack(int elem_size, const PackJob& a, const PackJob& b, hipStream_t s
 int launch_splitk_reduce(const float* work, int S, int64_t slice, int64_t work_ld, int M, int N, void* C,
                          int64_t ldc, const Epilogue& ep, hipStream_t stream);
 
+// Stream-K fixup of a persistent launch on `G` workgroups whose last S tiles (from
+// linear tile tile0 on, KT k-tiles each) were dealt out as k-tile shares: every
+// tail tile that more than one workgroup worked on gets the sum of its partial sums
+// (work slots 2w + p, in k order), through the fused epilogue when ep.kind != 0.
+int launch_streamk_fixup(const float* work, int G, int S, int KT, int tile0, int tiles_m, int tiles_n, int group_m,
+                         int M, int N, void* C, int64_t ldc, const Epilogue& ep, hipStream_t stream);
+
 }  // namespace dg

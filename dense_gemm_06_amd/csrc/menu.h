@@ -59,6 +59,10 @@ constexpr bool persistent_capable(int sched, int threads, int64_t K) {
     return sched == 5 && threads == 512 && K % 32 == 0 && K / 32 > 3;
 }
 
+// Shortest piece of a stream-K share, in k-tiles: the copy distance of the
+// persistent kernel plus one (streamk.h).
+constexpr int kSkMinPiece = 4;
+
 // Configurations whose kernel applies a fused epilogue (every other one stores the
 // plain fp32 accumulator only): all but the 32x32x16 ping-pong kernel.
 constexpr bool epilogue_capable(int sched) { return sched != 4; }
@@ -239,6 +243,11 @@ struct GemmArgs {
     int k_split, k_chunk;
     float* work;
     int64_t work_slice, work_ld;
+    // Stream-K (persistent software-pipelined kernel only): the last sk_tiles tiles
+    // of the linear order are dealt out as equal k-tile shares (streamk.h) to the
+    // workgroups blockIdx.x < sk_width; partial sums go to work, slot 2 w + p of
+    // 256 x 256 floats. sk_tiles = 0: every tile whole.
+    int sk_tiles, sk_width;
     Epilogue ep;            // C's element type is ep.out_dt when ep.kind != 0
 };
 

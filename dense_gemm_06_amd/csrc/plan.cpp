@@ -304,6 +304,7 @@ static int plan_uncached(int opA, int opB, int64_t M, int64_t N, int64_t K, int6
 
     int want_variant = GEMM_VARIANT_AUTO, want_bm = 0, want_bn = 0, want_vec = -1, want_remap = -1, want_group = 0;
     int want_wm = 0, want_wn = 0, want_sched = 0, want_split = 0, want_pack = 0, want_threads = 0, want_grid = 0;
+    int want_sk = 0, want_skw = 0;
     if (ws_bytes < 0) {
         set_error("workspace_bytes = %lld must be non-negative", (long long)ws_bytes);
         return GEMM_ERR_INVALID_VALUE;
@@ -348,6 +349,13 @@ static int plan_uncached(int opA, int opB, int64_t M, int64_t N, int64_t K, int6
             set_error("pack = %d must be 0 (heuristic), 1 (never) or 2 (always)", want_pack);
             return GEMM_ERR_INVALID_VALUE;
         }
+        want_sk = req->stream_k;
+        want_skw = req->sk_width;
+        if (want_sk < 0 || want_sk > 2 || want_skw < 0) {
+            set_error("stream_k = %d must be 0 (heuristic), 1 (never) or 2 (always), sk_width = %d non-negative",
+                      want_sk, want_skw);
+            return GEMM_ERR_INVALID_VALUE;
+        }
         if (want_vec == 1 && !vec_ok && (ws_bytes == 0 || want_pack == 1)) {
             set_error("16-byte loads requested but the A/B bases are not aligned to the element size");
             return GEMM_ERR_UNSUPPORTED;
@@ -370,7 +378,7 @@ static int plan_uncached(int opA, int opB, int64_t M, int64_t N, int64_t K, int6
 
     const MenuEntry* best = nullptr;
     double best_cost = 0;
-    int64_t best_split = 1, best_chunk = K, short_ws = -1, best_grid = 0;
+    int64_t best_split = 1, best_chunk = K, short_ws = -1, best_grid = 0, best_sk = 0, best_skw = 0;
     bool best_packed = false;
     for (int pass = 0; pass < 2; ++pass) {
     const bool packed = pass == 1;
@@ -446,7 +454,11 @@ static int plan_uncached(int opA, int opB, int64_t M, int64_t N, int64_t K, int6
         }
         // split candidates: none, or S slices of whole k-tiles (register-staged kernels)
         const int cand[] = {1, 2, 4, 8, 16};
-        for (int ci = 0; ci < (want_split >= 2 ? 1 : 5); ++ci) {
+        // (with stream_k = 2 only the unsplit cost is taken, as the base of the
+        // stream-K candidates below, which are then the only ones)
+        const int ncand = want_split >= 2 || want_sk == 2 ? 1 : 5;
+        double dp_cost_e = -1.0;  // this entry's cost unsplit (the stream-K candidates' base)
+        for (int ci = 0; ci < ncand; ++ci) {
             const int S = want_split >= 2 ? want_split : cand[ci];
             if ((want_split == 1 || packed) && S != 1) continue;
             int64_t slices = 1, chunk = Kx;
@@ -576,6 +588,8 @@ static int plan_uncached(int opA, int opB, int64_t M, int64_t N, int64_t K, int6
                 if (slices > 1) cost += (double)(slices + 1) * (double)M * (double)N * 4.0 / 1024.0 + 16000.0;
                 if (packed) cost += pack_cycles;
             }
+            if (slices == 1) dp_cost_e = cost;
+            if (want_sk == 2) continue;
             if (!best || cost < best_cost * (1 - 1e-9) ||
                 (cost <= best_cost * (1 + 1e-9) && e.bm * e.bn > best->bm * best->bn)) {
                 best = &e;
@@ -584,9 +598,83 @@ static int plan_uncached(int opA, int opB, int64_t M, int64_t N, int64_t K, int6
                 best_chunk = chunk;
                 best_packed = packed;
                 best_grid = grid_e;
+                best_sk = 0;
+                best_skw = 0;
+            }
+        }
+        // Stream-K tail ("Shared memory and tensor cores" section 13.10) on the
+        // persistent software-pipelined kernel: the tiles that leave the last round of
+        // a grid of G partly idle (all of them with fewer tiles than G) dealt out as
+        // equal k-tile shares to `width` workgroups (more than the tail's tiles, at
+        // most G); every share at least 4 k-tiles (whole k-tiles, at least 8 per tile,
+        // and S * KT / width >= 4), a 512 KiB workspace slot pair per workgroup, no
+        // packing and no split.
+        //
+        // Cost: this entry's unsplit cost, less the tail's time on one tile per
+        // workgroup, plus the tail's time as shares and the fixup. Per k-tile of a
+        // 256 x 256 tile, one workgroup takes about 0.42 us while at most ~160 compute
+        // units are busy and 0.95 us with all 256 (the chip is power-limited: fewer
+        // busy units run at a higher clock); the fixup costs 4 us plus 0.05 us per
+        // partial sum. Fitted on 31 timings (9 shapes, each against its unsplit
+        // time, alternated on one box): 4352^2 x 2048 fp16 (tail of 33 tiles of 64
+        // k-tiles) 92.6 us on 132 workgroups against 99.5 unsplit; x 8192 279.4
+        // against 344.4; x 4096 bf16, column-major B 147.9 against 176.8; 8448 x 8192
+        // x 2048 (four rounds and 32 tiles) 272.1 against 278.6; 6144^2 x 2048 bf16
+        // (two rounds and 64) 148.9 against 150.2; 4608^2 x 1024 (68 tiles of 32
+        // k-tiles) 66.8 against 59.0; 5120^2 x 4096 (144 tiles) 228.9 on 256
+        // workgroups against 191.7. A stream-K plan must gain 2% over the unsplit one.
+        // The heuristic considers it only behind whole rounds: with fewer tiles than
+        // workgroups (all tiles shared) split K is the measured choice (2048^2 x 8192
+        // fp16, 64 tiles: 85.3 us in two slices, 82.4-89.4 as stream-K shares on 128
+        // to 256 workgroups, which the per-k-tile times above do not model).
+        if (want_sk != 1 && !packed && want_split < 2 && e.sched == 5 && e.threads == 512 && Kx % e.bk == 0 &&
+            Kx / e.bk >= 8 && dp_cost_e > 0 && (want_sk == 2 || tiles > (want_grid > 0 ? want_grid : concurrent))) {
+            const int64_t G = want_grid > 0 ? want_grid : concurrent;
+            const int64_t KT = Kx / e.bk;
+            const int64_t S = tiles > G ? tiles % G : (tiles < G ? tiles : 0);
+            auto kt_us = [&](int64_t busy) {  // one workgroup's time per k-tile
+                return busy <= 160 ? 0.42 : 0.42 + 0.53 * (double)(std::min<int64_t>(busy, 256) - 160) / 96.0;
+            };
+            const double dp_tail = (double)KT * kt_us(S);
+            // widths: the one asked for, else 2S, 3S, ... and G
+            for (int64_t m = 2; S > 0; ++m) {
+                const int64_t width = want_skw > 0 ? want_skw : std::min(m * S, G);
+                const bool last = want_skw > 0 || width == G;
+                const int64_t need = width * 2 * e.bm * e.bn * 4;
+                if (width > S && width <= G && (S * KT) / width >= kSkMinPiece && need > ws_bytes) {
+                    if (want_sk == 2) short_ws = short_ws < 0 ? need : std::min(short_ws, need);
+                } else if (width > S && width <= G && (S * KT) / width >= kSkMinPiece) {
+                    const int64_t q = (S * KT + width - 1) / width;
+                    const int64_t partials = std::min<int64_t>(2 * width, width + S);
+                    const double sk_tail = (double)q * kt_us(width) + 4.0 + 0.05 * (double)partials;
+                    const double cost = dp_cost_e * 1.02 + (sk_tail - dp_tail) * kCycles16PerUs;
+                    if (!best || cost < best_cost * (1 - 1e-9)) {
+                        best = &e;
+                        best_cost = cost;
+                        best_split = 1;
+                        best_chunk = Kx;
+                        best_packed = false;
+                        best_grid = G;
+                        best_sk = S;
+                        best_skw = width;
+                    }
+                }
+                if (last) break;
             }
         }
     }
+    }
+    if (!best && want_sk == 2 && short_ws > 0) {
+        set_error("stream_k = 2 needs at least %lld bytes of workspace; %lld were given", (long long)short_ws,
+                  (long long)ws_bytes);
+        return GEMM_ERR_INVALID_VALUE;
+    }
+    if (!best && want_sk == 2) {
+        set_error("stream_k = 2 does not apply: it needs the 8-wave schedule-5 kernel (16-bit inputs, 16-byte aligned "
+                  "operands), K a multiple of 32 with at least 8 k-tiles, no packing or split, a tile count that "
+                  "leaves a partial round of the grid, shares of at least 4 k-tiles and sk_width above the tail's tiles "
+                  "and at most the grid");
+        return GEMM_ERR_INVALID_VALUE;
     }
     if (!best && short_ws > 0) {
         set_error("split_k = %d needs %lld bytes of workspace; %lld were given", want_split, (long long)short_ws,
@@ -619,18 +707,23 @@ static int plan_uncached(int opA, int opB, int64_t M, int64_t N, int64_t K, int6
     cfg.schedule = e.sched;
     cfg.tiles_m = ((best_packed && direct_copy(e.sched) ? Mp : M) + e.bm - 1) / e.bm;
     cfg.tiles_n = ((best_packed && direct_copy(e.sched) ? Np : N) + e.bn - 1) / e.bn;
-    cfg.grid = (int32_t)std::min<int64_t>(cfg.tiles_m * cfg.tiles_n, best_grid);
+    cfg.grid = (int32_t)(best_sk > 0 ? best_grid : std::min<int64_t>(cfg.tiles_m * cfg.tiles_n, best_grid));
     cfg.max_grid = want_grid;
     // Group enough tile rows that one XCD's share of the grid forms a compact
     // rectangle; the remap needs the grid to split evenly over the 8 XCDs.
     const int gm = want_group ? want_group : default_group_m(cfg.tiles_m, cfg.tiles_n);
     cfg.group_m = (int32_t)std::max<int64_t>(1, std::min<int64_t>(gm, cfg.tiles_m));
     cfg.tiles_total = cfg.tiles_m * cfg.tiles_n;
-    cfg.launches = (best_split > 1 || best_packed) ? 2 : 1;
+    cfg.launches = (best_split > 1 || best_packed || best_sk > 0) ? 2 : 1;
+    cfg.stream_k = best_sk > 0 ? 2 : 1;
+    cfg.sk_width = (int32_t)best_skw;
     cfg.split_k = (int32_t)best_split;
     cfg.k_chunk = (int32_t)best_chunk;
     cfg.pack = best_packed ? 2 : 1;
-    cfg.workspace_bytes = best_split > 1 ? split_workspace(best_split, M, N) : best_packed ? pack_need : 0;
+    cfg.workspace_bytes = best_split > 1    ? split_workspace(best_split, M, N)
+                          : best_packed     ? pack_need
+                          : best_sk > 0     ? best_skw * 2 * (int64_t)e.bm * e.bn * 4
+                                            : 0;
     cfg.xcd_remap = want_remap >= 0 ? want_remap : ((cfg.grid % 8 == 0 && cfg.grid >= 16) ? 1 : 0);
     cfg.est_cycles = best_cost;
     *out = cfg;
@@ -649,7 +742,7 @@ namespace {
 struct PlanKey {
     int64_t M, N, K, lda, ldb, ldc, ws;
     int32_t opA, opB, dtype, num_cus, a16, b16, fused, has_req;
-    int32_t req[13];
+    int32_t req[15];
     char arch[32];
 };
 
@@ -684,9 +777,9 @@ bool make_key(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, in
     k->fused = fused ? 1 : 0;
     k->has_req = req != nullptr;
     if (req) {
-        const int32_t in[13] = {req->variant, req->bm,       req->bn,      req->vec,     req->xcd_remap,
+        const int32_t in[15] = {req->variant, req->bm,       req->bn,      req->vec,     req->xcd_remap,
                                 req->group_m, req->waves_m,  req->waves_n, req->schedule, req->max_grid,
-                                req->split_k, req->pack,     req->threads};
+                                req->split_k, req->pack,     req->threads, req->stream_k, req->sk_width};
         memcpy(k->req, in, sizeof in);
     }
     memcpy(k->arch, arch, strlen(arch));

@@ -1,13 +1,17 @@
-// reduce.hip -- the fixed-order reduction that completes a split-K product.
+// reduce.hip -- the fixed-order reductions that complete a split-K or a stream-K
+// product.
 //
 // Each K slice of a split launch wrote its partial product of C into its own
-// plane of the caller's workspace; this kernel adds the planes in slice order
+// plane of the caller's workspace; splitk_reduce adds the planes in slice order
 // 0, 1, ..., S-1 and writes C once, so the result does not depend on the order
-// in which the slices ran (no atomics).
+// in which the slices ran (no atomics). streamk_fixup does the same for the tail
+// tiles of a stream-K launch whose k-tiles several workgroups shared: it adds each
+// such tile's partial sums in k order.
 #include <algorithm>
 
 #include "device_common.h"
 #include "launch.h"
+#include "streamk.h"
 
 namespace dg {
 
@@ -42,6 +46,60 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ w
                 if (j + e < N) c[e] = acc[e];
         }
     }
+}
+
+// Stream-K fixup: block (t, y) completes rows 16y .. 16y + 15 of tail tile t (tile
+// tile0 + t of the linear order, placed by the same raster as the product kernel),
+// if more than one workgroup shared its k-tiles; G is the number of workgroups the
+// tail was dealt to. Each thread owns 4 runs of 4
+// columns; the partial sums (slot 2w + p of workgroup w's piece p, 256 x 256 fp32)
+// are added in k order, i.e. in increasing w, the first one taken as it is.
+__global__ __launch_bounds__(256) void streamk_fixup(const float* __restrict__ work, int G, int S, int KT, int tile0,
+                                                     int tiles_m, int tiles_n, int group_m, int M, int N,
+                                                     void* __restrict__ Cv, int64_t ldc, Epilogue ep) {
+    const int t = blockIdx.x;
+    const int64_t iters = (int64_t)S * KT, lo = (int64_t)t * KT, hi = lo + KT;
+    const int w0 = sk_owner(lo, G, iters, KT);
+    if (sk_bound(w0 + 1, G, iters, KT) >= hi) return;  // one piece: its workgroup stored C
+    int tm, tn;
+    raster(tile0 + t, tiles_m, tiles_n, group_m, tm, tn);
+    const int r0 = blockIdx.y * 16 + (threadIdx.x >> 6), c = (threadIdx.x & 63) * 4;  // rows r0 + 4u
+    f32x4 acc[4];
+    bool first = true;
+    for (int w = w0; w < G; ++w) {
+        const int64_t b0 = sk_bound(w, G, iters, KT), b1 = sk_bound(w + 1, G, iters, KT);
+        if (b0 >= hi) break;
+        if (b1 <= b0 || b1 <= lo) continue;  // an empty share
+        const float* slot = work + (size_t)(2 * w + (b0 >= lo ? 0 : 1)) * 65536u;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(slot + (r0 + 4 * u) * 256 + c);
+            acc[u] = first ? v : acc[u] + v;
+        }
+        first = false;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int i = tm * 256 + r0 + 4 * u, j = tn * 256 + c;
+        if (i >= M || j >= N) continue;
+        if (ep.kind != 0) {
+            epilogue_run4_body(ep, Cv, ldc, N, i, j, acc[u]);
+            continue;
+        }
+        float* cp = static_cast<float*>(Cv) + (size_t)i * (size_t)ldc + j;
+        if (j + 4 <= N) {
+            __builtin_memcpy(cp, &acc[u], 16);
+        } else {
+            for (int e = 0; e < 4; ++e)
+                if (j + e < N) cp[e] = acc[u][e];
+        }
+    }
+}
+
+int launch_streamk_fixup(const float* work, int G, int S, int KT, int tile0, int tiles_m, int tiles_n, int group_m,
+                         int M, int N, void* C, int64_t ldc, const Epilogue& ep, hipStream_t stream) {
+    return launch_status(streamk_fixup, dim3((unsigned)S, 16), dim3(256), stream, work, G, S, KT, tile0, tiles_m,
+                         tiles_n, group_m, M, N, C, ldc, ep);
 }
 
 int launch_splitk_reduce(const float* work, int S, int64_t slice, int64_t work_ld, int M, int N, void* C,

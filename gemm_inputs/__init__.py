@@ -180,6 +180,8 @@ EXTRA_CONFIGS = {
     "m8_f32_shard": dict(M=512, N=4096, K=4096, dtype="f32", dist="uniform", op_b="N"),
     # four rounds of 256 output tiles of 256 x 256 (the persistent grid's case)
     "r4_f16_8192x8192x2048": dict(M=8192, N=8192, K=2048, dtype="f16", dist="uniform", op_b="N"),
+    # 289 tiles of 256 x 256: one round of 256 and a tail of 33 (stream-K with a workspace)
+    "t33_f16_4352x4352x2048": dict(M=4352, N=4352, K=2048, dtype="f16", dist="uniform", op_b="N"),
 }
 
 

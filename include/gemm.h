@@ -132,7 +132,20 @@ typedef struct gemm_config {
     int64_t workspace_bytes; /* out: workspace the configuration uses (0 without split or packing) */
     int32_t pack;        /* in/out: operand packing (gemm_ex_workspace); in: 0 = heuristic, 1 = never,
                             2 = always; out: 2 if the call packs, else 1 */
+    int32_t stream_k;    /* in/out: stream-K tail on the persistent grid of schedule 5 (8 waves, 16-byte
+                            aligned operands, K a multiple of 32 with at least 8 k-tiles, no packing
+                            and no split; "Shared memory and tensor cores" section 13.10): the
+                            tiles that do not fill a round of `grid` workgroups (all of them when
+                            there are fewer tiles than `grid`) are dealt out as equal shares of
+                            their k-tiles to sk_width workgroups, whose partial sums a second
+                            launch adds in k order. Needs a workspace of sk_width * 512 KiB. in:
+                            0 = heuristic, 1 = never, 2 = always (GEMM_ERR_INVALID_VALUE where it
+                            cannot apply); out: 2 if the call uses it, else 1 */
+    int32_t sk_width;    /* in/out: 0 = heuristic; workgroups the stream-K tail is dealt to (more
+                            than the tail's tiles, at most the grid, each share at least 4
+                            k-tiles); out: 0 when stream-K is not used */
     int32_t reserved;
+    int32_t reserved2;
 } gemm_config;
 
 /*

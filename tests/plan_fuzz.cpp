@@ -77,6 +77,8 @@ static void random_request(gemm_config* r) {
     r->split_k = (int32_t)(coin(60) ? 0 : pick(-1, 20));
     r->pack = (int32_t)(coin(60) ? 0 : pick(-1, 3));
     r->max_grid = (int32_t)(coin(70) ? 0 : pick(-1, 600));
+    r->stream_k = (int32_t)(coin(60) ? 0 : pick(-1, 3));
+    r->sk_width = (int32_t)(coin(70) ? 0 : pick(-1, 600));
 }
 
 static void check_plan(int opB, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int dtype, uintptr_t a,
@@ -97,7 +99,30 @@ static void check_plan(int opB, int64_t M, int64_t N, int64_t K, int64_t lda, in
     CHECK(!(c.split_k > 1 && packed), "split and packed");
     CHECK(c.workspace_bytes >= 0 && c.workspace_bytes <= (ws > 0 ? ws : 0), "workspace %lld of %lld",
           (long long)c.workspace_bytes, (long long)ws);
-    CHECK(c.launches == ((c.split_k > 1 || packed) ? 2 : 1), "launches %d", c.launches);
+    const bool sk = c.stream_k == 2;
+    CHECK(c.stream_k == 1 || c.stream_k == 2, "stream_k out %d", c.stream_k);
+    CHECK(c.launches == ((c.split_k > 1 || packed || sk) ? 2 : 1), "launches %d", c.launches);
+    CHECK(!req || req->stream_k != 1 || !sk, "stream-K used with stream_k = 1");
+    CHECK(!req || req->stream_k != 2 || sk, "stream_k = 2 accepted without stream-K");
+    if (sk) {
+        // the 8-wave persistent software-pipelined kernel on whole k-tiles, at least 8 of
+        // them; no packing or split; sk_width above the tail's tiles and at most the
+        // grid, shares of at least 4 k-tiles, 512 KiB of workspace per sharing workgroup
+        const int64_t tiles = c.tiles_m * c.tiles_n;
+        const int64_t S = tiles > c.grid ? tiles % c.grid : tiles;
+        const int64_t KT = K / 32;
+        CHECK(e.sched == 5 && e.threads == 512 && !packed && c.split_k == 1 && K % 32 == 0 && KT >= 8,
+              "stream-K on schedule %d, K %lld", e.sched, (long long)K);
+        CHECK(S > 0 && S < c.grid && c.sk_width > S && c.sk_width <= c.grid && (S * KT) / c.sk_width >= kSkMinPiece,
+              "stream-K tail %lld on %d of grid %d, KT %lld", (long long)S, c.sk_width, c.grid, (long long)KT);
+        CHECK(c.workspace_bytes == (int64_t)c.sk_width * 524288, "stream-K workspace %lld", (long long)c.workspace_bytes);
+        CHECK(!req || req->max_grid <= 0 || c.grid == req->max_grid, "stream-K grid %d, max_grid %d", c.grid,
+              req ? req->max_grid : 0);
+        CHECK(!req || req->sk_width <= 0 || c.sk_width == req->sk_width, "sk_width %d asked %d", c.sk_width,
+              req ? req->sk_width : 0);
+    } else {
+        CHECK(c.sk_width == 0, "sk_width %d without stream-K", c.sk_width);
+    }
     CHECK(std::isfinite(c.est_cycles) && c.est_cycles >= 0, "estimate %g", c.est_cycles);
     if (M > 0 && N > 0) {
         CHECK(c.tiles_m >= 1 && c.tiles_n >= 1 && c.tiles_m * c.bm >= M && c.tiles_n * c.bn >= N,
@@ -110,7 +135,7 @@ static void check_plan(int opB, int64_t M, int64_t N, int64_t K, int64_t lda, in
         const int64_t Kx = packed ? (K + 63) / 64 * 64 : K;
         const bool capped = req && req->max_grid > 0;
         CHECK((int64_t)c.grid == tiles ||
-                  (c.grid < tiles && persistent_capable(e.sched, e.threads, Kx) && c.split_k == 1 &&
+                  ((c.grid < tiles || sk) && persistent_capable(e.sched, e.threads, Kx) && c.split_k == 1 &&
                    c.grid == (capped ? req->max_grid : cus)),
               "grid %d for %lld tiles (max_grid %d, schedule %d, K %lld)", c.grid, (long long)tiles,
               req ? req->max_grid : 0, e.sched, (long long)K);

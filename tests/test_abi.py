@@ -342,6 +342,55 @@ def test_plan_fp32_choices_follow_measurements():
     assert st == 0 and c.schedule == 8
 
 
+def test_plan_stream_k():
+    """The stream-K tail of the persistent software-pipelined kernel: chosen with a
+    workspace where it was timed faster (a tail of 33 or 32 tiles behind whole rounds),
+    not where it was timed slower (a tail of 68 or 144 tiles) or where a round is
+    exactly full; never without a workspace or with stream_k = 1; forced with
+    stream_k = 2 where it applies and refused with the reason where it does not."""
+    def wsplan(M, N, K, dt, op_b=0, ws=1 << 30, req=None):
+        return dg.gemm_plan_workspace(0, op_b, M, N, K, K, N if op_b == 0 else K, N, dg.DTYPE_CODE[dt], 4096, 4096,
+                                      4096, 256, "gfx950", ws, req, check=False)
+    for (M, N, K, dt, op_b) in ((4352, 4352, 2048, "f16", 0), (4352, 4352, 8192, "f16", 0),
+                                (4352, 4352, 4096, "bf16", 1), (8448, 8192, 2048, "f16", 0)):
+        st, c = wsplan(M, N, K, dt, op_b)
+        tail = c.tiles_total % c.grid
+        assert st == 0 and c.stream_k == 2 and c.schedule == 5 and c.threads == 512 and c.grid == 256, (M, N, K)
+        assert tail in (32, 33) and c.sk_width > tail and c.launches == 2 and c.split_k == 1
+        assert c.workspace_bytes == c.sk_width * 512 * 1024
+        st, c1 = wsplan(M, N, K, dt, op_b, req=dg.request(stream_k=1))
+        assert st == 0 and c1.stream_k == 1 and c1.sk_width == 0 and c1.launches == 1 and c1.workspace_bytes == 0
+        st, c0 = wsplan(M, N, K, dt, op_b, ws=0)
+        assert st == 0 and c0.stream_k == 1 and c0.workspace_bytes == 0
+        # a workspace below the chosen width's need: a narrower width or none
+        st, cs = wsplan(M, N, K, dt, op_b, ws=c.workspace_bytes - 1)
+        assert st == 0 and (cs.stream_k == 1 or cs.sk_width < c.sk_width)
+    for (M, N, K) in ((4608, 4608, 1024), (5120, 5120, 4096), (4096, 4096, 4096), (8192, 8192, 2048)):
+        st, c = wsplan(M, N, K, "f16")
+        assert st == 0 and c.stream_k == 1, (M, N, K)
+    # forced: the width asked for, the grid of a max_grid, fewer tiles than the grid
+    st, c = wsplan(768, 1024, 512, "f16", req=dg.request(stream_k=2, max_grid=8, sk_width=5))
+    assert st == 0 and c.stream_k == 2 and c.grid == 8 and c.sk_width == 5 and c.tiles_total == 12
+    st, c = wsplan(512, 512, 2048, "bf16", op_b=1, req=dg.request(stream_k=2))
+    assert st == 0 and c.stream_k == 2 and c.grid == 256 and c.tiles_total == 4 and 4 < c.sk_width <= 64
+    # refused: a round exactly full, too few k-tiles, fp32, a width not above the tail,
+    # shares under 4 k-tiles, too little workspace, a split asked for as well
+    bad = [((4096, 4096, 4096, "f16", 0), dg.request(stream_k=2)),
+           ((4352, 4352, 224, "f16", 0), dg.request(stream_k=2)),
+           ((4352, 4352, 2048, "f32", 0), dg.request(stream_k=2)),
+           ((4352, 4352, 2048, "f16", 0), dg.request(stream_k=2, sk_width=33)),
+           ((4352, 4352, 256, "f16", 0), dg.request(stream_k=2, sk_width=256)),
+           ((4352, 4352, 2048, "f16", 0), dg.request(stream_k=2, split_k=2))]
+    for (M, N, K, dt, op_b), req in bad:
+        st, _ = wsplan(M, N, K, dt, op_b, req=req)
+        assert st == dg.GEMM_ERR_INVALID_VALUE and "stream_k" in dg.gemm_last_error(), (M, N, K, dt)
+    st, _ = wsplan(4352, 4352, 2048, "f16", ws=1 << 20, req=dg.request(stream_k=2))
+    assert st == dg.GEMM_ERR_INVALID_VALUE and "workspace" in dg.gemm_last_error()
+    for req in (dg.request(stream_k=3), dg.request(stream_k=-1), dg.request(sk_width=-2)):
+        st, _ = wsplan(4352, 4352, 2048, "f16", req=req)
+        assert st == dg.GEMM_ERR_INVALID_VALUE
+
+
 def test_plan_16bit_choices_follow_measurements():
     """16-bit choices with a workspace on shapes where the choice was timed against the
     previous model's (medians of five alternated passes, one box): few tiles facing a
