@@ -86,6 +86,9 @@ def parse():
                    help="also time the fused epilogue, the per-launch distribution, the clock under load and the "
                         "four-round problem with one workgroup per tile (more launches of the headline kernel, so a "
                         "kernel trace of such a run averages over more than the timed steps)")
+    p.add_argument("--mfma-ceiling", action="store_true",
+                   help="time libdgprobe.so's MFMA-only loop (every CU, no memory traffic) on changing random fp16 "
+                        "operands and on fixed ones: the power-limited ceiling of the 16-bit product")
     p.add_argument("--traffic-probe", type=int, default=0, metavar="MIB",
                    help="instead of GEMMs, run the counter-calibration kernels over MIB MiB each (direct LDS "
                         "copies of 64-byte row segments, 16-byte loads, 16-byte stores)")
@@ -453,6 +456,45 @@ def traffic_probe(mib):
     print(json.dumps({"traffic_probe": res}), flush=True)
 
 
+def mfma_ceiling(cus, iters=20000, reps=10):
+    """TFLOP/s of libdgprobe.so's MFMA-only loop on all compute units, after three
+    untimed launches, for operand fragments drawn uniform in [-1, 1) (as the benchmark's
+    fp16 inputs), all 0.5, and all zero."""
+    import ctypes
+    import numpy as np
+    import torch
+    from dense_gemm_06_amd import build as b
+    lib = ctypes.CDLL(b.PROBE_LIB)
+    lib.dg_probe_mfma_ceiling.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_void_p]
+    lib.dg_probe_mfma_frag_bytes.restype = ctypes.c_int64
+    lib.dg_probe_mfma_out_bytes.argtypes = [ctypes.c_int]
+    lib.dg_probe_mfma_out_bytes.restype = ctypes.c_int64
+    n = lib.dg_probe_mfma_frag_bytes() // 2
+    out = torch.empty(lib.dg_probe_mfma_out_bytes(cus) // 4, dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    res = {}
+    rng = np.random.default_rng(0)
+    for name, vals in (("random_uniform", rng.uniform(-1.0, 1.0, n)), ("constant_0.5", np.full(n, 0.5)),
+                       ("zero", np.zeros(n))):
+        frag = torch.from_numpy(vals.astype(np.float16)).to("cuda")
+        run = lambda: lib.dg_probe_mfma_ceiling(frag.data_ptr(), out.data_ptr(), cus, iters, s)
+        for _ in range(3):
+            if run() != 0:
+                raise RuntimeError("probe launch failed")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        flops = cus * 8 * iters * 64 * 32768.0
+        res[name] = {"ms_per_launch": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                     "frac_of_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["f16"], 4)}
+    print(json.dumps({"mfma_ceiling": res, "cus": cus, "iters": iters, "launches": reps}), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -465,6 +507,9 @@ def main():
         sys.exit(2)
     if a.traffic_probe:
         traffic_probe(a.traffic_probe)
+        return
+    if a.mfma_ceiling:
+        mfma_ceiling(torch.cuda.get_device_properties(0).multi_processor_count)
         return
     import dense_gemm_06_amd as dg
     dg.library()   # fail loudly if the HIP library is missing

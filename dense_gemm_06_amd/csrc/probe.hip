@@ -10,8 +10,17 @@
 //   kind 1  reads with global_load_dwordx4, 64 lanes covering 1 KB contiguously;
 //   kind 2  writes with global_store_dwordx4, 64 lanes covering 1 KB contiguously
 //           (the staged epilogue's whole-row stores).
-// Every byte is touched exactly once. This library is a measurement tool: the GEMM
-// library neither links nor calls it.
+// Every byte is touched exactly once.
+//
+// probe_mfma_ceiling measures the other bound of the 16-bit product: the rate at
+// which the matrix units retire v_mfma_f32_32x32x16_f16 on every compute unit (two
+// waves per SIMD, eight accumulators per wave as in the 8-wave software-pipelined
+// kernel) with no memory traffic at all, on operands that either change from one
+// instruction to the next (eight fragment sets per lane, uniform in [-1, 1) like
+// the benchmark's inputs) or stay fixed. The board's power limit makes the first
+// rate the attainable ceiling of any fp16 product on data of that kind.
+//
+// This library is a measurement tool: the GEMM library neither links nor calls it.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -22,6 +31,9 @@
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+constexpr int kMfmaSets = 8;  // operand fragment sets cycled by probe_mfma_ceiling
 
 constexpr int kRowElems = 4096;               // 16-bit elements per source row (8 KB)
 constexpr int64_t kPanelBytes = 256LL * 8192;  // one workgroup's 256 rows
@@ -65,9 +77,52 @@ __global__ __launch_bounds__(256) void probe_write(u32x4* __restrict__ dst, int6
         dst[i] = u32x4{(uint32_t)i, 1u, 2u, 3u};
 }
 
+// frag: 2 * kMfmaSets * 64 fragments of 8 fp16 (A and B of each set, one per lane);
+// out: one float per thread (keeps the accumulators live).
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void probe_mfma_ceiling(
+    const f16x8* __restrict__ frag, float* __restrict__ out, int iters) {
+    const int lane = threadIdx.x & 63;
+    f16x8 a[kMfmaSets], b[kMfmaSets];
+#pragma unroll
+    for (int s = 0; s < kMfmaSets; ++s) {
+        a[s] = frag[(2 * s) * 64 + lane];
+        b[s] = frag[(2 * s + 1) * 64 + lane];
+    }
+    f32x16 acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = f32x16{};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int s = 0; s < kMfmaSets; ++s)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[(s + j) % kMfmaSets], b[(s + 3 * j) % kMfmaSets],
+                                                               acc[j], 0, 0, 0);
+    }
+    float t = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) t += acc[j][e];
+    out[(size_t)blockIdx.x * 512 + threadIdx.x] = t;
+}
+
 }  // namespace
 
 extern "C" {
+
+// Bytes of the fragment table and of the output probe_mfma_ceiling needs for a grid.
+int64_t dg_probe_mfma_frag_bytes(void) { return 2 * kMfmaSets * 64 * 16; }
+int64_t dg_probe_mfma_out_bytes(int grid) { return (int64_t)grid * 512 * 4; }
+
+// Launch probe_mfma_ceiling: `grid` workgroups of 8 waves, each wave issuing iters *
+// 64 MFMAs of 32 x 32 x 16 (32768 FLOP each). Returns 0, 1 for invalid arguments, or
+// the hipError_t of the launch.
+int dg_probe_mfma_ceiling(const void* frag, void* out, int grid, int iters, void* stream) {
+    if (frag == nullptr || out == nullptr || grid <= 0 || iters <= 0) return 1;
+    return dg::launch_status(probe_mfma_ceiling, dim3((unsigned)grid), dim3(512), (hipStream_t)stream,
+                             static_cast<const f16x8*>(frag), static_cast<float*>(out), iters);
+}
 
 // Launch probe `kind` over `bytes` on `stream`. kind 0: src holds bytes / 8192 rows of
 // 4096 16-bit elements and bytes must be a positive multiple of 2 MiB (256 rows); kind
