@@ -220,6 +220,13 @@ int gemm_plan(int opA, int opB, int64_t M, int64_t N, int64_t K, int64_t lda, in
  * on the fastest kernels; C is written only within M x N. Packing needs
  * (Mp*Kp rounded up to 256 bytes + Np*Kp) elements of the input type, Mp, Np
  * = M, N rounded up to 256, Kp = K rounded up to 64; cfg->pack forces a choice.
+ * A third use is the stream-K tail of the persistent software-pipelined kernel
+ * ("Shared memory and tensor cores", section 13.10, split-K and stream-K): the
+ * tiles that leave the persistent grid's last round partly idle are dealt out as
+ * equal shares of their k-tiles to cfg->sk_width workgroups; shares that end
+ * inside a tile leave fp32 partial sums in the workspace (sk_width * 512 KiB),
+ * which a second kernel adds in k order into C, applying any epilogue (so results
+ * are reproducible call to call); cfg->stream_k forces a choice.
  * workspace_bytes = 0 (workspace may be NULL) behaves as gemm_ex. Otherwise the
  * workspace must be 16-byte aligned and its whole declared range must not overlap
  * A, B or C (GEMM_ERR_INVALID_VALUE, checked before any launch); its contents
