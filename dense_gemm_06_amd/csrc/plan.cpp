@@ -641,9 +641,12 @@ static int plan_uncached(int opA, int opB, int64_t M, int64_t N, int64_t K, int6
                 const int64_t width = want_skw > 0 ? want_skw : std::min(m * S, G);
                 const bool last = want_skw > 0 || width == G;
                 const int64_t need = width * 2 * e.bm * e.bn * 4;
-                if (width > S && width <= G && (S * KT) / width >= kSkMinPiece && need > ws_bytes) {
+                // (the share arithmetic takes width * S * KT below 2^53)
+                const bool fits = width > S && width <= G && (S * KT) / width >= kSkMinPiece &&
+                                  (double)width * (double)(S * KT) < 9.0e15;
+                if (fits && need > ws_bytes) {
                     if (want_sk == 2) short_ws = short_ws < 0 ? need : std::min(short_ws, need);
-                } else if (width > S && width <= G && (S * KT) / width >= kSkMinPiece) {
+                } else if (fits) {
                     const int64_t q = (S * KT + width - 1) / width;
                     const int64_t partials = std::min<int64_t>(2 * width, width + S);
                     const double sk_tail = (double)q * kt_us(width) + 4.0 + 0.05 * (double)partials;

@@ -29,13 +29,26 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "menu.h"
+
 namespace dg {
+
+// floor(a / d) for 0 <= a < 2^53 and 0 < d < 2^31: a double-precision quotient
+// (a and d convert exactly) corrected by one step, since the rounded quotient can
+// land on the next integer. A 64-bit integer division is a long instruction
+// sequence on the GPU, and the fixup kernel takes a dozen of these per tile.
+__host__ __device__ inline int64_t sk_div(int64_t a, int64_t d) {
+    int64_t q = (int64_t)((double)a / (double)d);
+    if (q * d > a) --q;
+    else if ((q + 1) * d <= a) ++q;
+    return q;
+}
 
 // First k-tile (in the tail's linear iteration space of `iters` = S * KT k-tiles)
 // of workgroup w's share, w = 0 .. G; bound(0) = 0 and bound(G) = iters.
 __host__ __device__ inline int64_t sk_bound(int w, int G, int64_t iters, int KT) {
-    int64_t b = (int64_t)w * iters / G;
-    const int64_t r = b % KT;
+    int64_t b = sk_div((int64_t)w * iters, G);
+    const int64_t r = b - sk_div(b, KT) * KT;
     if (r != 0) {
         if (r < kSkMinPiece) b -= r;
         else if (KT - r < kSkMinPiece) b += KT - r;
@@ -59,9 +72,9 @@ __host__ __device__ inline int sk_owner(int64_t it, int G, int64_t iters, int KT
 __host__ __device__ inline bool sk_piece(int w, int p, int G, int S, int KT, int& tile, int& kb, int& nk) {
     const int64_t iters = (int64_t)S * KT;
     const int64_t b0 = sk_bound(w, G, iters, KT), b1 = sk_bound(w + 1, G, iters, KT);
-    const int64_t s = p == 0 ? b0 : (b0 / KT + 1) * KT;
+    const int64_t s = p == 0 ? b0 : (sk_div(b0, KT) + 1) * KT;
     if (s >= b1) return false;
-    const int64_t t = s / KT;
+    const int64_t t = sk_div(s, KT);
     const int64_t e = b1 < (t + 1) * KT ? b1 : (t + 1) * KT;
     tile = (int)t;
     kb = (int)(s - t * KT);
