@@ -614,8 +614,8 @@ static int plan_uncached(int opA, int opB, int64_t M, int64_t N, int64_t K, int6
         // workgroup, plus the tail's time as shares and the fixup. Per k-tile of a
         // 256 x 256 tile, one workgroup takes about 0.42 us while at most ~160 compute
         // units are busy and 0.95 us with all 256 (the chip is power-limited: fewer
-        // busy units run at a higher clock); the fixup costs 4 us plus 0.05 us per
-        // partial sum. Fitted on 31 timings (9 shapes, each against its unsplit
+        // busy units run at a higher clock); the fixup costs 4 us plus 0.04 us per
+        // partial sum (10.6 us for the 165 of 4352^2 x 2048 on 132 workgroups). Fitted on 31 timings (9 shapes, each against its unsplit
         // time, alternated on one box): 4352^2 x 2048 fp16 (tail of 33 tiles of 64
         // k-tiles) 92.6 us on 132 workgroups against 99.5 unsplit; x 8192 279.4
         // against 344.4; x 4096 bf16, column-major B 147.9 against 176.8; 8448 x 8192
@@ -649,7 +649,7 @@ static int plan_uncached(int opA, int opB, int64_t M, int64_t N, int64_t K, int6
                 } else if (fits) {
                     const int64_t q = (S * KT + width - 1) / width;
                     const int64_t partials = std::min<int64_t>(2 * width, width + S);
-                    const double sk_tail = (double)q * kt_us(width) + 4.0 + 0.05 * (double)partials;
+                    const double sk_tail = (double)q * kt_us(width) + 4.0 + 0.04 * (double)partials;
                     const double cost = dp_cost_e * 1.02 + (sk_tail - dp_tail) * kCycles16PerUs;
                     if (!best || cost < best_cost * (1 - 1e-9)) {
                         best = &e;

@@ -48,54 +48,55 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ w
     }
 }
 
-// Stream-K fixup: block (t, y) completes rows 8y .. 8y + 7 of tail tile t (tile
+// Stream-K fixup: block (t, y) completes rows 16y .. 16y + 15 of tail tile t (tile
 // tile0 + t of the linear order, placed by the same raster as the product kernel),
 // if more than one workgroup shared its k-tiles; G is the number of workgroups the
-// tail was dealt to. Each thread owns 2 runs of 4 columns (rows 8y + r and 8y + r +
-// 4). The partial sums (slot 2w + p of workgroup w's piece p, 256 x 256 fp32) are
-// added in k order, i.e. in increasing w, the first one taken as it is; they are
-// gathered four pieces at a time so that each thread has up to eight loads in
-// flight rather than one.
+// tail was dealt to. Each thread owns 4 runs of 4 columns (rows 16y + r + 4u). The
+// partial sums (slot 2w + p of workgroup w's piece p, 256 x 256 fp32) are added in k
+// order, i.e. in increasing w, the first one taken as it is; they are gathered four
+// pieces at a time, so that a thread has up to sixteen loads in flight. (Grids of 32
+// and 64 blocks per tile, with fewer runs per thread, measured slower: each block
+// first works out the tile's pieces, which costs more than the loads it saves.)
 __global__ __launch_bounds__(256) void streamk_fixup(const float* __restrict__ work, int G, int S, int KT, int tile0,
                                                      int tiles_m, int tiles_n, int group_m, int M, int N,
                                                      void* __restrict__ Cv, int64_t ldc, Epilogue ep) {
     const int t = blockIdx.x;
     const int64_t iters = (int64_t)S * KT, lo = (int64_t)t * KT, hi = lo + KT;
     const int w0 = sk_owner(lo, G, iters, KT);
-    if (sk_bound(w0 + 1, G, iters, KT) >= hi) return;  // one piece: its workgroup stored C
+    int64_t b0 = sk_bound(w0, G, iters, KT), b1 = sk_bound(w0 + 1, G, iters, KT);
+    if (b1 >= hi) return;  // one piece: its workgroup stored C
     int tm, tn;
     raster(tile0 + t, tiles_m, tiles_n, group_m, tm, tn);
-    const int r0 = blockIdx.y * 8 + (threadIdx.x >> 6), c = (threadIdx.x & 63) * 4;  // rows r0, r0 + 4
-    f32x4 acc[2];
+    const int r0 = blockIdx.y * 16 + (threadIdx.x >> 6), c = (threadIdx.x & 63) * 4;  // rows r0 + 4u
+    f32x4 acc[4];
     bool first = true;
     int w = w0;
-    int64_t b0 = sk_bound(w0, G, iters, KT);
     for (;;) {
-        // the next (up to) four pieces in the tile, in k order
+        // the next (up to) four pieces in the tile, in k order; b0, b1 bound share w
         const float* slot[4];
         int n = 0;
         while (n < 4 && w < G && b0 < hi) {
-            const int64_t b1 = sk_bound(w + 1, G, iters, KT);
             if (b1 > b0 && b1 > lo) slot[n++] = work + (size_t)(2 * w + (b0 >= lo ? 0 : 1)) * 65536u;
             ++w;
             b0 = b1;
+            if (w < G) b1 = sk_bound(w + 1, G, iters, KT);
         }
         if (n == 0) break;
-        f32x4 v[4][2];
+        f32x4 v[4][4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             if (i < n)
 #pragma unroll
-                for (int u = 0; u < 2; ++u) v[i][u] = *reinterpret_cast<const f32x4*>(slot[i] + (r0 + 4 * u) * 256 + c);
+                for (int u = 0; u < 4; ++u) v[i][u] = *reinterpret_cast<const f32x4*>(slot[i] + (r0 + 4 * u) * 256 + c);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             if (i < n)
 #pragma unroll
-                for (int u = 0; u < 2; ++u) acc[u] = first && i == 0 ? v[i][u] : acc[u] + v[i][u];
+                for (int u = 0; u < 4; ++u) acc[u] = first && i == 0 ? v[i][u] : acc[u] + v[i][u];
         first = false;
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < 4; ++u) {
         const int i = tm * 256 + r0 + 4 * u, j = tn * 256 + c;
         if (i >= M || j >= N) continue;
         if (ep.kind != 0) {
@@ -114,7 +115,7 @@ __global__ __launch_bounds__(256) void streamk_fixup(const float* __restrict__ w
 
 int launch_streamk_fixup(const float* work, int G, int S, int KT, int tile0, int tiles_m, int tiles_n, int group_m,
                          int M, int N, void* C, int64_t ldc, const Epilogue& ep, hipStream_t stream) {
-    return launch_status(streamk_fixup, dim3((unsigned)S, 32), dim3(256), stream, work, G, S, KT, tile0, tiles_m,
+    return launch_status(streamk_fixup, dim3((unsigned)S, 16), dim3(256), stream, work, G, S, KT, tile0, tiles_m,
                          tiles_n, group_m, M, N, C, ldc, ep);
 }
 

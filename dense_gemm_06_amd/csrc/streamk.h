@@ -33,11 +33,13 @@
 
 namespace dg {
 
-// floor(a / d) for 0 <= a < 2^53 and 0 < d < 2^31: a double-precision quotient
-// (a and d convert exactly) corrected by one step, since the rounded quotient can
-// land on the next integer. A 64-bit integer division is a long instruction
-// sequence on the GPU, and the fixup kernel takes a dozen of these per tile.
+// floor(a / d) for 0 <= a < 2^53 and 0 < d < 2^31: a 32-bit division when a fits
+// in 32 bits, else a double-precision quotient (a and d convert exactly) corrected
+// by one step, since the rounded quotient can land on the next integer. A 64-bit
+// integer division is a long instruction sequence on the GPU, and the fixup kernel
+// takes several of these per tile before its first load.
 __host__ __device__ inline int64_t sk_div(int64_t a, int64_t d) {
+    if (a < ((int64_t)1 << 32)) return (int64_t)((uint32_t)a / (uint32_t)d);  // the common case
     int64_t q = (int64_t)((double)a / (double)d);
     if (q * d > a) --q;
     else if ((q + 1) * d <= a) ++q;
@@ -57,14 +59,15 @@ __host__ __device__ inline int64_t sk_bound(int w, int G, int64_t iters, int KT)
 }
 
 // The largest w in 0 .. G - 1 with sk_bound(w) <= it (bounds are non-decreasing).
+// Unmoved bounds are floor(w * iters / G), which puts the owner at floor(it * G /
+// iters) give or take the moves; the walks below correct the estimate (a step or
+// two: a move is at most 3 k-tiles, a share at least 4).
 __host__ __device__ inline int sk_owner(int64_t it, int G, int64_t iters, int KT) {
-    int lo = 0, hi = G - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (sk_bound(mid, G, iters, KT) <= it) lo = mid;
-        else hi = mid - 1;
-    }
-    return lo;
+    int64_t w = sk_div(it * G, iters);
+    if (w > G - 1) w = G - 1;
+    while (w > 0 && sk_bound((int)w, G, iters, KT) > it) --w;
+    while (w + 1 < G && sk_bound((int)w + 1, G, iters, KT) <= it) ++w;
+    return (int)w;
 }
 
 // Piece p (0 or 1) of workgroup w's share: tail tile `tile` (0 .. S - 1), its first
