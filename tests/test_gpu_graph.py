@@ -84,10 +84,17 @@ def test_plain_call_in_graph(case):
     run_case(call, [A, B], C)
 
 
-@pytest.mark.parametrize("case", ["split_k", "split_k_pipelined_f16", "split_k_pipelined_reg_bf16", "packed"])
+@pytest.mark.parametrize("case", ["split_k", "split_k_pipelined_f16", "split_k_pipelined_reg_bf16", "packed",
+                                  "stream_k_f16", "stream_k_bf16_T"])
 def test_workspace_call_in_graph(case):
     torch = _torch()
-    if case == "split_k":
+    if case == "stream_k_f16":
+        dtype, op_b, (M, N, K), pad = "f16", "N", (768, 1024, 512), (0, 0)
+        req = dg.request(schedule=5, waves_n=4, max_grid=8, stream_k=2, sk_width=5)
+    elif case == "stream_k_bf16_T":
+        dtype, op_b, (M, N, K), pad = "bf16", "T", (1000, 1000, 1024), (0, 0)
+        req = dg.request(schedule=5, waves_n=4, max_grid=12, stream_k=2, sk_width=9)
+    elif case == "split_k":
         dtype, op_b, (M, N, K), req, pad = "f32", "N", (256, 256, 8192), dg.request(split_k=8), (0, 0)
     elif case == "split_k_pipelined_f16":
         dtype, op_b, (M, N, K), req, pad = "f16", "N", (512, 768, 4096), dg.request(schedule=5, split_k=4), (0, 0)
@@ -101,8 +108,9 @@ def test_workspace_call_in_graph(case):
     W = [torch.empty(ws // 4, dtype=torch.float32, device="cuda") for _ in range(2)]
     _, plan = dg.gemm_plan_workspace(0, dg.OP_CODE[op_b], M, N, K, lda, ldb, N, dg.DTYPE_CODE[dtype], A.data_ptr(),
                                      B.data_ptr(), C[0].data_ptr(), 256, "gfx950", ws, req)
-    print(f"graph case {case}: split {plan.split_k} pack {plan.pack} launches {plan.launches}", flush=True)
-    assert plan.launches == 2
+    print(f"graph case {case}: split {plan.split_k} pack {plan.pack} stream-K {plan.stream_k} launches "
+          f"{plan.launches}", flush=True)
+    assert plan.launches == 2 and (plan.stream_k == 2) == case.startswith("stream_k")
 
     def call(i, s):
         dg.gemm_ex_workspace(0, dg.OP_CODE[op_b], M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C[i].data_ptr(), N,
