@@ -725,7 +725,11 @@ __device__ __forceinline__ void mfma32_sp_body(GemmArgs& g, const GroupArgs* ga)
     } else {
     // ---- the direct-copy form on a persistent grid: each workgroup takes one tile of
     // each round of `grid` tiles until a round has none for it (K a multiple of 32
-    // with more than D k-tiles, checked by the host). The stream of k-tile copies runs on across tiles: the last D iterations of
+    // with more than D k-tiles, checked by the host), then, with stream-K, the pieces
+    // of its share of the tail; a piece runs as a tile whose k-tiles are the piece's
+    // (its sources start at the piece's first k, and it has at least D + 1 k-tiles).
+    // Below, "tile" means such a unit. The stream of k-tile copies runs on across
+    // tiles: the last D iterations of
     // a tile, which have no k-tile of their own left to copy, copy k-tiles 0 .. D-1 of
     // the workgroup's next tile into the stages that follow, so the next tile starts
     // with its first D k-tiles in LDS and no pipeline fill. The finished tile's
