@@ -4,7 +4,8 @@ C ABI: the planner sees the same workspace size, so both run the same kernels an
 must give the same bits. Each case makes two calls in a row, the second on a
 smaller problem, so the second runs on scratch that still holds the first call's
 contents. One case packs the operands into the scratch, one splits K into it, one
-uses neither; the first case is also checked against the oracle.
+keeps the partial sums of a stream-K tail in it, one uses neither; the first case
+is also checked against the oracle.
 """
 from __future__ import annotations
 
@@ -54,6 +55,10 @@ CASES = {
     # 16 output tiles facing a long K: split K into partial planes in the scratch
     "split": lambda: [gi.make_operands(256, 256, 16384, "f32", "uniform", seed=3),
                       gi.make_operands(128, 192, 8192, "f32", "uniform", seed=4)],
+    # a stream-K tail on a persistent grid of 8 (12 and 12 tiles: tails of 4 over 5
+    # workgroups): partial sums in the scratch
+    "stream_k": lambda: [gi.make_operands(768, 1024, 512, "f16", "uniform", seed=7),
+                         gi.make_operands(600, 1024, 384, "f16", "uniform", seed=8)],
     # neither (the scratch is not used)
     "plain": lambda: [gi.make_operands(1024, 1024, 512, "f16", "uniform", seed=5),
                       gi.make_operands(200, 136, 100, "f16", "uniform", seed=6)],
@@ -64,7 +69,8 @@ CASES = {
 def test_noalloc_matches_workspace_call(name):
     for i, ops in enumerate(CASES[name]()):
         print(f"noalloc case {name} call {i}: M={ops.M} N={ops.N} K={ops.K} {ops.dtype} op {ops.op_b}", flush=True)
-        cfg = dg.request(pack=2) if name == "packed" else None
+        cfg = (dg.request(pack=2) if name == "packed" else
+               dg.request(schedule=5, waves_n=4, max_grid=8, stream_k=2, sk_width=5) if name == "stream_k" else None)
         got, plan = _run(ops, noalloc=True, cfg=cfg)
         ref, plan_ws = _run(ops, noalloc=False, cfg=cfg)
         assert plan.as_dict() == plan_ws.as_dict()
@@ -72,6 +78,8 @@ def test_noalloc_matches_workspace_call(name):
             assert plan.pack == 2
         if name == "split" and i == 0:
             assert plan.split_k > 1
+        if name == "stream_k":
+            assert plan.stream_k == 2 and plan.sk_width == 5 and plan.grid == 8
         if name == "plain":
             assert plan.pack == 1 and plan.split_k == 1
         check_untouched(got, ops.M, ops.N)
