@@ -452,11 +452,16 @@ static int plan_uncached(int opA, int opB, int64_t M, int64_t N, int64_t K, int6
         } else if (want_grid == 0 && tiles > concurrent && persistent_capable(e.sched, e.threads, Kx)) {
             grid_e = concurrent;
         }
-        // split candidates: none, or S slices of whole k-tiles (register-staged kernels)
-        const int cand[] = {1, 2, 4, 8, 16};
+        // split candidates: none, or S slices of whole k-tiles. Three and six slices
+        // bring few 256 x 256 tiles near 192 workgroups, where the software-pipelined
+        // kernel's split products measured best (medians of three alternated passes,
+        // one box: 512 x 4096 x 8192 fp16, 32 tiles, 50.4 us in six slices against 54.1
+        // in four and 55.5 in eight; 1024 x 4096 x 4096, 64 tiles, 51.1 in three against
+        // 55.2 in two and 54.2 in four)
+        const int cand[] = {1, 2, 3, 4, 6, 8, 16};
         // (with stream_k = 2 only the unsplit cost is taken, as the base of the
         // stream-K candidates below, which are then the only ones)
-        const int ncand = want_split >= 2 || want_sk == 2 ? 1 : 5;
+        const int ncand = want_split >= 2 || want_sk == 2 ? 1 : 7;
         double dp_cost_e = -1.0;  // this entry's cost unsplit (the stream-K candidates' base)
         for (int ci = 0; ci < ncand; ++ci) {
             const int S = want_split >= 2 ? want_split : cand[ci];
