@@ -29,7 +29,17 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ w
         const int j = (int)(q - (int64_t)i * quads) * 4;
         const float* w = work + (size_t)i * (size_t)work_ld + j;
         f32x4 acc = *reinterpret_cast<const f32x4*>(w);
-        for (int s = 1; s < S; ++s) acc += *reinterpret_cast<const f32x4*>(w + (size_t)s * (size_t)slice);
+        // planes 1 .. S-1 in order, their loads issued four at a time (a load per
+        // iteration would wait out one memory latency per plane)
+        int s = 1;
+        for (; s + 4 <= S; s += 4) {
+            f32x4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const f32x4*>(w + (size_t)(s + u) * (size_t)slice);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) acc += v[u];
+        }
+        for (; s < S; ++s) acc += *reinterpret_cast<const f32x4*>(w + (size_t)s * (size_t)slice);
         if (ep.kind != 0) {
             // the fused epilogue applies to the complete sum
             for (int e = 0; e < 4; ++e)
