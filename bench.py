@@ -18,10 +18,12 @@ milliseconds of sustained work): a small problem gets enough steps for about 5 m
 of launches (reported as `steps`), so that the start of the idle queue, paid once
 per timed window, does not weigh on its step time.
 
-Only the W + K headline launches run the headline kernel in the default command
-(the fused epilogue, the per-launch distribution and the clock probe, which
-launch it many more times, run only with --extended), so a kernel trace of the
-default command averages exactly those launches.
+Only the W + K headline launches run the headline kernel on its 256-workgroup grid
+in the default command (the fused epilogue, the per-launch distribution and the
+clock probe, which launch it many more times, run only with --extended; the K-split
+launches of the 512 x 4096 x 4096 shard run the same kernel on a 2-D grid), so a
+kernel trace of the default command, filtered by grid, averages exactly those
+launches.
 
 CPU baseline: the oracle (plain fp64 triple loop, OpenMP) timed on the host
 cores on a bounded sample of the same problem (its first r rows; about 10-20 s
